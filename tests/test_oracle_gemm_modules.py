@@ -1,0 +1,185 @@
+"""Pins for the oracle's FP8 GEMM and the module chains (CPU only).
+
+The GEMM is pinned exactly by brute force in rational arithmetic and by
+permutation matrices; the module chains by the module-tour shapes of the
+tutorial and by comparison with unquantised float64 autograd, whose distance
+from the FP8 chain is bounded by the formats' rounding error.
+"""
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from oracle import E4M3, E5M2
+
+
+def random_codes(shape, fmt, seed):
+    """Random finite codes of either sign."""
+    t = oracle.fp8_decode_table(fmt)
+    finite = np.array([c for c in range(256) if np.isfinite(t[c])], dtype=np.uint8)
+    return np.random.default_rng(seed).choice(finite, size=shape)
+
+
+@pytest.mark.parametrize("fa,fb", [(E4M3, E4M3), (E5M2, E4M3), (E4M3, E5M2), (E5M2, E5M2)])
+def test_gemm_exact_against_rational_brute_force(fa, fb):
+    M, N, K = 5, 4, 33
+    a = random_codes((M, K), fa, 1)
+    b = random_codes((N, K), fb, 2)
+    ta, tb = oracle.fp8_decode_table(fa), oracle.fp8_decode_table(fb)
+    c = oracle.fp8_gemm_tn(a, fa, b, fb)
+    for i in range(M):
+        for j in range(N):
+            terms = [Fraction(float(ta[a[i, k]])) * Fraction(float(tb[b[j, k]]))
+                     for k in range(K)]
+            exact = sum(terms)
+            if fa == fb == E4M3:
+                # every E4M3 product is a multiple of 2^-18 below 2^17.6: the
+                # float64 sum of K terms is exact
+                assert Fraction(float(c[i, j])) == exact
+            else:
+                # E5M2 spans 2^-16 .. 2^15.8: float64 summation error bound
+                bound = Fraction(K * 2 ** -52) * sum(abs(t) for t in terms)
+                assert abs(Fraction(float(c[i, j])) - exact) <= bound
+
+
+def test_gemm_permutation_and_epilogue():
+    """B = permutation matrix of 1.0 codes selects columns of A exactly; then
+    the scale_inv product and the bias are applied per column."""
+    K = 48
+    rng = np.random.default_rng(3)
+    a = random_codes((7, K), E4M3, 4)
+    a[np.isnan(oracle.fp8_decode(a, E4M3))] = 0
+    perm = rng.permutation(K)
+    b = np.zeros((K, K), dtype=np.uint8)
+    b[np.arange(K), perm] = 0x38                       # 1.0 in E4M3
+    bias = np.arange(K, dtype=np.float64)
+    c = oracle.fp8_gemm_tn(a, E4M3, b, E4M3, np.float32(0.5), np.float32(4.0), None)
+    np.testing.assert_array_equal(c, oracle.fp8_decode(a, E4M3)[:, perm] * 2.0)
+    bias_bits = oracle.f64_to_bf16_bits(bias)
+    c2 = oracle.fp8_gemm_tn(a, E4M3, b, E4M3, 1.0, 1.0, oracle.bf16_to_f64(bias_bits))
+    np.testing.assert_array_equal(c2, oracle.fp8_decode(a, E4M3)[:, perm] + bias[None, :])
+
+
+def bf16_bits(x):
+    return oracle.f64_to_bf16_bits(np.asarray(x, dtype=np.float64))
+
+
+def load_tour():
+    path = os.path.join(os.path.dirname(__file__), "golden", "module_tour.txt")
+    rows = []
+    for line in open(path):
+        line = line.split("#")[0].strip()
+        if line:
+            name, fin, fout, ishape, oshape = line.split()
+            rows.append((name, int(fin), int(fout), tuple(map(int, ishape.split(","))),
+                         tuple(map(int, oshape.split(",")))))
+    return rows
+
+
+@pytest.mark.parametrize("row", load_tour(), ids=lambda r: r[0])
+def test_module_tour_shapes(row):
+    name, fin, fout, ishape, oshape = row
+    rng = np.random.default_rng(0)
+    x = bf16_bits(rng.normal(size=ishape)).reshape(-1, fin)
+    g, b = bf16_bits(np.ones(fin)), bf16_bits(np.zeros(fin))
+    r = oracle.Recipe()
+    if name == "LayerNormLinear":
+        m = oracle.linear_fwd_meta(r)
+        out, _ = oracle.ln_linear_fwd(r, m, x, g, b, bf16_bits(0.02 * rng.normal(size=(fout, fin))))
+    else:
+        m = oracle.mlp_fwd_meta(r)
+        out, _ = oracle.ln_mlp_fwd(r, m, x, g, b, bf16_bits(0.02 * rng.normal(size=(fout, fin))),
+                                   None, bf16_bits(0.02 * rng.normal(size=(fin, fout))), None)
+    assert out.reshape(ishape[:-1] + (out.shape[-1],)).shape == oshape
+
+
+def make_linear_case(M=64, K=96, N=80, seed=0):
+    rng = np.random.default_rng(seed)
+    x = bf16_bits(rng.normal(size=(M, K)))
+    g = bf16_bits(1 + 0.1 * rng.normal(size=K))
+    b = bf16_bits(0.1 * rng.normal(size=K))
+    w = bf16_bits(0.02 * rng.normal(size=(N, K)))
+    bias = bf16_bits(0.1 * rng.normal(size=N))
+    dy = bf16_bits(1e-3 * rng.normal(size=(M, N)))
+    return x, g, b, w, bias, dy
+
+
+def torch_linear_reference(x, g, b, w, bias, dy, eps):
+    f = lambda bits: torch.from_numpy(oracle.bf16_to_f64(bits)).requires_grad_()
+    xt, gt, bt, wt, biast = f(x), f(g), f(b), f(w), f(bias)
+    y = F.layer_norm(xt, (xt.shape[1],), gt, bt, eps)
+    out = y @ wt.T + biast
+    out.backward(torch.from_numpy(oracle.bf16_to_f64(dy)))
+    return out.detach().numpy(), xt.grad.numpy(), gt.grad.numpy(), bt.grad.numpy(), \
+        wt.grad.numpy(), biast.grad.numpy()
+
+
+def rel_rows(a, ref):
+    """max |a - ref| per row over the row's L2 norm (the GEMM parity measure)."""
+    return (np.abs(a - ref).max(axis=1) / np.linalg.norm(ref, axis=1)).max()
+
+
+@pytest.mark.parametrize("fmt", [oracle.FORMAT_HYBRID, oracle.FORMAT_E4M3])
+def test_ln_linear_chain_tracks_unquantised_autograd(fmt):
+    """After a few steps (so the delayed scales are set), the FP8 chain stays
+    within the FP8 rounding error of the float64 autograd of the same module;
+    a transposed operand, a swapped scale or a dropped term would not."""
+    r = oracle.Recipe(format=fmt)
+    mf, mb = oracle.linear_fwd_meta(r), oracle.linear_bwd_meta(r)
+    for step in range(3):
+        x, g, b, w, bias, dy = make_linear_case(seed=step)
+        oracle.scaling_update(mf)
+        oracle.scaling_update(mb)
+        out, ctx = oracle.ln_linear_fwd(r, mf, x, g, b, w, bias)
+        grads = oracle.ln_linear_bwd(r, mf, mb, dy, ctx, x, g)
+    ref_out, ref_dx, ref_dg, ref_db, ref_dw, ref_dbias = torch_linear_reference(
+        x, g, b, w, bias, dy, r.eps64)
+    # E4M3 relative rounding <= 2^-4 per operand; sums of K terms average it down
+    assert rel_rows(out, ref_out) < 0.05
+    gtol = 0.08 if fmt == oracle.FORMAT_HYBRID else 0.05   # E5M2 rounding <= 2^-3
+    assert rel_rows(grads["dx"], ref_dx) < gtol
+    assert rel_rows(grads["dw"], ref_dw) < gtol
+    assert np.linalg.norm(grads["dgamma"] - ref_dg) / np.linalg.norm(ref_dg) < gtol
+    assert np.linalg.norm(grads["dbeta"] - ref_db) / np.linalg.norm(ref_db) < gtol
+    np.testing.assert_allclose(grads["dbias"], ref_dbias, rtol=1e-12, atol=0)
+    # history row 0 holds this step's amaxes; the scale came from earlier steps
+    assert mf.history[0, 0] == np.float32(np.abs(ctx["y"]).max())
+    assert mf.history[0, 1] == np.float32(np.abs(oracle.bf16_to_f64(w)).max())
+    assert mb.history[0, 0] == np.float32(np.abs(oracle.bf16_to_f64(dy)).max())
+    assert mf.scale[1] == np.float32(448.0) / mf.history[1:, 1].max()
+
+
+def test_ln_mlp_chain_tracks_unquantised_autograd():
+    r = oracle.Recipe()
+    mf, mb = oracle.mlp_fwd_meta(r), oracle.mlp_bwd_meta(r)
+    M, H, Fd = 64, 64, 128
+    for step in range(3):
+        rng = np.random.default_rng(100 + step)
+        x = bf16_bits(rng.normal(size=(M, H)))
+        g = bf16_bits(1 + 0.1 * rng.normal(size=H))
+        b = bf16_bits(0.1 * rng.normal(size=H))
+        w1 = bf16_bits(0.1 * rng.normal(size=(Fd, H)))
+        b1 = bf16_bits(0.1 * rng.normal(size=Fd))
+        w2 = bf16_bits(0.1 * rng.normal(size=(H, Fd)))
+        b2 = bf16_bits(0.1 * rng.normal(size=H))
+        dy = bf16_bits(1e-3 * rng.normal(size=(M, H)))
+        oracle.scaling_update(mf)
+        oracle.scaling_update(mb)
+        out, ctx = oracle.ln_mlp_fwd(r, mf, x, g, b, w1, b1, w2, b2)
+        grads = oracle.ln_mlp_bwd(r, mf, mb, dy, ctx, x, g)
+    f = lambda bits: torch.from_numpy(oracle.bf16_to_f64(bits)).requires_grad_()
+    xt, gt, bt, w1t, b1t, w2t, b2t = map(f, (x, g, b, w1, b1, w2, b2))
+    y = F.layer_norm(xt, (H,), gt, bt, r.eps64)
+    o = F.gelu(y @ w1t.T + b1t, approximate="tanh") @ w2t.T + b2t
+    o.backward(torch.from_numpy(oracle.bf16_to_f64(dy)))
+    assert rel_rows(out, o.detach().numpy()) < 0.05
+    assert rel_rows(grads["dx"], xt.grad.numpy()) < 0.1
+    assert rel_rows(grads["dw1"], w1t.grad.numpy()) < 0.1
+    assert rel_rows(grads["dw2"], w2t.grad.numpy()) < 0.1
+    assert np.linalg.norm(grads["db1"] - b1t.grad.numpy()) / np.linalg.norm(b1t.grad.numpy()) < 0.1
+    np.testing.assert_allclose(grads["db2"], b2t.grad.numpy(), rtol=1e-12)
+    assert mf.history[0, 2] == np.float32(np.abs(ctx["g"]).max())
