@@ -1,0 +1,387 @@
+"""Benchmark of the FP8 delayed-scaling LayerNorm path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--quick] [--no-cpu-baseline]
+
+The headline line times the standalone LayerNorm + FP8 E4M3 cast + per-tensor
+amax step on 65536 rows x 2048 (0.1 % of entries x100, input scale drifting
+1 -> 4 over 32 steps, amax history 1024): one step is the scale update plus the
+fused kernel over one of 32 resident input buffers.  `value` is GB/s of
+algorithmic traffic (2 B read + 1 B written per element, 8 B of row statistics
+per row).  Further workloads (the pages' GPT-style shapes: LayerNormLinear
+768 -> 2304 forward on 8 x 32 tokens and backward on 8 x 256 tokens,
+LayerNormMLP 768 -> 3072 -> 768 forward on 8 x 256 tokens, and the
+2048 / 8192 / 12-layer scale-up on 64 x 256 tokens, fwd + bwd) are reported in
+"workloads" with TFLOP/s against the FP8 MFMA peak.
+
+Every input is synthetic and generated on the device before timing.  The CPU
+baseline runs the oracle (numpy, float64) on a bounded sample of the headline
+workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "LayerNormLinear FP8 fwd TFLOP/s (% MFMA peak); LN+cast+amax GB/s (% HBM)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, TFLOP/s
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=32)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--quick", action="store_true", help="headline workload only")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--only", default=None, help="run one named workload")
+    return p.parse_args()
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "fp8_delayed_scaling_row_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(kernel_tag, src_names):
+    """HBM bytes per launch from a committed counter summary, if it was taken on
+    the current kernel source (else None)."""
+    path = os.path.join(PROFILE_DIR, f"{kernel_tag}_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_hash") != source_hash(*src_names):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+class Timer:
+    """HIP events on the stream the kernels run on (torch's current stream)."""
+
+    def __init__(self, torch):
+        self.t = torch
+        self.pairs = []
+
+    def start(self):
+        e = self.t.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def stop(self, s):
+        e = self.t.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs.append((s, e))
+
+    def mean_ms(self):
+        self.t.cuda.synchronize()
+        if not self.pairs:
+            return float("nan")
+        return sum(a.elapsed_time(b) for a, b in self.pairs) / len(self.pairs)
+
+
+# ---- headline: LN + cast + amax ----------------------------------------------
+
+def bench_ln_cast(torch, ops, inputs, steps, warmup):
+    rows, hidden, n_buf = 65536, 2048, 32
+    recipe = ops.Recipe(format=ops.FORMAT_E4M3, amax_history_len=1024)
+    wl = "ln_cast_amax_65536x2048"
+    xs = [inputs.spiky_normal_bf16((rows, hidden), inputs.seed_for(wl, "x", s),
+                                   drift=inputs.drift_factor(s, n_buf), device="cuda")
+          for s in range(n_buf)]
+    g, b = inputs.layernorm_params(hidden, wl, device="cuda")
+    meta = ops.Meta(recipe, 1, ops.META_FORWARD)
+    out = torch.empty((rows, hidden), dtype=torch.uint8, device="cuda")
+    mean = torch.empty(rows, dtype=torch.float32, device="cuda")
+    rstd = torch.empty(rows, dtype=torch.float32, device="cuda")
+    scale = meta.scale[0:1]
+    amax = meta.amax_ptr(0)
+
+    def step(s, timer=None):
+        ops.scaling_update(recipe, meta)
+        ev = timer.start() if timer else None
+        ops.ln_cast_amax(recipe, xs[s % n_buf], g, b, ops.E4M3, scale, amax, out, None, mean, rstd)
+        if timer:
+            timer.stop(ev)
+
+    for s in range(warmup):
+        step(s)
+    torch.cuda.synchronize()
+    kt = Timer(torch)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for s in range(steps):
+        step(s, kt)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    kernel_ms = kt.mean_ms()
+    bytes_step = rows * hidden * 3 + rows * 8
+    return dict(rows=rows, hidden=hidden, ms=ms, kernel_ms=kernel_ms, bytes=bytes_step,
+                scale=float(meta.scale[0].item()))
+
+
+# ---- GEMM-bound workloads ------------------------------------------------------
+
+def gemm_kernel_ms(torch, ops, M, N, K, out_dtype, reps=20):
+    """Average duration of one fp8ln_gemm launch at this shape (HIP events)."""
+    a = torch.randint(0, 0x77, (M, K), dtype=torch.uint8, device="cuda")
+    b = torch.randint(0, 0x77, (N, K), dtype=torch.uint8, device="cuda")
+    one = torch.ones(1, dtype=torch.float32, device="cuda")
+    out = torch.empty((M, N), dtype=out_dtype, device="cuda")
+    for _ in range(3):
+        ops.gemm(a, ops.E4M3, b, ops.E4M3, one, one, out)
+    t = Timer(torch)
+    for _ in range(reps):
+        e = t.start()
+        ops.gemm(a, ops.E4M3, b, ops.E4M3, one, one, out)
+        t.stop(e)
+    return t.mean_ms()
+
+
+def bench_linear_fwd(torch, ops, inputs, steps, warmup, M=256, K=768, N=2304):
+    recipe = ops.Recipe(format=ops.FORMAT_HYBRID, amax_history_len=16)
+    wl = f"ln_linear_fwd_{M}x{K}x{N}"
+    xs = [inputs.normal_bf16((M, K), inputs.seed_for(wl, "x", s), device="cuda") for s in range(16)]
+    g, b = inputs.layernorm_params(K, wl, device="cuda")
+    w = inputs.linear_weight(N, K, wl, "w", device="cuda")
+    bias = torch.zeros(N, dtype=torch.bfloat16, device="cuda")
+    mf, _ = ops.linear_metas(recipe)
+    ctx = ops.LinearCtx(M, K, N, training=False)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+    def step(s):
+        ops.scaling_update(recipe, mf)
+        ops.ln_linear_fwd(recipe, xs[s % 16], g, b, w, bias, out, mf, ctx)
+
+    ms = _time_steps(torch, step, steps, warmup)
+    flops = 2.0 * M * N * K
+    return dict(ms=ms, flops=flops, gemm=(M, N, K, torch.bfloat16))
+
+
+def bench_linear_bwd(torch, ops, inputs, steps, warmup, M=2048, K=768, N=2304):
+    recipe = ops.Recipe(format=ops.FORMAT_HYBRID, amax_history_len=16)
+    wl = f"ln_linear_bwd_{M}x{K}x{N}"
+    x = inputs.normal_bf16((M, K), inputs.seed_for(wl, "x"), device="cuda")
+    g, b = inputs.layernorm_params(K, wl, device="cuda")
+    w = inputs.linear_weight(N, K, wl, "w", device="cuda")
+    dys = [inputs.normal_bf16((M, N), inputs.seed_for(wl, "dy", s), std=1e-3, device="cuda")
+           for s in range(4)]
+    mf, mb = ops.linear_metas(recipe)
+    ctx = ops.LinearCtx(M, K, N, training=True)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    dx = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    dgamma = torch.empty(K, device="cuda")
+    dbeta = torch.empty(K, device="cuda")
+    dw = torch.empty((N, K), device="cuda")
+    dbias = torch.empty(N, device="cuda")
+    ws = torch.empty(ops.workspace_size(ops.OP_LN_LINEAR_BWD, M, K, N), dtype=torch.uint8, device="cuda")
+    ops.scaling_update(recipe, mf)
+    ops.ln_linear_fwd(recipe, x, g, b, w, None, out, mf, ctx)
+
+    def step(s):
+        ops.scaling_update(recipe, mb)
+        ops.ln_linear_bwd(recipe, dys[s % 4], x, g, ctx, mf, mb, dx, dgamma, dbeta, dw, dbias,
+                          workspace=ws)
+
+    ms = _time_steps(torch, step, steps, warmup)
+    flops = 2 * 2.0 * M * N * K
+    return dict(ms=ms, flops=flops, gemm=(N, K, M, torch.float32))
+
+
+def bench_mlp_fwd(torch, ops, inputs, steps, warmup, M=2048, H=768, F=3072):
+    recipe = ops.Recipe(format=ops.FORMAT_E4M3, amax_history_len=16)
+    wl = f"ln_mlp_fwd_{M}x{H}x{F}"
+    xs = [inputs.normal_bf16((M, H), inputs.seed_for(wl, "x", s), device="cuda") for s in range(4)]
+    g, b = inputs.layernorm_params(H, wl, device="cuda")
+    w1 = inputs.linear_weight(F, H, wl, "w1", device="cuda")
+    w2 = inputs.linear_weight(H, F, wl, "w2", device="cuda")
+    mf, _ = ops.mlp_metas(recipe)
+    ctx = ops.MlpCtx(M, H, F, training=False)
+    out = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+
+    def step(s):
+        ops.scaling_update(recipe, mf)
+        ops.ln_mlp_fwd(recipe, xs[s % 4], g, b, w1, None, w2, None, out, mf, ctx)
+
+    ms = _time_steps(torch, step, steps, warmup)
+    flops = 2 * 2.0 * M * H * F
+    return dict(ms=ms, flops=flops, gemm=(M, F, H, torch.bfloat16))
+
+
+def bench_mlp_stack(torch, ops, inputs, steps, warmup, fmt, M=16384, H=2048, F=8192, layers=12):
+    recipe = ops.Recipe(format=fmt, amax_history_len=1024)
+    wl = f"ln_mlp_x{layers}_{M}x{H}x{F}"
+    x0 = inputs.normal_bf16((M, H), inputs.seed_for(wl, "x"), device="cuda")
+    dy = inputs.normal_bf16((M, H), inputs.seed_for(wl, "dy"), std=1e-3, device="cuda")
+    L = []
+    for l in range(layers):
+        g, b = inputs.layernorm_params(H, f"{wl}/{l}", device="cuda")
+        w1 = inputs.linear_weight(F, H, f"{wl}/{l}", "w1", device="cuda")
+        w2 = inputs.linear_weight(H, F, f"{wl}/{l}", "w2", device="cuda")
+        mf, mb = ops.mlp_metas(recipe)
+        L.append(dict(g=g, b=b, w1=w1, w2=w2, mf=mf, mb=mb, ctx=ops.MlpCtx(M, H, F),
+                      out=torch.empty((M, H), dtype=torch.bfloat16, device="cuda"),
+                      dw1=torch.empty((F, H), device="cuda"), db1=torch.empty(F, device="cuda"),
+                      dw2=torch.empty((H, F), device="cuda"), db2=torch.empty(H, device="cuda"),
+                      dg=torch.empty(H, device="cuda"), dbt=torch.empty(H, device="cuda")))
+    dxs = [torch.empty((M, H), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    ws = torch.empty(ops.workspace_size(ops.OP_LN_MLP_BWD, M, H, F), dtype=torch.uint8, device="cuda")
+
+    def step(s):
+        x = x0
+        for d in L:
+            ops.scaling_update(recipe, d["mf"])
+            ops.ln_mlp_fwd(recipe, x, d["g"], d["b"], d["w1"], None, d["w2"], None, d["out"],
+                           d["mf"], d["ctx"])
+            x = d["out"]
+        grad = dy
+        for i, d in enumerate(reversed(L)):
+            xin = x0 if i == layers - 1 else L[layers - 2 - i]["out"]
+            dx = dxs[i % 2]
+            ops.scaling_update(recipe, d["mb"])
+            ops.ln_mlp_bwd(recipe, grad, xin, d["g"], d["ctx"], d["mf"], d["mb"], dx, d["dg"],
+                           d["dbt"], d["dw1"], d["db1"], d["dw2"], d["db2"], workspace=ws)
+            grad = dx
+
+    ms = _time_steps(torch, step, steps, warmup)
+    flops = layers * 6 * 2.0 * M * H * F
+    return dict(ms=ms, flops=flops, gemm=(M, F, H, torch.float32))
+
+
+def _time_steps(torch, step, steps, warmup):
+    for s in range(warmup):
+        step(s)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for s in range(steps):
+        step(s)
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+# ---- CPU baseline ----------------------------------------------------------------
+
+def cpu_baseline(inputs, budget_s=12.0):
+    """The oracle's LayerNorm + cast + amax on sampled 2048-row blocks of the
+    headline workload, repeated until budget_s of CPU time has passed."""
+    import numpy as np
+    import oracle
+    from fp8_delayed_scaling_row_amd.inputs import spiky_normal_bf16, seed_for
+    rows, hidden = 2048, 2048
+    x = spiky_normal_bf16((rows, hidden), seed_for("cpu-baseline", "x"), drift=2.0)
+    g, b = inputs.layernorm_params(hidden, "cpu-baseline")
+    bits = lambda t: t.view(__import__("torch").int16).numpy().view(np.uint16)
+    xb, gb, bb = bits(x), bits(g), bits(b)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.ln_cast_amax(xb, gb, bb, float(np.float32(1e-5)), np.float32(7.0), oracle.E4M3)
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    byts = n * (rows * hidden * 3 + rows * 8)
+    return dict(value=byts / dt / 1e9, unit="GB/s", cores=1, kind="oracle",
+                sample=f"{n} x LayerNorm+cast+amax of a 2048 x 2048 bf16 block "
+                       f"({dt:.1f} s, numpy float64, single thread)")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
+              "design is described, not built.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from fp8_delayed_scaling_row_amd import inputs, ops
+    ok, why = ops.check_support(0)
+    if not ok:
+        print(f"device 0 unsupported: {why}", file=sys.stderr)
+        sys.exit(1)
+
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    workloads = []
+    head = None
+    if args.only in (None, "ln_cast"):
+        log("ln_cast_amax 65536x2048 ...")
+        head = bench_ln_cast(torch, ops, inputs, args.steps, args.warmup)
+        torch.cuda.empty_cache()
+    if not args.quick:
+        runs = [
+            ("ln_linear_fwd", "LayerNormLinear fwd 8x32 tokens, 768->2304, HYBRID, history 16",
+             lambda: bench_linear_fwd(torch, ops, inputs, 200, 20)),
+            ("ln_linear_bwd", "LayerNormLinear bwd 2048 tokens, 768->2304, HYBRID (E5M2 grads)",
+             lambda: bench_linear_bwd(torch, ops, inputs, 100, 10)),
+            ("ln_mlp_fwd", "LayerNormMLP fwd 2048 tokens, 768->3072->768, E4M3, history 16",
+             lambda: bench_mlp_fwd(torch, ops, inputs, 100, 10)),
+            ("ln_mlp_x12_hybrid", "LayerNormMLP x12 fwd+bwd, 16384 tokens, 2048->8192->2048, HYBRID, history 1024",
+             lambda: bench_mlp_stack(torch, ops, inputs, 5, 2, ops.FORMAT_HYBRID)),
+            ("ln_mlp_x12_e4m3", "LayerNormMLP x12 fwd+bwd, 16384 tokens, 2048->8192->2048, E4M3, history 1024",
+             lambda: bench_mlp_stack(torch, ops, inputs, 5, 2, ops.FORMAT_E4M3)),
+        ]
+        for name, desc, fn in runs:
+            if args.only not in (None, name):
+                continue
+            log(f"{name} ...")
+            r = fn()
+            M, N, K, odt = r["gemm"]
+            gk_ms = gemm_kernel_ms(torch, ops, M, N, K, odt)
+            gflops = 2.0 * M * N * K
+            tflops = r["flops"] / (r["ms"] * 1e-3) / 1e12
+            workloads.append(dict(
+                workload=name, description=desc, ms_per_step=round(r["ms"], 5),
+                value=round(tflops, 2), unit="TFLOP/s",
+                frac_of_fp8_peak=round(tflops / FP8_PEAK_TFLOPS, 4),
+                roofline=dict(bound="mfma", kernel=f"fp8 gemm {M}x{N}x{K}",
+                              achieved=round(gflops / (gk_ms * 1e-3) / 1e12, 2),
+                              peak=FP8_PEAK_TFLOPS, unit="TFLOP/s",
+                              frac=round(gflops / (gk_ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
+                              kernel_ms=round(gk_ms, 5))))
+            torch.cuda.empty_cache()
+
+    line = dict(metric=METRIC, n_gpus=1, steps=args.steps, warmup=args.warmup,
+                higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f32",
+                data="synthetic")
+    if head:
+        gbs = head["bytes"] / (head["ms"] * 1e-3) / 1e9
+        kgbs = head["bytes"] / (head["kernel_ms"] * 1e-3) / 1e9
+        traffic = counter_traffic("ln_cast_amax_65536x2048", ["layernorm.hip", "device_common.hpp"])
+        line.update(value=round(gbs, 2), unit="GB/s", ms_per_step=round(head["ms"], 5),
+                    config=dict(workload="ln_cast_amax_65536x2048", rows=head["rows"],
+                                hidden=head["hidden"], out_dtype="fp8_e4m3",
+                                amax_history_len=1024, input="N(0,1) x drift 1->4, 0.1% x100",
+                                buffers=32),
+                    roofline=dict(bound="hbm", kernel="ln_cast_amax",
+                                  achieved=round(kgbs, 2), peak=HBM_PEAK_GBS, unit="GB/s",
+                                  frac=round(kgbs / HBM_PEAK_GBS, 4), traffic=traffic,
+                                  kernel_ms=round(head["kernel_ms"], 5),
+                                  bytes_per_launch=head["bytes"]))
+    line["workloads"] = workloads
+    if not args.no_cpu_baseline and head:
+        log("cpu baseline (oracle) ...")
+        line["cpu_baseline"] = cpu_baseline(inputs)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,654 @@
+// C-ABI entry points: argument validation, workspace carving and the order of
+// kernel launches for each fused module step.  Nothing here computes; every step
+// of the path runs in the gfx950 kernels behind launchers.hpp.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/fp8ln.h"
+#include "launchers.hpp"
+
+using namespace fp8ln;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return FP8LN_OK;
+    return fail(FP8LN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define FP8LN_TRY(expr, what)                       \
+    do {                                            \
+        int _s = hip_status((expr), (what));        \
+        if (_s != FP8LN_OK) return _s;              \
+    } while (0)
+
+// Per-device gfx950 check, cached (0 unknown, 1 yes, 2 no).
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_ok[kMaxDevices];
+
+int device_supported(int device, std::string* why) {
+    if (device < 0 || device >= kMaxDevices) {
+        if (why) *why = "device index out of range";
+        return 0;
+    }
+    int cached = g_dev_ok[device].load();
+    if (cached == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, device) != hipSuccess) {
+            if (why) *why = "hipGetDeviceProperties failed";
+            return 0;
+        }
+        cached = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_dev_ok[device].store(cached);
+        if (cached == 2 && why) *why = std::string("device architecture ") + prop.gcnArchName +
+                                       " is not gfx950";
+    }
+    if (cached == 2 && why && why->empty()) *why = "device architecture is not gfx950";
+    return cached == 1;
+}
+
+int check_current_device() {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+    std::string why;
+    if (!device_supported(dev, &why)) return fail(FP8LN_ERR_UNSUPPORTED, "%s", why.c_str());
+    return FP8LN_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+int check_recipe(const fp8ln_recipe* r) {
+    if (!r) return fail(FP8LN_ERR_INVALID_ARG, "recipe is NULL");
+    if (r->format < FP8LN_FORMAT_E4M3 || r->format > FP8LN_FORMAT_E5M2)
+        return fail(FP8LN_ERR_INVALID_ARG, "recipe.format %d is not E4M3/HYBRID/E5M2", r->format);
+    if (r->amax_history_len < 1 || r->amax_history_len > 1024)
+        return fail(FP8LN_ERR_INVALID_ARG, "recipe.amax_history_len %d outside 1..1024",
+                    r->amax_history_len);
+    if (r->margin < 0 || r->margin > 64)
+        return fail(FP8LN_ERR_INVALID_ARG, "recipe.margin %d outside 0..64", r->margin);
+    if (!(std::isfinite(r->ln_eps) && r->ln_eps > 0.0f))
+        return fail(FP8LN_ERR_INVALID_ARG, "recipe.ln_eps must be finite and > 0");
+    return FP8LN_OK;
+}
+
+int check_meta(const fp8ln_meta* m, int min_slots, int kind, const char* name) {
+    if (!m) return fail(FP8LN_ERR_INVALID_ARG, "%s meta is NULL", name);
+    if (!m->amax_history || !m->scale || !m->scale_inv)
+        return fail(FP8LN_ERR_INVALID_ARG, "%s meta has a NULL buffer", name);
+    if (m->n_slots < 1 || m->n_slots > 8)
+        return fail(FP8LN_ERR_INVALID_ARG, "%s meta n_slots %d outside 1..8", name, m->n_slots);
+    if (m->n_slots < min_slots)
+        return fail(FP8LN_ERR_INVALID_ARG, "%s meta needs %d slots, has %d", name, min_slots,
+                    m->n_slots);
+    if (m->kind != FP8LN_META_FORWARD && m->kind != FP8LN_META_BACKWARD)
+        return fail(FP8LN_ERR_INVALID_ARG, "%s meta kind %d invalid", name, m->kind);
+    if (kind >= 0 && m->kind != kind)
+        return fail(FP8LN_ERR_INVALID_ARG, "%s meta has the wrong kind", name);
+    return FP8LN_OK;
+}
+
+// FP8 encoding of the tensors a state block covers.
+int meta_fp8(const fp8ln_recipe* r, int kind) {
+    if (r->format == FP8LN_FORMAT_E4M3) return kE4M3;
+    if (r->format == FP8LN_FORMAT_E5M2) return kE5M2;
+    return kind == FP8LN_META_FORWARD ? kE4M3 : kE5M2;   // HYBRID
+}
+
+float fp8_max_of(int fp8) { return fp8 == kE4M3 ? 448.0f : 57344.0f; }
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Carves consecutive 256-byte aligned pieces out of a workspace.
+struct Carver {
+    uint8_t* base;
+    size_t used = 0;
+    void* take(size_t bytes) {
+        void* p = base ? base + used : nullptr;
+        used += align_up(bytes);
+        return p;
+    }
+};
+
+#define REQUIRE(cond, ...)                                      \
+    do {                                                        \
+        if (!(cond)) return fail(FP8LN_ERR_INVALID_ARG, __VA_ARGS__); \
+    } while (0)
+
+#define REQUIRE_PTR(p) REQUIRE((p) != nullptr, "%s is NULL", #p)
+#define REQUIRE_ALIGNED(p) REQUIRE(aligned16(p), "%s is not 16-byte aligned", #p)
+
+struct LinearWs {
+    uint8_t* dy_q;
+    uint8_t* dy_qt;
+    float* dln;
+    void* cast_ws;
+    void* ln_ws;
+    size_t bytes;
+};
+
+LinearWs linear_ws(void* base, int64_t M, int64_t K, int64_t N) {
+    Carver c{(uint8_t*)base};
+    LinearWs w;
+    w.dy_q = (uint8_t*)c.take((size_t)(M * N));
+    w.dy_qt = (uint8_t*)c.take((size_t)(M * N));
+    w.dln = (float*)c.take((size_t)(M * K) * sizeof(float));
+    w.cast_ws = c.take(cast_workspace(M, N));
+    w.ln_ws = c.take(ln_bwd_workspace(M, (int)K));
+    w.bytes = c.used;
+    return w;
+}
+
+struct MlpWs {
+    uint8_t* dy_q;
+    uint8_t* dy_qt;
+    float* dh;
+    uint8_t* dh_q;
+    uint8_t* dh_qt;
+    float* dln;
+    void* cast_ws;
+    void* ln_ws;
+    size_t bytes;
+};
+
+MlpWs mlp_ws(void* base, int64_t M, int64_t H, int64_t F) {
+    Carver c{(uint8_t*)base};
+    MlpWs w;
+    w.dy_q = (uint8_t*)c.take((size_t)(M * H));
+    w.dy_qt = (uint8_t*)c.take((size_t)(M * H));
+    w.dh = (float*)c.take((size_t)(M * F) * sizeof(float));
+    w.dh_q = (uint8_t*)c.take((size_t)(M * F));
+    w.dh_qt = (uint8_t*)c.take((size_t)(M * F));
+    w.dln = (float*)c.take((size_t)(M * H) * sizeof(float));
+    const size_t cw = std::max(cast_workspace(M, H), cast_workspace(M, F));
+    w.cast_ws = c.take(cw);
+    w.ln_ws = c.take(ln_bwd_workspace(M, (int)H));
+    w.bytes = c.used;
+    return w;
+}
+
+GemmParams gemm_params(int64_t M, int64_t N, int64_t K, const uint8_t* A, int afmt,
+                       const uint8_t* B, int bfmt, const float* sa, const float* sb,
+                       int epilogue) {
+    GemmParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.M = M; p.N = N; p.K = K;
+    p.A = A; p.B = B;
+    p.a_fp8 = afmt; p.b_fp8 = bfmt;
+    p.sinv_a = sa; p.sinv_b = sb;
+    p.epilogue = epilogue;
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fp8ln_status_string(int status) {
+    switch (status) {
+        case FP8LN_OK: return "ok";
+        case FP8LN_ERR_INVALID_ARG: return "invalid argument";
+        case FP8LN_ERR_UNSUPPORTED: return "unsupported";
+        case FP8LN_ERR_HIP: return "HIP error";
+        default: return "unknown status";
+    }
+}
+
+const char* fp8ln_last_error(void) { return g_last_error.c_str(); }
+
+int fp8ln_check_support(int device, char* reason, size_t reason_cap) {
+    int count = 0;
+    hipError_t e = hipGetDeviceCount(&count);
+    std::string why;
+    int ok = 0;
+    if (e != hipSuccess) why = std::string("no HIP device: ") + hipGetErrorString(e);
+    else if (device < 0 || device >= count) why = "device index out of range";
+    else ok = device_supported(device, &why);
+    if (reason && reason_cap) {
+        std::snprintf(reason, reason_cap, "%s", ok ? "" : why.c_str());
+    }
+    return ok;
+}
+
+size_t fp8ln_workspace_size(int32_t op, int64_t a, int64_t b, int64_t c) {
+    if (a < 0 || b <= 0) return 0;
+    switch (op) {
+        case FP8LN_OP_CAST_AMAX: return cast_workspace(a, b);
+        case FP8LN_OP_LAYERNORM_BWD: return ln_bwd_workspace(a, (int)b);
+        case FP8LN_OP_LN_LINEAR_BWD: return c > 0 ? linear_ws(nullptr, a, b, c).bytes : 0;
+        case FP8LN_OP_LN_MLP_BWD: return c > 0 ? mlp_ws(nullptr, a, b, c).bytes : 0;
+        default: return 0;
+    }
+}
+
+int fp8ln_meta_init(const fp8ln_recipe* recipe, const fp8ln_meta* meta, void* stream) {
+    int s = check_recipe(recipe);
+    if (s) return s;
+    if ((s = check_meta(meta, 1, -1, "state"))) return s;
+    if ((s = check_current_device())) return s;
+    FP8LN_TRY(launch_meta_init(meta->amax_history, meta->scale, meta->scale_inv,
+                               recipe->amax_history_len, meta->n_slots, as_stream(stream)),
+              "meta_init launch");
+    return FP8LN_OK;
+}
+
+int fp8ln_scaling_update(const fp8ln_recipe* recipe, const fp8ln_meta* meta, void* stream) {
+    int s = check_recipe(recipe);
+    if (s) return s;
+    if ((s = check_meta(meta, 1, -1, "state"))) return s;
+    if ((s = check_current_device())) return s;
+    const float fmax = fp8_max_of(meta_fp8(recipe, meta->kind));
+    FP8LN_TRY(launch_scaling_update(meta->amax_history, meta->scale, meta->scale_inv,
+                                    recipe->amax_history_len, meta->n_slots, recipe->margin, fmax,
+                                    as_stream(stream)),
+              "scaling_update launch");
+    return FP8LN_OK;
+}
+
+int fp8ln_ln_cast_amax(const fp8ln_recipe* recipe, int64_t rows, int64_t hidden,
+                       int32_t params_dtype, const void* x, const void* gamma, const void* beta,
+                       int32_t fp8_dtype, const float* scale, float* amax, uint8_t* out,
+                       uint8_t* out_t, float* mean, float* rstd, void* stream) {
+    int s = check_recipe(recipe);
+    if (s) return s;
+    REQUIRE(rows >= 0, "rows %lld < 0", (long long)rows);
+    if (params_dtype != FP8LN_DTYPE_BF16)
+        return fail(FP8LN_ERR_UNSUPPORTED, "params_dtype %d: only bf16 is supported", params_dtype);
+    REQUIRE(fp8_dtype == FP8LN_E4M3 || fp8_dtype == FP8LN_E5M2, "fp8_dtype %d invalid", fp8_dtype);
+    if (hidden <= 0 || hidden % 8 != 0 || hidden > 8192)
+        return fail(FP8LN_ERR_UNSUPPORTED, "hidden %lld must be a multiple of 8 in 8..8192",
+                    (long long)hidden);
+    if (out_t && (rows % 16 != 0 || hidden % 16 != 0))
+        return fail(FP8LN_ERR_UNSUPPORTED, "a transposed output needs rows and hidden % 16 == 0");
+    REQUIRE_PTR(gamma); REQUIRE_PTR(beta); REQUIRE_PTR(scale); REQUIRE_PTR(amax);
+    REQUIRE_ALIGNED(gamma); REQUIRE_ALIGNED(beta);
+    if (rows > 0) {
+        REQUIRE_PTR(x); REQUIRE_PTR(out);
+        REQUIRE_ALIGNED(x); REQUIRE_ALIGNED(out);
+        if (out_t) REQUIRE_ALIGNED(out_t);
+    }
+    if ((s = check_current_device())) return s;
+    if (rows == 0) return FP8LN_OK;
+    hipStream_t st = as_stream(stream);
+    FP8LN_TRY(launch_ln_cast_amax(rows, (int)hidden, x, gamma, beta, recipe->ln_eps, fp8_dtype,
+                                  scale, amax, out, mean, rstd, st),
+              "ln_cast_amax launch");
+    if (out_t) FP8LN_TRY(launch_transpose_u8(rows, hidden, out, out_t, st), "transpose launch");
+    return FP8LN_OK;
+}
+
+int fp8ln_cast_amax(int64_t rows, int64_t cols, int32_t in_dtype, const void* in,
+                    int32_t fp8_dtype, const float* scale, float* amax, uint8_t* out,
+                    uint8_t* out_t, float* colsum, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+    REQUIRE(rows >= 0 && cols >= 0, "negative size");
+    REQUIRE(in_dtype == FP8LN_DTYPE_BF16 || in_dtype == FP8LN_DTYPE_F32, "in_dtype %d invalid",
+            in_dtype);
+    REQUIRE(fp8_dtype == FP8LN_E4M3 || fp8_dtype == FP8LN_E5M2, "fp8_dtype %d invalid", fp8_dtype);
+    if (cols % 16 != 0) return fail(FP8LN_ERR_UNSUPPORTED, "cols %lld %% 16 != 0", (long long)cols);
+    if (out_t && rows % 16 != 0)
+        return fail(FP8LN_ERR_UNSUPPORTED, "a transposed output needs rows %% 16 == 0");
+    REQUIRE_PTR(scale); REQUIRE_PTR(amax);
+    if (rows > 0 && cols > 0) {
+        REQUIRE_PTR(in); REQUIRE_PTR(out);
+        REQUIRE_ALIGNED(in); REQUIRE_ALIGNED(out);
+        if (out_t) REQUIRE_ALIGNED(out_t);
+        if (colsum) {
+            REQUIRE(workspace && workspace_bytes >= cast_workspace(rows, cols),
+                    "column sums need %zu bytes of workspace", cast_workspace(rows, cols));
+        }
+    }
+    int s = check_current_device();
+    if (s) return s;
+    FP8LN_TRY(launch_cast_amax(rows, cols, in_dtype == FP8LN_DTYPE_F32, in, fp8_dtype, scale, amax,
+                               out, out_t, colsum, workspace, as_stream(stream)),
+              "cast_amax launch");
+    return FP8LN_OK;
+}
+
+int fp8ln_encode_range(uint32_t start, int64_t count, int32_t fp8_dtype, uint8_t* out,
+                       void* stream) {
+    REQUIRE(count >= 0 && count <= (int64_t(1) << 32), "count %lld outside 0..2^32",
+            (long long)count);
+    REQUIRE(fp8_dtype == FP8LN_E4M3 || fp8_dtype == FP8LN_E5M2, "fp8_dtype %d invalid", fp8_dtype);
+    if (count > 0) { REQUIRE_PTR(out); REQUIRE((reinterpret_cast<uintptr_t>(out) & 3) == 0, "out is not 4-byte aligned"); }
+    int s = check_current_device();
+    if (s) return s;
+    FP8LN_TRY(launch_encode_range(start, count, fp8_dtype, out, as_stream(stream)),
+              "encode_range launch");
+    return FP8LN_OK;
+}
+
+int fp8ln_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* A, int32_t a_dtype,
+               const uint8_t* B, int32_t b_dtype, const float* sinv_a, const float* sinv_b,
+               const void* bias, int32_t out_dtype, void* out, void* stream) {
+    REQUIRE(M >= 0 && N >= 0 && K >= 0, "negative size");
+    REQUIRE(a_dtype == FP8LN_E4M3 || a_dtype == FP8LN_E5M2, "a_dtype %d invalid", a_dtype);
+    REQUIRE(b_dtype == FP8LN_E4M3 || b_dtype == FP8LN_E5M2, "b_dtype %d invalid", b_dtype);
+    REQUIRE(out_dtype == FP8LN_DTYPE_BF16 || out_dtype == FP8LN_DTYPE_F32, "out_dtype %d invalid",
+            out_dtype);
+    if (N % 16 != 0 || K % 16 != 0)
+        return fail(FP8LN_ERR_UNSUPPORTED, "N and K must be multiples of 16 (N=%lld K=%lld)",
+                    (long long)N, (long long)K);
+    REQUIRE_PTR(sinv_a); REQUIRE_PTR(sinv_b);
+    if (M > 0 && N > 0) {
+        REQUIRE_PTR(out); REQUIRE_ALIGNED(out);
+        if (K > 0) { REQUIRE_PTR(A); REQUIRE_PTR(B); REQUIRE_ALIGNED(A); REQUIRE_ALIGNED(B); }
+        if (bias) REQUIRE_ALIGNED(bias);
+    }
+    REQUIRE(!(bias && out_dtype == FP8LN_DTYPE_F32), "bias is only applied to bf16 outputs");
+    int s = check_current_device();
+    if (s) return s;
+    GemmParams p = gemm_params(M, N, K, A, a_dtype, B, b_dtype, sinv_a, sinv_b,
+                               out_dtype == FP8LN_DTYPE_BF16 ? kEpiBf16Bias : kEpiF32);
+    p.bias = (const uint16_t*)bias;
+    p.out = out;
+    FP8LN_TRY(launch_gemm(p, as_stream(stream)), "gemm launch");
+    return FP8LN_OK;
+}
+
+int fp8ln_layernorm_bwd(int64_t rows, int64_t hidden, const float* dy, const void* x,
+                        const float* mean, const float* rstd, const void* gamma, void* dx,
+                        float* dgamma, float* dbeta, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+    REQUIRE(rows >= 0, "rows < 0");
+    if (hidden <= 0 || hidden % 8 != 0 || hidden > 4096)
+        return fail(FP8LN_ERR_UNSUPPORTED, "hidden %lld must be a multiple of 8 in 8..4096",
+                    (long long)hidden);
+    REQUIRE_PTR(gamma); REQUIRE_PTR(dgamma); REQUIRE_PTR(dbeta);
+    REQUIRE_ALIGNED(gamma);
+    if (rows > 0) {
+        REQUIRE_PTR(dy); REQUIRE_PTR(x); REQUIRE_PTR(mean); REQUIRE_PTR(rstd); REQUIRE_PTR(dx);
+        REQUIRE_ALIGNED(dy); REQUIRE_ALIGNED(x); REQUIRE_ALIGNED(dx);
+    }
+    REQUIRE(workspace && workspace_bytes >= ln_bwd_workspace(rows, (int)hidden),
+            "layernorm_bwd needs %zu bytes of workspace", ln_bwd_workspace(rows, (int)hidden));
+    int s = check_current_device();
+    if (s) return s;
+    FP8LN_TRY(launch_ln_bwd(rows, (int)hidden, dy, x, mean, rstd, gamma, dx, dgamma, dbeta,
+                            workspace, as_stream(stream)),
+              "layernorm_bwd launch");
+    return FP8LN_OK;
+}
+
+int fp8ln_ln_linear_fwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_features,
+                        int64_t out_features, int32_t params_dtype, const void* x,
+                        const void* gamma, const void* beta, const void* weight,
+                        const void* bias, void* out, const fp8ln_meta* fwd,
+                        const fp8ln_linear_ctx* ctx, void* stream) {
+    int s = check_recipe(recipe);
+    if (s) return s;
+    const int64_t M = tokens, K = in_features, N = out_features;
+    REQUIRE(M >= 0, "tokens < 0");
+    if (params_dtype != FP8LN_DTYPE_BF16)
+        return fail(FP8LN_ERR_UNSUPPORTED, "params_dtype %d: only bf16 is supported", params_dtype);
+    if (K <= 0 || K % 16 != 0 || K > 8192)
+        return fail(FP8LN_ERR_UNSUPPORTED, "in_features %lld must be a multiple of 16 in 16..8192",
+                    (long long)K);
+    if (N <= 0 || N % 16 != 0)
+        return fail(FP8LN_ERR_UNSUPPORTED, "out_features %lld must be a positive multiple of 16",
+                    (long long)N);
+    if ((s = check_meta(fwd, 2, FP8LN_META_FORWARD, "forward"))) return s;
+    REQUIRE_PTR(ctx);
+    REQUIRE(ctx->ln_q && ctx->w_q, "ctx.ln_q and ctx.w_q are required");
+    if (ctx->ln_qt && M % 16 != 0)
+        return fail(FP8LN_ERR_UNSUPPORTED, "ctx.ln_qt needs tokens %% 16 == 0");
+    REQUIRE_PTR(gamma); REQUIRE_PTR(beta); REQUIRE_PTR(weight);
+    REQUIRE_ALIGNED(gamma); REQUIRE_ALIGNED(beta); REQUIRE_ALIGNED(weight);
+    REQUIRE_ALIGNED(ctx->w_q);
+    if (ctx->w_qt) REQUIRE_ALIGNED(ctx->w_qt);
+    if (bias) REQUIRE_ALIGNED(bias);
+    if (M > 0) {
+        REQUIRE_PTR(x); REQUIRE_PTR(out);
+        REQUIRE_ALIGNED(x); REQUIRE_ALIGNED(out); REQUIRE_ALIGNED(ctx->ln_q);
+        if (ctx->ln_qt) REQUIRE_ALIGNED(ctx->ln_qt);
+    }
+    if ((s = check_current_device())) return s;
+    hipStream_t st = as_stream(stream);
+    const int f = meta_fp8(recipe, FP8LN_META_FORWARD);
+    float* hist = fwd->amax_history;
+    if (M > 0) {
+        FP8LN_TRY(launch_ln_cast_amax(M, (int)K, x, gamma, beta, recipe->ln_eps, f, fwd->scale + 0,
+                                      hist + 0, ctx->ln_q, ctx->mean, ctx->rstd, st),
+                  "ln_cast_amax launch");
+        if (ctx->ln_qt) FP8LN_TRY(launch_transpose_u8(M, K, ctx->ln_q, ctx->ln_qt, st), "transpose");
+    }
+    FP8LN_TRY(launch_cast_amax(N, K, false, weight, f, fwd->scale + 1, hist + 1, ctx->w_q,
+                               ctx->w_qt, nullptr, nullptr, st),
+              "weight cast launch");
+    GemmParams p = gemm_params(M, N, K, ctx->ln_q, f, ctx->w_q, f, fwd->scale_inv + 0,
+                               fwd->scale_inv + 1, kEpiBf16Bias);
+    p.bias = (const uint16_t*)bias;
+    p.out = out;
+    FP8LN_TRY(launch_gemm(p, st), "gemm launch");
+    return FP8LN_OK;
+}
+
+int fp8ln_ln_linear_bwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_features,
+                        int64_t out_features, int32_t params_dtype, const void* dy,
+                        const void* x, const void* gamma, const fp8ln_linear_ctx* ctx,
+                        const fp8ln_meta* fwd, const fp8ln_meta* bwd, void* dx,
+                        float* dgamma, float* dbeta, float* dweight, float* dbias,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    int s = check_recipe(recipe);
+    if (s) return s;
+    const int64_t M = tokens, K = in_features, N = out_features;
+    if (params_dtype != FP8LN_DTYPE_BF16)
+        return fail(FP8LN_ERR_UNSUPPORTED, "params_dtype %d: only bf16 is supported", params_dtype);
+    if (M < 0 || M % 16 != 0)
+        return fail(FP8LN_ERR_UNSUPPORTED, "tokens %lld must be a multiple of 16", (long long)M);
+    if (K <= 0 || K % 16 != 0 || K > 4096)
+        return fail(FP8LN_ERR_UNSUPPORTED, "in_features %lld must be a multiple of 16 in 16..4096",
+                    (long long)K);
+    if (N <= 0 || N % 16 != 0)
+        return fail(FP8LN_ERR_UNSUPPORTED, "out_features %lld must be a positive multiple of 16",
+                    (long long)N);
+    if ((s = check_meta(fwd, 2, FP8LN_META_FORWARD, "forward"))) return s;
+    if ((s = check_meta(bwd, 1, FP8LN_META_BACKWARD, "backward"))) return s;
+    REQUIRE_PTR(ctx);
+    REQUIRE(ctx->ln_qt && ctx->w_qt && ctx->mean && ctx->rstd,
+            "ctx needs ln_qt, w_qt, mean and rstd from a training forward");
+    REQUIRE_PTR(gamma); REQUIRE_PTR(dgamma); REQUIRE_PTR(dbeta); REQUIRE_PTR(dweight);
+    REQUIRE_ALIGNED(gamma); REQUIRE_ALIGNED(dweight); REQUIRE_ALIGNED(ctx->w_qt);
+    if (M > 0) {
+        REQUIRE_PTR(dy); REQUIRE_PTR(x); REQUIRE_PTR(dx);
+        REQUIRE_ALIGNED(dy); REQUIRE_ALIGNED(x); REQUIRE_ALIGNED(dx); REQUIRE_ALIGNED(ctx->ln_qt);
+    }
+    const LinearWs need = linear_ws(nullptr, M, K, N);
+    REQUIRE(workspace && workspace_bytes >= need.bytes, "ln_linear_bwd needs %zu bytes of workspace",
+            need.bytes);
+    REQUIRE_ALIGNED(workspace);
+    if ((s = check_current_device())) return s;
+    hipStream_t st = as_stream(stream);
+    const LinearWs w = linear_ws(workspace, M, K, N);
+    const int ff = meta_fp8(recipe, FP8LN_META_FORWARD);
+    const int bf = meta_fp8(recipe, FP8LN_META_BACKWARD);
+
+    FP8LN_TRY(launch_cast_amax(M, N, false, dy, bf, bwd->scale + 0, bwd->amax_history + 0, w.dy_q,
+                               w.dy_qt, dbias, w.cast_ws, st),
+              "grad cast launch");
+    // dgrad: dLN[M][K] = dy_q[M][N] . (w_qt[K][N])^T
+    GemmParams dg = gemm_params(M, K, N, w.dy_q, bf, ctx->w_qt, ff, bwd->scale_inv + 0,
+                                fwd->scale_inv + 1, kEpiF32);
+    dg.out = w.dln;
+    FP8LN_TRY(launch_gemm(dg, st), "dgrad launch");
+    // wgrad: dW[N][K] = dy_qt[N][M] . (ln_qt[K][M])^T
+    GemmParams wg = gemm_params(N, K, M, w.dy_qt, bf, ctx->ln_qt, ff, bwd->scale_inv + 0,
+                                fwd->scale_inv + 0, kEpiF32);
+    wg.out = dweight;
+    FP8LN_TRY(launch_gemm(wg, st), "wgrad launch");
+    FP8LN_TRY(launch_ln_bwd(M, (int)K, w.dln, x, ctx->mean, ctx->rstd, gamma, dx, dgamma, dbeta,
+                            w.ln_ws, st),
+              "layernorm_bwd launch");
+    return FP8LN_OK;
+}
+
+int fp8ln_ln_mlp_fwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t hidden, int64_t ffn,
+                     int32_t params_dtype, const void* x, const void* gamma, const void* beta,
+                     const void* w1, const void* b1, const void* w2, const void* b2, void* out,
+                     const fp8ln_meta* fwd, const fp8ln_mlp_ctx* ctx, void* stream) {
+    int s = check_recipe(recipe);
+    if (s) return s;
+    const int64_t M = tokens, H = hidden, F = ffn;
+    REQUIRE(M >= 0, "tokens < 0");
+    if (params_dtype != FP8LN_DTYPE_BF16)
+        return fail(FP8LN_ERR_UNSUPPORTED, "params_dtype %d: only bf16 is supported", params_dtype);
+    if (H <= 0 || H % 16 != 0 || H > 8192)
+        return fail(FP8LN_ERR_UNSUPPORTED, "hidden %lld must be a multiple of 16 in 16..8192",
+                    (long long)H);
+    if (F <= 0 || F % 16 != 0)
+        return fail(FP8LN_ERR_UNSUPPORTED, "ffn %lld must be a positive multiple of 16",
+                    (long long)F);
+    if ((s = check_meta(fwd, 4, FP8LN_META_FORWARD, "forward"))) return s;
+    REQUIRE_PTR(ctx);
+    REQUIRE(ctx->ln_q && ctx->w1_q && ctx->w2_q && ctx->g_q,
+            "ctx.ln_q, w1_q, w2_q and g_q are required");
+    if ((ctx->ln_qt || ctx->g_qt) && M % 16 != 0)
+        return fail(FP8LN_ERR_UNSUPPORTED, "transposed activations need tokens %% 16 == 0");
+    REQUIRE_PTR(gamma); REQUIRE_PTR(beta); REQUIRE_PTR(w1); REQUIRE_PTR(w2);
+    REQUIRE_ALIGNED(gamma); REQUIRE_ALIGNED(beta); REQUIRE_ALIGNED(w1); REQUIRE_ALIGNED(w2);
+    REQUIRE_ALIGNED(ctx->w1_q); REQUIRE_ALIGNED(ctx->w2_q);
+    if (ctx->w1_qt) REQUIRE_ALIGNED(ctx->w1_qt);
+    if (ctx->w2_qt) REQUIRE_ALIGNED(ctx->w2_qt);
+    if (b1) REQUIRE_ALIGNED(b1);
+    if (b2) REQUIRE_ALIGNED(b2);
+    if (M > 0) {
+        REQUIRE_PTR(x); REQUIRE_PTR(out);
+        REQUIRE_ALIGNED(x); REQUIRE_ALIGNED(out); REQUIRE_ALIGNED(ctx->ln_q);
+        REQUIRE_ALIGNED(ctx->g_q);
+        if (ctx->ln_qt) REQUIRE_ALIGNED(ctx->ln_qt);
+        if (ctx->g_qt) REQUIRE_ALIGNED(ctx->g_qt);
+        if (ctx->h) REQUIRE_ALIGNED(ctx->h);
+    }
+    if ((s = check_current_device())) return s;
+    hipStream_t st = as_stream(stream);
+    const int f = meta_fp8(recipe, FP8LN_META_FORWARD);
+    float* hist = fwd->amax_history;
+    if (M > 0) {
+        FP8LN_TRY(launch_ln_cast_amax(M, (int)H, x, gamma, beta, recipe->ln_eps, f, fwd->scale + 0,
+                                      hist + 0, ctx->ln_q, ctx->mean, ctx->rstd, st),
+                  "ln_cast_amax launch");
+        if (ctx->ln_qt) FP8LN_TRY(launch_transpose_u8(M, H, ctx->ln_q, ctx->ln_qt, st), "transpose");
+    }
+    FP8LN_TRY(launch_cast_amax(F, H, false, w1, f, fwd->scale + 1, hist + 1, ctx->w1_q, ctx->w1_qt,
+                               nullptr, nullptr, st),
+              "fc1 weight cast launch");
+    FP8LN_TRY(launch_cast_amax(H, F, false, w2, f, fwd->scale + 3, hist + 3, ctx->w2_q, ctx->w2_qt,
+                               nullptr, nullptr, st),
+              "fc2 weight cast launch");
+    GemmParams p1 = gemm_params(M, F, H, ctx->ln_q, f, ctx->w1_q, f, fwd->scale_inv + 0,
+                                fwd->scale_inv + 1, kEpiGeluFp8);
+    p1.bias = (const uint16_t*)b1;
+    p1.h_out = ctx->h;
+    p1.q_out = ctx->g_q;
+    p1.q_out_t = ctx->g_qt;
+    p1.q_scale = fwd->scale + 2;
+    p1.q_amax = hist + 2;
+    p1.q_fp8 = f;
+    FP8LN_TRY(launch_gemm(p1, st), "fc1 launch");
+    GemmParams p2 = gemm_params(M, H, F, ctx->g_q, f, ctx->w2_q, f, fwd->scale_inv + 2,
+                                fwd->scale_inv + 3, kEpiBf16Bias);
+    p2.bias = (const uint16_t*)b2;
+    p2.out = out;
+    FP8LN_TRY(launch_gemm(p2, st), "fc2 launch");
+    return FP8LN_OK;
+}
+
+int fp8ln_ln_mlp_bwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t hidden, int64_t ffn,
+                     int32_t params_dtype, const void* dy, const void* x, const void* gamma,
+                     const fp8ln_mlp_ctx* ctx, const fp8ln_meta* fwd, const fp8ln_meta* bwd,
+                     void* dx, float* dgamma, float* dbeta, float* dw1, float* db1, float* dw2,
+                     float* db2, void* workspace, size_t workspace_bytes, void* stream) {
+    int s = check_recipe(recipe);
+    if (s) return s;
+    const int64_t M = tokens, H = hidden, F = ffn;
+    if (params_dtype != FP8LN_DTYPE_BF16)
+        return fail(FP8LN_ERR_UNSUPPORTED, "params_dtype %d: only bf16 is supported", params_dtype);
+    if (M < 0 || M % 16 != 0)
+        return fail(FP8LN_ERR_UNSUPPORTED, "tokens %lld must be a multiple of 16", (long long)M);
+    if (H <= 0 || H % 16 != 0 || H > 4096)
+        return fail(FP8LN_ERR_UNSUPPORTED, "hidden %lld must be a multiple of 16 in 16..4096",
+                    (long long)H);
+    if (F <= 0 || F % 16 != 0)
+        return fail(FP8LN_ERR_UNSUPPORTED, "ffn %lld must be a positive multiple of 16",
+                    (long long)F);
+    if ((s = check_meta(fwd, 4, FP8LN_META_FORWARD, "forward"))) return s;
+    if ((s = check_meta(bwd, 2, FP8LN_META_BACKWARD, "backward"))) return s;
+    REQUIRE_PTR(ctx);
+    REQUIRE(ctx->ln_qt && ctx->w1_qt && ctx->w2_qt && ctx->g_qt && ctx->h && ctx->mean && ctx->rstd,
+            "ctx needs ln_qt, w1_qt, w2_qt, g_qt, h, mean and rstd from a training forward");
+    REQUIRE_PTR(gamma); REQUIRE_PTR(dgamma); REQUIRE_PTR(dbeta); REQUIRE_PTR(dw1);
+    REQUIRE_PTR(dw2);
+    REQUIRE_ALIGNED(gamma); REQUIRE_ALIGNED(dw1); REQUIRE_ALIGNED(dw2);
+    REQUIRE_ALIGNED(ctx->w1_qt); REQUIRE_ALIGNED(ctx->w2_qt);
+    if (M > 0) {
+        REQUIRE_PTR(dy); REQUIRE_PTR(x); REQUIRE_PTR(dx);
+        REQUIRE_ALIGNED(dy); REQUIRE_ALIGNED(x); REQUIRE_ALIGNED(dx);
+        REQUIRE_ALIGNED(ctx->ln_qt); REQUIRE_ALIGNED(ctx->g_qt); REQUIRE_ALIGNED(ctx->h);
+    }
+    const MlpWs need = mlp_ws(nullptr, M, H, F);
+    REQUIRE(workspace && workspace_bytes >= need.bytes, "ln_mlp_bwd needs %zu bytes of workspace",
+            need.bytes);
+    REQUIRE_ALIGNED(workspace);
+    if ((s = check_current_device())) return s;
+    hipStream_t st = as_stream(stream);
+    const MlpWs w = mlp_ws(workspace, M, H, F);
+    const int ff = meta_fp8(recipe, FP8LN_META_FORWARD);
+    const int bf = meta_fp8(recipe, FP8LN_META_BACKWARD);
+
+    FP8LN_TRY(launch_cast_amax(M, H, false, dy, bf, bwd->scale + 0, bwd->amax_history + 0, w.dy_q,
+                               w.dy_qt, db2, w.cast_ws, st),
+              "fc2 grad cast launch");
+    // fc2 dgrad with the GELU derivative: dH[M][F] = dy_q[M][H] . (w2_qt[F][H])^T * gelu'(h)
+    GemmParams dg2 = gemm_params(M, F, H, w.dy_q, bf, ctx->w2_qt, ff, bwd->scale_inv + 0,
+                                 fwd->scale_inv + 3, kEpiDGeluF32);
+    dg2.out = w.dh;
+    dg2.h_in = ctx->h;
+    FP8LN_TRY(launch_gemm(dg2, st), "fc2 dgrad launch");
+    FP8LN_TRY(launch_cast_amax(M, F, true, w.dh, bf, bwd->scale + 1, bwd->amax_history + 1, w.dh_q,
+                               w.dh_qt, db1, w.cast_ws, st),
+              "fc1 grad cast launch");
+    // fc2 wgrad: dW2[H][F] = dy_qt[H][M] . (g_qt[F][M])^T
+    GemmParams wg2 = gemm_params(H, F, M, w.dy_qt, bf, ctx->g_qt, ff, bwd->scale_inv + 0,
+                                 fwd->scale_inv + 2, kEpiF32);
+    wg2.out = dw2;
+    FP8LN_TRY(launch_gemm(wg2, st), "fc2 wgrad launch");
+    // fc1 dgrad: dLN[M][H] = dh_q[M][F] . (w1_qt[H][F])^T
+    GemmParams dg1 = gemm_params(M, H, F, w.dh_q, bf, ctx->w1_qt, ff, bwd->scale_inv + 1,
+                                 fwd->scale_inv + 1, kEpiF32);
+    dg1.out = w.dln;
+    FP8LN_TRY(launch_gemm(dg1, st), "fc1 dgrad launch");
+    // fc1 wgrad: dW1[F][H] = dh_qt[F][M] . (ln_qt[H][M])^T
+    GemmParams wg1 = gemm_params(F, H, M, w.dh_qt, bf, ctx->ln_qt, ff, bwd->scale_inv + 1,
+                                 fwd->scale_inv + 0, kEpiF32);
+    wg1.out = dw1;
+    FP8LN_TRY(launch_gemm(wg1, st), "fc1 wgrad launch");
+    FP8LN_TRY(launch_ln_bwd(M, (int)H, w.dln, x, ctx->mean, ctx->rstd, gamma, dx, dgamma, dbeta,
+                            w.ln_ws, st),
+              "layernorm_bwd launch");
+    return FP8LN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,123 @@
+// Device helpers shared by the gfx950 kernels: bf16 unpacking, the FP8 encoder,
+// wave reductions and the amax atomic.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launchers.hpp"
+
+namespace fp8ln {
+
+constexpr int kWave = 64;
+
+template <int FMT>
+struct Fp8Traits;
+template <>
+struct Fp8Traits<kE4M3> {
+    static constexpr float kMax = 448.0f;
+};
+template <>
+struct Fp8Traits<kE5M2> {
+    static constexpr float kMax = 57344.0f;
+};
+
+// ---- bf16 ------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// binary32 -> bf16, round to nearest even; NaN -> quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// Unpack 8 bf16 values held in a 16-byte word.
+__device__ __forceinline__ void unpack_bf16x8(const uint4& w, float* v) {
+    v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
+    v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+    v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z);
+    v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+}
+
+// ---- FP8 encoder -------------------------------------------------------------
+//
+// The hardware conversion rounds to nearest even in the OCP formats; the value is
+// first clamped to +-max with a median-of-three so that overflow (infinities
+// included) saturates.  The median does not keep NaN, so a NaN input is patched
+// to the canonical code 0x7F afterwards; callers find NaNs cheaply from the amax
+// bits they already track (|x| bits above 0x7f800000) and call the patch only then.
+
+template <int FMT, bool HI>
+__device__ __forceinline__ uint32_t cvt_pk(float a, float b, uint32_t old) {
+    constexpr float M = Fp8Traits<FMT>::kMax;
+    a = __builtin_amdgcn_fmed3f(a, -M, M);
+    b = __builtin_amdgcn_fmed3f(b, -M, M);
+    if constexpr (FMT == kE4M3)
+        return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
+    else
+        return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(a, b, (int)old, HI);
+}
+
+// Four values -> four codes in one 32-bit word (byte i = code of v[i]).
+template <int FMT>
+__device__ __forceinline__ uint32_t encode4(float v0, float v1, float v2, float v3) {
+    uint32_t r = cvt_pk<FMT, false>(v0, v1, 0u);
+    return cvt_pk<FMT, true>(v2, v3, r);
+}
+
+// Replace the code of every NaN among v[0..3] by 0x7F.
+__device__ __forceinline__ uint32_t patch_nan4(uint32_t codes, const float* v) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (v[i] != v[i]) codes = (codes & ~(0xffu << (8 * i))) | (0x7fu << (8 * i));
+    return codes;
+}
+
+// |x| as bits; integer max over these ranks NaN above +inf above every finite value.
+__device__ __forceinline__ uint32_t abs_bits(float x) { return __float_as_uint(x) & 0x7fffffffu; }
+
+constexpr uint32_t kInfBits = 0x7f800000u;
+
+// ---- reductions ----------------------------------------------------------------
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+        uint32_t o = (uint32_t)__shfl_xor((int)v, off, kWave);
+        v = v > o ? v : o;
+    }
+    return v;
+}
+
+// Block-wide max of amax bits followed by one atomic into *amax (a float whose
+// bits order like unsigned integers because it is never negative).  All threads of
+// the block must call it.  `smem` holds at least one uint32 per wave.
+__device__ __forceinline__ void block_amax_atomic(uint32_t bits, float* amax, uint32_t* smem) {
+    bits = wave_max_u32(bits);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    if (lane == 0) smem[wave] = bits;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t m = 0;
+        const int nw = (blockDim.x + kWave - 1) / kWave;
+        for (int w = 0; w < nw; ++w) m = smem[w] > m ? smem[w] : m;
+        if (m != 0) atomicMax(reinterpret_cast<unsigned int*>(amax), m);
+    }
+}
+
+}  // namespace fp8ln

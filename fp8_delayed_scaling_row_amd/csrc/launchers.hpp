@@ -1,0 +1,72 @@
+// Host-side launchers of the gfx950 kernels.  Each enqueues its kernels on
+// `stream` and returns the launch status; arguments are validated by the C-ABI
+// layer before any launcher runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fp8ln {
+
+// FP8 encodings (same values as fp8ln_fp8_dtype).
+enum Fp8Kind : int { kE4M3 = 0, kE5M2 = 1 };
+
+// scaling.hip
+hipError_t launch_meta_init(float* hist, float* scale, float* scale_inv, int len, int n_slots,
+                            hipStream_t stream);
+hipError_t launch_scaling_update(float* hist, float* scale, float* scale_inv, int len,
+                                 int n_slots, int margin, float fp8_max, hipStream_t stream);
+
+// layernorm.hip
+hipError_t launch_ln_cast_amax(int64_t rows, int hidden, const void* x, const void* gamma,
+                               const void* beta, float eps, int fp8, const float* scale,
+                               float* amax, uint8_t* out, float* mean, float* rstd,
+                               hipStream_t stream);
+size_t ln_bwd_workspace(int64_t rows, int hidden);
+hipError_t launch_ln_bwd(int64_t rows, int hidden, const float* dy, const void* x,
+                         const float* mean, const float* rstd, const void* gamma, void* dx,
+                         float* dgamma, float* dbeta, void* workspace, hipStream_t stream);
+
+// cast.hip
+size_t cast_workspace(int64_t rows, int64_t cols);
+hipError_t launch_cast_amax(int64_t rows, int64_t cols, bool in_f32, const void* in, int fp8,
+                            const float* scale, float* amax, uint8_t* out, uint8_t* out_t,
+                            float* colsum, void* workspace, hipStream_t stream);
+hipError_t launch_transpose_u8(int64_t rows, int64_t cols, const uint8_t* in, uint8_t* out,
+                               hipStream_t stream);
+hipError_t launch_encode_range(uint32_t start, int64_t count, int fp8, uint8_t* out,
+                               hipStream_t stream);
+
+// gemm.hip
+enum GemmEpilogue : int {
+    kEpiBf16Bias = 0,   // out bf16 = acc * alpha + bias
+    kEpiF32 = 1,        // out fp32 = acc * alpha
+    kEpiGeluFp8 = 2,    // h = acc * alpha + bias -> h bf16; g = gelu(h) -> FP8 (+T), amax
+    kEpiDGeluF32 = 3,   // out fp32 = acc * alpha * gelu'(h)
+};
+
+struct GemmParams {
+    int64_t M, N, K;
+    const uint8_t* A;       // [M][K]
+    const uint8_t* B;       // [N][K]
+    int a_fp8, b_fp8;
+    const float* sinv_a;    // device scalars; alpha = *sinv_a * *sinv_b
+    const float* sinv_b;
+    const uint16_t* bias;   // bf16 [N] or null
+    void* out;              // [M][N], bf16 or fp32
+    // kEpiGeluFp8
+    uint16_t* h_out;        // bf16 [M][N] or null
+    uint8_t* q_out;         // [M][N]
+    uint8_t* q_out_t;       // [N][M] or null
+    const float* q_scale;   // scale of the FP8 output
+    float* q_amax;          // amax of gelu(h)
+    int q_fp8;
+    // kEpiDGeluF32
+    const uint16_t* h_in;   // bf16 [M][N]
+    int epilogue;
+};
+
+hipError_t launch_gemm(const GemmParams& p, hipStream_t stream);
+
+}  // namespace fp8ln

@@ -1,0 +1,334 @@
+// LayerNorm kernels: the fused forward (row statistics, affine, scale, FP8 cast,
+// per-tensor amax) and the backward (dx plus deterministic dgamma/dbeta).
+//
+// The fused modules normalise each row and feed the result to an FP8 linear
+// layer in one operation (tutorial "Accelerating Transformer Training with
+// NVIDIA Transformer Engine ...", setup listing: LayerNormLinear, LayerNormMLP;
+// "Turbo-charging your transformer training", "The building blocks").  Epsilon
+// and the variance estimator are not on the pages: biased variance and the
+// recipe's epsilon (1e-5 by default, as in torch.nn.LayerNorm, which the
+// tutorial's plain-PyTorch mirror block uses).
+//
+// Layout: one 64-lane wave owns one row at a time; lane l holds the row's 16-byte
+// chunks l, l+64, l+128, ... (8 bf16 each), so every load and store of a wave is
+// one contiguous, fully coalesced span.  The row stays in registers between the
+// two statistics passes and the output pass, so x is read from HBM exactly once.
+#include "device_common.hpp"
+#include "launchers.hpp"
+
+namespace fp8ln {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWavesPerBlock = kThreads / kWave;
+
+// CPL: 16-byte chunks per lane (hidden <= CPL * 64 * 8).
+template <int CPL, int FMT>
+__global__ __launch_bounds__(kThreads) void ln_cast_amax_kernel(
+    const uint4* __restrict__ x, const uint4* __restrict__ gamma, const uint4* __restrict__ beta,
+    int64_t rows, int hidden, float eps, const float* __restrict__ scale_ptr,
+    float* __restrict__ amax_ptr, uint2* __restrict__ out, float* __restrict__ mean_out,
+    float* __restrict__ rstd_out) {
+    __shared__ uint32_t red[kWavesPerBlock];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int nchunk = hidden / 8;
+    const float inv_h = 1.0f / (float)hidden;
+    const float s = *scale_ptr;
+
+    constexpr bool kCacheParams = CPL <= 4;
+    float g[kCacheParams ? CPL * 8 : 1];
+    float b[kCacheParams ? CPL * 8 : 1];
+    if constexpr (kCacheParams) {
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = lane + i * kWave;
+            if (c < nchunk) {
+                unpack_bf16x8(gamma[c], g + 8 * i);
+                unpack_bf16x8(beta[c], b + 8 * i);
+            }
+        }
+    }
+
+    uint32_t amax_bits = 0;
+    for (int64_t row = (int64_t)blockIdx.x * kWavesPerBlock + wave; row < rows;
+         row += (int64_t)gridDim.x * kWavesPerBlock) {
+        const uint4* xr = x + row * nchunk;
+        float v[CPL * 8];
+        uint4 raw[CPL];
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = lane + i * kWave;
+            raw[i] = c < nchunk ? xr[c] : make_uint4(0, 0, 0, 0);
+        }
+        float sum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            unpack_bf16x8(raw[i], v + 8 * i);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) sum += v[8 * i + k];
+        }
+        const float mu = wave_sum(sum) * inv_h;
+        float sq = 0.0f;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const bool valid = lane + i * kWave < nchunk;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const float d = valid ? v[8 * i + k] - mu : 0.0f;
+                v[8 * i + k] = d;
+                sq += d * d;
+            }
+        }
+        const float var = wave_sum(sq) * inv_h;
+        const float rs = 1.0f / sqrtf(var + eps);
+
+        uint2* orow = out + row * nchunk;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = lane + i * kWave;
+            if (c < nchunk) {
+                float gg[8], bb[8];
+                if constexpr (kCacheParams) {
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) { gg[k] = g[8 * i + k]; bb[k] = b[8 * i + k]; }
+                } else {
+                    unpack_bf16x8(gamma[c], gg);
+                    unpack_bf16x8(beta[c], bb);
+                }
+                float y[8];
+                uint32_t cm = 0;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    y[k] = fmaf(v[8 * i + k] * rs, gg[k], bb[k]);
+                    const uint32_t ab = abs_bits(y[k]);
+                    cm = cm > ab ? cm : ab;
+                }
+                float ys[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) ys[k] = y[k] * s;
+                uint2 q;
+                q.x = encode4<FMT>(ys[0], ys[1], ys[2], ys[3]);
+                q.y = encode4<FMT>(ys[4], ys[5], ys[6], ys[7]);
+                if (__builtin_expect(cm > kInfBits, 0)) {
+                    q.x = patch_nan4(q.x, ys);
+                    q.y = patch_nan4(q.y, ys + 4);
+                }
+                orow[c] = q;
+                amax_bits = amax_bits > cm ? amax_bits : cm;
+            }
+        }
+        if (lane == 0) {
+            if (mean_out) mean_out[row] = mu;
+            if (rstd_out) rstd_out[row] = rs;
+        }
+    }
+    block_amax_atomic(amax_bits, amax_ptr, red);
+}
+
+template <int CPL>
+hipError_t launch_ln_fwd_cpl(int64_t rows, int hidden, const void* x, const void* gamma,
+                             const void* beta, float eps, int fp8, const float* scale,
+                             float* amax, uint8_t* out, float* mean, float* rstd,
+                             hipStream_t stream) {
+    int64_t want = (rows + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int64_t cap = 256 * 16;   // 16 blocks per CU on 256 CUs, then grid-stride
+    const int blocks = (int)(want < cap ? want : cap);
+    if (fp8 == kE4M3)
+        hipLaunchKernelGGL((ln_cast_amax_kernel<CPL, kE4M3>), dim3(blocks), dim3(kThreads), 0,
+                           stream, (const uint4*)x, (const uint4*)gamma, (const uint4*)beta,
+                           rows, hidden, eps, scale, amax, (uint2*)out, mean, rstd);
+    else
+        hipLaunchKernelGGL((ln_cast_amax_kernel<CPL, kE5M2>), dim3(blocks), dim3(kThreads), 0,
+                           stream, (const uint4*)x, (const uint4*)gamma, (const uint4*)beta,
+                           rows, hidden, eps, scale, amax, (uint2*)out, mean, rstd);
+    return hipGetLastError();
+}
+
+// ---- backward --------------------------------------------------------------
+
+// Per block: rows handled by its waves in grid-stride order; per lane: dgamma and
+// dbeta partial sums of its own columns.  Partials go to ws[block][2][hidden] and a
+// second kernel adds the blocks in a fixed order, so results are deterministic.
+template <int CPL>
+__global__ __launch_bounds__(kThreads) void ln_bwd_kernel(
+    const float4* __restrict__ dy, const uint4* __restrict__ x, const float* __restrict__ mean,
+    const float* __restrict__ rstd, const uint4* __restrict__ gamma, uint4* __restrict__ dx,
+    float* __restrict__ partial, int64_t rows, int hidden) {
+    extern __shared__ float sm[];   // [2][hidden]: dgamma, dbeta of the block
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int nchunk = hidden / 8;
+    const float inv_h = 1.0f / (float)hidden;
+
+    float g[CPL * 8];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int c = lane + i * kWave;
+        if (c < nchunk) unpack_bf16x8(gamma[c], g + 8 * i);
+        else
+#pragma unroll
+            for (int k = 0; k < 8; ++k) g[8 * i + k] = 0.0f;
+    }
+    float dg[CPL * 8], db[CPL * 8];
+#pragma unroll
+    for (int j = 0; j < CPL * 8; ++j) { dg[j] = 0.0f; db[j] = 0.0f; }
+
+    for (int64_t row = (int64_t)blockIdx.x * kWavesPerBlock + wave; row < rows;
+         row += (int64_t)gridDim.x * kWavesPerBlock) {
+        const float mu = mean[row];
+        const float rs = rstd[row];
+        float xh[CPL * 8], d[CPL * 8];
+        float s1 = 0.0f, s2 = 0.0f;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = lane + i * kWave;
+            if (c < nchunk) {
+                unpack_bf16x8(x[row * nchunk + c], xh + 8 * i);
+                const float4 a = dy[(row * nchunk + c) * 2];
+                const float4 b2 = dy[(row * nchunk + c) * 2 + 1];
+                d[8 * i + 0] = a.x; d[8 * i + 1] = a.y; d[8 * i + 2] = a.z; d[8 * i + 3] = a.w;
+                d[8 * i + 4] = b2.x; d[8 * i + 5] = b2.y; d[8 * i + 6] = b2.z; d[8 * i + 7] = b2.w;
+            } else {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) { xh[8 * i + k] = mu; d[8 * i + k] = 0.0f; }
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int j = 8 * i + k;
+                xh[j] = (xh[j] - mu) * rs;
+                const float gj = d[j] * g[j];
+                s1 += gj;
+                s2 += gj * xh[j];
+                dg[j] += d[j] * xh[j];
+                db[j] += d[j];
+            }
+        }
+        const float c1 = wave_sum(s1) * inv_h;
+        const float c2 = wave_sum(s2) * inv_h;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = lane + i * kWave;
+            if (c < nchunk) {
+                float o[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int j = 8 * i + k;
+                    o[k] = rs * (d[j] * g[j] - c1 - xh[j] * c2);
+                }
+                uint4 w;
+                w.x = pack_bf16x2(o[0], o[1]);
+                w.y = pack_bf16x2(o[2], o[3]);
+                w.z = pack_bf16x2(o[4], o[5]);
+                w.w = pack_bf16x2(o[6], o[7]);
+                dx[row * nchunk + c] = w;
+            }
+        }
+    }
+    // combine the block's waves in a fixed order (wave 0 first)
+    for (int w = 0; w < kWavesPerBlock; ++w) {
+        if (wave == w) {
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+                const int c = lane + i * kWave;
+                if (c < nchunk) {
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        float* pg = sm + c * 8 + k;
+                        float* pd = sm + hidden + c * 8 + k;
+                        *pg = w == 0 ? dg[8 * i + k] : *pg + dg[8 * i + k];
+                        *pd = w == 0 ? db[8 * i + k] : *pd + db[8 * i + k];
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+    float* pb = partial + (int64_t)blockIdx.x * 2 * hidden;
+    for (int j = threadIdx.x; j < 2 * hidden; j += kThreads) pb[j] = sm[j];
+}
+
+// out[j] = sum over blocks b of partial[b][j] (fixed order); j < 2 * hidden.
+__global__ __launch_bounds__(kThreads) void sum_partials_kernel(const float* __restrict__ partial,
+                                                                int nblocks, int width,
+                                                                float* __restrict__ out0,
+                                                                float* __restrict__ out1,
+                                                                int split) {
+    const int j = blockIdx.x * kThreads + threadIdx.x;
+    if (j >= width) return;
+    float acc = 0.0f;
+    for (int b = 0; b < nblocks; ++b) acc += partial[(int64_t)b * width + j];
+    if (j < split) out0[j] = acc;
+    else out1[j - split] = acc;
+}
+
+int ln_bwd_blocks(int64_t rows) {
+    const int64_t want = (rows + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int64_t cap = 512;
+    return (int)(want < cap ? (want > 0 ? want : 1) : cap);
+}
+
+template <int CPL>
+hipError_t launch_ln_bwd_cpl(int64_t rows, int hidden, const float* dy, const void* x,
+                             const float* mean, const float* rstd, const void* gamma, void* dx,
+                             float* dgamma, float* dbeta, void* workspace, hipStream_t stream) {
+    const int blocks = ln_bwd_blocks(rows);
+    const size_t smem = (size_t)2 * hidden * sizeof(float);
+    float* partial = (float*)workspace;
+    hipLaunchKernelGGL((ln_bwd_kernel<CPL>), dim3(blocks), dim3(kThreads), smem, stream,
+                       (const float4*)dy, (const uint4*)x, mean, rstd, (const uint4*)gamma,
+                       (uint4*)dx, partial, rows, hidden);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int width = 2 * hidden;
+    hipLaunchKernelGGL(sum_partials_kernel, dim3((width + kThreads - 1) / kThreads),
+                       dim3(kThreads), 0, stream, partial, blocks, width, dgamma, dbeta, hidden);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_ln_cast_amax(int64_t rows, int hidden, const void* x, const void* gamma,
+                               const void* beta, float eps, int fp8, const float* scale,
+                               float* amax, uint8_t* out, float* mean, float* rstd,
+                               hipStream_t stream) {
+    const int chunks = hidden / 8;
+    if (chunks <= 64)
+        return launch_ln_fwd_cpl<1>(rows, hidden, x, gamma, beta, eps, fp8, scale, amax, out,
+                                    mean, rstd, stream);
+    if (chunks <= 128)
+        return launch_ln_fwd_cpl<2>(rows, hidden, x, gamma, beta, eps, fp8, scale, amax, out,
+                                    mean, rstd, stream);
+    if (chunks <= 256)
+        return launch_ln_fwd_cpl<4>(rows, hidden, x, gamma, beta, eps, fp8, scale, amax, out,
+                                    mean, rstd, stream);
+    if (chunks <= 512)
+        return launch_ln_fwd_cpl<8>(rows, hidden, x, gamma, beta, eps, fp8, scale, amax, out,
+                                    mean, rstd, stream);
+    return launch_ln_fwd_cpl<16>(rows, hidden, x, gamma, beta, eps, fp8, scale, amax, out,
+                                 mean, rstd, stream);
+}
+
+size_t ln_bwd_workspace(int64_t rows, int hidden) {
+    return (size_t)ln_bwd_blocks(rows) * 2 * (size_t)hidden * sizeof(float);
+}
+
+hipError_t launch_ln_bwd(int64_t rows, int hidden, const float* dy, const void* x,
+                         const float* mean, const float* rstd, const void* gamma, void* dx,
+                         float* dgamma, float* dbeta, void* workspace, hipStream_t stream) {
+    const int chunks = hidden / 8;
+    if (chunks <= 64)
+        return launch_ln_bwd_cpl<1>(rows, hidden, dy, x, mean, rstd, gamma, dx, dgamma, dbeta,
+                                    workspace, stream);
+    if (chunks <= 128)
+        return launch_ln_bwd_cpl<2>(rows, hidden, dy, x, mean, rstd, gamma, dx, dgamma, dbeta,
+                                    workspace, stream);
+    if (chunks <= 256)
+        return launch_ln_bwd_cpl<4>(rows, hidden, dy, x, mean, rstd, gamma, dx, dgamma, dbeta,
+                                    workspace, stream);
+    return launch_ln_bwd_cpl<8>(rows, hidden, dy, x, mean, rstd, gamma, dx, dgamma, dbeta,
+                                workspace, stream);
+}
+
+}  // namespace fp8ln

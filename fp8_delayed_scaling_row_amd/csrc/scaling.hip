@@ -1,0 +1,120 @@
+// Delayed-scaling bookkeeping on the device: state initialisation and the
+// step-start scale update with history roll.
+//
+// The recipe keeps a per-tensor scale and a 2-D amax history with the newest
+// amaxes in row 0, reduced with "max" over 16 or 1024 steps (tutorial
+// "Accelerating Transformer Training with NVIDIA Transformer Engine ...", setup
+// and benchmark listings); "Turbo-charging your transformer training", "Playing
+// with lower-precision formats", says the scale follows each tensor's amax.
+// The update computes scale = fp8_max / max(history) / 2^margin as one binary32
+// division plus an exact power-of-two step, keeps the old scale when the
+// window's max is zero or not finite or the result is not a finite positive
+// number, sets scale_inv = 1 / scale, then moves every row down by one and clears
+// row 0.  All of it stays on the device: no value returns to the host.
+#include "device_common.hpp"
+#include "launchers.hpp"
+
+namespace fp8ln {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxHist = 1024;
+constexpr int kMaxSlots = 8;
+constexpr int kPerThread = kMaxHist * kMaxSlots / kThreads;   // values moved per thread
+
+__global__ __launch_bounds__(kThreads) void meta_init_kernel(float* hist, float* scale,
+                                                            float* scale_inv, int total,
+                                                            int n_slots) {
+    for (int i = threadIdx.x + blockIdx.x * blockDim.x; i < total; i += blockDim.x * gridDim.x)
+        hist[i] = 0.0f;
+    if (blockIdx.x == 0 && threadIdx.x < n_slots) {
+        scale[threadIdx.x] = 1.0f;
+        scale_inv[threadIdx.x] = 1.0f;
+    }
+}
+
+// One workgroup updates every slot of one state block.
+__global__ __launch_bounds__(kThreads) void scaling_update_kernel(float* hist, float* scale,
+                                                                 float* scale_inv, int len,
+                                                                 int n_slots, int margin,
+                                                                 float fp8_max) {
+    __shared__ float red_max[kThreads / kWave];
+    __shared__ int red_nan[kThreads / kWave];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+
+    for (int s = 0; s < n_slots; ++s) {
+        float m = 0.0f;
+        int nan = 0;
+        for (int i = tid; i < len; i += kThreads) {
+            const float v = hist[i * n_slots + s];
+            nan |= (v != v);
+            m = fmaxf(m, v);
+        }
+#pragma unroll
+        for (int off = kWave / 2; off > 0; off >>= 1) {
+            m = fmaxf(m, __shfl_xor(m, off, kWave));
+            nan |= __shfl_xor(nan, off, kWave);
+        }
+        if (lane == 0) {
+            red_max[wave] = m;
+            red_nan[wave] = nan;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            float a = 0.0f;
+            int any_nan = 0;
+            for (int w = 0; w < kThreads / kWave; ++w) {
+                a = fmaxf(a, red_max[w]);
+                any_nan |= red_nan[w];
+            }
+            float sc = scale[s];
+            if (!any_nan && a > 0.0f && a <= 3.402823466e38f) {
+                float ns = fp8_max / a;          // IEEE binary32 division
+                ns = ldexpf(ns, -margin);        // exact unless the result is subnormal
+                if (ns > 0.0f && ns <= 3.402823466e38f) sc = ns;
+            }
+            scale[s] = sc;
+            scale_inv[s] = 1.0f / sc;
+        }
+        __syncthreads();
+    }
+
+    // Roll: row i <- row i-1 for i >= 1, row 0 <- 0.  Read everything first.
+    const int moved = (len - 1) * n_slots;   // values in rows 0 .. len-2
+    float keep[kPerThread];
+#pragma unroll
+    for (int t = 0; t < kPerThread; ++t) {
+        const int j = tid + t * kThreads;
+        keep[t] = j < moved ? hist[j] : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < kPerThread; ++t) {
+        const int j = tid + t * kThreads;
+        if (j < moved) hist[j + n_slots] = keep[t];
+    }
+    if (tid < n_slots) hist[tid] = 0.0f;
+}
+
+}  // namespace
+
+hipError_t launch_meta_init(float* hist, float* scale, float* scale_inv, int len, int n_slots,
+                            hipStream_t stream) {
+    const int total = len * n_slots;
+    const int blocks = (total + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(meta_init_kernel, dim3(blocks), dim3(kThreads), 0, stream, hist, scale,
+                       scale_inv, total, n_slots);
+    return hipGetLastError();
+}
+
+hipError_t launch_scaling_update(float* hist, float* scale, float* scale_inv, int len,
+                                 int n_slots, int margin, float fp8_max, hipStream_t stream) {
+    hipLaunchKernelGGL(scaling_update_kernel, dim3(1), dim3(kThreads), 0, stream, hist, scale,
+                       scale_inv, len, n_slots, margin, fp8_max);
+    return hipGetLastError();
+}
+
+}  // namespace fp8ln

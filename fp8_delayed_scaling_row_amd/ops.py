@@ -1,0 +1,328 @@
+"""Python binding of libfp8ln: the C-ABI calls with torch tensors as buffers.
+
+Every function marshals tensor pointers and sizes and calls the entry point of
+the same name in include/fp8ln.h on torch's current HIP stream.  No step of the
+computation happens here; torch only provides device memory and the stream.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass
+
+import torch
+
+from . import _abi
+from ._abi import (DTYPE_BF16, DTYPE_F32, E4M3, E5M2, FORMAT_E4M3, FORMAT_E5M2, FORMAT_HYBRID,
+                   META_BACKWARD, META_FORWARD, OP_CAST_AMAX, OP_LAYERNORM_BWD, OP_LN_LINEAR_BWD,
+                   OP_LN_MLP_BWD, Fp8lnError, check, lib)
+
+__all__ = [
+    "Recipe", "Meta", "LinearCtx", "MlpCtx", "Fp8lnError", "FORMAT_E4M3", "FORMAT_HYBRID",
+    "FORMAT_E5M2", "E4M3", "E5M2", "META_FORWARD", "META_BACKWARD", "OP_CAST_AMAX",
+    "OP_LAYERNORM_BWD", "OP_LN_LINEAR_BWD", "OP_LN_MLP_BWD", "check_support", "workspace_size", "meta_init",
+    "scaling_update", "ln_cast_amax", "cast_amax", "encode_range", "gemm", "layernorm_bwd",
+    "ln_linear_fwd", "ln_linear_bwd", "ln_mlp_fwd", "ln_mlp_bwd", "fwd_fp8", "bwd_fp8",
+]
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return C.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _need(t, dtype, shape, name):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+
+
+def _opt(t, dtype, shape, name):
+    if t is not None:
+        _need(t, dtype, shape, name)
+
+
+@dataclass
+class Recipe:
+    """DelayedScaling recipe: format, amax_history_len, margin, LayerNorm eps."""
+    format: int = FORMAT_HYBRID
+    amax_history_len: int = 16
+    margin: int = 0
+    ln_eps: float = 1e-5
+
+    def as_c(self) -> _abi.Recipe:
+        return _abi.Recipe(self.format, self.amax_history_len, self.margin, self.ln_eps)
+
+
+def fwd_fp8(recipe: Recipe) -> int:
+    return E5M2 if recipe.format == FORMAT_E5M2 else E4M3
+
+
+def bwd_fp8(recipe: Recipe) -> int:
+    return E4M3 if recipe.format == FORMAT_E4M3 else E5M2
+
+
+class Meta:
+    """One direction's FP8 state of one module: history [L][n_slots], scale and
+    scale_inv [n_slots], all float32 device tensors."""
+
+    def __init__(self, recipe: Recipe, n_slots: int, kind: int, device="cuda", init=True):
+        self.recipe = recipe
+        self.kind = kind
+        self.history = torch.zeros((recipe.amax_history_len, n_slots), dtype=torch.float32,
+                                   device=device)
+        self.scale = torch.ones(n_slots, dtype=torch.float32, device=device)
+        self.scale_inv = torch.ones(n_slots, dtype=torch.float32, device=device)
+        if init:
+            meta_init(recipe, self)
+
+    @property
+    def n_slots(self) -> int:
+        return self.history.shape[1]
+
+    def as_c(self) -> _abi.MetaStruct:
+        return _abi.MetaStruct(self.history.data_ptr(), self.scale.data_ptr(),
+                               self.scale_inv.data_ptr(), self.n_slots, self.kind)
+
+    def amax_ptr(self, slot: int) -> int:
+        """Address of history row 0 for `slot` (where the step records its amax)."""
+        return self.history.data_ptr() + 4 * slot
+
+
+class LinearCtx:
+    """What LayerNormLinear's forward saves for its backward."""
+
+    def __init__(self, tokens: int, in_features: int, out_features: int, training=True,
+                 device="cuda"):
+        u8 = dict(dtype=torch.uint8, device=device)
+        self.ln_q = torch.empty((tokens, in_features), **u8)
+        self.w_q = torch.empty((out_features, in_features), **u8)
+        self.ln_qt = torch.empty((in_features, tokens), **u8) if training else None
+        self.w_qt = torch.empty((in_features, out_features), **u8) if training else None
+        self.mean = torch.empty(tokens, dtype=torch.float32, device=device)
+        self.rstd = torch.empty(tokens, dtype=torch.float32, device=device)
+
+    def as_c(self) -> _abi.LinearCtxStruct:
+        p = lambda t: None if t is None else t.data_ptr()
+        return _abi.LinearCtxStruct(p(self.ln_q), p(self.ln_qt), p(self.w_q), p(self.w_qt),
+                                    p(self.mean), p(self.rstd))
+
+
+class MlpCtx:
+    """What LayerNormMLP's forward saves for its backward."""
+
+    def __init__(self, tokens: int, hidden: int, ffn: int, training=True, device="cuda"):
+        u8 = dict(dtype=torch.uint8, device=device)
+        self.ln_q = torch.empty((tokens, hidden), **u8)
+        self.w1_q = torch.empty((ffn, hidden), **u8)
+        self.w2_q = torch.empty((hidden, ffn), **u8)
+        self.g_q = torch.empty((tokens, ffn), **u8)
+        self.ln_qt = torch.empty((hidden, tokens), **u8) if training else None
+        self.w1_qt = torch.empty((hidden, ffn), **u8) if training else None
+        self.w2_qt = torch.empty((ffn, hidden), **u8) if training else None
+        self.g_qt = torch.empty((ffn, tokens), **u8) if training else None
+        self.h = torch.empty((tokens, ffn), dtype=torch.bfloat16, device=device) if training else None
+        self.mean = torch.empty(tokens, dtype=torch.float32, device=device)
+        self.rstd = torch.empty(tokens, dtype=torch.float32, device=device)
+
+    def as_c(self) -> _abi.MlpCtxStruct:
+        p = lambda t: None if t is None else t.data_ptr()
+        return _abi.MlpCtxStruct(p(self.ln_q), p(self.ln_qt), p(self.w1_q), p(self.w1_qt),
+                                 p(self.w2_q), p(self.w2_qt), p(self.h), p(self.g_q),
+                                 p(self.g_qt), p(self.mean), p(self.rstd))
+
+
+# ---- library -----------------------------------------------------------------
+
+def check_support(device: int = 0):
+    buf = C.create_string_buffer(256)
+    ok = lib().fp8ln_check_support(device, buf, len(buf))
+    return ok == 1, buf.value.decode()
+
+
+def workspace_size(op: int, a: int, b: int, c: int = 0) -> int:
+    return int(lib().fp8ln_workspace_size(op, a, b, c))
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+# ---- delayed-scaling state ----------------------------------------------------
+
+def meta_init(recipe: Recipe, meta: Meta, stream=None) -> None:
+    r, m = recipe.as_c(), meta.as_c()
+    check(lib().fp8ln_meta_init(C.byref(r), C.byref(m), _stream(stream)))
+
+
+def scaling_update(recipe: Recipe, meta: Meta, stream=None) -> None:
+    r, m = recipe.as_c(), meta.as_c()
+    check(lib().fp8ln_scaling_update(C.byref(r), C.byref(m), _stream(stream)))
+
+
+# ---- kernels ------------------------------------------------------------------
+
+def ln_cast_amax(recipe: Recipe, x, gamma, beta, fp8_dtype: int, scale, amax_ptr: int, out,
+                 out_t=None, mean=None, rstd=None, stream=None) -> None:
+    """out = encode(LayerNorm(x) * scale); amax recorded at amax_ptr (a float32
+    device address, usually Meta.amax_ptr(slot)); scale is a 1-element float32
+    device tensor (or view)."""
+    rows, hidden = x.shape
+    _need(x, torch.bfloat16, (rows, hidden), "x")
+    _need(gamma, torch.bfloat16, (hidden,), "gamma")
+    _need(beta, torch.bfloat16, (hidden,), "beta")
+    _need(out, torch.uint8, (rows, hidden), "out")
+    _opt(out_t, torch.uint8, (hidden, rows), "out_t")
+    _opt(mean, torch.float32, (rows,), "mean")
+    _opt(rstd, torch.float32, (rows,), "rstd")
+    r = recipe.as_c()
+    check(lib().fp8ln_ln_cast_amax(C.byref(r), rows, hidden, DTYPE_BF16, _ptr(x), _ptr(gamma),
+                                   _ptr(beta), fp8_dtype, _ptr(scale), C.c_void_p(amax_ptr),
+                                   _ptr(out), _ptr(out_t), _ptr(mean), _ptr(rstd),
+                                   _stream(stream)))
+
+
+def cast_amax(x, fp8_dtype: int, scale, amax_ptr: int, out, out_t=None, colsum=None,
+              stream=None) -> None:
+    rows, cols = x.shape
+    if x.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("x must be bf16 or float32")
+    _need(out, torch.uint8, (rows, cols), "out")
+    _opt(out_t, torch.uint8, (cols, rows), "out_t")
+    _opt(colsum, torch.float32, (cols,), "colsum")
+    ws = None
+    nbytes = 0
+    if colsum is not None:
+        nbytes = workspace_size(_abi.OP_CAST_AMAX, rows, cols)
+        ws = _workspace(nbytes, x.device)
+    dt = DTYPE_F32 if x.dtype == torch.float32 else DTYPE_BF16
+    check(lib().fp8ln_cast_amax(rows, cols, dt, _ptr(x), fp8_dtype, _ptr(scale),
+                                C.c_void_p(amax_ptr), _ptr(out), _ptr(out_t), _ptr(colsum),
+                                _ptr(ws), nbytes, _stream(stream)))
+
+
+def encode_range(start: int, count: int, fp8_dtype: int, out, stream=None) -> None:
+    if out.dtype != torch.uint8 or out.numel() < count:
+        raise ValueError("out must be a uint8 tensor with at least count elements")
+    check(lib().fp8ln_encode_range(start & 0xFFFFFFFF, count, fp8_dtype, _ptr(out),
+                                   _stream(stream)))
+
+
+def gemm(a, a_dtype: int, b, b_dtype: int, sinv_a, sinv_b, out, bias=None, stream=None) -> None:
+    """out[m][n] = (sum_k a[m][k] b[n][k]) * sinv_a * sinv_b (+ bias[n])."""
+    M, K = a.shape
+    N = b.shape[0]
+    _need(a, torch.uint8, (M, K), "a")
+    _need(b, torch.uint8, (N, K), "b")
+    if out.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out must be bf16 or float32")
+    _need(out, out.dtype, (M, N), "out")
+    _opt(bias, torch.bfloat16, (N,), "bias")
+    od = DTYPE_BF16 if out.dtype == torch.bfloat16 else DTYPE_F32
+    check(lib().fp8ln_gemm(M, N, K, _ptr(a), a_dtype, _ptr(b), b_dtype, _ptr(sinv_a),
+                           _ptr(sinv_b), _ptr(bias), od, _ptr(out), _stream(stream)))
+
+
+def layernorm_bwd(dy, x, mean, rstd, gamma, dx, dgamma, dbeta, stream=None) -> None:
+    rows, hidden = x.shape
+    _need(dy, torch.float32, (rows, hidden), "dy")
+    _need(x, torch.bfloat16, (rows, hidden), "x")
+    _need(dx, torch.bfloat16, (rows, hidden), "dx")
+    nbytes = workspace_size(_abi.OP_LAYERNORM_BWD, rows, hidden)
+    ws = _workspace(nbytes, x.device)
+    check(lib().fp8ln_layernorm_bwd(rows, hidden, _ptr(dy), _ptr(x), _ptr(mean), _ptr(rstd),
+                                    _ptr(gamma), _ptr(dx), _ptr(dgamma), _ptr(dbeta), _ptr(ws),
+                                    nbytes, _stream(stream)))
+
+
+# ---- modules ------------------------------------------------------------------
+
+def ln_linear_fwd(recipe: Recipe, x, gamma, beta, weight, bias, out, fwd: Meta, ctx: LinearCtx,
+                  stream=None) -> None:
+    M, K = x.shape
+    N = weight.shape[0]
+    _need(x, torch.bfloat16, (M, K), "x")
+    _need(weight, torch.bfloat16, (N, K), "weight")
+    _opt(bias, torch.bfloat16, (N,), "bias")
+    _need(out, torch.bfloat16, (M, N), "out")
+    r, m, c = recipe.as_c(), fwd.as_c(), ctx.as_c()
+    check(lib().fp8ln_ln_linear_fwd(C.byref(r), M, K, N, DTYPE_BF16, _ptr(x), _ptr(gamma),
+                                    _ptr(beta), _ptr(weight), _ptr(bias), _ptr(out), C.byref(m),
+                                    C.byref(c), _stream(stream)))
+
+
+def ln_linear_bwd(recipe: Recipe, dy, x, gamma, ctx: LinearCtx, fwd: Meta, bwd: Meta, dx,
+                  dgamma, dbeta, dweight, dbias=None, workspace=None, stream=None) -> None:
+    M, N = dy.shape
+    K = x.shape[1]
+    _need(dy, torch.bfloat16, (M, N), "dy")
+    _need(dx, torch.bfloat16, (M, K), "dx")
+    _need(dweight, torch.float32, (N, K), "dweight")
+    _opt(dbias, torch.float32, (N,), "dbias")
+    nbytes = workspace_size(_abi.OP_LN_LINEAR_BWD, M, K, N)
+    if workspace is None:
+        workspace = _workspace(nbytes, dy.device)
+    r, mf, mb, c = recipe.as_c(), fwd.as_c(), bwd.as_c(), ctx.as_c()
+    check(lib().fp8ln_ln_linear_bwd(C.byref(r), M, K, N, DTYPE_BF16, _ptr(dy), _ptr(x),
+                                    _ptr(gamma), C.byref(c), C.byref(mf), C.byref(mb), _ptr(dx),
+                                    _ptr(dgamma), _ptr(dbeta), _ptr(dweight), _ptr(dbias),
+                                    _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def ln_mlp_fwd(recipe: Recipe, x, gamma, beta, w1, b1, w2, b2, out, fwd: Meta, ctx: MlpCtx,
+               stream=None) -> None:
+    M, H = x.shape
+    F = w1.shape[0]
+    _need(x, torch.bfloat16, (M, H), "x")
+    _need(w1, torch.bfloat16, (F, H), "w1")
+    _need(w2, torch.bfloat16, (H, F), "w2")
+    _opt(b1, torch.bfloat16, (F,), "b1")
+    _opt(b2, torch.bfloat16, (H,), "b2")
+    _need(out, torch.bfloat16, (M, H), "out")
+    r, m, c = recipe.as_c(), fwd.as_c(), ctx.as_c()
+    check(lib().fp8ln_ln_mlp_fwd(C.byref(r), M, H, F, DTYPE_BF16, _ptr(x), _ptr(gamma),
+                                 _ptr(beta), _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(out),
+                                 C.byref(m), C.byref(c), _stream(stream)))
+
+
+def ln_mlp_bwd(recipe: Recipe, dy, x, gamma, ctx: MlpCtx, fwd: Meta, bwd: Meta, dx, dgamma,
+               dbeta, dw1, db1, dw2, db2, workspace=None, stream=None) -> None:
+    M, H = dy.shape
+    F = ctx.w1_q.shape[0]
+    _need(dy, torch.bfloat16, (M, H), "dy")
+    _need(dx, torch.bfloat16, (M, H), "dx")
+    _need(dw1, torch.float32, (F, H), "dw1")
+    _need(dw2, torch.float32, (H, F), "dw2")
+    _opt(db1, torch.float32, (F,), "db1")
+    _opt(db2, torch.float32, (H,), "db2")
+    nbytes = workspace_size(_abi.OP_LN_MLP_BWD, M, H, F)
+    if workspace is None:
+        workspace = _workspace(nbytes, dy.device)
+    r, mf, mb, c = recipe.as_c(), fwd.as_c(), bwd.as_c(), ctx.as_c()
+    check(lib().fp8ln_ln_mlp_bwd(C.byref(r), M, H, F, DTYPE_BF16, _ptr(dy), _ptr(x), _ptr(gamma),
+                                 C.byref(c), C.byref(mf), C.byref(mb), _ptr(dx), _ptr(dgamma),
+                                 _ptr(dbeta), _ptr(dw1), _ptr(db1), _ptr(dw2), _ptr(db2),
+                                 _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def linear_metas(recipe: Recipe, device="cuda"):
+    """Fresh forward (2 slots) and backward (1 slot) state of a LayerNormLinear."""
+    return (Meta(recipe, 2, META_FORWARD, device), Meta(recipe, 1, META_BACKWARD, device))
+
+
+def mlp_metas(recipe: Recipe, device="cuda"):
+    """Fresh forward (4 slots) and backward (2 slots) state of a LayerNormMLP."""
+    return (Meta(recipe, 4, META_FORWARD, device), Meta(recipe, 2, META_BACKWARD, device))

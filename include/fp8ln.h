@@ -1,0 +1,319 @@
+/*
+ * fp8ln: FP8 delayed-scaling LayerNormLinear / LayerNormMLP for AMD MI355X (gfx950).
+ *
+ * The operation follows two pages on NVIDIA Transformer Engine:
+ *  [T] "Accelerating Transformer Training with NVIDIA Transformer Engine, Fused
+ *      Kernels, BF16, FP8, and GPU Benchmarking" (tutorial), and
+ *  [G] "Turbo-charging your transformer training: a hands-on guide".
+ * [T] setup listing builds LayerNormLinear(H, 3H) and LayerNormMLP(H, 4H) with bf16
+ * params and a DelayedScaling recipe (format HYBRID, amax_history_len 16,
+ * amax_compute_algo "max"); its "things to try" list adds Format.E4M3 and
+ * amax_history_len 1024; its benchmark listing reads the per-module state
+ * fp8_meta["scaling_fwd"] (a per-tensor scale vector and a 2-D amax history whose
+ * row 0 is the most recent).  [G] "The building blocks" describes LayerNormMLP as
+ * layer norm, two linear layers and GELU; "Playing with lower-precision formats:
+ * BF16 vs FP8" says delayed scaling tracks each tensor's amax and rescales it,
+ * that HYBRID mixes E4M3 and E5M2, and that autocast casts activations to FP8 with
+ * the scaling and returns gradients in BF16/FP32.
+ *
+ * Conventions shared by every entry point
+ *  - Every pointer argument is a device pointer unless stated otherwise, and the
+ *    caller owns every buffer: inputs, outputs, saved context, FP8 state and
+ *    workspace.  The library allocates no device memory and keeps no pointer
+ *    after a call returns.  Buffers must stay alive until the stream reaches the
+ *    call's kernels.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream) and runs
+ *    asynchronously.  No call synchronises the host or copies data to the host:
+ *    scales stay on the device from step to step.
+ *  - Arguments are validated before anything is launched.  A call that returns an
+ *    error has enqueued nothing.  fp8ln_last_error() gives a message for the most
+ *    recent failure on the calling host thread.
+ *  - Matrices are row-major and densely packed.  bf16 values are IEEE binary32
+ *    values truncated to their top 16 bits (stored as uint16).  FP8 tensors are
+ *    uint8 codes in the OCP 8-bit floating point formats: E4M3 (bias 7, no
+ *    infinities, largest finite 448) and E5M2 (bias 15, largest finite 57344).
+ *    Encoding rounds to nearest, ties to even, saturates to the largest finite
+ *    value (infinities included), keeps the sign of zero and writes every NaN as
+ *    0x7F.
+ *  - Only gfx950 devices are supported; on any other device every compute call
+ *    returns FP8LN_ERR_UNSUPPORTED.
+ */
+#ifndef FP8LN_H
+#define FP8LN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------- */
+typedef enum {
+    FP8LN_OK = 0,
+    FP8LN_ERR_INVALID_ARG = -1,   /* null pointer, bad size, bad enum value   */
+    FP8LN_ERR_UNSUPPORTED = -2,   /* valid request this build does not serve */
+    FP8LN_ERR_HIP = -3            /* a HIP runtime call or launch failed      */
+} fp8ln_status;
+
+/* Recipe formats ([T] setup listing: Format.HYBRID; "things to try": Format.E4M3;
+ * [G] "Common pitfalls": Format.E5M2).  HYBRID casts forward tensors (LayerNorm
+ * output, weights, GELU output) to E4M3 and gradients to E5M2; E4M3 and E5M2 use
+ * one format for both directions. */
+typedef enum {
+    FP8LN_FORMAT_E4M3 = 0,
+    FP8LN_FORMAT_HYBRID = 1,
+    FP8LN_FORMAT_E5M2 = 2
+} fp8ln_format;
+
+/* Encoding of one FP8 tensor. */
+typedef enum { FP8LN_E4M3 = 0, FP8LN_E5M2 = 1 } fp8ln_fp8_dtype;
+
+/* params_dtype of the modules ([T] setup listing: params_dtype=torch.bfloat16).
+ * FP8LN_DTYPE_F32 is accepted only as the input of fp8ln_cast_amax. */
+typedef enum { FP8LN_DTYPE_BF16 = 0, FP8LN_DTYPE_F32 = 1 } fp8ln_dtype;
+
+/* Direction of one FP8 state block (the tutorial's fp8_meta["scaling_fwd"] and its
+ * backward counterpart). */
+typedef enum { FP8LN_META_FORWARD = 0, FP8LN_META_BACKWARD = 1 } fp8ln_meta_kind;
+
+/* DelayedScaling recipe ([T] setup listing).  amax_compute_algo is always "max".
+ *   format            fp8ln_format
+ *   amax_history_len  1 .. 1024
+ *   margin            0 .. 64; scale = fp8_max / max(history) / 2^margin
+ *   ln_eps            LayerNorm epsilon, finite and > 0 (1e-5 by default) */
+typedef struct {
+    int32_t format;
+    int32_t amax_history_len;
+    int32_t margin;
+    float ln_eps;
+} fp8ln_recipe;
+
+/* One direction's FP8 state of one module, all device buffers owned by the caller:
+ *   amax_history  float [amax_history_len][n_slots], row 0 = newest
+ *   scale         float [n_slots]; must hold finite positive values
+ *   scale_inv     float [n_slots]
+ *   n_slots       1 .. 8
+ *   kind          fp8ln_meta_kind; picks the FP8 format of every slot
+ * Slots: LayerNormLinear forward {0: LN output, 1: weight}, backward {0: output
+ * gradient}.  LayerNormMLP forward {0: LN output, 1: fc1 weight, 2: GELU output,
+ * 3: fc2 weight}, backward {0: fc2 output gradient, 1: fc1 output gradient}. */
+typedef struct {
+    float* amax_history;
+    float* scale;
+    float* scale_inv;
+    int32_t n_slots;
+    int32_t kind;
+} fp8ln_meta;
+
+/* What LayerNormLinear's forward saves for its backward (device buffers).
+ * M = tokens, K = in_features, N = out_features.
+ *   ln_q   uint8 [M][K]  FP8 LayerNorm output (forward format)
+ *   ln_qt  uint8 [K][M]  its transpose; may be NULL for a forward-only call
+ *   w_q    uint8 [N][K]  FP8 weight
+ *   w_qt   uint8 [K][N]  its transpose; may be NULL for a forward-only call
+ *   mean   float [M]     row means
+ *   rstd   float [M]     row 1/sqrt(var + eps) */
+typedef struct {
+    uint8_t* ln_q;
+    uint8_t* ln_qt;
+    uint8_t* w_q;
+    uint8_t* w_qt;
+    float* mean;
+    float* rstd;
+} fp8ln_linear_ctx;
+
+/* What LayerNormMLP's forward saves for its backward (device buffers).
+ * M = tokens, H = hidden, F = ffn.
+ *   ln_q [M][H], ln_qt [H][M], w1_q [F][H], w1_qt [H][F], w2_q [H][F],
+ *   w2_qt [F][H], g_q [M][F] (FP8 GELU output), g_qt [F][M]: uint8
+ *   h     uint16 (bf16) [M][F]: fc1 output before GELU
+ *   mean, rstd float [M]
+ * The *_qt transposes and h may be NULL for a forward-only call. */
+typedef struct {
+    uint8_t* ln_q;
+    uint8_t* ln_qt;
+    uint8_t* w1_q;
+    uint8_t* w1_qt;
+    uint8_t* w2_q;
+    uint8_t* w2_qt;
+    uint16_t* h;
+    uint8_t* g_q;
+    uint8_t* g_qt;
+    float* mean;
+    float* rstd;
+} fp8ln_mlp_ctx;
+
+/* Workspace kinds for fp8ln_workspace_size. */
+typedef enum {
+    FP8LN_OP_CAST_AMAX = 0,        /* a = rows, b = cols (column sums requested) */
+    FP8LN_OP_LAYERNORM_BWD = 1,    /* a = rows, b = hidden */
+    FP8LN_OP_LN_LINEAR_BWD = 2,    /* a = tokens, b = in_features, c = out_features */
+    FP8LN_OP_LN_MLP_BWD = 3        /* a = tokens, b = hidden, c = ffn */
+} fp8ln_op;
+
+/* ---- library ------------------------------------------------------------ */
+
+/* Text for a status code (static storage). */
+const char* fp8ln_status_string(int status);
+
+/* Message for the most recent failed call on this host thread ("" if none). */
+const char* fp8ln_last_error(void);
+
+/* Whether `device` can run this library: 1 = yes, 0 = no (reason written to
+ * `reason`, a host buffer of `reason_cap` bytes, may be NULL), < 0 = error.
+ * The counterpart of the tutorial's capability probe ([T] setup listing). */
+int fp8ln_check_support(int device, char* reason, size_t reason_cap);
+
+/* Bytes of workspace that op needs (see fp8ln_op); 0 for bad arguments. */
+size_t fp8ln_workspace_size(int32_t op, int64_t a, int64_t b, int64_t c);
+
+/* ---- delayed-scaling state ([T] benchmark listing; [G] "Playing with
+ *      lower-precision formats") ------------------------------------------ */
+
+/* Start a module's state: history = 0, scale = scale_inv = 1. */
+int fp8ln_meta_init(const fp8ln_recipe* recipe, const fp8ln_meta* meta, void* stream);
+
+/* Step start: for every slot, a = max over all history rows; if a is finite and
+ * > 0, scale = fp8_max / a / 2^margin (binary32 division, then exact scaling by
+ * 2^-margin) unless that is not a finite positive number; otherwise the scale is
+ * kept.  scale_inv = 1 / scale.  Then every history row moves down one row (the
+ * oldest falls off) and row 0 is set to zero; the step's kernels record their
+ * amaxes into row 0.  fp8_max is 448 for E4M3 slots and 57344 for E5M2 slots. */
+int fp8ln_scaling_update(const fp8ln_recipe* recipe, const fp8ln_meta* meta, void* stream);
+
+/* ---- fused LayerNorm + FP8 cast + amax ([T] setup listing, LayerNormLinear;
+ *      [G] "The building blocks") ------------------------------------------ */
+
+/* For each of `rows` rows of x (bf16 [rows][hidden]):
+ *   mean, var (biased) of the row; rstd = 1 / sqrt(var + recipe->ln_eps);
+ *   y = (x - mean) * rstd * gamma + beta         (gamma, beta: bf16 [hidden])
+ *   out[r][j] = encode(y * (*scale))              (uint8 [rows][hidden])
+ *   out_t[j][r] = out[r][j]                       (optional, may be NULL)
+ *   *amax = max(*amax, max |y|)  (NaN, if any y is NaN, wins)
+ *   mean[r], rstd[r] saved if the pointers are not NULL.
+ * amax usually points into history row 0 of the owning slot.  hidden must be a
+ * multiple of 8 and at most 8192; params_dtype must be FP8LN_DTYPE_BF16; rows may
+ * be 0 (nothing is launched). */
+int fp8ln_ln_cast_amax(const fp8ln_recipe* recipe, int64_t rows, int64_t hidden,
+                       int32_t params_dtype, const void* x, const void* gamma,
+                       const void* beta, int32_t fp8_dtype, const float* scale,
+                       float* amax, uint8_t* out, uint8_t* out_t, float* mean,
+                       float* rstd, void* stream);
+
+/* Cast a [rows][cols] tensor (bf16 or fp32, in_dtype) to FP8:
+ *   out[r][c] = encode(in[r][c] * (*scale)); out_t[c][r] = out[r][c] (optional);
+ *   *amax = max(*amax, max |in|); colsum[c] = sum over rows of in[r][c] (optional,
+ *   fp32, needs workspace of fp8ln_workspace_size(FP8LN_OP_CAST_AMAX, rows, cols)).
+ * cols must be a multiple of 16. */
+int fp8ln_cast_amax(int64_t rows, int64_t cols, int32_t in_dtype, const void* in,
+                    int32_t fp8_dtype, const float* scale, float* amax, uint8_t* out,
+                    uint8_t* out_t, float* colsum, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* Encode `count` consecutive binary32 bit patterns start, start+1, ... (mod 2^32)
+ * with the same device encoder the kernels use: out[i] = encode(float(start + i)).
+ * Lets a caller check the encoder against every binary32 input. */
+int fp8ln_encode_range(uint32_t start, int64_t count, int32_t fp8_dtype, uint8_t* out,
+                       void* stream);
+
+/* ---- FP8 GEMM ([G] "Playing with lower-precision formats"; [T] intro, FP8
+ *      tensor cores) ------------------------------------------------------- */
+
+/* out[m][n] = (sum_k A[m][k] * B[n][k]) * (*sinv_a) * (*sinv_b) + bias[n]
+ * A: uint8 [M][K] codes in a_dtype; B: uint8 [N][K] codes in b_dtype (both keep
+ * the contraction index last); bias: bf16 [N] or NULL; out_dtype FP8LN_DTYPE_BF16
+ * or FP8LN_DTYPE_F32 (out is [M][N]).  K and N must be multiples of 16. */
+int fp8ln_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* A, int32_t a_dtype,
+               const uint8_t* B, int32_t b_dtype, const float* sinv_a, const float* sinv_b,
+               const void* bias, int32_t out_dtype, void* out, void* stream);
+
+/* ---- LayerNorm backward ---------------------------------------------------- */
+
+/* With xhat = (x - mean) * rstd and g = dy * gamma per row:
+ *   dx = rstd * (g - mean_j g - xhat * mean_j(g * xhat))        (bf16 [rows][hidden])
+ *   dgamma = sum over rows of dy * xhat, dbeta = sum over rows of dy (fp32 [hidden])
+ * dy is fp32 [rows][hidden]; x, gamma bf16; mean, rstd fp32 [rows] as saved by the
+ * forward.  Workspace: fp8ln_workspace_size(FP8LN_OP_LAYERNORM_BWD, rows, hidden). */
+int fp8ln_layernorm_bwd(int64_t rows, int64_t hidden, const float* dy, const void* x,
+                        const float* mean, const float* rstd, const void* gamma, void* dx,
+                        float* dgamma, float* dbeta, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/* ---- LayerNormLinear ([T] setup listing: te.LayerNormLinear(H, 3*H)) ------- */
+
+/* out = LN(x) W^T + bias with FP8 operands, for x bf16 [tokens][in_features],
+ * W bf16 [out_features][in_features] (torch.nn.Linear layout), bias bf16
+ * [out_features] or NULL, out bf16 [tokens][out_features]:
+ *   ln_q = encode(LN(x) * scale[0]), amax -> history[0][0]
+ *   w_q  = encode(W * scale[1]),     amax -> history[0][1]
+ *   out  = (ln_q . w_q^T) * scale_inv[0] * scale_inv[1] + bias
+ * fwd is the module's forward state (2 slots, kind FORWARD), already advanced by
+ * fp8ln_scaling_update for this step.  ctx receives what the backward needs.
+ * in_features: multiple of 16, at most 8192; out_features: multiple of 16; when
+ * ctx->ln_qt is set tokens must be a multiple of 16. */
+int fp8ln_ln_linear_fwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_features,
+                        int64_t out_features, int32_t params_dtype, const void* x,
+                        const void* gamma, const void* beta, const void* weight,
+                        const void* bias, void* out, const fp8ln_meta* fwd,
+                        const fp8ln_linear_ctx* ctx, void* stream);
+
+/* Backward of fp8ln_ln_linear_fwd for the output gradient dy bf16
+ * [tokens][out_features]:
+ *   dy_q = encode(dy * bwd.scale[0]) in the backward format, amax -> bwd history
+ *   dLN = (dy_q . w_q) * bwd.scale_inv[0] * fwd.scale_inv[1]           (dgrad)
+ *   dW  = (dy_q^T . ln_q) * bwd.scale_inv[0] * fwd.scale_inv[0]        (wgrad)
+ *   dbias = column sums of dy; dx, dgamma, dbeta from the LayerNorm backward.
+ * dx bf16 [tokens][in]; dgamma, dbeta fp32 [in]; dweight fp32 [out][in]; dbias
+ * fp32 [out] or NULL.  ctx must hold ln_qt and w_qt.  tokens: multiple of 16.
+ * Workspace: fp8ln_workspace_size(FP8LN_OP_LN_LINEAR_BWD, tokens, in, out). */
+int fp8ln_ln_linear_bwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_features,
+                        int64_t out_features, int32_t params_dtype, const void* dy,
+                        const void* x, const void* gamma, const fp8ln_linear_ctx* ctx,
+                        const fp8ln_meta* fwd, const fp8ln_meta* bwd, void* dx,
+                        float* dgamma, float* dbeta, float* dweight, float* dbias,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- LayerNormMLP ([T] setup listing: te.LayerNormMLP(H, 4*H); [G] "The
+ *      building blocks") ------------------------------------------------------ */
+
+/* out = fc2(GELU(fc1(LN(x)))) with FP8 operands, GELU in its tanh form:
+ *   ln_q = encode(LN(x) * scale[0])                         amax -> slot 0
+ *   w1_q = encode(W1 * scale[1]), w2_q = encode(W2 * scale[3])  slots 1, 3
+ *   h = (ln_q . w1_q^T) * scale_inv[0] * scale_inv[1] + b1   (saved as bf16)
+ *   g = gelu(h) from the fp32 h; g_q = encode(g * scale[2])  amax -> slot 2
+ *   out = (g_q . w2_q^T) * scale_inv[2] * scale_inv[3] + b2
+ * x bf16 [tokens][hidden]; W1 bf16 [ffn][hidden]; b1 bf16 [ffn] or NULL;
+ * W2 bf16 [hidden][ffn]; b2 bf16 [hidden] or NULL; out bf16 [tokens][hidden].
+ * hidden: multiple of 16, at most 8192; ffn: multiple of 16; when transposes are
+ * requested in ctx, tokens must be a multiple of 16. */
+int fp8ln_ln_mlp_fwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t hidden,
+                     int64_t ffn, int32_t params_dtype, const void* x, const void* gamma,
+                     const void* beta, const void* w1, const void* b1, const void* w2,
+                     const void* b2, void* out, const fp8ln_meta* fwd,
+                     const fp8ln_mlp_ctx* ctx, void* stream);
+
+/* Backward of fp8ln_ln_mlp_fwd for dy bf16 [tokens][hidden]:
+ *   dy_q = encode(dy * bwd.scale[0]); db2 = column sums of dy
+ *   dH = (dy_q . w2_q) * bwd.scale_inv[0] * fwd.scale_inv[3] * gelu'(h)
+ *   dh_q = encode(dH * bwd.scale[1]); db1 = column sums of dH
+ *   dW2 = (dy_q^T . g_q) * bwd.scale_inv[0] * fwd.scale_inv[2]
+ *   dLN = (dh_q . w1_q) * bwd.scale_inv[1] * fwd.scale_inv[1]
+ *   dW1 = (dh_q^T . ln_q) * bwd.scale_inv[1] * fwd.scale_inv[0]
+ *   dx, dgamma, dbeta from the LayerNorm backward.
+ * dx bf16 [tokens][hidden]; dgamma, dbeta, db2 fp32 [hidden]; dw1 fp32
+ * [ffn][hidden]; db1 fp32 [ffn]; dw2 fp32 [hidden][ffn]; db1, db2 may be NULL.
+ * ctx must hold every transpose and h.  tokens: multiple of 16.
+ * Workspace: fp8ln_workspace_size(FP8LN_OP_LN_MLP_BWD, tokens, hidden, ffn). */
+int fp8ln_ln_mlp_bwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t hidden,
+                     int64_t ffn, int32_t params_dtype, const void* dy, const void* x,
+                     const void* gamma, const fp8ln_mlp_ctx* ctx, const fp8ln_meta* fwd,
+                     const fp8ln_meta* bwd, void* dx, float* dgamma, float* dbeta,
+                     float* dw1, float* db1, float* dw2, float* db2, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8LN_H */

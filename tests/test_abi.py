@@ -1,0 +1,123 @@
+"""The C-ABI library loads and exports every entry point include/fp8ln.h declares,
+and its host-side checks reject bad arguments before touching a device (CPU)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from fp8_delayed_scaling_row_amd import _abi
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "fp8ln.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp8ln_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_abi.LIB_PATH):
+        pytest.fail(f"{_abi.LIB_PATH} is not built (python -m fp8_delayed_scaling_row_amd.build)")
+    return _abi.lib()
+
+
+def test_header_declares_the_expected_entry_points():
+    names = declared_functions()
+    for required in ("fp8ln_ln_cast_amax", "fp8ln_scaling_update", "fp8ln_ln_linear_fwd",
+                     "fp8ln_ln_linear_bwd", "fp8ln_ln_mlp_fwd", "fp8ln_ln_mlp_bwd",
+                     "fp8ln_meta_init", "fp8ln_gemm", "fp8ln_cast_amax"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_binding_covers_every_declared_symbol():
+    assert sorted(_abi.SIGNATURES) == declared_functions()
+
+
+def test_status_strings(lib):
+    assert lib.fp8ln_status_string(0) == b"ok"
+    assert lib.fp8ln_status_string(-1) == b"invalid argument"
+    assert lib.fp8ln_status_string(-2) == b"unsupported"
+    assert lib.fp8ln_status_string(-3) == b"HIP error"
+
+
+def test_workspace_sizes_are_host_only_and_monotone(lib):
+    f = lib.fp8ln_workspace_size
+    assert f(_abi.OP_LN_LINEAR_BWD, 2048, 768, 2304) > 2048 * 768 * 4
+    assert f(_abi.OP_LN_MLP_BWD, 2048, 768, 3072) > f(_abi.OP_LN_LINEAR_BWD, 2048, 768, 2304)
+    assert f(_abi.OP_CAST_AMAX, 2048, 2304, 0) == 32 * 2304 * 4
+    assert f(99, 1, 1, 1) == 0 and f(_abi.OP_LN_LINEAR_BWD, 16, 16, 0) == 0
+
+
+def _recipe(**kw):
+    r = dict(format=_abi.FORMAT_HYBRID, amax_history_len=16, margin=0, ln_eps=1e-5)
+    r.update(kw)
+    return _abi.Recipe(r["format"], r["amax_history_len"], r["margin"], r["ln_eps"])
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(amax_history_len=0), _abi.FP8LN_ERR_INVALID_ARG),
+    (dict(amax_history_len=1025), _abi.FP8LN_ERR_INVALID_ARG),
+    (dict(format=7), _abi.FP8LN_ERR_INVALID_ARG),
+    (dict(margin=-1), _abi.FP8LN_ERR_INVALID_ARG),
+    (dict(ln_eps=0.0), _abi.FP8LN_ERR_INVALID_ARG),
+    (dict(ln_eps=float("nan")), _abi.FP8LN_ERR_INVALID_ARG),
+])
+def test_bad_recipe_is_rejected_before_any_launch(lib, bad, status):
+    r = _recipe(**bad)
+    m = _abi.MetaStruct(16, 16, 16, 1, 0)     # never dereferenced
+    assert lib.fp8ln_scaling_update(C.byref(r), C.byref(m), None) == status
+    assert lib.fp8ln_last_error()
+
+
+def test_unsupported_shapes_and_dtypes_are_rejected(lib):
+    r = _recipe()
+    p = C.c_void_p(256)   # never dereferenced: validation fails first
+    # hidden not a multiple of 8
+    s = lib.fp8ln_ln_cast_amax(C.byref(r), 4, 12, _abi.DTYPE_BF16, p, p, p, 0, p, p, p, None,
+                               None, None, None)
+    assert s == _abi.FP8LN_ERR_UNSUPPORTED
+    # float32 params are not a supported params_dtype
+    s = lib.fp8ln_ln_cast_amax(C.byref(r), 4, 16, _abi.DTYPE_F32, p, p, p, 0, p, p, p, None,
+                               None, None, None)
+    assert s == _abi.FP8LN_ERR_UNSUPPORTED
+    # GEMM with K not a multiple of 16
+    s = lib.fp8ln_gemm(16, 16, 24, p, 0, p, 0, p, p, None, _abi.DTYPE_BF16, p, None)
+    assert s == _abi.FP8LN_ERR_UNSUPPORTED
+    # negative sizes
+    s = lib.fp8ln_gemm(-1, 16, 16, p, 0, p, 0, p, p, None, _abi.DTYPE_BF16, p, None)
+    assert s == _abi.FP8LN_ERR_INVALID_ARG
+    # backward needs tokens % 16 == 0
+    mf = _abi.MetaStruct(256, 256, 256, 2, _abi.META_FORWARD)
+    mb = _abi.MetaStruct(256, 256, 256, 1, _abi.META_BACKWARD)
+    ctx = _abi.LinearCtxStruct(256, 256, 256, 256, 256, 256)
+    s = lib.fp8ln_ln_linear_bwd(C.byref(r), 20, 768, 2304, _abi.DTYPE_BF16, p, p, p,
+                                C.byref(ctx), C.byref(mf), C.byref(mb), p, p, p, p, None, p,
+                                1 << 30, None)
+    assert s == _abi.FP8LN_ERR_UNSUPPORTED
+    # wrong meta kind
+    s = lib.fp8ln_ln_linear_bwd(C.byref(r), 32, 768, 2304, _abi.DTYPE_BF16, p, p, p,
+                                C.byref(ctx), C.byref(mb), C.byref(mf), p, p, p, p, None, p,
+                                1 << 30, None)
+    assert s == _abi.FP8LN_ERR_INVALID_ARG
+    # misaligned pointer
+    s = lib.fp8ln_cast_amax(16, 16, _abi.DTYPE_BF16, C.c_void_p(257), 0, p, p, p, None, None,
+                            None, 0, None)
+    assert s == _abi.FP8LN_ERR_INVALID_ARG
+    assert b"aligned" in lib.fp8ln_last_error()
+
+
+def test_check_support_reports_a_reason_without_a_gpu(lib):
+    buf = C.create_string_buffer(128)
+    ok = lib.fp8ln_check_support(0, buf, len(buf))
+    assert ok in (0, 1)
+    if ok == 0:
+        assert buf.value   # a reason is given

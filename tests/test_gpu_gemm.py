@@ -1,0 +1,127 @@
+"""GPU parity: the FP8 MFMA GEMM (bit-exact on exactly summable inputs, layout
+pins, and the oracle tolerance on random operands and ragged shapes)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_delayed_scaling_row_amd import ops
+from parity import assert_gemm_close, to_np
+
+pytestmark = pytest.mark.gpu
+
+FMT = {ops.E4M3: oracle.E4M3, ops.E5M2: oracle.E5M2}
+PAIRS = [(ops.E4M3, ops.E4M3), (ops.E5M2, ops.E4M3), (ops.E4M3, ops.E5M2), (ops.E5M2, ops.E5M2)]
+
+
+def _scalar(v):
+    return torch.tensor([v], dtype=torch.float32, device="cuda")
+
+
+def int_codes(shape, fp8, seed, lim=8):
+    """Codes of small integers in [-lim, lim] (exact in both formats)."""
+    vals = np.random.default_rng(seed).integers(-lim, lim + 1, size=shape).astype(np.float64)
+    return oracle.fp8_encode(vals, FMT[fp8]), vals
+
+
+def finite_codes(shape, fp8, seed):
+    t = oracle.fp8_decode_table(FMT[fp8])
+    fin = np.array([c for c in range(256) if np.isfinite(t[c])], dtype=np.uint8)
+    return np.random.default_rng(seed).choice(fin, size=shape)
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+@pytest.mark.parametrize("fa,fb", PAIRS, ids=["e4m3xe4m3", "e5m2xe4m3", "e4m3xe5m2", "e5m2xe5m2"])
+@pytest.mark.parametrize("M,N,K", [(16, 16, 128), (128, 128, 256), (130, 144, 272), (1, 16, 16),
+                                   (257, 400, 64)])
+def test_small_integer_gemm_is_bit_exact(fa, fb, M, N, K):
+    """|a|, |b| <= 8 and K <= 272: every partial sum is an integer below 2^24, so
+    fp32 accumulation in any order is exact."""
+    a, av = int_codes((M, K), fa, M * 7 + K)
+    b, bv = int_codes((N, K), fb, N * 3 + K)
+    out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    ops.gemm(dev(a), fa, dev(b), fb, _scalar(1.0), _scalar(1.0), out)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy(), av @ bv.T)
+
+
+def test_layout_pins_permutation_and_single_entries():
+    M, N, K = 64, 128, 256
+    rng = np.random.default_rng(0)
+    a, av = int_codes((M, K), ops.E4M3, 1)
+    perm = rng.permutation(K)[:N]
+    b = np.zeros((N, K), dtype=np.uint8)
+    b[np.arange(N), perm] = 0x38                        # 1.0: column n picks k = perm[n]
+    out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    ops.gemm(dev(a), ops.E4M3, dev(b), ops.E4M3, _scalar(1.0), _scalar(1.0), out)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy(), av[:, perm])
+    # one non-zero product: A[i][k] = 2, B[j][k] = 3 -> C[i][j] = 6 only
+    for (i, j, k) in [(0, 0, 0), (63, 127, 255), (17, 33, 129), (5, 100, 31)]:
+        a = np.zeros((M, K), dtype=np.uint8)
+        b = np.zeros((N, K), dtype=np.uint8)
+        a[i, k] = oracle.fp8_encode(2.0, oracle.E4M3)
+        b[j, k] = oracle.fp8_encode(3.0, oracle.E4M3)
+        ops.gemm(dev(a), ops.E4M3, dev(b), ops.E4M3, _scalar(1.0), _scalar(1.0), out)
+        torch.cuda.synchronize()
+        expect = np.zeros((M, N))
+        expect[i, j] = 6.0
+        np.testing.assert_array_equal(out.cpu().numpy(), expect)
+
+
+@pytest.mark.parametrize("fa,fb", PAIRS[:3], ids=["e4m3xe4m3", "e5m2xe4m3", "e4m3xe5m2"])
+@pytest.mark.parametrize("M,N,K,out_bf16", [
+    (256, 2304, 768, True),       # LayerNormLinear forward, batch 8 x 32
+    (2048, 768, 3072, True),      # fc2 of the LayerNormMLP
+    (333, 272, 528, True),        # ragged M, several tiles
+    (2304, 768, 2048, False),     # wgrad shape
+    (77, 48, 16, False),
+])
+def test_random_gemm_within_tolerance(fa, fb, M, N, K, out_bf16):
+    a = finite_codes((M, K), fa, 11 + M)
+    b = finite_codes((N, K), fb, 13 + N)
+    sa, sb = np.float32(1.0 / 37.0), np.float32(1.0 / 1536.0)
+    bias = None
+    bias_bits = None
+    if out_bf16:
+        bias_bits = oracle.f64_to_bf16_bits(np.random.default_rng(3).normal(size=N) * 50.0)
+        bias = torch.from_numpy(bias_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    out = torch.empty((M, N), dtype=torch.bfloat16 if out_bf16 else torch.float32, device="cuda")
+    ops.gemm(dev(a), fa, dev(b), fb, _scalar(float(sa)), _scalar(float(sb)), out, bias)
+    torch.cuda.synchronize()
+    ref = oracle.fp8_gemm_tn(a, FMT[fa], b, FMT[fb], sa, sb,
+                             None if bias_bits is None else oracle.bf16_to_f64(bias_bits))
+    # bf16 output rounding alone is 2^-9 relative per element
+    assert_gemm_close(to_np(out), ref, alarm=5e-3 if out_bf16 else 1e-5)
+
+
+def test_k_zero_gives_bias_and_m_zero_is_a_no_op():
+    N = 32
+    bias_bits = oracle.f64_to_bf16_bits(np.arange(N, dtype=np.float64))
+    bias = torch.from_numpy(bias_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    out = torch.full((4, N), 9.0, dtype=torch.bfloat16, device="cuda")
+    a = torch.empty((4, 0), dtype=torch.uint8, device="cuda")
+    b = torch.empty((N, 0), dtype=torch.uint8, device="cuda")
+    ops.gemm(a, ops.E4M3, b, ops.E4M3, _scalar(1.0), _scalar(1.0), out, bias)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_np(out), np.tile(np.arange(N, dtype=np.float64), (4, 1)))
+    out0 = torch.empty((0, N), dtype=torch.float32, device="cuda")
+    ops.gemm(torch.empty((0, 64), dtype=torch.uint8, device="cuda"), ops.E4M3,
+             torch.zeros((N, 64), dtype=torch.uint8, device="cuda"), ops.E4M3, _scalar(1.0),
+             _scalar(1.0), out0)
+    torch.cuda.synchronize()
+
+
+def test_gemm_is_deterministic():
+    M, N, K = 512, 768, 2048
+    a = dev(finite_codes((M, K), ops.E4M3, 1))
+    b = dev(finite_codes((N, K), ops.E4M3, 2))
+    o1 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    o2 = torch.empty_like(o1)
+    ops.gemm(a, ops.E4M3, b, ops.E4M3, _scalar(0.5), _scalar(0.25), o1)
+    ops.gemm(a, ops.E4M3, b, ops.E4M3, _scalar(0.5), _scalar(0.25), o2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)

@@ -1,0 +1,191 @@
+"""GPU parity: fused LayerNorm + FP8 cast + amax, the tensor cast (weights and
+gradients, with transposes and column sums) and the LayerNorm backward."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_delayed_scaling_row_amd import inputs, ops
+from parity import (assert_vector_close, compare_codes, ln_window, to_np, to_np_bits)
+
+pytestmark = pytest.mark.gpu
+
+FMT = {ops.E4M3: oracle.E4M3, ops.E5M2: oracle.E5M2}
+
+
+def _scalar(v):
+    return torch.tensor([v], dtype=torch.float32, device="cuda")
+
+
+def _oracle_ln(x_bits, g_bits, b_bits, eps, scale, fmt):
+    x = oracle.bf16_to_f64(x_bits)
+    g = oracle.bf16_to_f64(g_bits)
+    b = oracle.bf16_to_f64(b_bits)
+    y, mean, rstd = oracle.layernorm_fwd(x, g, b, eps)
+    gx = (x - mean[:, None]) * rstd[:, None] * g
+    return y, mean, rstd, gx, b
+
+
+@pytest.mark.parametrize("rows,hidden,fp8,with_t,scale", [
+    (1, 8, ops.E4M3, False, 1.0),
+    (37, 768, ops.E4M3, False, 448.0 / 5.3),
+    (256, 768, ops.E4M3, True, 448.0 / 5.3),
+    (300, 2048, ops.E4M3, False, 74.0),
+    (48, 1024, ops.E5M2, True, 5000.0),
+    (64, 8192, ops.E4M3, False, 60.0),
+    (16, 4096, ops.E4M3, True, 1.0),
+    (0, 768, ops.E4M3, False, 1.0),
+])
+def test_ln_cast_amax_matches_oracle(rows, hidden, fp8, with_t, scale):
+    wl = f"ln/{rows}x{hidden}"
+    x = inputs.spiky_normal_bf16((rows, hidden), inputs.seed_for(wl, "x"), drift=1.5)
+    g, b = inputs.layernorm_params(hidden, wl)
+    xd, gd, bd = x.cuda(), g.cuda(), b.cuda()
+    out = torch.empty((rows, hidden), dtype=torch.uint8, device="cuda")
+    out_t = torch.empty((hidden, rows), dtype=torch.uint8, device="cuda") if with_t else None
+    mean = torch.empty(rows, dtype=torch.float32, device="cuda")
+    rstd = torch.empty(rows, dtype=torch.float32, device="cuda")
+    amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    r = ops.Recipe()
+    ops.ln_cast_amax(r, xd, gd, bd, fp8, _scalar(scale), amax.data_ptr(), out, out_t, mean, rstd)
+    torch.cuda.synchronize()
+    if rows == 0:
+        assert amax.item() == 0.0
+        return
+    fmt = FMT[fp8]
+    y, om, orstd, gx, beta = _oracle_ln(to_np_bits(x), to_np_bits(g), to_np_bits(b),
+                                         float(np.float32(r.ln_eps)), scale, fmt)
+    sc = float(np.float32(scale))
+    exact = y * sc
+    stats = compare_codes(out.cpu().numpy(), exact, fmt, ln_window(gx, beta, sc, exact))
+    oamax = np.float32(np.abs(y).max())
+    assert abs(float(amax.item()) - float(oamax)) <= 1e-6 * float(oamax), (amax.item(), oamax)
+    np.testing.assert_allclose(mean.cpu().numpy(), om, rtol=1e-5, atol=1e-6)
+    np.testing.assert_allclose(rstd.cpu().numpy(), orstd, rtol=1e-5)
+    if with_t:
+        assert torch.equal(out_t, out.t().contiguous())
+    print(f"ln_cast_amax {rows}x{hidden}: {stats}")
+
+
+def test_ln_cast_amax_nan_and_inf_rows():
+    rows, hidden = 32, 256
+    x = inputs.normal_bf16((rows, hidden), inputs.seed_for("ln-nan", "x"))
+    x[3, 17] = float("nan")
+    x[9, 0] = float("inf")
+    g, b = inputs.layernorm_params(hidden, "ln-nan")
+    out = torch.empty((rows, hidden), dtype=torch.uint8, device="cuda")
+    amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    ops.ln_cast_amax(ops.Recipe(), x.cuda(), g.cuda(), b.cuda(), ops.E4M3, _scalar(2.0),
+                     amax.data_ptr(), out)
+    torch.cuda.synchronize()
+    q = out.cpu().numpy()
+    assert np.all(q[3] == 0x7F) and np.all(q[9] == 0x7F)   # whole rows become NaN
+    assert np.isnan(amax.item())
+    y, *_ = _oracle_ln(to_np_bits(x), to_np_bits(g), to_np_bits(b), float(np.float32(1e-5)),
+                       2.0, oracle.E4M3)
+    ok = np.ones(rows, bool)
+    ok[[3, 9]] = False
+    np.testing.assert_array_equal(q[~ok], oracle.fp8_encode(y[~ok] * 2.0, oracle.E4M3))
+
+
+def test_ln_cast_amax_full_size_sampled():
+    """65536 x 2048 with 0.1 % spikes and drift 4: every row's amax, and the
+    codes of 512 sampled rows plus the first and last rows."""
+    rows, hidden = 65536, 2048
+    x = inputs.spiky_normal_bf16((rows, hidden), inputs.seed_for("ln-full", "x"), drift=4.0,
+                                 device="cuda")
+    g, b = inputs.layernorm_params(hidden, "ln-full", device="cuda")
+    out = torch.empty((rows, hidden), dtype=torch.uint8, device="cuda")
+    amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    scale = 448.0 / 60.0
+    ops.ln_cast_amax(ops.Recipe(amax_history_len=1024, format=ops.FORMAT_E4M3), x, g, b,
+                     ops.E4M3, _scalar(scale), amax.data_ptr(), out)
+    torch.cuda.synchronize()
+    xb, gb, bb = to_np_bits(x), to_np_bits(g), to_np_bits(b)
+    eps = float(np.float32(1e-5))
+    oamax = 0.0
+    for r0 in range(0, rows, 8192):
+        y, *_ = _oracle_ln(xb[r0:r0 + 8192], gb, bb, eps, scale, oracle.E4M3)
+        oamax = max(oamax, float(np.abs(y).max()))
+    oamax = float(np.float32(oamax))
+    assert abs(amax.item() - oamax) <= 1e-6 * oamax
+    sample = np.unique(np.concatenate([[0, rows - 1],
+                                       np.random.default_rng(1).integers(0, rows, 512)]))
+    y, _, _, gx, beta = _oracle_ln(xb[sample], gb, bb, eps, scale, oracle.E4M3)
+    sc = float(np.float32(scale))
+    q = out[torch.from_numpy(sample).cuda()].cpu().numpy()
+    stats = compare_codes(q, y * sc, oracle.E4M3, ln_window(gx, beta, sc, y * sc))
+    print(f"full-size sample: {stats}")
+
+
+@pytest.mark.parametrize("rows,cols,in_f32,fp8,with_t,with_sum", [
+    (16, 16, False, ops.E4M3, True, True),
+    (2304, 768, False, ops.E4M3, True, False),
+    (2048, 2304, False, ops.E5M2, True, True),
+    (48, 80, False, ops.E4M3, True, True),
+    (100, 48, True, ops.E5M2, False, True),
+    (256, 3072, True, ops.E5M2, True, True),
+    (0, 64, False, ops.E4M3, False, True),
+])
+def test_cast_amax_matches_oracle(rows, cols, in_f32, fp8, with_t, with_sum):
+    wl = f"cast/{rows}x{cols}"
+    if in_f32:
+        xf = torch.randn((rows, cols), generator=torch.Generator().manual_seed(5)) * 3e-4
+        x = xf.to(torch.float32)
+        xv = x.numpy().astype(np.float64)
+    else:
+        x = inputs.normal_bf16((rows, cols), inputs.seed_for(wl, "x"), std=0.02)
+        xv = oracle.bf16_to_f64(to_np_bits(x))
+    xd = x.cuda()
+    out = torch.empty((rows, cols), dtype=torch.uint8, device="cuda")
+    out_t = torch.empty((cols, rows), dtype=torch.uint8, device="cuda") if with_t else None
+    colsum = torch.full((cols,), 7.0, dtype=torch.float32, device="cuda") if with_sum else None
+    amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    scale = float(np.float32(448.0 / 0.093 if fp8 == ops.E4M3 else 57344.0 / 0.0011))
+    ops.cast_amax(xd, fp8, _scalar(scale), amax.data_ptr(), out, out_t, colsum)
+    torch.cuda.synchronize()
+    if with_sum:
+        ref = xv.sum(axis=0)
+        got = colsum.cpu().numpy()
+        bound = 1e-5 * np.abs(xv).sum(axis=0) + 1e-30
+        assert np.all(np.abs(got - ref) <= bound), np.abs(got - ref).max()
+    if rows == 0:
+        assert amax.item() == 0.0
+        return
+    fmt = FMT[fp8]
+    exact = xv * scale
+    stats = compare_codes(out.cpu().numpy(), exact, fmt, 1e-6 * np.abs(exact))
+    assert np.float32(amax.item()) == np.float32(np.abs(xv).max())     # exact for these inputs
+    if with_t:
+        assert torch.equal(out_t, out.t().contiguous())
+    print(f"cast {rows}x{cols}: {stats}")
+
+
+@pytest.mark.parametrize("rows,hidden", [(1, 8), (37, 768), (2048, 768), (513, 2048),
+                                         (64, 4096), (0, 256)])
+def test_layernorm_bwd_matches_oracle(rows, hidden):
+    wl = f"lnb/{rows}x{hidden}"
+    x = inputs.normal_bf16((rows, hidden), inputs.seed_for(wl, "x"))
+    g, b = inputs.layernorm_params(hidden, wl)
+    dy = inputs.normal_bf16((rows, hidden), inputs.seed_for(wl, "dy"), std=1e-3).float()
+    xv = oracle.bf16_to_f64(to_np_bits(x))
+    gv = oracle.bf16_to_f64(to_np_bits(g))
+    _, mean, rstd = oracle.layernorm_fwd(xv, gv, oracle.bf16_to_f64(to_np_bits(b)),
+                                         float(np.float32(1e-5)))
+    mean32, rstd32 = mean.astype(np.float32), rstd.astype(np.float32)
+    dx = torch.empty((rows, hidden), dtype=torch.bfloat16, device="cuda")
+    dgamma = torch.empty(hidden, dtype=torch.float32, device="cuda")
+    dbeta = torch.empty(hidden, dtype=torch.float32, device="cuda")
+    ops.layernorm_bwd(dy.cuda(), x.cuda(), torch.from_numpy(mean32).cuda(),
+                      torch.from_numpy(rstd32).cuda(), g.cuda(), dx, dgamma, dbeta)
+    torch.cuda.synchronize()
+    odx, odg, odb = oracle.layernorm_bwd(dy.numpy().astype(np.float64), xv, gv,
+                                         mean32.astype(np.float64), rstd32.astype(np.float64))
+    if rows == 0:
+        assert torch.all(dgamma == 0) and torch.all(dbeta == 0)
+        return
+    gdx = to_np(dx)
+    norms = np.linalg.norm(odx, axis=1)
+    assert np.all(np.abs(gdx - odx).max(axis=1) <= 1e-2 * norms + 1e-30)   # bf16 output
+    assert_vector_close(dgamma.cpu().numpy(), odg, 1e-5, "dgamma")
+    assert_vector_close(dbeta.cpu().numpy(), odb, 1e-5, "dbeta")

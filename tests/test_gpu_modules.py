@@ -1,0 +1,282 @@
+"""GPU parity of the fused modules through the C ABI, step by step against the
+oracle's own chain on the same seeded inputs.
+
+Shapes follow the pages' GPT-style workload: hidden 768 with QKV width 2304 and
+FFN 3072 at 8 x 32 and 8 x 256 tokens, plus the hidden-2048 / FFN-8192 scale-up
+at 64 x 256 tokens.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_delayed_scaling_row_amd import inputs, ops
+from parity import (assert_gemm_close, assert_vector_close, compare_codes, ln_window, to_np,
+                    to_np_bits)
+
+pytestmark = pytest.mark.gpu
+
+OFMT = {ops.FORMAT_E4M3: oracle.FORMAT_E4M3, ops.FORMAT_HYBRID: oracle.FORMAT_HYBRID,
+        ops.FORMAT_E5M2: oracle.FORMAT_E5M2}
+EPS = float(np.float32(1e-5))
+U32 = 2.0 ** -24
+
+
+def orecipe(r: ops.Recipe):
+    return oracle.Recipe(format=OFMT[r.format], amax_history_len=r.amax_history_len,
+                         margin=r.margin, ln_eps=r.ln_eps)
+
+
+def f32bits(a):
+    return np.asarray(a, dtype=np.float32).view(np.uint32)
+
+
+def check_meta(gpu: ops.Meta, om: oracle.Meta, exact_slots, rel_slots, rel=1e-6, what=""):
+    gh = gpu.history.cpu().numpy()
+    gs = gpu.scale.cpu().numpy()
+    for s in exact_slots:
+        np.testing.assert_array_equal(f32bits(gh[:, s]), f32bits(om.history[:, s]),
+                                      err_msg=f"{what} history slot {s}")
+        np.testing.assert_array_equal(f32bits(gs[s]), f32bits(om.scale[s]),
+                                      err_msg=f"{what} scale slot {s}")
+    for s in rel_slots:
+        np.testing.assert_allclose(gh[:, s], om.history[:, s], rtol=rel, atol=0,
+                                   err_msg=f"{what} history slot {s}")
+        np.testing.assert_allclose(gs[s], om.scale[s], rtol=rel, err_msg=f"{what} scale {s}")
+
+
+def ln_parts(x_bits, g_bits, b_bits):
+    x = oracle.bf16_to_f64(x_bits)
+    g = oracle.bf16_to_f64(g_bits)
+    y, mean, rstd = oracle.layernorm_fwd(x, g, oracle.bf16_to_f64(b_bits), EPS)
+    return (x - mean[:, None]) * rstd[:, None] * g, oracle.bf16_to_f64(b_bits)
+
+
+def scale_slack(gpu_meta, om, slot, exact):
+    """Extra window for a delayed scale that differs from the oracle's by a few
+    ulps (its amax history came from an fp32 LayerNorm or GEMM)."""
+    gs = float(gpu_meta.scale[slot].item())
+    return abs(gs / float(om.scale[slot]) - 1.0) * np.abs(exact)
+
+
+# ---- LayerNormLinear -----------------------------------------------------------
+
+def run_linear(recipe, M, K, N, steps, workload, backward, check_every=1):
+    dev = "cuda"
+    g, b = inputs.layernorm_params(K, workload)
+    w = inputs.linear_weight(N, K, workload, "weight")
+    bias = inputs.normal_bf16((N,), inputs.seed_for(workload, "bias"), std=0.1)
+    gd, bd, wd, biasd = g.to(dev), b.to(dev), w.to(dev), bias.to(dev)
+    mf, mb = ops.linear_metas(recipe)
+    ctx = ops.LinearCtx(M, K, N, training=backward)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    dgamma = torch.empty(K, dtype=torch.float32, device=dev)
+    dbeta = torch.empty(K, dtype=torch.float32, device=dev)
+    dw = torch.empty((N, K), dtype=torch.float32, device=dev)
+    dbias = torch.empty(N, dtype=torch.float32, device=dev)
+    orc = orecipe(recipe)
+    omf, omb = oracle.linear_fwd_meta(orc), oracle.linear_bwd_meta(orc)
+    ffmt, bfmt = oracle.fwd_format(orc), oracle.bwd_format(orc)
+    gbits, bbits, wbits, biasbits = map(to_np_bits, (g, b, w, bias))
+    for step in range(steps):
+        x = inputs.normal_bf16((M, K), inputs.seed_for(workload, "x", step))
+        xd = x.to(dev)
+        ops.scaling_update(recipe, mf)
+        ops.ln_linear_fwd(recipe, xd, gd, bd, wd, biasd, out, mf, ctx)
+        oracle.scaling_update(omf, orc.margin)
+        xbits = to_np_bits(x)
+        oout, octx = oracle.ln_linear_fwd(orc, omf, xbits, gbits, bbits, wbits, biasbits)
+        if backward:
+            dy = inputs.normal_bf16((M, N), inputs.seed_for(workload, "dy", step), std=1e-3)
+            ops.scaling_update(recipe, mb)
+            ops.ln_linear_bwd(recipe, dy.to(dev), xd, gd, ctx, mf, mb, dx, dgamma, dbeta, dw,
+                              dbias)
+            oracle.scaling_update(omb, orc.margin)
+            og = oracle.ln_linear_bwd(orc, omf, omb, to_np_bits(dy), octx, xbits, gbits)
+        torch.cuda.synchronize()
+        if step % check_every and step != steps - 1:
+            continue
+        tag = f"step {step}"
+        assert_gemm_close(to_np(out), oout, what=f"{tag} out")
+        gx, beta = ln_parts(xbits, gbits, bbits)
+        s0 = float(omf.scale[0])
+        exact = octx["y"] * s0
+        compare_codes(ctx.ln_q.cpu().numpy(), exact, ffmt,
+                      ln_window(gx, beta, s0, exact) + scale_slack(mf, omf, 0, exact))
+        wex = oracle.bf16_to_f64(wbits) * float(omf.scale[1])
+        compare_codes(ctx.w_q.cpu().numpy(), wex, ffmt, 1e-6 * np.abs(wex))
+        if backward:
+            assert torch.equal(ctx.ln_qt, ctx.ln_q.t().contiguous())
+            assert torch.equal(ctx.w_qt, ctx.w_q.t().contiguous())
+        check_meta(mf, omf, exact_slots=[1], rel_slots=[0], what=f"{tag} fwd")
+        if backward:
+            check_meta(mb, omb, exact_slots=[0], rel_slots=[], what=f"{tag} bwd")
+            assert_gemm_close(to_np(dx), og["dx"], alarm=1e-2, what=f"{tag} dx")
+            assert_gemm_close(dw.cpu().numpy(), og["dw"], alarm=5e-3, what=f"{tag} dW")
+            assert_vector_close(dgamma.cpu().numpy(), og["dgamma"], 2e-3, f"{tag} dgamma")
+            assert_vector_close(dbeta.cpu().numpy(), og["dbeta"], 2e-3, f"{tag} dbeta")
+            assert_vector_close(dbias.cpu().numpy(), og["dbias"], 1e-5, f"{tag} dbias")
+
+
+def test_ln_linear_fwd_module_tour_16_steps():
+    """LayerNormLinear(768, 2304) on 8 x 32 tokens, HYBRID, history 16, 16 steps
+    with fresh inputs so the history fills."""
+    run_linear(ops.Recipe(format=ops.FORMAT_HYBRID, amax_history_len=16), 256, 768, 2304, 16,
+               "c0", backward=False)
+
+
+@pytest.mark.parametrize("fmt", [ops.FORMAT_HYBRID, ops.FORMAT_E4M3])
+def test_ln_linear_fwd_bwd_2048_tokens(fmt):
+    run_linear(ops.Recipe(format=fmt, amax_history_len=16), 2048, 768, 2304, 3, f"c3/{fmt}",
+               backward=True)
+
+
+@pytest.mark.parametrize("M,K,N", [(48, 64, 80), (16, 16, 16), (144, 256, 400)])
+def test_ln_linear_small_and_ragged(M, K, N):
+    run_linear(ops.Recipe(amax_history_len=4, margin=1), M, K, N, 5, f"lin/{M}/{K}/{N}",
+               backward=True)
+
+
+def test_ln_linear_fwd_ragged_tokens_forward_only():
+    run_linear(ops.Recipe(), 37, 768, 2304, 2, "lin-ragged", backward=False)
+
+
+# ---- LayerNormMLP --------------------------------------------------------------
+
+def gelu_code_window(ln_q, w1_q, fmt, alpha, h, scale, K):
+    """GEMM-fed window for the GELU output's codes: fp32 accumulation error of h
+    (serial bound K u sum |a b|), the epilogue's roundings, the fp32 GELU."""
+    a = oracle.fp8_decode(ln_q & 0x7F, fmt)
+    b = oracle.fp8_decode(w1_q & 0x7F, fmt)
+    abs_sum = a @ b.T
+    dh = K * U32 * float(alpha) * abs_sum + 4 * U32 * np.abs(h)
+    dg = np.abs(oracle.gelu_tanh_grad(h)) * dh + 1e-6 * np.abs(oracle.gelu_tanh(h)) \
+        + 2e-7 * np.abs(h)
+    return float(scale) * dg
+
+
+def run_mlp(recipe, M, H, F, steps, workload, backward, sample_rows=None):
+    dev = "cuda"
+    g, b = inputs.layernorm_params(H, workload)
+    w1 = inputs.linear_weight(F, H, workload, "w1")
+    w2 = inputs.linear_weight(H, F, workload, "w2")
+    b1 = inputs.normal_bf16((F,), inputs.seed_for(workload, "b1"), std=0.1)
+    b2 = inputs.normal_bf16((H,), inputs.seed_for(workload, "b2"), std=0.1)
+    gd, bd, w1d, w2d, b1d, b2d = (t.to(dev) for t in (g, b, w1, w2, b1, b2))
+    mf, mb = ops.mlp_metas(recipe)
+    ctx = ops.MlpCtx(M, H, F, training=True)
+    out = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    dx = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    dgamma = torch.empty(H, dtype=torch.float32, device=dev)
+    dbeta = torch.empty(H, dtype=torch.float32, device=dev)
+    dw1 = torch.empty((F, H), dtype=torch.float32, device=dev)
+    dw2 = torch.empty((H, F), dtype=torch.float32, device=dev)
+    db1 = torch.empty(F, dtype=torch.float32, device=dev)
+    db2 = torch.empty(H, dtype=torch.float32, device=dev)
+    orc = orecipe(recipe)
+    omf, omb = oracle.mlp_fwd_meta(orc), oracle.mlp_bwd_meta(orc)
+    ffmt = oracle.fwd_format(orc)
+    gbits, bbits, w1bits, w2bits, b1bits, b2bits = map(to_np_bits, (g, b, w1, w2, b1, b2))
+    rows = slice(None) if sample_rows is None else sample_rows
+    for step in range(steps):
+        x = inputs.normal_bf16((M, H), inputs.seed_for(workload, "x", step), device=dev)
+        ops.scaling_update(recipe, mf)
+        ops.ln_mlp_fwd(recipe, x, gd, bd, w1d, b1d, w2d, b2d, out, mf, ctx)
+        xbits = to_np_bits(x)
+        oracle.scaling_update(omf, orc.margin)
+        oout, octx = oracle.ln_mlp_fwd(orc, omf, xbits, gbits, bbits, w1bits, b1bits, w2bits,
+                                       b2bits)
+        if backward:
+            dy = inputs.normal_bf16((M, H), inputs.seed_for(workload, "dy", step), std=1e-3,
+                                    device=dev)
+            ops.scaling_update(recipe, mb)
+            ops.ln_mlp_bwd(recipe, dy, x, gd, ctx, mf, mb, dx, dgamma, dbeta, dw1, db1, dw2, db2)
+            oracle.scaling_update(omb, orc.margin)
+            og = oracle.ln_mlp_bwd(orc, omf, omb, to_np_bits(dy), octx, xbits, gbits)
+        torch.cuda.synchronize()
+        tag = f"step {step}"
+        assert_gemm_close(to_np(out)[rows], oout[rows], what=f"{tag} out")
+        assert_gemm_close(to_np(ctx.h)[rows], octx["h"][rows], what=f"{tag} h")
+        gx, beta = ln_parts(xbits[rows], gbits, bbits)
+        s0 = float(omf.scale[0])
+        exact = octx["y"][rows] * s0
+        compare_codes(ctx.ln_q.cpu().numpy()[rows], exact, ffmt,
+                      ln_window(gx, beta, s0, exact) + scale_slack(mf, omf, 0, exact))
+        alpha = np.float32(omf.scale_inv[0]) * np.float32(omf.scale_inv[1])
+        s2 = float(omf.scale[2])
+        gq = ctx.g_q.cpu().numpy()[rows]
+        win = gelu_code_window(octx["ln_q"][rows], octx["w1_q"], ffmt, alpha, octx["h"][rows],
+                               s2, H)
+        stats = compare_codes(gq, octx["g"][rows] * s2, ffmt,
+                              win + scale_slack(mf, omf, 2, octx["g"][rows] * s2))
+        assert torch.equal(ctx.g_qt, ctx.g_q.t().contiguous())
+        check_meta(mf, omf, exact_slots=[1, 3], rel_slots=[0], what=f"{tag} fwd")
+        np.testing.assert_allclose(mf.history.cpu().numpy()[:, 2], omf.history[:, 2], rtol=1e-4)
+        if backward:
+            check_meta(mb, omb, exact_slots=[0], rel_slots=[1], rel=5e-3, what=f"{tag} bwd")
+            assert_gemm_close(to_np(dx)[rows], og["dx"][rows], alarm=1e-2, what=f"{tag} dx")
+            assert_gemm_close(dw1.cpu().numpy(), og["dw1"], alarm=1e-2, what=f"{tag} dW1")
+            assert_gemm_close(dw2.cpu().numpy(), og["dw2"], alarm=5e-3, what=f"{tag} dW2")
+            assert_vector_close(db1.cpu().numpy(), og["db1"], 1e-3, f"{tag} db1")
+            assert_vector_close(db2.cpu().numpy(), og["db2"], 1e-5, f"{tag} db2")
+            assert_vector_close(dgamma.cpu().numpy(), og["dgamma"], 5e-3, f"{tag} dgamma")
+            assert_vector_close(dbeta.cpu().numpy(), og["dbeta"], 5e-3, f"{tag} dbeta")
+        print(f"{workload} {tag}: g codes {stats}")
+
+
+def test_ln_mlp_fwd_2048_tokens():
+    """LayerNormMLP 768 -> 3072 -> 768 on 8 x 256 tokens, E4M3 on both GEMM
+    inputs with separate histories, history 16."""
+    run_mlp(ops.Recipe(format=ops.FORMAT_E4M3, amax_history_len=16), 2048, 768, 3072, 4,
+            "c2", backward=False)
+
+
+@pytest.mark.parametrize("fmt", [ops.FORMAT_HYBRID, ops.FORMAT_E4M3])
+def test_ln_mlp_fwd_bwd_small(fmt):
+    run_mlp(ops.Recipe(format=fmt, amax_history_len=8), 256, 256, 1024, 3, f"mlp/{fmt}",
+            backward=True)
+
+
+def test_ln_mlp_ragged_tiles():
+    run_mlp(ops.Recipe(), 48, 80, 144, 3, "mlp-ragged", backward=True)
+
+
+@pytest.mark.parametrize("fmt", [ops.FORMAT_HYBRID, ops.FORMAT_E4M3])
+def test_ln_mlp_full_layer_sampled(fmt):
+    """One scale-up layer (16384 tokens, 2048 -> 8192 -> 2048), history 1024,
+    two steps; row-wise results compared on 64 sampled tokens, everything that
+    reduces over tokens (amaxes, weight gradients, bias gradients) in full."""
+    rows = np.unique(np.concatenate([[0, 16383],
+                                     np.random.default_rng(2).integers(0, 16384, 62)]))
+    run_mlp(ops.Recipe(format=fmt, amax_history_len=1024), 16384, 2048, 8192, 2, f"c4/{fmt}",
+            backward=True, sample_rows=rows)
+
+
+def test_modules_are_deterministic():
+    r = ops.Recipe()
+    M, H, F = 512, 768, 3072
+    x = inputs.normal_bf16((M, H), 1, device="cuda")
+    g, b = inputs.layernorm_params(H, "det", device="cuda")
+    w1 = inputs.linear_weight(F, H, "det", "w1", device="cuda")
+    w2 = inputs.linear_weight(H, F, "det", "w2", device="cuda")
+    dy = inputs.normal_bf16((M, H), 2, std=1e-3, device="cuda")
+    results = []
+    for _ in range(2):
+        mf, mb = ops.mlp_metas(r)
+        ctx = ops.MlpCtx(M, H, F)
+        out = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+        dx = torch.empty_like(out)
+        grads = [torch.empty(H, device="cuda"), torch.empty(H, device="cuda"),
+                 torch.empty((F, H), device="cuda"), torch.empty(F, device="cuda"),
+                 torch.empty((H, F), device="cuda"), torch.empty(H, device="cuda")]
+        for _step in range(2):
+            ops.scaling_update(r, mf)
+            ops.ln_mlp_fwd(r, x, g, b, w1, None, w2, None, out, mf, ctx)
+            ops.scaling_update(r, mb)
+            ops.ln_mlp_bwd(r, dy, x, g, ctx, mf, mb, dx, *grads)
+        torch.cuda.synchronize()
+        results.append([out.clone(), dx.clone(), mf.history.clone(), mb.history.clone()] +
+                       [t.clone() for t in grads])
+    for a, c in zip(*results):
+        assert torch.equal(a, c)
