@@ -44,6 +44,10 @@ def parse():
     p.add_argument("--quick", action="store_true", help="headline workload only")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only", default=None, help="run one named workload")
+    p.add_argument("--profile-ln", type=int, default=0, metavar="N",
+                   help="counter run: N headline launches plus 3 plain 1 GiB copies")
+    p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="write the counter summary of a --profile-ln run to profiles/")
     return p.parse_args()
 
 
@@ -133,6 +137,89 @@ def bench_ln_cast(torch, ops, inputs, steps, warmup):
     bytes_step = rows * hidden * 3 + rows * 8
     return dict(rows=rows, hidden=hidden, ms=ms, kernel_ms=kernel_ms, bytes=bytes_step,
                 scale=float(meta.scale[0].item()))
+
+
+COPY_BYTES = 1 << 30     # each calibration copy reads and writes this many bytes
+
+
+def profile_ln(torch, ops, inputs, n):
+    """Launches for a rocprofv3 --pmc run: n headline LayerNorm+cast launches and
+    three elementwise copies (neg) of a 1 GiB bf16 tensor, a plain kernel of known
+    traffic to calibrate FETCH_SIZE / WRITE_SIZE."""
+    rows, hidden = 65536, 2048
+    recipe = ops.Recipe(format=ops.FORMAT_E4M3, amax_history_len=1024)
+    wl = "ln_cast_amax_65536x2048"
+    xs = [inputs.spiky_normal_bf16((rows, hidden), inputs.seed_for(wl, "x", s),
+                                   drift=inputs.drift_factor(s, 32), device="cuda")
+          for s in range(min(n, 4))]
+    g, b = inputs.layernorm_params(hidden, wl, device="cuda")
+    meta = ops.Meta(recipe, 1, ops.META_FORWARD)
+    out = torch.empty((rows, hidden), dtype=torch.uint8, device="cuda")
+    mean = torch.empty(rows, dtype=torch.float32, device="cuda")
+    rstd = torch.empty(rows, dtype=torch.float32, device="cuda")
+    for s in range(n):
+        ops.scaling_update(recipe, meta)
+        ops.ln_cast_amax(recipe, xs[s % len(xs)], g, b, ops.E4M3, meta.scale[0:1],
+                         meta.amax_ptr(0), out, None, mean, rstd)
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps(dict(profile_ln=n, copies=3, copy_bytes=COPY_BYTES)), flush=True)
+
+
+def _read_counter_csv(path, counter):
+    """{kernel name: [values per dispatch]} for one counter of a rocprofv3 csv."""
+    import csv
+    per = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            if row.get("Counter_Name") != counter:
+                continue
+            per.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return per
+
+
+def summarize_counters(fetch_csv, write_csv):
+    fetch = _read_counter_csv(fetch_csv, "FETCH_SIZE")
+    write = _read_counter_csv(write_csv, "WRITE_SIZE")
+
+    def pick(d, key):
+        names = [k for k in d if key in k]
+        if not names:
+            raise SystemExit(f"no kernel matching {key!r} in the counter file")
+        vals = d[names[0]]
+        return names[0], sum(vals) / len(vals)
+
+    ln_name, ln_fetch = pick(fetch, "ln_cast_amax_kernel")
+    _, ln_write = pick(write, "ln_cast_amax_kernel")
+    cp_name, cp_fetch = pick(fetch, "neg")
+    _, cp_write = pick(write, "neg")
+    # counters are in KiB per dispatch; the copy moves COPY_BYTES each way
+    f_read = COPY_BYTES / (cp_fetch * 1024.0)
+    f_write = COPY_BYTES / (cp_write * 1024.0)
+    rows, hidden = 65536, 2048
+    read_b = ln_fetch * 1024.0 * f_read
+    write_b = ln_write * 1024.0 * f_write
+    d = dict(kernel=ln_name, workload="ln_cast_amax_65536x2048",
+             source_hash=source_hash("layernorm.hip", "device_common.hpp"),
+             fetch_kib_per_launch=ln_fetch, write_kib_per_launch=ln_write,
+             copy_kernel=cp_name, copy_fetch_kib=cp_fetch, copy_write_kib=cp_write,
+             copy_scale_read=f_read, copy_scale_write=f_write,
+             hbm_read_bytes_per_launch=read_b, hbm_write_bytes_per_launch=write_b,
+             hbm_bytes_per_launch=read_b + write_b,
+             algorithmic_bytes_per_launch=rows * hidden * 3 + rows * 8,
+             commands=["rocprofv3 --pmc FETCH_SIZE -d <dir> -o fetch --output-format csv -- "
+                       "python bench.py --profile-ln 8",
+                       "rocprofv3 --pmc WRITE_SIZE -d <dir> -o write --output-format csv -- "
+                       "python bench.py --profile-ln 8",
+                       "python bench.py --summarize-counters <fetch csv> <write csv>"])
+    os.makedirs(PROFILE_DIR, exist_ok=True)
+    path = os.path.join(PROFILE_DIR, "ln_cast_amax_65536x2048_counters.json")
+    with open(path, "w") as f:
+        json.dump(d, f, indent=1)
+    print(json.dumps(d))
 
 
 # ---- GEMM-bound workloads ------------------------------------------------------
@@ -306,6 +393,9 @@ def cpu_baseline(inputs, budget_s=12.0):
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
               "design is described, not built.", file=sys.stderr)
@@ -319,6 +409,10 @@ def main():
 
     def log(msg):
         print(msg, file=sys.stderr, flush=True)
+
+    if args.profile_ln:
+        profile_ln(torch, ops, inputs, args.profile_ln)
+        return
 
     workloads = []
     head = None

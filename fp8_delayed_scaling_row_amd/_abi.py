@@ -76,6 +76,9 @@ SIGNATURES = {
     "fp8ln_cast_amax": (C.c_int, [_I64, _I64, _I32, _P, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "fp8ln_encode_range": (C.c_int, [C.c_uint32, _I64, _I32, _P, _P]),
     "fp8ln_gemm": (C.c_int, [_I64, _I64, _I64, _P, _I32, _P, _I32, _P, _P, _P, _I32, _P, _P]),
+    "fp8ln_gemm_gelu_fp8": (C.c_int, [_I64, _I64, _I64, _P, _I32, _P, _I32, _P, _P, _P, _P, _P,
+                                      _P, _I32, _P, _P, _P]),
+    "fp8ln_gemm_dgelu": (C.c_int, [_I64, _I64, _I64, _P, _I32, _P, _I32, _P, _P, _P, _P, _P]),
     "fp8ln_layernorm_bwd": (C.c_int, [_I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "fp8ln_ln_linear_fwd": (C.c_int, [_RP, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _MP,
                                       C.POINTER(LinearCtxStruct), _P]),

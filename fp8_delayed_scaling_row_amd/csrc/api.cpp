@@ -369,6 +369,65 @@ int fp8ln_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* A, int32_t a_dtyp
     return FP8LN_OK;
 }
 
+int fp8ln_gemm_gelu_fp8(int64_t M, int64_t N, int64_t K, const uint8_t* A, int32_t a_dtype,
+                        const uint8_t* B, int32_t b_dtype, const float* sinv_a,
+                        const float* sinv_b, const void* bias, void* h_out, uint8_t* q_out,
+                        uint8_t* q_out_t, int32_t q_dtype, const float* q_scale, float* q_amax,
+                        void* stream) {
+    REQUIRE(M >= 0 && N >= 0 && K >= 0, "negative size");
+    REQUIRE(a_dtype == FP8LN_E4M3 || a_dtype == FP8LN_E5M2, "a_dtype %d invalid", a_dtype);
+    REQUIRE(b_dtype == FP8LN_E4M3 || b_dtype == FP8LN_E5M2, "b_dtype %d invalid", b_dtype);
+    REQUIRE(q_dtype == FP8LN_E4M3 || q_dtype == FP8LN_E5M2, "q_dtype %d invalid", q_dtype);
+    if (N % 16 != 0 || K % 16 != 0)
+        return fail(FP8LN_ERR_UNSUPPORTED, "N and K must be multiples of 16 (N=%lld K=%lld)",
+                    (long long)N, (long long)K);
+    if (q_out_t && M % 16 != 0)
+        return fail(FP8LN_ERR_UNSUPPORTED, "a transposed output needs M %% 16 == 0");
+    REQUIRE_PTR(sinv_a); REQUIRE_PTR(sinv_b); REQUIRE_PTR(q_scale); REQUIRE_PTR(q_amax);
+    if (M > 0 && N > 0) {
+        REQUIRE_PTR(q_out); REQUIRE_ALIGNED(q_out);
+        if (q_out_t) REQUIRE_ALIGNED(q_out_t);
+        if (h_out) REQUIRE_ALIGNED(h_out);
+        if (bias) REQUIRE_ALIGNED(bias);
+        if (K > 0) { REQUIRE_PTR(A); REQUIRE_PTR(B); REQUIRE_ALIGNED(A); REQUIRE_ALIGNED(B); }
+    }
+    int s = check_current_device();
+    if (s) return s;
+    GemmParams p = gemm_params(M, N, K, A, a_dtype, B, b_dtype, sinv_a, sinv_b, kEpiGeluFp8);
+    p.bias = (const uint16_t*)bias;
+    p.h_out = (uint16_t*)h_out;
+    p.q_out = q_out;
+    p.q_out_t = q_out_t;
+    p.q_scale = q_scale;
+    p.q_amax = q_amax;
+    p.q_fp8 = q_dtype;
+    FP8LN_TRY(launch_gemm(p, as_stream(stream)), "gemm_gelu launch");
+    return FP8LN_OK;
+}
+
+int fp8ln_gemm_dgelu(int64_t M, int64_t N, int64_t K, const uint8_t* A, int32_t a_dtype,
+                     const uint8_t* B, int32_t b_dtype, const float* sinv_a, const float* sinv_b,
+                     const void* h, float* out, void* stream) {
+    REQUIRE(M >= 0 && N >= 0 && K >= 0, "negative size");
+    REQUIRE(a_dtype == FP8LN_E4M3 || a_dtype == FP8LN_E5M2, "a_dtype %d invalid", a_dtype);
+    REQUIRE(b_dtype == FP8LN_E4M3 || b_dtype == FP8LN_E5M2, "b_dtype %d invalid", b_dtype);
+    if (N % 16 != 0 || K % 16 != 0)
+        return fail(FP8LN_ERR_UNSUPPORTED, "N and K must be multiples of 16 (N=%lld K=%lld)",
+                    (long long)N, (long long)K);
+    REQUIRE_PTR(sinv_a); REQUIRE_PTR(sinv_b);
+    if (M > 0 && N > 0) {
+        REQUIRE_PTR(out); REQUIRE_PTR(h); REQUIRE_ALIGNED(out); REQUIRE_ALIGNED(h);
+        if (K > 0) { REQUIRE_PTR(A); REQUIRE_PTR(B); REQUIRE_ALIGNED(A); REQUIRE_ALIGNED(B); }
+    }
+    int s = check_current_device();
+    if (s) return s;
+    GemmParams p = gemm_params(M, N, K, A, a_dtype, B, b_dtype, sinv_a, sinv_b, kEpiDGeluF32);
+    p.h_in = (const uint16_t*)h;
+    p.out = out;
+    FP8LN_TRY(launch_gemm(p, as_stream(stream)), "gemm_dgelu launch");
+    return FP8LN_OK;
+}
+
 int fp8ln_layernorm_bwd(int64_t rows, int64_t hidden, const float* dy, const void* x,
                         const float* mean, const float* rstd, const void* gamma, void* dx,
                         float* dgamma, float* dbeta, void* workspace, size_t workspace_bytes,

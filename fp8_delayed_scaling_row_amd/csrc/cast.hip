@@ -1,6 +1,7 @@
 // FP8 cast kernels: tensor cast with amax, optional transposed copy and column
 // sums (weights, output gradients, fc1 gradients), a byte transpose, and the
-// encoder over a range of binary32 bit patterns.
+// encoder over a range of binary32 bit patterns.  The cast scales with a
+// round-to-odd product, so its codes are those of the exact value * scale.
 //
 // Autocast casts the operands of the linear layers to FP8 with the delayed
 // scale and hands gradients back in higher precision ("Turbo-charging your
@@ -61,7 +62,7 @@ __global__ __launch_bounds__(kThreads) void cast_tile_kernel(
     for (int i = 0; i < 16; ++i) {
         const uint32_t ab = abs_bits(v[i]);
         cm = cm > ab ? cm : ab;
-        vs[i] = v[i] * s;
+        vs[i] = mul_round_odd(v[i], s);
     }
     uint4 q;
     q.x = encode4<FMT>(vs[0], vs[1], vs[2], vs[3]);

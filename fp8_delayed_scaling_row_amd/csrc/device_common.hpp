@@ -73,6 +73,25 @@ __device__ __forceinline__ uint32_t encode4(float v0, float v1, float v2, float 
     return cvt_pk<FMT, true>(v2, v3, r);
 }
 
+// v * s rounded to odd: the binary32 product with its last bit forced to 1
+// when it is inexact (moving one ulp toward the exact product when needed).  A
+// round-to-odd result at 24 bits followed by one round-to-nearest-even at <= 22
+// bits equals the correct rounding of the exact product, so the FP8 code of
+// v * s comes out as if the product had never been rounded to binary32.
+// Without it, inputs with few significant bits (bf16 weights and gradients)
+// times a binary32 scale land on FP8 rounding midpoints after the binary32
+// rounding for whole mantissa patterns at once.
+__device__ __forceinline__ float mul_round_odd(float v, float s) {
+    const float p = v * s;
+    const float e = fmaf(v, s, -p);            // exact remainder of the product
+    uint32_t b = __float_as_uint(p);
+    const bool fix = (e != 0.0f) && ((b & 1u) == 0u) && (p != 0.0f);
+    // same sign: the exact magnitude is larger -> step the bits up, else down
+    const uint32_t step = ((__float_as_uint(e) ^ b) & 0x80000000u) ? 0xffffffffu : 1u;
+    b += fix ? step : 0u;
+    return __uint_as_float(b);
+}
+
 // Replace the code of every NaN among v[0..3] by 0x7F.
 __device__ __forceinline__ uint32_t patch_nan4(uint32_t codes, const float* v) {
 #pragma unroll

@@ -20,7 +20,8 @@ __all__ = [
     "Recipe", "Meta", "LinearCtx", "MlpCtx", "Fp8lnError", "FORMAT_E4M3", "FORMAT_HYBRID",
     "FORMAT_E5M2", "E4M3", "E5M2", "META_FORWARD", "META_BACKWARD", "OP_CAST_AMAX",
     "OP_LAYERNORM_BWD", "OP_LN_LINEAR_BWD", "OP_LN_MLP_BWD", "check_support", "workspace_size", "meta_init",
-    "scaling_update", "ln_cast_amax", "cast_amax", "encode_range", "gemm", "layernorm_bwd",
+    "scaling_update", "ln_cast_amax", "cast_amax", "encode_range", "gemm", "gemm_gelu_fp8",
+    "gemm_dgelu", "layernorm_bwd",
     "ln_linear_fwd", "ln_linear_bwd", "ln_mlp_fwd", "ln_mlp_bwd", "fwd_fp8", "bwd_fp8",
 ]
 
@@ -234,6 +235,36 @@ def gemm(a, a_dtype: int, b, b_dtype: int, sinv_a, sinv_b, out, bias=None, strea
     od = DTYPE_BF16 if out.dtype == torch.bfloat16 else DTYPE_F32
     check(lib().fp8ln_gemm(M, N, K, _ptr(a), a_dtype, _ptr(b), b_dtype, _ptr(sinv_a),
                            _ptr(sinv_b), _ptr(bias), od, _ptr(out), _stream(stream)))
+
+
+def gemm_gelu_fp8(a, a_dtype: int, b, b_dtype: int, sinv_a, sinv_b, q_dtype: int, q_scale,
+                  q_amax_ptr: int, q_out, q_out_t=None, h_out=None, bias=None, stream=None):
+    """fc1 with the GELU epilogue: h = a.b^T * sinv_a * sinv_b + bias (fp32), h_out =
+    bf16(h), q_out = encode(gelu(h) * q_scale), amax of gelu(h) at q_amax_ptr."""
+    M, K = a.shape
+    N = b.shape[0]
+    _need(a, torch.uint8, (M, K), "a")
+    _need(b, torch.uint8, (N, K), "b")
+    _need(q_out, torch.uint8, (M, N), "q_out")
+    _opt(q_out_t, torch.uint8, (N, M), "q_out_t")
+    _opt(h_out, torch.bfloat16, (M, N), "h_out")
+    _opt(bias, torch.bfloat16, (N,), "bias")
+    check(lib().fp8ln_gemm_gelu_fp8(M, N, K, _ptr(a), a_dtype, _ptr(b), b_dtype, _ptr(sinv_a),
+                                    _ptr(sinv_b), _ptr(bias), _ptr(h_out), _ptr(q_out),
+                                    _ptr(q_out_t), q_dtype, _ptr(q_scale),
+                                    C.c_void_p(q_amax_ptr), _stream(stream)))
+
+
+def gemm_dgelu(a, a_dtype: int, b, b_dtype: int, sinv_a, sinv_b, h, out, stream=None):
+    """out = a.b^T * sinv_a * sinv_b * gelu'(h) (fp32)."""
+    M, K = a.shape
+    N = b.shape[0]
+    _need(a, torch.uint8, (M, K), "a")
+    _need(b, torch.uint8, (N, K), "b")
+    _need(h, torch.bfloat16, (M, N), "h")
+    _need(out, torch.float32, (M, N), "out")
+    check(lib().fp8ln_gemm_dgelu(M, N, K, _ptr(a), a_dtype, _ptr(b), b_dtype, _ptr(sinv_a),
+                                 _ptr(sinv_b), _ptr(h), _ptr(out), _stream(stream)))
 
 
 def layernorm_bwd(dy, x, mean, rstd, gamma, dx, dgamma, dbeta, stream=None) -> None:

@@ -228,6 +228,28 @@ int fp8ln_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* A, int32_t a_dtyp
                const uint8_t* B, int32_t b_dtype, const float* sinv_a, const float* sinv_b,
                const void* bias, int32_t out_dtype, void* out, void* stream);
 
+/* The fc1 step of LayerNormMLP ([G] "The building blocks": linear, GELU, linear)
+ * as its own call:
+ *   h = (sum_k A[m][k] B[n][k]) * (*sinv_a) * (*sinv_b) + bias[n]   (fp32)
+ *   h_out[m][n] = bf16(h)                          (optional, may be NULL)
+ *   g = gelu_tanh(h); q_out[m][n] = encode(g * (*q_scale)) in q_dtype
+ *   q_out_t[n][m] = q_out[m][n]                    (optional, needs M % 16 == 0)
+ *   *q_amax = max(*q_amax, max |g|)
+ * bias is bf16 [N] or NULL.  K and N must be multiples of 16. */
+int fp8ln_gemm_gelu_fp8(int64_t M, int64_t N, int64_t K, const uint8_t* A, int32_t a_dtype,
+                        const uint8_t* B, int32_t b_dtype, const float* sinv_a,
+                        const float* sinv_b, const void* bias, void* h_out, uint8_t* q_out,
+                        uint8_t* q_out_t, int32_t q_dtype, const float* q_scale, float* q_amax,
+                        void* stream);
+
+/* The fc2 dgrad step of the LayerNormMLP backward with the GELU derivative:
+ *   out[m][n] = (sum_k A[m][k] B[n][k]) * (*sinv_a) * (*sinv_b) * gelu_tanh'(h[m][n])
+ * h is the bf16 [M][N] fc1 output saved by the forward; out is fp32 [M][N].
+ * K and N must be multiples of 16. */
+int fp8ln_gemm_dgelu(int64_t M, int64_t N, int64_t K, const uint8_t* A, int32_t a_dtype,
+                     const uint8_t* B, int32_t b_dtype, const float* sinv_a, const float* sinv_b,
+                     const void* h, float* out, void* stream);
+
 /* ---- LayerNorm backward ---------------------------------------------------- */
 
 /* With xhat = (x - mean) * rstd and g = dy * gamma per row:

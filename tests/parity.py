@@ -1,13 +1,14 @@
 """Comparison rules between the HIP path and the oracle (test helpers).
 
-* FP8 codes: equal, except where the oracle's exact value v = y * scale lies
-  within a relative window of a rounding midpoint; there the two codes may be
-  neighbours in value order (+0 and -0 count as the same value).  The window for
-  a LayerNorm output is 1e-6 * max(|midpoint|, scale * (|gamma * xhat| + |beta|))
-  (the second term covers the cancellation between gamma * xhat and beta); a
-  product-fed cast (GELU of a GEMM output) gets the GEMM's own error bound.
-* GEMM-shaped outputs: max_ij |gpu - oracle| / ||oracle row i||_2 <= 2e-2, and a
-  tighter internal alarm on the per-row relative L2 error.
+* FP8 codes: the GPU code must encode a value within a window of the oracle's
+  exact value v.  For a LayerNorm output the window is
+  1e-6 * max(|v|, scale * (|gamma * xhat| + |beta|)) (the second term covers the
+  cancellation between gamma * xhat and beta), which allows a one-step difference
+  only next to a rounding midpoint; casts of bf16/fp32 tensors are exact (window
+  0); a GEMM-fed cast (GELU of fc1) gets the GEMM's own error bound.
+* GEMM-shaped outputs: max_ij |gpu - oracle| / ||oracle row i||_2 <= 2e-2, and an
+  alarm on the per-row relative L2 error (catches a dropped K tile or a wrong
+  epilogue term, which move rows by O(1)).
 """
 from __future__ import annotations
 
@@ -47,30 +48,39 @@ def midpoint_distance(v: np.ndarray, fmt: str):
     return np.minimum(d_lo, d_hi), near
 
 
-def compare_codes(gpu_codes: np.ndarray, exact: np.ndarray, fmt: str, window: np.ndarray):
-    """Check FP8 codes against the oracle under the near-boundary rule.
+def compare_codes(gpu_codes: np.ndarray, exact: np.ndarray, fmt: str, window):
+    """Check FP8 codes against the oracle.
 
     exact: the oracle's value before encoding (float64); window: the absolute
-    distance to a midpoint within which a one-step difference is accepted.
-    Returns a dict with counts; raises AssertionError on a violation."""
+    error bound of the HIP path's value.  The GPU code must be the encoding of
+    some value within [exact - window, exact + window]: with a window far below
+    the code spacing this is "equal, or one step off where the exact value lies
+    within the window of a rounding midpoint"; window 0 demands equality.  +0 and
+    -0 count as the same value; NaN must give 0x7F.  Returns counts; raises
+    AssertionError on a violation."""
     gpu_codes = np.asarray(gpu_codes, dtype=np.uint8).reshape(-1)
     exact = np.asarray(exact, dtype=np.float64).reshape(-1)
-    window = np.broadcast_to(np.asarray(window, dtype=np.float64), exact.shape).reshape(-1)
+    window = np.asarray(window, dtype=np.float64)
+    window = window.reshape(-1) if window.size == exact.size else \
+        np.broadcast_to(window, exact.shape).reshape(-1)
     ref = oracle.fp8_encode(exact, fmt)
-    gi, ri = signed_index(gpu_codes), signed_index(ref)
     nan = np.isnan(exact)
     assert np.all(gpu_codes[nan] == 0x7F), "NaN inputs must encode to 0x7F"
+    gi, ri = signed_index(gpu_codes), signed_index(ref)
+    lo = signed_index(oracle.fp8_encode(exact - window, fmt))
+    hi = signed_index(oracle.fp8_encode(exact + window, fmt))
+    bad = ((gi < lo) | (gi > hi)) & ~nan
     diff = (gi != ri) & ~nan
-    dist, _ = midpoint_distance(exact, fmt)
-    near = dist <= window
-    bad = diff & ~(near & (np.abs(gi - ri) == 1))
     if bad.any():
         idx = np.nonzero(bad)[0][:8]
+        dist, _ = midpoint_distance(exact[idx], fmt)
         raise AssertionError(
-            f"{int(bad.sum())} FP8 codes differ outside the rule; first at {idx.tolist()}: "
+            f"{int(bad.sum())} FP8 codes outside the rule; first at {idx.tolist()}: "
             f"gpu={gpu_codes[idx].tolist()} oracle={ref[idx].tolist()} "
-            f"exact={exact[idx].tolist()} dist={dist[idx].tolist()} window={window[idx].tolist()}")
-    return dict(n=int(exact.size), mismatched=int(diff.sum()), near_boundary=int(near.sum()))
+            f"exact={exact[idx].tolist()} midpoint distance={dist.tolist()} "
+            f"window={window[idx].tolist()}")
+    return dict(n=int(exact.size), mismatched=int(diff.sum()),
+                near_boundary=int(((lo != ri) | (hi != ri)).sum()))
 
 
 def ln_window(gamma_xhat: np.ndarray, beta: np.ndarray, scale: float, exact: np.ndarray):
@@ -99,7 +109,11 @@ def gemm_rel_error(gpu: np.ndarray, ref: np.ndarray):
     return float(a), float(b)
 
 
-def assert_gemm_close(gpu, ref, tol=2e-2, alarm=5e-3, what="output"):
+def assert_gemm_close(gpu, ref, tol=2e-2, alarm=2e-2, what="output"):
+    """The GEMM rule plus an alarm on each row's relative L2 error.  A one-step
+    FP8 code difference that the code rule allows moves a whole output row by up
+    to ~1e-2 in relative L2, so the alarm is only tightened where no code can
+    differ (operands given as codes)."""
     a, b = gemm_rel_error(gpu, ref)
     assert a <= tol, f"{what}: max |d| / row norm = {a:.3e} > {tol}"
     assert b <= alarm, f"{what}: row relative L2 error = {b:.3e} > {alarm}"

@@ -95,7 +95,8 @@ def test_random_gemm_within_tolerance(fa, fb, M, N, K, out_bf16):
     ref = oracle.fp8_gemm_tn(a, FMT[fa], b, FMT[fb], sa, sb,
                              None if bias_bits is None else oracle.bf16_to_f64(bias_bits))
     # bf16 output rounding alone is 2^-9 relative per element
-    assert_gemm_close(to_np(out), ref, alarm=5e-3 if out_bf16 else 1e-5)
+    # operands are given as codes, so only accumulation and output rounding differ
+    assert_gemm_close(to_np(out), ref, alarm=5e-3 if out_bf16 else 1e-3)
 
 
 def test_k_zero_gives_bias_and_m_zero_is_a_no_op():
@@ -125,3 +126,83 @@ def test_gemm_is_deterministic():
     ops.gemm(a, ops.E4M3, b, ops.E4M3, _scalar(0.5), _scalar(0.25), o2)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)
+
+
+# ---- the MLP epilogues, pinned on exactly representable GEMM results -----------
+
+GELU_REL = 2e-6     # fp32 GELU (tanh via exp): ~1e-6 of |h| plus a few ulps of g
+
+
+@pytest.mark.parametrize("M,N,K,q", [(64, 128, 64, ops.E4M3), (130, 272, 48, ops.E5M2),
+                                     (256, 3072, 32, ops.E4M3)])
+def test_gelu_epilogue_on_exact_products(M, N, K, q):
+    """Small integer operands and power-of-two scale_inv make every h exact in
+    fp32, so h (bf16) must match bit for bit and the GELU codes may differ only
+    where the fp32 GELU's own error reaches a rounding midpoint."""
+    a, av = int_codes((M, K), ops.E4M3, 5 + M, lim=4)
+    b, bv = int_codes((N, K), ops.E4M3, 7 + N, lim=4)
+    bias_bits = oracle.f64_to_bf16_bits(np.random.default_rng(N).integers(-64, 65, N) / 64.0)
+    bias = torch.from_numpy(bias_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    sa, sb, qs = 1.0 / 16.0, 1.0 / 4.0, float(np.float32(448.0 / 7.3))
+    q_out = torch.empty((M, N), dtype=torch.uint8, device="cuda")
+    q_t = torch.empty((N, M), dtype=torch.uint8, device="cuda") if M % 16 == 0 else None
+    h_out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    ops.gemm_gelu_fp8(dev(a), ops.E4M3, dev(b), ops.E4M3, _scalar(sa), _scalar(sb), q,
+                      _scalar(qs), amax.data_ptr(), q_out, q_t, h_out, bias)
+    torch.cuda.synchronize()
+    h = (av @ bv.T) * sa * sb + oracle.bf16_to_f64(bias_bits)[None, :]
+    np.testing.assert_array_equal(to_np(h_out), oracle.bf16_to_f64(oracle.f64_to_bf16_bits(h)))
+    g = oracle.gelu_tanh(h)
+    fmt = FMT[q]
+    from parity import compare_codes
+    stats = compare_codes(q_out.cpu().numpy(), g * qs, fmt,
+                          qs * (GELU_REL * np.abs(h) + 1e-6 * np.abs(g)))
+    assert stats["mismatched"] <= max(2, stats["n"] // 10000), stats
+    oamax = float(np.abs(g).max())
+    assert abs(amax.item() - oamax) <= 1e-5 * oamax
+    if q_t is not None:
+        assert torch.equal(q_t, q_out.t().contiguous())
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 128, 64), (130, 272, 48)])
+def test_dgelu_epilogue_on_exact_products(M, N, K):
+    a, av = int_codes((M, K), ops.E5M2, 9 + M, lim=4)
+    b, bv = int_codes((N, K), ops.E4M3, 3 + N, lim=4)
+    h_bits = oracle.f64_to_bf16_bits(np.random.default_rng(M).normal(size=(M, N)) * 2.0)
+    h = torch.from_numpy(h_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    sa, sb = 1.0 / 8.0, 2.0
+    ops.gemm_dgelu(dev(a), ops.E5M2, dev(b), ops.E4M3, _scalar(sa), _scalar(sb), h, out)
+    torch.cuda.synchronize()
+    acc = (av @ bv.T) * sa * sb
+    ref = acc * oracle.gelu_tanh_grad(oracle.bf16_to_f64(h_bits))
+    err = np.abs(out.cpu().numpy() - ref)
+    assert np.all(err <= 4e-6 * np.abs(acc) + 1e-30), err.max()
+
+
+@pytest.mark.parametrize("M,N,K", [(2048, 3072, 768), (333, 400, 272)])
+def test_gelu_gemm_random_within_tolerance(M, N, K):
+    """Gaussian-like operands: h under the GEMM rule, the GELU codes within the
+    GEMM's error bound carried through GELU'."""
+    rng = np.random.default_rng(K)
+    a = oracle.fp8_encode(rng.normal(size=(M, K)) * 60, oracle.E4M3)
+    b = oracle.fp8_encode(rng.normal(size=(N, K)) * 90, oracle.E4M3)
+    sa, sb = np.float32(1 / 60.0), np.float32(1 / 4500.0)
+    qs = np.float32(448.0 / 3.0)
+    q_out = torch.empty((M, N), dtype=torch.uint8, device="cuda")
+    h_out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    ops.gemm_gelu_fp8(dev(a), ops.E4M3, dev(b), ops.E4M3, _scalar(float(sa)), _scalar(float(sb)),
+                      ops.E4M3, _scalar(float(qs)), amax.data_ptr(), q_out, None, h_out)
+    torch.cuda.synchronize()
+    h = oracle.fp8_gemm_tn(a, oracle.E4M3, b, oracle.E4M3, sa, sb)
+    assert_gemm_close(to_np(h_out), h, alarm=5e-3)
+    abs_sum = oracle.fp8_gemm_tn(a & 0x7F, oracle.E4M3, b & 0x7F, oracle.E4M3, sa, sb)
+    dh = 2.0 ** -10 * abs_sum + 2.0 ** -22 * np.abs(h)
+    g = oracle.gelu_tanh(h)
+    from parity import compare_codes
+    win = float(qs) * (np.abs(oracle.gelu_tanh_grad(h)) * dh + GELU_REL * np.abs(h) +
+                       1e-6 * np.abs(g))
+    stats = compare_codes(q_out.cpu().numpy(), g * float(qs), oracle.E4M3, win)
+    print(f"gelu gemm {M}x{N}x{K}: {stats}")

@@ -118,16 +118,21 @@ def test_ln_cast_amax_full_size_sampled():
     print(f"full-size sample: {stats}")
 
 
-@pytest.mark.parametrize("rows,cols,in_f32,fp8,with_t,with_sum", [
-    (16, 16, False, ops.E4M3, True, True),
-    (2304, 768, False, ops.E4M3, True, False),
-    (2048, 2304, False, ops.E5M2, True, True),
-    (48, 80, False, ops.E4M3, True, True),
-    (100, 48, True, ops.E5M2, False, True),
-    (256, 3072, True, ops.E5M2, True, True),
-    (0, 64, False, ops.E4M3, False, True),
+@pytest.mark.parametrize("rows,cols,in_f32,fp8,with_t,with_sum,scale_from", [
+    (16, 16, False, ops.E4M3, True, True, None),
+    (2304, 768, False, ops.E4M3, True, False, None),
+    (2048, 2304, False, ops.E5M2, True, True, None),
+    (48, 80, False, ops.E4M3, True, True, None),
+    (100, 48, True, ops.E5M2, False, True, None),
+    (256, 3072, True, ops.E5M2, True, True, None),
+    (0, 64, False, ops.E4M3, False, True, None),
+    (2048, 2304, False, ops.E5M2, True, True, "amax"),
+    (2304, 768, False, ops.E4M3, True, False, "amax"),
 ])
-def test_cast_amax_matches_oracle(rows, cols, in_f32, fp8, with_t, with_sum):
+def test_cast_amax_matches_oracle(rows, cols, in_f32, fp8, with_t, with_sum, scale_from):
+    """scale_from="amax": the scale a delayed-scaling step would use,
+    fp8_max / amax of the same bf16 data; its products with the data hit FP8
+    rounding midpoints after a binary32 rounding for whole mantissa patterns."""
     wl = f"cast/{rows}x{cols}"
     if in_f32:
         xf = torch.randn((rows, cols), generator=torch.Generator().manual_seed(5)) * 3e-4
@@ -142,6 +147,9 @@ def test_cast_amax_matches_oracle(rows, cols, in_f32, fp8, with_t, with_sum):
     colsum = torch.full((cols,), 7.0, dtype=torch.float32, device="cuda") if with_sum else None
     amax = torch.zeros(1, dtype=torch.float32, device="cuda")
     scale = float(np.float32(448.0 / 0.093 if fp8 == ops.E4M3 else 57344.0 / 0.0011))
+    if scale_from == "amax" and rows:
+        fmax = np.float32(448.0 if fp8 == ops.E4M3 else 57344.0)
+        scale = float(fmax / np.float32(np.abs(xv).max()))
     ops.cast_amax(xd, fp8, _scalar(scale), amax.data_ptr(), out, out_t, colsum)
     torch.cuda.synchronize()
     if with_sum:
@@ -154,7 +162,9 @@ def test_cast_amax_matches_oracle(rows, cols, in_f32, fp8, with_t, with_sum):
         return
     fmt = FMT[fp8]
     exact = xv * scale
-    stats = compare_codes(out.cpu().numpy(), exact, fmt, 1e-6 * np.abs(exact))
+    # the cast scales with a round-to-odd product: codes equal the oracle's
+    stats = compare_codes(out.cpu().numpy(), exact, fmt, 0.0)
+    assert stats["mismatched"] == 0
     assert np.float32(amax.item()) == np.float32(np.abs(xv).max())     # exact for these inputs
     if with_t:
         assert torch.equal(out_t, out.t().contiguous())

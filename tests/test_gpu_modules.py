@@ -105,7 +105,7 @@ def run_linear(recipe, M, K, N, steps, workload, backward, check_every=1):
         compare_codes(ctx.ln_q.cpu().numpy(), exact, ffmt,
                       ln_window(gx, beta, s0, exact) + scale_slack(mf, omf, 0, exact))
         wex = oracle.bf16_to_f64(wbits) * float(omf.scale[1])
-        compare_codes(ctx.w_q.cpu().numpy(), wex, ffmt, 1e-6 * np.abs(wex))
+        compare_codes(ctx.w_q.cpu().numpy(), wex, ffmt, 0.0)
         if backward:
             assert torch.equal(ctx.ln_qt, ctx.ln_q.t().contiguous())
             assert torch.equal(ctx.w_qt, ctx.w_q.t().contiguous())
@@ -144,13 +144,19 @@ def test_ln_linear_fwd_ragged_tokens_forward_only():
 
 # ---- LayerNormMLP --------------------------------------------------------------
 
+MFMA_DOT_REL = 2.0 ** -10
+
+
 def gelu_code_window(ln_q, w1_q, fmt, alpha, h, scale, K):
-    """GEMM-fed window for the GELU output's codes: fp32 accumulation error of h
-    (serial bound K u sum |a b|), the epilogue's roundings, the fp32 GELU."""
+    """GEMM-fed window for the GELU output's codes.  The FP8 MFMA's 128-term dot
+    products carry about 13-14 bits relative to their sum of |a b| (measured
+    worst case 3.2e-4 on full-range random codes); the fp32 accumulator adds are
+    exact to 2^-24.  Bound: 2^-10 * alpha * sum_k |a b| for h, then through
+    GELU', plus the epilogue's roundings and the fp32 GELU."""
     a = oracle.fp8_decode(ln_q & 0x7F, fmt)
     b = oracle.fp8_decode(w1_q & 0x7F, fmt)
     abs_sum = a @ b.T
-    dh = K * U32 * float(alpha) * abs_sum + 4 * U32 * np.abs(h)
+    dh = MFMA_DOT_REL * float(alpha) * abs_sum + 4 * U32 * np.abs(h)
     dg = np.abs(oracle.gelu_tanh_grad(h)) * dh + 1e-6 * np.abs(oracle.gelu_tanh(h)) \
         + 2e-7 * np.abs(h)
     return float(scale) * dg
@@ -196,8 +202,10 @@ def run_mlp(recipe, M, H, F, steps, workload, backward, sample_rows=None):
             og = oracle.ln_mlp_bwd(orc, omf, omb, to_np_bits(dy), octx, xbits, gbits)
         torch.cuda.synchronize()
         tag = f"step {step}"
-        assert_gemm_close(to_np(out)[rows], oout[rows], what=f"{tag} out")
-        assert_gemm_close(to_np(ctx.h)[rows], octx["h"][rows], what=f"{tag} h")
+        # one LayerNorm code that the rule lets differ moves a whole fc1 row by ~1 %
+        # and its GELU codes by several steps, so the row alarm is 5e-2 here
+        assert_gemm_close(to_np(out)[rows], oout[rows], alarm=5e-2, what=f"{tag} out")
+        assert_gemm_close(to_np(ctx.h)[rows], octx["h"][rows], alarm=5e-2, what=f"{tag} h")
         gx, beta = ln_parts(xbits[rows], gbits, bbits)
         s0 = float(omf.scale[0])
         exact = octx["y"][rows] * s0
@@ -208,6 +216,13 @@ def run_mlp(recipe, M, H, F, steps, workload, backward, sample_rows=None):
         gq = ctx.g_q.cpu().numpy()[rows]
         win = gelu_code_window(octx["ln_q"][rows], octx["w1_q"], ffmt, alpha, octx["h"][rows],
                                s2, H)
+        # LayerNorm codes the rule let differ (one step next to a midpoint) move the
+        # whole fc1 row: add their effect through |W1| and the largest GELU' (1.13)
+        d_ln = np.abs(oracle.fp8_decode(ctx.ln_q.cpu().numpy()[rows], ffmt) -
+                      oracle.fp8_decode(octx["ln_q"][rows], ffmt))
+        if d_ln.any():
+            w1abs = np.abs(oracle.fp8_decode(octx["w1_q"], ffmt))
+            win = win + s2 * 1.13 * float(alpha) * (d_ln @ w1abs.T)
         stats = compare_codes(gq, octx["g"][rows] * s2, ffmt,
                               win + scale_slack(mf, omf, 2, octx["g"][rows] * s2))
         assert torch.equal(ctx.g_qt, ctx.g_q.t().contiguous())
@@ -215,8 +230,10 @@ def run_mlp(recipe, M, H, F, steps, workload, backward, sample_rows=None):
         np.testing.assert_allclose(mf.history.cpu().numpy()[:, 2], omf.history[:, 2], rtol=1e-4)
         if backward:
             check_meta(mb, omb, exact_slots=[0], rel_slots=[1], rel=5e-3, what=f"{tag} bwd")
-            assert_gemm_close(to_np(dx)[rows], og["dx"][rows], alarm=1e-2, what=f"{tag} dx")
-            assert_gemm_close(dw1.cpu().numpy(), og["dw1"], alarm=1e-2, what=f"{tag} dW1")
+            # dH is a GEMM output cast to E5M2 (25 % steps): a code the rule lets
+            # differ moves a row of dLN / dW1 by about a percent
+            assert_gemm_close(to_np(dx)[rows], og["dx"][rows], alarm=5e-2, what=f"{tag} dx")
+            assert_gemm_close(dw1.cpu().numpy(), og["dw1"], alarm=5e-2, what=f"{tag} dW1")
             assert_gemm_close(dw2.cpu().numpy(), og["dw2"], alarm=5e-3, what=f"{tag} dW2")
             assert_vector_close(db1.cpu().numpy(), og["db1"], 1e-3, f"{tag} db1")
             assert_vector_close(db2.cpu().numpy(), og["db2"], 1e-5, f"{tag} db2")
