@@ -113,6 +113,30 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// DPP lane permutations (VOP DPP control values of the gfx9 family).
+constexpr int kDppQuadSwap1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadSwap2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141; // lane i <-> 7-i within each 8 lanes
+constexpr int kDppRowMirror = 0x140;     // lane i <-> 15-i within each 16 lanes
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 64 lanes, every lane receiving the result: four DPP steps inside
+// each 16-lane row, then two cross-row exchanges.  Each step adds a value to its
+// mirror image, so every lane of a group computes the same bits.
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+    v += dpp_f32<kDppQuadSwap1>(v);
+    v += dpp_f32<kDppQuadSwap2>(v);
+    v += dpp_f32<kDppRowHalfMirror>(v);
+    v += dpp_f32<kDppRowMirror>(v);
+    v += __shfl_xor(v, 16, kWave);
+    v += __shfl_xor(v, 32, kWave);
+    return v;
+}
+
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
     for (int off = kWave / 2; off > 0; off >>= 1) {

@@ -11,15 +11,22 @@
 // wgrad products are all of this form once the cast kernels have written the
 // transposed operand copies.
 //
-// Tiling (gfx950): a 256-thread workgroup computes a 128 x 128 tile; its four
-// waves each own a 64 x 64 sub-tile made of 4 x 4 V_MFMA_F32_16X16X128_F8F6F4
-// results (the operand formats E4M3/E5M2 are picked per operand by the
-// instruction's cbsz/blgp fields).  The K loop steps 128 bytes at a time through
-// a double-buffered LDS stage (2 x 32 KB) with an XOR swizzle on 16-byte chunks
-// so that the fragment reads are bank-conflict free.  The epilogue goes through
-// LDS so every global store is a full 16- or 32-byte vector per lane.  Tiles are
+// Tiling (gfx950): for large problems a 512-thread workgroup owns a 256 x 256
+// output tile and its eight waves (4 along M x 2 along N, two per SIMD) each own
+// a 64 x 128 sub-tile; when that would leave CUs idle, a 256-thread workgroup
+// owns a 128 x 128 tile split 2 x 2 over four waves, two workgroups per CU.
+// Sub-tiles are built from V_MFMA_F32_32X32X64_F8F6F4 results accumulated in
+// fp32 registers.  The operand formats (E4M3 / E5M2) are chosen per operand by the instruction's
+// cbsz / blgp fields.  K advances 64 bytes per stage through a four-stage LDS
+// ring filled by direct-to-LDS buffer loads issued three stages ahead, so
+// memory latency hides behind three stages of MFMA work without holding any
+// registers; an XOR layout of 16-byte chunks keeps fragment reads free of bank
+// conflicts.
+// The MFMA computes the transposed product (B rows in, A rows out), so each
+// lane ends up holding four consecutive output columns of one row and the
+// epilogue stores straight from registers as 8- or 16-byte vectors.  Tiles are
 // ordered so that the blocks of one XCD (blocks are dealt to the 8 XCDs round
-// robin) cover a compact band of the output and share its operands in their L2.
+// robin) cover a compact band of the output and share operands in their L2.
 #include "device_common.hpp"
 #include "launchers.hpp"
 
@@ -28,21 +35,15 @@ namespace fp8ln {
 namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int kThreads = 256;
-constexpr int BM = 128;
-constexpr int BN = 128;
-constexpr int BK = 128;                       // bytes of K per stage
-constexpr int kStageBytes = BM * BK;          // one operand tile
-constexpr int kCPitch = BN + 4;               // floats per row of the epilogue tile
-constexpr int kCodePitch = BN + 16;           // bytes per row of the code tile
-constexpr int kSmemBytes =
-    (4 * kStageBytes > BM * kCPitch * 4) ? 4 * kStageBytes : BM * kCPitch * 4;
-constexpr int kGroupM = 8;                    // tile rows per ordering group
+constexpr int BKS = 64;        // bytes of K per pipeline stage
+constexpr int kGroupM = 8;     // tile rows per ordering group
+constexpr int kBufferWord3 = 0x00020000;      // raw buffer descriptor flags (gfx9 family)
+constexpr uint32_t kOutOfRange = 0x80000000u; // offset past any tile: loads read 0
 
-// 16-byte chunk c of LDS row `row` lives at chunk position swz(row, c).
-__device__ __forceinline__ int swz(int row, int c) { return c ^ ((row ^ (row >> 3)) & 7); }
+// 16-byte chunk c of LDS row r lives at chunk position swz(r, c).
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r ^ (r >> 3)) & 7); }
 
 // GELU, tanh form, with tanh(u) = 1 - 2 / (1 + e^(2u)).
 __device__ __forceinline__ float gelu_f(float h, float* tanh_out) {
@@ -63,12 +64,42 @@ __device__ __forceinline__ float gelu_grad_f(float h) {
     return 0.5f * (1.0f + t) + 0.5f * h * (1.0f - t * t) * k0 * fmaf(3.0f * k1, h * h, 1.0f);
 }
 
-template <int FA, int FB, int EPI, int QF>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
+// LDS layout of one operand stage: 64-byte rows stored in pairs as 128-byte
+// lines (line L holds rows 2L and 2L+1); the eight 16-byte slots of a line are
+// XOR-permuted with f(L) so that fragment reads of 16 consecutive rows (or 8,
+// in a 32-bank view) touch distinct banks.
+__device__ __forceinline__ int line_perm(int L) { return (L & 3) ^ ((L >> 2) & 1); }
+
+// Byte offset inside a stage of 16-byte chunk c (0..3) of row r.
+__device__ __forceinline__ int lds_off(int r, int c) {
+    const int L = r >> 1;
+    return L * 128 + ((((r & 1) << 2) | c) ^ line_perm(L)) * 16;
+}
+
+// s_waitcnt immediate that waits for at most n outstanding vector-memory ops
+// and leaves the other counters unconstrained (gfx9 encoding).
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+template <int BM, int BN, int WGM, int WGN, int FA, int FB, int EPI, int QF>
+__device__ __forceinline__ void gemm_tile(const GemmParams& p) {
+    constexpr int NW = WGM * WGN;              // waves per workgroup
+    constexpr int WM = BM / WGM, WN = BN / WGN;  // wave sub-tile
+    constexpr int TM = WM / 32, TN = WN / 32;  // 32 x 32 MFMA tiles per wave
+    constexpr int A_BYTES = BM * BKS, B_BYTES = BN * BKS;
+    constexpr int STAGE = A_BYTES + B_BYTES;
+    constexpr int A_DMA = A_BYTES / 1024 / NW;  // 1 KB direct-to-LDS loads per wave and stage
+    constexpr int B_DMA = B_BYTES / 1024 / NW;
+    constexpr int P = A_DMA + B_DMA;           // vector-memory ops per wave and stage
+    // one LDS array per pipeline stage, so the compiler tracks each stage's loads
+    __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t st2[STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t st3[STAGE];
+
     const int t = threadIdx.x;
     const int lane = t & (kWave - 1);
-    const int wave = t / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(t / kWave);
+    static_assert(A_DMA * NW * 1024 == A_BYTES && B_DMA * NW * 1024 == B_BYTES, "stage split");
     const int64_t M = p.M, N = p.N, K = p.K;
 
     // ---- tile order ---------------------------------------------------------
@@ -85,222 +116,228 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
     const int64_t m0 = (int64_t)tile_m * BM;
     const int64_t n0 = (int64_t)tile_n * BN;
 
-    // ---- global -> LDS staging ---------------------------------------------
-    const uint8_t* __restrict__ A = p.A;
-    const uint8_t* __restrict__ B = p.B;
-    uint4 ra[4], rb[4];
-    auto gload = [&](int64_t k0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int id = t + kThreads * i;
-            const int row = id >> 3;
-            const int64_t k = k0 + (id & 7) * 16;
-            const int64_t gm = m0 + row;
-            const int64_t gn = n0 + row;
-            ra[i] = (gm < M && k < K) ? *reinterpret_cast<const uint4*>(A + gm * K + k)
-                                      : make_uint4(0, 0, 0, 0);
-            rb[i] = (gn < N && k < K) ? *reinterpret_cast<const uint4*>(B + gn * K + k)
-                                      : make_uint4(0, 0, 0, 0);
-        }
+    // ---- global -> LDS, direct ------------------------------------------------
+    // Buffer descriptors cover only this tile's rows, so rows past M (or N) read
+    // as zero in hardware.  A direct-to-LDS load writes lane l's 16 bytes at
+    // base + 16 l, so each lane fetches the global chunk that belongs at its LDS
+    // position: DMA j of this wave fills positions u = (wave * DMA + j) * 64 + lane.
+    const int64_t rows_a = min<int64_t>(BM, M - m0);
+    const int64_t rows_b = min<int64_t>(BN, N - n0);
+    const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.A + m0 * K), (short)0, (int)(rows_a * K), kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.B + n0 * K), (short)0, (int)(rows_b * K), kBufferWord3);
+    uint32_t voff_a[A_DMA], voff_b[B_DMA];
+    int cofs_a[A_DMA], cofs_b[B_DMA];
+    auto place = [&](int u, uint32_t& voff, int& cofs) {
+        const int L = u >> 3;
+        const int x = (u & 7) ^ line_perm(L);
+        const int r = 2 * L + (x >> 2);
+        cofs = (x & 3) * 16;
+        voff = (uint32_t)(r * K + cofs);
     };
-    auto sstore = [&](int buf) {
-        uint8_t* sa = smem + buf * 2 * kStageBytes;
-        uint8_t* sb = sa + kStageBytes;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int id = t + kThreads * i;
-            const int row = id >> 3;
-            const int off = row * BK + swz(row, id & 7) * 16;
-            *reinterpret_cast<uint4*>(sa + off) = ra[i];
-            *reinterpret_cast<uint4*>(sb + off) = rb[i];
-        }
+    for (int j = 0; j < A_DMA; ++j) place((wave * A_DMA + j) * 64 + lane, voff_a[j], cofs_a[j]);
+#pragma unroll
+    for (int j = 0; j < B_DMA; ++j) place((wave * B_DMA + j) * 64 + lane, voff_b[j], cofs_b[j]);
+
+    using lds_ptr = __attribute__((address_space(3))) void*;
+    // One code path for every step: the K offset goes into the (range-checked)
+    // vector offset and chunks at or past K get an out-of-range offset, so the
+    // last partial step and the zero steps past the end read zeros.
+    auto issue = [&](uint8_t* stage, int64_t k0) {
+        uint8_t* sa = stage + wave * A_DMA * 1024;
+        uint8_t* sb = stage + A_BYTES + wave * B_DMA * 1024;
+#pragma unroll
+        for (int j = 0; j < A_DMA; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc_a, (lds_ptr)(sa + j * 1024), 16,
+                k0 + cofs_a[j] < K ? voff_a[j] + (uint32_t)k0 : kOutOfRange, 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < B_DMA; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc_b, (lds_ptr)(sb + j * 1024), 16,
+                k0 + cofs_b[j] < K ? voff_b[j] + (uint32_t)k0 : kOutOfRange, 0, 0, 0);
     };
 
     // ---- MFMA main loop ----------------------------------------------------
-    const int wm = wave >> 1;
-    const int wn = wave & 1;
-    const int fr = lane & 15;   // row of the 16-row operand block this lane feeds
-    const int fg = lane >> 4;   // which 32-byte slice of the 128-byte K step
-    v4f acc[4][4];
+    // A 32x32x64 operand fragment: lane l feeds row l % 32 with the K bytes
+    // [32 (l / 32), +32) of the stage, i.e. chunks 2 (l / 32) and 2 (l / 32) + 1.
+    const int wm = wave / WGN;
+    const int wn = wave % WGN;
+    const int fr = lane & 31;
+    const int fh = lane >> 5;
+    v16f acc[TN][TM];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int i = 0; i < TM; ++i) acc[j][i] = v16f{};
 
-    auto load_frag = [&](const uint8_t* s, int row) -> v8i {
-        const uint4 lo = *reinterpret_cast<const uint4*>(s + row * BK + swz(row, 2 * fg) * 16);
-        const uint4 hi = *reinterpret_cast<const uint4*>(s + row * BK + swz(row, 2 * fg + 1) * 16);
+    auto frag = [&](const uint8_t* s, int r) -> v8i {
+        const uint4 lo = *reinterpret_cast<const uint4*>(s + lds_off(r, 2 * fh));
+        const uint4 hi = *reinterpret_cast<const uint4*>(s + lds_off(r, 2 * fh + 1));
         return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                    (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     };
+    auto compute = [&](const uint8_t* stage) {
+        const uint8_t* sa = stage;
+        const uint8_t* sb = stage + A_BYTES;
+        v8i af[TM];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) af[i] = frag(sa, wm * WM + 32 * i + fr);
+        // D[n][m] = sum_k B[n][k] A[m][k]: the B rows are the MFMA's first operand
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const v8i bf = frag(sb, wn * WN + 32 * j + fr);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    bf, af[i], acc[j][i], FB, FA, 0, 0, 0, 0);
+        }
+    };
+    // Stage kt lives in st[kt % 4]; loads run three stages ahead.  Before reading
+    // stage kt a wave waits for its own loads of that stage (the two later stages
+    // may stay in flight), then the barrier makes every wave's loads visible and
+    // frees the stage read in the previous step, which is refilled right away.
+    // The barrier is a bare s_barrier: __syncthreads() adds a workgroup fence,
+    // which waits for every outstanding load, the prefetched stages included.
+    // The barrier also waits for the wave's own LDS reads, so no wave refills a
+    // stage another wave is still reading.  Every step
+    // looks the same: past the end of K the stages are filled with zeros (all
+    // chunks out of range), which add nothing to the sums, so the wait count is
+    // a constant and the loop runs a multiple of four steps.
+    auto step = [&](uint8_t* cur, uint8_t* refill, int kt) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * P));
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        issue(refill, (int64_t)(kt + 3) * BKS);
+        compute(cur);
+    };
 
-    const int nk = (int)((K + BK - 1) / BK);
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        if (kt + 1 < nk) gload((int64_t)(kt + 1) * BK);
-        const uint8_t* sa = smem + (kt & 1) * 2 * kStageBytes;
-        const uint8_t* sb = sa + kStageBytes;
-        v8i af[4], bfr[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) af[i] = load_frag(sa, wm * 64 + i * 16 + fr);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) bfr[j] = load_frag(sb, wn * 64 + j * 16 + fr);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    af[i], bfr[j], acc[i][j], FA, FB, 0, 0, 0, 0);
-        if (kt + 1 < nk) sstore((kt + 1) & 1);
-        __syncthreads();
+    const int nk = (int)((K + BKS - 1) / BKS);
+    issue(st0, 0);
+    issue(st1, BKS);
+    issue(st2, 2 * BKS);
+    for (int kt = 0; kt < nk; kt += 4) {
+        step(st0, st3, kt);
+        step(st1, st0, kt + 1);
+        step(st2, st1, kt + 2);
+        step(st3, st2, kt + 3);
     }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // the zero-filled look-ahead stages
 
-    // ---- epilogue: accumulators -> LDS tile (row-major fp32) ------------------
-    float* cs = reinterpret_cast<float*>(smem);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                cs[(wm * 64 + i * 16 + 4 * fg + r) * kCPitch + wn * 64 + j * 16 + fr] = acc[i][j][r];
-    __syncthreads();
-
+    // ---- epilogue straight from the accumulators -----------------------------
+    // acc[j][i] register r holds C[m][n] with m = m0 + wm WM + 32 i + (lane % 32)
+    // and n = n0 + wn WN + 32 j + 8 (r / 4) + 4 (lane / 32) + (r % 4).
     const float alpha = (*p.sinv_a) * (*p.sinv_b);
-    // thread t handles 8 chunks of 8 consecutive columns: id = t + 256 i,
-    // row = id / 16, columns 8 * (id % 16) .. +7
-    uint2 codes[8];
-    uint32_t amax_bits = 0;
     float qs = 0.0f;
     if constexpr (EPI == kEpiGeluFp8) qs = *p.q_scale;
+    uint32_t amax_bits = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int id = t + kThreads * i;
-        const int row = id >> 4;
-        const int c8 = (id & 15) * 8;
-        const int64_t gm = m0 + row;
-        const int64_t gn = n0 + c8;
-        const float4 lo = *reinterpret_cast<const float4*>(cs + row * kCPitch + c8);
-        const float4 hi = *reinterpret_cast<const float4*>(cs + row * kCPitch + c8 + 4);
-        float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        const bool ok = gm < M && gn < N;
+    for (int i = 0; i < TM; ++i) {
+        const int64_t gm = m0 + wm * WM + 32 * i + fr;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] *= alpha;
-        if constexpr (EPI == kEpiBf16Bias || EPI == kEpiGeluFp8) {
-            if (p.bias && ok) {
-                float bb[8];
-                unpack_bf16x8(*reinterpret_cast<const uint4*>(p.bias + gn), bb);
+        for (int j = 0; j < TN; ++j) {
 #pragma unroll
-                for (int k = 0; k < 8; ++k) v[k] += bb[k];
-            }
-        }
-        if constexpr (EPI == kEpiBf16Bias) {
-            if (ok) {
-                uint4 w;
-                w.x = pack_bf16x2(v[0], v[1]);
-                w.y = pack_bf16x2(v[2], v[3]);
-                w.z = pack_bf16x2(v[4], v[5]);
-                w.w = pack_bf16x2(v[6], v[7]);
-                *reinterpret_cast<uint4*>((uint16_t*)p.out + gm * N + gn) = w;
-            }
-        } else if constexpr (EPI == kEpiF32) {
-            if (ok) {
-                float4* o = reinterpret_cast<float4*>((float*)p.out + gm * N + gn);
-                o[0] = make_float4(v[0], v[1], v[2], v[3]);
-                o[1] = make_float4(v[4], v[5], v[6], v[7]);
-            }
-        } else if constexpr (EPI == kEpiDGeluF32) {
-            if (ok) {
-                float hh[8];
-                unpack_bf16x8(*reinterpret_cast<const uint4*>(p.h_in + gm * N + gn), hh);
+            for (int q = 0; q < 4; ++q) {
+                const int64_t gn = n0 + wn * WN + 32 * j + 8 * q + 4 * fh;
+                const bool ok = gm < M && gn < N;
+                float v[4];
 #pragma unroll
-                for (int k = 0; k < 8; ++k) v[k] *= gelu_grad_f(hh[k]);
-                float4* o = reinterpret_cast<float4*>((float*)p.out + gm * N + gn);
-                o[0] = make_float4(v[0], v[1], v[2], v[3]);
-                o[1] = make_float4(v[4], v[5], v[6], v[7]);
-            }
-        } else {   // kEpiGeluFp8
-            if (ok && p.h_out) {
-                uint4 w;
-                w.x = pack_bf16x2(v[0], v[1]);
-                w.y = pack_bf16x2(v[2], v[3]);
-                w.z = pack_bf16x2(v[4], v[5]);
-                w.w = pack_bf16x2(v[6], v[7]);
-                *reinterpret_cast<uint4*>(p.h_out + gm * N + gn) = w;
-            }
-            float g[8], gs[8];
-            uint32_t cm = 0;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                g[k] = gelu_f(v[k], nullptr);
-                const uint32_t ab = abs_bits(g[k]);
-                cm = cm > ab ? cm : ab;
-                gs[k] = g[k] * qs;
-            }
-            uint2 q;
-            q.x = encode4<QF>(gs[0], gs[1], gs[2], gs[3]);
-            q.y = encode4<QF>(gs[4], gs[5], gs[6], gs[7]);
-            if (__builtin_expect(cm > kInfBits, 0)) {
-                q.x = patch_nan4(q.x, gs);
-                q.y = patch_nan4(q.y, gs + 4);
-            }
-            codes[i] = q;
-            if (ok) {
-                *reinterpret_cast<uint2*>(p.q_out + gm * N + gn) = q;
-                amax_bits = amax_bits > cm ? amax_bits : cm;
-            }
-        }
-    }
-
-    if constexpr (EPI == kEpiGeluFp8) {
-        if (p.q_out_t) {
-            __syncthreads();   // every thread is done reading the fp32 tile
-            uint8_t* ct = smem;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int id = t + kThreads * i;
-                *reinterpret_cast<uint2*>(ct + (id >> 4) * kCodePitch + (id & 15) * 8) = codes[i];
-            }
-            __syncthreads();
-            // thread t writes 8 chunks of 8 consecutive rows of one column:
-            // id = t + 256 i, column = id / 16, rows 8 * (id % 16) .. +7
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int id = t + kThreads * i;
-                const int col = id >> 4;
-                const int r8 = (id & 15) * 8;
-                const int64_t gn = n0 + col;
-                const int64_t gm = m0 + r8;
-                if (gn < N && gm < M) {
-                    uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        w0 |= (uint32_t)ct[(r8 + k) * kCodePitch + col] << (8 * k);
-                        w1 |= (uint32_t)ct[(r8 + 4 + k) * kCodePitch + col] << (8 * k);
+                for (int e = 0; e < 4; ++e) v[e] = acc[j][i][4 * q + e] * alpha;
+                if constexpr (EPI == kEpiBf16Bias || EPI == kEpiGeluFp8) {
+                    if (p.bias && ok) {
+                        const uint2 bw = *reinterpret_cast<const uint2*>(p.bias + gn);
+                        v[0] += bf16_lo(bw.x); v[1] += bf16_hi(bw.x);
+                        v[2] += bf16_lo(bw.y); v[3] += bf16_hi(bw.y);
                     }
-                    uint8_t* dst = p.q_out_t + gn * M + gm;
-                    if (gm + 8 <= M) {
-                        *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
-                    } else {
-                        for (int k = 0; gm + k < M; ++k)
-                            dst[k] = (uint8_t)((k < 4 ? w0 : w1) >> (8 * (k & 3)));
+                }
+                if constexpr (EPI == kEpiBf16Bias) {
+                    if (ok)
+                        *reinterpret_cast<uint2*>((uint16_t*)p.out + gm * N + gn) =
+                            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                } else if constexpr (EPI == kEpiF32) {
+                    if (ok)
+                        *reinterpret_cast<float4*>((float*)p.out + gm * N + gn) =
+                            make_float4(v[0], v[1], v[2], v[3]);
+                } else if constexpr (EPI == kEpiDGeluF32) {
+                    if (ok) {
+                        const uint2 hw = *reinterpret_cast<const uint2*>(p.h_in + gm * N + gn);
+                        v[0] *= gelu_grad_f(bf16_lo(hw.x));
+                        v[1] *= gelu_grad_f(bf16_hi(hw.x));
+                        v[2] *= gelu_grad_f(bf16_lo(hw.y));
+                        v[3] *= gelu_grad_f(bf16_hi(hw.y));
+                        *reinterpret_cast<float4*>((float*)p.out + gm * N + gn) =
+                            make_float4(v[0], v[1], v[2], v[3]);
+                    }
+                } else {   // kEpiGeluFp8
+                    if (ok) {
+                        if (p.h_out)
+                            *reinterpret_cast<uint2*>(p.h_out + gm * N + gn) =
+                                make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                        float gs[4];
+                        uint32_t cm = 0;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float g = gelu_f(v[e], nullptr);
+                            const uint32_t ab = abs_bits(g);
+                            cm = cm > ab ? cm : ab;
+                            gs[e] = g * qs;
+                        }
+                        uint32_t code = encode4<QF>(gs[0], gs[1], gs[2], gs[3]);
+                        if (__builtin_expect(cm > kInfBits, 0)) code = patch_nan4(code, gs);
+                        *reinterpret_cast<uint32_t*>(p.q_out + gm * N + gn) = code;
+                        if (p.q_out_t) {
+                            // lanes with consecutive m write consecutive bytes of a row
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                p.q_out_t[(gn + e) * M + gm] = (uint8_t)(code >> (8 * e));
+                        }
+                        amax_bits = amax_bits > cm ? amax_bits : cm;
                     }
                 }
             }
         }
-        __shared__ uint32_t red[kThreads / kWave];
+    }
+    if constexpr (EPI == kEpiGeluFp8) {
+        __shared__ uint32_t red[NW];
         block_amax_atomic(amax_bits, p.q_amax, red);
     }
 }
 
+// 256 x 256 tiles, eight waves of 64 x 128 (two waves per SIMD).
+constexpr int kBigWavesM = 4, kBigWavesN = 2;
+
+template <int FA, int FB, int EPI, int QF>
+__global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(64 * kBigWavesM * kBigWavesN)
+void gemm_kernel_256(GemmParams p) {
+    gemm_tile<256, 256, kBigWavesM, kBigWavesN, FA, FB, EPI, QF>(p);
+}
+
+// 128 x 128 tiles, four waves of 64 x 64, two workgroups per CU.
+template <int FA, int FB, int EPI, int QF>
+__global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(256)
+void gemm_kernel_128(GemmParams p) {
+    gemm_tile<128, 128, 2, 2, FA, FB, EPI, QF>(p);
+}
+
+template <int BM, int BN, int FA, int FB, int EPI, int QF>
+hipError_t launch_tile(const GemmParams& p, hipStream_t stream) {
+    const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+    if constexpr (BM == 256)
+        hipLaunchKernelGGL((gemm_kernel_256<FA, FB, EPI, QF>), dim3((unsigned)tiles),
+                           dim3(64 * kBigWavesM * kBigWavesN), 0, stream, p);
+    else
+        hipLaunchKernelGGL((gemm_kernel_128<FA, FB, EPI, QF>), dim3((unsigned)tiles),
+                           dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+// 256 x 256 tiles when they give at least one tile per CU, else 128 x 128.
 template <int FA, int FB, int EPI, int QF>
 hipError_t launch_typed(const GemmParams& p, hipStream_t stream) {
-    const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-    hipLaunchKernelGGL((gemm_kernel<FA, FB, EPI, QF>), dim3((unsigned)tiles), dim3(kThreads), 0,
-                       stream, p);
-    return hipGetLastError();
+    const int64_t big = ((p.M + 255) / 256) * ((p.N + 255) / 256);
+    if (big >= 256) return launch_tile<256, 256, FA, FB, EPI, QF>(p, stream);
+    return launch_tile<128, 128, FA, FB, EPI, QF>(p, stream);
 }
 
 template <int FA, int FB>

@@ -24,6 +24,11 @@ constexpr int kThreads = 256;
 constexpr int kWavesPerBlock = kThreads / kWave;
 
 // CPL: 16-byte chunks per lane (hidden <= CPL * 64 * 8).
+//
+// Memory-level parallelism: a wave loads the next row it owns before it works on
+// the current one, so two rows per wave are in flight; gamma and beta stay in
+// registers as packed bf16 (half the registers of fp32 copies) and are widened
+// when used.  Row statistics use DPP reductions inside 16-lane rows.
 template <int CPL, int FMT>
 __global__ __launch_bounds__(kThreads) void ln_cast_amax_kernel(
     const uint4* __restrict__ x, const uint4* __restrict__ gamma, const uint4* __restrict__ beta,
@@ -37,39 +42,45 @@ __global__ __launch_bounds__(kThreads) void ln_cast_amax_kernel(
     const float inv_h = 1.0f / (float)hidden;
     const float s = *scale_ptr;
 
-    constexpr bool kCacheParams = CPL <= 4;
-    float g[kCacheParams ? CPL * 8 : 1];
-    float b[kCacheParams ? CPL * 8 : 1];
-    if constexpr (kCacheParams) {
+    uint4 gp[CPL], bp[CPL];   // packed bf16 gamma / beta of this lane's chunks
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-            const int c = lane + i * kWave;
-            if (c < nchunk) {
-                unpack_bf16x8(gamma[c], g + 8 * i);
-                unpack_bf16x8(beta[c], b + 8 * i);
-            }
-        }
+    for (int i = 0; i < CPL; ++i) {
+        const int c = lane + i * kWave;
+        gp[i] = c < nchunk ? gamma[c] : make_uint4(0, 0, 0, 0);
+        bp[i] = c < nchunk ? beta[c] : make_uint4(0, 0, 0, 0);
     }
 
-    uint32_t amax_bits = 0;
-    for (int64_t row = (int64_t)blockIdx.x * kWavesPerBlock + wave; row < rows;
-         row += (int64_t)gridDim.x * kWavesPerBlock) {
-        const uint4* xr = x + row * nchunk;
-        float v[CPL * 8];
-        uint4 raw[CPL];
+    const int64_t stride = (int64_t)gridDim.x * kWavesPerBlock;
+    int64_t row = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+    uint4 nxt[CPL];
+    auto load_row = [&](int64_t r, uint4* dst) {
+        const uint4* xr = x + r * nchunk;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
             const int c = lane + i * kWave;
-            raw[i] = c < nchunk ? xr[c] : make_uint4(0, 0, 0, 0);
+            dst[i] = (r < rows && c < nchunk) ? xr[c] : make_uint4(0, 0, 0, 0);
         }
+    };
+    load_row(row, nxt);
+
+    uint32_t amax_bits = 0;
+    for (; row < rows; row += stride) {
+        // Keep gamma/beta packed across iterations: without this the compiler
+        // hoists their widening out of the loop and holds 16 fp32 per chunk.
+#pragma unroll
+        for (int i = 0; i < CPL; ++i)
+            asm volatile("" : "+v"(gp[i].x), "+v"(gp[i].y), "+v"(gp[i].z), "+v"(gp[i].w),
+                         "+v"(bp[i].x), "+v"(bp[i].y), "+v"(bp[i].z), "+v"(bp[i].w));
+        float v[CPL * 8];
         float sum = 0.0f;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
-            unpack_bf16x8(raw[i], v + 8 * i);
+            unpack_bf16x8(nxt[i], v + 8 * i);
 #pragma unroll
             for (int k = 0; k < 8; ++k) sum += v[8 * i + k];
         }
-        const float mu = wave_sum(sum) * inv_h;
+        load_row(row + stride, nxt);   // next row in flight while this one is processed
+        const float mu = wave_sum_dpp(sum) * inv_h;
         float sq = 0.0f;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
@@ -81,7 +92,7 @@ __global__ __launch_bounds__(kThreads) void ln_cast_amax_kernel(
                 sq += d * d;
             }
         }
-        const float var = wave_sum(sq) * inv_h;
+        const float var = wave_sum_dpp(sq) * inv_h;
         const float rs = 1.0f / sqrtf(var + eps);
 
         uint2* orow = out + row * nchunk;
@@ -90,13 +101,8 @@ __global__ __launch_bounds__(kThreads) void ln_cast_amax_kernel(
             const int c = lane + i * kWave;
             if (c < nchunk) {
                 float gg[8], bb[8];
-                if constexpr (kCacheParams) {
-#pragma unroll
-                    for (int k = 0; k < 8; ++k) { gg[k] = g[8 * i + k]; bb[k] = b[8 * i + k]; }
-                } else {
-                    unpack_bf16x8(gamma[c], gg);
-                    unpack_bf16x8(beta[c], bb);
-                }
+                unpack_bf16x8(gp[i], gg);
+                unpack_bf16x8(bp[i], bb);
                 float y[8];
                 uint32_t cm = 0;
 #pragma unroll
@@ -132,8 +138,11 @@ hipError_t launch_ln_fwd_cpl(int64_t rows, int hidden, const void* x, const void
                              const void* beta, float eps, int fp8, const float* scale,
                              float* amax, uint8_t* out, float* mean, float* rstd,
                              hipStream_t stream) {
+    // Resident grid: as many workgroups as the CUs hold at once (register-limited
+    // occupancy, one wave per SIMD per workgroup), each looping over rows, so the
+    // row prefetch runs across the whole sweep instead of restarting per wave.
     int64_t want = (rows + kWavesPerBlock - 1) / kWavesPerBlock;
-    const int64_t cap = 256 * 16;   // 16 blocks per CU on 256 CUs, then grid-stride
+    const int64_t cap = 256 * (CPL <= 1 ? 8 : CPL <= 2 ? 6 : CPL <= 4 ? 4 : 2);
     const int blocks = (int)(want < cap ? want : cap);
     if (fp8 == kE4M3)
         hipLaunchKernelGGL((ln_cast_amax_kernel<CPL, kE4M3>), dim3(blocks), dim3(kThreads), 0,

@@ -21,7 +21,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMaxHist = 1024;
 constexpr int kMaxSlots = 8;
-constexpr int kPerThread = kMaxHist * kMaxSlots / kThreads;   // values moved per thread
+constexpr int kPerThread = kMaxHist * kMaxSlots / kThreads;   // history values per thread
 
 __global__ __launch_bounds__(kThreads) void meta_init_kernel(float* hist, float* scale,
                                                             float* scale_inv, int total,
@@ -34,67 +34,77 @@ __global__ __launch_bounds__(kThreads) void meta_init_kernel(float* hist, float*
     }
 }
 
-// One workgroup updates every slot of one state block.
+// One workgroup updates every slot of one state block in a single pass over the
+// history: every thread loads its share once into registers, the per-slot max
+// comes from those registers, and the shifted rows are written back from them.
 __global__ __launch_bounds__(kThreads) void scaling_update_kernel(float* hist, float* scale,
                                                                  float* scale_inv, int len,
                                                                  int n_slots, int margin,
                                                                  float fp8_max) {
-    __shared__ float red_max[kThreads / kWave];
-    __shared__ int red_nan[kThreads / kWave];
+    __shared__ float red_max[kThreads / kWave][kMaxSlots];
+    __shared__ int red_nan[kThreads / kWave][kMaxSlots];
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
+    const int total = len * n_slots;
 
-    for (int s = 0; s < n_slots; ++s) {
-        float m = 0.0f;
-        int nan = 0;
-        for (int i = tid; i < len; i += kThreads) {
-            const float v = hist[i * n_slots + s];
-            nan |= (v != v);
-            m = fmaxf(m, v);
+    // flat index j = tid + 256 t; its slot is j % n_slots
+    float keep[kPerThread];
+    float m[kMaxSlots];
+    int nan[kMaxSlots];
+#pragma unroll
+    for (int s = 0; s < kMaxSlots; ++s) { m[s] = 0.0f; nan[s] = 0; }
+#pragma unroll
+    for (int t = 0; t < kPerThread; ++t) {
+        const int j = tid + t * kThreads;
+        keep[t] = j < total ? hist[j] : 0.0f;
+        if (j < total) {
+            const int s = j % n_slots;
+#pragma unroll
+            for (int q = 0; q < kMaxSlots; ++q) {
+                if (q == s) {
+                    nan[q] |= (keep[t] != keep[t]);
+                    m[q] = fmaxf(m[q], keep[t]);
+                }
+            }
         }
+    }
+#pragma unroll
+    for (int q = 0; q < kMaxSlots; ++q) {
 #pragma unroll
         for (int off = kWave / 2; off > 0; off >>= 1) {
-            m = fmaxf(m, __shfl_xor(m, off, kWave));
-            nan |= __shfl_xor(nan, off, kWave);
+            m[q] = fmaxf(m[q], __shfl_xor(m[q], off, kWave));
+            nan[q] |= __shfl_xor(nan[q], off, kWave);
         }
         if (lane == 0) {
-            red_max[wave] = m;
-            red_nan[wave] = nan;
+            red_max[wave][q] = m[q];
+            red_nan[wave][q] = nan[q];
         }
-        __syncthreads();
-        if (tid == 0) {
-            float a = 0.0f;
-            int any_nan = 0;
-            for (int w = 0; w < kThreads / kWave; ++w) {
-                a = fmaxf(a, red_max[w]);
-                any_nan |= red_nan[w];
-            }
-            float sc = scale[s];
-            if (!any_nan && a > 0.0f && a <= 3.402823466e38f) {
-                float ns = fp8_max / a;          // IEEE binary32 division
-                ns = ldexpf(ns, -margin);        // exact unless the result is subnormal
-                if (ns > 0.0f && ns <= 3.402823466e38f) sc = ns;
-            }
-            scale[s] = sc;
-            scale_inv[s] = 1.0f / sc;
-        }
-        __syncthreads();
-    }
-
-    // Roll: row i <- row i-1 for i >= 1, row 0 <- 0.  Read everything first.
-    const int moved = (len - 1) * n_slots;   // values in rows 0 .. len-2
-    float keep[kPerThread];
-#pragma unroll
-    for (int t = 0; t < kPerThread; ++t) {
-        const int j = tid + t * kThreads;
-        keep[t] = j < moved ? hist[j] : 0.0f;
     }
     __syncthreads();
+    if (tid < n_slots) {
+        float a = 0.0f;
+        int any_nan = 0;
+        for (int w = 0; w < kThreads / kWave; ++w) {
+            a = fmaxf(a, red_max[w][tid]);
+            any_nan |= red_nan[w][tid];
+        }
+        float sc = scale[tid];
+        if (!any_nan && a > 0.0f && a <= 3.402823466e38f) {
+            float ns = fp8_max / a;          // IEEE binary32 division
+            ns = ldexpf(ns, -margin);        // exact unless the result is subnormal
+            if (ns > 0.0f && ns <= 3.402823466e38f) sc = ns;
+        }
+        scale[tid] = sc;
+        scale_inv[tid] = 1.0f / sc;
+    }
+    // Roll: row i <- row i-1 for i >= 1, row 0 <- 0, from the registers.  Every
+    // value was read before the barrier above, so no thread overwrites a value
+    // another thread still has to read.
 #pragma unroll
     for (int t = 0; t < kPerThread; ++t) {
         const int j = tid + t * kThreads;
-        if (j < moved) hist[j + n_slots] = keep[t];
+        if (j + n_slots < total) hist[j + n_slots] = keep[t];
     }
     if (tid < n_slots) hist[tid] = 0.0f;
 }
