@@ -32,6 +32,7 @@ OP_CAST_AMAX = 0
 OP_LAYERNORM_BWD = 1
 OP_LN_LINEAR_BWD = 2
 OP_LN_MLP_BWD = 3
+OP_GEMM_DGELU_FP8 = 4
 
 
 class Recipe(C.Structure):
@@ -79,6 +80,8 @@ SIGNATURES = {
     "fp8ln_gemm_gelu_fp8": (C.c_int, [_I64, _I64, _I64, _P, _I32, _P, _I32, _P, _P, _P, _P, _P,
                                       _P, _I32, _P, _P, _P]),
     "fp8ln_gemm_dgelu": (C.c_int, [_I64, _I64, _I64, _P, _I32, _P, _I32, _P, _P, _P, _P, _P]),
+    "fp8ln_gemm_dgelu_fp8": (C.c_int, [_I64, _I64, _I64, _P, _I32, _P, _I32, _P, _P, _P, _I32, _P,
+                                       _P, _P, _P, _P, _P, _SZ, _P]),
     "fp8ln_layernorm_bwd": (C.c_int, [_I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "fp8ln_ln_linear_fwd": (C.c_int, [_RP, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _MP,
                                       C.POINTER(LinearCtxStruct), _P]),

@@ -161,10 +161,14 @@ LinearWs linear_ws(void* base, int64_t M, int64_t K, int64_t N) {
     return w;
 }
 
+size_t dgelu_workspace(int64_t M, int64_t N) {
+    return (size_t)gemm_partial_rows_bound(M) * (size_t)N * sizeof(float);
+}
+
 struct MlpWs {
     uint8_t* dy_q;
     uint8_t* dy_qt;
-    float* dh;
+    float* dh_part;   // column sums of dH per GEMM tile row
     uint8_t* dh_q;
     uint8_t* dh_qt;
     float* dln;
@@ -178,12 +182,11 @@ MlpWs mlp_ws(void* base, int64_t M, int64_t H, int64_t F) {
     MlpWs w;
     w.dy_q = (uint8_t*)c.take((size_t)(M * H));
     w.dy_qt = (uint8_t*)c.take((size_t)(M * H));
-    w.dh = (float*)c.take((size_t)(M * F) * sizeof(float));
+    w.dh_part = (float*)c.take(dgelu_workspace(M, F));
     w.dh_q = (uint8_t*)c.take((size_t)(M * F));
     w.dh_qt = (uint8_t*)c.take((size_t)(M * F));
     w.dln = (float*)c.take((size_t)(M * H) * sizeof(float));
-    const size_t cw = std::max(cast_workspace(M, H), cast_workspace(M, F));
-    w.cast_ws = c.take(cw);
+    w.cast_ws = c.take(cast_workspace(M, H));
     w.ln_ws = c.take(ln_bwd_workspace(M, (int)H));
     w.bytes = c.used;
     return w;
@@ -237,6 +240,7 @@ size_t fp8ln_workspace_size(int32_t op, int64_t a, int64_t b, int64_t c) {
     switch (op) {
         case FP8LN_OP_CAST_AMAX: return cast_workspace(a, b);
         case FP8LN_OP_LAYERNORM_BWD: return ln_bwd_workspace(a, (int)b);
+        case FP8LN_OP_GEMM_DGELU_FP8: return dgelu_workspace(a, b);
         case FP8LN_OP_LN_LINEAR_BWD: return c > 0 ? linear_ws(nullptr, a, b, c).bytes : 0;
         case FP8LN_OP_LN_MLP_BWD: return c > 0 ? mlp_ws(nullptr, a, b, c).bytes : 0;
         default: return 0;
@@ -425,6 +429,50 @@ int fp8ln_gemm_dgelu(int64_t M, int64_t N, int64_t K, const uint8_t* A, int32_t 
     p.h_in = (const uint16_t*)h;
     p.out = out;
     FP8LN_TRY(launch_gemm(p, as_stream(stream)), "gemm_dgelu launch");
+    return FP8LN_OK;
+}
+
+int fp8ln_gemm_dgelu_fp8(int64_t M, int64_t N, int64_t K, const uint8_t* A, int32_t a_dtype,
+                         const uint8_t* B, int32_t b_dtype, const float* sinv_a,
+                         const float* sinv_b, const void* h, int32_t q_dtype,
+                         const float* q_scale, float* q_amax, uint8_t* q_out, uint8_t* q_out_t,
+                         float* dbias, void* workspace, size_t workspace_bytes, void* stream) {
+    REQUIRE(M >= 0 && N >= 0 && K >= 0, "negative size");
+    REQUIRE(a_dtype == FP8LN_E4M3 || a_dtype == FP8LN_E5M2, "a_dtype %d invalid", a_dtype);
+    REQUIRE(b_dtype == FP8LN_E4M3 || b_dtype == FP8LN_E5M2, "b_dtype %d invalid", b_dtype);
+    REQUIRE(q_dtype == FP8LN_E4M3 || q_dtype == FP8LN_E5M2, "q_dtype %d invalid", q_dtype);
+    if (N % 16 != 0 || K % 16 != 0)
+        return fail(FP8LN_ERR_UNSUPPORTED, "N and K must be multiples of 16 (N=%lld K=%lld)",
+                    (long long)N, (long long)K);
+    if (q_out_t && M % 16 != 0)
+        return fail(FP8LN_ERR_UNSUPPORTED, "a transposed output needs M %% 16 == 0");
+    REQUIRE_PTR(sinv_a); REQUIRE_PTR(sinv_b); REQUIRE_PTR(q_scale); REQUIRE_PTR(q_amax);
+    if (M > 0 && N > 0) {
+        REQUIRE_PTR(q_out); REQUIRE_PTR(h); REQUIRE_ALIGNED(q_out); REQUIRE_ALIGNED(h);
+        if (q_out_t) REQUIRE_ALIGNED(q_out_t);
+        if (K > 0) { REQUIRE_PTR(A); REQUIRE_PTR(B); REQUIRE_ALIGNED(A); REQUIRE_ALIGNED(B); }
+    }
+    if (dbias) {
+        REQUIRE(workspace && workspace_bytes >= dgelu_workspace(M, N),
+                "column sums need %zu bytes of workspace", dgelu_workspace(M, N));
+        REQUIRE_ALIGNED(workspace);
+    }
+    int s = check_current_device();
+    if (s) return s;
+    hipStream_t st = as_stream(stream);
+    GemmParams p = gemm_params(M, N, K, A, a_dtype, B, b_dtype, sinv_a, sinv_b, kEpiDGeluFp8);
+    p.h_in = (const uint16_t*)h;
+    p.q_out = q_out;
+    p.q_out_t = q_out_t;
+    p.q_scale = q_scale;
+    p.q_amax = q_amax;
+    p.q_fp8 = q_dtype;
+    p.col_partial = dbias ? (float*)workspace : nullptr;
+    FP8LN_TRY(launch_gemm(p, st), "gemm_dgelu_fp8 launch");
+    if (dbias)
+        FP8LN_TRY(launch_sum_partials((const float*)workspace, M > 0 ? gemm_partial_rows(M, N) : 0,
+                                      N, dbias, nullptr, N, st),
+                  "column sum launch");
     return FP8LN_OK;
 }
 
@@ -680,15 +728,22 @@ int fp8ln_ln_mlp_bwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t hidden,
     FP8LN_TRY(launch_cast_amax(M, H, false, dy, bf, bwd->scale + 0, bwd->amax_history + 0, w.dy_q,
                                w.dy_qt, db2, w.cast_ws, st),
               "fc2 grad cast launch");
-    // fc2 dgrad with the GELU derivative: dH[M][F] = dy_q[M][H] . (w2_qt[F][H])^T * gelu'(h)
+    // fc2 dgrad with the GELU derivative and the fc1 gradient cast fused:
+    // dH[M][F] = dy_q[M][H] . (w2_qt[F][H])^T * gelu'(h) -> dh_q, dh_qt, amax, db1
     GemmParams dg2 = gemm_params(M, F, H, w.dy_q, bf, ctx->w2_qt, ff, bwd->scale_inv + 0,
-                                 fwd->scale_inv + 3, kEpiDGeluF32);
-    dg2.out = w.dh;
+                                 fwd->scale_inv + 3, kEpiDGeluFp8);
     dg2.h_in = ctx->h;
+    dg2.q_out = w.dh_q;
+    dg2.q_out_t = w.dh_qt;
+    dg2.q_scale = bwd->scale + 1;
+    dg2.q_amax = bwd->amax_history + 1;
+    dg2.q_fp8 = bf;
+    dg2.col_partial = db1 ? w.dh_part : nullptr;
     FP8LN_TRY(launch_gemm(dg2, st), "fc2 dgrad launch");
-    FP8LN_TRY(launch_cast_amax(M, F, true, w.dh, bf, bwd->scale + 1, bwd->amax_history + 1, w.dh_q,
-                               w.dh_qt, db1, w.cast_ws, st),
-              "fc1 grad cast launch");
+    if (db1)
+        FP8LN_TRY(launch_sum_partials(w.dh_part, M > 0 ? gemm_partial_rows(M, F) : 0, F, db1,
+                                      nullptr, F, st),
+                  "db1 launch");
     // fc2 wgrad: dW2[H][F] = dy_qt[H][M] . (g_qt[F][M])^T
     GemmParams wg2 = gemm_params(H, F, M, w.dy_qt, bf, ctx->g_qt, ff, bwd->scale_inv + 0,
                                  fwd->scale_inv + 2, kEpiF32);

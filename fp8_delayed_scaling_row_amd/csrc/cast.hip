@@ -17,104 +17,120 @@ namespace fp8ln {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTile = 64;           // rows and columns of one tile
+constexpr int kTile = 64;           // rows and columns of one transposition tile
 constexpr int kTPad = kTile + 16;   // byte pitch of the transposition tile
+constexpr int kCT = 128;            // rows and columns of one cast tile
+constexpr int kCPitch = kCT + 4;    // byte pitch of the cast kernel's transposed codes
 
-// One block casts a 64 x 64 tile; thread t owns row t/4, columns 16*(t%4) .. +15.
+// One workgroup casts a 128 x 128 tile.  Thread t owns columns 8 (t % 16) .. +7
+// of rows 4 (t / 16) .. +3 and 64 + 4 (t / 16) .. +3, so each row is read and
+// written by 16 consecutive lanes as one contiguous segment.  For the
+// transposed copy a thread packs the codes of its four consecutive rows of one
+// column into a word in LDS; the tile then leaves as full 128-byte rows of the
+// transposed output.  Column sums of the tile (for the bias gradient) are
+// formed in a fixed order: a thread's eight rows, then the sixteen threads of a
+// column in order of t / 16.
 template <bool IN_F32, int FMT>
 __global__ __launch_bounds__(kThreads) void cast_tile_kernel(
     const void* __restrict__ in, int64_t rows, int64_t cols, const float* __restrict__ scale_ptr,
     float* __restrict__ amax_ptr, uint8_t* __restrict__ out, uint8_t* __restrict__ out_t,
     float* __restrict__ partial) {
-    __shared__ uint8_t tq[kTile][kTPad];
-    __shared__ float tv[kTile][kTile + 1];
+    __shared__ uint32_t tq[kCT * kCPitch / 4];
+    __shared__ float psum[kThreads / 16][kCT];
     __shared__ uint32_t red[kThreads / kWave];
     const int t = threadIdx.x;
-    const int lr = t / 4;
-    const int lc = (t % 4) * 16;
-    const int64_t r = (int64_t)blockIdx.y * kTile + lr;
-    const int64_t c0 = (int64_t)blockIdx.x * kTile + lc;
+    const int j = t % 16;
+    const int p = t / 16;
+    const int64_t r0 = (int64_t)blockIdx.y * kCT;
+    const int64_t c0 = (int64_t)blockIdx.x * kCT + 8 * j;
+    const bool col_ok = c0 < cols;   // cols % 16 == 0: a group is all in or all out
     const float s = *scale_ptr;
-    const bool active = r < rows && c0 < cols;
-
-    float v[16];
-    if (active) {
-        if constexpr (IN_F32) {
-            const float4* p = reinterpret_cast<const float4*>((const float*)in + r * cols + c0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float4 w = p[i];
-                v[4 * i + 0] = w.x; v[4 * i + 1] = w.y; v[4 * i + 2] = w.z; v[4 * i + 3] = w.w;
-            }
-        } else {
-            const uint4* p = reinterpret_cast<const uint4*>((const uint16_t*)in + r * cols + c0);
-            unpack_bf16x8(p[0], v);
-            unpack_bf16x8(p[1], v + 8);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = 0.0f;
-    }
 
     uint32_t cm = 0;
-    float vs[16];
+    float cs[8];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const uint32_t ab = abs_bits(v[i]);
-        cm = cm > ab ? cm : ab;
-        vs[i] = mul_round_odd(v[i], s);
-    }
-    uint4 q;
-    q.x = encode4<FMT>(vs[0], vs[1], vs[2], vs[3]);
-    q.y = encode4<FMT>(vs[4], vs[5], vs[6], vs[7]);
-    q.z = encode4<FMT>(vs[8], vs[9], vs[10], vs[11]);
-    q.w = encode4<FMT>(vs[12], vs[13], vs[14], vs[15]);
-    if (__builtin_expect(cm > kInfBits, 0)) {
-        q.x = patch_nan4(q.x, vs);
-        q.y = patch_nan4(q.y, vs + 4);
-        q.z = patch_nan4(q.z, vs + 8);
-        q.w = patch_nan4(q.w, vs + 12);
-    }
-    if (active) *reinterpret_cast<uint4*>(out + r * cols + c0) = q;
-
-    if (out_t) {
-        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    for (int e = 0; e < 8; ++e) cs[e] = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) tq[lc + i][lr] = (uint8_t)(w[i / 4] >> (8 * (i % 4)));
+    for (int half = 0; half < 2; ++half) {
+        uint32_t packed[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) packed[e] = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t r = r0 + 64 * half + 4 * p + i;
+            const bool ok = col_ok && r < rows;
+            float v[8];
+            if (ok) {
+                if constexpr (IN_F32) {
+                    const float4* q = reinterpret_cast<const float4*>((const float*)in + r * cols + c0);
+                    const float4 a = q[0], b = q[1];
+                    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+                    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+                } else {
+                    unpack_bf16x8(*reinterpret_cast<const uint4*>((const uint16_t*)in + r * cols + c0), v);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+            }
+            float vs[8];
+            uint32_t rm = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t ab = abs_bits(v[e]);
+                rm = rm > ab ? rm : ab;
+                vs[e] = mul_round_odd(v[e], s);
+                cs[e] += v[e];
+            }
+            uint32_t lo = encode4<FMT>(vs[0], vs[1], vs[2], vs[3]);
+            uint32_t hi = encode4<FMT>(vs[4], vs[5], vs[6], vs[7]);
+            if (__builtin_expect(rm > kInfBits, 0)) {
+                lo = patch_nan4(lo, vs);
+                hi = patch_nan4(hi, vs + 4);
+            }
+            cm = cm > rm ? cm : rm;
+            if (ok) *reinterpret_cast<uint2*>(out + r * cols + c0) = make_uint2(lo, hi);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                packed[e] |= ((lo >> (8 * e)) & 0xFFu) << (8 * i);
+                packed[4 + e] |= ((hi >> (8 * e)) & 0xFFu) << (8 * i);
+            }
+        }
+        if (out_t) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                tq[(8 * j + e) * (kCPitch / 4) + 16 * half + p] = packed[e];
+        }
     }
     if (partial) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) tv[lr][lc + i] = v[i];
+        for (int e = 0; e < 8; ++e) psum[p][8 * j + e] = cs[e];
     }
     __syncthreads();
     if (out_t) {
-        // thread t writes column t/4 of the tile, rows 16*(t%4) .. +15 (rows % 16 == 0)
-        const int64_t oc = (int64_t)blockIdx.x * kTile + lr;
-        const int64_t orow0 = (int64_t)blockIdx.y * kTile + lc;
-        if (oc < cols && orow0 < rows)
-            *reinterpret_cast<uint4*>(out_t + oc * rows + orow0) =
-                *reinterpret_cast<const uint4*>(&tq[lr][lc]);
+        // eight lanes per column write one 128-byte row of the transposed tile
+        const int seg = t % 8;
+        const int64_t orow = r0 + 16 * seg;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int cc = t / 8 + 32 * k;
+            const int64_t oc = (int64_t)blockIdx.x * kCT + cc;
+            const uint32_t* src = tq + cc * (kCPitch / 4) + 4 * seg;
+            if (oc < cols && orow < rows)
+                *reinterpret_cast<uint4*>(out_t + oc * rows + orow) =
+                    make_uint4(src[0], src[1], src[2], src[3]);
+        }
     }
-    if (partial && t < kTile) {
-        const int64_t pc = (int64_t)blockIdx.x * kTile + t;
+    if (partial && t < kCT) {
+        const int64_t pc = (int64_t)blockIdx.x * kCT + t;
         if (pc < cols) {
             float acc = 0.0f;
-            for (int i = 0; i < kTile; ++i) acc += tv[i][t];   // rows past the end are 0
+#pragma unroll
+            for (int k = 0; k < kThreads / 16; ++k) acc += psum[k][t];
             partial[(int64_t)blockIdx.y * cols + pc] = acc;
         }
     }
     block_amax_atomic(cm, amax_ptr, red);
-}
-
-// out[c] = sum over p of partial[p][c], in order of p.
-__global__ __launch_bounds__(kThreads) void colsum_kernel(const float* __restrict__ partial,
-                                                          int64_t np, int64_t cols,
-                                                          float* __restrict__ out) {
-    const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (c >= cols) return;
-    float acc = 0.0f;
-    for (int64_t p = 0; p < np; ++p) acc += partial[p * cols + c];
-    out[c] = acc;
 }
 
 // in [rows][cols] -> out [cols][rows], 64 x 64 byte tiles (cols % 16 == 0,
@@ -162,7 +178,7 @@ template <bool IN_F32>
 hipError_t launch_cast_fmt(int64_t rows, int64_t cols, const void* in, int fp8,
                            const float* scale, float* amax, uint8_t* out, uint8_t* out_t,
                            float* partial, hipStream_t stream) {
-    const dim3 grid((unsigned)((cols + kTile - 1) / kTile), (unsigned)((rows + kTile - 1) / kTile));
+    const dim3 grid((unsigned)((cols + kCT - 1) / kCT), (unsigned)((rows + kCT - 1) / kCT));
     if (fp8 == kE4M3)
         hipLaunchKernelGGL((cast_tile_kernel<IN_F32, kE4M3>), grid, dim3(kThreads), 0, stream, in,
                            rows, cols, scale, amax, out, out_t, partial);
@@ -175,7 +191,7 @@ hipError_t launch_cast_fmt(int64_t rows, int64_t cols, const void* in, int fp8,
 }  // namespace
 
 size_t cast_workspace(int64_t rows, int64_t cols) {
-    return (size_t)((rows + kTile - 1) / kTile) * (size_t)cols * sizeof(float);
+    return (size_t)((rows + kCT - 1) / kCT) * (size_t)cols * sizeof(float);
 }
 
 hipError_t launch_cast_amax(int64_t rows, int64_t cols, bool in_f32, const void* in, int fp8,
@@ -191,10 +207,8 @@ hipError_t launch_cast_amax(int64_t rows, int64_t cols, bool in_f32, const void*
         if (e != hipSuccess) return e;
     }
     if (!colsum) return hipSuccess;
-    const int64_t np = (rows + kTile - 1) / kTile;
-    hipLaunchKernelGGL(colsum_kernel, dim3((unsigned)((cols + kThreads - 1) / kThreads)),
-                       dim3(kThreads), 0, stream, partial, np, cols, colsum);
-    return hipGetLastError();
+    return launch_sum_partials(partial, (rows + kCT - 1) / kCT, cols, colsum, nullptr, cols,
+                               stream);
 }
 
 hipError_t launch_transpose_u8(int64_t rows, int64_t cols, const uint8_t* in, uint8_t* out,

@@ -80,6 +80,85 @@ __device__ __forceinline__ int lds_off(int r, int c) {
 // and leaves the other counters unconstrained (gfx9 encoding).
 constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
+typedef __attribute__((address_space(3))) uint8_t lds8;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// LDS accesses through address-space-3 pointers (ds_read / ds_write).
+template <class T>
+__device__ __forceinline__ void lds_st(lds8* a, T v) {
+    *reinterpret_cast<__attribute__((address_space(3))) T*>(a) = v;
+}
+template <class T>
+__device__ __forceinline__ T lds_ld(const lds8* a) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) T*>(a);
+}
+
+// Rows of RB bytes staged in a ring of LDS stages of STAGE bytes each: row r
+// lives in stage r / RPS, and its 16-byte chunk c at chunk position c ^ (r & SWM).
+template <int RB, int STAGE>
+struct Staging {
+    static constexpr int NC = RB / 16;
+    static constexpr int RPS = STAGE / RB;
+    static constexpr int SWM = (NC < 32 ? NC : 32) - 1;
+    static_assert(RB % 16 == 0 && RPS >= 1, "staging geometry");
+
+    template <class Ring>
+    __device__ __forceinline__ static lds8* at_stage(Ring ring, int s0, int r, int c16) {
+        return ring(s0 + r / RPS) + (r % RPS) * RB + ((c16 ^ (r & SWM)) << 4);
+    }
+    template <class Ring>
+    __device__ __forceinline__ static lds8* at(Ring ring, int r, int c16) {
+        return at_stage(ring, 0, r, c16);
+    }
+    // Copies ROWS staged rows (from stage s0 on) to dst, whose rows are ld bytes
+    // apart, as 16-byte chunks; rows at or past rows_valid and chunks at or past
+    // bytes_valid are skipped.  Each wave writes whole rows.
+    template <int ROWS, int NT, class Ring>
+    __device__ __forceinline__ static void copy_out(Ring ring, int t, uint8_t* dst, int64_t ld,
+                                                    int64_t rows_valid, int64_t bytes_valid,
+                                                    int s0 = 0) {
+        constexpr int TOTAL = ROWS * NC;
+        constexpr int PER_STAGE = RPS * NC / NT;   // loop iterations per stage
+        static_assert(TOTAL % NT == 0 && (RPS * NC) % NT == 0, "copy split");
+#pragma unroll
+        for (int it = 0; it < TOTAL / NT; ++it) {
+            const int u = it * NT + t;
+            const int r = u / NC, c = u % NC;
+            const u32x4 w = lds_ld<u32x4>(ring(s0 + it / PER_STAGE) + (r % RPS) * RB +
+                                          ((c ^ (r & SWM)) << 4));
+            if (r < rows_valid && c * 16 < bytes_valid)
+                *reinterpret_cast<u32x4*>(dst + r * ld + c * 16) = w;
+        }
+    }
+};
+
+// One butterfly step over lanes l and l ^ MASK: each keeps one half of its N
+// values and adds the partner's copy of that half.
+template <int N, int MASK>
+__device__ __forceinline__ void butterfly_step(float* v, int fr) {
+    const bool upper = (fr & MASK) != 0;
+#pragma unroll
+    for (int k = 0; k < N / 2; ++k) {
+        const float send = upper ? v[k] : v[k + N / 2];
+        const float keep = upper ? v[k + N / 2] : v[k];
+        v[k] = keep + __shfl_xor(send, MASK, kWave);
+    }
+}
+
+// Sums NV values over the 32 lanes that share lane / 32.  Afterwards lane l
+// holds in v[0 .. NV/32) the sums of the values at index (l % 32) * NV/32 + k.
+template <int NV>
+__device__ __forceinline__ void butterfly_sum(float* v, int fr) {
+    static_assert(NV % 32 == 0, "butterfly width");
+    butterfly_step<NV, 16>(v, fr);
+    butterfly_step<NV / 2, 8>(v, fr);
+    butterfly_step<NV / 4, 4>(v, fr);
+    butterfly_step<NV / 8, 2>(v, fr);
+    butterfly_step<NV / 16, 1>(v, fr);
+}
+
 template <int BM, int BN, int WGM, int WGN, int FA, int FB, int EPI, int QF>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p) {
     constexpr int NW = WGM * WGN;              // waves per workgroup
@@ -224,81 +303,259 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p) {
         step(st3, st2, kt + 3);
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // the zero-filled look-ahead stages
+    __syncthreads();                            // the ring is free for the epilogue
 
-    // ---- epilogue straight from the accumulators -----------------------------
+    // ---- epilogue ----------------------------------------------------------------
     // acc[j][i] register r holds C[m][n] with m = m0 + wm WM + 32 i + (lane % 32)
-    // and n = n0 + wn WN + 32 j + 8 (r / 4) + 4 (lane / 32) + (r % 4).
+    // and n = n0 + wn WN + 32 j + 8 (r / 4) + 4 (lane / 32) + (r % 4).  Results go
+    // through the LDS ring so that global stores are whole rows: a wave writes its
+    // values into a staged copy of (part of) the output tile, then every thread
+    // copies 16-byte chunks of complete rows out.  Staged rows of RB bytes fill
+    // the ring stages in order; chunk c of staged row r sits at chunk position
+    // c ^ (r % 32) (or r % chunks-per-row when a row holds fewer than 32 chunks),
+    // so the 32 rows a wave writes at once fall on different banks.
+    constexpr int NT = 64 * NW;
+    auto ring = [&](int sidx) -> lds8* {
+        return sidx == 0 ? (lds8*)st0 : sidx == 1 ? (lds8*)st1 : sidx == 2 ? (lds8*)st2 : (lds8*)st3;
+    };
     const float alpha = (*p.sinv_a) * (*p.sinv_b);
-    float qs = 0.0f;
-    if constexpr (EPI == kEpiGeluFp8) qs = *p.q_scale;
-    uint32_t amax_bits = 0;
+    const int row_w = wm * WM + fr;      // tile row of this lane's i = 0 values
+    const int col_w = wn * WN + 4 * fh;  // tile column of this lane's j = q = 0 values
+
+    if constexpr (EPI == kEpiDGeluFp8) {
+        // Bring the tile of h into the ring in the bf16 staging layout (direct
+        // loads, rows past M read as zero), then scale by gelu'(h) in place.
+        using G = Staging<BN * 2, STAGE>;
+        constexpr int IPW = BM * G::NC / 64 / NW;    // 64-chunk loads per wave
+        const int64_t rows_h = min<int64_t>(BM, M - m0);
+        const __amdgpu_buffer_rsrc_t rsrc_h = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(p.h_in + m0 * N), (short)0, (int)(rows_h * N * 2), kBufferWord3);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int64_t gm = m0 + wm * WM + 32 * i + fr;
+        for (int jj = 0; jj < IPW; ++jj) {
+            const int u0 = (wave * IPW + jj) * 64;
+            const int u = u0 + lane;
+            const int lr = u / G::NC;
+            const int c16 = (u % G::NC) ^ (lr & G::SWM);
+            const uint32_t voff = (uint32_t)(lr * N * 2 + n0 * 2 + c16 * 16);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc_h, (lds_ptr)(ring(u0 / (G::RPS * G::NC)) + (u0 % (G::RPS * G::NC)) * 16), 16,
+                voff, 0, 0, 0);
+        }
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __syncthreads();
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int lr = row_w + 32 * i;
+                    const int lc = col_w + 32 * j + 8 * q;
+                    const u32x2 hw = lds_ld<u32x2>(G::at(ring, lr, lc / 8) + 8 * fh);
+                    const bool ok = m0 + lr < M && n0 + lc < N;
+                    const float hv[4] = {bf16_lo(hw.x), bf16_hi(hw.x), bf16_lo(hw.y), bf16_hi(hw.y)};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        acc[j][i][4 * q + e] =
+                            ok ? acc[j][i][4 * q + e] * alpha * gelu_grad_f(hv[e]) : 0.0f;
+                }
+        __syncthreads();   // h is consumed: the ring takes the codes next
+    } else {
+        // alpha (and the bias) in place; values outside the product become 0
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int64_t gn = n0 + wn * WN + 32 * j + 8 * q + 4 * fh;
-                const bool ok = gm < M && gn < N;
-                float v[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = acc[j][i][4 * q + e] * alpha;
+                const int64_t gn = n0 + col_w + 32 * j + 8 * q;
+                float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
                 if constexpr (EPI == kEpiBf16Bias || EPI == kEpiGeluFp8) {
-                    if (p.bias && ok) {
+                    if (p.bias && gn < N) {
                         const uint2 bw = *reinterpret_cast<const uint2*>(p.bias + gn);
-                        v[0] += bf16_lo(bw.x); v[1] += bf16_hi(bw.x);
-                        v[2] += bf16_lo(bw.y); v[3] += bf16_hi(bw.y);
+                        bv[0] = bf16_lo(bw.x); bv[1] = bf16_hi(bw.x);
+                        bv[2] = bf16_lo(bw.y); bv[3] = bf16_hi(bw.y);
                     }
                 }
-                if constexpr (EPI == kEpiBf16Bias) {
-                    if (ok)
-                        *reinterpret_cast<uint2*>((uint16_t*)p.out + gm * N + gn) =
-                            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-                } else if constexpr (EPI == kEpiF32) {
-                    if (ok)
-                        *reinterpret_cast<float4*>((float*)p.out + gm * N + gn) =
-                            make_float4(v[0], v[1], v[2], v[3]);
-                } else if constexpr (EPI == kEpiDGeluF32) {
-                    if (ok) {
-                        const uint2 hw = *reinterpret_cast<const uint2*>(p.h_in + gm * N + gn);
-                        v[0] *= gelu_grad_f(bf16_lo(hw.x));
-                        v[1] *= gelu_grad_f(bf16_hi(hw.x));
-                        v[2] *= gelu_grad_f(bf16_lo(hw.y));
-                        v[3] *= gelu_grad_f(bf16_hi(hw.y));
-                        *reinterpret_cast<float4*>((float*)p.out + gm * N + gn) =
-                            make_float4(v[0], v[1], v[2], v[3]);
-                    }
-                } else {   // kEpiGeluFp8
-                    if (ok) {
-                        if (p.h_out)
-                            *reinterpret_cast<uint2*>(p.h_out + gm * N + gn) =
-                                make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-                        float gs[4];
-                        uint32_t cm = 0;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float g = gelu_f(v[e], nullptr);
-                            const uint32_t ab = abs_bits(g);
-                            cm = cm > ab ? cm : ab;
-                            gs[e] = g * qs;
-                        }
-                        uint32_t code = encode4<QF>(gs[0], gs[1], gs[2], gs[3]);
-                        if (__builtin_expect(cm > kInfBits, 0)) code = patch_nan4(code, gs);
-                        *reinterpret_cast<uint32_t*>(p.q_out + gm * N + gn) = code;
-                        if (p.q_out_t) {
-                            // lanes with consecutive m write consecutive bytes of a row
+                for (int i = 0; i < TM; ++i) {
+                    const bool ok = m0 + row_w + 32 * i < M && gn < N;
 #pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                p.q_out_t[(gn + e) * M + gm] = (uint8_t)(code >> (8 * e));
-                        }
-                        amax_bits = amax_bits > cm ? amax_bits : cm;
+                    for (int e = 0; e < 4; ++e) {
+                        const float x = acc[j][i][4 * q + e];
+                        if constexpr (EPI == kEpiBf16Bias || EPI == kEpiGeluFp8)
+                            acc[j][i][4 * q + e] = ok ? fmaf(x, alpha, bv[e]) : 0.0f;
+                        else
+                            acc[j][i][4 * q + e] = ok ? x * alpha : 0.0f;
                     }
                 }
             }
+    }
+
+    if constexpr (EPI == kEpiDGeluF32) {
+        // gelu'(h) from global memory, one 8-byte read per four values
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t gm = m0 + row_w + 32 * i;
+                    const int64_t gn = n0 + col_w + 32 * j + 8 * q;
+                    if (gm < M && gn < N) {
+                        const uint2 hw = *reinterpret_cast<const uint2*>(p.h_in + gm * N + gn);
+                        acc[j][i][4 * q + 0] *= gelu_grad_f(bf16_lo(hw.x));
+                        acc[j][i][4 * q + 1] *= gelu_grad_f(bf16_hi(hw.x));
+                        acc[j][i][4 * q + 2] *= gelu_grad_f(bf16_lo(hw.y));
+                        acc[j][i][4 * q + 3] *= gelu_grad_f(bf16_hi(hw.y));
+                    }
+                }
+    }
+
+    if constexpr (EPI == kEpiF32 || EPI == kEpiDGeluF32) {
+        // fp32 rows; a 256 x 256 tile goes out in two passes of 128 rows
+        using G = Staging<BN * 4, STAGE>;
+        constexpr int PASSES = (BM * BN * 4 + 4 * STAGE - 1) / (4 * STAGE);
+        constexpr int RPP = BM / PASSES;
+        static_assert(RPP % WM == 0 && RPP <= 4 * G::RPS, "f32 staging");
+#pragma unroll
+        for (int ps = 0; ps < PASSES; ++ps) {
+            if (wm * WM >= ps * RPP && wm * WM < (ps + 1) * RPP) {
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int lr = row_w + 32 * i - ps * RPP;
+                            const int lc = col_w + 32 * j + 8 * q;
+                            lds_st(G::at(ring, lr, lc / 4),
+                                   f32x4{acc[j][i][4 * q], acc[j][i][4 * q + 1],
+                                         acc[j][i][4 * q + 2], acc[j][i][4 * q + 3]});
+                        }
+            }
+            __syncthreads();
+            G::template copy_out<RPP, NT>(ring, t, (uint8_t*)p.out + ((m0 + ps * RPP) * N + n0) * 4,
+                                         N * 4, M - m0 - ps * RPP, (N - n0) * 4);
+            __syncthreads();
         }
     }
-    if constexpr (EPI == kEpiGeluFp8) {
+
+    if constexpr (EPI == kEpiBf16Bias || EPI == kEpiGeluFp8) {
+        uint16_t* hdst = EPI == kEpiBf16Bias ? (uint16_t*)p.out : p.h_out;
+        if (hdst) {
+            using G = Staging<BN * 2, STAGE>;
+            static_assert(BM <= 4 * G::RPS, "bf16 staging");
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int lr = row_w + 32 * i;
+                        const int lc = col_w + 32 * j + 8 * q;
+                        lds_st(G::at(ring, lr, lc / 8) + 8 * fh,
+                               u32x2{pack_bf16x2(acc[j][i][4 * q], acc[j][i][4 * q + 1]),
+                                     pack_bf16x2(acc[j][i][4 * q + 2], acc[j][i][4 * q + 3])});
+                    }
+            __syncthreads();
+            G::template copy_out<BM, NT>(ring, t, (uint8_t*)(hdst + m0 * N + n0), N * 2, M - m0,
+                                        (N - n0) * 2);
+            __syncthreads();
+        }
+    }
+
+    if constexpr (EPI == kEpiGeluFp8 || EPI == kEpiDGeluFp8) {
+        // FP8 codes: the row-major tile in the first stages of the ring, the
+        // transposed tile (rows = output columns) in the stages after it.  For
+        // the transposed copy the four lanes of a quad swap bytes so that each
+        // holds one column of four consecutive rows, written as one word.
+        using Q = Staging<BN, STAGE>;
+        using QT = Staging<BM, STAGE>;
+        constexpr int QS = BM * BN / STAGE;    // stages taken by the row-major codes
+        static_assert(QS >= 1 && BM <= QS * Q::RPS && BN <= (4 - QS) * QT::RPS, "code staging");
+        const float qs = *p.q_scale;
+        uint32_t amax_bits = 0;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int lr = row_w + 32 * i;
+                    const int lc = col_w + 32 * j + 8 * q;
+                    float gs[4];
+                    uint32_t cm = 0;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float g;
+                        if constexpr (EPI == kEpiGeluFp8) {
+                            g = gelu_f(acc[j][i][4 * q + e], nullptr);
+                            gs[e] = g * qs;
+                        } else {
+                            g = acc[j][i][4 * q + e];
+                            gs[e] = mul_round_odd(g, qs);
+                        }
+                        const uint32_t ab = abs_bits(g);
+                        cm = cm > ab ? cm : ab;
+                    }
+                    uint32_t code = encode4<QF>(gs[0], gs[1], gs[2], gs[3]);
+                    if (__builtin_expect(cm > kInfBits, 0)) code = patch_nan4(code, gs);
+                    if constexpr (EPI == kEpiGeluFp8) {
+                        // rows and columns outside the product carry gelu(0) = 0
+                        if (!(m0 + lr < M && n0 + lc < N)) cm = 0;
+                    }
+                    amax_bits = amax_bits > cm ? amax_bits : cm;
+                    lds_st(Q::at(ring, lr, lc / 16) + 4 * ((lc / 4) % 4), code);
+                    if (p.q_out_t) {
+                        const int odd = fr & 1, hi2 = fr & 2;
+                        const uint32_t o2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)code,
+                                                                              kDppQuadSwap2, 0xF, 0xF, false);
+                        const uint32_t c2 = hi2 ? __builtin_amdgcn_perm(o2, code, 0x03020706u)
+                                                : __builtin_amdgcn_perm(o2, code, 0x05040100u);
+                        const uint32_t o1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)c2,
+                                                                              kDppQuadSwap1, 0xF, 0xF, false);
+                        const uint32_t ct = odd ? __builtin_amdgcn_perm(o1, c2, 0x03070105u)
+                                                : __builtin_amdgcn_perm(o1, c2, 0x06020400u);
+                        const int tn = lc + (fr & 3);          // staged row = output column
+                        const int tm = (lr & ~3);              // first of the four rows
+                        lds_st(QT::at_stage(ring, QS, tn, tm / 16) + 4 * ((tm / 4) % 4), ct);
+                    }
+                }
+        __syncthreads();
+        Q::template copy_out<BM, NT>(ring, t, p.q_out + m0 * N + n0, N, M - m0, N - n0);
+        if (p.q_out_t)
+            QT::template copy_out<BN, NT>(ring, t, p.q_out_t + n0 * M + m0, M, N - n0, M - m0, QS);
+        if constexpr (EPI == kEpiDGeluFp8) {
+            if (p.col_partial) {
+                // column sums of the tile in a fixed order: over i in a lane, a
+                // butterfly over the 32 lanes of equal lane / 32, then over wm
+                constexpr int NV = 16 * TN;   // columns per lane
+                float v[NV];
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        float a = 0.0f;
+#pragma unroll
+                        for (int i = 0; i < TM; ++i) a += acc[j][i][r];
+                        v[16 * j + r] = a;
+                    }
+                butterfly_sum<NV>(v, fr);
+                __shared__ float colp[WGM][BN];
+#pragma unroll
+                for (int k = 0; k < NV / 32; ++k) {
+                    const int c = fr * (NV / 32) + k;   // = 16 j + 4 q + e
+                    const int j = c / 16, q = (c / 4) % 4, e = c % 4;
+                    colp[wm][col_w + 32 * j + 8 * q + e] = v[k];
+                }
+                __syncthreads();
+                if (t < BN && n0 + t < N) {
+                    float a = 0.0f;
+#pragma unroll
+                    for (int w = 0; w < WGM; ++w) a += colp[w][t];
+                    p.col_partial[(int64_t)tile_m * N + n0 + t] = a;
+                }
+            }
+        }
         __shared__ uint32_t red[NW];
         block_amax_atomic(amax_bits, p.q_amax, red);
     }
@@ -333,10 +590,11 @@ hipError_t launch_tile(const GemmParams& p, hipStream_t stream) {
 }
 
 // 256 x 256 tiles when they give at least one tile per CU, else 128 x 128.
+bool use_big_tiles(int64_t M, int64_t N) { return ((M + 255) / 256) * ((N + 255) / 256) >= 256; }
+
 template <int FA, int FB, int EPI, int QF>
 hipError_t launch_typed(const GemmParams& p, hipStream_t stream) {
-    const int64_t big = ((p.M + 255) / 256) * ((p.N + 255) / 256);
-    if (big >= 256) return launch_tile<256, 256, FA, FB, EPI, QF>(p, stream);
+    if (use_big_tiles(p.M, p.N)) return launch_tile<256, 256, FA, FB, EPI, QF>(p, stream);
     return launch_tile<128, 128, FA, FB, EPI, QF>(p, stream);
 }
 
@@ -349,11 +607,18 @@ hipError_t launch_epi(const GemmParams& p, hipStream_t stream) {
         case kEpiGeluFp8:
             return p.q_fp8 == kE4M3 ? launch_typed<FA, FB, kEpiGeluFp8, kE4M3>(p, stream)
                                     : launch_typed<FA, FB, kEpiGeluFp8, kE5M2>(p, stream);
+        case kEpiDGeluFp8:
+            return p.q_fp8 == kE4M3 ? launch_typed<FA, FB, kEpiDGeluFp8, kE4M3>(p, stream)
+                                    : launch_typed<FA, FB, kEpiDGeluFp8, kE5M2>(p, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
+
+int64_t gemm_partial_rows(int64_t M, int64_t N) {
+    return use_big_tiles(M, N) ? (M + 255) / 256 : (M + 127) / 128;
+}
 
 hipError_t launch_gemm(const GemmParams& p, hipStream_t stream) {
     if (p.M == 0 || p.N == 0) return hipSuccess;

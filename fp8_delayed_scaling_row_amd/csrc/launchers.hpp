@@ -33,6 +33,10 @@ size_t cast_workspace(int64_t rows, int64_t cols);
 hipError_t launch_cast_amax(int64_t rows, int64_t cols, bool in_f32, const void* in, int fp8,
                             const float* scale, float* amax, uint8_t* out, uint8_t* out_t,
                             float* colsum, void* workspace, hipStream_t stream);
+// out[j] = sum over r < nrows of partial[r][j] in a fixed order; columns j < split
+// go to out0[j], the others to out1[j - split].
+hipError_t launch_sum_partials(const float* partial, int64_t nrows, int64_t width, float* out0,
+                               float* out1, int64_t split, hipStream_t stream);
 hipError_t launch_transpose_u8(int64_t rows, int64_t cols, const uint8_t* in, uint8_t* out,
                                hipStream_t stream);
 hipError_t launch_encode_range(uint32_t start, int64_t count, int fp8, uint8_t* out,
@@ -44,6 +48,7 @@ enum GemmEpilogue : int {
     kEpiF32 = 1,        // out fp32 = acc * alpha
     kEpiGeluFp8 = 2,    // h = acc * alpha + bias -> h bf16; g = gelu(h) -> FP8 (+T), amax
     kEpiDGeluF32 = 3,   // out fp32 = acc * alpha * gelu'(h)
+    kEpiDGeluFp8 = 4,   // d = acc * alpha * gelu'(h) -> FP8 (+T), amax, column partial sums
 };
 
 struct GemmParams {
@@ -62,10 +67,16 @@ struct GemmParams {
     const float* q_scale;   // scale of the FP8 output
     float* q_amax;          // amax of gelu(h)
     int q_fp8;
-    // kEpiDGeluF32
+    // kEpiDGeluF32, kEpiDGeluFp8 (which also uses q_out, q_out_t, q_scale, q_amax, q_fp8)
     const uint16_t* h_in;   // bf16 [M][N]
+    float* col_partial;     // kEpiDGeluFp8: [ceil(M / tile rows)][N] column sums, or null
     int epilogue;
 };
+
+// Rows of the col_partial array launch_gemm writes for an M-row product (its
+// tile height), and an upper bound for workspace sizing.
+int64_t gemm_partial_rows(int64_t M, int64_t N);
+inline int64_t gemm_partial_rows_bound(int64_t M) { return (M + 127) / 128; }
 
 hipError_t launch_gemm(const GemmParams& p, hipStream_t stream);
 

@@ -258,20 +258,6 @@ __global__ __launch_bounds__(kThreads) void ln_bwd_kernel(
     for (int j = threadIdx.x; j < 2 * hidden; j += kThreads) pb[j] = sm[j];
 }
 
-// out[j] = sum over blocks b of partial[b][j] (fixed order); j < 2 * hidden.
-__global__ __launch_bounds__(kThreads) void sum_partials_kernel(const float* __restrict__ partial,
-                                                                int nblocks, int width,
-                                                                float* __restrict__ out0,
-                                                                float* __restrict__ out1,
-                                                                int split) {
-    const int j = blockIdx.x * kThreads + threadIdx.x;
-    if (j >= width) return;
-    float acc = 0.0f;
-    for (int b = 0; b < nblocks; ++b) acc += partial[(int64_t)b * width + j];
-    if (j < split) out0[j] = acc;
-    else out1[j - split] = acc;
-}
-
 int ln_bwd_blocks(int64_t rows) {
     const int64_t want = (rows + kWavesPerBlock - 1) / kWavesPerBlock;
     const int64_t cap = 512;
@@ -290,10 +276,8 @@ hipError_t launch_ln_bwd_cpl(int64_t rows, int hidden, const float* dy, const vo
                        (uint4*)dx, partial, rows, hidden);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int width = 2 * hidden;
-    hipLaunchKernelGGL(sum_partials_kernel, dim3((width + kThreads - 1) / kThreads),
-                       dim3(kThreads), 0, stream, partial, blocks, width, dgamma, dbeta, hidden);
-    return hipGetLastError();
+    return launch_sum_partials(partial, blocks, 2 * (int64_t)hidden, dgamma, dbeta, hidden,
+                               stream);
 }
 
 }  // namespace

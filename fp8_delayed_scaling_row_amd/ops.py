@@ -14,14 +14,14 @@ import torch
 from . import _abi
 from ._abi import (DTYPE_BF16, DTYPE_F32, E4M3, E5M2, FORMAT_E4M3, FORMAT_E5M2, FORMAT_HYBRID,
                    META_BACKWARD, META_FORWARD, OP_CAST_AMAX, OP_LAYERNORM_BWD, OP_LN_LINEAR_BWD,
-                   OP_LN_MLP_BWD, Fp8lnError, check, lib)
+                   OP_LN_MLP_BWD, OP_GEMM_DGELU_FP8, Fp8lnError, check, lib)
 
 __all__ = [
     "Recipe", "Meta", "LinearCtx", "MlpCtx", "Fp8lnError", "FORMAT_E4M3", "FORMAT_HYBRID",
     "FORMAT_E5M2", "E4M3", "E5M2", "META_FORWARD", "META_BACKWARD", "OP_CAST_AMAX",
-    "OP_LAYERNORM_BWD", "OP_LN_LINEAR_BWD", "OP_LN_MLP_BWD", "check_support", "workspace_size", "meta_init",
+    "OP_LAYERNORM_BWD", "OP_LN_LINEAR_BWD", "OP_LN_MLP_BWD", "OP_GEMM_DGELU_FP8", "check_support", "workspace_size", "meta_init",
     "scaling_update", "ln_cast_amax", "cast_amax", "encode_range", "gemm", "gemm_gelu_fp8",
-    "gemm_dgelu", "layernorm_bwd",
+    "gemm_dgelu", "gemm_dgelu_fp8", "layernorm_bwd",
     "ln_linear_fwd", "ln_linear_bwd", "ln_mlp_fwd", "ln_mlp_bwd", "fwd_fp8", "bwd_fp8",
 ]
 
@@ -265,6 +265,26 @@ def gemm_dgelu(a, a_dtype: int, b, b_dtype: int, sinv_a, sinv_b, h, out, stream=
     _need(out, torch.float32, (M, N), "out")
     check(lib().fp8ln_gemm_dgelu(M, N, K, _ptr(a), a_dtype, _ptr(b), b_dtype, _ptr(sinv_a),
                                  _ptr(sinv_b), _ptr(h), _ptr(out), _stream(stream)))
+
+
+def gemm_dgelu_fp8(a, a_dtype: int, b, b_dtype: int, sinv_a, sinv_b, h, q_dtype: int, q_scale,
+                   q_amax_ptr: int, q_out, q_out_t=None, dbias=None, stream=None):
+    """d = a.b^T * sinv_a * sinv_b * gelu'(h) (fp32, not stored); q_out = encode(d *
+    q_scale), q_out_t its transpose, amax of d at q_amax_ptr, dbias = column sums of d."""
+    M, K = a.shape
+    N = b.shape[0]
+    _need(a, torch.uint8, (M, K), "a")
+    _need(b, torch.uint8, (N, K), "b")
+    _need(h, torch.bfloat16, (M, N), "h")
+    _need(q_out, torch.uint8, (M, N), "q_out")
+    _opt(q_out_t, torch.uint8, (N, M), "q_out_t")
+    _opt(dbias, torch.float32, (N,), "dbias")
+    nbytes = workspace_size(OP_GEMM_DGELU_FP8, M, N) if dbias is not None else 0
+    ws = _workspace(nbytes, a.device) if dbias is not None else None
+    check(lib().fp8ln_gemm_dgelu_fp8(M, N, K, _ptr(a), a_dtype, _ptr(b), b_dtype, _ptr(sinv_a),
+                                     _ptr(sinv_b), _ptr(h), q_dtype, _ptr(q_scale),
+                                     C.c_void_p(q_amax_ptr), _ptr(q_out), _ptr(q_out_t),
+                                     _ptr(dbias), _ptr(ws), nbytes, _stream(stream)))
 
 
 def layernorm_bwd(dy, x, mean, rstd, gamma, dx, dgamma, dbeta, stream=None) -> None:

@@ -149,7 +149,8 @@ typedef enum {
     FP8LN_OP_CAST_AMAX = 0,        /* a = rows, b = cols (column sums requested) */
     FP8LN_OP_LAYERNORM_BWD = 1,    /* a = rows, b = hidden */
     FP8LN_OP_LN_LINEAR_BWD = 2,    /* a = tokens, b = in_features, c = out_features */
-    FP8LN_OP_LN_MLP_BWD = 3        /* a = tokens, b = hidden, c = ffn */
+    FP8LN_OP_LN_MLP_BWD = 3,       /* a = tokens, b = hidden, c = ffn */
+    FP8LN_OP_GEMM_DGELU_FP8 = 4    /* a = M, b = N (column sums requested) */
 } fp8ln_op;
 
 /* ---- library ------------------------------------------------------------ */
@@ -249,6 +250,23 @@ int fp8ln_gemm_gelu_fp8(int64_t M, int64_t N, int64_t K, const uint8_t* A, int32
 int fp8ln_gemm_dgelu(int64_t M, int64_t N, int64_t K, const uint8_t* A, int32_t a_dtype,
                      const uint8_t* B, int32_t b_dtype, const float* sinv_a, const float* sinv_b,
                      const void* h, float* out, void* stream);
+
+/* The same product with the gradient cast of the fc1 output fused in, which is
+ * how the LayerNormMLP backward runs it (HYBRID: gradients in E5M2):
+ *   d = (sum_k A[m][k] B[n][k]) * (*sinv_a) * (*sinv_b) * gelu_tanh'(h[m][n])  (fp32)
+ *   q_out[m][n] = encode(d * (*q_scale)) in q_dtype, from the exact product
+ *   q_out_t[n][m] = q_out[m][n]                    (optional, needs M % 16 == 0)
+ *   *q_amax = max(*q_amax, max |d|)
+ *   dbias[n] = sum_m d[m][n]                       (optional; fixed summation order)
+ * The d values and codes equal those of fp8ln_gemm_dgelu followed by
+ * fp8ln_cast_amax on its output.  dbias needs a workspace of
+ * fp8ln_workspace_size(FP8LN_OP_GEMM_DGELU_FP8, M, N) bytes.  K and N must be
+ * multiples of 16. */
+int fp8ln_gemm_dgelu_fp8(int64_t M, int64_t N, int64_t K, const uint8_t* A, int32_t a_dtype,
+                         const uint8_t* B, int32_t b_dtype, const float* sinv_a,
+                         const float* sinv_b, const void* h, int32_t q_dtype,
+                         const float* q_scale, float* q_amax, uint8_t* q_out, uint8_t* q_out_t,
+                         float* dbias, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---- LayerNorm backward ---------------------------------------------------- */
 

@@ -53,7 +53,10 @@ def test_workspace_sizes_are_host_only_and_monotone(lib):
     f = lib.fp8ln_workspace_size
     assert f(_abi.OP_LN_LINEAR_BWD, 2048, 768, 2304) > 2048 * 768 * 4
     assert f(_abi.OP_LN_MLP_BWD, 2048, 768, 3072) > f(_abi.OP_LN_LINEAR_BWD, 2048, 768, 2304)
-    assert f(_abi.OP_CAST_AMAX, 2048, 2304, 0) == 32 * 2304 * 4
+    # one fp32 row of column sums per 128-row tile
+    assert f(_abi.OP_CAST_AMAX, 2048, 2304, 0) == 16 * 2304 * 4
+    assert f(_abi.OP_CAST_AMAX, 2049, 2304, 0) == 17 * 2304 * 4
+    assert f(_abi.OP_GEMM_DGELU_FP8, 2048, 3072, 0) == 16 * 3072 * 4
     assert f(99, 1, 1, 1) == 0 and f(_abi.OP_LN_LINEAR_BWD, 16, 16, 0) == 0
 
 

@@ -206,3 +206,80 @@ def test_gelu_gemm_random_within_tolerance(M, N, K):
                        1e-6 * np.abs(g))
     stats = compare_codes(q_out.cpu().numpy(), g * float(qs), oracle.E4M3, win)
     print(f"gelu gemm {M}x{N}x{K}: {stats}")
+
+
+# ---- the large-tile kernel (at least 256 output tiles of 256 x 256) -------------
+
+BIG = [(4096, 4096, 64), (4000, 4112, 48)]   # the second is ragged in M and N
+
+
+@pytest.mark.parametrize("fa,fb", PAIRS, ids=["e4m3xe4m3", "e5m2xe4m3", "e4m3xe5m2", "e5m2xe5m2"])
+@pytest.mark.parametrize("M,N,K", BIG)
+def test_small_integer_gemm_large_tiles_is_bit_exact(fa, fb, M, N, K):
+    """Exact integer products through the 256 x 256 kernel: fp32 output bit for
+    bit, and bf16 output (with a bias on a 1/64 grid) equal to the round-to-
+    nearest-even of the exact value."""
+    a, av = int_codes((M, K), fa, M + K)
+    b, bv = int_codes((N, K), fb, N + 2 * K)
+    exact = av @ bv.T
+    out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    ops.gemm(dev(a), fa, dev(b), fb, _scalar(1.0), _scalar(1.0), out)
+    bias_bits = oracle.f64_to_bf16_bits(np.random.default_rng(N).integers(-64, 65, N) / 64.0)
+    bias = torch.from_numpy(bias_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    ob = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ops.gemm(dev(a), fa, dev(b), fb, _scalar(0.5), _scalar(0.25), ob, bias)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy(), exact)
+    ref = oracle.f64_to_bf16_bits(exact * 0.125 + oracle.bf16_to_f64(bias_bits)[None, :])
+    np.testing.assert_array_equal(ob.view(torch.int16).cpu().numpy().view(np.uint16), ref)
+
+
+@pytest.mark.parametrize("M,N,K", BIG)
+def test_gelu_epilogue_large_tiles_on_exact_products(M, N, K):
+    test_gelu_epilogue_on_exact_products(M, N, K, ops.E4M3)
+
+
+# ---- fc2 dgrad with the fc1 gradient cast fused ---------------------------------
+
+@pytest.mark.parametrize("M,N,K,q", [(130, 272, 48, ops.E5M2), (256, 3072, 64, ops.E5M2),
+                                     (4096, 4096, 64, ops.E5M2), (4000, 4112, 48, ops.E4M3)])
+def test_dgelu_fp8_epilogue_equals_dgelu_then_cast(M, N, K, q):
+    """The fused epilogue computes the same fp32 d = acc * alpha * gelu'(h) as the
+    fp32 epilogue and casts it like the cast kernel: codes, transpose and amax
+    agree bit for bit; the bias gradient (summed in another order) to fp32
+    rounding, and it is the same on every run."""
+    a = dev(finite_codes((M, K), ops.E5M2, 21 + M))
+    b = dev(finite_codes((N, K), ops.E4M3, 22 + N))
+    h_bits = oracle.f64_to_bf16_bits(np.random.default_rng(M + N).normal(size=(M, N)) * 2.0)
+    h = torch.from_numpy(h_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    sa, sb = _scalar(1.0 / 3000.0), _scalar(1.0 / 700.0)
+    scale = _scalar(float(np.float32(57344.0 / 9.0)) if q == ops.E5M2 else 448.0 / 9.0)
+    has_t = M % 16 == 0
+
+    d = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    ops.gemm_dgelu(a, ops.E5M2, b, ops.E4M3, sa, sb, h, d)
+    q1 = torch.empty((M, N), dtype=torch.uint8, device="cuda")
+    q1t = torch.empty((N, M), dtype=torch.uint8, device="cuda") if has_t else None
+    amax1 = torch.zeros(1, dtype=torch.float32, device="cuda")
+    db1 = torch.empty(N, dtype=torch.float32, device="cuda")
+    ops.cast_amax(d, q, scale, amax1.data_ptr(), q1, q1t, db1)
+
+    runs = []
+    for _ in range(2):
+        q2 = torch.empty((M, N), dtype=torch.uint8, device="cuda")
+        q2t = torch.empty((N, M), dtype=torch.uint8, device="cuda") if has_t else None
+        amax2 = torch.zeros(1, dtype=torch.float32, device="cuda")
+        db2 = torch.empty(N, dtype=torch.float32, device="cuda")
+        ops.gemm_dgelu_fp8(a, ops.E5M2, b, ops.E4M3, sa, sb, h, q, scale, amax2.data_ptr(), q2,
+                           q2t, db2)
+        runs.append((q2, q2t, amax2, db2))
+    torch.cuda.synchronize()
+    q2, q2t, amax2, db2 = runs[0]
+    assert torch.equal(q1, q2)
+    if has_t:
+        assert torch.equal(q1t, q2t)
+        assert torch.equal(q2t, q2.t().contiguous())
+    assert amax1.item() == amax2.item() and amax2.item() > 0
+    dsum = d.abs().sum(dim=0)
+    assert torch.all((db1 - db2).abs() <= 2e-6 * dsum + 1e-30)
+    assert torch.equal(runs[1][3], db2) and torch.equal(runs[1][0], q2)
