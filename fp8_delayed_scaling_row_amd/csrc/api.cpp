@@ -470,7 +470,7 @@ int fp8ln_gemm_dgelu_fp8(int64_t M, int64_t N, int64_t K, const uint8_t* A, int3
     p.col_partial = dbias ? (float*)workspace : nullptr;
     FP8LN_TRY(launch_gemm(p, st), "gemm_dgelu_fp8 launch");
     if (dbias)
-        FP8LN_TRY(launch_sum_partials((const float*)workspace, M > 0 ? gemm_partial_rows(M, N) : 0,
+        FP8LN_TRY(launch_sum_partials((const float*)workspace, M > 0 ? gemm_partial_rows(M, N, K) : 0,
                                       N, dbias, nullptr, N, st),
                   "column sum launch");
     return FP8LN_OK;
@@ -741,7 +741,7 @@ int fp8ln_ln_mlp_bwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t hidden,
     dg2.col_partial = db1 ? w.dh_part : nullptr;
     FP8LN_TRY(launch_gemm(dg2, st), "fc2 dgrad launch");
     if (db1)
-        FP8LN_TRY(launch_sum_partials(w.dh_part, M > 0 ? gemm_partial_rows(M, F) : 0, F, db1,
+        FP8LN_TRY(launch_sum_partials(w.dh_part, M > 0 ? gemm_partial_rows(M, F, H) : 0, F, db1,
                                       nullptr, F, st),
                   "db1 launch");
     // fc2 wgrad: dW2[H][F] = dy_qt[H][M] . (g_qt[F][M])^T

@@ -11,22 +11,25 @@
 // wgrad products are all of this form once the cast kernels have written the
 // transposed operand copies.
 //
-// Tiling (gfx950): for large problems a 512-thread workgroup owns a 256 x 256
-// output tile and its eight waves (4 along M x 2 along N, two per SIMD) each own
-// a 64 x 128 sub-tile; when that would leave CUs idle, a 256-thread workgroup
-// owns a 128 x 128 tile split 2 x 2 over four waves, two workgroups per CU.
-// Sub-tiles are built from V_MFMA_F32_32X32X64_F8F6F4 results accumulated in
-// fp32 registers.  The operand formats (E4M3 / E5M2) are chosen per operand by the instruction's
-// cbsz / blgp fields.  K advances 64 bytes per stage through a four-stage LDS
-// ring filled by direct-to-LDS buffer loads issued three stages ahead, so
-// memory latency hides behind three stages of MFMA work without holding any
-// registers; an XOR layout of 16-byte chunks keeps fragment reads free of bank
-// conflicts.
+// Tiling (gfx950): every wave owns a 64 x 128 sub-tile (64 x 64 for the smallest
+// tile) built from V_MFMA_F32_32X32X64_F8F6F4 results accumulated in fp32
+// registers, two waves per SIMD.  Three workgroup shapes: 256 x 256 over eight
+// waves (one workgroup per CU, least LDS and L2 traffic per MFMA, for long K);
+// 128 x 256 over four waves with a three-stage ring, two workgroups per CU so
+// that one's epilogue overlaps the other's main loop (K up to 2048); and 128 x
+// 128 over four waves for problems too small to fill the CUs otherwise.  The
+// operand formats (E4M3 / E5M2) are chosen per operand by the instruction's
+// cbsz / blgp fields.  K advances 64 bytes per stage through an LDS ring filled
+// by direct-to-LDS buffer loads issued NS - 1 stages ahead, so memory latency
+// hides behind MFMA work without holding any registers; an XOR layout of
+// 16-byte chunks keeps fragment reads free of bank conflicts.
+//
 // The MFMA computes the transposed product (B rows in, A rows out), so each
-// lane ends up holding four consecutive output columns of one row and the
-// epilogue stores straight from registers as 8- or 16-byte vectors.  Tiles are
-// ordered so that the blocks of one XCD (blocks are dealt to the 8 XCDs round
-// robin) cover a compact band of the output and share operands in their L2.
+// lane ends up holding four consecutive output columns of one row; the
+// epilogue stages results through the (then idle) LDS ring and writes whole
+// output rows.  Tiles are ordered so that the blocks of one XCD (blocks are
+// dealt to the 8 XCDs round robin) cover a compact band of the output and
+// share operands in their L2.
 #include "device_common.hpp"
 #include "launchers.hpp"
 
@@ -45,23 +48,36 @@ constexpr uint32_t kOutOfRange = 0x80000000u; // offset past any tile: loads rea
 // 16-byte chunk c of LDS row r lives at chunk position swz(r, c).
 __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r ^ (r >> 3)) & 7); }
 
-// GELU, tanh form, with tanh(u) = 1 - 2 / (1 + e^(2u)).
-__device__ __forceinline__ float gelu_f(float h, float* tanh_out) {
-    const float k0 = 0.7978845608028654f;   // sqrt(2 / pi)
-    const float k1 = 0.044715f;
-    const float u = k0 * fmaf(k1 * h, h * h, h);
-    const float e = __expf(2.0f * u);
-    const float t = 1.0f - 2.0f / (1.0f + e);
-    if (tanh_out) *tanh_out = t;
-    return 0.5f * h * (1.0f + t);
+// GELU, tanh form: gelu(h) = h/2 (1 + t), t = tanh(k0 (h + k1 h^3)), with
+// k0 = sqrt(2 / pi), k1 = 0.044715, and its derivative
+//     gelu'(h) = (1 + t)/2 + h/2 (1 - t^2) k0 (1 + 3 k1 h^2).
+// t = 1 - 2 / (1 + 2^v) with v = 2 log2(e) k0 h (1 + k1 h^2); 2^v and the
+// reciprocal are the hardware's (about one ulp each), which keeps the whole
+// function near 1e-7 relative to |h| and costs about a dozen operations.
+constexpr float kGeluK0 = 0.7978845608028654f;                 // sqrt(2 / pi)
+constexpr float kGeluK1 = 0.044715f;
+constexpr float kGeluV0 = 2.0f * 1.4426950408889634f * 0.7978845608028654f;   // 2 log2(e) k0
+constexpr float kGeluV1 = kGeluV0 * 0.044715f;
+
+__device__ __forceinline__ float gelu_tanh_t(float h, float h2) {
+    const float v = h * fmaf(kGeluV1, h2, kGeluV0);
+    const float e = __builtin_amdgcn_exp2f(v);
+    return fmaf(-2.0f, __builtin_amdgcn_rcpf(1.0f + e), 1.0f);
+}
+
+__device__ __forceinline__ float gelu_f(float h) {
+    const float t = gelu_tanh_t(h, h * h);
+    const float hh = 0.5f * h;
+    return fmaf(hh, t, hh);
 }
 
 __device__ __forceinline__ float gelu_grad_f(float h) {
-    const float k0 = 0.7978845608028654f;
-    const float k1 = 0.044715f;
-    float t;
-    gelu_f(h, &t);
-    return 0.5f * (1.0f + t) + 0.5f * h * (1.0f - t * t) * k0 * fmaf(3.0f * k1, h * h, 1.0f);
+    const float h2 = h * h;
+    const float t = gelu_tanh_t(h, h2);
+    const float a = fmaf(0.5f, t, 0.5f);                                   // (1 + t) / 2
+    const float b = fmaf(-t, t, 1.0f);                                     // 1 - t^2
+    const float c = fmaf(1.5f * kGeluK0 * kGeluK1, h2, 0.5f * kGeluK0);    // k0 (1 + 3 k1 h^2) / 2
+    return fmaf(h * b, c, a);
 }
 
 // LDS layout of one operand stage: 64-byte rows stored in pairs as 128-byte
@@ -105,20 +121,15 @@ struct Staging {
     static_assert(RB % 16 == 0 && RPS >= 1, "staging geometry");
 
     template <class Ring>
-    __device__ __forceinline__ static lds8* at_stage(Ring ring, int s0, int r, int c16) {
-        return ring(s0 + r / RPS) + (r % RPS) * RB + ((c16 ^ (r & SWM)) << 4);
-    }
-    template <class Ring>
     __device__ __forceinline__ static lds8* at(Ring ring, int r, int c16) {
-        return at_stage(ring, 0, r, c16);
+        return ring(r / RPS) + (r % RPS) * RB + ((c16 ^ (r & SWM)) << 4);
     }
-    // Copies ROWS staged rows (from stage s0 on) to dst, whose rows are ld bytes
+    // Copies ROWS staged rows to dst, whose rows are ld bytes
     // apart, as 16-byte chunks; rows at or past rows_valid and chunks at or past
     // bytes_valid are skipped.  Each wave writes whole rows.
     template <int ROWS, int NT, class Ring>
     __device__ __forceinline__ static void copy_out(Ring ring, int t, uint8_t* dst, int64_t ld,
-                                                    int64_t rows_valid, int64_t bytes_valid,
-                                                    int s0 = 0) {
+                                                    int64_t rows_valid, int64_t bytes_valid) {
         constexpr int TOTAL = ROWS * NC;
         constexpr int PER_STAGE = RPS * NC / NT;   // loop iterations per stage
         static_assert(TOTAL % NT == 0 && (RPS * NC) % NT == 0, "copy split");
@@ -126,7 +137,7 @@ struct Staging {
         for (int it = 0; it < TOTAL / NT; ++it) {
             const int u = it * NT + t;
             const int r = u / NC, c = u % NC;
-            const u32x4 w = lds_ld<u32x4>(ring(s0 + it / PER_STAGE) + (r % RPS) * RB +
+            const u32x4 w = lds_ld<u32x4>(ring(it / PER_STAGE) + (r % RPS) * RB +
                                           ((c ^ (r & SWM)) << 4));
             if (r < rows_valid && c * 16 < bytes_valid)
                 *reinterpret_cast<u32x4*>(dst + r * ld + c * 16) = w;
@@ -159,8 +170,9 @@ __device__ __forceinline__ void butterfly_sum(float* v, int fr) {
     butterfly_step<NV / 16, 1>(v, fr);
 }
 
-template <int BM, int BN, int WGM, int WGN, int FA, int FB, int EPI, int QF>
+template <int BM, int BN, int WGM, int WGN, int NS, int FA, int FB, int EPI, int QF>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p) {
+    static_assert(NS == 3 || NS == 4, "three or four pipeline stages");
     constexpr int NW = WGM * WGN;              // waves per workgroup
     constexpr int WM = BM / WGM, WN = BN / WGN;  // wave sub-tile
     constexpr int TM = WM / 32, TN = WN / 32;  // 32 x 32 MFMA tiles per wave
@@ -173,7 +185,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p) {
     __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t st2[STAGE];
-    __shared__ __attribute__((aligned(16))) uint8_t st3[STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t st3[NS == 4 ? STAGE : 16];
 
     const int t = threadIdx.x;
     const int lane = t & (kWave - 1);
@@ -274,33 +286,41 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p) {
                     bf, af[i], acc[j][i], FB, FA, 0, 0, 0, 0);
         }
     };
-    // Stage kt lives in st[kt % 4]; loads run three stages ahead.  Before reading
-    // stage kt a wave waits for its own loads of that stage (the two later stages
-    // may stay in flight), then the barrier makes every wave's loads visible and
-    // frees the stage read in the previous step, which is refilled right away.
-    // The barrier is a bare s_barrier: __syncthreads() adds a workgroup fence,
-    // which waits for every outstanding load, the prefetched stages included.
-    // The barrier also waits for the wave's own LDS reads, so no wave refills a
-    // stage another wave is still reading.  Every step
-    // looks the same: past the end of K the stages are filled with zeros (all
-    // chunks out of range), which add nothing to the sums, so the wait count is
-    // a constant and the loop runs a multiple of four steps.
+    // Stage kt lives in st[kt % NS]; loads run NS - 1 stages ahead.  Before
+    // reading stage kt a wave waits for its own loads of that stage (the NS - 2
+    // later stages may stay in flight), then the barrier makes every wave's loads
+    // visible and frees the stage read in the previous step, which is refilled
+    // right away.  The barrier is a bare s_barrier: __syncthreads() adds a
+    // workgroup fence, which waits for every outstanding load, the prefetched
+    // stages included.  The barrier also waits for the wave's own LDS reads, so
+    // no wave refills a stage another wave is still reading.  Every step looks
+    // the same: past the end of K the stages are filled with zeros (all chunks
+    // out of range), which add nothing to the sums, so the wait count is a
+    // constant and the loop runs a multiple of NS steps.
     auto step = [&](uint8_t* cur, uint8_t* refill, int kt) {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * P));
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * P));
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        issue(refill, (int64_t)(kt + 3) * BKS);
+        issue(refill, (int64_t)(kt + NS - 1) * BKS);
         compute(cur);
     };
 
     const int nk = (int)((K + BKS - 1) / BKS);
     issue(st0, 0);
     issue(st1, BKS);
-    issue(st2, 2 * BKS);
-    for (int kt = 0; kt < nk; kt += 4) {
-        step(st0, st3, kt);
-        step(st1, st0, kt + 1);
-        step(st2, st1, kt + 2);
-        step(st3, st2, kt + 3);
+    if constexpr (NS == 4) {
+        issue(st2, 2 * BKS);
+        for (int kt = 0; kt < nk; kt += 4) {
+            step(st0, st3, kt);
+            step(st1, st0, kt + 1);
+            step(st2, st1, kt + 2);
+            step(st3, st2, kt + 3);
+        }
+    } else {
+        for (int kt = 0; kt < nk; kt += 3) {
+            step(st0, st2, kt);
+            step(st1, st0, kt + 1);
+            step(st2, st1, kt + 2);
+        }
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // the zero-filled look-ahead stages
     __syncthreads();                            // the ring is free for the epilogue
@@ -413,9 +433,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p) {
     if constexpr (EPI == kEpiF32 || EPI == kEpiDGeluF32) {
         // fp32 rows; a 256 x 256 tile goes out in two passes of 128 rows
         using G = Staging<BN * 4, STAGE>;
-        constexpr int PASSES = (BM * BN * 4 + 4 * STAGE - 1) / (4 * STAGE);
+        constexpr int PASSES = (BM * BN * 4 + NS * STAGE - 1) / (NS * STAGE);
         constexpr int RPP = BM / PASSES;
-        static_assert(RPP % WM == 0 && RPP <= 4 * G::RPS, "f32 staging");
+        static_assert(RPP % WM == 0 && RPP <= NS * G::RPS, "f32 staging");
 #pragma unroll
         for (int ps = 0; ps < PASSES; ++ps) {
             if (wm * WM >= ps * RPP && wm * WM < (ps + 1) * RPP) {
@@ -443,7 +463,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p) {
         uint16_t* hdst = EPI == kEpiBf16Bias ? (uint16_t*)p.out : p.h_out;
         if (hdst) {
             using G = Staging<BN * 2, STAGE>;
-            static_assert(BM <= 4 * G::RPS, "bf16 staging");
+            static_assert(BM <= NS * G::RPS, "bf16 staging");
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -464,16 +484,16 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p) {
     }
 
     if constexpr (EPI == kEpiGeluFp8 || EPI == kEpiDGeluFp8) {
-        // FP8 codes: the row-major tile in the first stages of the ring, the
-        // transposed tile (rows = output columns) in the stages after it.  For
-        // the transposed copy the four lanes of a quad swap bytes so that each
-        // holds one column of four consecutive rows, written as one word.
+        // FP8 codes: first the row-major tile goes through the ring, then the
+        // transposed one (rows = output columns).  For the transposed copy the
+        // four lanes of a quad swap bytes so that each holds one column of four
+        // consecutive rows, written as one word.
         using Q = Staging<BN, STAGE>;
         using QT = Staging<BM, STAGE>;
-        constexpr int QS = BM * BN / STAGE;    // stages taken by the row-major codes
-        static_assert(QS >= 1 && BM <= QS * Q::RPS && BN <= (4 - QS) * QT::RPS, "code staging");
+        static_assert(BM <= NS * Q::RPS && BN <= NS * QT::RPS, "code staging");
         const float qs = *p.q_scale;
         uint32_t amax_bits = 0;
+        uint32_t codes[TM][TN][4];
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -488,7 +508,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p) {
                     for (int e = 0; e < 4; ++e) {
                         float g;
                         if constexpr (EPI == kEpiGeluFp8) {
-                            g = gelu_f(acc[j][i][4 * q + e], nullptr);
+                            g = gelu_f(acc[j][i][4 * q + e]);
                             gs[e] = g * qs;
                         } else {
                             g = acc[j][i][4 * q + e];
@@ -504,26 +524,36 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p) {
                         if (!(m0 + lr < M && n0 + lc < N)) cm = 0;
                     }
                     amax_bits = amax_bits > cm ? amax_bits : cm;
+                    codes[i][j][q] = code;
                     lds_st(Q::at(ring, lr, lc / 16) + 4 * ((lc / 4) % 4), code);
-                    if (p.q_out_t) {
-                        const int odd = fr & 1, hi2 = fr & 2;
-                        const uint32_t o2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)code,
-                                                                              kDppQuadSwap2, 0xF, 0xF, false);
-                        const uint32_t c2 = hi2 ? __builtin_amdgcn_perm(o2, code, 0x03020706u)
-                                                : __builtin_amdgcn_perm(o2, code, 0x05040100u);
-                        const uint32_t o1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)c2,
-                                                                              kDppQuadSwap1, 0xF, 0xF, false);
-                        const uint32_t ct = odd ? __builtin_amdgcn_perm(o1, c2, 0x03070105u)
-                                                : __builtin_amdgcn_perm(o1, c2, 0x06020400u);
-                        const int tn = lc + (fr & 3);          // staged row = output column
-                        const int tm = (lr & ~3);              // first of the four rows
-                        lds_st(QT::at_stage(ring, QS, tn, tm / 16) + 4 * ((tm / 4) % 4), ct);
-                    }
                 }
         __syncthreads();
         Q::template copy_out<BM, NT>(ring, t, p.q_out + m0 * N + n0, N, M - m0, N - n0);
-        if (p.q_out_t)
-            QT::template copy_out<BN, NT>(ring, t, p.q_out_t + n0 * M + m0, M, N - n0, M - m0, QS);
+        if (p.q_out_t) {
+            __syncthreads();
+            const bool odd = fr & 1, hi2 = fr & 2;
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint32_t code = codes[i][j][q];
+                        const uint32_t o2 = (uint32_t)__builtin_amdgcn_mov_dpp(
+                            (int)code, kDppQuadSwap2, 0xF, 0xF, false);
+                        const uint32_t c2 = hi2 ? __builtin_amdgcn_perm(o2, code, 0x03020706u)
+                                                : __builtin_amdgcn_perm(o2, code, 0x05040100u);
+                        const uint32_t o1 = (uint32_t)__builtin_amdgcn_mov_dpp(
+                            (int)c2, kDppQuadSwap1, 0xF, 0xF, false);
+                        const uint32_t ct = odd ? __builtin_amdgcn_perm(o1, c2, 0x03070105u)
+                                                : __builtin_amdgcn_perm(o1, c2, 0x06020400u);
+                        const int tn = col_w + 32 * j + 8 * q + (fr & 3);  // staged row = column
+                        const int tm = (row_w + 32 * i) & ~3;              // first of four rows
+                        lds_st(QT::at(ring, tn, tm / 16) + 4 * ((tm / 4) % 4), ct);
+                    }
+            __syncthreads();
+            QT::template copy_out<BN, NT>(ring, t, p.q_out_t + n0 * M + m0, M, N - n0, M - m0);
+        }
         if constexpr (EPI == kEpiDGeluFp8) {
             if (p.col_partial) {
                 // column sums of the tile in a fixed order: over i in a lane, a
@@ -561,41 +591,64 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p) {
     }
 }
 
-// 256 x 256 tiles, eight waves of 64 x 128 (two waves per SIMD).
-constexpr int kBigWavesM = 4, kBigWavesN = 2;
-
+// 256 x 256 tiles, eight waves of 64 x 128 (two waves per SIMD), one workgroup
+// per CU.
 template <int FA, int FB, int EPI, int QF>
-__global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(64 * kBigWavesM * kBigWavesN)
+__global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(512)
 void gemm_kernel_256(GemmParams p) {
-    gemm_tile<256, 256, kBigWavesM, kBigWavesN, FA, FB, EPI, QF>(p);
+    gemm_tile<256, 256, 4, 2, 4, FA, FB, EPI, QF>(p);
+}
+
+// 128 x 256 tiles, four waves of 64 x 128 and a three-stage ring (72 KB), so two
+// workgroups share a CU and one's epilogue overlaps the other's main loop.
+template <int FA, int FB, int EPI, int QF>
+__global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(256)
+void gemm_kernel_128x256(GemmParams p) {
+    gemm_tile<128, 256, 2, 2, 3, FA, FB, EPI, QF>(p);
 }
 
 // 128 x 128 tiles, four waves of 64 x 64, two workgroups per CU.
 template <int FA, int FB, int EPI, int QF>
 __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(256)
 void gemm_kernel_128(GemmParams p) {
-    gemm_tile<128, 128, 2, 2, FA, FB, EPI, QF>(p);
+    gemm_tile<128, 128, 2, 2, 4, FA, FB, EPI, QF>(p);
 }
 
-template <int BM, int BN, int FA, int FB, int EPI, int QF>
-hipError_t launch_tile(const GemmParams& p, hipStream_t stream) {
-    const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-    if constexpr (BM == 256)
-        hipLaunchKernelGGL((gemm_kernel_256<FA, FB, EPI, QF>), dim3((unsigned)tiles),
-                           dim3(64 * kBigWavesM * kBigWavesN), 0, stream, p);
-    else
-        hipLaunchKernelGGL((gemm_kernel_128<FA, FB, EPI, QF>), dim3((unsigned)tiles),
-                           dim3(256), 0, stream, p);
-    return hipGetLastError();
-}
+enum TileShape { kTile256, kTile128x256, kTile128 };
 
-// 256 x 256 tiles when they give at least one tile per CU, else 128 x 128.
-bool use_big_tiles(int64_t M, int64_t N) { return ((M + 255) / 256) * ((N + 255) / 256) >= 256; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Large problems: with K up to 2048 the epilogue is a large share of a tile's
+// time, and two 128 x 256 workgroups per CU hide one's epilogue behind the
+// other's main loop; with longer K the 256 x 256 tile's lower LDS and L2
+// traffic per MFMA wins.  Problems too small to fill the CUs with either take
+// 128 x 128 tiles.
+TileShape pick_tile(int64_t M, int64_t N, int64_t K) {
+    const bool long_k = K > 2048;
+    if (long_k && cdiv(M, 256) * cdiv(N, 256) >= 256) return kTile256;
+    if (cdiv(M, 128) * cdiv(N, 256) >= 512) return kTile128x256;
+    return kTile128;
+}
 
 template <int FA, int FB, int EPI, int QF>
 hipError_t launch_typed(const GemmParams& p, hipStream_t stream) {
-    if (use_big_tiles(p.M, p.N)) return launch_tile<256, 256, FA, FB, EPI, QF>(p, stream);
-    return launch_tile<128, 128, FA, FB, EPI, QF>(p, stream);
+    switch (pick_tile(p.M, p.N, p.K)) {
+        case kTile256:
+            hipLaunchKernelGGL((gemm_kernel_256<FA, FB, EPI, QF>),
+                               dim3((unsigned)(cdiv(p.M, 256) * cdiv(p.N, 256))), dim3(512), 0,
+                               stream, p);
+            break;
+        case kTile128x256:
+            hipLaunchKernelGGL((gemm_kernel_128x256<FA, FB, EPI, QF>),
+                               dim3((unsigned)(cdiv(p.M, 128) * cdiv(p.N, 256))), dim3(256), 0,
+                               stream, p);
+            break;
+        default:
+            hipLaunchKernelGGL((gemm_kernel_128<FA, FB, EPI, QF>),
+                               dim3((unsigned)(cdiv(p.M, 128) * cdiv(p.N, 128))), dim3(256), 0,
+                               stream, p);
+    }
+    return hipGetLastError();
 }
 
 template <int FA, int FB>
@@ -616,8 +669,8 @@ hipError_t launch_epi(const GemmParams& p, hipStream_t stream) {
 
 }  // namespace
 
-int64_t gemm_partial_rows(int64_t M, int64_t N) {
-    return use_big_tiles(M, N) ? (M + 255) / 256 : (M + 127) / 128;
+int64_t gemm_partial_rows(int64_t M, int64_t N, int64_t K) {
+    return pick_tile(M, N, K) == kTile256 ? cdiv(M, 256) : cdiv(M, 128);
 }
 
 hipError_t launch_gemm(const GemmParams& p, hipStream_t stream) {

@@ -75,7 +75,7 @@ struct GemmParams {
 
 // Rows of the col_partial array launch_gemm writes for an M-row product (its
 // tile height), and an upper bound for workspace sizing.
-int64_t gemm_partial_rows(int64_t M, int64_t N);
+int64_t gemm_partial_rows(int64_t M, int64_t N, int64_t K);
 inline int64_t gemm_partial_rows_bound(int64_t M) { return (M + 127) / 128; }
 
 hipError_t launch_gemm(const GemmParams& p, hipStream_t stream);

@@ -210,7 +210,9 @@ def test_gelu_gemm_random_within_tolerance(M, N, K):
 
 # ---- the large-tile kernel (at least 256 output tiles of 256 x 256) -------------
 
-BIG = [(4096, 4096, 64), (4000, 4112, 48)]   # the second is ragged in M and N
+# 128 x 256 tiles (K <= 2048; the second is ragged in M and N), then 256 x 256
+# tiles (K > 2048)
+BIG = [(4096, 4096, 64), (4000, 4112, 48), (2048, 8192, 2176)]
 
 
 @pytest.mark.parametrize("fa,fb", PAIRS, ids=["e4m3xe4m3", "e5m2xe4m3", "e4m3xe5m2", "e5m2xe5m2"])
@@ -242,7 +244,8 @@ def test_gelu_epilogue_large_tiles_on_exact_products(M, N, K):
 # ---- fc2 dgrad with the fc1 gradient cast fused ---------------------------------
 
 @pytest.mark.parametrize("M,N,K,q", [(130, 272, 48, ops.E5M2), (256, 3072, 64, ops.E5M2),
-                                     (4096, 4096, 64, ops.E5M2), (4000, 4112, 48, ops.E4M3)])
+                                     (4096, 4096, 64, ops.E5M2), (4000, 4112, 48, ops.E4M3),
+                                     (2048, 8192, 2176, ops.E5M2)])
 def test_dgelu_fp8_epilogue_equals_dgelu_then_cast(M, N, K, q):
     """The fused epilogue computes the same fp32 d = acc * alpha * gelu'(h) as the
     fp32 epilogue and casts it like the cast kernel: codes, transpose and amax
