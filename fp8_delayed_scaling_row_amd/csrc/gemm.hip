@@ -126,7 +126,8 @@ struct Staging {
     }
     // Copies ROWS staged rows to dst, whose rows are ld bytes
     // apart, as 16-byte chunks; rows at or past rows_valid and chunks at or past
-    // bytes_valid are skipped.  Each wave writes whole rows.
+    // bytes_valid are skipped.  Each wave writes whole rows, with non-temporal
+    // stores (the output is not read again by this kernel).
     template <int ROWS, int NT, class Ring>
     __device__ __forceinline__ static void copy_out(Ring ring, int t, uint8_t* dst, int64_t ld,
                                                     int64_t rows_valid, int64_t bytes_valid) {
@@ -140,7 +141,7 @@ struct Staging {
             const u32x4 w = lds_ld<u32x4>(ring(it / PER_STAGE) + (r % RPS) * RB +
                                           ((c ^ (r & SWM)) << 4));
             if (r < rows_valid && c * 16 < bytes_valid)
-                *reinterpret_cast<u32x4*>(dst + r * ld + c * 16) = w;
+                __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(dst + r * ld + c * 16));
         }
     }
 };

@@ -26,15 +26,27 @@ constexpr int kWavesPerBlock = kThreads / kWave;
 // CPL: 16-byte chunks per lane (hidden <= CPL * 64 * 8).
 //
 // Memory-level parallelism: a wave loads the next row it owns before it works on
-// the current one, so two rows per wave are in flight; gamma and beta stay in
-// registers as packed bf16 (half the registers of fp32 copies) and are widened
-// when used.  Row statistics use DPP reductions inside 16-lane rows.
+// the current one, so two rows per wave are in flight.  Both rows stay packed
+// as bf16 (CPL * 4 registers each) and are widened in each of the three passes
+// (sum, squared deviations, output); gamma and beta sit in LDS.  With the
+// register count that low, eight waves share each SIMD.  Row statistics use DPP
+// reductions inside 16-lane rows.
+// An empty asm that claims to change the packed row: the compiler cannot reuse
+// the widened values of an earlier pass and keep 8 fp32 per chunk live.
+template <int CPL>
+__device__ __forceinline__ void keep_packed(uint4 (&r)[CPL]) {
+#pragma unroll
+    for (int i = 0; i < CPL; ++i)
+        asm volatile("" : "+v"(r[i].x), "+v"(r[i].y), "+v"(r[i].z), "+v"(r[i].w));
+}
+
 template <int CPL, int FMT>
 __global__ __launch_bounds__(kThreads) void ln_cast_amax_kernel(
     const uint4* __restrict__ x, const uint4* __restrict__ gamma, const uint4* __restrict__ beta,
     int64_t rows, int hidden, float eps, const float* __restrict__ scale_ptr,
     float* __restrict__ amax_ptr, uint2* __restrict__ out, float* __restrict__ mean_out,
     float* __restrict__ rstd_out) {
+    __shared__ uint4 gb[2][CPL * kWave];   // gamma, beta as packed bf16 chunks
     __shared__ uint32_t red[kWavesPerBlock];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
@@ -42,72 +54,70 @@ __global__ __launch_bounds__(kThreads) void ln_cast_amax_kernel(
     const float inv_h = 1.0f / (float)hidden;
     const float s = *scale_ptr;
 
-    uint4 gp[CPL], bp[CPL];   // packed bf16 gamma / beta of this lane's chunks
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-        const int c = lane + i * kWave;
-        gp[i] = c < nchunk ? gamma[c] : make_uint4(0, 0, 0, 0);
-        bp[i] = c < nchunk ? beta[c] : make_uint4(0, 0, 0, 0);
+    for (int c = threadIdx.x; c < CPL * kWave; c += kThreads) {
+        gb[0][c] = c < nchunk ? gamma[c] : make_uint4(0, 0, 0, 0);
+        gb[1][c] = c < nchunk ? beta[c] : make_uint4(0, 0, 0, 0);
     }
+    __syncthreads();
 
     const int64_t stride = (int64_t)gridDim.x * kWavesPerBlock;
     int64_t row = (int64_t)blockIdx.x * kWavesPerBlock + wave;
-    uint4 nxt[CPL];
+    uint4 cur[CPL], nxt[CPL];
     auto load_row = [&](int64_t r, uint4* dst) {
         const uint4* xr = x + r * nchunk;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
             const int c = lane + i * kWave;
-            dst[i] = (r < rows && c < nchunk) ? xr[c] : make_uint4(0, 0, 0, 0);
+            dst[i] = (r < rows && c < nchunk) ? load_nt(xr + c) : make_uint4(0, 0, 0, 0);
         }
     };
     load_row(row, nxt);
 
     uint32_t amax_bits = 0;
     for (; row < rows; row += stride) {
-        // Keep gamma/beta packed across iterations: without this the compiler
-        // hoists their widening out of the loop and holds 16 fp32 per chunk.
 #pragma unroll
-        for (int i = 0; i < CPL; ++i)
-            asm volatile("" : "+v"(gp[i].x), "+v"(gp[i].y), "+v"(gp[i].z), "+v"(gp[i].w),
-                         "+v"(bp[i].x), "+v"(bp[i].y), "+v"(bp[i].z), "+v"(bp[i].w));
-        float v[CPL * 8];
+        for (int i = 0; i < CPL; ++i) cur[i] = nxt[i];
+        load_row(row + stride, nxt);   // next row in flight while this one is processed
         float sum = 0.0f;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
-            unpack_bf16x8(nxt[i], v + 8 * i);
+            float v[8];
+            unpack_bf16x8(cur[i], v);
 #pragma unroll
-            for (int k = 0; k < 8; ++k) sum += v[8 * i + k];
+            for (int k = 0; k < 8; ++k) sum += v[k];
         }
-        load_row(row + stride, nxt);   // next row in flight while this one is processed
         const float mu = wave_sum_dpp(sum) * inv_h;
+        keep_packed(cur);
         float sq = 0.0f;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
             const bool valid = lane + i * kWave < nchunk;
+            float v[8];
+            unpack_bf16x8(cur[i], v);
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                const float d = valid ? v[8 * i + k] - mu : 0.0f;
-                v[8 * i + k] = d;
+                const float d = valid ? v[k] - mu : 0.0f;
                 sq += d * d;
             }
         }
         const float var = wave_sum_dpp(sq) * inv_h;
         const float rs = 1.0f / sqrtf(var + eps);
+        keep_packed(cur);
 
         uint2* orow = out + row * nchunk;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
             const int c = lane + i * kWave;
             if (c < nchunk) {
-                float gg[8], bb[8];
-                unpack_bf16x8(gp[i], gg);
-                unpack_bf16x8(bp[i], bb);
+                float v[8], gg[8], bb[8];
+                unpack_bf16x8(cur[i], v);
+                unpack_bf16x8(gb[0][c], gg);
+                unpack_bf16x8(gb[1][c], bb);
                 float y[8];
                 uint32_t cm = 0;
 #pragma unroll
                 for (int k = 0; k < 8; ++k) {
-                    y[k] = fmaf(v[8 * i + k] * rs, gg[k], bb[k]);
+                    y[k] = fmaf((v[k] - mu) * rs, gg[k], bb[k]);
                     const uint32_t ab = abs_bits(y[k]);
                     cm = cm > ab ? cm : ab;
                 }
@@ -121,7 +131,7 @@ __global__ __launch_bounds__(kThreads) void ln_cast_amax_kernel(
                     q.x = patch_nan4(q.x, ys);
                     q.y = patch_nan4(q.y, ys + 4);
                 }
-                orow[c] = q;
+                store_nt(orow + c, q);
                 amax_bits = amax_bits > cm ? amax_bits : cm;
             }
         }
@@ -138,12 +148,29 @@ hipError_t launch_ln_fwd_cpl(int64_t rows, int hidden, const void* x, const void
                              const void* beta, float eps, int fp8, const float* scale,
                              float* amax, uint8_t* out, float* mean, float* rstd,
                              hipStream_t stream) {
-    // Resident grid: as many workgroups as the CUs hold at once (register-limited
-    // occupancy, one wave per SIMD per workgroup), each looping over rows, so the
-    // row prefetch runs across the whole sweep instead of restarting per wave.
+    // Resident grid: as many workgroups as the CUs hold at once, each looping
+    // over rows, so the row prefetch runs across the whole sweep instead of
+    // restarting per wave (a second round of workgroups would run alone at the
+    // end of the sweep).
+    static int resident[2] = {0, 0};   // per output format, from the occupancy query
+    int& per_cu = resident[fp8 == kE4M3 ? 0 : 1];
+    if (per_cu == 0) {
+        int nb = 0;
+        hipError_t e = fp8 == kE4M3
+            ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, ln_cast_amax_kernel<CPL, kE4M3>,
+                                                          kThreads, 0)
+            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, ln_cast_amax_kernel<CPL, kE5M2>,
+                                                          kThreads, 0);
+        if (e != hipSuccess) return e;
+        int dev = 0, cus = 0;
+        if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+        if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) !=
+            hipSuccess)
+            return e;
+        per_cu = (nb > 0 ? nb : 1) * cus;
+    }
     int64_t want = (rows + kWavesPerBlock - 1) / kWavesPerBlock;
-    const int64_t cap = 256 * (CPL <= 1 ? 8 : CPL <= 2 ? 6 : CPL <= 4 ? 4 : 2);
-    const int blocks = (int)(want < cap ? want : cap);
+    const int blocks = (int)(want < per_cu ? want : per_cu);
     if (fp8 == kE4M3)
         hipLaunchKernelGGL((ln_cast_amax_kernel<CPL, kE4M3>), dim3(blocks), dim3(kThreads), 0,
                            stream, (const uint4*)x, (const uint4*)gamma, (const uint4*)beta,
@@ -194,9 +221,9 @@ __global__ __launch_bounds__(kThreads) void ln_bwd_kernel(
         for (int i = 0; i < CPL; ++i) {
             const int c = lane + i * kWave;
             if (c < nchunk) {
-                unpack_bf16x8(x[row * nchunk + c], xh + 8 * i);
-                const float4 a = dy[(row * nchunk + c) * 2];
-                const float4 b2 = dy[(row * nchunk + c) * 2 + 1];
+                unpack_bf16x8(load_nt(x + row * nchunk + c), xh + 8 * i);
+                const float4 a = load_nt(dy + (row * nchunk + c) * 2);
+                const float4 b2 = load_nt(dy + (row * nchunk + c) * 2 + 1);
                 d[8 * i + 0] = a.x; d[8 * i + 1] = a.y; d[8 * i + 2] = a.z; d[8 * i + 3] = a.w;
                 d[8 * i + 4] = b2.x; d[8 * i + 5] = b2.y; d[8 * i + 6] = b2.z; d[8 * i + 7] = b2.w;
             } else {
@@ -231,7 +258,7 @@ __global__ __launch_bounds__(kThreads) void ln_bwd_kernel(
                 w.y = pack_bf16x2(o[2], o[3]);
                 w.z = pack_bf16x2(o[4], o[5]);
                 w.w = pack_bf16x2(o[6], o[7]);
-                dx[row * nchunk + c] = w;
+                store_nt(dx + row * nchunk + c, w);
             }
         }
     }

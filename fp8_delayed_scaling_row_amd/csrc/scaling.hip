@@ -34,9 +34,24 @@ __global__ __launch_bounds__(kThreads) void meta_init_kernel(float* hist, float*
     }
 }
 
+// Wave-wide max with fmaxf semantics (a NaN operand is dropped): DPP steps
+// inside each 16-lane row, then two shuffles across rows.
+__device__ __forceinline__ float wave_max_f32(float v) {
+    v = fmaxf(v, dpp_f32<kDppQuadSwap1>(v));
+    v = fmaxf(v, dpp_f32<kDppQuadSwap2>(v));
+    v = fmaxf(v, dpp_f32<kDppRowHalfMirror>(v));
+    v = fmaxf(v, dpp_f32<kDppRowMirror>(v));
+    v = fmaxf(v, __shfl_xor(v, 16, kWave));
+    v = fmaxf(v, __shfl_xor(v, 32, kWave));
+    return v;
+}
+
 // One workgroup updates every slot of one state block in a single pass over the
 // history: every thread loads its share once into registers, the per-slot max
 // comes from those registers, and the shifted rows are written back from them.
+// Element j = tid + 256 t of the flattened [len][n_slots] history belongs to
+// slot j % n_slots; when n_slots divides 256 (1, 2, 4, 8 slots) that slot is the
+// same for all of a thread's elements and one running max suffices.
 __global__ __launch_bounds__(kThreads) void scaling_update_kernel(float* hist, float* scale,
                                                                  float* scale_inv, int len,
                                                                  int n_slots, int margin,
@@ -48,37 +63,49 @@ __global__ __launch_bounds__(kThreads) void scaling_update_kernel(float* hist, f
     const int wave = tid / kWave;
     const int total = len * n_slots;
 
-    // flat index j = tid + 256 t; its slot is j % n_slots
     float keep[kPerThread];
-    float m[kMaxSlots];
-    int nan[kMaxSlots];
-#pragma unroll
-    for (int s = 0; s < kMaxSlots; ++s) { m[s] = 0.0f; nan[s] = 0; }
 #pragma unroll
     for (int t = 0; t < kPerThread; ++t) {
         const int j = tid + t * kThreads;
         keep[t] = j < total ? hist[j] : 0.0f;
-        if (j < total) {
-            const int s = j % n_slots;
+    }
+    float m[kMaxSlots];
+    int nan[kMaxSlots];
 #pragma unroll
-            for (int q = 0; q < kMaxSlots; ++q) {
-                if (q == s) {
-                    nan[q] |= (keep[t] != keep[t]);
+    for (int q = 0; q < kMaxSlots; ++q) { m[q] = 0.0f; nan[q] = 0; }
+    if (kThreads % n_slots == 0) {
+        float mm = 0.0f;
+        int nn = 0;
+#pragma unroll
+        for (int t = 0; t < kPerThread; ++t) {   // elements past the end hold 0
+            mm = fmaxf(mm, keep[t]);
+            nn |= keep[t] != keep[t];
+        }
+        const int sl = tid % n_slots;
+#pragma unroll
+        for (int q = 0; q < kMaxSlots; ++q)
+            if (q == sl) { m[q] = mm; nan[q] = nn; }
+    } else {
+        const int ds = kThreads % n_slots;
+        int sl = tid % n_slots;
+#pragma unroll
+        for (int t = 0; t < kPerThread; ++t) {
+#pragma unroll
+            for (int q = 0; q < kMaxSlots; ++q)
+                if (q == sl) {
                     m[q] = fmaxf(m[q], keep[t]);
+                    nan[q] |= keep[t] != keep[t];
                 }
-            }
+            sl += ds;
+            sl -= sl >= n_slots ? n_slots : 0;
         }
     }
-#pragma unroll
-    for (int q = 0; q < kMaxSlots; ++q) {
-#pragma unroll
-        for (int off = kWave / 2; off > 0; off >>= 1) {
-            m[q] = fmaxf(m[q], __shfl_xor(m[q], off, kWave));
-            nan[q] |= __shfl_xor(nan[q], off, kWave);
-        }
+    for (int q = 0; q < n_slots; ++q) {   // uniform bound
+        const float wm = wave_max_f32(m[q]);
+        const int wn = __any(nan[q]);
         if (lane == 0) {
-            red_max[wave][q] = m[q];
-            red_nan[wave][q] = nan[q];
+            red_max[wave][q] = wm;
+            red_nan[wave][q] = wn;
         }
     }
     __syncthreads();
