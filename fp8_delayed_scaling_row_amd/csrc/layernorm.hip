@@ -25,103 +25,107 @@ constexpr int kWavesPerBlock = kThreads / kWave;
 
 // CPL: 16-byte chunks per lane (hidden <= CPL * 64 * 8).
 //
-// Memory-level parallelism: a wave loads the next row it owns before it works on
-// the current one, so two rows per wave are in flight.  Both rows stay packed
-// as bf16 (CPL * 4 registers each) and are widened in each of the three passes
-// (sum, squared deviations, output); gamma and beta sit in LDS.  With the
-// register count that low, eight waves share each SIMD.  Row statistics use DPP
-// reductions inside 16-lane rows.
-// An empty asm that claims to change the packed row: the compiler cannot reuse
-// the widened values of an earlier pass and keep 8 fp32 per chunk live.
-template <int CPL>
-__device__ __forceinline__ void keep_packed(uint4 (&r)[CPL]) {
-#pragma unroll
-    for (int i = 0; i < CPL; ++i)
-        asm volatile("" : "+v"(r[i].x), "+v"(r[i].y), "+v"(r[i].z), "+v"(r[i].w));
-}
-
-template <int CPL, int FMT>
+// The kernel is bound by VALU issue (a wave64 fp32 operation occupies a SIMD for
+// four cycles), so it is written to spend few operations per element: the row
+// is widened once and kept centred (x - mean) in fp32 registers between the
+// passes, gamma and beta are widened once per workgroup into LDS, rows that fill
+// every lane skip the per-element validity test, and the amax uses a
+// three-operand max.  Memory-level parallelism: a wave loads the next row it owns
+// (packed bf16, non-temporal) before it works on the current one.  Row
+// statistics use DPP reductions inside 16-lane rows.  FULL: hidden is exactly
+// CPL * 512, so every lane owns CPL whole chunks and no lane needs masking.
+template <int CPL, int FMT, bool FULL>
 __global__ __launch_bounds__(kThreads) void ln_cast_amax_kernel(
     const uint4* __restrict__ x, const uint4* __restrict__ gamma, const uint4* __restrict__ beta,
     int64_t rows, int hidden, float eps, const float* __restrict__ scale_ptr,
     float* __restrict__ amax_ptr, uint2* __restrict__ out, float* __restrict__ mean_out,
     float* __restrict__ rstd_out) {
-    __shared__ uint4 gb[2][CPL * kWave];   // gamma, beta as packed bf16 chunks
+    __shared__ float4 gb[2][CPL * kWave][2];   // gamma, beta widened to fp32, 8 per chunk
     __shared__ uint32_t red[kWavesPerBlock];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    const int nchunk = hidden / 8;
+    const int nchunk = FULL ? CPL * kWave : hidden / 8;
     const float inv_h = 1.0f / (float)hidden;
     const float s = *scale_ptr;
 
     for (int c = threadIdx.x; c < CPL * kWave; c += kThreads) {
-        gb[0][c] = c < nchunk ? gamma[c] : make_uint4(0, 0, 0, 0);
-        gb[1][c] = c < nchunk ? beta[c] : make_uint4(0, 0, 0, 0);
+        float g[8], b[8];
+        unpack_bf16x8(c < nchunk ? gamma[c] : make_uint4(0, 0, 0, 0), g);
+        unpack_bf16x8(c < nchunk ? beta[c] : make_uint4(0, 0, 0, 0), b);
+        gb[0][c][0] = make_float4(g[0], g[1], g[2], g[3]);
+        gb[0][c][1] = make_float4(g[4], g[5], g[6], g[7]);
+        gb[1][c][0] = make_float4(b[0], b[1], b[2], b[3]);
+        gb[1][c][1] = make_float4(b[4], b[5], b[6], b[7]);
     }
     __syncthreads();
 
     const int64_t stride = (int64_t)gridDim.x * kWavesPerBlock;
     int64_t row = (int64_t)blockIdx.x * kWavesPerBlock + wave;
-    uint4 cur[CPL], nxt[CPL];
-    auto load_row = [&](int64_t r, uint4* dst) {
-        const uint4* xr = x + r * nchunk;
+    uint4 nxt[CPL];
+    // Past the last row a wave reloads the last row instead (and never uses it),
+    // so the loads need no branch and the loop-carried row needs no copies.
+    auto load_row = [&](int64_t r) {
+        const uint4* xr = x + (r < rows ? r : rows - 1) * nchunk;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
             const int c = lane + i * kWave;
-            dst[i] = (r < rows && c < nchunk) ? load_nt(xr + c) : make_uint4(0, 0, 0, 0);
+            nxt[i] = (FULL || c < nchunk) ? load_nt(xr + c) : make_uint4(0, 0, 0, 0);
         }
     };
-    load_row(row, nxt);
+    load_row(row);
 
     uint32_t amax_bits = 0;
     for (; row < rows; row += stride) {
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) cur[i] = nxt[i];
-        load_row(row + stride, nxt);   // next row in flight while this one is processed
+        float d[CPL * 8];
         float sum = 0.0f;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
-            float v[8];
-            unpack_bf16x8(cur[i], v);
+            unpack_bf16x8(nxt[i], d + 8 * i);
 #pragma unroll
-            for (int k = 0; k < 8; ++k) sum += v[k];
+            for (int k = 0; k < 8; ++k) sum += d[8 * i + k];
         }
+        // the next row goes in flight now; the fence keeps the compiler from
+        // hoisting these loads above the widening (which would copy the row)
+        __builtin_amdgcn_sched_barrier(0);
+        load_row(row + stride);
         const float mu = wave_sum_dpp(sum) * inv_h;
-        keep_packed(cur);
         float sq = 0.0f;
+        if constexpr (FULL) {
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-            const bool valid = lane + i * kWave < nchunk;
-            float v[8];
-            unpack_bf16x8(cur[i], v);
+            for (int j = 0; j < CPL * 8; ++j) {
+                d[j] -= mu;
+                sq += d[j] * d[j];
+            }
+        } else {
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const float d = valid ? v[k] - mu : 0.0f;
-                sq += d * d;
+            for (int i = 0; i < CPL; ++i) {
+                const bool valid = lane + i * kWave < nchunk;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    d[8 * i + k] = valid ? d[8 * i + k] - mu : 0.0f;
+                    sq += d[8 * i + k] * d[8 * i + k];
+                }
             }
         }
         const float var = wave_sum_dpp(sq) * inv_h;
         const float rs = 1.0f / sqrtf(var + eps);
-        keep_packed(cur);
 
         uint2* orow = out + row * nchunk;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
             const int c = lane + i * kWave;
-            if (c < nchunk) {
-                float v[8], gg[8], bb[8];
-                unpack_bf16x8(cur[i], v);
-                unpack_bf16x8(gb[0][c], gg);
-                unpack_bf16x8(gb[1][c], bb);
-                float y[8];
-                uint32_t cm = 0;
+            if (FULL || c < nchunk) {
+                const float4 g0 = gb[0][c][0], g1 = gb[0][c][1];
+                const float4 b0 = gb[1][c][0], b1 = gb[1][c][1];
+                const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+                const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+                float y[8], ys[8];
+                uint32_t cm = amax_bits;
 #pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    y[k] = fmaf((v[k] - mu) * rs, gg[k], bb[k]);
-                    const uint32_t ab = abs_bits(y[k]);
-                    cm = cm > ab ? cm : ab;
-                }
-                float ys[8];
+                for (int k = 0; k < 8; ++k) y[k] = fmaf(d[8 * i + k] * rs, gg[k], bb[k]);
+#pragma unroll
+                for (int k = 0; k < 8; k += 2)
+                    cm = max(cm, max(abs_bits(y[k]), abs_bits(y[k + 1])));   // v_max3_u32
 #pragma unroll
                 for (int k = 0; k < 8; ++k) ys[k] = y[k] * s;
                 uint2 q;
@@ -132,7 +136,7 @@ __global__ __launch_bounds__(kThreads) void ln_cast_amax_kernel(
                     q.y = patch_nan4(q.y, ys + 4);
                 }
                 store_nt(orow + c, q);
-                amax_bits = amax_bits > cm ? amax_bits : cm;
+                amax_bits = cm;
             }
         }
         if (lane == 0) {
@@ -143,11 +147,11 @@ __global__ __launch_bounds__(kThreads) void ln_cast_amax_kernel(
     block_amax_atomic(amax_bits, amax_ptr, red);
 }
 
-template <int CPL>
-hipError_t launch_ln_fwd_cpl(int64_t rows, int hidden, const void* x, const void* gamma,
-                             const void* beta, float eps, int fp8, const float* scale,
-                             float* amax, uint8_t* out, float* mean, float* rstd,
-                             hipStream_t stream) {
+template <int CPL, bool FULL>
+hipError_t launch_ln_fwd_full(int64_t rows, int hidden, const void* x, const void* gamma,
+                              const void* beta, float eps, int fp8, const float* scale,
+                              float* amax, uint8_t* out, float* mean, float* rstd,
+                              hipStream_t stream) {
     // Resident grid: as many workgroups as the CUs hold at once, each looping
     // over rows, so the row prefetch runs across the whole sweep instead of
     // restarting per wave (a second round of workgroups would run alone at the
@@ -157,10 +161,10 @@ hipError_t launch_ln_fwd_cpl(int64_t rows, int hidden, const void* x, const void
     if (per_cu == 0) {
         int nb = 0;
         hipError_t e = fp8 == kE4M3
-            ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, ln_cast_amax_kernel<CPL, kE4M3>,
-                                                          kThreads, 0)
-            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, ln_cast_amax_kernel<CPL, kE5M2>,
-                                                          kThreads, 0);
+            ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                  &nb, ln_cast_amax_kernel<CPL, kE4M3, FULL>, kThreads, 0)
+            : hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                  &nb, ln_cast_amax_kernel<CPL, kE5M2, FULL>, kThreads, 0);
         if (e != hipSuccess) return e;
         int dev = 0, cus = 0;
         if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
@@ -169,17 +173,30 @@ hipError_t launch_ln_fwd_cpl(int64_t rows, int hidden, const void* x, const void
             return e;
         per_cu = (nb > 0 ? nb : 1) * cus;
     }
+    if (rows == 0) return hipSuccess;
     int64_t want = (rows + kWavesPerBlock - 1) / kWavesPerBlock;
     const int blocks = (int)(want < per_cu ? want : per_cu);
     if (fp8 == kE4M3)
-        hipLaunchKernelGGL((ln_cast_amax_kernel<CPL, kE4M3>), dim3(blocks), dim3(kThreads), 0,
-                           stream, (const uint4*)x, (const uint4*)gamma, (const uint4*)beta,
+        hipLaunchKernelGGL((ln_cast_amax_kernel<CPL, kE4M3, FULL>), dim3(blocks), dim3(kThreads),
+                           0, stream, (const uint4*)x, (const uint4*)gamma, (const uint4*)beta,
                            rows, hidden, eps, scale, amax, (uint2*)out, mean, rstd);
     else
-        hipLaunchKernelGGL((ln_cast_amax_kernel<CPL, kE5M2>), dim3(blocks), dim3(kThreads), 0,
-                           stream, (const uint4*)x, (const uint4*)gamma, (const uint4*)beta,
+        hipLaunchKernelGGL((ln_cast_amax_kernel<CPL, kE5M2, FULL>), dim3(blocks), dim3(kThreads),
+                           0, stream, (const uint4*)x, (const uint4*)gamma, (const uint4*)beta,
                            rows, hidden, eps, scale, amax, (uint2*)out, mean, rstd);
     return hipGetLastError();
+}
+
+template <int CPL>
+hipError_t launch_ln_fwd_cpl(int64_t rows, int hidden, const void* x, const void* gamma,
+                             const void* beta, float eps, int fp8, const float* scale,
+                             float* amax, uint8_t* out, float* mean, float* rstd,
+                             hipStream_t stream) {
+    if (hidden == CPL * kWave * 8)
+        return launch_ln_fwd_full<CPL, true>(rows, hidden, x, gamma, beta, eps, fp8, scale, amax,
+                                             out, mean, rstd, stream);
+    return launch_ln_fwd_full<CPL, false>(rows, hidden, x, gamma, beta, eps, fp8, scale, amax,
+                                          out, mean, rstd, stream);
 }
 
 // ---- backward --------------------------------------------------------------
