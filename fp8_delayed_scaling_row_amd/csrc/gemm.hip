@@ -173,7 +173,7 @@ __device__ __forceinline__ void butterfly_sum(float* v, int fr) {
 
 template <int BM, int BN, int WGM, int WGN, int NS, int FA, int FB, int EPI, int QF>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p) {
-    static_assert(NS >= 3 && NS <= 5, "three to five pipeline stages");
+    static_assert(NS == 3 || NS == 4, "three or four pipeline stages");
     constexpr int NW = WGM * WGN;              // waves per workgroup
     constexpr int WM = BM / WGM, WN = BN / WGN;  // wave sub-tile
     constexpr int TM = WM / 32, TN = WN / 32;  // 32 x 32 MFMA tiles per wave
@@ -186,8 +186,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p) {
     __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t st2[STAGE];
-    __shared__ __attribute__((aligned(16))) uint8_t st3[NS >= 4 ? STAGE : 16];
-    __shared__ __attribute__((aligned(16))) uint8_t st4[NS >= 5 ? STAGE : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t st3[NS == 4 ? STAGE : 16];
 
     const int t = threadIdx.x;
     const int lane = t & (kWave - 1);
@@ -315,17 +314,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p) {
     const int nk = (int)((K + BKS - 1) / BKS);
     issue(st0, 0);
     issue(st1, BKS);
-    if constexpr (NS == 5) {
-        issue(st2, 2 * BKS);
-        issue(st3, 3 * BKS);
-        for (int kt = 0; kt < nk; kt += 5) {
-            step(st0, st4, kt);
-            step(st1, st0, kt + 1);
-            step(st2, st1, kt + 2);
-            step(st3, st2, kt + 3);
-            step(st4, st3, kt + 4);
-        }
-    } else if constexpr (NS == 4) {
+    if constexpr (NS == 4) {
         issue(st2, 2 * BKS);
         for (int kt = 0; kt < nk; kt += 4) {
             step(st0, st3, kt);
@@ -354,8 +343,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p) {
     // so the 32 rows a wave writes at once fall on different banks.
     constexpr int NT = 64 * NW;
     auto ring = [&](int sidx) -> lds8* {
-        return sidx == 0 ? (lds8*)st0 : sidx == 1 ? (lds8*)st1 : sidx == 2 ? (lds8*)st2
-             : sidx == 3 ? (lds8*)st3 : (lds8*)st4;
+        return sidx == 0 ? (lds8*)st0 : sidx == 1 ? (lds8*)st1 : sidx == 2 ? (lds8*)st2 : (lds8*)st3;
     };
     const float alpha = (*p.sinv_a) * (*p.sinv_b);
     const int row_w = wm * WM + fr;      // tile row of this lane's i = 0 values
@@ -615,9 +603,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p) {
 template <int FA, int FB, int EPI, int QF>
 __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(512)
 void gemm_kernel_256(GemmParams p) {
-    // five ring stages (the whole 160 KB LDS) unless the epilogue needs LDS of its own
-    constexpr int NS = (EPI == kEpiGeluFp8 || EPI == kEpiDGeluFp8) ? 4 : 5;
-    gemm_tile<256, 256, 4, 2, NS, FA, FB, EPI, QF>(p);
+    gemm_tile<256, 256, 4, 2, 4, FA, FB, EPI, QF>(p);
 }
 
 // 128 x 256 tiles, four waves of 64 x 128 and a three-stage ring (72 KB), so two
