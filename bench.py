@@ -13,6 +13,11 @@ LayerNormMLP 768 -> 3072 -> 768 forward on 8 x 256 tokens, and the
 2048 / 8192 / 12-layer scale-up on 64 x 256 tokens, fwd + bwd) are reported in
 "workloads" with TFLOP/s against the FP8 MFMA peak.
 
+Step times are replays of consecutive steps captured once in a HIP graph (the
+same kernels on the same buffers, without host launch gaps); the host-launched
+step time is reported beside them as eager_ms_per_step.  The roofline's kernel
+duration comes from HIP events around eager launches of that kernel.
+
 Every input is synthetic and generated on the device before timing.  The CPU
 baseline runs the oracle (numpy, float64) on a bounded sample of the headline
 workload on this host.
@@ -134,11 +139,14 @@ def bench_ln_cast(torch, ops, inputs, steps, warmup):
         step(s, kt)
     t1.record()
     torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / steps
+    eager_ms = t0.elapsed_time(t1) / steps
     kernel_ms = kt.mean_ms()
+    # whole steps replayed from a HIP graph of n_buf consecutive steps (one per
+    # input buffer), so no host launch gap sits between the update and the kernel
+    ms = _graph_ms(torch, step, n_buf, max(1, steps // n_buf)) / n_buf
     bytes_step = rows * hidden * 3 + rows * 8
-    return dict(rows=rows, hidden=hidden, ms=ms, kernel_ms=kernel_ms, bytes=bytes_step,
-                scale=float(meta.scale[0].item()))
+    return dict(rows=rows, hidden=hidden, ms=ms, eager_ms=eager_ms, kernel_ms=kernel_ms,
+                bytes=bytes_step, scale=float(meta.scale[0].item()))
 
 
 COPY_BYTES = 1 << 30     # each calibration copy reads and writes this many bytes
@@ -227,19 +235,47 @@ def summarize_counters(fetch_csv, write_csv):
 # ---- GEMM-bound workloads ------------------------------------------------------
 
 def gemm_kernel_ms(torch, ops, M, N, K, out_dtype, reps=20):
-    """Average duration of one fp8ln_gemm launch at this shape (HIP events)."""
+    """Average duration of one fp8ln_gemm launch at this shape: `reps` launches
+    captured in a HIP graph and replayed, timed with HIP events on the replay
+    stream (no host launch overhead between them)."""
     a = torch.randint(0, 0x77, (M, K), dtype=torch.uint8, device="cuda")
     b = torch.randint(0, 0x77, (N, K), dtype=torch.uint8, device="cuda")
     one = torch.ones(1, dtype=torch.float32, device="cuda")
     out = torch.empty((M, N), dtype=out_dtype, device="cuda")
-    for _ in range(3):
-        ops.gemm(a, ops.E4M3, b, ops.E4M3, one, one, out)
-    t = Timer(torch)
-    for _ in range(reps):
-        e = t.start()
-        ops.gemm(a, ops.E4M3, b, ops.E4M3, one, one, out)
-        t.stop(e)
-    return t.mean_ms()
+
+    def launches(_):
+        for _ in range(reps):
+            ops.gemm(a, ops.E4M3, b, ops.E4M3, one, one, out)
+
+    return _graph_ms(torch, launches, 1, 3) / reps
+
+
+def _graph_ms(torch, step, unroll, replays):
+    """Capture steps 0 .. unroll-1 in one HIP graph (after a warm run on the
+    capture stream) and return the average replay time in ms."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for s in range(unroll):
+            step(s)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for s in range(unroll):
+            step(s)
+    graph.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(replays):
+        graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / replays
+    del graph
+    return ms
 
 
 def bench_linear_fwd(torch, ops, inputs, steps, warmup, M=256, K=768, N=2304):
@@ -257,9 +293,9 @@ def bench_linear_fwd(torch, ops, inputs, steps, warmup, M=256, K=768, N=2304):
         ops.scaling_update(recipe, mf)
         ops.ln_linear_fwd(recipe, xs[s % 16], g, b, w, bias, out, mf, ctx)
 
-    ms = _time_steps(torch, step, steps, warmup)
+    t = _time_steps(torch, step, steps, warmup, unroll=16)
     flops = 2.0 * M * N * K
-    return dict(ms=ms, flops=flops, gemm=(M, N, K, torch.bfloat16))
+    return dict(t, flops=flops, gemm=(M, N, K, torch.bfloat16))
 
 
 def bench_linear_bwd(torch, ops, inputs, steps, warmup, M=2048, K=768, N=2304):
@@ -287,9 +323,9 @@ def bench_linear_bwd(torch, ops, inputs, steps, warmup, M=2048, K=768, N=2304):
         ops.ln_linear_bwd(recipe, dys[s % 4], x, g, ctx, mf, mb, dx, dgamma, dbeta, dw, dbias,
                           workspace=ws)
 
-    ms = _time_steps(torch, step, steps, warmup)
+    t = _time_steps(torch, step, steps, warmup, unroll=4)
     flops = 2 * 2.0 * M * N * K
-    return dict(ms=ms, flops=flops, gemm=(N, K, M, torch.float32))
+    return dict(t, flops=flops, gemm=(N, K, M, torch.float32))
 
 
 def bench_mlp_fwd(torch, ops, inputs, steps, warmup, M=2048, H=768, F=3072):
@@ -307,9 +343,9 @@ def bench_mlp_fwd(torch, ops, inputs, steps, warmup, M=2048, H=768, F=3072):
         ops.scaling_update(recipe, mf)
         ops.ln_mlp_fwd(recipe, xs[s % 4], g, b, w1, None, w2, None, out, mf, ctx)
 
-    ms = _time_steps(torch, step, steps, warmup)
+    t = _time_steps(torch, step, steps, warmup, unroll=4)
     flops = 2 * 2.0 * M * H * F
-    return dict(ms=ms, flops=flops, gemm=(M, F, H, torch.bfloat16))
+    return dict(t, flops=flops, gemm=(M, F, H, torch.bfloat16))
 
 
 def bench_mlp_stack(torch, ops, inputs, steps, warmup, fmt, M=16384, H=2048, F=8192, layers=12):
@@ -347,12 +383,16 @@ def bench_mlp_stack(torch, ops, inputs, steps, warmup, fmt, M=16384, H=2048, F=8
                            d["dbt"], d["dw1"], d["db1"], d["dw2"], d["db2"], workspace=ws)
             grad = dx
 
-    ms = _time_steps(torch, step, steps, warmup)
+    t = _time_steps(torch, step, steps, warmup, unroll=1)
     flops = layers * 6 * 2.0 * M * H * F
-    return dict(ms=ms, flops=flops, gemm=(M, F, H, torch.float32))
+    return dict(t, flops=flops, gemm=(M, F, H, torch.float32))
 
 
-def _time_steps(torch, step, steps, warmup):
+def _time_steps(torch, step, steps, warmup, unroll=4):
+    """Step time two ways on the same kernels and buffers: `eager_ms` with every
+    step launched from the host, and `ms` with `unroll` consecutive steps
+    replayed from one captured HIP graph (the launch-bound small workloads are
+    host-bound when launched eagerly from Python)."""
     for s in range(warmup):
         step(s)
     torch.cuda.synchronize()
@@ -363,7 +403,9 @@ def _time_steps(torch, step, steps, warmup):
         step(s)
     t1.record()
     torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / steps
+    eager = t0.elapsed_time(t1) / steps
+    replays = max(1, steps // unroll)
+    return dict(ms=_graph_ms(torch, step, unroll, replays) / unroll, eager_ms=eager)
 
 
 # ---- CPU baseline ----------------------------------------------------------------
@@ -452,6 +494,7 @@ def main():
             tflops = r["flops"] / (r["ms"] * 1e-3) / 1e12
             workloads.append(dict(
                 workload=name, description=desc, ms_per_step=round(r["ms"], 5),
+                eager_ms_per_step=round(r["eager_ms"], 5),
                 value=round(tflops, 2), unit="TFLOP/s",
                 frac_of_fp8_peak=round(tflops / FP8_PEAK_TFLOPS, 4),
                 roofline=dict(bound="mfma", kernel=f"fp8 gemm {M}x{N}x{K}",
@@ -469,6 +512,7 @@ def main():
         kgbs = head["bytes"] / (head["kernel_ms"] * 1e-3) / 1e9
         traffic = counter_traffic("ln_cast_amax_65536x2048", ["layernorm.hip", "device_common.hpp"])
         line.update(value=round(gbs, 2), unit="GB/s", ms_per_step=round(head["ms"], 5),
+                    eager_ms_per_step=round(head["eager_ms"], 5),
                     config=dict(workload="ln_cast_amax_65536x2048", rows=head["rows"],
                                 hidden=head["hidden"], out_dtype="fp8_e4m3",
                                 amax_history_len=1024, input="N(0,1) x drift 1->4, 0.1% x100",

@@ -621,25 +621,35 @@ void gemm_kernel_128(GemmParams p) {
     gemm_tile<128, 128, 2, 2, 4, FA, FB, EPI, QF>(p);
 }
 
-enum TileShape { kTile256, kTile128x256, kTile128 };
+// 64 x 64 tiles, four waves of 32 x 32, up to four workgroups per CU: for
+// problems that leave most CUs idle even with 128 x 128 tiles.
+template <int FA, int FB, int EPI, int QF>
+__global__ __attribute__((amdgpu_waves_per_eu(4, 4))) __launch_bounds__(256)
+void gemm_kernel_64(GemmParams p) {
+    gemm_tile<64, 64, 2, 2, 4, FA, FB, EPI, QF>(p);
+}
+
+enum TileShape { kTile256, kTile128x256, kTile128, kTile64 };
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Large problems: with K up to 2048 the epilogue is a large share of a tile's
 // time, and two 128 x 256 workgroups per CU hide one's epilogue behind the
 // other's main loop; with longer K the 256 x 256 tile's lower LDS and L2
-// traffic per MFMA wins.  Problems too small to fill the CUs with either take
-// 128 x 128 tiles.
-TileShape pick_tile(int64_t M, int64_t N, int64_t K) {
+// traffic per MFMA wins.  Smaller problems take 128 x 128 tiles, and 64 x 64
+// tiles when even those would leave most CUs idle (the fused dH epilogue needs
+// at least 64 columns per wave, so it stays on 128 x 128).
+TileShape pick_tile(int64_t M, int64_t N, int64_t K, int epi) {
     const bool long_k = K > 2048;
     if (long_k && cdiv(M, 256) * cdiv(N, 256) >= 256) return kTile256;
     if (cdiv(M, 128) * cdiv(N, 256) >= 512) return kTile128x256;
-    return kTile128;
+    if (epi == kEpiDGeluFp8 || cdiv(M, 128) * cdiv(N, 128) >= 128) return kTile128;
+    return kTile64;
 }
 
 template <int FA, int FB, int EPI, int QF>
 hipError_t launch_typed(const GemmParams& p, hipStream_t stream) {
-    switch (pick_tile(p.M, p.N, p.K)) {
+    switch (pick_tile(p.M, p.N, p.K, EPI)) {
         case kTile256:
             hipLaunchKernelGGL((gemm_kernel_256<FA, FB, EPI, QF>),
                                dim3((unsigned)(cdiv(p.M, 256) * cdiv(p.N, 256))), dim3(512), 0,
@@ -650,6 +660,14 @@ hipError_t launch_typed(const GemmParams& p, hipStream_t stream) {
                                dim3((unsigned)(cdiv(p.M, 128) * cdiv(p.N, 256))), dim3(256), 0,
                                stream, p);
             break;
+        case kTile64:
+            if constexpr (EPI != kEpiDGeluFp8) {
+                hipLaunchKernelGGL((gemm_kernel_64<FA, FB, EPI, QF>),
+                                   dim3((unsigned)(cdiv(p.M, 64) * cdiv(p.N, 64))), dim3(256), 0,
+                                   stream, p);
+                break;
+            }
+            [[fallthrough]];
         default:
             hipLaunchKernelGGL((gemm_kernel_128<FA, FB, EPI, QF>),
                                dim3((unsigned)(cdiv(p.M, 128) * cdiv(p.N, 128))), dim3(256), 0,
@@ -677,7 +695,7 @@ hipError_t launch_epi(const GemmParams& p, hipStream_t stream) {
 }  // namespace
 
 int64_t gemm_partial_rows(int64_t M, int64_t N, int64_t K) {
-    return pick_tile(M, N, K) == kTile256 ? cdiv(M, 256) : cdiv(M, 128);
+    return pick_tile(M, N, K, kEpiDGeluFp8) == kTile256 ? cdiv(M, 256) : cdiv(M, 128);
 }
 
 hipError_t launch_gemm(const GemmParams& p, hipStream_t stream) {
