@@ -9,6 +9,8 @@
 // HYBRID: E4M3 forward, E5M2 gradients).  The transposed copy exists because the
 // backward's GEMMs contract over the other index (dgrad over output features,
 // wgrad over tokens) and the GEMM reads operands with the contraction index last.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launchers.hpp"
 
@@ -46,6 +48,26 @@ __global__ __launch_bounds__(kThreads) void cast_tile_kernel(
     const bool col_ok = c0 < cols;   // cols % 16 == 0: a group is all in or all out
     const float s = *scale_ptr;
 
+    // All eight row loads of the thread go out before any arithmetic.
+    typedef typename std::conditional<IN_F32, float4, uint4>::type Raw;
+    constexpr int RPR = IN_F32 ? 2 : 1;   // 16-byte loads per row segment of 8 values
+    Raw raw[8][RPR];
+#pragma unroll
+    for (int h = 0; h < 8; ++h) {
+        const int64_t r = r0 + 64 * (h / 4) + 4 * p + (h % 4);
+        const bool ok = col_ok && r < rows;
+#pragma unroll
+        for (int k = 0; k < RPR; ++k) {
+            if constexpr (IN_F32) {
+                const float4* q = reinterpret_cast<const float4*>((const float*)in + r * cols + c0);
+                raw[h][k] = ok ? load_nt(q + k) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            } else {
+                const uint4* q = reinterpret_cast<const uint4*>((const uint16_t*)in + r * cols + c0);
+                raw[h][k] = ok ? load_nt(q) : make_uint4(0, 0, 0, 0);
+            }
+        }
+    }
+
     uint32_t cm = 0;
     float cs[8];
 #pragma unroll
@@ -59,19 +81,13 @@ __global__ __launch_bounds__(kThreads) void cast_tile_kernel(
         for (int i = 0; i < 4; ++i) {
             const int64_t r = r0 + 64 * half + 4 * p + i;
             const bool ok = col_ok && r < rows;
+            const Raw* w = raw[4 * half + i];
             float v[8];
-            if (ok) {
-                if constexpr (IN_F32) {
-                    const float4* q = reinterpret_cast<const float4*>((const float*)in + r * cols + c0);
-                    const float4 a = load_nt(q), b = load_nt(q + 1);
-                    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-                    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-                } else {
-                    unpack_bf16x8(load_nt(reinterpret_cast<const uint4*>((const uint16_t*)in + r * cols + c0)), v);
-                }
+            if constexpr (IN_F32) {
+                v[0] = w[0].x; v[1] = w[0].y; v[2] = w[0].z; v[3] = w[0].w;
+                v[4] = w[1].x; v[5] = w[1].y; v[6] = w[1].z; v[7] = w[1].w;
             } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+                unpack_bf16x8(w[0], v);
             }
             float vs[8];
             uint32_t rm = 0;
