@@ -152,6 +152,27 @@ def bench_ln_cast(torch, ops, inputs, steps, warmup):
 COPY_BYTES = 1 << 30     # each calibration copy reads and writes this many bytes
 
 
+def copy_ceiling_gbs(torch, reps=10):
+    """Read + write GB/s of a plain device-to-device copy of 1 GiB (torch's copy
+    kernel) on this machine: a practical ceiling for a streaming kernel, next to the
+    8 TB/s of the spec sheet."""
+    src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * COPY_BYTES / (ms * 1e-3) / 1e9
+
+
 def profile_ln(torch, ops, inputs, n):
     """Launches for a rocprofv3 --pmc run: n headline LayerNorm+cast launches and
     three elementwise copies (neg) of a 1 GiB bf16 tensor, a plain kernel of known
@@ -470,6 +491,7 @@ def main():
         log("ln_cast_amax 65536x2048 ...")
         head = bench_ln_cast(torch, ops, inputs, args.steps, args.warmup)
         torch.cuda.empty_cache()
+        head["copy_gbs"] = copy_ceiling_gbs(torch)
     if not args.quick:
         runs = [
             ("ln_linear_fwd", "LayerNormLinear fwd 8x32 tokens, 768->2304, HYBRID, history 16",
@@ -521,7 +543,9 @@ def main():
                                   achieved=round(kgbs, 2), peak=HBM_PEAK_GBS, unit="GB/s",
                                   frac=round(kgbs / HBM_PEAK_GBS, 4), traffic=traffic,
                                   kernel_ms=round(head["kernel_ms"], 5),
-                                  bytes_per_launch=head["bytes"]))
+                                  bytes_per_launch=head["bytes"],
+                                  copy_ceiling=round(head["copy_gbs"], 1),
+                                  frac_of_copy_ceiling=round(kgbs / head["copy_gbs"], 4)))
     line["workloads"] = workloads
     if not args.no_cpu_baseline and head:
         log("cpu baseline (oracle) ...")

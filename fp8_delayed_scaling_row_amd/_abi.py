@@ -47,14 +47,16 @@ class MetaStruct(C.Structure):
 
 class LinearCtxStruct(C.Structure):
     _fields_ = [("ln_q", C.c_void_p), ("ln_qt", C.c_void_p), ("w_q", C.c_void_p),
-                ("w_qt", C.c_void_p), ("mean", C.c_void_p), ("rstd", C.c_void_p)]
+                ("w_qt", C.c_void_p), ("mean", C.c_void_p), ("rstd", C.c_void_p),
+                ("w_scale_inv", C.c_void_p), ("reuse_weight_codes", C.c_int32)]
 
 
 class MlpCtxStruct(C.Structure):
     _fields_ = [("ln_q", C.c_void_p), ("ln_qt", C.c_void_p), ("w1_q", C.c_void_p),
                 ("w1_qt", C.c_void_p), ("w2_q", C.c_void_p), ("w2_qt", C.c_void_p),
                 ("h", C.c_void_p), ("g_q", C.c_void_p), ("g_qt", C.c_void_p),
-                ("mean", C.c_void_p), ("rstd", C.c_void_p)]
+                ("mean", C.c_void_p), ("rstd", C.c_void_p), ("w_scale_inv", C.c_void_p),
+                ("reuse_weight_codes", C.c_int32)]
 
 
 _P = C.c_void_p

@@ -522,8 +522,11 @@ int fp8ln_ln_linear_fwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_f
     REQUIRE(ctx->ln_q && ctx->w_q, "ctx.ln_q and ctx.w_q are required");
     if (ctx->ln_qt && M % 16 != 0)
         return fail(FP8LN_ERR_UNSUPPORTED, "ctx.ln_qt needs tokens %% 16 == 0");
-    REQUIRE_PTR(gamma); REQUIRE_PTR(beta); REQUIRE_PTR(weight);
-    REQUIRE_ALIGNED(gamma); REQUIRE_ALIGNED(beta); REQUIRE_ALIGNED(weight);
+    REQUIRE(!ctx->reuse_weight_codes || ctx->w_scale_inv,
+            "reuse_weight_codes needs ctx.w_scale_inv from an earlier forward");
+    REQUIRE_PTR(gamma); REQUIRE_PTR(beta);
+    if (!ctx->reuse_weight_codes) { REQUIRE_PTR(weight); REQUIRE_ALIGNED(weight); }
+    REQUIRE_ALIGNED(gamma); REQUIRE_ALIGNED(beta);
     REQUIRE_ALIGNED(ctx->w_q);
     if (ctx->w_qt) REQUIRE_ALIGNED(ctx->w_qt);
     if (bias) REQUIRE_ALIGNED(bias);
@@ -542,11 +545,16 @@ int fp8ln_ln_linear_fwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_f
                   "ln_cast_amax launch");
         if (ctx->ln_qt) FP8LN_TRY(launch_transpose_u8(M, K, ctx->ln_q, ctx->ln_qt, st), "transpose");
     }
-    FP8LN_TRY(launch_cast_amax(N, K, false, weight, f, fwd->scale + 1, hist + 1, ctx->w_q,
-                               ctx->w_qt, nullptr, nullptr, st),
-              "weight cast launch");
-    GemmParams p = gemm_params(M, N, K, ctx->ln_q, f, ctx->w_q, f, fwd->scale_inv + 0,
-                               fwd->scale_inv + 1, kEpiBf16Bias);
+    // FP8 weight storage: reuse the codes (and their scale_inv) of an earlier
+    // forward of this ctx, or cast now and record the scale_inv that goes with them
+    const float* w_sinv = ctx->w_scale_inv ? ctx->w_scale_inv : fwd->scale_inv + 1;
+    if (!ctx->reuse_weight_codes)
+        FP8LN_TRY(launch_cast_amax(N, K, false, weight, f, fwd->scale + 1, hist + 1, ctx->w_q,
+                                   ctx->w_qt, nullptr, nullptr, st, fwd->scale_inv + 1,
+                                   ctx->w_scale_inv),
+                  "weight cast launch");
+    GemmParams p = gemm_params(M, N, K, ctx->ln_q, f, ctx->w_q, f, fwd->scale_inv + 0, w_sinv,
+                               kEpiBf16Bias);
     p.bias = (const uint16_t*)bias;
     p.out = out;
     FP8LN_TRY(launch_gemm(p, st), "gemm launch");
@@ -598,7 +606,8 @@ int fp8ln_ln_linear_bwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_f
               "grad cast launch");
     // dgrad: dLN[M][K] = dy_q[M][N] . (w_qt[K][N])^T
     GemmParams dg = gemm_params(M, K, N, w.dy_q, bf, ctx->w_qt, ff, bwd->scale_inv + 0,
-                                fwd->scale_inv + 1, kEpiF32);
+                                ctx->w_scale_inv ? ctx->w_scale_inv : fwd->scale_inv + 1,
+                                kEpiF32);
     dg.out = w.dln;
     FP8LN_TRY(launch_gemm(dg, st), "dgrad launch");
     // wgrad: dW[N][K] = dy_qt[N][M] . (ln_qt[K][M])^T
@@ -634,8 +643,13 @@ int fp8ln_ln_mlp_fwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t hidden,
             "ctx.ln_q, w1_q, w2_q and g_q are required");
     if ((ctx->ln_qt || ctx->g_qt) && M % 16 != 0)
         return fail(FP8LN_ERR_UNSUPPORTED, "transposed activations need tokens %% 16 == 0");
-    REQUIRE_PTR(gamma); REQUIRE_PTR(beta); REQUIRE_PTR(w1); REQUIRE_PTR(w2);
-    REQUIRE_ALIGNED(gamma); REQUIRE_ALIGNED(beta); REQUIRE_ALIGNED(w1); REQUIRE_ALIGNED(w2);
+    REQUIRE(!ctx->reuse_weight_codes || ctx->w_scale_inv,
+            "reuse_weight_codes needs ctx.w_scale_inv from an earlier forward");
+    REQUIRE_PTR(gamma); REQUIRE_PTR(beta);
+    if (!ctx->reuse_weight_codes) {
+        REQUIRE_PTR(w1); REQUIRE_PTR(w2); REQUIRE_ALIGNED(w1); REQUIRE_ALIGNED(w2);
+    }
+    REQUIRE_ALIGNED(gamma); REQUIRE_ALIGNED(beta);
     REQUIRE_ALIGNED(ctx->w1_q); REQUIRE_ALIGNED(ctx->w2_q);
     if (ctx->w1_qt) REQUIRE_ALIGNED(ctx->w1_qt);
     if (ctx->w2_qt) REQUIRE_ALIGNED(ctx->w2_qt);
@@ -659,14 +673,23 @@ int fp8ln_ln_mlp_fwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t hidden,
                   "ln_cast_amax launch");
         if (ctx->ln_qt) FP8LN_TRY(launch_transpose_u8(M, H, ctx->ln_q, ctx->ln_qt, st), "transpose");
     }
-    FP8LN_TRY(launch_cast_amax(F, H, false, w1, f, fwd->scale + 1, hist + 1, ctx->w1_q, ctx->w1_qt,
-                               nullptr, nullptr, st),
-              "fc1 weight cast launch");
-    FP8LN_TRY(launch_cast_amax(H, F, false, w2, f, fwd->scale + 3, hist + 3, ctx->w2_q, ctx->w2_qt,
-                               nullptr, nullptr, st),
-              "fc2 weight cast launch");
-    GemmParams p1 = gemm_params(M, F, H, ctx->ln_q, f, ctx->w1_q, f, fwd->scale_inv + 0,
-                                fwd->scale_inv + 1, kEpiGeluFp8);
+    // FP8 weight storage: reuse the codes (and their scale_inv) of an earlier
+    // forward of this ctx, or cast now and record the scale_inv of each
+    float* wsi = ctx->w_scale_inv;
+    const float* w1_sinv = wsi ? wsi + 0 : fwd->scale_inv + 1;
+    const float* w2_sinv = wsi ? wsi + 1 : fwd->scale_inv + 3;
+    if (!ctx->reuse_weight_codes) {
+        FP8LN_TRY(launch_cast_amax(F, H, false, w1, f, fwd->scale + 1, hist + 1, ctx->w1_q,
+                                   ctx->w1_qt, nullptr, nullptr, st, fwd->scale_inv + 1,
+                                   wsi ? wsi + 0 : nullptr),
+                  "fc1 weight cast launch");
+        FP8LN_TRY(launch_cast_amax(H, F, false, w2, f, fwd->scale + 3, hist + 3, ctx->w2_q,
+                                   ctx->w2_qt, nullptr, nullptr, st, fwd->scale_inv + 3,
+                                   wsi ? wsi + 1 : nullptr),
+                  "fc2 weight cast launch");
+    }
+    GemmParams p1 = gemm_params(M, F, H, ctx->ln_q, f, ctx->w1_q, f, fwd->scale_inv + 0, w1_sinv,
+                                kEpiGeluFp8);
     p1.bias = (const uint16_t*)b1;
     p1.h_out = ctx->h;
     p1.q_out = ctx->g_q;
@@ -675,8 +698,8 @@ int fp8ln_ln_mlp_fwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t hidden,
     p1.q_amax = hist + 2;
     p1.q_fp8 = f;
     FP8LN_TRY(launch_gemm(p1, st), "fc1 launch");
-    GemmParams p2 = gemm_params(M, H, F, ctx->g_q, f, ctx->w2_q, f, fwd->scale_inv + 2,
-                                fwd->scale_inv + 3, kEpiBf16Bias);
+    GemmParams p2 = gemm_params(M, H, F, ctx->g_q, f, ctx->w2_q, f, fwd->scale_inv + 2, w2_sinv,
+                                kEpiBf16Bias);
     p2.bias = (const uint16_t*)b2;
     p2.out = out;
     FP8LN_TRY(launch_gemm(p2, st), "fc2 launch");
@@ -731,7 +754,8 @@ int fp8ln_ln_mlp_bwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t hidden,
     // fc2 dgrad with the GELU derivative and the fc1 gradient cast fused:
     // dH[M][F] = dy_q[M][H] . (w2_qt[F][H])^T * gelu'(h) -> dh_q, dh_qt, amax, db1
     GemmParams dg2 = gemm_params(M, F, H, w.dy_q, bf, ctx->w2_qt, ff, bwd->scale_inv + 0,
-                                 fwd->scale_inv + 3, kEpiDGeluFp8);
+                                 ctx->w_scale_inv ? ctx->w_scale_inv + 1 : fwd->scale_inv + 3,
+                                 kEpiDGeluFp8);
     dg2.h_in = ctx->h;
     dg2.q_out = w.dh_q;
     dg2.q_out_t = w.dh_qt;
@@ -751,7 +775,8 @@ int fp8ln_ln_mlp_bwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t hidden,
     FP8LN_TRY(launch_gemm(wg2, st), "fc2 wgrad launch");
     // fc1 dgrad: dLN[M][H] = dh_q[M][F] . (w1_qt[H][F])^T
     GemmParams dg1 = gemm_params(M, H, F, w.dh_q, bf, ctx->w1_qt, ff, bwd->scale_inv + 1,
-                                 fwd->scale_inv + 1, kEpiF32);
+                                 ctx->w_scale_inv ? ctx->w_scale_inv + 0 : fwd->scale_inv + 1,
+                                 kEpiF32);
     dg1.out = w.dln;
     FP8LN_TRY(launch_gemm(dg1, st), "fc1 dgrad launch");
     // fc1 wgrad: dW1[F][H] = dh_qt[F][M] . (ln_qt[H][M])^T

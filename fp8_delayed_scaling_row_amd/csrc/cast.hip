@@ -36,8 +36,9 @@ template <bool IN_F32, int FMT>
 __global__ __launch_bounds__(kThreads) void cast_tile_kernel(
     const void* __restrict__ in, int64_t rows, int64_t cols, const float* __restrict__ scale_ptr,
     float* __restrict__ amax_ptr, uint8_t* __restrict__ out, uint8_t* __restrict__ out_t,
-    float* __restrict__ partial) {
+    float* __restrict__ partial, const float* __restrict__ copy_src, float* __restrict__ copy_dst) {
     __shared__ uint32_t tq[kCT * kCPitch / 4];
+    if (copy_dst && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *copy_dst = *copy_src;
     __shared__ float psum[kThreads / 16][kCT];
     __shared__ uint32_t red[kThreads / kWave];
     const int t = threadIdx.x;
@@ -193,14 +194,15 @@ __global__ __launch_bounds__(kThreads) void encode_range_kernel(uint32_t start, 
 template <bool IN_F32>
 hipError_t launch_cast_fmt(int64_t rows, int64_t cols, const void* in, int fp8,
                            const float* scale, float* amax, uint8_t* out, uint8_t* out_t,
-                           float* partial, hipStream_t stream) {
+                           float* partial, const float* copy_src, float* copy_dst,
+                           hipStream_t stream) {
     const dim3 grid((unsigned)((cols + kCT - 1) / kCT), (unsigned)((rows + kCT - 1) / kCT));
     if (fp8 == kE4M3)
         hipLaunchKernelGGL((cast_tile_kernel<IN_F32, kE4M3>), grid, dim3(kThreads), 0, stream, in,
-                           rows, cols, scale, amax, out, out_t, partial);
+                           rows, cols, scale, amax, out, out_t, partial, copy_src, copy_dst);
     else
         hipLaunchKernelGGL((cast_tile_kernel<IN_F32, kE5M2>), grid, dim3(kThreads), 0, stream, in,
-                           rows, cols, scale, amax, out, out_t, partial);
+                           rows, cols, scale, amax, out, out_t, partial, copy_src, copy_dst);
     return hipGetLastError();
 }
 
@@ -212,14 +214,15 @@ size_t cast_workspace(int64_t rows, int64_t cols) {
 
 hipError_t launch_cast_amax(int64_t rows, int64_t cols, bool in_f32, const void* in, int fp8,
                             const float* scale, float* amax, uint8_t* out, uint8_t* out_t,
-                            float* colsum, void* workspace, hipStream_t stream) {
+                            float* colsum, void* workspace, hipStream_t stream,
+                            const float* copy_src, float* copy_dst) {
     if (cols == 0) return hipSuccess;
     float* partial = colsum ? (float*)workspace : nullptr;
     if (rows > 0) {
         hipError_t e = in_f32 ? launch_cast_fmt<true>(rows, cols, in, fp8, scale, amax, out,
-                                                      out_t, partial, stream)
+                                                      out_t, partial, copy_src, copy_dst, stream)
                               : launch_cast_fmt<false>(rows, cols, in, fp8, scale, amax, out,
-                                                       out_t, partial, stream);
+                                                       out_t, partial, copy_src, copy_dst, stream);
         if (e != hipSuccess) return e;
     }
     if (!colsum) return hipSuccess;

@@ -30,9 +30,12 @@ hipError_t launch_ln_bwd(int64_t rows, int hidden, const float* dy, const void* 
 
 // cast.hip
 size_t cast_workspace(int64_t rows, int64_t cols);
+// copy_src / copy_dst: when given, *copy_dst = *copy_src is done by the cast
+// kernel (the scale_inv that goes with the codes it writes).
 hipError_t launch_cast_amax(int64_t rows, int64_t cols, bool in_f32, const void* in, int fp8,
                             const float* scale, float* amax, uint8_t* out, uint8_t* out_t,
-                            float* colsum, void* workspace, hipStream_t stream);
+                            float* colsum, void* workspace, hipStream_t stream,
+                            const float* copy_src = nullptr, float* copy_dst = nullptr);
 // out[j] = sum over r < nrows of partial[r][j] in a fixed order; columns j < split
 // go to out0[j], the others to out1[j - split].
 hipError_t launch_sum_partials(const float* partial, int64_t nrows, int64_t width, float* out0,

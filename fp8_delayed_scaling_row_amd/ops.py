@@ -115,11 +115,16 @@ class LinearCtx:
         self.w_qt = torch.empty((in_features, out_features), **u8) if training else None
         self.mean = torch.empty(tokens, dtype=torch.float32, device=device)
         self.rstd = torch.empty(tokens, dtype=torch.float32, device=device)
+        # scale_inv of the cached weight codes; set reuse_weight_codes to skip the
+        # weight cast while the weight is unchanged (FP8 weight storage)
+        self.w_scale_inv = torch.ones(1, dtype=torch.float32, device=device)
+        self.reuse_weight_codes = False
 
     def as_c(self) -> _abi.LinearCtxStruct:
         p = lambda t: None if t is None else t.data_ptr()
         return _abi.LinearCtxStruct(p(self.ln_q), p(self.ln_qt), p(self.w_q), p(self.w_qt),
-                                    p(self.mean), p(self.rstd))
+                                    p(self.mean), p(self.rstd), p(self.w_scale_inv),
+                                    int(bool(self.reuse_weight_codes)))
 
 
 class MlpCtx:
@@ -138,12 +143,15 @@ class MlpCtx:
         self.h = torch.empty((tokens, ffn), dtype=torch.bfloat16, device=device) if training else None
         self.mean = torch.empty(tokens, dtype=torch.float32, device=device)
         self.rstd = torch.empty(tokens, dtype=torch.float32, device=device)
+        self.w_scale_inv = torch.ones(2, dtype=torch.float32, device=device)   # fc1, fc2
+        self.reuse_weight_codes = False
 
     def as_c(self) -> _abi.MlpCtxStruct:
         p = lambda t: None if t is None else t.data_ptr()
         return _abi.MlpCtxStruct(p(self.ln_q), p(self.ln_qt), p(self.w1_q), p(self.w1_qt),
                                  p(self.w2_q), p(self.w2_qt), p(self.h), p(self.g_q),
-                                 p(self.g_qt), p(self.mean), p(self.rstd))
+                                 p(self.g_qt), p(self.mean), p(self.rstd), p(self.w_scale_inv),
+                                 int(bool(self.reuse_weight_codes)))
 
 
 # ---- library -----------------------------------------------------------------

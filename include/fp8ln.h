@@ -113,7 +113,16 @@ typedef struct {
  *   w_q    uint8 [N][K]  FP8 weight
  *   w_qt   uint8 [K][N]  its transpose; may be NULL for a forward-only call
  *   mean   float [M]     row means
- *   rstd   float [M]     row 1/sqrt(var + eps) */
+ *   rstd   float [M]     row 1/sqrt(var + eps)
+ *   w_scale_inv  float [1]  the scale_inv the w_q codes were made with: every
+ *                forward that casts the weight writes it, and the GEMMs on w_q /
+ *                w_qt dequantise with it.  May be NULL (then the forward meta's
+ *                scale_inv is used, which is the same value in a normal step).
+ *   reuse_weight_codes  FP8 weight storage ([T] "things to try next": FP8 model
+ *                init): 1 = the weight has not changed since a forward of this
+ *                ctx wrote w_q (w_qt) and w_scale_inv, so the weight cast is
+ *                skipped and those codes are used as they are; that step records
+ *                no weight amax.  Needs w_scale_inv.  0 = cast the weight. */
 typedef struct {
     uint8_t* ln_q;
     uint8_t* ln_qt;
@@ -121,6 +130,8 @@ typedef struct {
     uint8_t* w_qt;
     float* mean;
     float* rstd;
+    float* w_scale_inv;
+    int32_t reuse_weight_codes;
 } fp8ln_linear_ctx;
 
 /* What LayerNormMLP's forward saves for its backward (device buffers).
@@ -129,6 +140,9 @@ typedef struct {
  *   w2_qt [F][H], g_q [M][F] (FP8 GELU output), g_qt [F][M]: uint8
  *   h     uint16 (bf16) [M][F]: fc1 output before GELU
  *   mean, rstd float [M]
+ *   w_scale_inv float [2]: scale_inv of the w1 and w2 codes (as for
+ *   fp8ln_linear_ctx); reuse_weight_codes: skip both weight casts (as for
+ *   fp8ln_linear_ctx).
  * The *_qt transposes and h may be NULL for a forward-only call. */
 typedef struct {
     uint8_t* ln_q;
@@ -142,6 +156,8 @@ typedef struct {
     uint8_t* g_qt;
     float* mean;
     float* rstd;
+    float* w_scale_inv;
+    int32_t reuse_weight_codes;
 } fp8ln_mlp_ctx;
 
 /* Workspace kinds for fp8ln_workspace_size. */

@@ -21,8 +21,12 @@ Readings (the pages name the modules and the recipe, not their internals):
 * The GEMM epilogue is acc * scale_inv_a * scale_inv_b + bias; the MLP applies
   GELU (tanh form) to fc1's output in full precision and casts it to FP8 for
   fc2; fc1's output h is kept as bf16 for the backward's GELU derivative.
+* FP8 weight storage ("things to try next": FP8 model init): a forward may
+  reuse the FP8 codes an earlier forward made of the unchanged weight, with the
+  scale_inv they were made with; such a step records no weight amax.
 * Backward: the output gradient is cast to FP8 in the backward format; dgrad
-  multiplies it with the forward's FP8 weight codes, wgrad with the forward's
+  multiplies it with the forward's FP8 weight codes (and their scale_inv),
+  wgrad with the forward's
   FP8 input codes; bias gradients are column sums of the unquantised
   gradient; dx, dgamma, dbeta come from the LayerNorm backward.  Results are
   float64 here; the HIP path returns dx in bf16 and the rest in fp32 ("converts
@@ -109,19 +113,31 @@ def _bias(b_bits, n):
     return np.zeros(n) if b_bits is None else bf16_to_f64(b_bits)
 
 
+def _weight(meta: Meta, slot: int, w_bits, fmt: str, cached):
+    """The weight's FP8 codes and the scale_inv they were made with.  Without a
+    cache the weight is cast with the slot's scale and its amax recorded; with
+    FP8 weight storage (cached = (codes, scale_inv) of an earlier forward on the
+    unchanged weight) the stored codes are used as they are and this step
+    records no weight amax."""
+    if cached is not None:
+        return cached[0], np.float32(cached[1]), None
+    w_q, w_amax = cast_amax(bf16_to_f64(w_bits), meta.scale[slot], fmt)
+    meta.record_amax(slot, w_amax)
+    return w_q, np.float32(meta.scale_inv[slot]), w_amax
+
+
 def ln_linear_fwd(recipe: Recipe, meta: Meta, x_bits, gamma_bits, beta_bits, w_bits,
-                  bias_bits=None):
-    """out = LN(x) W^T + b with FP8 operands.  x [M][K], W [N][K]."""
+                  bias_bits=None, cached_w=None):
+    """out = LN(x) W^T + b with FP8 operands.  x [M][K], W [N][K].  cached_w:
+    (w_q, w_sinv) of an earlier forward to reuse (FP8 weight storage)."""
     fmt = fwd_format(recipe)
     ln = ln_cast_amax(x_bits, gamma_bits, beta_bits, recipe.eps64, meta.scale[0], fmt)
-    w = bf16_to_f64(w_bits)
-    w_q, w_amax = cast_amax(w, meta.scale[1], fmt)
     meta.record_amax(0, ln["amax"])
-    meta.record_amax(1, w_amax)
-    out = fp8_gemm_tn(ln["q"], fmt, w_q, fmt, meta.scale_inv[0], meta.scale_inv[1],
-                      _bias(bias_bits, w.shape[0]))
-    ctx = dict(ln_q=ln["q"], w_q=w_q, mean=ln["mean"], rstd=ln["rstd"], y=ln["y"],
-               ln_amax=ln["amax"], w_amax=w_amax)
+    w_q, w_sinv, w_amax = _weight(meta, 1, w_bits, fmt, cached_w)
+    out = fp8_gemm_tn(ln["q"], fmt, w_q, fmt, meta.scale_inv[0], w_sinv,
+                      _bias(bias_bits, w_q.shape[0]))
+    ctx = dict(ln_q=ln["q"], w_q=w_q, w_sinv=w_sinv, mean=ln["mean"], rstd=ln["rstd"],
+               y=ln["y"], ln_amax=ln["amax"], w_amax=w_amax)
     return out, ctx
 
 
@@ -134,8 +150,7 @@ def ln_linear_bwd(recipe: Recipe, meta_fwd: Meta, meta_bwd: Meta, dy_bits, ctx, 
     meta_bwd.record_amax(0, dy_amax)
     dbias = dy.sum(axis=0)
     # dgrad: dLN[m][k] = sum_n dy[m][n] W[n][k]
-    dln = fp8_gemm_tn(dy_q, bfmt, ctx["w_q"].T, ffmt, meta_bwd.scale_inv[0],
-                      meta_fwd.scale_inv[1])
+    dln = fp8_gemm_tn(dy_q, bfmt, ctx["w_q"].T, ffmt, meta_bwd.scale_inv[0], ctx["w_sinv"])
     # wgrad: dW[n][k] = sum_m dy[m][n] LN(x)[m][k]
     dw = fp8_gemm_tn(dy_q.T, bfmt, ctx["ln_q"].T, ffmt, meta_bwd.scale_inv[0],
                      meta_fwd.scale_inv[0])
@@ -146,27 +161,25 @@ def ln_linear_bwd(recipe: Recipe, meta_fwd: Meta, meta_bwd: Meta, dy_bits, ctx, 
 
 
 def ln_mlp_fwd(recipe: Recipe, meta: Meta, x_bits, gamma_bits, beta_bits, w1_bits, b1_bits,
-               w2_bits, b2_bits):
-    """out = fc2(GELU(fc1(LN(x)))) with FP8 operands.  W1 [F][H], W2 [H][F]."""
+               w2_bits, b2_bits, cached_w=None):
+    """out = fc2(GELU(fc1(LN(x)))) with FP8 operands.  W1 [F][H], W2 [H][F].
+    cached_w: ((w1_q, w1_sinv), (w2_q, w2_sinv)) of an earlier forward to reuse."""
     fmt = fwd_format(recipe)
     ln = ln_cast_amax(x_bits, gamma_bits, beta_bits, recipe.eps64, meta.scale[0], fmt)
-    w1 = bf16_to_f64(w1_bits)
-    w2 = bf16_to_f64(w2_bits)
-    w1_q, w1_amax = cast_amax(w1, meta.scale[1], fmt)
-    w2_q, w2_amax = cast_amax(w2, meta.scale[3], fmt)
     meta.record_amax(0, ln["amax"])
-    meta.record_amax(1, w1_amax)
-    meta.record_amax(3, w2_amax)
-    h = fp8_gemm_tn(ln["q"], fmt, w1_q, fmt, meta.scale_inv[0], meta.scale_inv[1],
-                    _bias(b1_bits, w1.shape[0]))
+    c1, c2 = (None, None) if cached_w is None else cached_w
+    w1_q, w1_sinv, w1_amax = _weight(meta, 1, w1_bits, fmt, c1)
+    w2_q, w2_sinv, w2_amax = _weight(meta, 3, w2_bits, fmt, c2)
+    h = fp8_gemm_tn(ln["q"], fmt, w1_q, fmt, meta.scale_inv[0], w1_sinv,
+                    _bias(b1_bits, w1_q.shape[0]))
     g = gelu_tanh(h)
     g_q, g_amax = cast_amax(g, meta.scale[2], fmt)
     meta.record_amax(2, g_amax)
-    out = fp8_gemm_tn(g_q, fmt, w2_q, fmt, meta.scale_inv[2], meta.scale_inv[3],
-                      _bias(b2_bits, w2.shape[0]))
-    ctx = dict(ln_q=ln["q"], w1_q=w1_q, w2_q=w2_q, h=h, h_bits=f64_to_bf16_bits(h), g=g,
-               g_q=g_q, mean=ln["mean"], rstd=ln["rstd"], y=ln["y"], ln_amax=ln["amax"],
-               w1_amax=w1_amax, w2_amax=w2_amax, g_amax=g_amax)
+    out = fp8_gemm_tn(g_q, fmt, w2_q, fmt, meta.scale_inv[2], w2_sinv,
+                      _bias(b2_bits, w2_q.shape[0]))
+    ctx = dict(ln_q=ln["q"], w1_q=w1_q, w2_q=w2_q, w1_sinv=w1_sinv, w2_sinv=w2_sinv, h=h,
+               h_bits=f64_to_bf16_bits(h), g=g, g_q=g_q, mean=ln["mean"], rstd=ln["rstd"],
+               y=ln["y"], ln_amax=ln["amax"], w1_amax=w1_amax, w2_amax=w2_amax, g_amax=g_amax)
     return out, ctx
 
 
@@ -179,16 +192,14 @@ def ln_mlp_bwd(recipe: Recipe, meta_fwd: Meta, meta_bwd: Meta, dy_bits, ctx, x_b
     meta_bwd.record_amax(0, dy_amax)
     db2 = dy.sum(axis=0)
     # fc2 dgrad, then the GELU derivative at the saved bf16 h
-    dg = fp8_gemm_tn(dy_q, bfmt, ctx["w2_q"].T, ffmt, meta_bwd.scale_inv[0],
-                     meta_fwd.scale_inv[3])
+    dg = fp8_gemm_tn(dy_q, bfmt, ctx["w2_q"].T, ffmt, meta_bwd.scale_inv[0], ctx["w2_sinv"])
     dh = dg * gelu_tanh_grad(bf16_to_f64(ctx["h_bits"]))
     dh_q, dh_amax = cast_amax(dh, meta_bwd.scale[1], bfmt)
     meta_bwd.record_amax(1, dh_amax)
     db1 = dh.sum(axis=0)
     dw2 = fp8_gemm_tn(dy_q.T, bfmt, ctx["g_q"].T, ffmt, meta_bwd.scale_inv[0],
                       meta_fwd.scale_inv[2])
-    dln = fp8_gemm_tn(dh_q, bfmt, ctx["w1_q"].T, ffmt, meta_bwd.scale_inv[1],
-                      meta_fwd.scale_inv[1])
+    dln = fp8_gemm_tn(dh_q, bfmt, ctx["w1_q"].T, ffmt, meta_bwd.scale_inv[1], ctx["w1_sinv"])
     dw1 = fp8_gemm_tn(dh_q.T, bfmt, ctx["ln_q"].T, ffmt, meta_bwd.scale_inv[1],
                       meta_fwd.scale_inv[0])
     dx, dgamma, dbeta = layernorm_bwd(dln, bf16_to_f64(x_bits), bf16_to_f64(gamma_bits),

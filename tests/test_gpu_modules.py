@@ -61,7 +61,10 @@ def scale_slack(gpu_meta, om, slot, exact):
 
 # ---- LayerNormLinear -----------------------------------------------------------
 
-def run_linear(recipe, M, K, N, steps, workload, backward, check_every=1):
+def run_linear(recipe, M, K, N, steps, workload, backward, check_every=1, reuse_from=None):
+    """reuse_from: from this step on the forward reuses the FP8 weight codes of the
+    last step that cast the weight (FP8 weight storage), on the GPU and in the
+    oracle alike."""
     dev = "cuda"
     g, b = inputs.layernorm_params(K, workload)
     w = inputs.linear_weight(N, K, workload, "weight")
@@ -79,14 +82,20 @@ def run_linear(recipe, M, K, N, steps, workload, backward, check_every=1):
     omf, omb = oracle.linear_fwd_meta(orc), oracle.linear_bwd_meta(orc)
     ffmt, bfmt = oracle.fwd_format(orc), oracle.bwd_format(orc)
     gbits, bbits, wbits, biasbits = map(to_np_bits, (g, b, w, bias))
+    cached = None
     for step in range(steps):
+        reuse = reuse_from is not None and step >= reuse_from
+        ctx.reuse_weight_codes = reuse
         x = inputs.normal_bf16((M, K), inputs.seed_for(workload, "x", step))
         xd = x.to(dev)
         ops.scaling_update(recipe, mf)
         ops.ln_linear_fwd(recipe, xd, gd, bd, wd, biasd, out, mf, ctx)
         oracle.scaling_update(omf, orc.margin)
         xbits = to_np_bits(x)
-        oout, octx = oracle.ln_linear_fwd(orc, omf, xbits, gbits, bbits, wbits, biasbits)
+        oout, octx = oracle.ln_linear_fwd(orc, omf, xbits, gbits, bbits, wbits, biasbits,
+                                          cached_w=cached if reuse else None)
+        if not reuse:
+            cached = (octx["w_q"], octx["w_sinv"])
         if backward:
             dy = inputs.normal_bf16((M, N), inputs.seed_for(workload, "dy", step), std=1e-3)
             ops.scaling_update(recipe, mb)
@@ -104,8 +113,12 @@ def run_linear(recipe, M, K, N, steps, workload, backward, check_every=1):
         exact = octx["y"] * s0
         compare_codes(ctx.ln_q.cpu().numpy(), exact, ffmt,
                       ln_window(gx, beta, s0, exact) + scale_slack(mf, omf, 0, exact))
-        wex = oracle.bf16_to_f64(wbits) * float(omf.scale[1])
-        compare_codes(ctx.w_q.cpu().numpy(), wex, ffmt, 0.0)
+        if reuse:
+            np.testing.assert_array_equal(ctx.w_q.cpu().numpy(), octx["w_q"])
+        else:
+            wex = oracle.bf16_to_f64(wbits) * float(omf.scale[1])
+            compare_codes(ctx.w_q.cpu().numpy(), wex, ffmt, 0.0)
+        assert ctx.w_scale_inv.item() == float(octx["w_sinv"])
         if backward:
             assert torch.equal(ctx.ln_qt, ctx.ln_q.t().contiguous())
             assert torch.equal(ctx.w_qt, ctx.w_q.t().contiguous())
@@ -138,6 +151,15 @@ def test_ln_linear_small_and_ragged(M, K, N):
                backward=True)
 
 
+def test_ln_linear_fp8_weight_storage():
+    """Steps 2.. reuse the weight codes cast at step 1: the forward skips the
+    weight cast, the GEMMs use the stored scale_inv, the weight slot records no
+    amax (its history rows stay zero, as in the oracle), and every output still
+    matches the oracle run in the same mode."""
+    run_linear(ops.Recipe(format=ops.FORMAT_HYBRID, amax_history_len=4), 256, 768, 2304, 6,
+               "lin/fp8-weights", backward=True, reuse_from=2)
+
+
 def test_ln_linear_fwd_ragged_tokens_forward_only():
     run_linear(ops.Recipe(), 37, 768, 2304, 2, "lin-ragged", backward=False)
 
@@ -162,7 +184,7 @@ def gelu_code_window(ln_q, w1_q, fmt, alpha, h, scale, K):
     return float(scale) * dg
 
 
-def run_mlp(recipe, M, H, F, steps, workload, backward, sample_rows=None):
+def run_mlp(recipe, M, H, F, steps, workload, backward, sample_rows=None, reuse_from=None):
     dev = "cuda"
     g, b = inputs.layernorm_params(H, workload)
     w1 = inputs.linear_weight(F, H, workload, "w1")
@@ -185,14 +207,19 @@ def run_mlp(recipe, M, H, F, steps, workload, backward, sample_rows=None):
     ffmt = oracle.fwd_format(orc)
     gbits, bbits, w1bits, w2bits, b1bits, b2bits = map(to_np_bits, (g, b, w1, w2, b1, b2))
     rows = slice(None) if sample_rows is None else sample_rows
+    cached = None
     for step in range(steps):
+        reuse = reuse_from is not None and step >= reuse_from
+        ctx.reuse_weight_codes = reuse
         x = inputs.normal_bf16((M, H), inputs.seed_for(workload, "x", step), device=dev)
         ops.scaling_update(recipe, mf)
         ops.ln_mlp_fwd(recipe, x, gd, bd, w1d, b1d, w2d, b2d, out, mf, ctx)
         xbits = to_np_bits(x)
         oracle.scaling_update(omf, orc.margin)
         oout, octx = oracle.ln_mlp_fwd(orc, omf, xbits, gbits, bbits, w1bits, b1bits, w2bits,
-                                       b2bits)
+                                       b2bits, cached_w=cached if reuse else None)
+        if not reuse:
+            cached = ((octx["w1_q"], octx["w1_sinv"]), (octx["w2_q"], octx["w2_sinv"]))
         if backward:
             dy = inputs.normal_bf16((M, H), inputs.seed_for(workload, "dy", step), std=1e-3,
                                     device=dev)
@@ -211,7 +238,12 @@ def run_mlp(recipe, M, H, F, steps, workload, backward, sample_rows=None):
         exact = octx["y"][rows] * s0
         compare_codes(ctx.ln_q.cpu().numpy()[rows], exact, ffmt,
                       ln_window(gx, beta, s0, exact) + scale_slack(mf, omf, 0, exact))
-        alpha = np.float32(omf.scale_inv[0]) * np.float32(omf.scale_inv[1])
+        alpha = np.float32(omf.scale_inv[0]) * np.float32(octx["w1_sinv"])
+        np.testing.assert_array_equal(ctx.w_scale_inv.cpu().numpy(),
+                                      np.array([octx["w1_sinv"], octx["w2_sinv"]], np.float32))
+        if reuse:
+            np.testing.assert_array_equal(ctx.w1_q.cpu().numpy(), octx["w1_q"])
+            np.testing.assert_array_equal(ctx.w2_q.cpu().numpy(), octx["w2_q"])
         s2 = float(omf.scale[2])
         gq = ctx.g_q.cpu().numpy()[rows]
         win = gelu_code_window(octx["ln_q"][rows], octx["w1_q"], ffmt, alpha, octx["h"][rows],
@@ -257,6 +289,13 @@ def test_ln_mlp_fwd_bwd_small(fmt):
 
 def test_ln_mlp_ragged_tiles():
     run_mlp(ops.Recipe(), 48, 80, 144, 3, "mlp-ragged", backward=True)
+
+
+def test_ln_mlp_fp8_weight_storage():
+    """Both weights' codes cast at step 1 are reused from step 2 on (forward and
+    backward), matching the oracle run in the same mode."""
+    run_mlp(ops.Recipe(format=ops.FORMAT_HYBRID, amax_history_len=4), 256, 256, 1024, 5,
+            "mlp/fp8-weights", backward=True, reuse_from=2)
 
 
 @pytest.mark.parametrize("fmt", [ops.FORMAT_HYBRID, ops.FORMAT_E4M3])

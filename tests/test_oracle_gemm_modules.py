@@ -183,3 +183,52 @@ def test_ln_mlp_chain_tracks_unquantised_autograd():
     assert np.linalg.norm(grads["db1"] - b1t.grad.numpy()) / np.linalg.norm(b1t.grad.numpy()) < 0.1
     np.testing.assert_allclose(grads["db2"], b2t.grad.numpy(), rtol=1e-12)
     assert mf.history[0, 2] == np.float32(np.abs(ctx["g"]).max())
+
+
+# ---- FP8 weight storage (reuse of an earlier forward's weight codes) -----------
+
+def _lin_inputs(M=32, K=48, N=64, seed=7):
+    from fp8_delayed_scaling_row_amd import inputs
+    rng_bits = lambda t: t.view(np.uint16) if isinstance(t, np.ndarray) else \
+        t.view(__import__("torch").int16).numpy().view(np.uint16)
+    x = rng_bits(inputs.normal_bf16((M, K), seed))
+    g, b = (rng_bits(t) for t in inputs.layernorm_params(K, "reuse-pin"))
+    w = rng_bits(inputs.linear_weight(N, K, "reuse-pin", "w"))
+    return x, g, b, w
+
+
+def test_weight_reuse_equals_the_cast_it_reuses():
+    """Reusing the codes and scale_inv of a forward on the same weight gives that
+    forward's output exactly, and leaves the weight slot's amax unrecorded."""
+    import copy
+    x, g, b, w = _lin_inputs()
+    recipe = oracle.Recipe(format=oracle.FORMAT_HYBRID, amax_history_len=4)
+    meta = oracle.linear_fwd_meta(recipe)
+    oracle.scaling_update(meta, 0)
+    m_cast, m_reuse = copy.deepcopy(meta), copy.deepcopy(meta)
+    out1, ctx1 = oracle.ln_linear_fwd(recipe, m_cast, x, g, b, w)
+    out2, ctx2 = oracle.ln_linear_fwd(recipe, m_reuse, x, g, b, w,
+                                      cached_w=(ctx1["w_q"], ctx1["w_sinv"]))
+    np.testing.assert_array_equal(out1, out2)
+    assert m_cast.history[0, 1] == ctx1["w_amax"] > 0
+    assert m_reuse.history[0, 1] == 0.0 and ctx2["w_amax"] is None
+    assert m_reuse.history[0, 0] == m_cast.history[0, 0]
+
+
+def test_weight_reuse_keeps_the_stored_scale():
+    """After the weight slot's scale moves, a reusing forward still dequantises
+    with the scale_inv stored with the codes: its output equals the GEMM of the
+    stored codes with that scale_inv, and differs from a fresh cast's GEMM."""
+    x, g, b, w = _lin_inputs()
+    recipe = oracle.Recipe(format=oracle.FORMAT_HYBRID, amax_history_len=4)
+    meta = oracle.linear_fwd_meta(recipe)
+    oracle.scaling_update(meta, 0)
+    _, ctx1 = oracle.ln_linear_fwd(recipe, meta, x, g, b, w)     # scale 1: codes of w * 1
+    oracle.scaling_update(meta, 0)                                 # now scale = 448 / amax(w)
+    assert meta.scale[1] != 1.0
+    out, ctx = oracle.ln_linear_fwd(recipe, meta, x, g, b, w,
+                                    cached_w=(ctx1["w_q"], ctx1["w_sinv"]))
+    want = oracle.fp8_gemm_tn(ctx["ln_q"], oracle.E4M3, ctx1["w_q"], oracle.E4M3,
+                              meta.scale_inv[0], np.float32(1.0))
+    np.testing.assert_array_equal(out, want)
+    assert ctx["w_sinv"] == np.float32(1.0)
