@@ -25,6 +25,9 @@ E5M2 = 1
 DTYPE_BF16 = 0
 DTYPE_F32 = 1
 
+GELU_TANH = 0
+GELU_ERF = 1
+
 META_FORWARD = 0
 META_BACKWARD = 1
 
@@ -37,7 +40,7 @@ OP_GEMM_DGELU_FP8 = 4
 
 class Recipe(C.Structure):
     _fields_ = [("format", C.c_int32), ("amax_history_len", C.c_int32),
-                ("margin", C.c_int32), ("ln_eps", C.c_float)]
+                ("margin", C.c_int32), ("ln_eps", C.c_float), ("activation", C.c_int32)]
 
 
 class MetaStruct(C.Structure):
@@ -80,10 +83,11 @@ SIGNATURES = {
     "fp8ln_encode_range": (C.c_int, [C.c_uint32, _I64, _I32, _P, _P]),
     "fp8ln_gemm": (C.c_int, [_I64, _I64, _I64, _P, _I32, _P, _I32, _P, _P, _P, _I32, _P, _P]),
     "fp8ln_gemm_gelu_fp8": (C.c_int, [_I64, _I64, _I64, _P, _I32, _P, _I32, _P, _P, _P, _P, _P,
-                                      _P, _I32, _P, _P, _P]),
-    "fp8ln_gemm_dgelu": (C.c_int, [_I64, _I64, _I64, _P, _I32, _P, _I32, _P, _P, _P, _P, _P]),
+                                      _P, _I32, _P, _P, _I32, _P]),
+    "fp8ln_gemm_dgelu": (C.c_int, [_I64, _I64, _I64, _P, _I32, _P, _I32, _P, _P, _P, _P, _I32,
+                                   _P]),
     "fp8ln_gemm_dgelu_fp8": (C.c_int, [_I64, _I64, _I64, _P, _I32, _P, _I32, _P, _P, _P, _I32, _P,
-                                       _P, _P, _P, _P, _P, _SZ, _P]),
+                                       _P, _P, _P, _P, _I32, _P, _SZ, _P]),
     "fp8ln_layernorm_bwd": (C.c_int, [_I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "fp8ln_ln_linear_fwd": (C.c_int, [_RP, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _MP,
                                       C.POINTER(LinearCtxStruct), _P]),

@@ -88,6 +88,9 @@ int check_recipe(const fp8ln_recipe* r) {
         return fail(FP8LN_ERR_INVALID_ARG, "recipe.margin %d outside 0..64", r->margin);
     if (!(std::isfinite(r->ln_eps) && r->ln_eps > 0.0f))
         return fail(FP8LN_ERR_INVALID_ARG, "recipe.ln_eps must be finite and > 0");
+    if (r->activation != FP8LN_GELU_TANH && r->activation != FP8LN_GELU_ERF)
+        return fail(FP8LN_ERR_INVALID_ARG, "recipe.activation %d is not GELU_TANH/GELU_ERF",
+                    r->activation);
     return FP8LN_OK;
 }
 
@@ -377,7 +380,9 @@ int fp8ln_gemm_gelu_fp8(int64_t M, int64_t N, int64_t K, const uint8_t* A, int32
                         const uint8_t* B, int32_t b_dtype, const float* sinv_a,
                         const float* sinv_b, const void* bias, void* h_out, uint8_t* q_out,
                         uint8_t* q_out_t, int32_t q_dtype, const float* q_scale, float* q_amax,
-                        void* stream) {
+                        int32_t activation, void* stream) {
+    REQUIRE(activation == FP8LN_GELU_TANH || activation == FP8LN_GELU_ERF,
+            "activation %d invalid", activation);
     REQUIRE(M >= 0 && N >= 0 && K >= 0, "negative size");
     REQUIRE(a_dtype == FP8LN_E4M3 || a_dtype == FP8LN_E5M2, "a_dtype %d invalid", a_dtype);
     REQUIRE(b_dtype == FP8LN_E4M3 || b_dtype == FP8LN_E5M2, "b_dtype %d invalid", b_dtype);
@@ -405,13 +410,16 @@ int fp8ln_gemm_gelu_fp8(int64_t M, int64_t N, int64_t K, const uint8_t* A, int32
     p.q_scale = q_scale;
     p.q_amax = q_amax;
     p.q_fp8 = q_dtype;
+    p.gelu_erf = activation == FP8LN_GELU_ERF;
     FP8LN_TRY(launch_gemm(p, as_stream(stream)), "gemm_gelu launch");
     return FP8LN_OK;
 }
 
 int fp8ln_gemm_dgelu(int64_t M, int64_t N, int64_t K, const uint8_t* A, int32_t a_dtype,
                      const uint8_t* B, int32_t b_dtype, const float* sinv_a, const float* sinv_b,
-                     const void* h, float* out, void* stream) {
+                     const void* h, float* out, int32_t activation, void* stream) {
+    REQUIRE(activation == FP8LN_GELU_TANH || activation == FP8LN_GELU_ERF,
+            "activation %d invalid", activation);
     REQUIRE(M >= 0 && N >= 0 && K >= 0, "negative size");
     REQUIRE(a_dtype == FP8LN_E4M3 || a_dtype == FP8LN_E5M2, "a_dtype %d invalid", a_dtype);
     REQUIRE(b_dtype == FP8LN_E4M3 || b_dtype == FP8LN_E5M2, "b_dtype %d invalid", b_dtype);
@@ -428,6 +436,7 @@ int fp8ln_gemm_dgelu(int64_t M, int64_t N, int64_t K, const uint8_t* A, int32_t 
     GemmParams p = gemm_params(M, N, K, A, a_dtype, B, b_dtype, sinv_a, sinv_b, kEpiDGeluF32);
     p.h_in = (const uint16_t*)h;
     p.out = out;
+    p.gelu_erf = activation == FP8LN_GELU_ERF;
     FP8LN_TRY(launch_gemm(p, as_stream(stream)), "gemm_dgelu launch");
     return FP8LN_OK;
 }
@@ -436,8 +445,11 @@ int fp8ln_gemm_dgelu_fp8(int64_t M, int64_t N, int64_t K, const uint8_t* A, int3
                          const uint8_t* B, int32_t b_dtype, const float* sinv_a,
                          const float* sinv_b, const void* h, int32_t q_dtype,
                          const float* q_scale, float* q_amax, uint8_t* q_out, uint8_t* q_out_t,
-                         float* dbias, void* workspace, size_t workspace_bytes, void* stream) {
+                         float* dbias, int32_t activation, void* workspace,
+                         size_t workspace_bytes, void* stream) {
     REQUIRE(M >= 0 && N >= 0 && K >= 0, "negative size");
+    REQUIRE(activation == FP8LN_GELU_TANH || activation == FP8LN_GELU_ERF,
+            "activation %d invalid", activation);
     REQUIRE(a_dtype == FP8LN_E4M3 || a_dtype == FP8LN_E5M2, "a_dtype %d invalid", a_dtype);
     REQUIRE(b_dtype == FP8LN_E4M3 || b_dtype == FP8LN_E5M2, "b_dtype %d invalid", b_dtype);
     REQUIRE(q_dtype == FP8LN_E4M3 || q_dtype == FP8LN_E5M2, "q_dtype %d invalid", q_dtype);
@@ -468,6 +480,7 @@ int fp8ln_gemm_dgelu_fp8(int64_t M, int64_t N, int64_t K, const uint8_t* A, int3
     p.q_amax = q_amax;
     p.q_fp8 = q_dtype;
     p.col_partial = dbias ? (float*)workspace : nullptr;
+    p.gelu_erf = activation == FP8LN_GELU_ERF;
     FP8LN_TRY(launch_gemm(p, st), "gemm_dgelu_fp8 launch");
     if (dbias)
         FP8LN_TRY(launch_sum_partials((const float*)workspace, M > 0 ? gemm_partial_rows(M, N, K) : 0,
@@ -697,6 +710,7 @@ int fp8ln_ln_mlp_fwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t hidden,
     p1.q_scale = fwd->scale + 2;
     p1.q_amax = hist + 2;
     p1.q_fp8 = f;
+    p1.gelu_erf = recipe->activation == FP8LN_GELU_ERF;
     FP8LN_TRY(launch_gemm(p1, st), "fc1 launch");
     GemmParams p2 = gemm_params(M, H, F, ctx->g_q, f, ctx->w2_q, f, fwd->scale_inv + 2, w2_sinv,
                                 kEpiBf16Bias);
@@ -763,6 +777,7 @@ int fp8ln_ln_mlp_bwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t hidden,
     dg2.q_amax = bwd->amax_history + 1;
     dg2.q_fp8 = bf;
     dg2.col_partial = db1 ? w.dh_part : nullptr;
+    dg2.gelu_erf = recipe->activation == FP8LN_GELU_ERF;
     FP8LN_TRY(launch_gemm(dg2, st), "fc2 dgrad launch");
     if (db1)
         FP8LN_TRY(launch_sum_partials(w.dh_part, M > 0 ? gemm_partial_rows(M, F, H) : 0, F, db1,

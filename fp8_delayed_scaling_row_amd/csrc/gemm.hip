@@ -71,6 +71,19 @@ __device__ __forceinline__ float gelu_f(float h) {
     return fmaf(hh, t, hh);
 }
 
+// GELU, erf form: gelu(h) = h/2 (1 + erf(h / sqrt 2)),
+// gelu'(h) = (1 + erf(h / sqrt 2)) / 2 + h exp(-h^2 / 2) / sqrt(2 pi).
+__device__ __forceinline__ float gelu_erf_f(float h) {
+    const float hh = 0.5f * h;
+    return fmaf(hh, erff(h * 0.70710678118654752f), hh);
+}
+
+__device__ __forceinline__ float gelu_erf_grad_f(float h) {
+    const float e = erff(h * 0.70710678118654752f);
+    const float d = __expf(-0.5f * h * h) * 0.39894228040143268f;   // 1 / sqrt(2 pi)
+    return fmaf(h, d, fmaf(0.5f, e, 0.5f));
+}
+
 __device__ __forceinline__ float gelu_grad_f(float h) {
     const float h2 = h * h;
     const float t = gelu_tanh_t(h, h2);
@@ -382,9 +395,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p) {
                     const bool ok = m0 + lr < M && n0 + lc < N;
                     const float hv[4] = {bf16_lo(hw.x), bf16_hi(hw.x), bf16_lo(hw.y), bf16_hi(hw.y)};
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        acc[j][i][4 * q + e] =
-                            ok ? acc[j][i][4 * q + e] * alpha * gelu_grad_f(hv[e]) : 0.0f;
+                    for (int e = 0; e < 4; ++e) {
+                        const float gp = p.gelu_erf ? gelu_erf_grad_f(hv[e]) : gelu_grad_f(hv[e]);
+                        acc[j][i][4 * q + e] = ok ? acc[j][i][4 * q + e] * alpha * gp : 0.0f;
+                    }
                 }
         __syncthreads();   // h is consumed: the ring takes the codes next
     } else {
@@ -429,10 +443,12 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p) {
                     const int64_t gn = n0 + col_w + 32 * j + 8 * q;
                     if (gm < M && gn < N) {
                         const uint2 hw = *reinterpret_cast<const uint2*>(p.h_in + gm * N + gn);
-                        acc[j][i][4 * q + 0] *= gelu_grad_f(bf16_lo(hw.x));
-                        acc[j][i][4 * q + 1] *= gelu_grad_f(bf16_hi(hw.x));
-                        acc[j][i][4 * q + 2] *= gelu_grad_f(bf16_lo(hw.y));
-                        acc[j][i][4 * q + 3] *= gelu_grad_f(bf16_hi(hw.y));
+                        const float hv[4] = {bf16_lo(hw.x), bf16_hi(hw.x), bf16_lo(hw.y),
+                                             bf16_hi(hw.y)};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            acc[j][i][4 * q + e] *= p.gelu_erf ? gelu_erf_grad_f(hv[e])
+                                                               : gelu_grad_f(hv[e]);
                     }
                 }
     }
@@ -515,7 +531,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p) {
                     for (int e = 0; e < 4; ++e) {
                         float g;
                         if constexpr (EPI == kEpiGeluFp8) {
-                            g = gelu_f(acc[j][i][4 * q + e]);
+                            g = p.gelu_erf ? gelu_erf_f(acc[j][i][4 * q + e])
+                                           : gelu_f(acc[j][i][4 * q + e]);
                             gs[e] = g * qs;
                         } else {
                             g = acc[j][i][4 * q + e];

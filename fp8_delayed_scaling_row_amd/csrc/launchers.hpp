@@ -73,6 +73,7 @@ struct GemmParams {
     // kEpiDGeluF32, kEpiDGeluFp8 (which also uses q_out, q_out_t, q_scale, q_amax, q_fp8)
     const uint16_t* h_in;   // bf16 [M][N]
     float* col_partial;     // kEpiDGeluFp8: [ceil(M / tile rows)][N] column sums, or null
+    int gelu_erf;           // GELU epilogues: 0 = tanh form, 1 = erf form
     int epilogue;
 };
 

@@ -13,12 +13,13 @@ import torch
 
 from . import _abi
 from ._abi import (DTYPE_BF16, DTYPE_F32, E4M3, E5M2, FORMAT_E4M3, FORMAT_E5M2, FORMAT_HYBRID,
+                   GELU_ERF, GELU_TANH,
                    META_BACKWARD, META_FORWARD, OP_CAST_AMAX, OP_LAYERNORM_BWD, OP_LN_LINEAR_BWD,
                    OP_LN_MLP_BWD, OP_GEMM_DGELU_FP8, Fp8lnError, check, lib)
 
 __all__ = [
     "Recipe", "Meta", "LinearCtx", "MlpCtx", "Fp8lnError", "FORMAT_E4M3", "FORMAT_HYBRID",
-    "FORMAT_E5M2", "E4M3", "E5M2", "META_FORWARD", "META_BACKWARD", "OP_CAST_AMAX",
+    "FORMAT_E5M2", "GELU_TANH", "GELU_ERF", "E4M3", "E5M2", "META_FORWARD", "META_BACKWARD", "OP_CAST_AMAX",
     "OP_LAYERNORM_BWD", "OP_LN_LINEAR_BWD", "OP_LN_MLP_BWD", "OP_GEMM_DGELU_FP8", "check_support", "workspace_size", "meta_init",
     "scaling_update", "ln_cast_amax", "cast_amax", "encode_range", "gemm", "gemm_gelu_fp8",
     "gemm_dgelu", "gemm_dgelu_fp8", "layernorm_bwd",
@@ -58,14 +59,17 @@ def _opt(t, dtype, shape, name):
 
 @dataclass
 class Recipe:
-    """DelayedScaling recipe: format, amax_history_len, margin, LayerNorm eps."""
+    """DelayedScaling recipe: format, amax_history_len, margin, LayerNorm eps, and
+    the LayerNormMLP activation (GELU_TANH or GELU_ERF)."""
     format: int = FORMAT_HYBRID
     amax_history_len: int = 16
     margin: int = 0
     ln_eps: float = 1e-5
+    activation: int = 0
 
     def as_c(self) -> _abi.Recipe:
-        return _abi.Recipe(self.format, self.amax_history_len, self.margin, self.ln_eps)
+        return _abi.Recipe(self.format, self.amax_history_len, self.margin, self.ln_eps,
+                           self.activation)
 
 
 def fwd_fp8(recipe: Recipe) -> int:
@@ -246,7 +250,8 @@ def gemm(a, a_dtype: int, b, b_dtype: int, sinv_a, sinv_b, out, bias=None, strea
 
 
 def gemm_gelu_fp8(a, a_dtype: int, b, b_dtype: int, sinv_a, sinv_b, q_dtype: int, q_scale,
-                  q_amax_ptr: int, q_out, q_out_t=None, h_out=None, bias=None, stream=None):
+                  q_amax_ptr: int, q_out, q_out_t=None, h_out=None, bias=None,
+                  activation: int = GELU_TANH, stream=None):
     """fc1 with the GELU epilogue: h = a.b^T * sinv_a * sinv_b + bias (fp32), h_out =
     bf16(h), q_out = encode(gelu(h) * q_scale), amax of gelu(h) at q_amax_ptr."""
     M, K = a.shape
@@ -260,10 +265,11 @@ def gemm_gelu_fp8(a, a_dtype: int, b, b_dtype: int, sinv_a, sinv_b, q_dtype: int
     check(lib().fp8ln_gemm_gelu_fp8(M, N, K, _ptr(a), a_dtype, _ptr(b), b_dtype, _ptr(sinv_a),
                                     _ptr(sinv_b), _ptr(bias), _ptr(h_out), _ptr(q_out),
                                     _ptr(q_out_t), q_dtype, _ptr(q_scale),
-                                    C.c_void_p(q_amax_ptr), _stream(stream)))
+                                    C.c_void_p(q_amax_ptr), activation, _stream(stream)))
 
 
-def gemm_dgelu(a, a_dtype: int, b, b_dtype: int, sinv_a, sinv_b, h, out, stream=None):
+def gemm_dgelu(a, a_dtype: int, b, b_dtype: int, sinv_a, sinv_b, h, out,
+               activation: int = GELU_TANH, stream=None):
     """out = a.b^T * sinv_a * sinv_b * gelu'(h) (fp32)."""
     M, K = a.shape
     N = b.shape[0]
@@ -272,11 +278,12 @@ def gemm_dgelu(a, a_dtype: int, b, b_dtype: int, sinv_a, sinv_b, h, out, stream=
     _need(h, torch.bfloat16, (M, N), "h")
     _need(out, torch.float32, (M, N), "out")
     check(lib().fp8ln_gemm_dgelu(M, N, K, _ptr(a), a_dtype, _ptr(b), b_dtype, _ptr(sinv_a),
-                                 _ptr(sinv_b), _ptr(h), _ptr(out), _stream(stream)))
+                                 _ptr(sinv_b), _ptr(h), _ptr(out), activation, _stream(stream)))
 
 
 def gemm_dgelu_fp8(a, a_dtype: int, b, b_dtype: int, sinv_a, sinv_b, h, q_dtype: int, q_scale,
-                   q_amax_ptr: int, q_out, q_out_t=None, dbias=None, stream=None):
+                   q_amax_ptr: int, q_out, q_out_t=None, dbias=None, activation: int = GELU_TANH,
+                   stream=None):
     """d = a.b^T * sinv_a * sinv_b * gelu'(h) (fp32, not stored); q_out = encode(d *
     q_scale), q_out_t its transpose, amax of d at q_amax_ptr, dbias = column sums of d."""
     M, K = a.shape
@@ -292,7 +299,7 @@ def gemm_dgelu_fp8(a, a_dtype: int, b, b_dtype: int, sinv_a, sinv_b, h, q_dtype:
     check(lib().fp8ln_gemm_dgelu_fp8(M, N, K, _ptr(a), a_dtype, _ptr(b), b_dtype, _ptr(sinv_a),
                                      _ptr(sinv_b), _ptr(h), q_dtype, _ptr(q_scale),
                                      C.c_void_p(q_amax_ptr), _ptr(q_out), _ptr(q_out_t),
-                                     _ptr(dbias), _ptr(ws), nbytes, _stream(stream)))
+                                     _ptr(dbias), activation, _ptr(ws), nbytes, _stream(stream)))
 
 
 def layernorm_bwd(dy, x, mean, rstd, gamma, dx, dgamma, dbeta, stream=None) -> None:

@@ -77,16 +77,24 @@ typedef enum { FP8LN_DTYPE_BF16 = 0, FP8LN_DTYPE_F32 = 1 } fp8ln_dtype;
  * backward counterpart). */
 typedef enum { FP8LN_META_FORWARD = 0, FP8LN_META_BACKWARD = 1 } fp8ln_meta_kind;
 
-/* DelayedScaling recipe ([T] setup listing).  amax_compute_algo is always "max".
+/* LayerNormMLP activation: GELU with the tanh approximation (the default), or the
+ * exact erf form of the plain-PyTorch mirror block's nn.GELU() ([T] model
+ * listing). */
+typedef enum { FP8LN_GELU_TANH = 0, FP8LN_GELU_ERF = 1 } fp8ln_activation;
+
+/* DelayedScaling recipe ([T] setup listing) plus the module settings the steps
+ * need.  amax_compute_algo is always "max".
  *   format            fp8ln_format
  *   amax_history_len  1 .. 1024
  *   margin            0 .. 64; scale = fp8_max / max(history) / 2^margin
- *   ln_eps            LayerNorm epsilon, finite and > 0 (1e-5 by default) */
+ *   ln_eps            LayerNorm epsilon, finite and > 0 (1e-5 by default)
+ *   activation        fp8ln_activation of LayerNormMLP */
 typedef struct {
     int32_t format;
     int32_t amax_history_len;
     int32_t margin;
     float ln_eps;
+    int32_t activation;
 } fp8ln_recipe;
 
 /* One direction's FP8 state of one module, all device buffers owned by the caller:
@@ -249,7 +257,7 @@ int fp8ln_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* A, int32_t a_dtyp
  * as its own call:
  *   h = (sum_k A[m][k] B[n][k]) * (*sinv_a) * (*sinv_b) + bias[n]   (fp32)
  *   h_out[m][n] = bf16(h)                          (optional, may be NULL)
- *   g = gelu_tanh(h); q_out[m][n] = encode(g * (*q_scale)) in q_dtype
+ *   g = gelu(h) (activation: fp8ln_activation); q_out[m][n] = encode(g * (*q_scale))
  *   q_out_t[n][m] = q_out[m][n]                    (optional, needs M % 16 == 0)
  *   *q_amax = max(*q_amax, max |g|)
  * bias is bf16 [N] or NULL.  K and N must be multiples of 16. */
@@ -257,19 +265,20 @@ int fp8ln_gemm_gelu_fp8(int64_t M, int64_t N, int64_t K, const uint8_t* A, int32
                         const uint8_t* B, int32_t b_dtype, const float* sinv_a,
                         const float* sinv_b, const void* bias, void* h_out, uint8_t* q_out,
                         uint8_t* q_out_t, int32_t q_dtype, const float* q_scale, float* q_amax,
-                        void* stream);
+                        int32_t activation, void* stream);
 
 /* The fc2 dgrad step of the LayerNormMLP backward with the GELU derivative:
- *   out[m][n] = (sum_k A[m][k] B[n][k]) * (*sinv_a) * (*sinv_b) * gelu_tanh'(h[m][n])
+ *   out[m][n] = (sum_k A[m][k] B[n][k]) * (*sinv_a) * (*sinv_b) * gelu'(h[m][n])
+ * (gelu of the given fp8ln_activation).
  * h is the bf16 [M][N] fc1 output saved by the forward; out is fp32 [M][N].
  * K and N must be multiples of 16. */
 int fp8ln_gemm_dgelu(int64_t M, int64_t N, int64_t K, const uint8_t* A, int32_t a_dtype,
                      const uint8_t* B, int32_t b_dtype, const float* sinv_a, const float* sinv_b,
-                     const void* h, float* out, void* stream);
+                     const void* h, float* out, int32_t activation, void* stream);
 
 /* The same product with the gradient cast of the fc1 output fused in, which is
  * how the LayerNormMLP backward runs it (HYBRID: gradients in E5M2):
- *   d = (sum_k A[m][k] B[n][k]) * (*sinv_a) * (*sinv_b) * gelu_tanh'(h[m][n])  (fp32)
+ *   d = (sum_k A[m][k] B[n][k]) * (*sinv_a) * (*sinv_b) * gelu'(h[m][n])   (fp32)
  *   q_out[m][n] = encode(d * (*q_scale)) in q_dtype, from the exact product
  *   q_out_t[n][m] = q_out[m][n]                    (optional, needs M % 16 == 0)
  *   *q_amax = max(*q_amax, max |d|)
@@ -282,7 +291,8 @@ int fp8ln_gemm_dgelu_fp8(int64_t M, int64_t N, int64_t K, const uint8_t* A, int3
                          const uint8_t* B, int32_t b_dtype, const float* sinv_a,
                          const float* sinv_b, const void* h, int32_t q_dtype,
                          const float* q_scale, float* q_amax, uint8_t* q_out, uint8_t* q_out_t,
-                         float* dbias, void* workspace, size_t workspace_bytes, void* stream);
+                         float* dbias, int32_t activation, void* workspace,
+                         size_t workspace_bytes, void* stream);
 
 /* ---- LayerNorm backward ---------------------------------------------------- */
 

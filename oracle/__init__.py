@@ -30,9 +30,10 @@ from .codec import (E4M3, E5M2, FP8_MAX, bf16_to_f64, f64_to_bf16_bits, fp8_deco
                     fp8_decode_table, fp8_encode, fp8_positive_values)
 from .scaling import Meta, fp8_max_for, scaling_update
 from .layernorm import layernorm_fwd, layernorm_bwd
-from .gelu import gelu_tanh, gelu_tanh_grad
+from .gelu import gelu_erf, gelu_erf_grad, gelu_tanh, gelu_tanh_grad
 from .gemm import fp8_gemm_tn
-from .modules import (Recipe, FORMAT_E4M3, FORMAT_HYBRID, FORMAT_E5M2, cast_amax,
+from .modules import (Recipe, FORMAT_E4M3, FORMAT_HYBRID, FORMAT_E5M2, GELU_ERF, GELU_TANH,
+                      cast_amax,
                       ln_cast_amax, ln_linear_fwd, ln_linear_bwd, ln_mlp_fwd, ln_mlp_bwd,
                       fwd_format, bwd_format, linear_fwd_meta, linear_bwd_meta,
                       mlp_fwd_meta, mlp_bwd_meta)
@@ -41,6 +42,7 @@ __all__ = [
     "E4M3", "E5M2", "FP8_MAX", "bf16_to_f64", "f64_to_bf16_bits", "fp8_decode",
     "fp8_decode_table", "fp8_encode", "fp8_positive_values", "Meta", "fp8_max_for",
     "scaling_update", "layernorm_fwd", "layernorm_bwd", "gelu_tanh", "gelu_tanh_grad",
+    "gelu_erf", "gelu_erf_grad", "GELU_TANH", "GELU_ERF",
     "fp8_gemm_tn", "Recipe", "FORMAT_E4M3", "FORMAT_HYBRID", "FORMAT_E5M2", "cast_amax",
     "ln_cast_amax", "ln_linear_fwd", "ln_linear_bwd", "ln_mlp_fwd", "ln_mlp_bwd",
     "fwd_format", "bwd_format", "linear_fwd_meta", "linear_bwd_meta", "mlp_fwd_meta",

@@ -19,7 +19,8 @@ Readings (the pages name the modules and the recipe, not their internals):
 * amax is the largest |value| of the tensor before scaling, rounded to
   binary32; q = encode(value * scale) with the slot's binary32 scale.
 * The GEMM epilogue is acc * scale_inv_a * scale_inv_b + bias; the MLP applies
-  GELU (tanh form) to fc1's output in full precision and casts it to FP8 for
+  GELU (tanh form by default, erf form as the alternative activation) to fc1's
+  output in full precision and casts it to FP8 for
   fc2; fc1's output h is kept as bf16 for the backward's GELU derivative.
 * FP8 weight storage ("things to try next": FP8 model init): a forward may
   reuse the FP8 codes an earlier forward made of the unchanged weight, with the
@@ -39,7 +40,18 @@ from dataclasses import dataclass
 import numpy as np
 
 from .codec import E4M3, E5M2, bf16_to_f64, f64_to_bf16_bits, fp8_encode
-from .gelu import gelu_tanh, gelu_tanh_grad
+from .gelu import gelu_erf, gelu_erf_grad, gelu_tanh, gelu_tanh_grad
+
+GELU_TANH = 0
+GELU_ERF = 1
+
+
+def _gelu(recipe, h):
+    return gelu_erf(h) if recipe.activation == GELU_ERF else gelu_tanh(h)
+
+
+def _gelu_grad(recipe, h):
+    return gelu_erf_grad(h) if recipe.activation == GELU_ERF else gelu_tanh_grad(h)
 from .gemm import fp8_gemm_tn
 from .layernorm import layernorm_bwd, layernorm_fwd
 from .scaling import Meta
@@ -55,6 +67,7 @@ class Recipe:
     amax_history_len: int = 16
     margin: int = 0
     ln_eps: float = 1e-5
+    activation: int = 0          # 0: GELU tanh form, 1: GELU erf form
 
     @property
     def eps64(self) -> float:
@@ -172,7 +185,7 @@ def ln_mlp_fwd(recipe: Recipe, meta: Meta, x_bits, gamma_bits, beta_bits, w1_bit
     w2_q, w2_sinv, w2_amax = _weight(meta, 3, w2_bits, fmt, c2)
     h = fp8_gemm_tn(ln["q"], fmt, w1_q, fmt, meta.scale_inv[0], w1_sinv,
                     _bias(b1_bits, w1_q.shape[0]))
-    g = gelu_tanh(h)
+    g = _gelu(recipe, h)
     g_q, g_amax = cast_amax(g, meta.scale[2], fmt)
     meta.record_amax(2, g_amax)
     out = fp8_gemm_tn(g_q, fmt, w2_q, fmt, meta.scale_inv[2], w2_sinv,
@@ -193,7 +206,7 @@ def ln_mlp_bwd(recipe: Recipe, meta_fwd: Meta, meta_bwd: Meta, dy_bits, ctx, x_b
     db2 = dy.sum(axis=0)
     # fc2 dgrad, then the GELU derivative at the saved bf16 h
     dg = fp8_gemm_tn(dy_q, bfmt, ctx["w2_q"].T, ffmt, meta_bwd.scale_inv[0], ctx["w2_sinv"])
-    dh = dg * gelu_tanh_grad(bf16_to_f64(ctx["h_bits"]))
+    dh = dg * _gelu_grad(recipe, bf16_to_f64(ctx["h_bits"]))
     dh_q, dh_amax = cast_amax(dh, meta_bwd.scale[1], bfmt)
     meta_bwd.record_amax(1, dh_amax)
     db1 = dh.sum(axis=0)

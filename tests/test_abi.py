@@ -61,9 +61,11 @@ def test_workspace_sizes_are_host_only_and_monotone(lib):
 
 
 def _recipe(**kw):
-    r = dict(format=_abi.FORMAT_HYBRID, amax_history_len=16, margin=0, ln_eps=1e-5)
+    r = dict(format=_abi.FORMAT_HYBRID, amax_history_len=16, margin=0, ln_eps=1e-5,
+             activation=_abi.GELU_TANH)
     r.update(kw)
-    return _abi.Recipe(r["format"], r["amax_history_len"], r["margin"], r["ln_eps"])
+    return _abi.Recipe(r["format"], r["amax_history_len"], r["margin"], r["ln_eps"],
+                       r["activation"])
 
 
 @pytest.mark.parametrize("bad,status", [
@@ -73,6 +75,7 @@ def _recipe(**kw):
     (dict(margin=-1), _abi.FP8LN_ERR_INVALID_ARG),
     (dict(ln_eps=0.0), _abi.FP8LN_ERR_INVALID_ARG),
     (dict(ln_eps=float("nan")), _abi.FP8LN_ERR_INVALID_ARG),
+    (dict(activation=2), _abi.FP8LN_ERR_INVALID_ARG),
 ])
 def test_bad_recipe_is_rejected_before_any_launch(lib, bad, status):
     r = _recipe(**bad)

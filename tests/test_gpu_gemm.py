@@ -133,9 +133,18 @@ def test_gemm_is_deterministic():
 GELU_REL = 2e-6     # fp32 GELU (tanh via exp): ~1e-6 of |h| plus a few ulps of g
 
 
+GELU = {ops.GELU_TANH: (oracle.gelu_tanh, oracle.gelu_tanh_grad),
+        ops.GELU_ERF: (oracle.gelu_erf, oracle.gelu_erf_grad)}
+
+
+@pytest.mark.parametrize("act", [ops.GELU_TANH, ops.GELU_ERF], ids=["tanh", "erf"])
 @pytest.mark.parametrize("M,N,K,q", [(64, 128, 64, ops.E4M3), (130, 272, 48, ops.E5M2),
                                      (256, 3072, 32, ops.E4M3)])
-def test_gelu_epilogue_on_exact_products(M, N, K, q):
+def test_gelu_epilogue_on_exact_products(M, N, K, q, act):
+    gelu_exact_case(M, N, K, q, act)
+
+
+def gelu_exact_case(M, N, K, q, act):
     """Small integer operands and power-of-two scale_inv make every h exact in
     fp32, so h (bf16) must match bit for bit and the GELU codes may differ only
     where the fp32 GELU's own error reaches a rounding midpoint."""
@@ -149,11 +158,11 @@ def test_gelu_epilogue_on_exact_products(M, N, K, q):
     h_out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     amax = torch.zeros(1, dtype=torch.float32, device="cuda")
     ops.gemm_gelu_fp8(dev(a), ops.E4M3, dev(b), ops.E4M3, _scalar(sa), _scalar(sb), q,
-                      _scalar(qs), amax.data_ptr(), q_out, q_t, h_out, bias)
+                      _scalar(qs), amax.data_ptr(), q_out, q_t, h_out, bias, activation=act)
     torch.cuda.synchronize()
     h = (av @ bv.T) * sa * sb + oracle.bf16_to_f64(bias_bits)[None, :]
     np.testing.assert_array_equal(to_np(h_out), oracle.bf16_to_f64(oracle.f64_to_bf16_bits(h)))
-    g = oracle.gelu_tanh(h)
+    g = GELU[act][0](h)
     fmt = FMT[q]
     from parity import compare_codes
     stats = compare_codes(q_out.cpu().numpy(), g * qs, fmt,
@@ -165,18 +174,20 @@ def test_gelu_epilogue_on_exact_products(M, N, K, q):
         assert torch.equal(q_t, q_out.t().contiguous())
 
 
+@pytest.mark.parametrize("act", [ops.GELU_TANH, ops.GELU_ERF], ids=["tanh", "erf"])
 @pytest.mark.parametrize("M,N,K", [(64, 128, 64), (130, 272, 48)])
-def test_dgelu_epilogue_on_exact_products(M, N, K):
+def test_dgelu_epilogue_on_exact_products(M, N, K, act):
     a, av = int_codes((M, K), ops.E5M2, 9 + M, lim=4)
     b, bv = int_codes((N, K), ops.E4M3, 3 + N, lim=4)
     h_bits = oracle.f64_to_bf16_bits(np.random.default_rng(M).normal(size=(M, N)) * 2.0)
     h = torch.from_numpy(h_bits.view(np.int16)).view(torch.bfloat16).cuda()
     out = torch.empty((M, N), dtype=torch.float32, device="cuda")
     sa, sb = 1.0 / 8.0, 2.0
-    ops.gemm_dgelu(dev(a), ops.E5M2, dev(b), ops.E4M3, _scalar(sa), _scalar(sb), h, out)
+    ops.gemm_dgelu(dev(a), ops.E5M2, dev(b), ops.E4M3, _scalar(sa), _scalar(sb), h, out,
+                   activation=act)
     torch.cuda.synchronize()
     acc = (av @ bv.T) * sa * sb
-    ref = acc * oracle.gelu_tanh_grad(oracle.bf16_to_f64(h_bits))
+    ref = acc * GELU[act][1](oracle.bf16_to_f64(h_bits))
     err = np.abs(out.cpu().numpy() - ref)
     assert np.all(err <= 4e-6 * np.abs(acc) + 1e-30), err.max()
 
@@ -238,15 +249,18 @@ def test_small_integer_gemm_large_tiles_is_bit_exact(fa, fb, M, N, K):
 
 @pytest.mark.parametrize("M,N,K", BIG)
 def test_gelu_epilogue_large_tiles_on_exact_products(M, N, K):
-    test_gelu_epilogue_on_exact_products(M, N, K, ops.E4M3)
+    gelu_exact_case(M, N, K, ops.E4M3, ops.GELU_TANH)
+    gelu_exact_case(M, N, K, ops.E4M3, ops.GELU_ERF)
 
 
 # ---- fc2 dgrad with the fc1 gradient cast fused ---------------------------------
 
-@pytest.mark.parametrize("M,N,K,q", [(130, 272, 48, ops.E5M2), (256, 3072, 64, ops.E5M2),
-                                     (4096, 4096, 64, ops.E5M2), (4000, 4112, 48, ops.E4M3),
-                                     (2048, 8192, 2176, ops.E5M2)])
-def test_dgelu_fp8_epilogue_equals_dgelu_then_cast(M, N, K, q):
+@pytest.mark.parametrize("M,N,K,q,act", [(130, 272, 48, ops.E5M2, ops.GELU_TANH),
+                                         (256, 3072, 64, ops.E5M2, ops.GELU_ERF),
+                                         (4096, 4096, 64, ops.E5M2, ops.GELU_TANH),
+                                         (4000, 4112, 48, ops.E4M3, ops.GELU_ERF),
+                                         (2048, 8192, 2176, ops.E5M2, ops.GELU_TANH)])
+def test_dgelu_fp8_epilogue_equals_dgelu_then_cast(M, N, K, q, act):
     """The fused epilogue computes the same fp32 d = acc * alpha * gelu'(h) as the
     fp32 epilogue and casts it like the cast kernel: codes, transpose and amax
     agree bit for bit; the bias gradient (summed in another order) to fp32
@@ -260,7 +274,7 @@ def test_dgelu_fp8_epilogue_equals_dgelu_then_cast(M, N, K, q):
     has_t = M % 16 == 0
 
     d = torch.empty((M, N), dtype=torch.float32, device="cuda")
-    ops.gemm_dgelu(a, ops.E5M2, b, ops.E4M3, sa, sb, h, d)
+    ops.gemm_dgelu(a, ops.E5M2, b, ops.E4M3, sa, sb, h, d, activation=act)
     q1 = torch.empty((M, N), dtype=torch.uint8, device="cuda")
     q1t = torch.empty((N, M), dtype=torch.uint8, device="cuda") if has_t else None
     amax1 = torch.zeros(1, dtype=torch.float32, device="cuda")
@@ -274,7 +288,7 @@ def test_dgelu_fp8_epilogue_equals_dgelu_then_cast(M, N, K, q):
         amax2 = torch.zeros(1, dtype=torch.float32, device="cuda")
         db2 = torch.empty(N, dtype=torch.float32, device="cuda")
         ops.gemm_dgelu_fp8(a, ops.E5M2, b, ops.E4M3, sa, sb, h, q, scale, amax2.data_ptr(), q2,
-                           q2t, db2)
+                           q2t, db2, activation=act)
         runs.append((q2, q2t, amax2, db2))
     torch.cuda.synchronize()
     q2, q2t, amax2, db2 = runs[0]

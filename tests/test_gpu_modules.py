@@ -24,7 +24,7 @@ U32 = 2.0 ** -24
 
 def orecipe(r: ops.Recipe):
     return oracle.Recipe(format=OFMT[r.format], amax_history_len=r.amax_history_len,
-                         margin=r.margin, ln_eps=r.ln_eps)
+                         margin=r.margin, ln_eps=r.ln_eps, activation=r.activation)
 
 
 def f32bits(a):
@@ -139,7 +139,7 @@ def test_ln_linear_fwd_module_tour_16_steps():
                "c0", backward=False)
 
 
-@pytest.mark.parametrize("fmt", [ops.FORMAT_HYBRID, ops.FORMAT_E4M3])
+@pytest.mark.parametrize("fmt", [ops.FORMAT_HYBRID, ops.FORMAT_E4M3, ops.FORMAT_E5M2])
 def test_ln_linear_fwd_bwd_2048_tokens(fmt):
     run_linear(ops.Recipe(format=fmt, amax_history_len=16), 2048, 768, 2304, 3, f"c3/{fmt}",
                backward=True)
@@ -169,7 +169,7 @@ def test_ln_linear_fwd_ragged_tokens_forward_only():
 MFMA_DOT_REL = 2.0 ** -10
 
 
-def gelu_code_window(ln_q, w1_q, fmt, alpha, h, scale, K):
+def gelu_code_window(ln_q, w1_q, fmt, alpha, h, scale, K, act=ops.GELU_TANH):
     """GEMM-fed window for the GELU output's codes.  The FP8 MFMA's 128-term dot
     products carry about 13-14 bits relative to their sum of |a b| (measured
     worst case 3.2e-4 on full-range random codes); the fp32 accumulator adds are
@@ -179,8 +179,9 @@ def gelu_code_window(ln_q, w1_q, fmt, alpha, h, scale, K):
     b = oracle.fp8_decode(w1_q & 0x7F, fmt)
     abs_sum = a @ b.T
     dh = MFMA_DOT_REL * float(alpha) * abs_sum + 4 * U32 * np.abs(h)
-    dg = np.abs(oracle.gelu_tanh_grad(h)) * dh + 1e-6 * np.abs(oracle.gelu_tanh(h)) \
-        + 2e-7 * np.abs(h)
+    gelu, gelu_grad = ((oracle.gelu_erf, oracle.gelu_erf_grad) if act == ops.GELU_ERF
+                       else (oracle.gelu_tanh, oracle.gelu_tanh_grad))
+    dg = np.abs(gelu_grad(h)) * dh + 1e-6 * np.abs(gelu(h)) + 2e-7 * np.abs(h)
     return float(scale) * dg
 
 
@@ -247,7 +248,7 @@ def run_mlp(recipe, M, H, F, steps, workload, backward, sample_rows=None, reuse_
         s2 = float(omf.scale[2])
         gq = ctx.g_q.cpu().numpy()[rows]
         win = gelu_code_window(octx["ln_q"][rows], octx["w1_q"], ffmt, alpha, octx["h"][rows],
-                               s2, H)
+                               s2, H, recipe.activation)
         # LayerNorm codes the rule let differ (one step next to a midpoint) move the
         # whole fc1 row: add their effect through |W1| and the largest GELU' (1.13)
         d_ln = np.abs(oracle.fp8_decode(ctx.ln_q.cpu().numpy()[rows], ffmt) -
@@ -281,7 +282,7 @@ def test_ln_mlp_fwd_2048_tokens():
             "c2", backward=False)
 
 
-@pytest.mark.parametrize("fmt", [ops.FORMAT_HYBRID, ops.FORMAT_E4M3])
+@pytest.mark.parametrize("fmt", [ops.FORMAT_HYBRID, ops.FORMAT_E4M3, ops.FORMAT_E5M2])
 def test_ln_mlp_fwd_bwd_small(fmt):
     run_mlp(ops.Recipe(format=fmt, amax_history_len=8), 256, 256, 1024, 3, f"mlp/{fmt}",
             backward=True)
@@ -289,6 +290,13 @@ def test_ln_mlp_fwd_bwd_small(fmt):
 
 def test_ln_mlp_ragged_tiles():
     run_mlp(ops.Recipe(), 48, 80, 144, 3, "mlp-ragged", backward=True)
+
+
+@pytest.mark.parametrize("fmt", [ops.FORMAT_HYBRID, ops.FORMAT_E4M3])
+def test_ln_mlp_erf_gelu(fmt):
+    """LayerNormMLP with the erf form of GELU (nn.GELU() of the mirror block)."""
+    run_mlp(ops.Recipe(format=fmt, amax_history_len=8, activation=ops.GELU_ERF), 256, 256,
+            1024, 3, f"mlp-erf/{fmt}", backward=True)
 
 
 def test_ln_mlp_fp8_weight_storage():

@@ -110,3 +110,25 @@ def test_gelu_tanh_grad_matches_finite_differences_and_autograd():
     ht = torch.from_numpy(h).requires_grad_()
     F.gelu(ht, approximate="tanh").sum().backward()
     np.testing.assert_allclose(oracle.gelu_tanh_grad(h), ht.grad.numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_gelu_erf_matches_torch_and_identities():
+    h = np.linspace(-12.0, 12.0, 4801)
+    ref = F.gelu(torch.from_numpy(h)).numpy()             # the exact erf form
+    np.testing.assert_allclose(oracle.gelu_erf(h), ref, rtol=1e-14, atol=1e-15)
+    # gelu(x) - gelu(-x) = x, since erf is odd
+    np.testing.assert_allclose(oracle.gelu_erf(h) - oracle.gelu_erf(-h), h, atol=1e-13)
+    assert oracle.gelu_erf(0.0) == 0.0
+    assert abs(oracle.gelu_erf(30.0) - 30.0) < 1e-12 and abs(oracle.gelu_erf(-30.0)) < 1e-12
+    # Phi(1) = 0.841344746068543 (standard normal CDF at 1): gelu(1) = Phi(1)
+    assert abs(float(oracle.gelu_erf(1.0)) - 0.841344746068543) < 1e-14
+
+
+def test_gelu_erf_grad_matches_finite_differences_and_autograd():
+    h = np.linspace(-9.0, 9.0, 3601)
+    d = 1e-6
+    num = (oracle.gelu_erf(h + d) - oracle.gelu_erf(h - d)) / (2 * d)
+    np.testing.assert_allclose(oracle.gelu_erf_grad(h), num, rtol=1e-7, atol=1e-9)
+    ht = torch.from_numpy(h.copy()).requires_grad_(True)
+    F.gelu(ht).sum().backward()
+    np.testing.assert_allclose(oracle.gelu_erf_grad(h), ht.grad.numpy(), rtol=1e-12, atol=1e-14)
