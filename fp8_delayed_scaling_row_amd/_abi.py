@@ -36,6 +36,7 @@ OP_LAYERNORM_BWD = 1
 OP_LN_LINEAR_BWD = 2
 OP_LN_MLP_BWD = 3
 OP_GEMM_DGELU_FP8 = 4
+OP_LINEAR_BWD = 5
 
 
 class Recipe(C.Structure):
@@ -89,6 +90,10 @@ SIGNATURES = {
     "fp8ln_gemm_dgelu_fp8": (C.c_int, [_I64, _I64, _I64, _P, _I32, _P, _I32, _P, _P, _P, _I32, _P,
                                        _P, _P, _P, _P, _I32, _P, _SZ, _P]),
     "fp8ln_layernorm_bwd": (C.c_int, [_I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "fp8ln_linear_fwd": (C.c_int, [_RP, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _MP,
+                                   C.POINTER(LinearCtxStruct), _P]),
+    "fp8ln_linear_bwd": (C.c_int, [_RP, _I64, _I64, _I64, _I32, _P, C.POINTER(LinearCtxStruct),
+                                   _MP, _MP, _P, _P, _P, _P, _SZ, _P]),
     "fp8ln_ln_linear_fwd": (C.c_int, [_RP, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _MP,
                                       C.POINTER(LinearCtxStruct), _P]),
     "fp8ln_ln_linear_bwd": (C.c_int, [_RP, _I64, _I64, _I64, _I32, _P, _P, _P,

@@ -168,6 +168,24 @@ size_t dgelu_workspace(int64_t M, int64_t N) {
     return (size_t)gemm_partial_rows_bound(M) * (size_t)N * sizeof(float);
 }
 
+struct LinearOnlyWs {
+    uint8_t* dy_q;
+    uint8_t* dy_qt;
+    void* cast_ws;
+    size_t bytes;
+};
+
+LinearOnlyWs linear_only_ws(void* base, int64_t M, int64_t K, int64_t N) {
+    Carver c{(uint8_t*)base};
+    LinearOnlyWs w;
+    w.dy_q = (uint8_t*)c.take((size_t)(M * N));
+    w.dy_qt = (uint8_t*)c.take((size_t)(M * N));
+    w.cast_ws = c.take(cast_workspace(M, N));
+    (void)K;
+    w.bytes = c.used;
+    return w;
+}
+
 struct MlpWs {
     uint8_t* dy_q;
     uint8_t* dy_qt;
@@ -244,6 +262,7 @@ size_t fp8ln_workspace_size(int32_t op, int64_t a, int64_t b, int64_t c) {
         case FP8LN_OP_CAST_AMAX: return cast_workspace(a, b);
         case FP8LN_OP_LAYERNORM_BWD: return ln_bwd_workspace(a, (int)b);
         case FP8LN_OP_GEMM_DGELU_FP8: return dgelu_workspace(a, b);
+        case FP8LN_OP_LINEAR_BWD: return c > 0 ? linear_only_ws(nullptr, a, b, c).bytes : 0;
         case FP8LN_OP_LN_LINEAR_BWD: return c > 0 ? linear_ws(nullptr, a, b, c).bytes : 0;
         case FP8LN_OP_LN_MLP_BWD: return c > 0 ? mlp_ws(nullptr, a, b, c).bytes : 0;
         default: return 0;
@@ -510,6 +529,112 @@ int fp8ln_layernorm_bwd(int64_t rows, int64_t hidden, const float* dy, const voi
     FP8LN_TRY(launch_ln_bwd(rows, (int)hidden, dy, x, mean, rstd, gamma, dx, dgamma, dbeta,
                             workspace, as_stream(stream)),
               "layernorm_bwd launch");
+    return FP8LN_OK;
+}
+
+int fp8ln_linear_fwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_features,
+                     int64_t out_features, int32_t params_dtype, const void* x,
+                     const void* weight, const void* bias, void* out, const fp8ln_meta* fwd,
+                     const fp8ln_linear_ctx* ctx, void* stream) {
+    int s = check_recipe(recipe);
+    if (s) return s;
+    const int64_t M = tokens, K = in_features, N = out_features;
+    REQUIRE(M >= 0, "tokens < 0");
+    if (params_dtype != FP8LN_DTYPE_BF16)
+        return fail(FP8LN_ERR_UNSUPPORTED, "params_dtype %d: only bf16 is supported", params_dtype);
+    if (K <= 0 || K % 16 != 0)
+        return fail(FP8LN_ERR_UNSUPPORTED, "in_features %lld must be a positive multiple of 16",
+                    (long long)K);
+    if (N <= 0 || N % 16 != 0)
+        return fail(FP8LN_ERR_UNSUPPORTED, "out_features %lld must be a positive multiple of 16",
+                    (long long)N);
+    if ((s = check_meta(fwd, 2, FP8LN_META_FORWARD, "forward"))) return s;
+    REQUIRE_PTR(ctx);
+    REQUIRE(ctx->w_q, "ctx.w_q is required");
+    REQUIRE(M == 0 || ctx->ln_q, "ctx.ln_q (the input codes) is required");
+    if (ctx->ln_qt && M % 16 != 0)
+        return fail(FP8LN_ERR_UNSUPPORTED, "ctx.ln_qt needs tokens %% 16 == 0");
+    REQUIRE(!ctx->reuse_weight_codes || ctx->w_scale_inv,
+            "reuse_weight_codes needs ctx.w_scale_inv from an earlier forward");
+    if (!ctx->reuse_weight_codes) { REQUIRE_PTR(weight); REQUIRE_ALIGNED(weight); }
+    REQUIRE_ALIGNED(ctx->w_q);
+    if (ctx->w_qt) REQUIRE_ALIGNED(ctx->w_qt);
+    if (bias) REQUIRE_ALIGNED(bias);
+    if (M > 0) {
+        REQUIRE_PTR(x); REQUIRE_PTR(out);
+        REQUIRE_ALIGNED(x); REQUIRE_ALIGNED(out); REQUIRE_ALIGNED(ctx->ln_q);
+        if (ctx->ln_qt) REQUIRE_ALIGNED(ctx->ln_qt);
+    }
+    if ((s = check_current_device())) return s;
+    hipStream_t st = as_stream(stream);
+    const int f = meta_fp8(recipe, FP8LN_META_FORWARD);
+    float* hist = fwd->amax_history;
+    if (M > 0)
+        FP8LN_TRY(launch_cast_amax(M, K, false, x, f, fwd->scale + 0, hist + 0, ctx->ln_q,
+                                   ctx->ln_qt, nullptr, nullptr, st),
+                  "input cast launch");
+    const float* w_sinv = ctx->w_scale_inv ? ctx->w_scale_inv : fwd->scale_inv + 1;
+    if (!ctx->reuse_weight_codes)
+        FP8LN_TRY(launch_cast_amax(N, K, false, weight, f, fwd->scale + 1, hist + 1, ctx->w_q,
+                                   ctx->w_qt, nullptr, nullptr, st, fwd->scale_inv + 1,
+                                   ctx->w_scale_inv),
+                  "weight cast launch");
+    GemmParams p = gemm_params(M, N, K, ctx->ln_q, f, ctx->w_q, f, fwd->scale_inv + 0, w_sinv,
+                               kEpiBf16Bias);
+    p.bias = (const uint16_t*)bias;
+    p.out = out;
+    FP8LN_TRY(launch_gemm(p, st), "gemm launch");
+    return FP8LN_OK;
+}
+
+int fp8ln_linear_bwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_features,
+                     int64_t out_features, int32_t params_dtype, const void* dy,
+                     const fp8ln_linear_ctx* ctx, const fp8ln_meta* fwd, const fp8ln_meta* bwd,
+                     void* dx, float* dweight, float* dbias, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+    int s = check_recipe(recipe);
+    if (s) return s;
+    const int64_t M = tokens, K = in_features, N = out_features;
+    if (params_dtype != FP8LN_DTYPE_BF16)
+        return fail(FP8LN_ERR_UNSUPPORTED, "params_dtype %d: only bf16 is supported", params_dtype);
+    if (M < 0 || M % 16 != 0)
+        return fail(FP8LN_ERR_UNSUPPORTED, "tokens %lld must be a multiple of 16", (long long)M);
+    if (K <= 0 || K % 16 != 0 || N <= 0 || N % 16 != 0)
+        return fail(FP8LN_ERR_UNSUPPORTED, "in/out_features must be positive multiples of 16");
+    if ((s = check_meta(fwd, 2, FP8LN_META_FORWARD, "forward"))) return s;
+    if ((s = check_meta(bwd, 1, FP8LN_META_BACKWARD, "backward"))) return s;
+    REQUIRE_PTR(ctx);
+    REQUIRE(ctx->w_qt && (M == 0 || ctx->ln_qt),
+            "ctx needs ln_qt and w_qt from a training forward");
+    REQUIRE_PTR(dweight);
+    REQUIRE_ALIGNED(dweight); REQUIRE_ALIGNED(ctx->w_qt);
+    if (M > 0) {
+        REQUIRE_PTR(dy); REQUIRE_PTR(dx);
+        REQUIRE_ALIGNED(dy); REQUIRE_ALIGNED(dx); REQUIRE_ALIGNED(ctx->ln_qt);
+    }
+    const LinearOnlyWs need = linear_only_ws(nullptr, M, K, N);
+    REQUIRE(need.bytes == 0 || (workspace && workspace_bytes >= need.bytes),
+            "linear_bwd needs %zu bytes of workspace", need.bytes);
+    REQUIRE_ALIGNED(workspace);
+    if ((s = check_current_device())) return s;
+    hipStream_t st = as_stream(stream);
+    const LinearOnlyWs w = linear_only_ws(workspace, M, K, N);
+    const int ff = meta_fp8(recipe, FP8LN_META_FORWARD);
+    const int bf = meta_fp8(recipe, FP8LN_META_BACKWARD);
+    FP8LN_TRY(launch_cast_amax(M, N, false, dy, bf, bwd->scale + 0, bwd->amax_history + 0, w.dy_q,
+                               w.dy_qt, dbias, w.cast_ws, st),
+              "grad cast launch");
+    // dgrad: dx[M][K] = dy_q[M][N] . (w_qt[K][N])^T, bf16 out
+    GemmParams dg = gemm_params(M, K, N, w.dy_q, bf, ctx->w_qt, ff, bwd->scale_inv + 0,
+                                ctx->w_scale_inv ? ctx->w_scale_inv : fwd->scale_inv + 1,
+                                kEpiBf16Bias);
+    dg.out = dx;
+    FP8LN_TRY(launch_gemm(dg, st), "dgrad launch");
+    // wgrad: dW[N][K] = dy_qt[N][M] . (x_qt[K][M])^T
+    GemmParams wg = gemm_params(N, K, M, w.dy_qt, bf, ctx->ln_qt, ff, bwd->scale_inv + 0,
+                                fwd->scale_inv + 0, kEpiF32);
+    wg.out = dweight;
+    FP8LN_TRY(launch_gemm(wg, st), "wgrad launch");
     return FP8LN_OK;
 }
 

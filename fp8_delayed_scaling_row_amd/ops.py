@@ -15,14 +15,15 @@ from . import _abi
 from ._abi import (DTYPE_BF16, DTYPE_F32, E4M3, E5M2, FORMAT_E4M3, FORMAT_E5M2, FORMAT_HYBRID,
                    GELU_ERF, GELU_TANH,
                    META_BACKWARD, META_FORWARD, OP_CAST_AMAX, OP_LAYERNORM_BWD, OP_LN_LINEAR_BWD,
-                   OP_LN_MLP_BWD, OP_GEMM_DGELU_FP8, Fp8lnError, check, lib)
+                   OP_LN_MLP_BWD, OP_GEMM_DGELU_FP8, OP_LINEAR_BWD, Fp8lnError, check, lib)
 
 __all__ = [
     "Recipe", "Meta", "LinearCtx", "MlpCtx", "Fp8lnError", "FORMAT_E4M3", "FORMAT_HYBRID",
     "FORMAT_E5M2", "GELU_TANH", "GELU_ERF", "E4M3", "E5M2", "META_FORWARD", "META_BACKWARD", "OP_CAST_AMAX",
-    "OP_LAYERNORM_BWD", "OP_LN_LINEAR_BWD", "OP_LN_MLP_BWD", "OP_GEMM_DGELU_FP8", "check_support", "workspace_size", "meta_init",
+    "OP_LAYERNORM_BWD", "OP_LN_LINEAR_BWD", "OP_LN_MLP_BWD", "OP_GEMM_DGELU_FP8", "OP_LINEAR_BWD",
+    "check_support", "workspace_size", "meta_init",
     "scaling_update", "ln_cast_amax", "cast_amax", "encode_range", "gemm", "gemm_gelu_fp8",
-    "gemm_dgelu", "gemm_dgelu_fp8", "layernorm_bwd",
+    "gemm_dgelu", "gemm_dgelu_fp8", "layernorm_bwd", "linear_fwd", "linear_bwd",
     "ln_linear_fwd", "ln_linear_bwd", "ln_mlp_fwd", "ln_mlp_bwd", "fwd_fp8", "bwd_fp8",
 ]
 
@@ -108,7 +109,8 @@ class Meta:
 
 
 class LinearCtx:
-    """What LayerNormLinear's forward saves for its backward."""
+    """What LayerNormLinear's (or Linear's) forward saves for its backward; for
+    Linear, ln_q / ln_qt hold the input's codes and mean / rstd go unused."""
 
     def __init__(self, tokens: int, in_features: int, out_features: int, training=True,
                  device="cuda"):
@@ -316,6 +318,36 @@ def layernorm_bwd(dy, x, mean, rstd, gamma, dx, dgamma, dbeta, stream=None) -> N
 
 # ---- modules ------------------------------------------------------------------
 
+def linear_fwd(recipe: Recipe, x, weight, bias, out, fwd: Meta, ctx: LinearCtx,
+               stream=None) -> None:
+    M, K = x.shape
+    N = weight.shape[0]
+    _need(x, torch.bfloat16, (M, K), "x")
+    _need(weight, torch.bfloat16, (N, K), "weight")
+    _opt(bias, torch.bfloat16, (N,), "bias")
+    _need(out, torch.bfloat16, (M, N), "out")
+    r, m, c = recipe.as_c(), fwd.as_c(), ctx.as_c()
+    check(lib().fp8ln_linear_fwd(C.byref(r), M, K, N, DTYPE_BF16, _ptr(x), _ptr(weight),
+                                 _ptr(bias), _ptr(out), C.byref(m), C.byref(c), _stream(stream)))
+
+
+def linear_bwd(recipe: Recipe, dy, ctx: LinearCtx, fwd: Meta, bwd: Meta, dx, dweight,
+               dbias=None, workspace=None, stream=None) -> None:
+    M, N = dy.shape
+    K = dx.shape[1]
+    _need(dy, torch.bfloat16, (M, N), "dy")
+    _need(dx, torch.bfloat16, (M, K), "dx")
+    _need(dweight, torch.float32, (N, K), "dweight")
+    _opt(dbias, torch.float32, (N,), "dbias")
+    nbytes = workspace_size(OP_LINEAR_BWD, M, K, N)
+    if workspace is None:
+        workspace = _workspace(nbytes, dy.device)
+    r, mf, mb, c = recipe.as_c(), fwd.as_c(), bwd.as_c(), ctx.as_c()
+    check(lib().fp8ln_linear_bwd(C.byref(r), M, K, N, DTYPE_BF16, _ptr(dy), C.byref(c),
+                                 C.byref(mf), C.byref(mb), _ptr(dx), _ptr(dweight), _ptr(dbias),
+                                 _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
 def ln_linear_fwd(recipe: Recipe, x, gamma, beta, weight, bias, out, fwd: Meta, ctx: LinearCtx,
                   stream=None) -> None:
     M, K = x.shape
@@ -385,7 +417,8 @@ def ln_mlp_bwd(recipe: Recipe, dy, x, gamma, ctx: MlpCtx, fwd: Meta, bwd: Meta, 
 
 
 def linear_metas(recipe: Recipe, device="cuda"):
-    """Fresh forward (2 slots) and backward (1 slot) state of a LayerNormLinear."""
+    """Fresh forward (2 slots) and backward (1 slot) state of a LayerNormLinear or
+    a Linear."""
     return (Meta(recipe, 2, META_FORWARD, device), Meta(recipe, 1, META_BACKWARD, device))
 
 

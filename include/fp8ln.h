@@ -174,7 +174,8 @@ typedef enum {
     FP8LN_OP_LAYERNORM_BWD = 1,    /* a = rows, b = hidden */
     FP8LN_OP_LN_LINEAR_BWD = 2,    /* a = tokens, b = in_features, c = out_features */
     FP8LN_OP_LN_MLP_BWD = 3,       /* a = tokens, b = hidden, c = ffn */
-    FP8LN_OP_GEMM_DGELU_FP8 = 4    /* a = M, b = N (column sums requested) */
+    FP8LN_OP_GEMM_DGELU_FP8 = 4,   /* a = M, b = N (column sums requested) */
+    FP8LN_OP_LINEAR_BWD = 5        /* a = tokens, b = in_features, c = out_features */
 } fp8ln_op;
 
 /* ---- library ------------------------------------------------------------ */
@@ -305,6 +306,36 @@ int fp8ln_layernorm_bwd(int64_t rows, int64_t hidden, const float* dy, const voi
                         const float* mean, const float* rstd, const void* gamma, void* dx,
                         float* dgamma, float* dbeta, void* workspace, size_t workspace_bytes,
                         void* stream);
+
+/* ---- Linear ([T] setup listing, module tour: te.Linear) --------------------- */
+
+/* out = x W^T + bias with FP8 operands (a Linear layer without the LayerNorm), for
+ * x bf16 [tokens][in_features], W bf16 [out_features][in_features], bias bf16
+ * [out_features] or NULL, out bf16 [tokens][out_features]:
+ *   x_q = encode(x * scale[0]), amax -> history[0][0]   (stored in ctx->ln_q,
+ *         its transpose in ctx->ln_qt when set)
+ *   w_q = encode(W * scale[1]), amax -> history[0][1]   (or reused, see
+ *         fp8ln_linear_ctx.reuse_weight_codes)
+ *   out = (x_q . w_q^T) * scale_inv[0] * w_scale_inv + bias
+ * ctx->mean and ctx->rstd are not used.  in_features, out_features: multiples of
+ * 16; when ctx->ln_qt is set tokens must be a multiple of 16. */
+int fp8ln_linear_fwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_features,
+                     int64_t out_features, int32_t params_dtype, const void* x,
+                     const void* weight, const void* bias, void* out, const fp8ln_meta* fwd,
+                     const fp8ln_linear_ctx* ctx, void* stream);
+
+/* Backward of fp8ln_linear_fwd for dy bf16 [tokens][out_features]:
+ *   dy_q = encode(dy * bwd.scale[0]) in the backward format, amax -> bwd history
+ *   dx = (dy_q . w_q) * bwd.scale_inv[0] * w_scale_inv          (bf16 [tokens][in])
+ *   dW = (dy_q^T . x_q) * bwd.scale_inv[0] * fwd.scale_inv[0]   (fp32 [out][in])
+ *   dbias = column sums of dy (fp32 [out], or NULL)
+ * ctx must hold ln_qt (the input codes' transpose) and w_qt.  tokens: multiple of 16.
+ * Workspace: fp8ln_workspace_size(FP8LN_OP_LINEAR_BWD, tokens, in, out). */
+int fp8ln_linear_bwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_features,
+                     int64_t out_features, int32_t params_dtype, const void* dy,
+                     const fp8ln_linear_ctx* ctx, const fp8ln_meta* fwd, const fp8ln_meta* bwd,
+                     void* dx, float* dweight, float* dbias, void* workspace,
+                     size_t workspace_bytes, void* stream);
 
 /* ---- LayerNormLinear ([T] setup listing: te.LayerNormLinear(H, 3*H)) ------- */
 

@@ -139,6 +139,32 @@ def _weight(meta: Meta, slot: int, w_bits, fmt: str, cached):
     return w_q, np.float32(meta.scale_inv[slot]), w_amax
 
 
+def linear_fwd(recipe: Recipe, meta: Meta, x_bits, w_bits, bias_bits=None, cached_w=None):
+    """out = x W^T + b with FP8 operands (Linear: no LayerNorm).  Slot 0 is the
+    input x itself; the rest is ln_linear_fwd."""
+    fmt = fwd_format(recipe)
+    x_q, x_amax = cast_amax(bf16_to_f64(x_bits), meta.scale[0], fmt)
+    meta.record_amax(0, x_amax)
+    w_q, w_sinv, w_amax = _weight(meta, 1, w_bits, fmt, cached_w)
+    out = fp8_gemm_tn(x_q, fmt, w_q, fmt, meta.scale_inv[0], w_sinv,
+                      _bias(bias_bits, w_q.shape[0]))
+    ctx = dict(x_q=x_q, w_q=w_q, w_sinv=w_sinv, x_amax=x_amax, w_amax=w_amax)
+    return out, ctx
+
+
+def linear_bwd(recipe: Recipe, meta_fwd: Meta, meta_bwd: Meta, dy_bits, ctx):
+    """Gradients of linear_fwd for dy [M][N]: dx = dy W, dW = dy^T x (both from
+    FP8 codes), dbias = column sums of dy."""
+    ffmt, bfmt = fwd_format(recipe), bwd_format(recipe)
+    dy = bf16_to_f64(dy_bits)
+    dy_q, dy_amax = cast_amax(dy, meta_bwd.scale[0], bfmt)
+    meta_bwd.record_amax(0, dy_amax)
+    dx = fp8_gemm_tn(dy_q, bfmt, ctx["w_q"].T, ffmt, meta_bwd.scale_inv[0], ctx["w_sinv"])
+    dw = fp8_gemm_tn(dy_q.T, bfmt, ctx["x_q"].T, ffmt, meta_bwd.scale_inv[0],
+                     meta_fwd.scale_inv[0])
+    return dict(dx=dx, dw=dw, dbias=dy.sum(axis=0), dy_q=dy_q, dy_amax=dy_amax)
+
+
 def ln_linear_fwd(recipe: Recipe, meta: Meta, x_bits, gamma_bits, beta_bits, w_bits,
                   bias_bits=None, cached_w=None):
     """out = LN(x) W^T + b with FP8 operands.  x [M][K], W [N][K].  cached_w:

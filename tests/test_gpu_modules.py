@@ -164,6 +164,97 @@ def test_ln_linear_fwd_ragged_tokens_forward_only():
     run_linear(ops.Recipe(), 37, 768, 2304, 2, "lin-ragged", backward=False)
 
 
+# ---- Linear (no LayerNorm) -------------------------------------------------------
+
+def run_plain_linear(recipe, M, K, N, steps, workload, backward, reuse_from=None,
+                     with_bias=True):
+    """Linear's chain step by step against the oracle.  Every FP8 code here comes
+    from a bf16 value times a binary32 scale, so codes, amaxes and scales are
+    compared bit for bit; the GEMM outputs follow the GEMM rule."""
+    dev = "cuda"
+    w = inputs.linear_weight(N, K, workload, "weight")
+    bias = inputs.normal_bf16((N,), inputs.seed_for(workload, "bias"), std=0.1)
+    wd = w.to(dev)
+    biasd = bias.to(dev) if with_bias else None
+    mf, mb = ops.linear_metas(recipe)
+    ctx = ops.LinearCtx(M, K, N, training=backward)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    dw = torch.empty((N, K), dtype=torch.float32, device=dev)
+    dbias = torch.full((N,), float("nan"), dtype=torch.float32, device=dev)
+    orc = orecipe(recipe)
+    omf, omb = oracle.linear_fwd_meta(orc), oracle.linear_bwd_meta(orc)
+    ffmt, bfmt = oracle.fwd_format(orc), oracle.bwd_format(orc)
+    wbits = to_np_bits(w)
+    biasbits = to_np_bits(bias) if with_bias else None
+    cached = None
+    for step in range(steps):
+        reuse = reuse_from is not None and step >= reuse_from
+        ctx.reuse_weight_codes = reuse
+        x = inputs.normal_bf16((M, K), inputs.seed_for(workload, "x", step))
+        ops.scaling_update(recipe, mf)
+        ops.linear_fwd(recipe, x.to(dev), wd, biasd, out, mf, ctx)
+        oracle.scaling_update(omf, orc.margin)
+        oout, octx = oracle.linear_fwd(orc, omf, to_np_bits(x), wbits, biasbits,
+                                       cached_w=cached if reuse else None)
+        if not reuse:
+            cached = (octx["w_q"], octx["w_sinv"])
+        if backward:
+            dy = inputs.normal_bf16((M, N), inputs.seed_for(workload, "dy", step), std=1e-3)
+            ops.scaling_update(recipe, mb)
+            ops.linear_bwd(recipe, dy.to(dev), ctx, mf, mb, dx, dw, dbias)
+            oracle.scaling_update(omb, orc.margin)
+            og = oracle.linear_bwd(orc, omf, omb, to_np_bits(dy), octx)
+        torch.cuda.synchronize()
+        tag = f"step {step}"
+        np.testing.assert_array_equal(ctx.ln_q.cpu().numpy(), octx["x_q"], err_msg=f"{tag} x_q")
+        np.testing.assert_array_equal(ctx.w_q.cpu().numpy(), octx["w_q"], err_msg=f"{tag} w_q")
+        assert ctx.w_scale_inv.item() == float(octx["w_sinv"])
+        check_meta(mf, omf, exact_slots=[0, 1], rel_slots=[], what=f"{tag} fwd")
+        if M > 0:
+            assert_gemm_close(to_np(out), oout, alarm=5e-3, what=f"{tag} out")
+        if backward:
+            assert torch.equal(ctx.ln_qt, ctx.ln_q.t().contiguous())
+            assert torch.equal(ctx.w_qt, ctx.w_q.t().contiguous())
+            check_meta(mb, omb, exact_slots=[0], rel_slots=[], what=f"{tag} bwd")
+            if M > 0:
+                assert_gemm_close(to_np(dx), og["dx"], alarm=5e-3, what=f"{tag} dx")
+                assert_gemm_close(dw.cpu().numpy(), og["dw"], alarm=1e-3, what=f"{tag} dW")
+                assert_vector_close(dbias.cpu().numpy(), og["dbias"], 1e-5, f"{tag} dbias")
+            else:
+                assert not dw.any().item(), "dW of zero tokens must be zero"
+                assert not dbias.any().item(), "dbias of zero tokens must be zero"
+
+
+@pytest.mark.parametrize("fmt", [ops.FORMAT_HYBRID, ops.FORMAT_E4M3, ops.FORMAT_E5M2])
+def test_linear_fwd_bwd_2048_tokens(fmt):
+    """Linear(768, 2304) on 8 x 256 tokens, three steps."""
+    run_plain_linear(ops.Recipe(format=fmt, amax_history_len=16), 2048, 768, 2304, 3,
+                     f"plin/{fmt}", backward=True)
+
+
+@pytest.mark.parametrize("M,K,N", [(48, 64, 80), (16, 16, 16), (144, 256, 400), (0, 64, 32)])
+def test_linear_small_ragged_and_empty(M, K, N):
+    run_plain_linear(ops.Recipe(amax_history_len=4, margin=1), M, K, N, 3,
+                     f"plin/{M}/{K}/{N}", backward=True, with_bias=(M != 16))
+
+
+def test_linear_forward_only_ragged_tokens():
+    run_plain_linear(ops.Recipe(), 37, 768, 2304, 2, "plin-ragged", backward=False)
+
+
+def test_linear_fp8_weight_storage():
+    run_plain_linear(ops.Recipe(amax_history_len=4), 256, 768, 2304, 5, "plin/fp8-weights",
+                     backward=True, reuse_from=2)
+
+
+def test_linear_large_tiles():
+    """A shape that takes the large GEMM tiles in all three products (long K in
+    the weight gradient)."""
+    run_plain_linear(ops.Recipe(amax_history_len=2), 4096, 2048, 2048, 1, "plin/large",
+                     backward=True)
+
+
 # ---- LayerNormMLP --------------------------------------------------------------
 
 MFMA_DOT_REL = 2.0 ** -10

@@ -232,3 +232,49 @@ def test_weight_reuse_keeps_the_stored_scale():
                               meta.scale_inv[0], np.float32(1.0))
     np.testing.assert_array_equal(out, want)
     assert ctx["w_sinv"] == np.float32(1.0)
+
+
+# ---- Linear (no LayerNorm) ----------------------------------------------------
+
+@pytest.mark.parametrize("fmt", [oracle.FORMAT_HYBRID, oracle.FORMAT_E4M3, oracle.FORMAT_E5M2])
+def test_linear_chain_is_exact_on_representable_values(fmt):
+    """With unit scales and inputs every format holds exactly, each cast is the
+    identity and every product and sum is exact in float64, so the chain equals
+    the plain matrix algebra of a linear layer (a transposed operand, a swapped
+    scale or a dropped bias would not)."""
+    rng = np.random.default_rng(31)
+    vals = np.array([0.0, 0.25, 0.5, 1.0, 1.5, 2.0, -0.25, -0.5, -1.0, -1.5, -2.0])
+    M, K, N = 24, 40, 56
+    x, w, dy = (rng.choice(vals, size=s) for s in [(M, K), (N, K), (M, N)])
+    bias = rng.choice(vals, size=N)
+    r = oracle.Recipe(format=fmt)
+    mf, mb = oracle.linear_fwd_meta(r), oracle.linear_bwd_meta(r)   # scales start at 1
+    out, ctx = oracle.linear_fwd(r, mf, bf16_bits(x), bf16_bits(w), bf16_bits(bias))
+    g = oracle.linear_bwd(r, mf, mb, bf16_bits(dy), ctx)
+    np.testing.assert_array_equal(out, x @ w.T + bias)
+    np.testing.assert_array_equal(g["dx"], dy @ w)
+    np.testing.assert_array_equal(g["dw"], dy.T @ x)
+    np.testing.assert_array_equal(g["dbias"], dy.sum(axis=0))
+    assert mf.history[0, 0] == np.abs(x).max() and mf.history[0, 1] == np.abs(w).max()
+    assert mb.history[0, 0] == np.abs(dy).max()
+
+
+def test_linear_chain_tracks_unquantised_autograd():
+    """After the delayed scales settle, the FP8 Linear stays within FP8 rounding
+    of float64 autograd of x W^T + b."""
+    r = oracle.Recipe()
+    mf, mb = oracle.linear_fwd_meta(r), oracle.linear_bwd_meta(r)
+    for step in range(3):
+        x, _, _, w, bias, dy = make_linear_case(seed=50 + step)
+        oracle.scaling_update(mf)
+        oracle.scaling_update(mb)
+        out, ctx = oracle.linear_fwd(r, mf, x, w, bias)
+        grads = oracle.linear_bwd(r, mf, mb, dy, ctx)
+    f = lambda bits: torch.from_numpy(oracle.bf16_to_f64(bits)).requires_grad_()
+    xt, wt, bt = f(x), f(w), f(bias)
+    ref = xt @ wt.T + bt
+    ref.backward(torch.from_numpy(oracle.bf16_to_f64(dy)))
+    assert rel_rows(out, ref.detach().numpy()) < 0.05
+    assert rel_rows(grads["dx"], xt.grad.numpy()) < 0.08
+    assert rel_rows(grads["dw"], wt.grad.numpy()) < 0.08
+    np.testing.assert_allclose(grads["dbias"], bt.grad.numpy(), rtol=1e-12, atol=0)
