@@ -90,6 +90,9 @@ SIGNATURES = {
     "fp8ln_gemm_dgelu_fp8": (C.c_int, [_I64, _I64, _I64, _P, _I32, _P, _I32, _P, _P, _P, _I32, _P,
                                        _P, _P, _P, _P, _I32, _P, _SZ, _P]),
     "fp8ln_layernorm_bwd": (C.c_int, [_I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "fp8ln_layernorm_fwd": (C.c_int, [_I64, _I64, C.c_float, _P, _P, _P, _P, _P, _P, _P]),
+    "fp8ln_layernorm_bwd_bf16": (C.c_int, [_I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
+                                           _P]),
     "fp8ln_linear_fwd": (C.c_int, [_RP, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _MP,
                                    C.POINTER(LinearCtxStruct), _P]),
     "fp8ln_linear_bwd": (C.c_int, [_RP, _I64, _I64, _I64, _I32, _P, C.POINTER(LinearCtxStruct),

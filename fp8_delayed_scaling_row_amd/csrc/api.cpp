@@ -526,7 +526,54 @@ int fp8ln_layernorm_bwd(int64_t rows, int64_t hidden, const float* dy, const voi
             "layernorm_bwd needs %zu bytes of workspace", ln_bwd_workspace(rows, (int)hidden));
     int s = check_current_device();
     if (s) return s;
-    FP8LN_TRY(launch_ln_bwd(rows, (int)hidden, dy, x, mean, rstd, gamma, dx, dgamma, dbeta,
+    FP8LN_TRY(launch_ln_bwd(rows, (int)hidden, dy, false, x, mean, rstd, gamma, dx, dgamma, dbeta,
+                            workspace, as_stream(stream)),
+              "layernorm_bwd launch");
+    return FP8LN_OK;
+}
+
+int fp8ln_layernorm_fwd(int64_t rows, int64_t hidden, float eps, const void* x,
+                        const void* gamma, const void* beta, void* y, float* mean, float* rstd,
+                        void* stream) {
+    REQUIRE(rows >= 0, "rows %lld < 0", (long long)rows);
+    REQUIRE(eps > 0.0f && eps <= 3.402823466e38f, "eps must be a positive finite number");
+    if (hidden <= 0 || hidden % 8 != 0 || hidden > 8192)
+        return fail(FP8LN_ERR_UNSUPPORTED, "hidden %lld must be a multiple of 8 in 8..8192",
+                    (long long)hidden);
+    REQUIRE_PTR(gamma); REQUIRE_PTR(beta);
+    REQUIRE_ALIGNED(gamma); REQUIRE_ALIGNED(beta);
+    if (rows > 0) {
+        REQUIRE_PTR(x); REQUIRE_PTR(y);
+        REQUIRE_ALIGNED(x); REQUIRE_ALIGNED(y);
+    }
+    int s = check_current_device();
+    if (s) return s;
+    if (rows == 0) return FP8LN_OK;
+    FP8LN_TRY(launch_ln_cast_amax(rows, (int)hidden, x, gamma, beta, eps, kLnOutBf16, nullptr,
+                                  nullptr, y, mean, rstd, as_stream(stream)),
+              "layernorm_fwd launch");
+    return FP8LN_OK;
+}
+
+int fp8ln_layernorm_bwd_bf16(int64_t rows, int64_t hidden, const void* dy, const void* x,
+                             const float* mean, const float* rstd, const void* gamma, void* dx,
+                             float* dgamma, float* dbeta, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    REQUIRE(rows >= 0, "rows < 0");
+    if (hidden <= 0 || hidden % 8 != 0 || hidden > 4096)
+        return fail(FP8LN_ERR_UNSUPPORTED, "hidden %lld must be a multiple of 8 in 8..4096",
+                    (long long)hidden);
+    REQUIRE_PTR(gamma); REQUIRE_PTR(dgamma); REQUIRE_PTR(dbeta);
+    REQUIRE_ALIGNED(gamma);
+    if (rows > 0) {
+        REQUIRE_PTR(dy); REQUIRE_PTR(x); REQUIRE_PTR(mean); REQUIRE_PTR(rstd); REQUIRE_PTR(dx);
+        REQUIRE_ALIGNED(dy); REQUIRE_ALIGNED(x); REQUIRE_ALIGNED(dx);
+    }
+    REQUIRE(workspace && workspace_bytes >= ln_bwd_workspace(rows, (int)hidden),
+            "layernorm_bwd needs %zu bytes of workspace", ln_bwd_workspace(rows, (int)hidden));
+    int s = check_current_device();
+    if (s) return s;
+    FP8LN_TRY(launch_ln_bwd(rows, (int)hidden, dy, true, x, mean, rstd, gamma, dx, dgamma, dbeta,
                             workspace, as_stream(stream)),
               "layernorm_bwd launch");
     return FP8LN_OK;
@@ -753,7 +800,7 @@ int fp8ln_ln_linear_bwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_f
                                 fwd->scale_inv + 0, kEpiF32);
     wg.out = dweight;
     FP8LN_TRY(launch_gemm(wg, st), "wgrad launch");
-    FP8LN_TRY(launch_ln_bwd(M, (int)K, w.dln, x, ctx->mean, ctx->rstd, gamma, dx, dgamma, dbeta,
+    FP8LN_TRY(launch_ln_bwd(M, (int)K, w.dln, false, x, ctx->mean, ctx->rstd, gamma, dx, dgamma, dbeta,
                             w.ln_ws, st),
               "layernorm_bwd launch");
     return FP8LN_OK;
@@ -924,7 +971,7 @@ int fp8ln_ln_mlp_bwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t hidden,
                                  fwd->scale_inv + 0, kEpiF32);
     wg1.out = dw1;
     FP8LN_TRY(launch_gemm(wg1, st), "fc1 wgrad launch");
-    FP8LN_TRY(launch_ln_bwd(M, (int)H, w.dln, x, ctx->mean, ctx->rstd, gamma, dx, dgamma, dbeta,
+    FP8LN_TRY(launch_ln_bwd(M, (int)H, w.dln, false, x, ctx->mean, ctx->rstd, gamma, dx, dgamma, dbeta,
                             w.ln_ws, st),
               "layernorm_bwd launch");
     return FP8LN_OK;

@@ -18,13 +18,15 @@ hipError_t launch_meta_init(float* hist, float* scale, float* scale_inv, int len
 hipError_t launch_scaling_update(float* hist, float* scale, float* scale_inv, int len,
                                  int n_slots, int margin, float fp8_max, hipStream_t stream);
 
-// layernorm.hip
+// layernorm.hip.  fp8 = kLnOutBf16 selects the plain LayerNorm (bf16 output,
+// scale and amax unused).
+constexpr int kLnOutBf16 = 2;
 hipError_t launch_ln_cast_amax(int64_t rows, int hidden, const void* x, const void* gamma,
                                const void* beta, float eps, int fp8, const float* scale,
-                               float* amax, uint8_t* out, float* mean, float* rstd,
+                               float* amax, void* out, float* mean, float* rstd,
                                hipStream_t stream);
 size_t ln_bwd_workspace(int64_t rows, int hidden);
-hipError_t launch_ln_bwd(int64_t rows, int hidden, const float* dy, const void* x,
+hipError_t launch_ln_bwd(int64_t rows, int hidden, const void* dy, bool dy_bf16, const void* x,
                          const float* mean, const float* rstd, const void* gamma, void* dx,
                          float* dgamma, float* dbeta, void* workspace, hipStream_t stream);
 

@@ -34,11 +34,12 @@ constexpr int kWavesPerBlock = kThreads / kWave;
 // (packed bf16, non-temporal) before it works on the current one.  Row
 // statistics use DPP reductions inside 16-lane rows.  FULL: hidden is exactly
 // CPL * 512, so every lane owns CPL whole chunks and no lane needs masking.
+// FMT kLnOutBf16 is the plain LayerNorm: y rounded to bf16, no scale, no amax.
 template <int CPL, int FMT, bool FULL>
 __global__ __launch_bounds__(kThreads) void ln_cast_amax_kernel(
     const uint4* __restrict__ x, const uint4* __restrict__ gamma, const uint4* __restrict__ beta,
     int64_t rows, int hidden, float eps, const float* __restrict__ scale_ptr,
-    float* __restrict__ amax_ptr, uint2* __restrict__ out, float* __restrict__ mean_out,
+    float* __restrict__ amax_ptr, void* __restrict__ out, float* __restrict__ mean_out,
     float* __restrict__ rstd_out) {
     __shared__ float4 gb[2][CPL * kWave][2];   // gamma, beta widened to fp32, 8 per chunk
     __shared__ uint32_t red[kWavesPerBlock];
@@ -46,7 +47,8 @@ __global__ __launch_bounds__(kThreads) void ln_cast_amax_kernel(
     const int wave = threadIdx.x / kWave;
     const int nchunk = FULL ? CPL * kWave : hidden / 8;
     const float inv_h = 1.0f / (float)hidden;
-    const float s = *scale_ptr;
+    constexpr bool kBf16 = FMT == kLnOutBf16;
+    const float s = kBf16 ? 1.0f : *scale_ptr;
 
     for (int c = threadIdx.x; c < CPL * kWave; c += kThreads) {
         float g[8], b[8];
@@ -110,7 +112,8 @@ __global__ __launch_bounds__(kThreads) void ln_cast_amax_kernel(
         const float var = wave_sum_dpp(sq) * inv_h;
         const float rs = 1.0f / sqrtf(var + eps);
 
-        uint2* orow = out + row * nchunk;
+        uint2* orow = (uint2*)out + row * nchunk;
+        uint4* orow16 = (uint4*)out + row * nchunk;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
             const int c = lane + i * kWave;
@@ -123,20 +126,29 @@ __global__ __launch_bounds__(kThreads) void ln_cast_amax_kernel(
                 uint32_t cm = amax_bits;
 #pragma unroll
                 for (int k = 0; k < 8; ++k) y[k] = fmaf(d[8 * i + k] * rs, gg[k], bb[k]);
+                if constexpr (kBf16) {
+                    uint4 w;
+                    w.x = pack_bf16x2(y[0], y[1]);
+                    w.y = pack_bf16x2(y[2], y[3]);
+                    w.z = pack_bf16x2(y[4], y[5]);
+                    w.w = pack_bf16x2(y[6], y[7]);
+                    store_nt(orow16 + c, w);
+                } else {
 #pragma unroll
-                for (int k = 0; k < 8; k += 2)
-                    cm = max(cm, max(abs_bits(y[k]), abs_bits(y[k + 1])));   // v_max3_u32
+                    for (int k = 0; k < 8; k += 2)
+                        cm = max(cm, max(abs_bits(y[k]), abs_bits(y[k + 1])));   // v_max3_u32
 #pragma unroll
-                for (int k = 0; k < 8; ++k) ys[k] = y[k] * s;
-                uint2 q;
-                q.x = encode4<FMT>(ys[0], ys[1], ys[2], ys[3]);
-                q.y = encode4<FMT>(ys[4], ys[5], ys[6], ys[7]);
-                if (__builtin_expect(cm > kInfBits, 0)) {
-                    q.x = patch_nan4(q.x, ys);
-                    q.y = patch_nan4(q.y, ys + 4);
+                    for (int k = 0; k < 8; ++k) ys[k] = y[k] * s;
+                    uint2 q;
+                    q.x = encode4<FMT>(ys[0], ys[1], ys[2], ys[3]);
+                    q.y = encode4<FMT>(ys[4], ys[5], ys[6], ys[7]);
+                    if (__builtin_expect(cm > kInfBits, 0)) {
+                        q.x = patch_nan4(q.x, ys);
+                        q.y = patch_nan4(q.y, ys + 4);
+                    }
+                    store_nt(orow + c, q);
+                    amax_bits = cm;
                 }
-                store_nt(orow + c, q);
-                amax_bits = cm;
             }
         }
         if (lane == 0) {
@@ -144,27 +156,29 @@ __global__ __launch_bounds__(kThreads) void ln_cast_amax_kernel(
             if (rstd_out) rstd_out[row] = rs;
         }
     }
-    block_amax_atomic(amax_bits, amax_ptr, red);
+    if constexpr (!kBf16) block_amax_atomic(amax_bits, amax_ptr, red);
 }
 
 template <int CPL, bool FULL>
 hipError_t launch_ln_fwd_full(int64_t rows, int hidden, const void* x, const void* gamma,
                               const void* beta, float eps, int fp8, const float* scale,
-                              float* amax, uint8_t* out, float* mean, float* rstd,
+                              float* amax, void* out, float* mean, float* rstd,
                               hipStream_t stream) {
     // Resident grid: as many workgroups as the CUs hold at once, each looping
     // over rows, so the row prefetch runs across the whole sweep instead of
     // restarting per wave (a second round of workgroups would run alone at the
     // end of the sweep).
-    static int resident[2] = {0, 0};   // per output format, from the occupancy query
-    int& per_cu = resident[fp8 == kE4M3 ? 0 : 1];
+    static int resident[3] = {0, 0, 0};   // per output format, from the occupancy query
+    int& per_cu = resident[fp8];
     if (per_cu == 0) {
         int nb = 0;
         hipError_t e = fp8 == kE4M3
             ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
                   &nb, ln_cast_amax_kernel<CPL, kE4M3, FULL>, kThreads, 0)
-            : hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                  &nb, ln_cast_amax_kernel<CPL, kE5M2, FULL>, kThreads, 0);
+            : fp8 == kE5M2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                                 &nb, ln_cast_amax_kernel<CPL, kE5M2, FULL>, kThreads, 0)
+                           : hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                                 &nb, ln_cast_amax_kernel<CPL, kLnOutBf16, FULL>, kThreads, 0);
         if (e != hipSuccess) return e;
         int dev = 0, cus = 0;
         if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
@@ -179,18 +193,22 @@ hipError_t launch_ln_fwd_full(int64_t rows, int hidden, const void* x, const voi
     if (fp8 == kE4M3)
         hipLaunchKernelGGL((ln_cast_amax_kernel<CPL, kE4M3, FULL>), dim3(blocks), dim3(kThreads),
                            0, stream, (const uint4*)x, (const uint4*)gamma, (const uint4*)beta,
-                           rows, hidden, eps, scale, amax, (uint2*)out, mean, rstd);
-    else
+                           rows, hidden, eps, scale, amax, out, mean, rstd);
+    else if (fp8 == kE5M2)
         hipLaunchKernelGGL((ln_cast_amax_kernel<CPL, kE5M2, FULL>), dim3(blocks), dim3(kThreads),
                            0, stream, (const uint4*)x, (const uint4*)gamma, (const uint4*)beta,
-                           rows, hidden, eps, scale, amax, (uint2*)out, mean, rstd);
+                           rows, hidden, eps, scale, amax, out, mean, rstd);
+    else
+        hipLaunchKernelGGL((ln_cast_amax_kernel<CPL, kLnOutBf16, FULL>), dim3(blocks),
+                           dim3(kThreads), 0, stream, (const uint4*)x, (const uint4*)gamma,
+                           (const uint4*)beta, rows, hidden, eps, scale, amax, out, mean, rstd);
     return hipGetLastError();
 }
 
 template <int CPL>
 hipError_t launch_ln_fwd_cpl(int64_t rows, int hidden, const void* x, const void* gamma,
                              const void* beta, float eps, int fp8, const float* scale,
-                             float* amax, uint8_t* out, float* mean, float* rstd,
+                             float* amax, void* out, float* mean, float* rstd,
                              hipStream_t stream) {
     if (hidden == CPL * kWave * 8)
         return launch_ln_fwd_full<CPL, true>(rows, hidden, x, gamma, beta, eps, fp8, scale, amax,
@@ -204,9 +222,11 @@ hipError_t launch_ln_fwd_cpl(int64_t rows, int hidden, const void* x, const void
 // Per block: rows handled by its waves in grid-stride order; per lane: dgamma and
 // dbeta partial sums of its own columns.  Partials go to ws[block][2][hidden] and a
 // second kernel adds the blocks in a fixed order, so results are deterministic.
-template <int CPL>
+// DY_BF16: dy arrives as bf16 (the plain LayerNorm module) instead of fp32 (the
+// dgrad GEMM's output inside the fused modules).
+template <int CPL, bool DY_BF16>
 __global__ __launch_bounds__(kThreads) void ln_bwd_kernel(
-    const float4* __restrict__ dy, const uint4* __restrict__ x, const float* __restrict__ mean,
+    const void* __restrict__ dy_raw, const uint4* __restrict__ x, const float* __restrict__ mean,
     const float* __restrict__ rstd, const uint4* __restrict__ gamma, uint4* __restrict__ dx,
     float* __restrict__ partial, int64_t rows, int hidden) {
     extern __shared__ float sm[];   // [2][hidden]: dgamma, dbeta of the block
@@ -239,10 +259,16 @@ __global__ __launch_bounds__(kThreads) void ln_bwd_kernel(
             const int c = lane + i * kWave;
             if (c < nchunk) {
                 unpack_bf16x8(load_nt(x + row * nchunk + c), xh + 8 * i);
-                const float4 a = load_nt(dy + (row * nchunk + c) * 2);
-                const float4 b2 = load_nt(dy + (row * nchunk + c) * 2 + 1);
-                d[8 * i + 0] = a.x; d[8 * i + 1] = a.y; d[8 * i + 2] = a.z; d[8 * i + 3] = a.w;
-                d[8 * i + 4] = b2.x; d[8 * i + 5] = b2.y; d[8 * i + 6] = b2.z; d[8 * i + 7] = b2.w;
+                if constexpr (DY_BF16) {
+                    unpack_bf16x8(load_nt((const uint4*)dy_raw + row * nchunk + c), d + 8 * i);
+                } else {
+                    const float4* dy = (const float4*)dy_raw;
+                    const float4 a = load_nt(dy + (row * nchunk + c) * 2);
+                    const float4 b2 = load_nt(dy + (row * nchunk + c) * 2 + 1);
+                    d[8 * i + 0] = a.x; d[8 * i + 1] = a.y; d[8 * i + 2] = a.z;
+                    d[8 * i + 3] = a.w; d[8 * i + 4] = b2.x; d[8 * i + 5] = b2.y;
+                    d[8 * i + 6] = b2.z; d[8 * i + 7] = b2.w;
+                }
             } else {
 #pragma unroll
                 for (int k = 0; k < 8; ++k) { xh[8 * i + k] = mu; d[8 * i + k] = 0.0f; }
@@ -309,15 +335,21 @@ int ln_bwd_blocks(int64_t rows) {
 }
 
 template <int CPL>
-hipError_t launch_ln_bwd_cpl(int64_t rows, int hidden, const float* dy, const void* x,
-                             const float* mean, const float* rstd, const void* gamma, void* dx,
-                             float* dgamma, float* dbeta, void* workspace, hipStream_t stream) {
+hipError_t launch_ln_bwd_cpl(int64_t rows, int hidden, const void* dy, bool dy_bf16,
+                             const void* x, const float* mean, const float* rstd,
+                             const void* gamma, void* dx, float* dgamma, float* dbeta,
+                             void* workspace, hipStream_t stream) {
     const int blocks = ln_bwd_blocks(rows);
     const size_t smem = (size_t)2 * hidden * sizeof(float);
     float* partial = (float*)workspace;
-    hipLaunchKernelGGL((ln_bwd_kernel<CPL>), dim3(blocks), dim3(kThreads), smem, stream,
-                       (const float4*)dy, (const uint4*)x, mean, rstd, (const uint4*)gamma,
-                       (uint4*)dx, partial, rows, hidden);
+    if (dy_bf16)
+        hipLaunchKernelGGL((ln_bwd_kernel<CPL, true>), dim3(blocks), dim3(kThreads), smem, stream,
+                           dy, (const uint4*)x, mean, rstd, (const uint4*)gamma, (uint4*)dx,
+                           partial, rows, hidden);
+    else
+        hipLaunchKernelGGL((ln_bwd_kernel<CPL, false>), dim3(blocks), dim3(kThreads), smem,
+                           stream, dy, (const uint4*)x, mean, rstd, (const uint4*)gamma,
+                           (uint4*)dx, partial, rows, hidden);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_sum_partials(partial, blocks, 2 * (int64_t)hidden, dgamma, dbeta, hidden,
@@ -328,7 +360,7 @@ hipError_t launch_ln_bwd_cpl(int64_t rows, int hidden, const float* dy, const vo
 
 hipError_t launch_ln_cast_amax(int64_t rows, int hidden, const void* x, const void* gamma,
                                const void* beta, float eps, int fp8, const float* scale,
-                               float* amax, uint8_t* out, float* mean, float* rstd,
+                               float* amax, void* out, float* mean, float* rstd,
                                hipStream_t stream) {
     const int chunks = hidden / 8;
     if (chunks <= 64)
@@ -351,20 +383,20 @@ size_t ln_bwd_workspace(int64_t rows, int hidden) {
     return (size_t)ln_bwd_blocks(rows) * 2 * (size_t)hidden * sizeof(float);
 }
 
-hipError_t launch_ln_bwd(int64_t rows, int hidden, const float* dy, const void* x,
+hipError_t launch_ln_bwd(int64_t rows, int hidden, const void* dy, bool dy_bf16, const void* x,
                          const float* mean, const float* rstd, const void* gamma, void* dx,
                          float* dgamma, float* dbeta, void* workspace, hipStream_t stream) {
     const int chunks = hidden / 8;
     if (chunks <= 64)
-        return launch_ln_bwd_cpl<1>(rows, hidden, dy, x, mean, rstd, gamma, dx, dgamma, dbeta,
+        return launch_ln_bwd_cpl<1>(rows, hidden, dy, dy_bf16, x, mean, rstd, gamma, dx, dgamma, dbeta,
                                     workspace, stream);
     if (chunks <= 128)
-        return launch_ln_bwd_cpl<2>(rows, hidden, dy, x, mean, rstd, gamma, dx, dgamma, dbeta,
+        return launch_ln_bwd_cpl<2>(rows, hidden, dy, dy_bf16, x, mean, rstd, gamma, dx, dgamma, dbeta,
                                     workspace, stream);
     if (chunks <= 256)
-        return launch_ln_bwd_cpl<4>(rows, hidden, dy, x, mean, rstd, gamma, dx, dgamma, dbeta,
+        return launch_ln_bwd_cpl<4>(rows, hidden, dy, dy_bf16, x, mean, rstd, gamma, dx, dgamma, dbeta,
                                     workspace, stream);
-    return launch_ln_bwd_cpl<8>(rows, hidden, dy, x, mean, rstd, gamma, dx, dgamma, dbeta,
+    return launch_ln_bwd_cpl<8>(rows, hidden, dy, dy_bf16, x, mean, rstd, gamma, dx, dgamma, dbeta,
                                 workspace, stream);
 }
 

@@ -23,7 +23,8 @@ __all__ = [
     "OP_LAYERNORM_BWD", "OP_LN_LINEAR_BWD", "OP_LN_MLP_BWD", "OP_GEMM_DGELU_FP8", "OP_LINEAR_BWD",
     "check_support", "workspace_size", "meta_init",
     "scaling_update", "ln_cast_amax", "cast_amax", "encode_range", "gemm", "gemm_gelu_fp8",
-    "gemm_dgelu", "gemm_dgelu_fp8", "layernorm_bwd", "linear_fwd", "linear_bwd",
+    "gemm_dgelu", "gemm_dgelu_fp8", "layernorm_bwd", "layernorm_fwd", "layernorm_bwd_bf16",
+    "linear_fwd", "linear_bwd",
     "ln_linear_fwd", "ln_linear_bwd", "ln_mlp_fwd", "ln_mlp_bwd", "fwd_fp8", "bwd_fp8",
 ]
 
@@ -314,6 +315,30 @@ def layernorm_bwd(dy, x, mean, rstd, gamma, dx, dgamma, dbeta, stream=None) -> N
     check(lib().fp8ln_layernorm_bwd(rows, hidden, _ptr(dy), _ptr(x), _ptr(mean), _ptr(rstd),
                                     _ptr(gamma), _ptr(dx), _ptr(dgamma), _ptr(dbeta), _ptr(ws),
                                     nbytes, _stream(stream)))
+
+
+def layernorm_fwd(x, gamma, beta, y, mean=None, rstd=None, eps=1e-5, stream=None) -> None:
+    """The plain LayerNorm module's forward: y = LN(x) in bf16."""
+    M, H = x.shape
+    _need(x, torch.bfloat16, (M, H), "x")
+    _need(y, torch.bfloat16, (M, H), "y")
+    _need(gamma, torch.bfloat16, (H,), "gamma")
+    _need(beta, torch.bfloat16, (H,), "beta")
+    _opt(mean, torch.float32, (M,), "mean")
+    _opt(rstd, torch.float32, (M,), "rstd")
+    check(lib().fp8ln_layernorm_fwd(M, H, float(eps), _ptr(x), _ptr(gamma), _ptr(beta), _ptr(y),
+                                    _ptr(mean), _ptr(rstd), _stream(stream)))
+
+
+def layernorm_bwd_bf16(dy, x, mean, rstd, gamma, dx, dgamma, dbeta, stream=None) -> None:
+    """The plain LayerNorm module's backward, for a bf16 incoming gradient."""
+    M, H = x.shape
+    _need(dy, torch.bfloat16, (M, H), "dy")
+    _need(dx, torch.bfloat16, (M, H), "dx")
+    ws = _workspace(workspace_size(OP_LAYERNORM_BWD, M, H), x.device)
+    check(lib().fp8ln_layernorm_bwd_bf16(M, H, _ptr(dy), _ptr(x), _ptr(mean), _ptr(rstd),
+                                         _ptr(gamma), _ptr(dx), _ptr(dgamma), _ptr(dbeta),
+                                         _ptr(ws), ws.numel(), _stream(stream)))
 
 
 # ---- modules ------------------------------------------------------------------

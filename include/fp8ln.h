@@ -307,6 +307,25 @@ int fp8ln_layernorm_bwd(int64_t rows, int64_t hidden, const float* dy, const voi
                         float* dgamma, float* dbeta, void* workspace, size_t workspace_bytes,
                         void* stream);
 
+/* ---- LayerNorm ([T] setup listing, module tour: te.LayerNorm) --------------- */
+
+/* The plain LayerNorm module (no FP8 output): per row of x bf16 [rows][hidden],
+ *   mean = sum x / hidden, var = sum (x - mean)^2 / hidden (biased),
+ *   rstd = 1 / sqrt(var + eps), y = (x - mean) * rstd * gamma + beta
+ * computed in fp32 and rounded to bf16 (nearest-even) into y [rows][hidden].
+ * mean and rstd (fp32 [rows]) are written when not NULL; the backward needs them.
+ * hidden: multiple of 8, at most 8192.  x, y, gamma, beta: 16-byte aligned. */
+int fp8ln_layernorm_fwd(int64_t rows, int64_t hidden, float eps, const void* x,
+                        const void* gamma, const void* beta, void* y, float* mean, float* rstd,
+                        void* stream);
+
+/* fp8ln_layernorm_bwd for a bf16 dy [rows][hidden] (the gradient that reaches a
+ * plain LayerNorm module); same outputs, limits and workspace. */
+int fp8ln_layernorm_bwd_bf16(int64_t rows, int64_t hidden, const void* dy, const void* x,
+                             const float* mean, const float* rstd, const void* gamma, void* dx,
+                             float* dgamma, float* dbeta, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
 /* ---- Linear ([T] setup listing, module tour: te.Linear) --------------------- */
 
 /* out = x W^T + bias with FP8 operands (a Linear layer without the LayerNorm), for

@@ -122,6 +122,14 @@ def ln_cast_amax(x_bits, gamma_bits, beta_bits, eps: float, scale: np.float32, f
     return dict(q=q, amax=amax, y=y, mean=mean, rstd=rstd)
 
 
+def layernorm(x_bits, gamma_bits, beta_bits, eps: float):
+    """The plain LayerNorm module: y = LN(x) rounded once to bf16.  Returns
+    dict(y_bits, y, mean, rstd)."""
+    y, mean, rstd = layernorm_fwd(bf16_to_f64(x_bits), bf16_to_f64(gamma_bits),
+                                  bf16_to_f64(beta_bits), eps)
+    return dict(y_bits=f64_to_bf16_bits(y), y=y, mean=mean, rstd=rstd)
+
+
 def _bias(b_bits, n):
     return np.zeros(n) if b_bits is None else bf16_to_f64(b_bits)
 

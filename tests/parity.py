@@ -126,3 +126,23 @@ def assert_vector_close(gpu, ref, tol, what):
     e = np.linalg.norm(gpu - ref) / max(np.linalg.norm(ref), 1e-300)
     assert e <= tol, f"{what}: relative L2 error {e:.3e} > {tol}"
     return e
+
+
+def compare_bf16(gpu_bits, exact, window):
+    """bf16 outputs of an fp32 computation against the float64 result: each GPU
+    value must lie between the roundings of exact - window and exact + window
+    (rounding is monotone), so it equals the rounding of exact except next to a
+    rounding midpoint, where the neighbour is allowed.  Returns counts."""
+    g = oracle.bf16_to_f64(np.asarray(gpu_bits, dtype=np.uint16).reshape(-1))
+    exact = np.asarray(exact, dtype=np.float64).reshape(-1)
+    window = np.broadcast_to(np.asarray(window, dtype=np.float64).reshape(-1)
+                             if np.size(window) == exact.size else window, exact.shape)
+    lo = oracle.bf16_to_f64(oracle.f64_to_bf16_bits(exact - window))
+    hi = oracle.bf16_to_f64(oracle.f64_to_bf16_bits(exact + window))
+    ref = oracle.bf16_to_f64(oracle.f64_to_bf16_bits(exact))
+    bad = (g < lo) | (g > hi)
+    if bad.any():
+        idx = np.nonzero(bad)[0][:8]
+        raise AssertionError(f"{int(bad.sum())} bf16 values outside the rule; first at "
+                             f"{idx.tolist()}: gpu={g[idx].tolist()} exact={exact[idx].tolist()}")
+    return dict(n=int(exact.size), mismatched=int((g != ref).sum()))

@@ -6,7 +6,8 @@ import torch
 
 import oracle
 from fp8_delayed_scaling_row_amd import inputs, ops
-from parity import (assert_vector_close, compare_codes, ln_window, to_np, to_np_bits)
+from parity import (assert_vector_close, compare_bf16, compare_codes, ln_window, to_np,
+                    to_np_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -194,6 +195,84 @@ def test_layernorm_bwd_matches_oracle(rows, hidden):
     if rows == 0:
         assert torch.all(dgamma == 0) and torch.all(dbeta == 0)
         return
+    gdx = to_np(dx)
+    norms = np.linalg.norm(odx, axis=1)
+    assert np.all(np.abs(gdx - odx).max(axis=1) <= 1e-2 * norms + 1e-30)   # bf16 output
+    assert_vector_close(dgamma.cpu().numpy(), odg, 1e-5, "dgamma")
+    assert_vector_close(dbeta.cpu().numpy(), odb, 1e-5, "dbeta")
+
+
+# ---- the plain LayerNorm module -------------------------------------------------
+
+@pytest.mark.parametrize("rows,hidden", [(1, 8), (37, 768), (256, 768), (300, 2048),
+                                         (64, 8192), (2000, 1000), (0, 768)])
+def test_layernorm_module_fwd_matches_oracle(rows, hidden):
+    """bf16 LayerNorm output: the rounding of the float64 result, or its
+    neighbour where the fp32 result lies within the LayerNorm window of a bf16
+    rounding midpoint; mean and rstd as in the fused LayerNorm's test."""
+    wl = f"lnm/{rows}x{hidden}"
+    x = inputs.normal_bf16((rows, hidden), inputs.seed_for(wl, "x"), std=3.0, mean=1.0)
+    g, b = inputs.layernorm_params(hidden, wl)
+    y = torch.full((rows, hidden), float("nan"), dtype=torch.bfloat16, device="cuda")
+    mean = torch.empty(rows, dtype=torch.float32, device="cuda")
+    rstd = torch.empty(rows, dtype=torch.float32, device="cuda")
+    ops.layernorm_fwd(x.cuda(), g.cuda(), b.cuda(), y, mean, rstd)
+    torch.cuda.synchronize()
+    eps = float(np.float32(1e-5))
+    ref = oracle.layernorm(to_np_bits(x), to_np_bits(g), to_np_bits(b), eps)
+    if rows == 0:
+        return
+    # Rows here have a non-zero mean, so x - mean cancels: an fp32 mean carries an
+    # absolute error that is small against |x| + |mean| but not against |x - mean|.
+    # The window is 1e-6 of the magnitudes entering the computation:
+    # |gamma| rstd (|x| + |mean|) + |beta|, and |y| itself.
+    xv = oracle.bf16_to_f64(to_np_bits(x))
+    gv, bv = (oracle.bf16_to_f64(to_np_bits(t)) for t in (g, b))
+    mag = np.abs(gv) * ref["rstd"][:, None] * (np.abs(xv) + np.abs(ref["mean"])[:, None]) + \
+        np.abs(bv)
+    stats = compare_bf16(to_np_bits(y), ref["y"], 1e-6 * np.maximum(np.abs(ref["y"]), mag))
+    np.testing.assert_allclose(mean.cpu().numpy(), ref["mean"], rtol=1e-5,
+                               atol=1e-6 * np.abs(oracle.bf16_to_f64(to_np_bits(x))).max())
+    np.testing.assert_allclose(rstd.cpu().numpy(), ref["rstd"], rtol=1e-5)
+    assert stats["mismatched"] <= 2 + stats["n"] // 200, stats
+    print(f"layernorm {rows}x{hidden}: {stats}")
+
+
+@pytest.mark.parametrize("rows,hidden", [(1, 8), (37, 768), (2048, 768), (513, 2048),
+                                         (64, 4096), (0, 256)])
+def test_layernorm_module_bwd_bf16_grad(rows, hidden):
+    """The plain LayerNorm backward with a bf16 incoming gradient against the
+    oracle's float64 backward; and on the same values it equals the fp32-gradient
+    entry bit for bit."""
+    wl = f"lnmb/{rows}x{hidden}"
+    x = inputs.normal_bf16((rows, hidden), inputs.seed_for(wl, "x"))
+    g, b = inputs.layernorm_params(hidden, wl)
+    dy = inputs.normal_bf16((rows, hidden), inputs.seed_for(wl, "dy"), std=1e-2)
+    xd, gd, bd = x.cuda(), g.cuda(), b.cuda()
+    mean = torch.empty(rows, dtype=torch.float32, device="cuda")
+    rstd = torch.empty(rows, dtype=torch.float32, device="cuda")
+    y = torch.empty((rows, hidden), dtype=torch.bfloat16, device="cuda")
+    ops.layernorm_fwd(xd, gd, bd, y, mean, rstd)
+    outs = []
+    for dyd in (dy.cuda(), dy.float().cuda()):
+        dx = torch.empty((rows, hidden), dtype=torch.bfloat16, device="cuda")
+        dgamma = torch.empty(hidden, dtype=torch.float32, device="cuda")
+        dbeta = torch.empty(hidden, dtype=torch.float32, device="cuda")
+        if dyd.dtype == torch.bfloat16:
+            ops.layernorm_bwd_bf16(dyd, xd, mean, rstd, gd, dx, dgamma, dbeta)
+        else:
+            ops.layernorm_bwd(dyd, xd, mean, rstd, gd, dx, dgamma, dbeta)
+        outs.append((dx, dgamma, dbeta))
+    torch.cuda.synchronize()
+    for a, c in zip(*outs):
+        assert torch.equal(a, c)
+    dx, dgamma, dbeta = outs[0]
+    if rows == 0:
+        assert torch.all(dgamma == 0) and torch.all(dbeta == 0)
+        return
+    m64, r64 = mean.cpu().numpy().astype(np.float64), rstd.cpu().numpy().astype(np.float64)
+    xv, gv = oracle.bf16_to_f64(to_np_bits(x)), oracle.bf16_to_f64(to_np_bits(g))
+    odx, odg, odb = oracle.layernorm_bwd(oracle.bf16_to_f64(to_np_bits(dy)), xv, gv, m64, r64)
     gdx = to_np(dx)
     norms = np.linalg.norm(odx, axis=1)
     assert np.all(np.abs(gdx - odx).max(axis=1) <= 1e-2 * norms + 1e-30)   # bf16 output

@@ -132,3 +132,23 @@ def test_gelu_erf_grad_matches_finite_differences_and_autograd():
     ht = torch.from_numpy(h.copy()).requires_grad_(True)
     F.gelu(ht).sum().backward()
     np.testing.assert_allclose(oracle.gelu_erf_grad(h), ht.grad.numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_layernorm_module_rounds_the_float64_result_once():
+    """The plain LayerNorm module's bf16 output is one nearest-even rounding of
+    the float64 LayerNorm: it matches torch's float64 layer_norm converted to
+    bf16 through float32 wherever that double rounding is harmless, i.e. the
+    float64 value is not within a float32 ulp of a bf16 midpoint."""
+    rng = np.random.default_rng(5)
+    H = 96
+    x = oracle.f64_to_bf16_bits(rng.normal(1.0, 3.0, size=(40, H)))
+    g = oracle.f64_to_bf16_bits(1 + 0.1 * rng.normal(size=H))
+    b = oracle.f64_to_bf16_bits(0.1 * rng.normal(size=H))
+    out = oracle.layernorm(x, g, b, 1e-5)
+    t = lambda bits: torch.from_numpy(oracle.bf16_to_f64(bits))
+    ref = F.layer_norm(t(x), (H,), t(g), t(b), 1e-5)
+    np.testing.assert_allclose(out["y"], ref.numpy(), rtol=1e-12, atol=1e-12)
+    tb = ref.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert (out["y_bits"] == tb).mean() > 0.999
+    assert np.all(np.abs(oracle.bf16_to_f64(out["y_bits"]) - ref.numpy())
+                  <= 2.0 ** -8 * np.abs(ref.numpy()))
