@@ -37,6 +37,8 @@ OP_LN_LINEAR_BWD = 2
 OP_LN_MLP_BWD = 3
 OP_GEMM_DGELU_FP8 = 4
 OP_LINEAR_BWD = 5
+OP_LN_LINEAR_BWD_BF16 = 6
+OP_TRANSPOSE_BF16 = 7
 
 
 class Recipe(C.Structure):
@@ -90,6 +92,15 @@ SIGNATURES = {
     "fp8ln_gemm_dgelu_fp8": (C.c_int, [_I64, _I64, _I64, _P, _I32, _P, _I32, _P, _P, _P, _I32, _P,
                                        _P, _P, _P, _P, _I32, _P, _SZ, _P]),
     "fp8ln_layernorm_bwd": (C.c_int, [_I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "fp8ln_gemm_bf16": (C.c_int, [_I64, _I64, _I64, _P, _P, _P, _I32, _P, _P]),
+    "fp8ln_gemm_gelu_bf16": (C.c_int, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _I32, _P]),
+    "fp8ln_transpose_bf16": (C.c_int, [_I64, _I64, _P, _P, _P, _P, _SZ, _P]),
+    "fp8ln_ln_linear_fwd_bf16": (C.c_int, [_I64, _I64, _I64, C.c_float, _P, _P, _P, _P, _P, _P,
+                                           _P, _P, _P, _P]),
+    "fp8ln_ln_linear_bwd_bf16": (C.c_int, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                           _P, _P, _P, _P, _SZ, _P]),
+    "fp8ln_ln_mlp_fwd_bf16": (C.c_int, [_I64, _I64, _I64, C.c_float, _I32, _P, _P, _P, _P, _P,
+                                        _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "fp8ln_layernorm_fwd": (C.c_int, [_I64, _I64, C.c_float, _P, _P, _P, _P, _P, _P, _P]),
     "fp8ln_layernorm_bwd_bf16": (C.c_int, [_I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
                                            _P]),

@@ -186,6 +186,30 @@ LinearOnlyWs linear_only_ws(void* base, int64_t M, int64_t K, int64_t N) {
     return w;
 }
 
+// BF16 LayerNormLinear backward: transposed dy, LN output and weight, fp32 dLN.
+struct LinearBf16Ws {
+    void* dy_t;      // bf16 [N][M]
+    void* ln_t;      // bf16 [K][M]
+    void* w_t;       // bf16 [K][N]
+    float* dln;      // fp32 [M][K]
+    void* sum_ws;    // column-sum partials of dy
+    void* ln_ws;
+    size_t bytes;
+};
+
+LinearBf16Ws linear_bf16_ws(void* base, int64_t M, int64_t K, int64_t N) {
+    Carver c{(uint8_t*)base};
+    LinearBf16Ws w;
+    w.dy_t = c.take((size_t)(M * N) * 2);
+    w.ln_t = c.take((size_t)(M * K) * 2);
+    w.w_t = c.take((size_t)(K * N) * 2);
+    w.dln = (float*)c.take((size_t)(M * K) * sizeof(float));
+    w.sum_ws = c.take(transpose_b16_workspace(M, N));
+    w.ln_ws = c.take(ln_bwd_workspace(M, (int)K));
+    w.bytes = c.used;
+    return w;
+}
+
 struct MlpWs {
     uint8_t* dy_q;
     uint8_t* dy_qt;
@@ -211,6 +235,18 @@ MlpWs mlp_ws(void* base, int64_t M, int64_t H, int64_t F) {
     w.ln_ws = c.take(ln_bwd_workspace(M, (int)H));
     w.bytes = c.used;
     return w;
+}
+
+int check_bf16_module(int64_t M, int64_t K, int64_t N, float eps) {
+    REQUIRE(M >= 0, "tokens < 0");
+    REQUIRE(eps > 0.0f && eps <= 3.402823466e38f, "eps must be a positive finite number");
+    if (K <= 0 || K % 16 != 0 || K > 8192)
+        return fail(FP8LN_ERR_UNSUPPORTED, "hidden %lld must be a multiple of 16 in 16..8192",
+                    (long long)K);
+    if (N <= 0 || N % 16 != 0)
+        return fail(FP8LN_ERR_UNSUPPORTED, "output width %lld must be a positive multiple of 16",
+                    (long long)N);
+    return FP8LN_OK;
 }
 
 GemmParams gemm_params(int64_t M, int64_t N, int64_t K, const uint8_t* A, int afmt,
@@ -263,6 +299,9 @@ size_t fp8ln_workspace_size(int32_t op, int64_t a, int64_t b, int64_t c) {
         case FP8LN_OP_LAYERNORM_BWD: return ln_bwd_workspace(a, (int)b);
         case FP8LN_OP_GEMM_DGELU_FP8: return dgelu_workspace(a, b);
         case FP8LN_OP_LINEAR_BWD: return c > 0 ? linear_only_ws(nullptr, a, b, c).bytes : 0;
+        case FP8LN_OP_LN_LINEAR_BWD_BF16:
+            return b > 0 && c > 0 ? linear_bf16_ws(nullptr, a, b, c).bytes : 0;
+        case FP8LN_OP_TRANSPOSE_BF16: return transpose_b16_workspace(a, b);
         case FP8LN_OP_LN_LINEAR_BWD: return c > 0 ? linear_ws(nullptr, a, b, c).bytes : 0;
         case FP8LN_OP_LN_MLP_BWD: return c > 0 ? mlp_ws(nullptr, a, b, c).bytes : 0;
         default: return 0;
@@ -529,6 +568,196 @@ int fp8ln_layernorm_bwd(int64_t rows, int64_t hidden, const float* dy, const voi
     FP8LN_TRY(launch_ln_bwd(rows, (int)hidden, dy, false, x, mean, rstd, gamma, dx, dgamma, dbeta,
                             workspace, as_stream(stream)),
               "layernorm_bwd launch");
+    return FP8LN_OK;
+}
+
+// ---- BF16 path ------------------------------------------------------------------
+
+int fp8ln_gemm_bf16(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
+                    const void* bias, int32_t out_dtype, void* out, void* stream) {
+    REQUIRE(M >= 0 && N >= 0 && K >= 0, "negative size");
+    REQUIRE(out_dtype == FP8LN_DTYPE_BF16 || out_dtype == FP8LN_DTYPE_F32, "out_dtype %d invalid",
+            out_dtype);
+    if (N % 16 != 0 || K % 16 != 0)
+        return fail(FP8LN_ERR_UNSUPPORTED, "N and K must be multiples of 16 (N=%lld K=%lld)",
+                    (long long)N, (long long)K);
+    if (M > 0 && N > 0) {
+        REQUIRE_PTR(out); REQUIRE_ALIGNED(out);
+        if (K > 0) { REQUIRE_PTR(A); REQUIRE_PTR(B); REQUIRE_ALIGNED(A); REQUIRE_ALIGNED(B); }
+        if (bias) REQUIRE_ALIGNED(bias);
+    }
+    REQUIRE(!(bias && out_dtype == FP8LN_DTYPE_F32), "bias is only applied to bf16 outputs");
+    int s = check_current_device();
+    if (s) return s;
+    GemmParams p = gemm_params(M, N, K, (const uint8_t*)A, kOpBf16, (const uint8_t*)B, kOpBf16,
+                               nullptr, nullptr,
+                               out_dtype == FP8LN_DTYPE_BF16 ? kEpiBf16Bias : kEpiF32);
+    p.bias = (const uint16_t*)bias;
+    p.out = out;
+    FP8LN_TRY(launch_gemm(p, as_stream(stream)), "gemm launch");
+    return FP8LN_OK;
+}
+
+int fp8ln_gemm_gelu_bf16(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
+                         const void* bias, void* h_out, void* out, int32_t activation,
+                         void* stream) {
+    REQUIRE(activation == FP8LN_GELU_TANH || activation == FP8LN_GELU_ERF,
+            "activation %d invalid", activation);
+    REQUIRE(M >= 0 && N >= 0 && K >= 0, "negative size");
+    if (N % 16 != 0 || K % 16 != 0)
+        return fail(FP8LN_ERR_UNSUPPORTED, "N and K must be multiples of 16 (N=%lld K=%lld)",
+                    (long long)N, (long long)K);
+    if (M > 0 && N > 0) {
+        REQUIRE_PTR(out); REQUIRE_ALIGNED(out);
+        if (h_out) REQUIRE_ALIGNED(h_out);
+        if (K > 0) { REQUIRE_PTR(A); REQUIRE_PTR(B); REQUIRE_ALIGNED(A); REQUIRE_ALIGNED(B); }
+        if (bias) REQUIRE_ALIGNED(bias);
+    }
+    int s = check_current_device();
+    if (s) return s;
+    GemmParams p = gemm_params(M, N, K, (const uint8_t*)A, kOpBf16, (const uint8_t*)B, kOpBf16,
+                               nullptr, nullptr, kEpiGeluBf16);
+    p.bias = (const uint16_t*)bias;
+    p.h_out = (uint16_t*)h_out;
+    p.out = out;
+    p.gelu_erf = activation == FP8LN_GELU_ERF;
+    FP8LN_TRY(launch_gemm(p, as_stream(stream)), "gemm launch");
+    return FP8LN_OK;
+}
+
+int fp8ln_transpose_bf16(int64_t rows, int64_t cols, const void* in, void* out, float* colsum,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+    REQUIRE(rows >= 0 && cols >= 0, "negative size");
+    if (rows % 8 != 0 || cols % 8 != 0)
+        return fail(FP8LN_ERR_UNSUPPORTED, "rows and cols must be multiples of 8");
+    if (rows > 0 && cols > 0) {
+        REQUIRE_PTR(in); REQUIRE_PTR(out); REQUIRE_ALIGNED(in); REQUIRE_ALIGNED(out);
+    }
+    if (colsum) {
+        const size_t need = transpose_b16_workspace(rows, cols);
+        REQUIRE(need == 0 || (workspace && workspace_bytes >= need),
+                "column sums need %zu bytes of workspace", need);
+    }
+    int s = check_current_device();
+    if (s) return s;
+    FP8LN_TRY(launch_transpose_b16(rows, cols, in, out, colsum, workspace, as_stream(stream)),
+              "transpose launch");
+    return FP8LN_OK;
+}
+
+int fp8ln_ln_linear_fwd_bf16(int64_t tokens, int64_t in_features, int64_t out_features,
+                             float eps, const void* x, const void* gamma, const void* beta,
+                             const void* weight, const void* bias, void* out, void* ln_out,
+                             float* mean, float* rstd, void* stream) {
+    const int64_t M = tokens, K = in_features, N = out_features;
+    int s = check_bf16_module(M, K, N, eps);
+    if (s) return s;
+    REQUIRE_PTR(gamma); REQUIRE_PTR(beta); REQUIRE_PTR(weight);
+    REQUIRE_ALIGNED(gamma); REQUIRE_ALIGNED(beta); REQUIRE_ALIGNED(weight);
+    if (bias) REQUIRE_ALIGNED(bias);
+    if (M > 0) {
+        REQUIRE_PTR(x); REQUIRE_PTR(out); REQUIRE_PTR(ln_out);
+        REQUIRE_ALIGNED(x); REQUIRE_ALIGNED(out); REQUIRE_ALIGNED(ln_out);
+    }
+    if ((s = check_current_device())) return s;
+    if (M == 0) return FP8LN_OK;
+    hipStream_t st = as_stream(stream);
+    FP8LN_TRY(launch_ln_cast_amax(M, (int)K, x, gamma, beta, eps, kLnOutBf16, nullptr, nullptr,
+                                  ln_out, mean, rstd, st),
+              "layernorm launch");
+    GemmParams p = gemm_params(M, N, K, (const uint8_t*)ln_out, kOpBf16, (const uint8_t*)weight,
+                               kOpBf16, nullptr, nullptr, kEpiBf16Bias);
+    p.bias = (const uint16_t*)bias;
+    p.out = out;
+    FP8LN_TRY(launch_gemm(p, st), "gemm launch");
+    return FP8LN_OK;
+}
+
+int fp8ln_ln_linear_bwd_bf16(int64_t tokens, int64_t in_features, int64_t out_features,
+                             const void* dy, const void* x, const void* gamma,
+                             const void* weight, const void* ln_out, const float* mean,
+                             const float* rstd, void* dx, float* dgamma, float* dbeta,
+                             float* dweight, float* dbias, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    const int64_t M = tokens, K = in_features, N = out_features;
+    int s = check_bf16_module(M, K, N, 1.0f);
+    if (s) return s;
+    if (M % 16 != 0)
+        return fail(FP8LN_ERR_UNSUPPORTED, "tokens %lld must be a multiple of 16", (long long)M);
+    if (K > 4096)
+        return fail(FP8LN_ERR_UNSUPPORTED, "in_features %lld: the backward takes at most 4096",
+                    (long long)K);
+    REQUIRE_PTR(gamma); REQUIRE_PTR(weight); REQUIRE_PTR(dgamma); REQUIRE_PTR(dbeta);
+    REQUIRE_PTR(dweight);
+    REQUIRE_ALIGNED(gamma); REQUIRE_ALIGNED(weight); REQUIRE_ALIGNED(dweight);
+    if (M > 0) {
+        REQUIRE_PTR(dy); REQUIRE_PTR(x); REQUIRE_PTR(ln_out); REQUIRE_PTR(mean);
+        REQUIRE_PTR(rstd); REQUIRE_PTR(dx);
+        REQUIRE_ALIGNED(dy); REQUIRE_ALIGNED(x); REQUIRE_ALIGNED(ln_out); REQUIRE_ALIGNED(dx);
+    }
+    const LinearBf16Ws need = linear_bf16_ws(nullptr, M, K, N);
+    REQUIRE(workspace && workspace_bytes >= need.bytes,
+            "ln_linear_bwd_bf16 needs %zu bytes of workspace", need.bytes);
+    REQUIRE_ALIGNED(workspace);
+    if ((s = check_current_device())) return s;
+    hipStream_t st = as_stream(stream);
+    const LinearBf16Ws w = linear_bf16_ws(workspace, M, K, N);
+    FP8LN_TRY(launch_transpose_b16(M, N, dy, w.dy_t, dbias, w.sum_ws, st), "dy transpose");
+    FP8LN_TRY(launch_transpose_b16(N, K, weight, w.w_t, nullptr, nullptr, st), "w transpose");
+    FP8LN_TRY(launch_transpose_b16(M, K, ln_out, w.ln_t, nullptr, nullptr, st), "ln transpose");
+    // dgrad: dLN[M][K] = dy[M][N] . (w_t[K][N])^T
+    GemmParams dg = gemm_params(M, K, N, (const uint8_t*)dy, kOpBf16, (const uint8_t*)w.w_t,
+                                kOpBf16, nullptr, nullptr, kEpiF32);
+    dg.out = w.dln;
+    FP8LN_TRY(launch_gemm(dg, st), "dgrad launch");
+    // wgrad: dW[N][K] = dy_t[N][M] . (ln_t[K][M])^T
+    GemmParams wg = gemm_params(N, K, M, (const uint8_t*)w.dy_t, kOpBf16, (const uint8_t*)w.ln_t,
+                                kOpBf16, nullptr, nullptr, kEpiF32);
+    wg.out = dweight;
+    FP8LN_TRY(launch_gemm(wg, st), "wgrad launch");
+    FP8LN_TRY(launch_ln_bwd(M, (int)K, w.dln, false, x, mean, rstd, gamma, dx, dgamma, dbeta,
+                            w.ln_ws, st),
+              "layernorm backward launch");
+    return FP8LN_OK;
+}
+
+int fp8ln_ln_mlp_fwd_bf16(int64_t tokens, int64_t hidden, int64_t ffn, float eps,
+                          int32_t activation, const void* x, const void* gamma, const void* beta,
+                          const void* w1, const void* b1, const void* w2, const void* b2,
+                          void* out, void* ln_out, void* h, void* g, float* mean, float* rstd,
+                          void* stream) {
+    const int64_t M = tokens, H = hidden, F = ffn;
+    int s = check_bf16_module(M, H, F, eps);
+    if (s) return s;
+    REQUIRE(activation == FP8LN_GELU_TANH || activation == FP8LN_GELU_ERF,
+            "activation %d invalid", activation);
+    REQUIRE_PTR(gamma); REQUIRE_PTR(beta); REQUIRE_PTR(w1); REQUIRE_PTR(w2);
+    REQUIRE_ALIGNED(gamma); REQUIRE_ALIGNED(beta); REQUIRE_ALIGNED(w1); REQUIRE_ALIGNED(w2);
+    if (b1) REQUIRE_ALIGNED(b1);
+    if (b2) REQUIRE_ALIGNED(b2);
+    if (M > 0) {
+        REQUIRE_PTR(x); REQUIRE_PTR(out); REQUIRE_PTR(ln_out); REQUIRE_PTR(g);
+        REQUIRE_ALIGNED(x); REQUIRE_ALIGNED(out); REQUIRE_ALIGNED(ln_out); REQUIRE_ALIGNED(g);
+        if (h) REQUIRE_ALIGNED(h);
+    }
+    if ((s = check_current_device())) return s;
+    if (M == 0) return FP8LN_OK;
+    hipStream_t st = as_stream(stream);
+    FP8LN_TRY(launch_ln_cast_amax(M, (int)H, x, gamma, beta, eps, kLnOutBf16, nullptr, nullptr,
+                                  ln_out, mean, rstd, st),
+              "layernorm launch");
+    GemmParams p1 = gemm_params(M, F, H, (const uint8_t*)ln_out, kOpBf16, (const uint8_t*)w1,
+                                kOpBf16, nullptr, nullptr, kEpiGeluBf16);
+    p1.bias = (const uint16_t*)b1;
+    p1.h_out = (uint16_t*)h;
+    p1.out = g;
+    p1.gelu_erf = activation == FP8LN_GELU_ERF;
+    FP8LN_TRY(launch_gemm(p1, st), "fc1 launch");
+    GemmParams p2 = gemm_params(M, H, F, (const uint8_t*)g, kOpBf16, (const uint8_t*)w2, kOpBf16,
+                                nullptr, nullptr, kEpiBf16Bias);
+    p2.bias = (const uint16_t*)b2;
+    p2.out = out;
+    FP8LN_TRY(launch_gemm(p2, st), "fc2 launch");
     return FP8LN_OK;
 }
 

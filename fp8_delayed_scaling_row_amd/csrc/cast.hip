@@ -174,6 +174,48 @@ __global__ __launch_bounds__(kThreads) void transpose_u8_kernel(const uint8_t* _
                  *reinterpret_cast<const uint4*>(&tile[lr][lc]));
 }
 
+// in [rows][cols] -> out [cols][rows] for 16-bit elements (bf16), 64 x 64 tiles
+// (rows % 8 == 0, cols % 8 == 0).  With partial set, row tile y also writes the
+// fp32 column sums of its 64 rows to partial[y][cols], summed in row order.
+__global__ __launch_bounds__(kThreads) void transpose_b16_kernel(const uint16_t* __restrict__ in,
+                                                                 int64_t rows, int64_t cols,
+                                                                 uint16_t* __restrict__ out,
+                                                                 float* __restrict__ partial) {
+    __shared__ uint16_t tile[kTile][kTile + 2];
+    const int t = threadIdx.x;
+    const int64_t r0 = (int64_t)blockIdx.y * kTile;
+    const int64_t c0 = (int64_t)blockIdx.x * kTile;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int u = t + h * kThreads;        // 64 rows x 8 chunks of 8 elements
+        const int lr = u / 8, lc = (u % 8) * 8;
+        uint4 w = make_uint4(0, 0, 0, 0);
+        if (r0 + lr < rows && c0 + lc < cols)
+            w = load_nt(reinterpret_cast<const uint4*>(in + (r0 + lr) * cols + c0 + lc));
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) tile[lr][lc + i] = (uint16_t)(ws[i / 2] >> (16 * (i % 2)));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int u = t + h * kThreads;        // 64 output rows x 8 chunks
+        const int oc = u / 8, orr = (u % 8) * 8;
+        uint32_t v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            v[i] = (uint32_t)tile[orr + 2 * i][oc] | ((uint32_t)tile[orr + 2 * i + 1][oc] << 16);
+        if (c0 + oc < cols && r0 + orr < rows)
+            store_nt(reinterpret_cast<uint4*>(out + (c0 + oc) * rows + r0 + orr),
+                     make_uint4(v[0], v[1], v[2], v[3]));
+    }
+    if (partial && t < kTile && c0 + t < cols) {
+        float a = 0.0f;
+        for (int r = 0; r < kTile; ++r) a += __uint_as_float((uint32_t)tile[r][t] << 16);
+        partial[(int64_t)blockIdx.y * cols + c0 + t] = a;
+    }
+}
+
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void encode_range_kernel(uint32_t start, int64_t count,
                                                                 uint8_t* __restrict__ out) {
@@ -236,6 +278,27 @@ hipError_t launch_transpose_u8(int64_t rows, int64_t cols, const uint8_t* in, ui
     const dim3 grid((unsigned)((cols + kTile - 1) / kTile), (unsigned)((rows + kTile - 1) / kTile));
     hipLaunchKernelGGL(transpose_u8_kernel, grid, dim3(kThreads), 0, stream, in, rows, cols, out);
     return hipGetLastError();
+}
+
+size_t transpose_b16_workspace(int64_t rows, int64_t cols) {
+    return (size_t)((rows + kTile - 1) / kTile) * (size_t)cols * sizeof(float);
+}
+
+hipError_t launch_transpose_b16(int64_t rows, int64_t cols, const void* in, void* out,
+                                float* colsum, void* workspace, hipStream_t stream) {
+    if (cols == 0) return hipSuccess;
+    float* partial = colsum ? (float*)workspace : nullptr;
+    if (rows > 0) {
+        const dim3 grid((unsigned)((cols + kTile - 1) / kTile),
+                        (unsigned)((rows + kTile - 1) / kTile));
+        hipLaunchKernelGGL(transpose_b16_kernel, grid, dim3(kThreads), 0, stream,
+                           (const uint16_t*)in, rows, cols, (uint16_t*)out, partial);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (!colsum) return hipSuccess;
+    return launch_sum_partials(partial, (rows + kTile - 1) / kTile, cols, colsum, nullptr, cols,
+                               stream);
 }
 
 hipError_t launch_encode_range(uint32_t start, int64_t count, int fp8, uint8_t* out,

@@ -38,6 +38,8 @@ namespace fp8ln {
 namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int BKS = 64;        // bytes of K per pipeline stage
@@ -51,9 +53,11 @@ __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r ^ (r >> 3)) & 
 // GELU, tanh form: gelu(h) = h/2 (1 + t), t = tanh(k0 (h + k1 h^3)), with
 // k0 = sqrt(2 / pi), k1 = 0.044715, and its derivative
 //     gelu'(h) = (1 + t)/2 + h/2 (1 - t^2) k0 (1 + 3 k1 h^2).
-// t = 1 - 2 / (1 + 2^v) with v = 2 log2(e) k0 h (1 + k1 h^2); 2^v and the
-// reciprocal are the hardware's (about one ulp each), which keeps the whole
-// function near 1e-7 relative to |h| and costs about a dozen operations.
+// With v = 2 log2(e) k0 h (1 + k1 h^2): (1 + t)/2 = 1 / (1 + 2^-v), so
+// gelu(h) = h / (1 + 2^-v), which has no cancellation for negative h (the
+// form h/2 + h/2 t loses the relative accuracy of small negative outputs), and
+// t = 1 - 2 / (1 + 2^v) for the derivative.  2^v and the reciprocal are the
+// hardware's (about one ulp each).
 constexpr float kGeluK0 = 0.7978845608028654f;                 // sqrt(2 / pi)
 constexpr float kGeluK1 = 0.044715f;
 constexpr float kGeluV0 = 2.0f * 1.4426950408889634f * 0.7978845608028654f;   // 2 log2(e) k0
@@ -66,16 +70,15 @@ __device__ __forceinline__ float gelu_tanh_t(float h, float h2) {
 }
 
 __device__ __forceinline__ float gelu_f(float h) {
-    const float t = gelu_tanh_t(h, h * h);
-    const float hh = 0.5f * h;
-    return fmaf(hh, t, hh);
+    const float nv = h * fmaf(-kGeluV1, h * h, -kGeluV0);   // -v
+    return h * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(nv));
 }
 
-// GELU, erf form: gelu(h) = h/2 (1 + erf(h / sqrt 2)),
+// GELU, erf form: gelu(h) = h/2 (1 + erf(h / sqrt 2)) = h/2 erfc(-h / sqrt 2)
+// (erfc keeps small negative outputs accurate), and
 // gelu'(h) = (1 + erf(h / sqrt 2)) / 2 + h exp(-h^2 / 2) / sqrt(2 pi).
 __device__ __forceinline__ float gelu_erf_f(float h) {
-    const float hh = 0.5f * h;
-    return fmaf(hh, erff(h * 0.70710678118654752f), hh);
+    return 0.5f * h * erfcf(h * -0.70710678118654752f);
 }
 
 __device__ __forceinline__ float gelu_erf_grad_f(float h) {
@@ -290,6 +293,33 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p) {
         v8i af[TM];
 #pragma unroll
         for (int i = 0; i < TM; ++i) af[i] = frag(sa, wm * WM + 32 * i + fr);
+        if constexpr (FA == kOpBf16) {
+            // bf16: a stage holds 32 elements of K per row, two 32x32x16 MFMAs.
+            // Each lane splits its 32-byte fragment into halves h = 0, 1; MFMA h
+            // sums over the elements of half h of every lane.  A and B split
+            // alike, so every k meets its partner exactly once.
+            static_assert(FB == kOpBf16, "bf16 takes bf16");
+            v8i bfr[TN];
+#pragma unroll
+            for (int j = 0; j < TN; ++j) bfr[j] = frag(sb, wn * WN + 32 * j + fr);
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int i = 0; i < TM; ++i) {
+                        const v8i& bv = bfr[j];
+                        const v8i& av = af[i];
+                        const v4i b4 = h ? v4i{bv[4], bv[5], bv[6], bv[7]}
+                                         : v4i{bv[0], bv[1], bv[2], bv[3]};
+                        const v4i a4 = h ? v4i{av[4], av[5], av[6], av[7]}
+                                         : v4i{av[0], av[1], av[2], av[3]};
+                        acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            __builtin_bit_cast(v8bf, b4), __builtin_bit_cast(v8bf, a4),
+                            acc[j][i], 0, 0, 0);
+                    }
+            return;
+        }
         // D[n][m] = sum_k B[n][k] A[m][k]: the B rows are the MFMA's first operand
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
@@ -358,7 +388,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p) {
     auto ring = [&](int sidx) -> lds8* {
         return sidx == 0 ? (lds8*)st0 : sidx == 1 ? (lds8*)st1 : sidx == 2 ? (lds8*)st2 : (lds8*)st3;
     };
-    const float alpha = (*p.sinv_a) * (*p.sinv_b);
+    const float alpha = FA == kOpBf16 ? 1.0f : (*p.sinv_a) * (*p.sinv_b);   // bf16: no scales
     const int row_w = wm * WM + fr;      // tile row of this lane's i = 0 values
     const int col_w = wn * WN + 4 * fh;  // tile column of this lane's j = q = 0 values
 
@@ -409,7 +439,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p) {
             for (int q = 0; q < 4; ++q) {
                 const int64_t gn = n0 + col_w + 32 * j + 8 * q;
                 float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-                if constexpr (EPI == kEpiBf16Bias || EPI == kEpiGeluFp8) {
+                if constexpr (EPI == kEpiBf16Bias || EPI == kEpiGeluFp8 || EPI == kEpiGeluBf16) {
                     if (p.bias && gn < N) {
                         const uint2 bw = *reinterpret_cast<const uint2*>(p.bias + gn);
                         bv[0] = bf16_lo(bw.x); bv[1] = bf16_hi(bw.x);
@@ -422,7 +452,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const float x = acc[j][i][4 * q + e];
-                        if constexpr (EPI == kEpiBf16Bias || EPI == kEpiGeluFp8)
+                        if constexpr (EPI == kEpiBf16Bias || EPI == kEpiGeluFp8 ||
+                                      EPI == kEpiGeluBf16)
                             acc[j][i][4 * q + e] = ok ? fmaf(x, alpha, bv[e]) : 0.0f;
                         else
                             acc[j][i][4 * q + e] = ok ? x * alpha : 0.0f;
@@ -482,28 +513,41 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p) {
         }
     }
 
-    if constexpr (EPI == kEpiBf16Bias || EPI == kEpiGeluFp8) {
+    // bf16 rows of the tile through the ring
+    auto bf16_out = [&](uint16_t* dst) {
+        using G = Staging<BN * 2, STAGE>;
+        static_assert(BM <= NS * G::RPS, "bf16 staging");
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int lr = row_w + 32 * i;
+                    const int lc = col_w + 32 * j + 8 * q;
+                    lds_st(G::at(ring, lr, lc / 8) + 8 * fh,
+                           u32x2{pack_bf16x2(acc[j][i][4 * q], acc[j][i][4 * q + 1]),
+                                 pack_bf16x2(acc[j][i][4 * q + 2], acc[j][i][4 * q + 3])});
+                }
+        __syncthreads();
+        G::template copy_out<BM, NT>(ring, t, (uint8_t*)(dst + m0 * N + n0), N * 2, M - m0,
+                                    (N - n0) * 2);
+        __syncthreads();
+    };
+    if constexpr (EPI == kEpiBf16Bias || EPI == kEpiGeluFp8 || EPI == kEpiGeluBf16) {
         uint16_t* hdst = EPI == kEpiBf16Bias ? (uint16_t*)p.out : p.h_out;
-        if (hdst) {
-            using G = Staging<BN * 2, STAGE>;
-            static_assert(BM <= NS * G::RPS, "bf16 staging");
+        if (hdst) bf16_out(hdst);
+    }
+    if constexpr (EPI == kEpiGeluBf16) {
+        // rows and columns outside the product hold 0 and gelu(0) = 0
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int j = 0; j < TN; ++j)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int lr = row_w + 32 * i;
-                        const int lc = col_w + 32 * j + 8 * q;
-                        lds_st(G::at(ring, lr, lc / 8) + 8 * fh,
-                               u32x2{pack_bf16x2(acc[j][i][4 * q], acc[j][i][4 * q + 1]),
-                                     pack_bf16x2(acc[j][i][4 * q + 2], acc[j][i][4 * q + 3])});
-                    }
-            __syncthreads();
-            G::template copy_out<BM, NT>(ring, t, (uint8_t*)(hdst + m0 * N + n0), N * 2, M - m0,
-                                        (N - n0) * 2);
-            __syncthreads();
-        }
+                for (int r = 0; r < 16; ++r)
+                    acc[j][i][r] = p.gelu_erf ? gelu_erf_f(acc[j][i][r]) : gelu_f(acc[j][i][r]);
+        bf16_out((uint16_t*)p.out);
     }
 
     if constexpr (EPI == kEpiGeluFp8 || EPI == kEpiDGeluFp8) {
@@ -715,8 +759,24 @@ int64_t gemm_partial_rows(int64_t M, int64_t N, int64_t K) {
     return pick_tile(M, N, K, kEpiDGeluFp8) == kTile256 ? cdiv(M, 256) : cdiv(M, 128);
 }
 
+static hipError_t launch_gemm_bf16(const GemmParams& p, hipStream_t stream) {
+    GemmParams q = p;
+    q.K = 2 * p.K;   // the tiles count K in bytes
+    switch (p.epilogue) {
+        case kEpiBf16Bias: return launch_typed<kOpBf16, kOpBf16, kEpiBf16Bias, kE4M3>(q, stream);
+        case kEpiF32: return launch_typed<kOpBf16, kOpBf16, kEpiF32, kE4M3>(q, stream);
+        case kEpiGeluBf16: return launch_typed<kOpBf16, kOpBf16, kEpiGeluBf16, kE4M3>(q, stream);
+        case kEpiDGeluF32: return launch_typed<kOpBf16, kOpBf16, kEpiDGeluF32, kE4M3>(q, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_gemm(const GemmParams& p, hipStream_t stream) {
     if (p.M == 0 || p.N == 0) return hipSuccess;
+    if (p.a_fp8 == kOpBf16 || p.b_fp8 == kOpBf16) {
+        if (p.a_fp8 != p.b_fp8) return hipErrorInvalidValue;
+        return launch_gemm_bf16(p, stream);
+    }
     if (p.a_fp8 == kE4M3 && p.b_fp8 == kE4M3) return launch_epi<kE4M3, kE4M3>(p, stream);
     if (p.a_fp8 == kE5M2 && p.b_fp8 == kE4M3) return launch_epi<kE5M2, kE4M3>(p, stream);
     if (p.a_fp8 == kE4M3 && p.b_fp8 == kE5M2) return launch_epi<kE4M3, kE5M2>(p, stream);

@@ -46,6 +46,11 @@ hipError_t launch_transpose_u8(int64_t rows, int64_t cols, const uint8_t* in, ui
                                hipStream_t stream);
 hipError_t launch_encode_range(uint32_t start, int64_t count, int fp8, uint8_t* out,
                                hipStream_t stream);
+// bf16 [rows][cols] -> [cols][rows] (rows, cols % 8 == 0); colsum (optional) gets
+// the fp32 column sums and needs transpose_b16_workspace bytes of workspace.
+size_t transpose_b16_workspace(int64_t rows, int64_t cols);
+hipError_t launch_transpose_b16(int64_t rows, int64_t cols, const void* in, void* out,
+                                float* colsum, void* workspace, hipStream_t stream);
 
 // gemm.hip
 enum GemmEpilogue : int {
@@ -54,13 +59,19 @@ enum GemmEpilogue : int {
     kEpiGeluFp8 = 2,    // h = acc * alpha + bias -> h bf16; g = gelu(h) -> FP8 (+T), amax
     kEpiDGeluF32 = 3,   // out fp32 = acc * alpha * gelu'(h)
     kEpiDGeluFp8 = 4,   // d = acc * alpha * gelu'(h) -> FP8 (+T), amax, column partial sums
+    kEpiGeluBf16 = 5,   // h = acc * alpha + bias -> h bf16 (optional); out bf16 = gelu(h)
 };
+
+// GEMM operand kind besides the FP8 formats: bf16 values.  Both operands of a
+// product are then bf16 (K counts elements, not bytes), and the epilogues are
+// kEpiBf16Bias, kEpiF32, kEpiGeluBf16 and kEpiDGeluF32.
+constexpr int kOpBf16 = 2;
 
 struct GemmParams {
     int64_t M, N, K;
-    const uint8_t* A;       // [M][K]
+    const uint8_t* A;       // [M][K] codes (or bf16 values)
     const uint8_t* B;       // [N][K]
-    int a_fp8, b_fp8;
+    int a_fp8, b_fp8;       // kE4M3, kE5M2, or kOpBf16 for both
     const float* sinv_a;    // device scalars; alpha = *sinv_a * *sinv_b
     const float* sinv_b;
     const uint16_t* bias;   // bf16 [N] or null

@@ -24,7 +24,8 @@ __all__ = [
     "check_support", "workspace_size", "meta_init",
     "scaling_update", "ln_cast_amax", "cast_amax", "encode_range", "gemm", "gemm_gelu_fp8",
     "gemm_dgelu", "gemm_dgelu_fp8", "layernorm_bwd", "layernorm_fwd", "layernorm_bwd_bf16",
-    "linear_fwd", "linear_bwd",
+    "linear_fwd", "linear_bwd", "gemm_bf16", "gemm_gelu_bf16", "transpose_bf16",
+    "ln_linear_fwd_bf16", "ln_linear_bwd_bf16", "ln_mlp_fwd_bf16",
     "ln_linear_fwd", "ln_linear_bwd", "ln_mlp_fwd", "ln_mlp_bwd", "fwd_fp8", "bwd_fp8",
 ]
 
@@ -339,6 +340,93 @@ def layernorm_bwd_bf16(dy, x, mean, rstd, gamma, dx, dgamma, dbeta, stream=None)
     check(lib().fp8ln_layernorm_bwd_bf16(M, H, _ptr(dy), _ptr(x), _ptr(mean), _ptr(rstd),
                                          _ptr(gamma), _ptr(dx), _ptr(dgamma), _ptr(dbeta),
                                          _ptr(ws), ws.numel(), _stream(stream)))
+
+
+# ---- BF16 path (no FP8) ---------------------------------------------------------
+
+def gemm_bf16(a, b, out, bias=None, stream=None) -> None:
+    """out = a . b^T (+ bias) with bf16 operands; out bf16, or fp32 without bias."""
+    M, K = a.shape
+    N = b.shape[0]
+    _need(a, torch.bfloat16, (M, K), "a")
+    _need(b, torch.bfloat16, (N, K), "b")
+    _opt(bias, torch.bfloat16, (N,), "bias")
+    odt = DTYPE_BF16 if out.dtype == torch.bfloat16 else DTYPE_F32
+    _need(out, out.dtype, (M, N), "out")
+    check(lib().fp8ln_gemm_bf16(M, N, K, _ptr(a), _ptr(b), _ptr(bias), odt, _ptr(out),
+                                _stream(stream)))
+
+
+def gemm_gelu_bf16(a, b, out, bias=None, h_out=None, activation=GELU_TANH, stream=None) -> None:
+    M, K = a.shape
+    N = b.shape[0]
+    _need(a, torch.bfloat16, (M, K), "a")
+    _need(b, torch.bfloat16, (N, K), "b")
+    _opt(bias, torch.bfloat16, (N,), "bias")
+    _need(out, torch.bfloat16, (M, N), "out")
+    _opt(h_out, torch.bfloat16, (M, N), "h_out")
+    check(lib().fp8ln_gemm_gelu_bf16(M, N, K, _ptr(a), _ptr(b), _ptr(bias), _ptr(h_out),
+                                     _ptr(out), int(activation), _stream(stream)))
+
+
+def transpose_bf16(x, out, colsum=None, stream=None) -> None:
+    R, Cc = x.shape
+    _need(x, torch.bfloat16, (R, Cc), "x")
+    _need(out, torch.bfloat16, (Cc, R), "out")
+    _opt(colsum, torch.float32, (Cc,), "colsum")
+    ws = _workspace(workspace_size(_abi.OP_TRANSPOSE_BF16, R, Cc), x.device)
+    check(lib().fp8ln_transpose_bf16(R, Cc, _ptr(x), _ptr(out), _ptr(colsum), _ptr(ws),
+                                     ws.numel(), _stream(stream)))
+
+
+def ln_linear_fwd_bf16(x, gamma, beta, weight, bias, out, ln_out, mean=None, rstd=None,
+                       eps=1e-5, stream=None) -> None:
+    M, K = x.shape
+    N = weight.shape[0]
+    _need(x, torch.bfloat16, (M, K), "x")
+    _need(weight, torch.bfloat16, (N, K), "weight")
+    _opt(bias, torch.bfloat16, (N,), "bias")
+    _need(out, torch.bfloat16, (M, N), "out")
+    _need(ln_out, torch.bfloat16, (M, K), "ln_out")
+    check(lib().fp8ln_ln_linear_fwd_bf16(M, K, N, float(eps), _ptr(x), _ptr(gamma), _ptr(beta),
+                                         _ptr(weight), _ptr(bias), _ptr(out), _ptr(ln_out),
+                                         _ptr(mean), _ptr(rstd), _stream(stream)))
+
+
+def ln_linear_bwd_bf16(dy, x, gamma, weight, ln_out, mean, rstd, dx, dgamma, dbeta, dweight,
+                       dbias=None, workspace=None, stream=None) -> None:
+    M, N = dy.shape
+    K = x.shape[1]
+    _need(dy, torch.bfloat16, (M, N), "dy")
+    _need(dx, torch.bfloat16, (M, K), "dx")
+    _need(dweight, torch.float32, (N, K), "dweight")
+    _opt(dbias, torch.float32, (N,), "dbias")
+    nbytes = workspace_size(_abi.OP_LN_LINEAR_BWD_BF16, M, K, N)
+    if workspace is None:
+        workspace = _workspace(nbytes, dy.device)
+    check(lib().fp8ln_ln_linear_bwd_bf16(M, K, N, _ptr(dy), _ptr(x), _ptr(gamma), _ptr(weight),
+                                         _ptr(ln_out), _ptr(mean), _ptr(rstd), _ptr(dx),
+                                         _ptr(dgamma), _ptr(dbeta), _ptr(dweight), _ptr(dbias),
+                                         _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def ln_mlp_fwd_bf16(x, gamma, beta, w1, b1, w2, b2, out, ln_out, g, h=None, mean=None,
+                    rstd=None, eps=1e-5, activation=GELU_TANH, stream=None) -> None:
+    M, H = x.shape
+    F = w1.shape[0]
+    _need(x, torch.bfloat16, (M, H), "x")
+    _need(w1, torch.bfloat16, (F, H), "w1")
+    _need(w2, torch.bfloat16, (H, F), "w2")
+    _opt(b1, torch.bfloat16, (F,), "b1")
+    _opt(b2, torch.bfloat16, (H,), "b2")
+    _need(out, torch.bfloat16, (M, H), "out")
+    _need(ln_out, torch.bfloat16, (M, H), "ln_out")
+    _need(g, torch.bfloat16, (M, F), "g")
+    _opt(h, torch.bfloat16, (M, F), "h")
+    check(lib().fp8ln_ln_mlp_fwd_bf16(M, H, F, float(eps), int(activation), _ptr(x), _ptr(gamma),
+                                      _ptr(beta), _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2),
+                                      _ptr(out), _ptr(ln_out), _ptr(h), _ptr(g), _ptr(mean),
+                                      _ptr(rstd), _stream(stream)))
 
 
 # ---- modules ------------------------------------------------------------------

@@ -175,7 +175,9 @@ typedef enum {
     FP8LN_OP_LN_LINEAR_BWD = 2,    /* a = tokens, b = in_features, c = out_features */
     FP8LN_OP_LN_MLP_BWD = 3,       /* a = tokens, b = hidden, c = ffn */
     FP8LN_OP_GEMM_DGELU_FP8 = 4,   /* a = M, b = N (column sums requested) */
-    FP8LN_OP_LINEAR_BWD = 5        /* a = tokens, b = in_features, c = out_features */
+    FP8LN_OP_LINEAR_BWD = 5,       /* a = tokens, b = in_features, c = out_features */
+    FP8LN_OP_LN_LINEAR_BWD_BF16 = 6, /* a = tokens, b = in_features, c = out_features */
+    FP8LN_OP_TRANSPOSE_BF16 = 7    /* a = rows, b = cols (column sums requested) */
 } fp8ln_op;
 
 /* ---- library ------------------------------------------------------------ */
@@ -306,6 +308,62 @@ int fp8ln_layernorm_bwd(int64_t rows, int64_t hidden, const float* dy, const voi
                         const float* mean, const float* rstd, const void* gamma, void* dx,
                         float* dgamma, float* dbeta, void* workspace, size_t workspace_bytes,
                         void* stream);
+
+/* ---- BF16 path ([G] "Playing with lower-precision formats: BF16 vs FP8"; [T]
+ *      benchmark listing and results: the same modules without FP8) ---------- */
+
+/* The modules without FP8: every GEMM multiplies bf16 values on the bf16 matrix
+ * cores with fp32 accumulation; there are no scales, amaxes or histories.
+ *
+ * out[m][n] = sum_k A[m][k] * B[n][k] + bias[n]
+ * A bf16 [M][K], B bf16 [N][K] (contraction index last), bias bf16 [N] or NULL,
+ * out [M][N] in out_dtype (bf16, or fp32 without bias).  N, K: multiples of 16. */
+int fp8ln_gemm_bf16(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
+                    const void* bias, int32_t out_dtype, void* out, void* stream);
+
+/* h = A . B^T + bias (fp32); h_out = bf16(h) when h_out is not NULL;
+ * out = bf16(gelu(h)) with gelu of the given activation form.  Shapes as above. */
+int fp8ln_gemm_gelu_bf16(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
+                         const void* bias, void* h_out, void* out, int32_t activation,
+                         void* stream);
+
+/* out[c][r] = in[r][c] for bf16 [rows][cols] (rows, cols multiples of 8), and
+ * colsum[c] = sum over r of in[r][c] in fp32 when colsum is not NULL (workspace:
+ * fp8ln_workspace_size(FP8LN_OP_TRANSPOSE_BF16, rows, cols)). */
+int fp8ln_transpose_bf16(int64_t rows, int64_t cols, const void* in, void* out, float* colsum,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* BF16 LayerNormLinear forward: ln_out = bf16(LN(x)) (as fp8ln_layernorm_fwd;
+ * mean, rstd written when not NULL), out = ln_out . W^T + bias in bf16.
+ * x bf16 [tokens][in], W bf16 [out][in], bias bf16 [out] or NULL, ln_out bf16
+ * [tokens][in] (kept for the backward).  in: multiple of 16 up to 8192; out:
+ * multiple of 16. */
+int fp8ln_ln_linear_fwd_bf16(int64_t tokens, int64_t in_features, int64_t out_features,
+                             float eps, const void* x, const void* gamma, const void* beta,
+                             const void* weight, const void* bias, void* out, void* ln_out,
+                             float* mean, float* rstd, void* stream);
+
+/* Its backward for dy bf16 [tokens][out]:
+ *   dLN = dy . W (fp32), dW = dy^T . ln_out (fp32 [out][in]), dbias = column sums
+ *   of dy (fp32, or NULL), then the LayerNorm backward gives dx (bf16), dgamma and
+ *   dbeta (fp32).
+ * tokens: multiple of 16; in at most 4096.  Workspace:
+ * fp8ln_workspace_size(FP8LN_OP_LN_LINEAR_BWD_BF16, tokens, in, out). */
+int fp8ln_ln_linear_bwd_bf16(int64_t tokens, int64_t in_features, int64_t out_features,
+                             const void* dy, const void* x, const void* gamma,
+                             const void* weight, const void* ln_out, const float* mean,
+                             const float* rstd, void* dx, float* dgamma, float* dbeta,
+                             float* dweight, float* dbias, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* BF16 LayerNormMLP forward: ln_out = bf16(LN(x)); h = ln_out . W1^T + b1 (fp32,
+ * stored as bf16 when h is not NULL); g = bf16(gelu(h)) [tokens][ffn];
+ * out = g . W2^T + b2 in bf16.  W1 bf16 [ffn][hidden], W2 bf16 [hidden][ffn]. */
+int fp8ln_ln_mlp_fwd_bf16(int64_t tokens, int64_t hidden, int64_t ffn, float eps,
+                          int32_t activation, const void* x, const void* gamma, const void* beta,
+                          const void* w1, const void* b1, const void* w2, const void* b2,
+                          void* out, void* ln_out, void* h, void* g, float* mean, float* rstd,
+                          void* stream);
 
 /* ---- LayerNorm ([T] setup listing, module tour: te.LayerNorm) --------------- */
 

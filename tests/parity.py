@@ -145,4 +145,5 @@ def compare_bf16(gpu_bits, exact, window):
         idx = np.nonzero(bad)[0][:8]
         raise AssertionError(f"{int(bad.sum())} bf16 values outside the rule; first at "
                              f"{idx.tolist()}: gpu={g[idx].tolist()} exact={exact[idx].tolist()}")
-    return dict(n=int(exact.size), mismatched=int((g != ref).sum()))
+    return dict(n=int(exact.size), mismatched=int((g != ref).sum()),
+                near_boundary=int(((lo != ref) | (hi != ref)).sum()))
