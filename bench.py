@@ -11,7 +11,9 @@ per row).  Further workloads (the pages' GPT-style shapes: LayerNormLinear
 768 -> 2304 forward on 8 x 32 tokens and backward on 8 x 256 tokens,
 LayerNormMLP 768 -> 3072 -> 768 forward on 8 x 256 tokens, and the
 2048 / 8192 / 12-layer scale-up on 64 x 256 tokens, fwd + bwd) are reported in
-"workloads" with TFLOP/s against the FP8 MFMA peak.
+"workloads" with TFLOP/s against the FP8 MFMA peak, and the same modules without
+FP8 (bf16 GEMMs, "_bf16" workloads, against the BF16 MFMA peak) with the FP8
+speedup over them, the comparison the pages make.
 
 Step times are replays of consecutive steps captured once in a HIP graph (the
 same kernels on the same buffers, without host launch gaps); the host-launched
@@ -38,6 +40,7 @@ if ROOT not in sys.path:
 METRIC = "LayerNormLinear FP8 fwd TFLOP/s (% MFMA peak); LN+cast+amax GB/s (% HBM)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, TFLOP/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense BF16 MFMA, TFLOP/s
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
@@ -255,18 +258,25 @@ def summarize_counters(fetch_csv, write_csv):
 
 # ---- GEMM-bound workloads ------------------------------------------------------
 
-def gemm_kernel_ms(torch, ops, M, N, K, out_dtype, reps=20):
-    """Average duration of one fp8ln_gemm launch at this shape: `reps` launches
-    captured in a HIP graph and replayed, timed with HIP events on the replay
-    stream (no host launch overhead between them)."""
-    a = torch.randint(0, 0x77, (M, K), dtype=torch.uint8, device="cuda")
-    b = torch.randint(0, 0x77, (N, K), dtype=torch.uint8, device="cuda")
-    one = torch.ones(1, dtype=torch.float32, device="cuda")
+def gemm_kernel_ms(torch, ops, M, N, K, out_dtype, reps=20, bf16=False):
+    """Average duration of one fp8ln_gemm (or fp8ln_gemm_bf16) launch at this
+    shape: `reps` launches captured in a HIP graph and replayed, timed with HIP
+    events on the replay stream (no host launch overhead between them)."""
     out = torch.empty((M, N), dtype=out_dtype, device="cuda")
+    if bf16:
+        a = torch.randn((M, K), device="cuda").to(torch.bfloat16)
+        b = torch.randn((N, K), device="cuda").to(torch.bfloat16)
+    else:
+        a = torch.randint(0, 0x77, (M, K), dtype=torch.uint8, device="cuda")
+        b = torch.randint(0, 0x77, (N, K), dtype=torch.uint8, device="cuda")
+    one = torch.ones(1, dtype=torch.float32, device="cuda")
 
     def launches(_):
         for _ in range(reps):
-            ops.gemm(a, ops.E4M3, b, ops.E4M3, one, one, out)
+            if bf16:
+                ops.gemm_bf16(a, b, out)
+            else:
+                ops.gemm(a, ops.E4M3, b, ops.E4M3, one, one, out)
 
     return _graph_ms(torch, launches, 1, 3) / reps
 
@@ -299,7 +309,7 @@ def _graph_ms(torch, step, unroll, replays):
     return ms
 
 
-def bench_linear_fwd(torch, ops, inputs, steps, warmup, M=256, K=768, N=2304):
+def bench_linear_fwd(torch, ops, inputs, steps, warmup, M=256, K=768, N=2304, reuse=False):
     recipe = ops.Recipe(format=ops.FORMAT_HYBRID, amax_history_len=16)
     wl = f"ln_linear_fwd_{M}x{K}x{N}"
     xs = [inputs.normal_bf16((M, K), inputs.seed_for(wl, "x", s), device="cuda") for s in range(16)]
@@ -309,6 +319,10 @@ def bench_linear_fwd(torch, ops, inputs, steps, warmup, M=256, K=768, N=2304):
     mf, _ = ops.linear_metas(recipe)
     ctx = ops.LinearCtx(M, K, N, training=False)
     out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    if reuse:   # FP8 weight storage: cast once, then reuse the codes
+        ops.scaling_update(recipe, mf)
+        ops.ln_linear_fwd(recipe, xs[0], g, b, w, bias, out, mf, ctx)
+        ctx.reuse_weight_codes = True
 
     def step(s):
         ops.scaling_update(recipe, mf)
@@ -349,7 +363,7 @@ def bench_linear_bwd(torch, ops, inputs, steps, warmup, M=2048, K=768, N=2304):
     return dict(t, flops=flops, gemm=(N, K, M, torch.float32))
 
 
-def bench_mlp_fwd(torch, ops, inputs, steps, warmup, M=2048, H=768, F=3072):
+def bench_mlp_fwd(torch, ops, inputs, steps, warmup, M=2048, H=768, F=3072, reuse=False):
     recipe = ops.Recipe(format=ops.FORMAT_E4M3, amax_history_len=16)
     wl = f"ln_mlp_fwd_{M}x{H}x{F}"
     xs = [inputs.normal_bf16((M, H), inputs.seed_for(wl, "x", s), device="cuda") for s in range(4)]
@@ -359,6 +373,10 @@ def bench_mlp_fwd(torch, ops, inputs, steps, warmup, M=2048, H=768, F=3072):
     mf, _ = ops.mlp_metas(recipe)
     ctx = ops.MlpCtx(M, H, F, training=False)
     out = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+    if reuse:   # FP8 weight storage: cast once, then reuse the codes
+        ops.scaling_update(recipe, mf)
+        ops.ln_mlp_fwd(recipe, xs[0], g, b, w1, None, w2, None, out, mf, ctx)
+        ctx.reuse_weight_codes = True
 
     def step(s):
         ops.scaling_update(recipe, mf)
@@ -367,6 +385,67 @@ def bench_mlp_fwd(torch, ops, inputs, steps, warmup, M=2048, H=768, F=3072):
     t = _time_steps(torch, step, steps, warmup, unroll=4)
     flops = 2 * 2.0 * M * H * F
     return dict(t, flops=flops, gemm=(M, F, H, torch.bfloat16))
+
+
+def bench_linear_fwd_bf16(torch, ops, inputs, steps, warmup, M=256, K=768, N=2304):
+    wl = f"ln_linear_fwd_{M}x{K}x{N}"
+    xs = [inputs.normal_bf16((M, K), inputs.seed_for(wl, "x", s), device="cuda") for s in range(16)]
+    g, b = inputs.layernorm_params(K, wl, device="cuda")
+    w = inputs.linear_weight(N, K, wl, "w", device="cuda")
+    bias = torch.zeros(N, dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ln_out = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+
+    def step(s):
+        ops.ln_linear_fwd_bf16(xs[s % 16], g, b, w, bias, out, ln_out)
+
+    t = _time_steps(torch, step, steps, warmup, unroll=16)
+    return dict(t, flops=2.0 * M * N * K, gemm=(M, N, K, torch.bfloat16), bf16=True)
+
+
+def bench_linear_bwd_bf16(torch, ops, inputs, steps, warmup, M=2048, K=768, N=2304):
+    wl = f"ln_linear_bwd_{M}x{K}x{N}"
+    x = inputs.normal_bf16((M, K), inputs.seed_for(wl, "x"), device="cuda")
+    g, b = inputs.layernorm_params(K, wl, device="cuda")
+    w = inputs.linear_weight(N, K, wl, "w", device="cuda")
+    dys = [inputs.normal_bf16((M, N), inputs.seed_for(wl, "dy", s), std=1e-3, device="cuda")
+           for s in range(4)]
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ln_out = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    mean = torch.empty(M, device="cuda")
+    rstd = torch.empty(M, device="cuda")
+    dx = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    dgamma = torch.empty(K, device="cuda")
+    dbeta = torch.empty(K, device="cuda")
+    dw = torch.empty((N, K), device="cuda")
+    dbias = torch.empty(N, device="cuda")
+    ws = torch.empty(ops.workspace_size(ops._abi.OP_LN_LINEAR_BWD_BF16, M, K, N),
+                     dtype=torch.uint8, device="cuda")
+    ops.ln_linear_fwd_bf16(x, g, b, w, None, out, ln_out, mean, rstd)
+
+    def step(s):
+        ops.ln_linear_bwd_bf16(dys[s % 4], x, g, w, ln_out, mean, rstd, dx, dgamma, dbeta, dw,
+                               dbias, workspace=ws)
+
+    t = _time_steps(torch, step, steps, warmup, unroll=4)
+    return dict(t, flops=2 * 2.0 * M * N * K, gemm=(N, K, M, torch.float32), bf16=True)
+
+
+def bench_mlp_fwd_bf16(torch, ops, inputs, steps, warmup, M=2048, H=768, F=3072):
+    wl = f"ln_mlp_fwd_{M}x{H}x{F}"
+    xs = [inputs.normal_bf16((M, H), inputs.seed_for(wl, "x", s), device="cuda") for s in range(4)]
+    g, b = inputs.layernorm_params(H, wl, device="cuda")
+    w1 = inputs.linear_weight(F, H, wl, "w1", device="cuda")
+    w2 = inputs.linear_weight(H, F, wl, "w2", device="cuda")
+    out = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+    ln_out = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+    gg = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
+
+    def step(s):
+        ops.ln_mlp_fwd_bf16(xs[s % 4], g, b, w1, None, w2, None, out, ln_out, gg)
+
+    t = _time_steps(torch, step, steps, warmup, unroll=4)
+    return dict(t, flops=2 * 2.0 * M * H * F, gemm=(M, F, H, torch.bfloat16), bf16=True)
 
 
 def bench_mlp_stack(torch, ops, inputs, steps, warmup, fmt, M=16384, H=2048, F=8192, layers=12):
@@ -407,6 +486,45 @@ def bench_mlp_stack(torch, ops, inputs, steps, warmup, fmt, M=16384, H=2048, F=8
     t = _time_steps(torch, step, steps, warmup, unroll=1)
     flops = layers * 6 * 2.0 * M * H * F
     return dict(t, flops=flops, gemm=(M, F, H, torch.float32))
+
+
+def bench_mlp_stack_bf16(torch, ops, inputs, steps, warmup, M=16384, H=2048, F=8192, layers=12):
+    """The 12-layer stack of bench_mlp_stack without FP8 (same inputs)."""
+    wl = f"ln_mlp_x{layers}_{M}x{H}x{F}"
+    x0 = inputs.normal_bf16((M, H), inputs.seed_for(wl, "x"), device="cuda")
+    dy = inputs.normal_bf16((M, H), inputs.seed_for(wl, "dy"), std=1e-3, device="cuda")
+    bf = lambda *s: torch.empty(s, dtype=torch.bfloat16, device="cuda")
+    f32 = lambda *s: torch.empty(s, device="cuda")
+    L = []
+    for l in range(layers):
+        g, b = inputs.layernorm_params(H, f"{wl}/{l}", device="cuda")
+        w1 = inputs.linear_weight(F, H, f"{wl}/{l}", "w1", device="cuda")
+        w2 = inputs.linear_weight(H, F, f"{wl}/{l}", "w2", device="cuda")
+        L.append(dict(g=g, b=b, w1=w1, w2=w2, out=bf(M, H), ln=bf(M, H), h=bf(M, F),
+                      gg=bf(M, F), mean=f32(M), rstd=f32(M), dw1=f32(F, H), db1=f32(F),
+                      dw2=f32(H, F), db2=f32(H), dg=f32(H), dbt=f32(H)))
+    dxs = [bf(M, H) for _ in range(2)]
+    ws = torch.empty(ops.workspace_size(ops._abi.OP_LN_MLP_BWD_BF16, M, H, F), dtype=torch.uint8,
+                     device="cuda")
+
+    def step(s):
+        x = x0
+        for d in L:
+            ops.ln_mlp_fwd_bf16(x, d["g"], d["b"], d["w1"], None, d["w2"], None, d["out"],
+                                d["ln"], d["gg"], h=d["h"], mean=d["mean"], rstd=d["rstd"])
+            x = d["out"]
+        grad = dy
+        for i, d in enumerate(reversed(L)):
+            xin = x0 if i == layers - 1 else L[layers - 2 - i]["out"]
+            dx = dxs[i % 2]
+            ops.ln_mlp_bwd_bf16(grad, xin, d["g"], d["w1"], d["w2"], d["ln"], d["h"], d["gg"],
+                                d["mean"], d["rstd"], dx, d["dg"], d["dbt"], d["dw1"], d["db1"],
+                                d["dw2"], d["db2"], workspace=ws)
+            grad = dx
+
+    t = _time_steps(torch, step, steps, warmup, unroll=1)
+    flops = layers * 6 * 2.0 * M * H * F
+    return dict(t, flops=flops, gemm=(M, F, H, torch.float32), bf16=True)
 
 
 def _time_steps(torch, step, steps, warmup, unroll=4):
@@ -500,10 +618,26 @@ def main():
              lambda: bench_linear_bwd(torch, ops, inputs, 100, 10)),
             ("ln_mlp_fwd", "LayerNormMLP fwd 2048 tokens, 768->3072->768, E4M3, history 16",
              lambda: bench_mlp_fwd(torch, ops, inputs, 100, 10)),
+            ("ln_linear_fwd_fp8w", "LayerNormLinear fwd 8x32 tokens, 768->2304, HYBRID, FP8 weight storage",
+             lambda: bench_linear_fwd(torch, ops, inputs, 200, 20, reuse=True)),
+            ("ln_mlp_fwd_fp8w", "LayerNormMLP fwd 2048 tokens, 768->3072->768, E4M3, FP8 weight storage",
+             lambda: bench_mlp_fwd(torch, ops, inputs, 100, 10, reuse=True)),
+            ("ln_linear_fwd_bf16", "LayerNormLinear fwd 8x32 tokens, 768->2304, bf16 (no FP8)",
+             lambda: bench_linear_fwd_bf16(torch, ops, inputs, 200, 20)),
+            ("ln_linear_bwd_bf16", "LayerNormLinear bwd 2048 tokens, 768->2304, bf16 (no FP8)",
+             lambda: bench_linear_bwd_bf16(torch, ops, inputs, 100, 10)),
+            ("ln_mlp_fwd_bf16", "LayerNormMLP fwd 2048 tokens, 768->3072->768, bf16 (no FP8)",
+             lambda: bench_mlp_fwd_bf16(torch, ops, inputs, 100, 10)),
+            ("ln_mlp_fwd_16384", "LayerNormMLP fwd 16384 tokens, 2048->8192->2048, E4M3",
+             lambda: bench_mlp_fwd(torch, ops, inputs, 20, 3, M=16384, H=2048, F=8192)),
+            ("ln_mlp_fwd_16384_bf16", "LayerNormMLP fwd 16384 tokens, 2048->8192->2048, bf16 (no FP8)",
+             lambda: bench_mlp_fwd_bf16(torch, ops, inputs, 20, 3, M=16384, H=2048, F=8192)),
             ("ln_mlp_x12_hybrid", "LayerNormMLP x12 fwd+bwd, 16384 tokens, 2048->8192->2048, HYBRID, history 1024",
              lambda: bench_mlp_stack(torch, ops, inputs, 5, 2, ops.FORMAT_HYBRID)),
             ("ln_mlp_x12_e4m3", "LayerNormMLP x12 fwd+bwd, 16384 tokens, 2048->8192->2048, E4M3, history 1024",
              lambda: bench_mlp_stack(torch, ops, inputs, 5, 2, ops.FORMAT_E4M3)),
+            ("ln_mlp_x12_bf16", "LayerNormMLP x12 fwd+bwd, 16384 tokens, 2048->8192->2048, bf16 (no FP8)",
+             lambda: bench_mlp_stack_bf16(torch, ops, inputs, 5, 2)),
         ]
         for name, desc, fn in runs:
             if args.only not in (None, name):
@@ -511,19 +645,27 @@ def main():
             log(f"{name} ...")
             r = fn()
             M, N, K, odt = r["gemm"]
-            gk_ms = gemm_kernel_ms(torch, ops, M, N, K, odt)
+            bf16 = r.get("bf16", False)
+            gk_ms = gemm_kernel_ms(torch, ops, M, N, K, odt, bf16=bf16)
             gflops = 2.0 * M * N * K
             tflops = r["flops"] / (r["ms"] * 1e-3) / 1e12
-            workloads.append(dict(
-                workload=name, description=desc, ms_per_step=round(r["ms"], 5),
-                eager_ms_per_step=round(r["eager_ms"], 5),
+            peak = BF16_PEAK_TFLOPS if bf16 else FP8_PEAK_TFLOPS
+            w = dict(
+                workload=name, description=desc, precision="bf16" if bf16 else "fp8",
+                ms_per_step=round(r["ms"], 5), eager_ms_per_step=round(r["eager_ms"], 5),
                 value=round(tflops, 2), unit="TFLOP/s",
-                frac_of_fp8_peak=round(tflops / FP8_PEAK_TFLOPS, 4),
-                roofline=dict(bound="mfma", kernel=f"fp8 gemm {M}x{N}x{K}",
+                frac_of_peak=round(tflops / peak, 4),
+                roofline=dict(bound="mfma", kernel=f"{'bf16' if bf16 else 'fp8'} gemm {M}x{N}x{K}",
                               achieved=round(gflops / (gk_ms * 1e-3) / 1e12, 2),
-                              peak=FP8_PEAK_TFLOPS, unit="TFLOP/s",
-                              frac=round(gflops / (gk_ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
-                              kernel_ms=round(gk_ms, 5))))
+                              peak=peak, unit="TFLOP/s",
+                              frac=round(gflops / (gk_ms * 1e-3) / 1e12 / peak, 4),
+                              kernel_ms=round(gk_ms, 5)))
+            twin = name.replace("_bf16", "")
+            twin = "ln_mlp_x12_hybrid" if twin == "ln_mlp_x12" else twin
+            fp8_twin = [x for x in workloads if x["workload"] == twin]
+            if bf16 and fp8_twin:
+                w["fp8_speedup"] = round(r["ms"] / fp8_twin[0]["ms_per_step"], 3)
+            workloads.append(w)
             torch.cuda.empty_cache()
 
     line = dict(metric=METRIC, n_gpus=1, steps=args.steps, warmup=args.warmup,

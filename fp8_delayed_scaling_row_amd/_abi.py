@@ -39,6 +39,7 @@ OP_GEMM_DGELU_FP8 = 4
 OP_LINEAR_BWD = 5
 OP_LN_LINEAR_BWD_BF16 = 6
 OP_TRANSPOSE_BF16 = 7
+OP_LN_MLP_BWD_BF16 = 8
 
 
 class Recipe(C.Structure):
@@ -94,6 +95,8 @@ SIGNATURES = {
     "fp8ln_layernorm_bwd": (C.c_int, [_I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "fp8ln_gemm_bf16": (C.c_int, [_I64, _I64, _I64, _P, _P, _P, _I32, _P, _P]),
     "fp8ln_gemm_gelu_bf16": (C.c_int, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _I32, _P]),
+    "fp8ln_gemm_dgelu_bf16": (C.c_int, [_I64, _I64, _I64, _P, _P, _P, _P, _I32, _P]),
+    "fp8ln_ln_mlp_bwd_bf16": (C.c_int, [_I64, _I64, _I64, _I32] + [_P] * 18 + [_SZ, _P]),
     "fp8ln_transpose_bf16": (C.c_int, [_I64, _I64, _P, _P, _P, _P, _SZ, _P]),
     "fp8ln_ln_linear_fwd_bf16": (C.c_int, [_I64, _I64, _I64, C.c_float, _P, _P, _P, _P, _P, _P,
                                            _P, _P, _P, _P]),

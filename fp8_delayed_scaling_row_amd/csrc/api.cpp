@@ -210,6 +210,38 @@ LinearBf16Ws linear_bf16_ws(void* base, int64_t M, int64_t K, int64_t N) {
     return w;
 }
 
+// BF16 LayerNormMLP backward: transposed operands, bf16 dH, fp32 dLN.
+struct MlpBf16Ws {
+    void* dy_t;      // [H][M]
+    void* g_t;       // [F][M]
+    void* w2_t;      // [F][H]
+    void* w1_t;      // [H][F]
+    void* ln_t;      // [H][M]
+    void* dh;        // [M][F]
+    void* dh_t;      // [F][M]
+    float* dln;      // fp32 [M][H]
+    void* sum_ws;
+    void* ln_ws;
+    size_t bytes;
+};
+
+MlpBf16Ws mlp_bf16_ws(void* base, int64_t M, int64_t H, int64_t F) {
+    Carver c{(uint8_t*)base};
+    MlpBf16Ws w;
+    w.dy_t = c.take((size_t)(M * H) * 2);
+    w.g_t = c.take((size_t)(M * F) * 2);
+    w.w2_t = c.take((size_t)(H * F) * 2);
+    w.w1_t = c.take((size_t)(H * F) * 2);
+    w.ln_t = c.take((size_t)(M * H) * 2);
+    w.dh = c.take((size_t)(M * F) * 2);
+    w.dh_t = c.take((size_t)(M * F) * 2);
+    w.dln = (float*)c.take((size_t)(M * H) * sizeof(float));
+    w.sum_ws = c.take(std::max(transpose_b16_workspace(M, H), transpose_b16_workspace(M, F)));
+    w.ln_ws = c.take(ln_bwd_workspace(M, (int)H));
+    w.bytes = c.used;
+    return w;
+}
+
 struct MlpWs {
     uint8_t* dy_q;
     uint8_t* dy_qt;
@@ -302,6 +334,8 @@ size_t fp8ln_workspace_size(int32_t op, int64_t a, int64_t b, int64_t c) {
         case FP8LN_OP_LN_LINEAR_BWD_BF16:
             return b > 0 && c > 0 ? linear_bf16_ws(nullptr, a, b, c).bytes : 0;
         case FP8LN_OP_TRANSPOSE_BF16: return transpose_b16_workspace(a, b);
+        case FP8LN_OP_LN_MLP_BWD_BF16:
+            return b > 0 && c > 0 ? mlp_bf16_ws(nullptr, a, b, c).bytes : 0;
         case FP8LN_OP_LN_LINEAR_BWD: return c > 0 ? linear_ws(nullptr, a, b, c).bytes : 0;
         case FP8LN_OP_LN_MLP_BWD: return c > 0 ? mlp_ws(nullptr, a, b, c).bytes : 0;
         default: return 0;
@@ -625,6 +659,29 @@ int fp8ln_gemm_gelu_bf16(int64_t M, int64_t N, int64_t K, const void* A, const v
     return FP8LN_OK;
 }
 
+int fp8ln_gemm_dgelu_bf16(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
+                          const void* h, void* out, int32_t activation, void* stream) {
+    REQUIRE(activation == FP8LN_GELU_TANH || activation == FP8LN_GELU_ERF,
+            "activation %d invalid", activation);
+    REQUIRE(M >= 0 && N >= 0 && K >= 0, "negative size");
+    if (N % 16 != 0 || K % 16 != 0)
+        return fail(FP8LN_ERR_UNSUPPORTED, "N and K must be multiples of 16 (N=%lld K=%lld)",
+                    (long long)N, (long long)K);
+    if (M > 0 && N > 0) {
+        REQUIRE_PTR(out); REQUIRE_PTR(h); REQUIRE_ALIGNED(out); REQUIRE_ALIGNED(h);
+        if (K > 0) { REQUIRE_PTR(A); REQUIRE_PTR(B); REQUIRE_ALIGNED(A); REQUIRE_ALIGNED(B); }
+    }
+    int s = check_current_device();
+    if (s) return s;
+    GemmParams p = gemm_params(M, N, K, (const uint8_t*)A, kOpBf16, (const uint8_t*)B, kOpBf16,
+                               nullptr, nullptr, kEpiDGeluBf16);
+    p.h_in = (const uint16_t*)h;
+    p.out = out;
+    p.gelu_erf = activation == FP8LN_GELU_ERF;
+    FP8LN_TRY(launch_gemm(p, as_stream(stream)), "gemm launch");
+    return FP8LN_OK;
+}
+
 int fp8ln_transpose_bf16(int64_t rows, int64_t cols, const void* in, void* out, float* colsum,
                          void* workspace, size_t workspace_bytes, void* stream) {
     REQUIRE(rows >= 0 && cols >= 0, "negative size");
@@ -758,6 +815,68 @@ int fp8ln_ln_mlp_fwd_bf16(int64_t tokens, int64_t hidden, int64_t ffn, float eps
     p2.bias = (const uint16_t*)b2;
     p2.out = out;
     FP8LN_TRY(launch_gemm(p2, st), "fc2 launch");
+    return FP8LN_OK;
+}
+
+int fp8ln_ln_mlp_bwd_bf16(int64_t tokens, int64_t hidden, int64_t ffn, int32_t activation,
+                          const void* dy, const void* x, const void* gamma, const void* w1,
+                          const void* w2, const void* ln_out, const void* h, const void* g,
+                          const float* mean, const float* rstd, void* dx, float* dgamma,
+                          float* dbeta, float* dw1, float* db1, float* dw2, float* db2,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    const int64_t M = tokens, H = hidden, F = ffn;
+    int s = check_bf16_module(M, H, F, 1.0f);
+    if (s) return s;
+    REQUIRE(activation == FP8LN_GELU_TANH || activation == FP8LN_GELU_ERF,
+            "activation %d invalid", activation);
+    if (M % 16 != 0)
+        return fail(FP8LN_ERR_UNSUPPORTED, "tokens %lld must be a multiple of 16", (long long)M);
+    if (H > 4096)
+        return fail(FP8LN_ERR_UNSUPPORTED, "hidden %lld: the backward takes at most 4096",
+                    (long long)H);
+    REQUIRE_PTR(gamma); REQUIRE_PTR(w1); REQUIRE_PTR(w2); REQUIRE_PTR(dgamma); REQUIRE_PTR(dbeta);
+    REQUIRE_PTR(dw1); REQUIRE_PTR(dw2);
+    REQUIRE_ALIGNED(gamma); REQUIRE_ALIGNED(w1); REQUIRE_ALIGNED(w2); REQUIRE_ALIGNED(dw1);
+    REQUIRE_ALIGNED(dw2);
+    if (M > 0) {
+        REQUIRE_PTR(dy); REQUIRE_PTR(x); REQUIRE_PTR(ln_out); REQUIRE_PTR(h); REQUIRE_PTR(g);
+        REQUIRE_PTR(mean); REQUIRE_PTR(rstd); REQUIRE_PTR(dx);
+        REQUIRE_ALIGNED(dy); REQUIRE_ALIGNED(x); REQUIRE_ALIGNED(ln_out); REQUIRE_ALIGNED(h);
+        REQUIRE_ALIGNED(g); REQUIRE_ALIGNED(dx);
+    }
+    const MlpBf16Ws need = mlp_bf16_ws(nullptr, M, H, F);
+    REQUIRE(workspace && workspace_bytes >= need.bytes,
+            "ln_mlp_bwd_bf16 needs %zu bytes of workspace", need.bytes);
+    REQUIRE_ALIGNED(workspace);
+    if ((s = check_current_device())) return s;
+    hipStream_t st = as_stream(stream);
+    const MlpBf16Ws w = mlp_bf16_ws(workspace, M, H, F);
+    auto gemm = [&](int64_t m, int64_t n, int64_t k, const void* a, const void* b, int epi,
+                    void* out) {
+        GemmParams p = gemm_params(m, n, k, (const uint8_t*)a, kOpBf16, (const uint8_t*)b,
+                                   kOpBf16, nullptr, nullptr, epi);
+        p.out = out;
+        p.h_in = (const uint16_t*)h;
+        p.gelu_erf = activation == FP8LN_GELU_ERF;
+        return launch_gemm(p, st);
+    };
+    FP8LN_TRY(launch_transpose_b16(M, H, dy, w.dy_t, db2, w.sum_ws, st), "dy transpose");
+    FP8LN_TRY(launch_transpose_b16(M, F, g, w.g_t, nullptr, nullptr, st), "g transpose");
+    FP8LN_TRY(launch_transpose_b16(H, F, w2, w.w2_t, nullptr, nullptr, st), "w2 transpose");
+    // fc2 wgrad: dW2[H][F] = dy_t[H][M] . (g_t[F][M])^T
+    FP8LN_TRY(gemm(H, F, M, w.dy_t, w.g_t, kEpiF32, dw2), "fc2 wgrad launch");
+    // fc2 dgrad with GELU': dH[M][F] = (dy[M][H] . (w2_t[F][H])^T) * gelu'(h)
+    FP8LN_TRY(gemm(M, F, H, dy, w.w2_t, kEpiDGeluBf16, w.dh), "fc2 dgrad launch");
+    FP8LN_TRY(launch_transpose_b16(M, F, w.dh, w.dh_t, db1, w.sum_ws, st), "dH transpose");
+    FP8LN_TRY(launch_transpose_b16(F, H, w1, w.w1_t, nullptr, nullptr, st), "w1 transpose");
+    FP8LN_TRY(launch_transpose_b16(M, H, ln_out, w.ln_t, nullptr, nullptr, st), "ln transpose");
+    // fc1 wgrad: dW1[F][H] = dh_t[F][M] . (ln_t[H][M])^T
+    FP8LN_TRY(gemm(F, H, M, w.dh_t, w.ln_t, kEpiF32, dw1), "fc1 wgrad launch");
+    // fc1 dgrad: dLN[M][H] = dH[M][F] . (w1_t[H][F])^T
+    FP8LN_TRY(gemm(M, H, F, w.dh, w.w1_t, kEpiF32, w.dln), "fc1 dgrad launch");
+    FP8LN_TRY(launch_ln_bwd(M, (int)H, w.dln, false, x, mean, rstd, gamma, dx, dgamma, dbeta,
+                            w.ln_ws, st),
+              "layernorm backward launch");
     return FP8LN_OK;
 }
 

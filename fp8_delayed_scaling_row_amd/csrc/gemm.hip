@@ -53,47 +53,41 @@ __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r ^ (r >> 3)) & 
 // GELU, tanh form: gelu(h) = h/2 (1 + t), t = tanh(k0 (h + k1 h^3)), with
 // k0 = sqrt(2 / pi), k1 = 0.044715, and its derivative
 //     gelu'(h) = (1 + t)/2 + h/2 (1 - t^2) k0 (1 + 3 k1 h^2).
-// With v = 2 log2(e) k0 h (1 + k1 h^2): (1 + t)/2 = 1 / (1 + 2^-v), so
-// gelu(h) = h / (1 + 2^-v), which has no cancellation for negative h (the
-// form h/2 + h/2 t loses the relative accuracy of small negative outputs), and
-// t = 1 - 2 / (1 + 2^v) for the derivative.  2^v and the reciprocal are the
-// hardware's (about one ulp each).
+// With v = 2 log2(e) k0 h (1 + k1 h^2): s = (1 + t)/2 = 1 / (1 + 2^-v) and
+// (1 - t^2) / 4 = s (1 - s), so
+//     gelu(h) = h s,   gelu'(h) = s (1 + 2 k0 (1 + 3 k1 h^2) h (1 - s)),
+// neither of which cancels for negative h (the forms h/2 + h/2 t and
+// (1 + t)/2 + ... lose the relative accuracy of small values there).  2^-v and
+// the reciprocal are the hardware's (about one ulp each).
 constexpr float kGeluK0 = 0.7978845608028654f;                 // sqrt(2 / pi)
 constexpr float kGeluK1 = 0.044715f;
 constexpr float kGeluV0 = 2.0f * 1.4426950408889634f * 0.7978845608028654f;   // 2 log2(e) k0
 constexpr float kGeluV1 = kGeluV0 * 0.044715f;
-
-__device__ __forceinline__ float gelu_tanh_t(float h, float h2) {
-    const float v = h * fmaf(kGeluV1, h2, kGeluV0);
-    const float e = __builtin_amdgcn_exp2f(v);
-    return fmaf(-2.0f, __builtin_amdgcn_rcpf(1.0f + e), 1.0f);
-}
 
 __device__ __forceinline__ float gelu_f(float h) {
     const float nv = h * fmaf(-kGeluV1, h * h, -kGeluV0);   // -v
     return h * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(nv));
 }
 
+__device__ __forceinline__ float gelu_grad_f(float h) {
+    const float h2 = h * h;
+    const float nv = h * fmaf(-kGeluV1, h2, -kGeluV0);                      // -v
+    const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(nv));
+    const float c = fmaf(6.0f * kGeluK0 * kGeluK1, h2, 2.0f * kGeluK0);    // 2 k0 (1 + 3 k1 h^2)
+    return sg * fmaf(h * (1.0f - sg), c, 1.0f);
+}
+
 // GELU, erf form: gelu(h) = h/2 (1 + erf(h / sqrt 2)) = h/2 erfc(-h / sqrt 2)
-// (erfc keeps small negative outputs accurate), and
-// gelu'(h) = (1 + erf(h / sqrt 2)) / 2 + h exp(-h^2 / 2) / sqrt(2 pi).
+// and gelu'(h) = erfc(-h / sqrt 2) / 2 + h exp(-h^2 / 2) / sqrt(2 pi) (erfc keeps
+// the small values for negative h accurate).
 __device__ __forceinline__ float gelu_erf_f(float h) {
     return 0.5f * h * erfcf(h * -0.70710678118654752f);
 }
 
 __device__ __forceinline__ float gelu_erf_grad_f(float h) {
-    const float e = erff(h * 0.70710678118654752f);
+    const float e = erfcf(h * -0.70710678118654752f);
     const float d = __expf(-0.5f * h * h) * 0.39894228040143268f;   // 1 / sqrt(2 pi)
-    return fmaf(h, d, fmaf(0.5f, e, 0.5f));
-}
-
-__device__ __forceinline__ float gelu_grad_f(float h) {
-    const float h2 = h * h;
-    const float t = gelu_tanh_t(h, h2);
-    const float a = fmaf(0.5f, t, 0.5f);                                   // (1 + t) / 2
-    const float b = fmaf(-t, t, 1.0f);                                     // 1 - t^2
-    const float c = fmaf(1.5f * kGeluK0 * kGeluK1, h2, 0.5f * kGeluK0);    // k0 (1 + 3 k1 h^2) / 2
-    return fmaf(h * b, c, a);
+    return fmaf(h, d, 0.5f * e);
 }
 
 // LDS layout of one operand stage: 64-byte rows stored in pairs as 128-byte
@@ -462,7 +456,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p) {
             }
     }
 
-    if constexpr (EPI == kEpiDGeluF32) {
+    if constexpr (EPI == kEpiDGeluF32 || EPI == kEpiDGeluBf16) {
         // gelu'(h) from global memory, one 8-byte read per four values
 #pragma unroll
         for (int i = 0; i < TM; ++i)
@@ -538,6 +532,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p) {
         uint16_t* hdst = EPI == kEpiBf16Bias ? (uint16_t*)p.out : p.h_out;
         if (hdst) bf16_out(hdst);
     }
+    if constexpr (EPI == kEpiDGeluBf16) bf16_out((uint16_t*)p.out);
     if constexpr (EPI == kEpiGeluBf16) {
         // rows and columns outside the product hold 0 and gelu(0) = 0
 #pragma unroll
@@ -767,6 +762,7 @@ static hipError_t launch_gemm_bf16(const GemmParams& p, hipStream_t stream) {
         case kEpiF32: return launch_typed<kOpBf16, kOpBf16, kEpiF32, kE4M3>(q, stream);
         case kEpiGeluBf16: return launch_typed<kOpBf16, kOpBf16, kEpiGeluBf16, kE4M3>(q, stream);
         case kEpiDGeluF32: return launch_typed<kOpBf16, kOpBf16, kEpiDGeluF32, kE4M3>(q, stream);
+        case kEpiDGeluBf16: return launch_typed<kOpBf16, kOpBf16, kEpiDGeluBf16, kE4M3>(q, stream);
         default: return hipErrorInvalidValue;
     }
 }

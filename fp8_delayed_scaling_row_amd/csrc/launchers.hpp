@@ -60,11 +60,12 @@ enum GemmEpilogue : int {
     kEpiDGeluF32 = 3,   // out fp32 = acc * alpha * gelu'(h)
     kEpiDGeluFp8 = 4,   // d = acc * alpha * gelu'(h) -> FP8 (+T), amax, column partial sums
     kEpiGeluBf16 = 5,   // h = acc * alpha + bias -> h bf16 (optional); out bf16 = gelu(h)
+    kEpiDGeluBf16 = 6,  // out bf16 = acc * alpha * gelu'(h)
 };
 
 // GEMM operand kind besides the FP8 formats: bf16 values.  Both operands of a
 // product are then bf16 (K counts elements, not bytes), and the epilogues are
-// kEpiBf16Bias, kEpiF32, kEpiGeluBf16 and kEpiDGeluF32.
+// kEpiBf16Bias, kEpiF32, kEpiGeluBf16, kEpiDGeluF32 and kEpiDGeluBf16.
 constexpr int kOpBf16 = 2;
 
 struct GemmParams {
@@ -83,7 +84,8 @@ struct GemmParams {
     const float* q_scale;   // scale of the FP8 output
     float* q_amax;          // amax of gelu(h)
     int q_fp8;
-    // kEpiDGeluF32, kEpiDGeluFp8 (which also uses q_out, q_out_t, q_scale, q_amax, q_fp8)
+    // kEpiDGeluF32, kEpiDGeluBf16, kEpiDGeluFp8 (which also uses q_out, q_out_t, q_scale,
+    // q_amax, q_fp8)
     const uint16_t* h_in;   // bf16 [M][N]
     float* col_partial;     // kEpiDGeluFp8: [ceil(M / tile rows)][N] column sums, or null
     int gelu_erf;           // GELU epilogues: 0 = tanh form, 1 = erf form

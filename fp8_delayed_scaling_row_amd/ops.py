@@ -25,7 +25,8 @@ __all__ = [
     "scaling_update", "ln_cast_amax", "cast_amax", "encode_range", "gemm", "gemm_gelu_fp8",
     "gemm_dgelu", "gemm_dgelu_fp8", "layernorm_bwd", "layernorm_fwd", "layernorm_bwd_bf16",
     "linear_fwd", "linear_bwd", "gemm_bf16", "gemm_gelu_bf16", "transpose_bf16",
-    "ln_linear_fwd_bf16", "ln_linear_bwd_bf16", "ln_mlp_fwd_bf16",
+    "ln_linear_fwd_bf16", "ln_linear_bwd_bf16", "ln_mlp_fwd_bf16", "ln_mlp_bwd_bf16",
+    "gemm_dgelu_bf16",
     "ln_linear_fwd", "ln_linear_bwd", "ln_mlp_fwd", "ln_mlp_bwd", "fwd_fp8", "bwd_fp8",
 ]
 
@@ -369,6 +370,18 @@ def gemm_gelu_bf16(a, b, out, bias=None, h_out=None, activation=GELU_TANH, strea
                                      _ptr(out), int(activation), _stream(stream)))
 
 
+def gemm_dgelu_bf16(a, b, h, out, activation=GELU_TANH, stream=None) -> None:
+    """out = bf16((a . b^T) * gelu'(h)) with bf16 operands."""
+    M, K = a.shape
+    N = b.shape[0]
+    _need(a, torch.bfloat16, (M, K), "a")
+    _need(b, torch.bfloat16, (N, K), "b")
+    _need(h, torch.bfloat16, (M, N), "h")
+    _need(out, torch.bfloat16, (M, N), "out")
+    check(lib().fp8ln_gemm_dgelu_bf16(M, N, K, _ptr(a), _ptr(b), _ptr(h), _ptr(out),
+                                      int(activation), _stream(stream)))
+
+
 def transpose_bf16(x, out, colsum=None, stream=None) -> None:
     R, Cc = x.shape
     _need(x, torch.bfloat16, (R, Cc), "x")
@@ -427,6 +440,28 @@ def ln_mlp_fwd_bf16(x, gamma, beta, w1, b1, w2, b2, out, ln_out, g, h=None, mean
                                       _ptr(beta), _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2),
                                       _ptr(out), _ptr(ln_out), _ptr(h), _ptr(g), _ptr(mean),
                                       _ptr(rstd), _stream(stream)))
+
+
+def ln_mlp_bwd_bf16(dy, x, gamma, w1, w2, ln_out, h, g, mean, rstd, dx, dgamma, dbeta, dw1,
+                    db1, dw2, db2, activation=GELU_TANH, workspace=None, stream=None) -> None:
+    M, H = dy.shape
+    F = w1.shape[0]
+    _need(dy, torch.bfloat16, (M, H), "dy")
+    _need(h, torch.bfloat16, (M, F), "h")
+    _need(g, torch.bfloat16, (M, F), "g")
+    _need(dx, torch.bfloat16, (M, H), "dx")
+    _need(dw1, torch.float32, (F, H), "dw1")
+    _need(dw2, torch.float32, (H, F), "dw2")
+    _opt(db1, torch.float32, (F,), "db1")
+    _opt(db2, torch.float32, (H,), "db2")
+    nbytes = workspace_size(_abi.OP_LN_MLP_BWD_BF16, M, H, F)
+    if workspace is None:
+        workspace = _workspace(nbytes, dy.device)
+    check(lib().fp8ln_ln_mlp_bwd_bf16(M, H, F, int(activation), _ptr(dy), _ptr(x), _ptr(gamma),
+                                      _ptr(w1), _ptr(w2), _ptr(ln_out), _ptr(h), _ptr(g),
+                                      _ptr(mean), _ptr(rstd), _ptr(dx), _ptr(dgamma),
+                                      _ptr(dbeta), _ptr(dw1), _ptr(db1), _ptr(dw2), _ptr(db2),
+                                      _ptr(workspace), workspace.numel(), _stream(stream)))
 
 
 # ---- modules ------------------------------------------------------------------

@@ -177,7 +177,8 @@ typedef enum {
     FP8LN_OP_GEMM_DGELU_FP8 = 4,   /* a = M, b = N (column sums requested) */
     FP8LN_OP_LINEAR_BWD = 5,       /* a = tokens, b = in_features, c = out_features */
     FP8LN_OP_LN_LINEAR_BWD_BF16 = 6, /* a = tokens, b = in_features, c = out_features */
-    FP8LN_OP_TRANSPOSE_BF16 = 7    /* a = rows, b = cols (column sums requested) */
+    FP8LN_OP_TRANSPOSE_BF16 = 7,   /* a = rows, b = cols (column sums requested) */
+    FP8LN_OP_LN_MLP_BWD_BF16 = 8   /* a = tokens, b = hidden, c = ffn */
 } fp8ln_op;
 
 /* ---- library ------------------------------------------------------------ */
@@ -327,6 +328,11 @@ int fp8ln_gemm_gelu_bf16(int64_t M, int64_t N, int64_t K, const void* A, const v
                          const void* bias, void* h_out, void* out, int32_t activation,
                          void* stream);
 
+/* out = bf16((A . B^T) * gelu'(h)) with h bf16 [M][N] and gelu' of the given
+ * activation form (the fc2 dgrad of the BF16 LayerNormMLP).  Shapes as above. */
+int fp8ln_gemm_dgelu_bf16(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
+                          const void* h, void* out, int32_t activation, void* stream);
+
 /* out[c][r] = in[r][c] for bf16 [rows][cols] (rows, cols multiples of 8), and
  * colsum[c] = sum over r of in[r][c] in fp32 when colsum is not NULL (workspace:
  * fp8ln_workspace_size(FP8LN_OP_TRANSPOSE_BF16, rows, cols)). */
@@ -364,6 +370,21 @@ int fp8ln_ln_mlp_fwd_bf16(int64_t tokens, int64_t hidden, int64_t ffn, float eps
                           const void* w1, const void* b1, const void* w2, const void* b2,
                           void* out, void* ln_out, void* h, void* g, float* mean, float* rstd,
                           void* stream);
+
+/* Backward of fp8ln_ln_mlp_fwd_bf16 for dy bf16 [tokens][hidden], from the
+ * forward's ln_out, h and g (all bf16) and mean, rstd:
+ *   dW2 = dy^T . g, db2 = column sums of dy
+ *   dH = (dy . W2) * gelu'(h) (bf16), dW1 = dH^T . ln_out, db1 = column sums of dH
+ *   dLN = dH . W1 (fp32), then the LayerNorm backward gives dx, dgamma, dbeta.
+ * dW1, dW2, db1, db2, dgamma, dbeta fp32; db1 / db2 may be NULL.  tokens: multiple
+ * of 16; hidden at most 4096.  Workspace:
+ * fp8ln_workspace_size(FP8LN_OP_LN_MLP_BWD_BF16, tokens, hidden, ffn). */
+int fp8ln_ln_mlp_bwd_bf16(int64_t tokens, int64_t hidden, int64_t ffn, int32_t activation,
+                          const void* dy, const void* x, const void* gamma, const void* w1,
+                          const void* w2, const void* ln_out, const void* h, const void* g,
+                          const float* mean, const float* rstd, void* dx, float* dgamma,
+                          float* dbeta, float* dw1, float* db1, float* dw2, float* db2,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---- LayerNorm ([T] setup listing, module tour: te.LayerNorm) --------------- */
 

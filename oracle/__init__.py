@@ -32,7 +32,8 @@ from .scaling import Meta, fp8_max_for, scaling_update
 from .layernorm import layernorm_fwd, layernorm_bwd
 from .gelu import gelu_erf, gelu_erf_grad, gelu_tanh, gelu_tanh_grad
 from .gemm import fp8_gemm_tn
-from .bf16_path import gemm_bf16, ln_linear_fwd_bf16, ln_linear_bwd_bf16, ln_mlp_fwd_bf16
+from .bf16_path import (gemm_bf16, ln_linear_fwd_bf16, ln_linear_bwd_bf16, ln_mlp_fwd_bf16,
+                        ln_mlp_bwd_bf16)
 from .modules import (Recipe, FORMAT_E4M3, FORMAT_HYBRID, FORMAT_E5M2, GELU_ERF, GELU_TANH,
                       cast_amax,
                       ln_cast_amax, layernorm, linear_fwd, linear_bwd, ln_linear_fwd, ln_linear_bwd, ln_mlp_fwd, ln_mlp_bwd,
@@ -45,7 +46,7 @@ __all__ = [
     "scaling_update", "layernorm_fwd", "layernorm_bwd", "gelu_tanh", "gelu_tanh_grad",
     "gelu_erf", "gelu_erf_grad", "GELU_TANH", "GELU_ERF",
     "fp8_gemm_tn", "gemm_bf16", "ln_linear_fwd_bf16", "ln_linear_bwd_bf16",
-    "ln_mlp_fwd_bf16", "Recipe", "FORMAT_E4M3", "FORMAT_HYBRID", "FORMAT_E5M2", "cast_amax",
+    "ln_mlp_fwd_bf16", "ln_mlp_bwd_bf16", "Recipe", "FORMAT_E4M3", "FORMAT_HYBRID", "FORMAT_E5M2", "cast_amax",
     "ln_cast_amax", "layernorm", "linear_fwd", "linear_bwd", "ln_linear_fwd", "ln_linear_bwd", "ln_mlp_fwd", "ln_mlp_bwd",
     "fwd_format", "bwd_format", "linear_fwd_meta", "linear_bwd_meta", "mlp_fwd_meta",
     "mlp_bwd_meta",

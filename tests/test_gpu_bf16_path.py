@@ -196,3 +196,71 @@ def test_bf16_ln_mlp_fwd(M, H, F, act):
     assert_gemm_close(to_np(gg)[rows], g_ref, tol=4e-3, alarm=3e-3, what="g")
     o_ref = oracle.gemm_bf16(to_np_bits(gg)[rows], w2b, b2b)
     assert_gemm_close(to_np(out)[rows], o_ref, tol=4e-3, alarm=3e-3, what="out (same g)")
+
+
+GELU_GRAD = {ops.GELU_TANH: oracle.gelu_tanh_grad, ops.GELU_ERF: oracle.gelu_erf_grad}
+
+
+@pytest.mark.parametrize("act", [ops.GELU_TANH, ops.GELU_ERF], ids=["tanh", "erf"])
+@pytest.mark.parametrize("M,N,K", [(64, 128, 64), (130, 272, 48), (2048, 3072, 768)])
+def test_bf16_dgelu_epilogue_on_exact_products(M, N, K, act):
+    """Exact products times gelu'(h): the bf16 output is the rounding of the
+    float64 value except within the fp32 gelu' error (4e-6 of |acc|) of a
+    midpoint."""
+    a, av = int_bf16((M, K), 9 + M, lim=3)
+    b, bv = int_bf16((N, K), 3 + N, lim=3)
+    h_bits = oracle.f64_to_bf16_bits(np.random.default_rng(M).normal(size=(M, N)) * 2.0)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ops.gemm_dgelu_bf16(bf16_dev(a), bf16_dev(b), bf16_dev(h_bits), out, activation=act)
+    torch.cuda.synchronize()
+    acc = av @ bv.T
+    ref = acc * GELU_GRAD[act](oracle.bf16_to_f64(h_bits))
+    stats = compare_bf16(to_np_bits(out), ref, 4e-6 * np.abs(acc))
+    print(f"dgelu bf16 {M}x{N}: {stats}")
+
+
+@pytest.mark.parametrize("act", [ops.GELU_TANH, ops.GELU_ERF], ids=["tanh", "erf"])
+@pytest.mark.parametrize("M,H,F", [(2048, 768, 3072), (144, 256, 400), (0, 64, 128)])
+def test_bf16_ln_mlp_bwd(M, H, F, act):
+    """The BF16 LayerNormMLP backward against the oracle fed the GPU forward's own
+    bf16 tensors (ln_out, h, g) and row statistics."""
+    wl = f"bf16mlpb/{M}/{H}/{F}"
+    x = inputs.normal_bf16((M, H), inputs.seed_for(wl, "x"))
+    g, b = inputs.layernorm_params(H, wl)
+    w1 = inputs.linear_weight(F, H, wl, "w1")
+    w2 = inputs.linear_weight(H, F, wl, "w2")
+    b1 = inputs.normal_bf16((F,), inputs.seed_for(wl, "b1"), std=0.1)
+    dy = inputs.normal_bf16((M, H), inputs.seed_for(wl, "dy"), std=1e-2)
+    d = lambda t: t.cuda()
+    f32 = lambda *s: torch.full(s, float("nan"), dtype=torch.float32, device="cuda")
+    bf = lambda *s: torch.empty(s, dtype=torch.bfloat16, device="cuda")
+    out, ln_out, hh, gg = bf(M, H), bf(M, H), bf(M, F), bf(M, F)
+    mean, rstd = f32(M), f32(M)
+    xd, gd, bd, w1d, w2d = d(x), d(g), d(b), d(w1), d(w2)
+    ops.ln_mlp_fwd_bf16(xd, gd, bd, w1d, d(b1), w2d, None, out, ln_out, gg, h=hh, mean=mean,
+                        rstd=rstd, activation=act)
+    dx = bf(M, H)
+    dgamma, dbeta, dw1, db1, dw2, db2 = f32(H), f32(H), f32(F, H), f32(F), f32(H, F), f32(H)
+    ops.ln_mlp_bwd_bf16(d(dy), xd, gd, w1d, w2d, ln_out, hh, gg, mean, rstd, dx, dgamma, dbeta,
+                        dw1, db1, dw2, db2, activation=act)
+    torch.cuda.synchronize()
+    if M == 0:
+        for t in (dgamma, dbeta, dw1, db1, dw2, db2):
+            assert not t.any().item()
+        return
+    ctx = dict(ln_bits=to_np_bits(ln_out), h_bits=to_np_bits(hh), g_bits=to_np_bits(gg),
+               mean=mean.cpu().numpy().astype(np.float64),
+               rstd=rstd.cpu().numpy().astype(np.float64))
+    og = oracle.ln_mlp_bwd_bf16(to_np_bits(dy), ctx, to_np_bits(x), to_np_bits(g),
+                                to_np_bits(w1), to_np_bits(w2), act)
+    assert_gemm_close(dw2.cpu().numpy(), og["dw2"], tol=1e-5, alarm=1e-5, what="dW2")
+    assert_vector_close(db2.cpu().numpy(), og["db2"], 1e-6, "db2")
+    # dH is rounded to bf16 on both sides; a value next to a midpoint may round
+    # the other way, which moves the sums below by far less than these bounds
+    assert_gemm_close(dw1.cpu().numpy(), og["dw1"], tol=1e-3, alarm=1e-3, what="dW1")
+    assert_vector_close(db1.cpu().numpy(), og["db1"], 1e-3, "db1")
+    assert_vector_close(dgamma.cpu().numpy(), og["dgamma"], 1e-3, "dgamma")
+    assert_vector_close(dbeta.cpu().numpy(), og["dbeta"], 1e-3, "dbeta")
+    gdx, odx = to_np(dx), og["dx"]
+    norms = np.linalg.norm(odx, axis=1)
+    assert np.all(np.abs(gdx - odx).max(axis=1) <= 1e-2 * norms + 1e-30)

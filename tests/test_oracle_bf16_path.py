@@ -123,3 +123,53 @@ def test_bf16_mlp_tracks_float64_autograd(act, approx):
     out, _ = oracle.ln_mlp_fwd_bf16(x, g, b, w1, b1, w2, b2, EPS, act)
     ref = _torch_mlp(x, g, b, w1, b1, w2, b2, approx).detach().numpy()
     assert rel_rows(out, ref) < 8e-3
+
+
+@pytest.mark.parametrize("act,approx", [(oracle.GELU_TANH, "tanh"), (oracle.GELU_ERF, "none")])
+def test_bf16_mlp_backward_tracks_float64_autograd(act, approx):
+    """The backward's only roundings are the stored bf16 h (for gelu'), bf16 g
+    (fc2's weight gradient) and bf16 dH; the gradients stay within those
+    roundings of float64 autograd."""
+    rng = np.random.default_rng(8)
+    M, H, Fd = 48, 64, 128
+    x, g, b = bits(rng.normal(size=(M, H))), bits(1 + 0.1 * rng.normal(size=H)), \
+        bits(0.1 * rng.normal(size=H))
+    w1, b1 = bits(0.1 * rng.normal(size=(Fd, H))), bits(0.1 * rng.normal(size=Fd))
+    w2, b2 = bits(0.1 * rng.normal(size=(H, Fd))), bits(0.1 * rng.normal(size=H))
+    dy = bits(1e-2 * rng.normal(size=(M, H)))
+    _, ctx = oracle.ln_mlp_fwd_bf16(x, g, b, w1, b1, w2, b2, EPS, act)
+    gr = oracle.ln_mlp_bwd_bf16(dy, ctx, x, g, w1, w2, act)
+    t = lambda a: torch.from_numpy(oracle.bf16_to_f64(a)).requires_grad_()
+    xt, gt, bt, w1t, b1t, w2t, b2t = map(t, (x, g, b, w1, b1, w2, b2))
+    y = F.layer_norm(xt, (H,), gt, bt, EPS)
+    out = F.gelu(y @ w1t.T + b1t, approximate=approx) @ w2t.T + b2t
+    out.backward(torch.from_numpy(oracle.bf16_to_f64(dy)))
+    assert rel_rows(gr["dw2"], w2t.grad.numpy()) < 1e-2
+    assert rel_rows(gr["dw1"], w1t.grad.numpy()) < 1e-2
+    assert rel_rows(gr["dx"], xt.grad.numpy()) < 1e-2
+    for got, ref in ((gr["db1"], b1t.grad), (gr["dgamma"], gt.grad), (gr["dbeta"], bt.grad)):
+        assert np.linalg.norm(got - ref.numpy()) / np.linalg.norm(ref.numpy()) < 1e-2
+    np.testing.assert_allclose(gr["db2"], b2t.grad.numpy(), rtol=1e-12, atol=0)
+
+
+def test_bf16_mlp_backward_on_unit_rows_with_linear_gelu_region():
+    """Large positive h (> 8) puts GELU where gelu(h) = h and gelu'(h) = 1 to far
+    below bf16 resolution: the backward is then the plain algebra of two linear
+    layers, dH = dy W2 (bf16), dW2 = dy^T g, dW1 = dH^T x."""
+    rng = np.random.default_rng(9)
+    M, H, Fd = 16, 32, 48
+    x = unit_rows(M, H, 10)
+    w1 = np.zeros((Fd, H))
+    b1 = 8.0 + rng.integers(0, 8, size=Fd)          # h = b1 >= 8 for every row
+    w2 = rng.integers(-2, 3, size=(H, Fd)) / 4.0
+    dy = rng.integers(-2, 3, size=(M, H)) / 8.0
+    args = (bits(x), bits(np.ones(H)), bits(np.zeros(H)), bits(w1), bits(b1), bits(w2),
+            bits(np.zeros(H)))
+    out, ctx = oracle.ln_mlp_fwd_bf16(*args, EPS)
+    np.testing.assert_array_equal(oracle.bf16_to_f64(ctx["g_bits"]), np.tile(b1, (M, 1)))
+    gr = oracle.ln_mlp_bwd_bf16(bits(dy), ctx, bits(x), bits(np.ones(H)), bits(w1), bits(w2))
+    dh = dy @ w2
+    np.testing.assert_array_equal(oracle.bf16_to_f64(gr["dh_bits"]), dh)
+    np.testing.assert_array_equal(gr["dw2"], dy.T @ np.tile(b1, (M, 1)))
+    np.testing.assert_array_equal(gr["dw1"], dh.T @ x)
+    np.testing.assert_array_equal(gr["db1"], dh.sum(axis=0))
