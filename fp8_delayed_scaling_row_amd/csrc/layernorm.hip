@@ -1,5 +1,5 @@
-// LayerNorm kernels: the fused forward (row statistics, affine, scale, FP8 cast,
-// per-tensor amax) and the backward (dx plus deterministic dgamma/dbeta).
+// The fused LayerNorm forward: row statistics, affine, scale, FP8 cast and
+// per-tensor amax in one pass (and the plain bf16-output LayerNorm).
 //
 // The fused modules normalise each row and feed the result to an FP8 linear
 // layer in one operation (tutorial "Accelerating Transformer Training with
@@ -217,145 +217,6 @@ hipError_t launch_ln_fwd_cpl(int64_t rows, int hidden, const void* x, const void
                                           out, mean, rstd, stream);
 }
 
-// ---- backward --------------------------------------------------------------
-
-// Per block: rows handled by its waves in grid-stride order; per lane: dgamma and
-// dbeta partial sums of its own columns.  Partials go to ws[block][2][hidden] and a
-// second kernel adds the blocks in a fixed order, so results are deterministic.
-// DY_BF16: dy arrives as bf16 (the plain LayerNorm module) instead of fp32 (the
-// dgrad GEMM's output inside the fused modules).
-template <int CPL, bool DY_BF16>
-__global__ __launch_bounds__(kThreads) void ln_bwd_kernel(
-    const void* __restrict__ dy_raw, const uint4* __restrict__ x, const float* __restrict__ mean,
-    const float* __restrict__ rstd, const uint4* __restrict__ gamma, uint4* __restrict__ dx,
-    float* __restrict__ partial, int64_t rows, int hidden) {
-    extern __shared__ float sm[];   // [2][hidden]: dgamma, dbeta of the block
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    const int nchunk = hidden / 8;
-    const float inv_h = 1.0f / (float)hidden;
-
-    float g[CPL * 8];
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-        const int c = lane + i * kWave;
-        if (c < nchunk) unpack_bf16x8(gamma[c], g + 8 * i);
-        else
-#pragma unroll
-            for (int k = 0; k < 8; ++k) g[8 * i + k] = 0.0f;
-    }
-    float dg[CPL * 8], db[CPL * 8];
-#pragma unroll
-    for (int j = 0; j < CPL * 8; ++j) { dg[j] = 0.0f; db[j] = 0.0f; }
-
-    for (int64_t row = (int64_t)blockIdx.x * kWavesPerBlock + wave; row < rows;
-         row += (int64_t)gridDim.x * kWavesPerBlock) {
-        const float mu = mean[row];
-        const float rs = rstd[row];
-        float xh[CPL * 8], d[CPL * 8];
-        float s1 = 0.0f, s2 = 0.0f;
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-            const int c = lane + i * kWave;
-            if (c < nchunk) {
-                unpack_bf16x8(load_nt(x + row * nchunk + c), xh + 8 * i);
-                if constexpr (DY_BF16) {
-                    unpack_bf16x8(load_nt((const uint4*)dy_raw + row * nchunk + c), d + 8 * i);
-                } else {
-                    const float4* dy = (const float4*)dy_raw;
-                    const float4 a = load_nt(dy + (row * nchunk + c) * 2);
-                    const float4 b2 = load_nt(dy + (row * nchunk + c) * 2 + 1);
-                    d[8 * i + 0] = a.x; d[8 * i + 1] = a.y; d[8 * i + 2] = a.z;
-                    d[8 * i + 3] = a.w; d[8 * i + 4] = b2.x; d[8 * i + 5] = b2.y;
-                    d[8 * i + 6] = b2.z; d[8 * i + 7] = b2.w;
-                }
-            } else {
-#pragma unroll
-                for (int k = 0; k < 8; ++k) { xh[8 * i + k] = mu; d[8 * i + k] = 0.0f; }
-            }
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int j = 8 * i + k;
-                xh[j] = (xh[j] - mu) * rs;
-                const float gj = d[j] * g[j];
-                s1 += gj;
-                s2 += gj * xh[j];
-                dg[j] += d[j] * xh[j];
-                db[j] += d[j];
-            }
-        }
-        const float c1 = wave_sum(s1) * inv_h;
-        const float c2 = wave_sum(s2) * inv_h;
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-            const int c = lane + i * kWave;
-            if (c < nchunk) {
-                float o[8];
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    const int j = 8 * i + k;
-                    o[k] = rs * (d[j] * g[j] - c1 - xh[j] * c2);
-                }
-                uint4 w;
-                w.x = pack_bf16x2(o[0], o[1]);
-                w.y = pack_bf16x2(o[2], o[3]);
-                w.z = pack_bf16x2(o[4], o[5]);
-                w.w = pack_bf16x2(o[6], o[7]);
-                store_nt(dx + row * nchunk + c, w);
-            }
-        }
-    }
-    // combine the block's waves in a fixed order (wave 0 first)
-    for (int w = 0; w < kWavesPerBlock; ++w) {
-        if (wave == w) {
-#pragma unroll
-            for (int i = 0; i < CPL; ++i) {
-                const int c = lane + i * kWave;
-                if (c < nchunk) {
-#pragma unroll
-                    for (int k = 0; k < 8; ++k) {
-                        float* pg = sm + c * 8 + k;
-                        float* pd = sm + hidden + c * 8 + k;
-                        *pg = w == 0 ? dg[8 * i + k] : *pg + dg[8 * i + k];
-                        *pd = w == 0 ? db[8 * i + k] : *pd + db[8 * i + k];
-                    }
-                }
-            }
-        }
-        __syncthreads();
-    }
-    float* pb = partial + (int64_t)blockIdx.x * 2 * hidden;
-    for (int j = threadIdx.x; j < 2 * hidden; j += kThreads) pb[j] = sm[j];
-}
-
-int ln_bwd_blocks(int64_t rows) {
-    const int64_t want = (rows + kWavesPerBlock - 1) / kWavesPerBlock;
-    const int64_t cap = 512;
-    return (int)(want < cap ? (want > 0 ? want : 1) : cap);
-}
-
-template <int CPL>
-hipError_t launch_ln_bwd_cpl(int64_t rows, int hidden, const void* dy, bool dy_bf16,
-                             const void* x, const float* mean, const float* rstd,
-                             const void* gamma, void* dx, float* dgamma, float* dbeta,
-                             void* workspace, hipStream_t stream) {
-    const int blocks = ln_bwd_blocks(rows);
-    const size_t smem = (size_t)2 * hidden * sizeof(float);
-    float* partial = (float*)workspace;
-    if (dy_bf16)
-        hipLaunchKernelGGL((ln_bwd_kernel<CPL, true>), dim3(blocks), dim3(kThreads), smem, stream,
-                           dy, (const uint4*)x, mean, rstd, (const uint4*)gamma, (uint4*)dx,
-                           partial, rows, hidden);
-    else
-        hipLaunchKernelGGL((ln_bwd_kernel<CPL, false>), dim3(blocks), dim3(kThreads), smem,
-                           stream, dy, (const uint4*)x, mean, rstd, (const uint4*)gamma,
-                           (uint4*)dx, partial, rows, hidden);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return launch_sum_partials(partial, blocks, 2 * (int64_t)hidden, dgamma, dbeta, hidden,
-                               stream);
-}
-
 }  // namespace
 
 hipError_t launch_ln_cast_amax(int64_t rows, int hidden, const void* x, const void* gamma,
@@ -377,27 +238,6 @@ hipError_t launch_ln_cast_amax(int64_t rows, int hidden, const void* x, const vo
                                     mean, rstd, stream);
     return launch_ln_fwd_cpl<16>(rows, hidden, x, gamma, beta, eps, fp8, scale, amax, out,
                                  mean, rstd, stream);
-}
-
-size_t ln_bwd_workspace(int64_t rows, int hidden) {
-    return (size_t)ln_bwd_blocks(rows) * 2 * (size_t)hidden * sizeof(float);
-}
-
-hipError_t launch_ln_bwd(int64_t rows, int hidden, const void* dy, bool dy_bf16, const void* x,
-                         const float* mean, const float* rstd, const void* gamma, void* dx,
-                         float* dgamma, float* dbeta, void* workspace, hipStream_t stream) {
-    const int chunks = hidden / 8;
-    if (chunks <= 64)
-        return launch_ln_bwd_cpl<1>(rows, hidden, dy, dy_bf16, x, mean, rstd, gamma, dx, dgamma, dbeta,
-                                    workspace, stream);
-    if (chunks <= 128)
-        return launch_ln_bwd_cpl<2>(rows, hidden, dy, dy_bf16, x, mean, rstd, gamma, dx, dgamma, dbeta,
-                                    workspace, stream);
-    if (chunks <= 256)
-        return launch_ln_bwd_cpl<4>(rows, hidden, dy, dy_bf16, x, mean, rstd, gamma, dx, dgamma, dbeta,
-                                    workspace, stream);
-    return launch_ln_bwd_cpl<8>(rows, hidden, dy, dy_bf16, x, mean, rstd, gamma, dx, dgamma, dbeta,
-                                workspace, stream);
 }
 
 }  // namespace fp8ln
