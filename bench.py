@@ -56,6 +56,8 @@ def parse():
                    help="counter run: N headline launches plus 3 plain 1 GiB copies")
     p.add_argument("--profile-gemm", type=int, nargs=4, metavar=("M", "N", "K", "REPS"),
                    help="counter run: REPS launches of one E4M3 GEMM (fp32 output)")
+    p.add_argument("--bf16", action="store_true",
+                   help="with --profile-gemm: the bf16 GEMM instead of the FP8 one")
     p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="write the counter summary of a --profile-ln run to profiles/")
     return p.parse_args()
@@ -598,8 +600,8 @@ def main():
         return
     if args.profile_gemm:
         M, N, K, reps = args.profile_gemm
-        ms = gemm_kernel_ms(torch, ops, M, N, K, torch.float32, reps=reps)
-        print(json.dumps(dict(profile_gemm=[M, N, K], reps=reps, kernel_ms=ms,
+        ms = gemm_kernel_ms(torch, ops, M, N, K, torch.float32, reps=reps, bf16=args.bf16)
+        print(json.dumps(dict(profile_gemm=[M, N, K], bf16=args.bf16, reps=reps, kernel_ms=ms,
                               tflops=2.0 * M * N * K / (ms * 1e-3) / 1e12)), flush=True)
         return
 

@@ -30,6 +30,8 @@
 // output rows.  Tiles are ordered so that the blocks of one XCD (blocks are
 // dealt to the 8 XCDs round robin) cover a compact band of the output and
 // share operands in their L2.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launchers.hpp"
 
@@ -88,6 +90,20 @@ __device__ __forceinline__ float gelu_erf_grad_f(float h) {
     const float e = erfcf(h * -0.70710678118654752f);
     const float d = __expf(-0.5f * h * h) * 0.39894228040143268f;   // 1 / sqrt(2 pi)
     return fmaf(h, d, 0.5f * e);
+}
+
+// The activation form as a compile-time choice.  Epilogues branch on the
+// (uniform) runtime flag once, around whole loops, so a value never pays for
+// both forms.
+template <bool ERF>
+__device__ __forceinline__ float act_f(float h) {
+    if constexpr (ERF) return gelu_erf_f(h);
+    else return gelu_f(h);
+}
+template <bool ERF>
+__device__ __forceinline__ float act_grad_f(float h) {
+    if constexpr (ERF) return gelu_erf_grad_f(h);
+    else return gelu_grad_f(h);
 }
 
 // LDS layout of one operand stage: 64-byte rows stored in pairs as 128-byte
@@ -407,23 +423,29 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p) {
         }
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __syncthreads();
+        auto scale_by_dgelu = [&](auto erf) __attribute__((always_inline)) {
+            constexpr bool ERF = decltype(erf)::value;
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+            for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
+                for (int j = 0; j < TN; ++j)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int lr = row_w + 32 * i;
-                    const int lc = col_w + 32 * j + 8 * q;
-                    const u32x2 hw = lds_ld<u32x2>(G::at(ring, lr, lc / 8) + 8 * fh);
-                    const bool ok = m0 + lr < M && n0 + lc < N;
-                    const float hv[4] = {bf16_lo(hw.x), bf16_hi(hw.x), bf16_lo(hw.y), bf16_hi(hw.y)};
+                    for (int q = 0; q < 4; ++q) {
+                        const int lr = row_w + 32 * i;
+                        const int lc = col_w + 32 * j + 8 * q;
+                        const u32x2 hw = lds_ld<u32x2>(G::at(ring, lr, lc / 8) + 8 * fh);
+                        const bool ok = m0 + lr < M && n0 + lc < N;
+                        const float hv[4] = {bf16_lo(hw.x), bf16_hi(hw.x), bf16_lo(hw.y),
+                                             bf16_hi(hw.y)};
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float gp = p.gelu_erf ? gelu_erf_grad_f(hv[e]) : gelu_grad_f(hv[e]);
-                        acc[j][i][4 * q + e] = ok ? acc[j][i][4 * q + e] * alpha * gp : 0.0f;
+                        for (int e = 0; e < 4; ++e) {
+                            const float gp = act_grad_f<ERF>(hv[e]);
+                            acc[j][i][4 * q + e] = ok ? acc[j][i][4 * q + e] * alpha * gp : 0.0f;
+                        }
                     }
-                }
+        };
+        if (p.gelu_erf) scale_by_dgelu(std::true_type{});
+        else scale_by_dgelu(std::false_type{});
         __syncthreads();   // h is consumed: the ring takes the codes next
     } else {
         // alpha (and the bias) in place; values outside the product become 0
@@ -457,7 +479,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p) {
     }
 
     if constexpr (EPI == kEpiDGeluF32 || EPI == kEpiDGeluBf16) {
-        // gelu'(h) from global memory, one 8-byte read per four values
+        // gelu'(h) from global memory, one 8-byte read per four values (here the
+        // per-value choice of the form measured faster than two loop copies)
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -533,17 +556,22 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p) {
         if (hdst) bf16_out(hdst);
     }
     if constexpr (EPI == kEpiDGeluBf16) bf16_out((uint16_t*)p.out);
-    if constexpr (EPI == kEpiGeluBf16) {
-        // rows and columns outside the product hold 0 and gelu(0) = 0
+    // gelu in place on every accumulator (values outside the product are 0, and
+    // gelu(0) = 0)
+    auto apply_gelu = [&](auto erf) __attribute__((always_inline)) {
+        constexpr bool ERF = decltype(erf)::value;
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    acc[j][i][r] = p.gelu_erf ? gelu_erf_f(acc[j][i][r]) : gelu_f(acc[j][i][r]);
-        bf16_out((uint16_t*)p.out);
+                for (int r = 0; r < 16; ++r) acc[j][i][r] = act_f<ERF>(acc[j][i][r]);
+    };
+    if constexpr (EPI == kEpiGeluBf16 || EPI == kEpiGeluFp8) {
+        if (p.gelu_erf) apply_gelu(std::true_type{});
+        else apply_gelu(std::false_type{});
     }
+    if constexpr (EPI == kEpiGeluBf16) bf16_out((uint16_t*)p.out);
 
     if constexpr (EPI == kEpiGeluFp8 || EPI == kEpiDGeluFp8) {
         // FP8 codes: first the row-major tile goes through the ring, then the
@@ -570,8 +598,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p) {
                     for (int e = 0; e < 4; ++e) {
                         float g;
                         if constexpr (EPI == kEpiGeluFp8) {
-                            g = p.gelu_erf ? gelu_erf_f(acc[j][i][4 * q + e])
-                                           : gelu_f(acc[j][i][4 * q + e]);
+                            g = acc[j][i][4 * q + e];   // gelu(h), applied above
                             gs[e] = g * qs;
                         } else {
                             g = acc[j][i][4 * q + e];
