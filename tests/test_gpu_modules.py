@@ -435,3 +435,97 @@ def test_modules_are_deterministic():
                        [t.clone() for t in grads])
     for a, c in zip(*results):
         assert torch.equal(a, c)
+
+
+def _oracle_meta(gpu: ops.Meta, fmt, n):
+    """The GPU state block as an oracle Meta (identical-input mode)."""
+    return oracle.Meta(gpu.history.cpu().numpy().copy(), gpu.scale.cpu().numpy().copy(),
+                       gpu.scale_inv.cpu().numpy().copy(), [fmt] * n)
+
+
+@pytest.mark.parametrize("fmt", [ops.FORMAT_HYBRID, ops.FORMAT_E4M3])
+def test_ln_mlp_x12_chain_layers_0_5_11(fmt):
+    """The 12-layer scale-up chain (16384 tokens, 2048 -> 8192 -> 2048, history
+    1024, each layer's output the next one's input, as the benchmark runs it), two
+    steps.  At layers 0, 5 and 11 of the second step the oracle takes the GPU's own
+    layer input, incoming gradient and state blocks (identical-input mode, so FP8
+    rounding flips do not compound across layers) and the layer's row-wise results
+    are compared on sampled tokens."""
+    M, H, F, L = 16384, 2048, 8192, 12
+    recipe = ops.Recipe(format=fmt, amax_history_len=1024)
+    orc = orecipe(recipe)
+    ffmt, bfmt = oracle.fwd_format(orc), oracle.bwd_format(orc)
+    wl = f"ln_mlp_x{L}_{M}x{H}x{F}"
+    rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(12).integers(0, M, 30)]))
+    rows_t = torch.from_numpy(rows).cuda()
+    x0 = inputs.normal_bf16((M, H), inputs.seed_for(wl, "x"), device="cuda")
+    dy = inputs.normal_bf16((M, H), inputs.seed_for(wl, "dy"), std=1e-3, device="cuda")
+    f32 = lambda *s: torch.empty(s, dtype=torch.float32, device="cuda")
+    layers = []
+    for l in range(L):
+        g, b = inputs.layernorm_params(H, f"{wl}/{l}")
+        w1 = inputs.linear_weight(F, H, f"{wl}/{l}", "w1")
+        w2 = inputs.linear_weight(H, F, f"{wl}/{l}", "w2")
+        mf, mb = ops.mlp_metas(recipe)
+        layers.append(dict(bits=[to_np_bits(t) for t in (g, b, w1, w2)],
+                           dev=[t.cuda() for t in (g, b, w1, w2)], mf=mf, mb=mb,
+                           ctx=ops.MlpCtx(M, H, F),
+                           out=torch.empty((M, H), dtype=torch.bfloat16, device="cuda"),
+                           grads=[f32(H), f32(H), f32(F, H), f32(F), f32(H, F), f32(H)]))
+    dxs = [torch.empty((M, H), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    checks = (0, 5, 11)
+    saved = {}
+    for step in range(2):
+        x = x0
+        for l, d in enumerate(layers):
+            g, b, w1, w2 = d["dev"]
+            ops.scaling_update(recipe, d["mf"])
+            if step == 1 and l in checks:
+                saved[l] = dict(x=to_np_bits(x[rows_t]), mf=_oracle_meta(d["mf"], ffmt, 4))
+            ops.ln_mlp_fwd(recipe, x, g, b, w1, None, w2, None, d["out"], d["mf"], d["ctx"])
+            x = d["out"]
+        grad = dy
+        for i in range(L):
+            l = L - 1 - i
+            d = layers[l]
+            xin = x0 if l == 0 else layers[l - 1]["out"]
+            ops.scaling_update(recipe, d["mb"])
+            if step == 1 and l in checks:
+                saved[l]["dy"] = to_np_bits(grad[rows_t])
+                saved[l]["mb"] = _oracle_meta(d["mb"], bfmt, 2)
+            dx = dxs[i % 2]
+            ops.ln_mlp_bwd(recipe, grad, xin, d["dev"][0], d["ctx"], d["mf"], d["mb"], dx,
+                           *d["grads"])
+            if step == 1 and l in checks:
+                saved[l]["dx"] = to_np(dx[rows_t])
+            grad = dx
+    torch.cuda.synchronize()
+    for l in checks:
+        d, sv = layers[l], saved[l]
+        gbits, bbits, w1bits, w2bits = d["bits"]
+        omf, omb = sv["mf"], sv["mb"]
+        oout, octx = oracle.ln_mlp_fwd(orc, omf, sv["x"], gbits, bbits, w1bits, None, w2bits,
+                                       None)
+        og = oracle.ln_mlp_bwd(orc, omf, omb, sv["dy"], octx, sv["x"], gbits)
+        ctx = d["ctx"]
+        tag = f"layer {l}"
+        assert_gemm_close(to_np(d["out"][rows_t]), oout, alarm=5e-2, what=f"{tag} out")
+        assert_gemm_close(to_np(ctx.h[rows_t]), octx["h"], alarm=5e-2, what=f"{tag} h")
+        gx, beta = ln_parts(sv["x"], gbits, bbits)
+        s0 = float(omf.scale[0])
+        exact = octx["y"] * s0
+        lnq = ctx.ln_q[rows_t].cpu().numpy()
+        compare_codes(lnq, exact, ffmt, ln_window(gx, beta, s0, exact))
+        np.testing.assert_array_equal(
+            ctx.w1_q.cpu().numpy(), octx["w1_q"], err_msg=f"{tag} fc1 weight codes")
+        alpha = np.float32(omf.scale_inv[0]) * np.float32(octx["w1_sinv"])
+        s2 = float(omf.scale[2])
+        win = gelu_code_window(octx["ln_q"], octx["w1_q"], ffmt, alpha, octx["h"], s2, H,
+                               recipe.activation)
+        d_ln = np.abs(oracle.fp8_decode(lnq, ffmt) - oracle.fp8_decode(octx["ln_q"], ffmt))
+        if d_ln.any():
+            w1abs = np.abs(oracle.fp8_decode(octx["w1_q"], ffmt))
+            win = win + s2 * 1.13 * float(alpha) * (d_ln @ w1abs.T)
+        stats = compare_codes(ctx.g_q[rows_t].cpu().numpy(), octx["g"] * s2, ffmt, win)
+        assert_gemm_close(sv["dx"], og["dx"], alarm=5e-2, what=f"{tag} dx")
+        print(f"{fmt} {tag}: g codes {stats}")
