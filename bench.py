@@ -42,6 +42,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, TFLOP/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense BF16 MFMA, TFLOP/s
 PROFILE_DIR = os.path.join(ROOT, "profiles")
+# sources of the headline LayerNorm kernel (a counter summary holds for these only)
+LN_SOURCES = ["layernorm.hip", "ln_fwd_body.hpp", "device_common.hpp"]
 
 
 def parse():
@@ -239,7 +241,7 @@ def summarize_counters(fetch_csv, write_csv):
     read_b = ln_fetch * 1024.0 * f_read
     write_b = ln_write * 1024.0 * f_write
     d = dict(kernel=ln_name, workload="ln_cast_amax_65536x2048",
-             source_hash=source_hash("layernorm.hip", "device_common.hpp"),
+             source_hash=source_hash(*LN_SOURCES),
              fetch_kib_per_launch=ln_fetch, write_kib_per_launch=ln_write,
              copy_kernel=cp_name, copy_fetch_kib=cp_fetch, copy_write_kib=cp_write,
              copy_scale_read=f_read, copy_scale_write=f_write,
@@ -676,7 +678,7 @@ def main():
     if head:
         gbs = head["bytes"] / (head["ms"] * 1e-3) / 1e9
         kgbs = head["bytes"] / (head["kernel_ms"] * 1e-3) / 1e9
-        traffic = counter_traffic("ln_cast_amax_65536x2048", ["layernorm.hip", "device_common.hpp"])
+        traffic = counter_traffic("ln_cast_amax_65536x2048", LN_SOURCES)
         line.update(value=round(gbs, 2), unit="GB/s", ms_per_step=round(head["ms"], 5),
                     eager_ms_per_step=round(head["eager_ms"], 5),
                     config=dict(workload="ln_cast_amax_65536x2048", rows=head["rows"],

@@ -1072,16 +1072,27 @@ int fp8ln_ln_linear_fwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_f
     hipStream_t st = as_stream(stream);
     const int f = meta_fp8(recipe, FP8LN_META_FORWARD);
     float* hist = fwd->amax_history;
-    if (M > 0) {
-        FP8LN_TRY(launch_ln_cast_amax(M, (int)K, x, gamma, beta, recipe->ln_eps, f, fwd->scale + 0,
-                                      hist + 0, ctx->ln_q, ctx->mean, ctx->rstd, st),
-                  "ln_cast_amax launch");
-        if (ctx->ln_qt) FP8LN_TRY(launch_transpose_u8(M, K, ctx->ln_q, ctx->ln_qt, st), "transpose");
-    }
     // FP8 weight storage: reuse the codes (and their scale_inv) of an earlier
     // forward of this ctx, or cast now and record the scale_inv that goes with them
     const float* w_sinv = ctx->w_scale_inv ? ctx->w_scale_inv : fwd->scale_inv + 1;
-    if (!ctx->reuse_weight_codes)
+    bool fused = false;   // LayerNorm rows and weight cast in one launch (small shapes)
+    if (M > 0 && !ctx->reuse_weight_codes) {
+        const CastJob wj{weight, N, K, fwd->scale + 1, hist + 1, ctx->w_q, ctx->w_qt,
+                         fwd->scale_inv + 1, ctx->w_scale_inv};
+        FP8LN_TRY(launch_fwd_prologue(M, (int)K, x, gamma, beta, recipe->ln_eps, f,
+                                      fwd->scale + 0, hist + 0, ctx->ln_q, ctx->mean, ctx->rstd,
+                                      &wj, 1, &fused, st),
+                  "forward prologue launch");
+    }
+    if (M > 0) {
+        if (!fused)
+            FP8LN_TRY(launch_ln_cast_amax(M, (int)K, x, gamma, beta, recipe->ln_eps, f,
+                                          fwd->scale + 0, hist + 0, ctx->ln_q, ctx->mean,
+                                          ctx->rstd, st),
+                      "ln_cast_amax launch");
+        if (ctx->ln_qt) FP8LN_TRY(launch_transpose_u8(M, K, ctx->ln_q, ctx->ln_qt, st), "transpose");
+    }
+    if (!ctx->reuse_weight_codes && !fused)
         FP8LN_TRY(launch_cast_amax(N, K, false, weight, f, fwd->scale + 1, hist + 1, ctx->w_q,
                                    ctx->w_qt, nullptr, nullptr, st, fwd->scale_inv + 1,
                                    ctx->w_scale_inv),
@@ -1200,18 +1211,32 @@ int fp8ln_ln_mlp_fwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t hidden,
     hipStream_t st = as_stream(stream);
     const int f = meta_fp8(recipe, FP8LN_META_FORWARD);
     float* hist = fwd->amax_history;
-    if (M > 0) {
-        FP8LN_TRY(launch_ln_cast_amax(M, (int)H, x, gamma, beta, recipe->ln_eps, f, fwd->scale + 0,
-                                      hist + 0, ctx->ln_q, ctx->mean, ctx->rstd, st),
-                  "ln_cast_amax launch");
-        if (ctx->ln_qt) FP8LN_TRY(launch_transpose_u8(M, H, ctx->ln_q, ctx->ln_qt, st), "transpose");
-    }
     // FP8 weight storage: reuse the codes (and their scale_inv) of an earlier
     // forward of this ctx, or cast now and record the scale_inv of each
     float* wsi = ctx->w_scale_inv;
     const float* w1_sinv = wsi ? wsi + 0 : fwd->scale_inv + 1;
     const float* w2_sinv = wsi ? wsi + 1 : fwd->scale_inv + 3;
-    if (!ctx->reuse_weight_codes) {
+    bool fused = false;   // LayerNorm rows and both weight casts in one launch (small shapes)
+    if (M > 0 && !ctx->reuse_weight_codes) {
+        const CastJob wj[2] = {
+            {w1, F, H, fwd->scale + 1, hist + 1, ctx->w1_q, ctx->w1_qt, fwd->scale_inv + 1,
+             wsi ? wsi + 0 : nullptr},
+            {w2, H, F, fwd->scale + 3, hist + 3, ctx->w2_q, ctx->w2_qt, fwd->scale_inv + 3,
+             wsi ? wsi + 1 : nullptr}};
+        FP8LN_TRY(launch_fwd_prologue(M, (int)H, x, gamma, beta, recipe->ln_eps, f,
+                                      fwd->scale + 0, hist + 0, ctx->ln_q, ctx->mean, ctx->rstd,
+                                      wj, 2, &fused, st),
+                  "forward prologue launch");
+    }
+    if (M > 0) {
+        if (!fused)
+            FP8LN_TRY(launch_ln_cast_amax(M, (int)H, x, gamma, beta, recipe->ln_eps, f,
+                                          fwd->scale + 0, hist + 0, ctx->ln_q, ctx->mean,
+                                          ctx->rstd, st),
+                      "ln_cast_amax launch");
+        if (ctx->ln_qt) FP8LN_TRY(launch_transpose_u8(M, H, ctx->ln_q, ctx->ln_qt, st), "transpose");
+    }
+    if (!ctx->reuse_weight_codes && !fused) {
         FP8LN_TRY(launch_cast_amax(F, H, false, w1, f, fwd->scale + 1, hist + 1, ctx->w1_q,
                                    ctx->w1_qt, nullptr, nullptr, st, fwd->scale_inv + 1,
                                    wsi ? wsi + 0 : nullptr),

@@ -51,16 +51,14 @@ __device__ __forceinline__ void store_nt(uint2* p, uint2 v) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// binary32 -> bf16, round to nearest even; NaN -> quiet NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
-}
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
+// Two binary32 values -> two bf16 (lo in the low half), rounded to nearest even
+// by gfx950's packed conversion (one v_cvt_pk_bf16_f32 for the pair); a NaN
+// stays a quiet NaN.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+    const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 // Unpack 8 bf16 values held in a 16-byte word.
@@ -170,9 +168,16 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return v;
 }
 
-// Block-wide max of amax bits followed by one atomic into *amax (a float whose
-// bits order like unsigned integers because it is never negative).  All threads of
-// the block must call it.  `smem` holds at least one uint32 per wave.
+// Block-wide max of amax bits followed by at most one atomic into *amax (a float
+// whose bits order like unsigned integers because it is never negative).  All
+// threads of the block must call it.  `smem` holds at least one uint32 per wave.
+//
+// Atomics on one address serialise in the L2 (some ten nanoseconds each), so a
+// grid of thousands of workgroups would queue thousands of them.  The stored
+// value only ever grows during a step, so any value read from it is at most its
+// final value: a block whose max does not exceed what it reads cannot change the
+// result and skips the atomic.  Typically only a handful of blocks, those that
+// raise the running max, issue one.
 __device__ __forceinline__ void block_amax_atomic(uint32_t bits, float* amax, uint32_t* smem) {
     bits = wave_max_u32(bits);
     const int lane = threadIdx.x & (kWave - 1);
@@ -183,7 +188,9 @@ __device__ __forceinline__ void block_amax_atomic(uint32_t bits, float* amax, ui
         uint32_t m = 0;
         const int nw = (blockDim.x + kWave - 1) / kWave;
         for (int w = 0; w < nw; ++w) m = smem[w] > m ? smem[w] : m;
-        if (m != 0) atomicMax(reinterpret_cast<unsigned int*>(amax), m);
+        unsigned int* a = reinterpret_cast<unsigned int*>(amax);
+        if (m != 0 && m > __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+            atomicMax(a, m);
     }
 }
 

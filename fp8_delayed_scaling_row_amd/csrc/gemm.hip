@@ -719,11 +719,15 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Large problems: with K up to 2048 the epilogue is a large share of a tile's
 // time, and two 128 x 256 workgroups per CU hide one's epilogue behind the
 // other's main loop; with longer K the 256 x 256 tile's lower LDS and L2
-// traffic per MFMA wins.  Smaller problems take 128 x 128 tiles, and 64 x 64
+// traffic per MFMA wins.  The plain epilogues (fp32 or bf16 + bias out) are
+// short enough that the 256 x 256 tile already wins at K = 2048 (16384 x 8192
+// x 2048, fp32 out: 314 against 330 us); the GELU and GELU' epilogues measured
+// faster on 128 x 256 there.  Smaller problems take 128 x 128 tiles, and 64 x 64
 // tiles when even those would leave most CUs idle (the fused dH epilogue needs
 // at least 64 columns per wave, so it stays on 128 x 128).
 TileShape pick_tile(int64_t M, int64_t N, int64_t K, int epi) {
-    const bool long_k = K > 2048;
+    const bool light = epi == kEpiF32 || epi == kEpiBf16Bias;
+    const bool long_k = light ? K >= 2048 : K > 2048;
     if (long_k && cdiv(M, 256) * cdiv(N, 256) >= 256) return kTile256;
     if (cdiv(M, 128) * cdiv(N, 256) >= 512) return kTile128x256;
     if (epi == kEpiDGeluFp8 || cdiv(M, 128) * cdiv(N, 128) >= 128) return kTile128;

@@ -30,6 +30,28 @@ hipError_t launch_ln_bwd(int64_t rows, int hidden, const void* dy, bool dy_bf16,
                          const float* mean, const float* rstd, const void* gamma, void* dx,
                          float* dgamma, float* dbeta, void* workspace, hipStream_t stream);
 
+// prologue.hip: the LayerNorm + cast + amax of the rows and up to two weight
+// casts (bf16 [rows][cols] -> codes, optional transposed copy, amax, scale_inv
+// copy as in launch_cast_amax) in one launch.  Launches only when every workgroup
+// fits on the GPU at once and hidden <= 2048; *launched says whether it did (the
+// caller otherwise launches the kernels one by one).
+constexpr int kMaxPrologueCasts = 2;
+struct CastJob {
+    const void* in;
+    int64_t rows, cols;
+    const float* scale;
+    float* amax;
+    uint8_t* out;
+    uint8_t* out_t;
+    const float* copy_src;
+    float* copy_dst;
+};
+hipError_t launch_fwd_prologue(int64_t rows, int hidden, const void* x, const void* gamma,
+                               const void* beta, float eps, int fp8, const float* scale,
+                               float* amax, uint8_t* out, float* mean, float* rstd,
+                               const CastJob* casts, int n_casts, bool* launched,
+                               hipStream_t stream);
+
 // cast.hip
 size_t cast_workspace(int64_t rows, int64_t cols);
 // copy_src / copy_dst: when given, *copy_dst = *copy_src is done by the cast

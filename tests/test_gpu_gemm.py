@@ -36,9 +36,9 @@ def dev(a):
 
 @pytest.mark.parametrize("fa,fb", PAIRS, ids=["e4m3xe4m3", "e5m2xe4m3", "e4m3xe5m2", "e5m2xe5m2"])
 @pytest.mark.parametrize("M,N,K", [(16, 16, 128), (128, 128, 256), (130, 144, 272), (1, 16, 16),
-                                   (257, 400, 64)])
+                                   (257, 400, 64), (96, 208, 1024)])
 def test_small_integer_gemm_is_bit_exact(fa, fb, M, N, K):
-    """|a|, |b| <= 8 and K <= 272: every partial sum is an integer below 2^24, so
+    """|a|, |b| <= 8 and K <= 1024: every partial sum is an integer below 2^24, so
     fp32 accumulation in any order is exact."""
     a, av = int_codes((M, K), fa, M * 7 + K)
     b, bv = int_codes((N, K), fb, N * 3 + K)

@@ -529,3 +529,92 @@ def test_ln_mlp_x12_chain_layers_0_5_11(fmt):
         stats = compare_codes(ctx.g_q[rows_t].cpu().numpy(), octx["g"] * s2, ffmt, win)
         assert_gemm_close(sv["dx"], og["dx"], alarm=5e-2, what=f"{tag} dx")
         print(f"{fmt} {tag}: g codes {stats}")
+
+
+# ---- the fused forward front equals the standalone kernels -----------------------
+
+def _set_meta(meta, scales):
+    meta.scale.copy_(torch.tensor(scales, dtype=torch.float32))
+    meta.scale_inv.copy_(1.0 / meta.scale)
+    meta.history.zero_()
+
+
+@pytest.mark.parametrize("M,K,N,fmt", [(256, 768, 2304, ops.FORMAT_HYBRID),
+                                       (80, 1008, 208, ops.FORMAT_E5M2),
+                                       (2048, 768, 2304, ops.FORMAT_E4M3)],
+                         ids=["8x32_tokens", "ragged", "2048_tokens"])
+def test_ln_linear_fwd_equals_standalone_entry_points(M, K, N, fmt):
+    """At small shapes the forward runs the LayerNorm rows and the weight cast in
+    one launch; its codes, row statistics, amaxes and output must equal, bit for
+    bit, those of the standalone LayerNorm+cast, cast and GEMM entry points fed
+    the same scales."""
+    recipe = ops.Recipe(format=fmt, amax_history_len=16)
+    wl = f"prologue/{M}x{K}x{N}"
+    x = inputs.normal_bf16((M, K), inputs.seed_for(wl, "x"), std=2.0, mean=0.5).cuda()
+    g, b = (t.cuda() for t in inputs.layernorm_params(K, wl))
+    w = inputs.linear_weight(N, K, wl, "w").cuda()
+    bias = inputs.normal_bf16((N,), inputs.seed_for(wl, "bias"), std=0.1).cuda()
+    ma, _ = ops.linear_metas(recipe)
+    mb, _ = ops.linear_metas(recipe)
+    for m in (ma, mb):
+        _set_meta(m, [3.25, 1791.0])
+    ctx = ops.LinearCtx(M, K, N, training=True)
+    out_a = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ops.ln_linear_fwd(recipe, x, g, b, w, bias, out_a, ma, ctx)
+
+    f = ops.fwd_fp8(recipe)
+    ln_q = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    ln_qt = torch.empty((K, M), dtype=torch.uint8, device="cuda")
+    mean = torch.empty(M, dtype=torch.float32, device="cuda")
+    rstd = torch.empty(M, dtype=torch.float32, device="cuda")
+    w_q = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+    w_qt = torch.empty((K, N), dtype=torch.uint8, device="cuda")
+    out_b = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ops.ln_cast_amax(recipe, x, g, b, f, mb.scale[0:1], mb.amax_ptr(0), ln_q, ln_qt, mean, rstd)
+    ops.cast_amax(w, f, mb.scale[1:2], mb.amax_ptr(1), w_q, w_qt)
+    ops.gemm(ln_q, f, w_q, f, mb.scale_inv[0:1], mb.scale_inv[1:2], out_b, bias)
+    torch.cuda.synchronize()
+    assert torch.equal(ctx.ln_q, ln_q) and torch.equal(ctx.ln_qt, ln_qt)
+    assert torch.equal(ctx.w_q, w_q) and torch.equal(ctx.w_qt, w_qt)
+    assert torch.equal(ctx.mean.view(torch.int32), mean.view(torch.int32))
+    assert torch.equal(ctx.rstd.view(torch.int32), rstd.view(torch.int32))
+    assert torch.equal(ma.history.view(torch.int32), mb.history.view(torch.int32))
+    assert torch.equal(out_a.view(torch.int16), out_b.view(torch.int16))
+    assert float(ctx.w_scale_inv.item()) == float(mb.scale_inv[1].item())
+
+
+@pytest.mark.parametrize("M,H,F", [(2048, 768, 3072), (96, 512, 1040)])
+def test_ln_mlp_fwd_front_equals_standalone_entry_points(M, H, F):
+    """The MLP forward's fused front (LayerNorm rows and both weight casts in one
+    launch) against the standalone entry points, bit for bit: LayerNorm codes,
+    statistics, weight codes and the amaxes of those three slots."""
+    recipe = ops.Recipe(format=ops.FORMAT_E4M3, amax_history_len=16)
+    wl = f"prologue-mlp/{M}x{H}x{F}"
+    x = inputs.normal_bf16((M, H), inputs.seed_for(wl, "x")).cuda()
+    g, b = (t.cuda() for t in inputs.layernorm_params(H, wl))
+    w1 = inputs.linear_weight(F, H, wl, "w1").cuda()
+    w2 = inputs.linear_weight(H, F, wl, "w2").cuda()
+    ma, _ = ops.mlp_metas(recipe)
+    mb, _ = ops.mlp_metas(recipe)
+    for m in (ma, mb):
+        _set_meta(m, [5.5, 2100.0, 11.0, 1900.0])
+    ctx = ops.MlpCtx(M, H, F, training=True)
+    out = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+    ops.ln_mlp_fwd(recipe, x, g, b, w1, None, w2, None, out, ma, ctx)
+    f = ops.fwd_fp8(recipe)
+    ln_q = torch.empty((M, H), dtype=torch.uint8, device="cuda")
+    mean = torch.empty(M, dtype=torch.float32, device="cuda")
+    rstd = torch.empty(M, dtype=torch.float32, device="cuda")
+    w1_q, w1_qt = (torch.empty(s, dtype=torch.uint8, device="cuda") for s in ((F, H), (H, F)))
+    w2_q, w2_qt = (torch.empty(s, dtype=torch.uint8, device="cuda") for s in ((H, F), (F, H)))
+    ops.ln_cast_amax(recipe, x, g, b, f, mb.scale[0:1], mb.amax_ptr(0), ln_q, None, mean, rstd)
+    ops.cast_amax(w1, f, mb.scale[1:2], mb.amax_ptr(1), w1_q, w1_qt)
+    ops.cast_amax(w2, f, mb.scale[3:4], mb.amax_ptr(3), w2_q, w2_qt)
+    torch.cuda.synchronize()
+    assert torch.equal(ctx.ln_q, ln_q)
+    assert torch.equal(ctx.mean.view(torch.int32), mean.view(torch.int32))
+    assert torch.equal(ctx.rstd.view(torch.int32), rstd.view(torch.int32))
+    assert torch.equal(ctx.w1_q, w1_q) and torch.equal(ctx.w1_qt, w1_qt)
+    assert torch.equal(ctx.w2_q, w2_q) and torch.equal(ctx.w2_qt, w2_qt)
+    for s in (0, 1, 3):
+        assert ma.history[0, s].view(torch.int32).item() == mb.history[0, s].view(torch.int32).item()
