@@ -60,6 +60,8 @@ def parse():
                    help="counter run: REPS launches of one E4M3 GEMM (fp32 output)")
     p.add_argument("--bf16", action="store_true",
                    help="with --profile-gemm: the bf16 GEMM instead of the FP8 one")
+    p.add_argument("--oracle-workloads", action="store_true",
+                   help="time the oracle on each GEMM-bound workload's shapes (host only)")
     p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="write the counter summary of a --profile-ln run to profiles/")
     return p.parse_args()
@@ -580,8 +582,87 @@ def cpu_baseline(inputs, budget_s=12.0):
                        f"({dt:.1f} s, numpy float64, single thread)")
 
 
+def oracle_workloads(inputs, log):
+    """The oracle (numpy float64; its GEMMs are float64 BLAS products) timed on one
+    step of each GEMM-bound workload's shapes on this host: LayerNormLinear forward
+    at 8 x 32 tokens, its backward at 2048 tokens, LayerNormMLP forward at 2048
+    tokens, and one layer (forward + backward) of the 16384-token 2048/8192
+    scale-up, whose 12-layer step is that time x 12."""
+    import numpy as np
+    import torch
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max((d.get("num_threads", 1) for d in threadpool_info()), default=1)
+    except Exception:   # noqa: BLE001 - the count is informational
+        blas_threads = None
+    bits = lambda t: t.view(torch.int16).numpy().view(np.uint16)
+    orc = oracle.Recipe(format=oracle.FORMAT_HYBRID, amax_history_len=16)
+
+    def linear_parts(M, K, N, wl):
+        g, b = inputs.layernorm_params(K, wl)
+        w = inputs.linear_weight(N, K, wl, "w")
+        x = inputs.normal_bf16((M, K), inputs.seed_for(wl, "x"))
+        dy = inputs.normal_bf16((M, N), inputs.seed_for(wl, "dy"), std=1e-3)
+        return bits(x), bits(g), bits(b), bits(w), bits(dy)
+
+    def mlp_parts(M, H, F, wl):
+        g, b = inputs.layernorm_params(H, wl)
+        w1 = inputs.linear_weight(F, H, wl, "w1")
+        w2 = inputs.linear_weight(H, F, wl, "w2")
+        x = inputs.normal_bf16((M, H), inputs.seed_for(wl, "x"))
+        dy = inputs.normal_bf16((M, H), inputs.seed_for(wl, "dy"), std=1e-3)
+        return bits(x), bits(g), bits(b), bits(w1), bits(w2), bits(dy)
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        r = fn()
+        return time.perf_counter() - t0, r
+
+    out = []
+    # LayerNormLinear fwd, 256 tokens, 768 -> 2304
+    x, g, b, w, dy = linear_parts(256, 768, 2304, "oracle/ln_linear_fwd")
+    mf = oracle.linear_fwd_meta(orc)
+    dt, _ = timed(lambda: oracle.ln_linear_fwd(orc, mf, x, g, b, w))
+    out.append(dict(workload="ln_linear_fwd", oracle_ms=dt * 1e3, flops=2.0 * 256 * 2304 * 768))
+    # LayerNormLinear bwd, 2048 tokens
+    x, g, b, w, dy = linear_parts(2048, 768, 2304, "oracle/ln_linear_bwd")
+    mf, mb = oracle.linear_fwd_meta(orc), oracle.linear_bwd_meta(orc)
+    _, (o, ctx) = timed(lambda: oracle.ln_linear_fwd(orc, mf, x, g, b, w))
+    dt, _ = timed(lambda: oracle.ln_linear_bwd(orc, mf, mb, dy, ctx, x, g))
+    out.append(dict(workload="ln_linear_bwd", oracle_ms=dt * 1e3,
+                    flops=2 * 2.0 * 2048 * 2304 * 768))
+    # LayerNormMLP fwd, 2048 tokens, 768 -> 3072 -> 768
+    orc4 = oracle.Recipe(format=oracle.FORMAT_E4M3, amax_history_len=16)
+    x, g, b, w1, w2, dy = mlp_parts(2048, 768, 3072, "oracle/ln_mlp_fwd")
+    mf = oracle.mlp_fwd_meta(orc4)
+    dt, _ = timed(lambda: oracle.ln_mlp_fwd(orc4, mf, x, g, b, w1, None, w2, None))
+    out.append(dict(workload="ln_mlp_fwd", oracle_ms=dt * 1e3, flops=2 * 2.0 * 2048 * 3072 * 768))
+    # one layer of the scale-up, forward + backward
+    log("oracle: one 16384 x 2048 x 8192 layer ...")
+    orc_h = oracle.Recipe(format=oracle.FORMAT_HYBRID, amax_history_len=1024)
+    x, g, b, w1, w2, dy = mlp_parts(16384, 2048, 8192, "oracle/ln_mlp_x12")
+    mf, mb = oracle.mlp_fwd_meta(orc_h), oracle.mlp_bwd_meta(orc_h)
+    dtf, (o, ctx) = timed(lambda: oracle.ln_mlp_fwd(orc_h, mf, x, g, b, w1, None, w2, None))
+    log(f"oracle: layer forward {dtf:.1f} s; backward ...")
+    dtb, _ = timed(lambda: oracle.ln_mlp_bwd(orc_h, mf, mb, dy, ctx, x, g))
+    log(f"oracle: layer backward {dtb:.1f} s")
+    out.append(dict(workload="ln_mlp_x12_hybrid", oracle_ms_one_layer=(dtf + dtb) * 1e3,
+                    oracle_ms=(dtf + dtb) * 12e3, extrapolated_from="one layer x 12",
+                    flops=12 * 6 * 2.0 * 16384 * 8192 * 2048))
+    for r in out:
+        r["oracle_tflops"] = r["flops"] / (r["oracle_ms"] * 1e-3) / 1e12
+    return dict(kind="oracle", blas_threads=blas_threads, cores=os.cpu_count(),
+                workloads=out)
+
+
 def main():
     args = parse()
+    if args.oracle_workloads:
+        from fp8_delayed_scaling_row_amd import inputs
+        print(json.dumps(dict(oracle_workloads=oracle_workloads(
+            inputs, lambda m: print(m, file=sys.stderr, flush=True)))), flush=True)
+        return
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
         return

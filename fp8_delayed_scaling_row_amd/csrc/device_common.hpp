@@ -172,12 +172,16 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // whose bits order like unsigned integers because it is never negative).  All
 // threads of the block must call it.  `smem` holds at least one uint32 per wave.
 //
-// Atomics on one address serialise in the L2 (some ten nanoseconds each), so a
-// grid of thousands of workgroups would queue thousands of them.  The stored
-// value only ever grows during a step, so any value read from it is at most its
-// final value: a block whose max does not exceed what it reads cannot change the
-// result and skips the atomic.  Typically only a handful of blocks, those that
-// raise the running max, issue one.
+// Atomics on one address serialise in the L2 (some ten nanoseconds each), so the
+// thousands of workgroups of a streaming kernel, which all finish together,
+// would queue thousands of them.  The stored value only ever grows during a
+// step, so any value read from it is at most its final value: with CHECK, a
+// block whose max does not exceed what it reads cannot change the result and
+// skips the atomic; typically only a handful of blocks, those that raise the
+// running max, issue one.  GEMM epilogues finish spread over the whole kernel,
+// where the atomics do not queue and the read would only add a round trip to
+// each tile's end: they call it without CHECK.
+template <bool CHECK = true>
 __device__ __forceinline__ void block_amax_atomic(uint32_t bits, float* amax, uint32_t* smem) {
     bits = wave_max_u32(bits);
     const int lane = threadIdx.x & (kWave - 1);
@@ -189,7 +193,8 @@ __device__ __forceinline__ void block_amax_atomic(uint32_t bits, float* amax, ui
         const int nw = (blockDim.x + kWave - 1) / kWave;
         for (int w = 0; w < nw; ++w) m = smem[w] > m ? smem[w] : m;
         unsigned int* a = reinterpret_cast<unsigned int*>(amax);
-        if (m != 0 && m > __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+        if (m != 0 &&
+            (!CHECK || m > __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)))
             atomicMax(a, m);
     }
 }

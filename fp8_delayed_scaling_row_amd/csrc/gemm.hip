@@ -348,9 +348,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p) {
     // workgroup fence, which waits for every outstanding load, the prefetched
     // stages included.  The barrier also waits for the wave's own LDS reads, so
     // no wave refills a stage another wave is still reading.  Every step looks
-    // the same: past the end of K the stages are filled with zeros (all chunks
-    // out of range), which add nothing to the sums, so the wait count is a
-    // constant and the loop runs a multiple of NS steps.
+    // the same: the look-ahead stages past the end of K are filled with zeros
+    // (all chunks out of range), so the wait count is a constant.
     auto step = [&](uint8_t* cur, uint8_t* refill, int kt) {
         // Scheduling fences keep the wait, the barrier and the refill at the top
         // of the step: left to itself the scheduler sinks the refill below the
@@ -364,23 +363,32 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p) {
         compute(cur);
     };
 
+    // Whole rounds of NS steps, then the last nk % NS steps one by one (the same
+    // step code, so the waits stay constant; only stages past K are zero-filled,
+    // and no step multiplies one).
     const int nk = (int)((K + BKS - 1) / BKS);
+    int kt = 0;
     issue(st0, 0);
     issue(st1, BKS);
     if constexpr (NS == 4) {
         issue(st2, 2 * BKS);
-        for (int kt = 0; kt < nk; kt += 4) {
+        for (; kt + 4 <= nk; kt += 4) {
             step(st0, st3, kt);
             step(st1, st0, kt + 1);
             step(st2, st1, kt + 2);
             step(st3, st2, kt + 3);
         }
+        if (kt < nk) step(st0, st3, kt);
+        if (kt + 1 < nk) step(st1, st0, kt + 1);
+        if (kt + 2 < nk) step(st2, st1, kt + 2);
     } else {
-        for (int kt = 0; kt < nk; kt += 3) {
+        for (; kt + 3 <= nk; kt += 3) {
             step(st0, st2, kt);
             step(st1, st0, kt + 1);
             step(st2, st1, kt + 2);
         }
+        if (kt < nk) step(st0, st2, kt);
+        if (kt + 1 < nk) step(st1, st0, kt + 1);
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // the zero-filled look-ahead stages
     __syncthreads();                            // the ring is free for the epilogue
@@ -677,7 +685,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p) {
             }
         }
         __shared__ uint32_t red[NW];
-        block_amax_atomic(amax_bits, p.q_amax, red);
+        block_amax_atomic<false>(amax_bits, p.q_amax, red);
     }
 }
 

@@ -223,7 +223,10 @@ def test_gelu_gemm_random_within_tolerance(M, N, K):
 
 # 128 x 256 tiles (K <= 2048; the second is ragged in M and N), then 256 x 256
 # tiles (K > 2048)
-BIG = [(4096, 4096, 64), (4000, 4112, 48), (2048, 8192, 2176)]
+# K steps of 64 bytes left after whole rounds of the ring: 256 x 256 tiles (four
+# stages) with 2, 1 and 3 steps over, 128 x 256 tiles (three stages) with 1 and 2
+BIG = [(4096, 4096, 64), (4000, 4112, 48), (2048, 8192, 2176), (2048, 8192, 2112),
+       (2048, 8192, 2240), (4096, 4096, 320)]
 
 
 @pytest.mark.parametrize("fa,fb", PAIRS, ids=["e4m3xe4m3", "e5m2xe4m3", "e4m3xe5m2", "e5m2xe5m2"])
