@@ -720,11 +720,11 @@ def main():
             ("ln_mlp_fwd_16384_bf16", "LayerNormMLP fwd 16384 tokens, 2048->8192->2048, bf16 (no FP8)",
              lambda: bench_mlp_fwd_bf16(torch, ops, inputs, 20, 3, M=16384, H=2048, F=8192)),
             ("ln_mlp_x12_hybrid", "LayerNormMLP x12 fwd+bwd, 16384 tokens, 2048->8192->2048, HYBRID, history 1024",
-             lambda: bench_mlp_stack(torch, ops, inputs, 5, 2, ops.FORMAT_HYBRID)),
+             lambda: bench_mlp_stack(torch, ops, inputs, 20, 5, ops.FORMAT_HYBRID)),
             ("ln_mlp_x12_e4m3", "LayerNormMLP x12 fwd+bwd, 16384 tokens, 2048->8192->2048, E4M3, history 1024",
-             lambda: bench_mlp_stack(torch, ops, inputs, 5, 2, ops.FORMAT_E4M3)),
+             lambda: bench_mlp_stack(torch, ops, inputs, 20, 5, ops.FORMAT_E4M3)),
             ("ln_mlp_x12_bf16", "LayerNormMLP x12 fwd+bwd, 16384 tokens, 2048->8192->2048, bf16 (no FP8)",
-             lambda: bench_mlp_stack_bf16(torch, ops, inputs, 5, 2)),
+             lambda: bench_mlp_stack_bf16(torch, ops, inputs, 20, 5)),
         ]
         for name, desc, fn in runs:
             if args.only not in (None, name):
