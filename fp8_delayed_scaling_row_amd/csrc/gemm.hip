@@ -197,8 +197,14 @@ __device__ __forceinline__ void butterfly_sum(float* v, int fr) {
     butterfly_step<NV / 16, 1>(v, fr);
 }
 
-template <int BM, int BN, int WGM, int WGN, int NS, int FA, int FB, int EPI, int QF>
+// EPIX = epilogue + 16 ACT: ACT 1 and 2 fix the GELU form at compile time (tanh,
+// erf) for the GELU / GELU' epilogues whose loops would otherwise be compiled
+// once per form behind a runtime branch, which makes the register allocator
+// spill the accumulators; ACT 0 reads the form from the parameters.
+template <int BM, int BN, int WGM, int WGN, int NS, int FA, int FB, int EPIX, int QF>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p) {
+    constexpr int EPI = EPIX % 16;
+    constexpr int ACT = EPIX / 16;
     static_assert(NS == 3 || NS == 4, "three or four pipeline stages");
     constexpr int NW = WGM * WGN;              // waves per workgroup
     constexpr int WM = BM / WGM, WN = BN / WGN;  // wave sub-tile
@@ -452,8 +458,12 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p) {
                         }
                     }
         };
-        if (p.gelu_erf) scale_by_dgelu(std::true_type{});
-        else scale_by_dgelu(std::false_type{});
+        if constexpr (ACT != 0) {
+            scale_by_dgelu(std::integral_constant<bool, ACT == 2>{});
+        } else {
+            if (p.gelu_erf) scale_by_dgelu(std::true_type{});
+            else scale_by_dgelu(std::false_type{});
+        }
         __syncthreads();   // h is consumed: the ring takes the codes next
     } else {
         // alpha (and the bias) in place; values outside the product become 0
@@ -576,8 +586,12 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p) {
                 for (int r = 0; r < 16; ++r) acc[j][i][r] = act_f<ERF>(acc[j][i][r]);
     };
     if constexpr (EPI == kEpiGeluBf16 || EPI == kEpiGeluFp8) {
-        if (p.gelu_erf) apply_gelu(std::true_type{});
-        else apply_gelu(std::false_type{});
+        if constexpr (ACT != 0) {
+            apply_gelu(std::integral_constant<bool, ACT == 2>{});
+        } else {
+            if (p.gelu_erf) apply_gelu(std::true_type{});
+            else apply_gelu(std::false_type{});
+        }
     }
     if constexpr (EPI == kEpiGeluBf16) bf16_out((uint16_t*)p.out);
 
@@ -744,7 +758,7 @@ TileShape pick_tile(int64_t M, int64_t N, int64_t K, int epi) {
 
 template <int FA, int FB, int EPI, int QF>
 hipError_t launch_typed(const GemmParams& p, hipStream_t stream) {
-    switch (pick_tile(p.M, p.N, p.K, EPI)) {
+    switch (pick_tile(p.M, p.N, p.K, EPI % 16)) {
         case kTile256:
             hipLaunchKernelGGL((gemm_kernel_256<FA, FB, EPI, QF>),
                                dim3((unsigned)(cdiv(p.M, 256) * cdiv(p.N, 256))), dim3(512), 0,
@@ -756,7 +770,7 @@ hipError_t launch_typed(const GemmParams& p, hipStream_t stream) {
                                stream, p);
             break;
         case kTile64:
-            if constexpr (EPI != kEpiDGeluFp8) {
+            if constexpr (EPI % 16 != kEpiDGeluFp8) {
                 hipLaunchKernelGGL((gemm_kernel_64<FA, FB, EPI, QF>),
                                    dim3((unsigned)(cdiv(p.M, 64) * cdiv(p.N, 64))), dim3(256), 0,
                                    stream, p);
@@ -771,6 +785,14 @@ hipError_t launch_typed(const GemmParams& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// The GELU form as a compile-time part of the epilogue (epilogue + 16 for tanh,
+// + 32 for erf) where a runtime choice would spill.
+template <int FA, int FB, int EPI, int QF>
+hipError_t launch_act(const GemmParams& p, hipStream_t stream) {
+    return p.gelu_erf ? launch_typed<FA, FB, EPI + 32, QF>(p, stream)
+                      : launch_typed<FA, FB, EPI + 16, QF>(p, stream);
+}
+
 template <int FA, int FB>
 hipError_t launch_epi(const GemmParams& p, hipStream_t stream) {
     switch (p.epilogue) {
@@ -778,11 +800,11 @@ hipError_t launch_epi(const GemmParams& p, hipStream_t stream) {
         case kEpiF32: return launch_typed<FA, FB, kEpiF32, kE4M3>(p, stream);
         case kEpiDGeluF32: return launch_typed<FA, FB, kEpiDGeluF32, kE4M3>(p, stream);
         case kEpiGeluFp8:
-            return p.q_fp8 == kE4M3 ? launch_typed<FA, FB, kEpiGeluFp8, kE4M3>(p, stream)
-                                    : launch_typed<FA, FB, kEpiGeluFp8, kE5M2>(p, stream);
+            return p.q_fp8 == kE4M3 ? launch_act<FA, FB, kEpiGeluFp8, kE4M3>(p, stream)
+                                    : launch_act<FA, FB, kEpiGeluFp8, kE5M2>(p, stream);
         case kEpiDGeluFp8:
-            return p.q_fp8 == kE4M3 ? launch_typed<FA, FB, kEpiDGeluFp8, kE4M3>(p, stream)
-                                    : launch_typed<FA, FB, kEpiDGeluFp8, kE5M2>(p, stream);
+            return p.q_fp8 == kE4M3 ? launch_act<FA, FB, kEpiDGeluFp8, kE4M3>(p, stream)
+                                    : launch_act<FA, FB, kEpiDGeluFp8, kE5M2>(p, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -799,7 +821,7 @@ static hipError_t launch_gemm_bf16(const GemmParams& p, hipStream_t stream) {
     switch (p.epilogue) {
         case kEpiBf16Bias: return launch_typed<kOpBf16, kOpBf16, kEpiBf16Bias, kE4M3>(q, stream);
         case kEpiF32: return launch_typed<kOpBf16, kOpBf16, kEpiF32, kE4M3>(q, stream);
-        case kEpiGeluBf16: return launch_typed<kOpBf16, kOpBf16, kEpiGeluBf16, kE4M3>(q, stream);
+        case kEpiGeluBf16: return launch_act<kOpBf16, kOpBf16, kEpiGeluBf16, kE4M3>(q, stream);
         case kEpiDGeluF32: return launch_typed<kOpBf16, kOpBf16, kEpiDGeluF32, kE4M3>(q, stream);
         case kEpiDGeluBf16: return launch_typed<kOpBf16, kOpBf16, kEpiDGeluBf16, kE4M3>(q, stream);
         default: return hipErrorInvalidValue;
