@@ -1153,12 +1153,13 @@ int fp8ln_ln_linear_bwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_f
                                 ctx->w_scale_inv ? ctx->w_scale_inv : fwd->scale_inv + 1,
                                 kEpiF32);
     dg.out = w.dln;
-    FP8LN_TRY(launch_gemm(dg, st), "dgrad launch");
     // wgrad: dW[N][K] = dy_qt[N][M] . (ln_qt[K][M])^T
     GemmParams wg = gemm_params(N, K, M, w.dy_qt, bf, ctx->ln_qt, ff, bwd->scale_inv + 0,
                                 fwd->scale_inv + 0, kEpiF32);
     wg.out = dweight;
-    FP8LN_TRY(launch_gemm(wg, st), "wgrad launch");
+    // independent products: one launch when both are small
+    const GemmParams grads[2] = {dg, wg};
+    FP8LN_TRY(launch_gemm_group(grads, 2, st), "dgrad / wgrad launch");
     FP8LN_TRY(launch_ln_bwd(M, (int)K, w.dln, false, x, ctx->mean, ctx->rstd, gamma, dx, dgamma, dbeta,
                             w.ln_ws, st),
               "layernorm_bwd launch");
@@ -1332,18 +1333,18 @@ int fp8ln_ln_mlp_bwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t hidden,
     GemmParams wg2 = gemm_params(H, F, M, w.dy_qt, bf, ctx->g_qt, ff, bwd->scale_inv + 0,
                                  fwd->scale_inv + 2, kEpiF32);
     wg2.out = dw2;
-    FP8LN_TRY(launch_gemm(wg2, st), "fc2 wgrad launch");
     // fc1 dgrad: dLN[M][H] = dh_q[M][F] . (w1_qt[H][F])^T
     GemmParams dg1 = gemm_params(M, H, F, w.dh_q, bf, ctx->w1_qt, ff, bwd->scale_inv + 1,
                                  ctx->w_scale_inv ? ctx->w_scale_inv + 0 : fwd->scale_inv + 1,
                                  kEpiF32);
     dg1.out = w.dln;
-    FP8LN_TRY(launch_gemm(dg1, st), "fc1 dgrad launch");
     // fc1 wgrad: dW1[F][H] = dh_qt[F][M] . (ln_qt[H][M])^T
     GemmParams wg1 = gemm_params(F, H, M, w.dh_qt, bf, ctx->ln_qt, ff, bwd->scale_inv + 1,
                                  fwd->scale_inv + 0, kEpiF32);
     wg1.out = dw1;
-    FP8LN_TRY(launch_gemm(wg1, st), "fc1 wgrad launch");
+    // three independent products: one launch when all are small
+    const GemmParams grads[3] = {wg2, dg1, wg1};
+    FP8LN_TRY(launch_gemm_group(grads, 3, st), "fc2 wgrad / fc1 dgrad / fc1 wgrad launch");
     FP8LN_TRY(launch_ln_bwd(M, (int)H, w.dln, false, x, ctx->mean, ctx->rstd, gamma, dx, dgamma, dbeta,
                             w.ln_ws, st),
               "layernorm_bwd launch");

@@ -201,8 +201,13 @@ __device__ __forceinline__ void butterfly_sum(float* v, int fr) {
 // erf) for the GELU / GELU' epilogues whose loops would otherwise be compiled
 // once per form behind a runtime branch, which makes the register allocator
 // spill the accumulators; ACT 0 reads the form from the parameters.
-template <int BM, int BN, int WGM, int WGN, int NS, int FA, int FB, int EPIX, int QF>
-__device__ __forceinline__ void gemm_tile(const GemmParams& p) {
+// vb: the tile's block index (the kernel's own, or its index inside one problem
+// of a grouped launch).  GROUP only tags the grouped kernel's instantiation (the
+// same specialization called from two kernels does not resolve in hipcc's host
+// pass).
+template <int BM, int BN, int WGM, int WGN, int NS, int FA, int FB, int EPIX, int QF,
+          bool GROUP = false>
+__device__ __forceinline__ void gemm_tile(const GemmParams& p, int vb) {
     constexpr int EPI = EPIX % 16;
     constexpr int ACT = EPIX / 16;
     static_assert(NS == 3 || NS == 4, "three or four pipeline stages");
@@ -230,7 +235,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p) {
     const int tiles_m = (int)((M + BM - 1) / BM);
     const int tiles_n = (int)((N + BN - 1) / BN);
     const int total = tiles_m * tiles_n;
-    int b = blockIdx.x;
+    int b = vb;
     if ((total & 7) == 0) b = (b & 7) * (total >> 3) + (b >> 3);   // one band per XCD
     const int per_group = kGroupM * tiles_n;
     const int first_m = (b / per_group) * kGroupM;
@@ -708,7 +713,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p) {
 template <int FA, int FB, int EPI, int QF>
 __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(512)
 void gemm_kernel_256(GemmParams p) {
-    gemm_tile<256, 256, 4, 2, 4, FA, FB, EPI, QF>(p);
+    gemm_tile<256, 256, 4, 2, 4, FA, FB, EPI, QF>(p, blockIdx.x);
 }
 
 // 128 x 256 tiles, four waves of 64 x 128 and a three-stage ring (72 KB), so two
@@ -716,14 +721,14 @@ void gemm_kernel_256(GemmParams p) {
 template <int FA, int FB, int EPI, int QF>
 __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(256)
 void gemm_kernel_128x256(GemmParams p) {
-    gemm_tile<128, 256, 2, 2, 3, FA, FB, EPI, QF>(p);
+    gemm_tile<128, 256, 2, 2, 3, FA, FB, EPI, QF>(p, blockIdx.x);
 }
 
 // 128 x 128 tiles, four waves of 64 x 64, two workgroups per CU.
 template <int FA, int FB, int EPI, int QF>
 __global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(256)
 void gemm_kernel_128(GemmParams p) {
-    gemm_tile<128, 128, 2, 2, 4, FA, FB, EPI, QF>(p);
+    gemm_tile<128, 128, 2, 2, 4, FA, FB, EPI, QF>(p, blockIdx.x);
 }
 
 // 64 x 64 tiles, four waves of 32 x 32, up to four workgroups per CU: for
@@ -731,7 +736,39 @@ void gemm_kernel_128(GemmParams p) {
 template <int FA, int FB, int EPI, int QF>
 __global__ __attribute__((amdgpu_waves_per_eu(4, 4))) __launch_bounds__(256)
 void gemm_kernel_64(GemmParams p) {
-    gemm_tile<64, 64, 2, 2, 4, FA, FB, EPI, QF>(p);
+    gemm_tile<64, 64, 2, 2, 4, FA, FB, EPI, QF>(p, blockIdx.x);
+}
+
+// Up to kMaxGemmGroup independent small fp32-output products in one launch:
+// blocks [start[k], start[k + 1]) are the tiles of product k, each computed
+// exactly as the kernel of that tile shape computes it alone.  Small problems leave
+// most CUs idle one by one; side by side their tiles share the GPU and their
+// launch latencies overlap.
+struct GemmGroup {
+    GemmParams p[kMaxGemmGroup];
+    int start[kMaxGemmGroup + 1];
+};
+
+template <int FA, int FB>
+__global__ __attribute__((amdgpu_waves_per_eu(4, 4))) __launch_bounds__(256)
+void gemm_kernel_64_group(GemmGroup g) {
+    const int b = blockIdx.x;
+    int k = 0;
+#pragma unroll
+    for (int j = 1; j < kMaxGemmGroup; ++j) k += b >= g.start[j];
+    gemm_tile<64, 64, 2, 2, 4, FA, FB, kEpiF32, kE4M3, true>(g.p[k], b - g.start[k]);
+}
+
+// The same on 128 x 128 tiles (half the LDS traffic per MFMA of 64 x 64 tiles),
+// when the grouped products together have enough of them to occupy the CUs.
+template <int FA, int FB>
+__global__ __attribute__((amdgpu_waves_per_eu(2, 2))) __launch_bounds__(256)
+void gemm_kernel_128_group(GemmGroup g) {
+    const int b = blockIdx.x;
+    int k = 0;
+#pragma unroll
+    for (int j = 1; j < kMaxGemmGroup; ++j) k += b >= g.start[j];
+    gemm_tile<128, 128, 2, 2, 4, FA, FB, kEpiF32, kE4M3, true>(g.p[k], b - g.start[k]);
 }
 
 enum TileShape { kTile256, kTile128x256, kTile128, kTile64 };
@@ -826,6 +863,55 @@ static hipError_t launch_gemm_bf16(const GemmParams& p, hipStream_t stream) {
         case kEpiDGeluBf16: return launch_typed<kOpBf16, kOpBf16, kEpiDGeluBf16, kE4M3>(q, stream);
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_gemm_group(const GemmParams* ps, int n, hipStream_t stream) {
+    bool grouped = n >= 2 && n <= kMaxGemmGroup;
+    int64_t tiles128 = 0;
+    for (int k = 0; grouped && k < n; ++k) {
+        const GemmParams& q = ps[k];
+        const TileShape ts = q.M > 0 && q.N > 0 ? pick_tile(q.M, q.N, q.K, kEpiF32) : kTile256;
+        grouped = q.epilogue == kEpiF32 && q.a_fp8 == ps[0].a_fp8 && q.b_fp8 == ps[0].b_fp8 &&
+                  q.a_fp8 != kOpBf16 && q.b_fp8 != kOpBf16 && (ts == kTile64 || ts == kTile128);
+        tiles128 += cdiv(q.M, 128) * cdiv(q.N, 128);
+    }
+    if (!grouped) {
+        for (int k = 0; k < n; ++k) {
+            const hipError_t e = launch_gemm(ps[k], stream);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
+    // 128 x 128 tiles once the group has enough of them for half the CUs
+    // (the single-product rule asks that of one product alone)
+    const int bt = tiles128 >= 128 ? 128 : 64;
+    GemmGroup g{};
+    int total = 0;
+    for (int k = 0; k < kMaxGemmGroup; ++k) {
+        g.start[k] = total;
+        if (k < n) {
+            g.p[k] = ps[k];
+            total += (int)(cdiv(ps[k].M, bt) * cdiv(ps[k].N, bt));
+        }
+    }
+    g.start[kMaxGemmGroup] = total;
+    const int fa = ps[0].a_fp8, fb = ps[0].b_fp8;
+#define FP8LN_GROUP_LAUNCH(A, B)                                                              \
+    if (bt == 128)                                                                           \
+        hipLaunchKernelGGL((gemm_kernel_128_group<A, B>), dim3(total), dim3(256), 0, stream, g); \
+    else                                                                                     \
+        hipLaunchKernelGGL((gemm_kernel_64_group<A, B>), dim3(total), dim3(256), 0, stream, g)
+    if (fa == kE4M3 && fb == kE4M3) {
+        FP8LN_GROUP_LAUNCH(kE4M3, kE4M3);
+    } else if (fa == kE5M2 && fb == kE4M3) {
+        FP8LN_GROUP_LAUNCH(kE5M2, kE4M3);
+    } else if (fa == kE4M3 && fb == kE5M2) {
+        FP8LN_GROUP_LAUNCH(kE4M3, kE5M2);
+    } else {
+        FP8LN_GROUP_LAUNCH(kE5M2, kE5M2);
+    }
+#undef FP8LN_GROUP_LAUNCH
+    return hipGetLastError();
 }
 
 hipError_t launch_gemm(const GemmParams& p, hipStream_t stream) {

@@ -120,5 +120,11 @@ int64_t gemm_partial_rows(int64_t M, int64_t N, int64_t K);
 inline int64_t gemm_partial_rows_bound(int64_t M) { return (M + 127) / 128; }
 
 hipError_t launch_gemm(const GemmParams& p, hipStream_t stream);
+// n (<= kMaxGemmGroup) independent products in one launch when all of them are
+// small fp32-output FP8 products of the same operand formats (their tiles then
+// share the GPU); otherwise one launch_gemm after the other.  Results are those
+// of launch_gemm either way.
+constexpr int kMaxGemmGroup = 3;
+hipError_t launch_gemm_group(const GemmParams* ps, int n, hipStream_t stream);
 
 }  // namespace fp8ln
