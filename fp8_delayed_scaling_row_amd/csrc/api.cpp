@@ -143,6 +143,54 @@ struct Carver {
 #define REQUIRE_PTR(p) REQUIRE((p) != nullptr, "%s is NULL", #p)
 #define REQUIRE_ALIGNED(p) REQUIRE(aligned16(p), "%s is not 16-byte aligned", #p)
 
+// Size limits of one GEMM product C[M][N] = A[M][K] . B[N][K]^T.  The tiles read
+// each operand tile (up to kGemmTileRows rows of K elements) and the fused
+// GELU' epilogue's h tile (up to kGemmTileRows rows of N bf16 values) through a
+// buffer descriptor with a 32-bit record count and 32-bit offsets, and offsets
+// at 2^31 stand for "past the tile" (read as zero), so a tile must span fewer
+// than 2^31 bytes: K * element bytes <= 8388607 (about 2^23), N <= 4194303 when
+// h is read.  The launch grid counts tiles in 32 bits, so M and N are bounded
+// too (at most 2^22 tiles of 64 x 64).
+constexpr int64_t kGemmTileRows = 256;
+constexpr int64_t kGemmTileBytes = 2147483647;   // INT32_MAX
+constexpr int64_t kGemmMaxTiles64 = int64_t(1) << 22;
+constexpr int64_t kGemmMaxDim = int64_t(1) << 36;
+
+int check_gemm_size(int64_t M, int64_t N, int64_t K, int64_t elem_bytes, bool reads_h,
+                    const char* what) {
+    if (M > kGemmMaxDim || N > kGemmMaxDim || K > kGemmMaxDim)
+        return fail(FP8LN_ERR_UNSUPPORTED, "%s: a dimension exceeds 2^36", what);
+    if (K * elem_bytes > kGemmTileBytes / kGemmTileRows)
+        return fail(FP8LN_ERR_UNSUPPORTED,
+                    "%s: contraction length %lld (%lld bytes per row) exceeds the %lld-byte "
+                    "rows that 32-bit tile offsets allow",
+                    what, (long long)K, (long long)(K * elem_bytes),
+                    (long long)(kGemmTileBytes / kGemmTileRows));
+    if (reads_h && N * 2 > kGemmTileBytes / kGemmTileRows)
+        return fail(FP8LN_ERR_UNSUPPORTED, "%s: h rows of %lld bf16 values exceed 32-bit offsets",
+                    what, (long long)N);
+    if (((M + 63) / 64) * ((N + 63) / 64) > kGemmMaxTiles64)
+        return fail(FP8LN_ERR_UNSUPPORTED, "%s: %lld x %lld output exceeds 2^22 tiles of 64 x 64",
+                    what, (long long)M, (long long)N);
+    return FP8LN_OK;
+}
+
+// The transposition kernels take one 64-row tile per grid row (grid y < 65536).
+constexpr int64_t kMaxTransposeRows = int64_t(65535) * 64;
+
+int check_transpose_rows(int64_t rows, const char* what) {
+    if (rows > kMaxTransposeRows)
+        return fail(FP8LN_ERR_UNSUPPORTED, "%s: %lld rows exceed the %lld a transposed copy allows",
+                    what, (long long)rows, (long long)kMaxTransposeRows);
+    return FP8LN_OK;
+}
+
+#define CHECK(expr)                 \
+    do {                            \
+        int _c = (expr);            \
+        if (_c != FP8LN_OK) return _c; \
+    } while (0)
+
 struct LinearWs {
     uint8_t* dy_q;
     uint8_t* dy_qt;
@@ -388,6 +436,7 @@ int fp8ln_ln_cast_amax(const fp8ln_recipe* recipe, int64_t rows, int64_t hidden,
         REQUIRE_ALIGNED(x); REQUIRE_ALIGNED(out);
         if (out_t) REQUIRE_ALIGNED(out_t);
     }
+    if (out_t) CHECK(check_transpose_rows(rows, "ln_cast_amax"));
     if ((s = check_current_device())) return s;
     if (rows == 0) return FP8LN_OK;
     hipStream_t st = as_stream(stream);
@@ -458,6 +507,7 @@ int fp8ln_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* A, int32_t a_dtyp
         if (bias) REQUIRE_ALIGNED(bias);
     }
     REQUIRE(!(bias && out_dtype == FP8LN_DTYPE_F32), "bias is only applied to bf16 outputs");
+    CHECK(check_gemm_size(M, N, K, 1, false, "gemm"));
     int s = check_current_device();
     if (s) return s;
     GemmParams p = gemm_params(M, N, K, A, a_dtype, B, b_dtype, sinv_a, sinv_b,
@@ -492,6 +542,7 @@ int fp8ln_gemm_gelu_fp8(int64_t M, int64_t N, int64_t K, const uint8_t* A, int32
         if (bias) REQUIRE_ALIGNED(bias);
         if (K > 0) { REQUIRE_PTR(A); REQUIRE_PTR(B); REQUIRE_ALIGNED(A); REQUIRE_ALIGNED(B); }
     }
+    CHECK(check_gemm_size(M, N, K, 1, false, "gemm_gelu_fp8"));
     int s = check_current_device();
     if (s) return s;
     GemmParams p = gemm_params(M, N, K, A, a_dtype, B, b_dtype, sinv_a, sinv_b, kEpiGeluFp8);
@@ -523,6 +574,7 @@ int fp8ln_gemm_dgelu(int64_t M, int64_t N, int64_t K, const uint8_t* A, int32_t 
         REQUIRE_PTR(out); REQUIRE_PTR(h); REQUIRE_ALIGNED(out); REQUIRE_ALIGNED(h);
         if (K > 0) { REQUIRE_PTR(A); REQUIRE_PTR(B); REQUIRE_ALIGNED(A); REQUIRE_ALIGNED(B); }
     }
+    CHECK(check_gemm_size(M, N, K, 1, true, "gemm_dgelu"));
     int s = check_current_device();
     if (s) return s;
     GemmParams p = gemm_params(M, N, K, A, a_dtype, B, b_dtype, sinv_a, sinv_b, kEpiDGeluF32);
@@ -561,6 +613,7 @@ int fp8ln_gemm_dgelu_fp8(int64_t M, int64_t N, int64_t K, const uint8_t* A, int3
                 "column sums need %zu bytes of workspace", dgelu_workspace(M, N));
         REQUIRE_ALIGNED(workspace);
     }
+    CHECK(check_gemm_size(M, N, K, 1, true, "gemm_dgelu_fp8"));
     int s = check_current_device();
     if (s) return s;
     hipStream_t st = as_stream(stream);
@@ -621,6 +674,7 @@ int fp8ln_gemm_bf16(int64_t M, int64_t N, int64_t K, const void* A, const void* 
         if (bias) REQUIRE_ALIGNED(bias);
     }
     REQUIRE(!(bias && out_dtype == FP8LN_DTYPE_F32), "bias is only applied to bf16 outputs");
+    CHECK(check_gemm_size(M, N, K, 2, false, "gemm_bf16"));
     int s = check_current_device();
     if (s) return s;
     GemmParams p = gemm_params(M, N, K, (const uint8_t*)A, kOpBf16, (const uint8_t*)B, kOpBf16,
@@ -647,6 +701,7 @@ int fp8ln_gemm_gelu_bf16(int64_t M, int64_t N, int64_t K, const void* A, const v
         if (K > 0) { REQUIRE_PTR(A); REQUIRE_PTR(B); REQUIRE_ALIGNED(A); REQUIRE_ALIGNED(B); }
         if (bias) REQUIRE_ALIGNED(bias);
     }
+    CHECK(check_gemm_size(M, N, K, 2, false, "gemm_gelu_bf16"));
     int s = check_current_device();
     if (s) return s;
     GemmParams p = gemm_params(M, N, K, (const uint8_t*)A, kOpBf16, (const uint8_t*)B, kOpBf16,
@@ -671,6 +726,7 @@ int fp8ln_gemm_dgelu_bf16(int64_t M, int64_t N, int64_t K, const void* A, const 
         REQUIRE_PTR(out); REQUIRE_PTR(h); REQUIRE_ALIGNED(out); REQUIRE_ALIGNED(h);
         if (K > 0) { REQUIRE_PTR(A); REQUIRE_PTR(B); REQUIRE_ALIGNED(A); REQUIRE_ALIGNED(B); }
     }
+    CHECK(check_gemm_size(M, N, K, 2, true, "gemm_dgelu_bf16"));
     int s = check_current_device();
     if (s) return s;
     GemmParams p = gemm_params(M, N, K, (const uint8_t*)A, kOpBf16, (const uint8_t*)B, kOpBf16,
@@ -695,6 +751,7 @@ int fp8ln_transpose_bf16(int64_t rows, int64_t cols, const void* in, void* out, 
         REQUIRE(need == 0 || (workspace && workspace_bytes >= need),
                 "column sums need %zu bytes of workspace", need);
     }
+    CHECK(check_transpose_rows(rows, "transpose_bf16"));
     int s = check_current_device();
     if (s) return s;
     FP8LN_TRY(launch_transpose_b16(rows, cols, in, out, colsum, workspace, as_stream(stream)),
@@ -716,6 +773,7 @@ int fp8ln_ln_linear_fwd_bf16(int64_t tokens, int64_t in_features, int64_t out_fe
         REQUIRE_PTR(x); REQUIRE_PTR(out); REQUIRE_PTR(ln_out);
         REQUIRE_ALIGNED(x); REQUIRE_ALIGNED(out); REQUIRE_ALIGNED(ln_out);
     }
+    CHECK(check_gemm_size(tokens, out_features, in_features, 2, false, "ln_linear_fwd_bf16"));
     if ((s = check_current_device())) return s;
     if (M == 0) return FP8LN_OK;
     hipStream_t st = as_stream(stream);
@@ -756,6 +814,9 @@ int fp8ln_ln_linear_bwd_bf16(int64_t tokens, int64_t in_features, int64_t out_fe
     REQUIRE(workspace && workspace_bytes >= need.bytes,
             "ln_linear_bwd_bf16 needs %zu bytes of workspace", need.bytes);
     REQUIRE_ALIGNED(workspace);
+    CHECK(check_transpose_rows(tokens, "ln_linear_bwd_bf16"));
+    CHECK(check_gemm_size(tokens, in_features, out_features, 2, false, "ln_linear_bwd_bf16 dgrad"));
+    CHECK(check_gemm_size(out_features, in_features, tokens, 2, false, "ln_linear_bwd_bf16 wgrad"));
     if ((s = check_current_device())) return s;
     hipStream_t st = as_stream(stream);
     const LinearBf16Ws w = linear_bf16_ws(workspace, M, K, N);
@@ -797,6 +858,8 @@ int fp8ln_ln_mlp_fwd_bf16(int64_t tokens, int64_t hidden, int64_t ffn, float eps
         REQUIRE_ALIGNED(x); REQUIRE_ALIGNED(out); REQUIRE_ALIGNED(ln_out); REQUIRE_ALIGNED(g);
         if (h) REQUIRE_ALIGNED(h);
     }
+    CHECK(check_gemm_size(tokens, ffn, hidden, 2, false, "ln_mlp_fwd_bf16 fc1"));
+    CHECK(check_gemm_size(tokens, hidden, ffn, 2, false, "ln_mlp_fwd_bf16 fc2"));
     if ((s = check_current_device())) return s;
     if (M == 0) return FP8LN_OK;
     hipStream_t st = as_stream(stream);
@@ -848,6 +911,10 @@ int fp8ln_ln_mlp_bwd_bf16(int64_t tokens, int64_t hidden, int64_t ffn, int32_t a
     REQUIRE(workspace && workspace_bytes >= need.bytes,
             "ln_mlp_bwd_bf16 needs %zu bytes of workspace", need.bytes);
     REQUIRE_ALIGNED(workspace);
+    CHECK(check_transpose_rows(tokens, "ln_mlp_bwd_bf16"));
+    CHECK(check_gemm_size(tokens, ffn, hidden, 2, true, "ln_mlp_bwd_bf16 fc2 dgrad"));
+    CHECK(check_gemm_size(hidden, ffn, tokens, 2, false, "ln_mlp_bwd_bf16 wgrad"));
+    CHECK(check_gemm_size(tokens, hidden, ffn, 2, false, "ln_mlp_bwd_bf16 fc1 dgrad"));
     if ((s = check_current_device())) return s;
     hipStream_t st = as_stream(stream);
     const MlpBf16Ws w = mlp_bf16_ws(workspace, M, H, F);
@@ -960,6 +1027,7 @@ int fp8ln_linear_fwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_feat
         REQUIRE_ALIGNED(x); REQUIRE_ALIGNED(out); REQUIRE_ALIGNED(ctx->ln_q);
         if (ctx->ln_qt) REQUIRE_ALIGNED(ctx->ln_qt);
     }
+    CHECK(check_gemm_size(tokens, out_features, in_features, 1, false, "linear_fwd"));
     if ((s = check_current_device())) return s;
     hipStream_t st = as_stream(stream);
     const int f = meta_fp8(recipe, FP8LN_META_FORWARD);
@@ -1011,6 +1079,8 @@ int fp8ln_linear_bwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_feat
     REQUIRE(need.bytes == 0 || (workspace && workspace_bytes >= need.bytes),
             "linear_bwd needs %zu bytes of workspace", need.bytes);
     REQUIRE_ALIGNED(workspace);
+    CHECK(check_gemm_size(tokens, in_features, out_features, 1, false, "linear_bwd dgrad"));
+    CHECK(check_gemm_size(out_features, in_features, tokens, 1, false, "linear_bwd wgrad"));
     if ((s = check_current_device())) return s;
     hipStream_t st = as_stream(stream);
     const LinearOnlyWs w = linear_only_ws(workspace, M, K, N);
@@ -1068,6 +1138,8 @@ int fp8ln_ln_linear_fwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_f
         REQUIRE_ALIGNED(x); REQUIRE_ALIGNED(out); REQUIRE_ALIGNED(ctx->ln_q);
         if (ctx->ln_qt) REQUIRE_ALIGNED(ctx->ln_qt);
     }
+    if (ctx->ln_qt) CHECK(check_transpose_rows(M, "ln_linear_fwd"));
+    CHECK(check_gemm_size(M, N, K, 1, false, "ln_linear_fwd"));
     if ((s = check_current_device())) return s;
     hipStream_t st = as_stream(stream);
     const int f = meta_fp8(recipe, FP8LN_META_FORWARD);
@@ -1139,6 +1211,8 @@ int fp8ln_ln_linear_bwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_f
     REQUIRE(workspace && workspace_bytes >= need.bytes, "ln_linear_bwd needs %zu bytes of workspace",
             need.bytes);
     REQUIRE_ALIGNED(workspace);
+    CHECK(check_gemm_size(M, K, N, 1, false, "ln_linear_bwd dgrad"));
+    CHECK(check_gemm_size(N, K, M, 1, false, "ln_linear_bwd wgrad"));
     if ((s = check_current_device())) return s;
     hipStream_t st = as_stream(stream);
     const LinearWs w = linear_ws(workspace, M, K, N);
@@ -1208,6 +1282,9 @@ int fp8ln_ln_mlp_fwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t hidden,
         if (ctx->g_qt) REQUIRE_ALIGNED(ctx->g_qt);
         if (ctx->h) REQUIRE_ALIGNED(ctx->h);
     }
+    if (ctx->ln_qt) CHECK(check_transpose_rows(M, "ln_mlp_fwd"));
+    CHECK(check_gemm_size(M, F, H, 1, false, "ln_mlp_fwd fc1"));
+    CHECK(check_gemm_size(M, H, F, 1, false, "ln_mlp_fwd fc2"));
     if ((s = check_current_device())) return s;
     hipStream_t st = as_stream(stream);
     const int f = meta_fp8(recipe, FP8LN_META_FORWARD);
@@ -1302,6 +1379,9 @@ int fp8ln_ln_mlp_bwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t hidden,
     REQUIRE(workspace && workspace_bytes >= need.bytes, "ln_mlp_bwd needs %zu bytes of workspace",
             need.bytes);
     REQUIRE_ALIGNED(workspace);
+    CHECK(check_gemm_size(M, F, H, 1, true, "ln_mlp_bwd fc2 dgrad"));
+    CHECK(check_gemm_size(H, F, M, 1, false, "ln_mlp_bwd wgrad"));
+    CHECK(check_gemm_size(M, H, F, 1, false, "ln_mlp_bwd fc1 dgrad"));
     if ((s = check_current_device())) return s;
     hipStream_t st = as_stream(stream);
     const MlpWs w = mlp_ws(workspace, M, H, F);

@@ -201,6 +201,7 @@ hipError_t launch_cast_amax(int64_t rows, int64_t cols, bool in_f32, const void*
 hipError_t launch_transpose_u8(int64_t rows, int64_t cols, const uint8_t* in, uint8_t* out,
                                hipStream_t stream) {
     if (rows == 0 || cols == 0) return hipSuccess;
+    if ((rows + kTile - 1) / kTile > 65535) return hipErrorInvalidValue;   // grid y limit
     const dim3 grid((unsigned)((cols + kTile - 1) / kTile), (unsigned)((rows + kTile - 1) / kTile));
     hipLaunchKernelGGL(transpose_u8_kernel, grid, dim3(kThreads), 0, stream, in, rows, cols, out);
     return hipGetLastError();
@@ -214,6 +215,7 @@ hipError_t launch_transpose_b16(int64_t rows, int64_t cols, const void* in, void
                                 float* colsum, void* workspace, hipStream_t stream) {
     if (cols == 0) return hipSuccess;
     float* partial = colsum ? (float*)workspace : nullptr;
+    if ((rows + kTile - 1) / kTile > 65535) return hipErrorInvalidValue;   // grid y limit
     if (rows > 0) {
         const dim3 grid((unsigned)((cols + kTile - 1) / kTile),
                         (unsigned)((rows + kTile - 1) / kTile));

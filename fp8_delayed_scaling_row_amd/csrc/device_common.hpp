@@ -107,7 +107,11 @@ __device__ __forceinline__ float mul_round_odd(float v, float s) {
     const float p = v * s;
     const float e = fmaf(v, s, -p);            // exact remainder of the product
     uint32_t b = __float_as_uint(p);
-    const bool fix = (e != 0.0f) && ((b & 1u) == 0u) && (p != 0.0f);
+    // only a finite non-zero product is adjusted: an infinite product (an
+    // infinite v, or an overflow) has a NaN or infinite remainder and must stay
+    // infinite, so that the encoder saturates it
+    const bool fix = (e != 0.0f) && ((b & 1u) == 0u) && (p != 0.0f) &&
+                     ((b & 0x7f800000u) != 0x7f800000u);
     // same sign: the exact magnitude is larger -> step the bits up, else down
     const uint32_t step = ((__float_as_uint(e) ^ b) & 0x80000000u) ? 0xffffffffu : 1u;
     b += fix ? step : 0u;

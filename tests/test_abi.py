@@ -127,3 +127,78 @@ def test_check_support_reports_a_reason_without_a_gpu(lib):
     assert ok in (0, 1)
     if ok == 0:
         assert buf.value   # a reason is given
+
+
+# ---- size limits of the GEMM tiles (checked on the host, before any launch) ----
+
+BIG_K = 1 << 23          # 256 rows of 2^23 bytes reach 2^31: past the 32-bit tile offsets
+OK_K = (1 << 23) - 16    # the largest multiple of 16 below the limit
+
+
+def test_gemm_contraction_length_is_bounded(lib):
+    p = C.c_void_p(256)   # never dereferenced
+    s = lib.fp8ln_gemm(16, 16, BIG_K, p, 0, p, 0, p, p, None, _abi.DTYPE_F32, p, None)
+    assert s == _abi.FP8LN_ERR_UNSUPPORTED
+    assert b"contraction" in lib.fp8ln_last_error()
+    # bf16 operands: K counts elements of 2 bytes
+    s = lib.fp8ln_gemm_bf16(16, 16, BIG_K // 2, p, p, None, _abi.DTYPE_F32, p, None)
+    assert s == _abi.FP8LN_ERR_UNSUPPORTED
+    # the fused GELU' epilogue reads h rows of N bf16 values
+    s = lib.fp8ln_gemm_dgelu(16, BIG_K // 2, 16, p, 0, p, 0, p, p, p, p, 0, None)
+    assert s == _abi.FP8LN_ERR_UNSUPPORTED
+    s = lib.fp8ln_gemm_dgelu_fp8(16, BIG_K // 2, 16, p, 0, p, 0, p, p, p, 1, p, p, p, None,
+                                 None, 0, None, 0, None)
+    assert s == _abi.FP8LN_ERR_UNSUPPORTED
+
+
+def test_gemm_output_tiles_are_bounded(lib):
+    p = C.c_void_p(256)
+    s = lib.fp8ln_gemm(1 << 20, 1 << 20, 16, p, 0, p, 0, p, p, None, _abi.DTYPE_F32, p, None)
+    assert s == _abi.FP8LN_ERR_UNSUPPORTED
+
+
+def test_token_count_of_the_weight_gradient_is_bounded(lib):
+    """wgrad contracts over tokens: a backward over 2^23 tokens is refused
+    before any launch (its workspace is never touched)."""
+    r = _recipe()
+    p = C.c_void_p(256)
+    mf = _abi.MetaStruct(256, 256, 256, 2, _abi.META_FORWARD)
+    mb = _abi.MetaStruct(256, 256, 256, 1, _abi.META_BACKWARD)
+    ctx = _abi.LinearCtxStruct(256, 256, 256, 256, 256, 256)
+    huge = C.c_size_t(-1).value
+    s = lib.fp8ln_ln_linear_bwd(C.byref(r), BIG_K, 768, 2304, _abi.DTYPE_BF16, p, p, p,
+                                C.byref(ctx), C.byref(mf), C.byref(mb), p, p, p, p, None, p,
+                                huge, None)
+    assert s == _abi.FP8LN_ERR_UNSUPPORTED
+    assert b"wgrad" in lib.fp8ln_last_error()
+    s = lib.fp8ln_linear_bwd(C.byref(r), BIG_K, 768, 2304, _abi.DTYPE_BF16, p, C.byref(ctx),
+                             C.byref(mf), C.byref(mb), p, p, None, p, huge, None)
+    assert s == _abi.FP8LN_ERR_UNSUPPORTED
+    mf4 = _abi.MetaStruct(256, 256, 256, 4, _abi.META_FORWARD)
+    mb2 = _abi.MetaStruct(256, 256, 256, 2, _abi.META_BACKWARD)
+    mctx = _abi.MlpCtxStruct(*([256] * 11))
+    s = lib.fp8ln_ln_mlp_bwd(C.byref(r), BIG_K, 768, 3072, _abi.DTYPE_BF16, p, p, p,
+                             C.byref(mctx), C.byref(mf4), C.byref(mb2), p, p, p, p, p, p, p, p,
+                             huge, None)
+    assert s == _abi.FP8LN_ERR_UNSUPPORTED
+    # the BF16 backward as well (2-byte operands: half the tokens suffice)
+    s = lib.fp8ln_ln_linear_bwd_bf16(BIG_K // 2, 768, 2304, p, p, p, p, p, p, p, p, p, p, p,
+                                     None, p, huge, None)
+    assert s == _abi.FP8LN_ERR_UNSUPPORTED
+
+
+def test_transposed_copies_bound_the_rows(lib):
+    r = _recipe()
+    p = C.c_void_p(256)
+    s = lib.fp8ln_ln_cast_amax(C.byref(r), 65536 * 64, 64, _abi.DTYPE_BF16, p, p, p, 0, p, p,
+                               p, p, None, None, None)
+    assert s == _abi.FP8LN_ERR_UNSUPPORTED
+
+
+def test_largest_contraction_passes_the_size_check(lib):
+    """K just below the limit passes validation: without a GPU the call gets as
+    far as the device check (a HIP error or UNSUPPORTED device), never the size
+    error."""
+    p = C.c_void_p(256)
+    lib.fp8ln_gemm(16, 16, OK_K, p, 0, p, 0, p, p, None, _abi.DTYPE_F32, p, None)
+    assert b"contraction" not in lib.fp8ln_last_error()

@@ -172,6 +172,47 @@ def test_cast_amax_matches_oracle(rows, cols, in_f32, fp8, with_t, with_sum, sca
     print(f"cast {rows}x{cols}: {stats}")
 
 
+@pytest.mark.parametrize("fp8", [ops.E4M3, ops.E5M2])
+@pytest.mark.parametrize("in_f32", [False, True])
+@pytest.mark.parametrize("with_nan", [False, True])
+def test_cast_amax_infinities_nan_and_overflow(fp8, in_f32, with_nan):
+    """Weights and gradients may hold infinities, NaNs or values whose scaled
+    product overflows binary32: infinities and overflowing products saturate to
+    +-max, NaN encodes to 0x7F, and the amax is inf (NaN when a NaN is
+    present), all as the oracle encodes the exact products."""
+    rows, cols = 96, 160
+    rng = np.random.default_rng(11 + 2 * fp8 + int(in_f32))
+    xv = rng.normal(size=(rows, cols)) * 0.02
+    flat = xv.reshape(-1)
+    idx = rng.permutation(flat.size)
+    flat[idx[0:7]] = np.inf
+    flat[idx[7:14]] = -np.inf
+    flat[idx[14:30]] = 3.0e38 * rng.choice([-1.0, 1.0], size=16)    # product overflows
+    flat[idx[30:60]] = rng.normal(size=30) * 1e4                     # past +-max after scaling
+    if with_nan:
+        flat[idx[60:63]] = np.nan
+    if in_f32:
+        x = torch.from_numpy(xv.astype(np.float32))
+        xv = x.numpy().astype(np.float64)
+    else:
+        bits = oracle.f64_to_bf16_bits(xv)
+        x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
+        xv = oracle.bf16_to_f64(bits)
+    out = torch.empty((rows, cols), dtype=torch.uint8, device="cuda")
+    out_t = torch.empty((cols, rows), dtype=torch.uint8, device="cuda")
+    amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    scale = float(np.float32(448.0 / 0.093 if fp8 == ops.E4M3 else 57344.0 / 0.0011))
+    ops.cast_amax(x.cuda(), fp8, _scalar(scale), amax.data_ptr(), out, out_t, None)
+    torch.cuda.synchronize()
+    with np.errstate(over="ignore", invalid="ignore"):
+        exact = xv * scale
+    stats = compare_codes(out.cpu().numpy(), exact, FMT[fp8], 0.0)
+    assert stats["mismatched"] == 0
+    assert torch.equal(out_t, out.t().contiguous())
+    a = amax.item()
+    assert np.isnan(a) if with_nan else a == np.inf
+
+
 @pytest.mark.parametrize("rows,hidden", [(1, 8), (37, 768), (2048, 768), (513, 2048),
                                          (64, 4096), (0, 256)])
 def test_layernorm_bwd_matches_oracle(rows, hidden):
