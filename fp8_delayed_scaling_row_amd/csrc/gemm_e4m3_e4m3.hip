@@ -1,0 +1,6 @@
+// FP8 GEMM kernels for operands E4M3 X E4M3 (A x B); see gemm_kernels.hpp.
+#include "gemm_kernels.hpp"
+
+namespace fp8ln {
+FP8LN_GEMM_PAIR_DEFINE(kE4M3, kE4M3, e4m3_e4m3)
+}  // namespace fp8ln
