@@ -25,6 +25,12 @@ written from the method as the pages describe it:
 
 Where the pages are silent the oracle takes a stated reading; each module's
 docstring names the readings it depends on.
+
+oracle.cxx is a second implementation of the same steps in plain C++17
+(oracle/cpp/fp8ln_oracle.cpp: table-exact FP8 codec, float64 LayerNorm, exact
+integer-accumulated FP8 GEMM, binary32 delayed-scaling bookkeeping and the
+module chains), with OpenMP over rows; it is pinned on its own and against this
+one, and is the one the benchmark times on the host cores.
 """
 from .codec import (E4M3, E5M2, FP8_MAX, bf16_to_f64, f64_to_bf16_bits, fp8_decode,
                     fp8_decode_table, fp8_encode, fp8_positive_values)
