@@ -116,6 +116,9 @@ SIGNATURES = {
     "fp8ln_ln_linear_bwd": (C.c_int, [_RP, _I64, _I64, _I64, _I32, _P, _P, _P,
                                       C.POINTER(LinearCtxStruct), _MP, _MP, _P, _P, _P, _P, _P,
                                       _P, _SZ, _P]),
+    "fp8ln_ln_linear_bwd_noalloc": (C.c_int, [_RP, _I64, _I64, _I64, _I32, _P, _P, _P,
+                                              C.POINTER(LinearCtxStruct), _MP, _MP, _P, _P, _P,
+                                              _P, _P, _P]),
     "fp8ln_ln_mlp_fwd": (C.c_int, [_RP, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _P,
                                    _MP, C.POINTER(MlpCtxStruct), _P]),
     "fp8ln_ln_mlp_bwd": (C.c_int, [_RP, _I64, _I64, _I64, _I32, _P, _P, _P,

@@ -344,6 +344,10 @@ GemmParams gemm_params(int64_t M, int64_t N, int64_t K, const uint8_t* A, int af
 
 }  // namespace
 
+namespace fp8ln {
+int report_error(int status, const char* message) { return fail(status, "%s", message); }
+}  // namespace fp8ln
+
 extern "C" {
 
 const char* fp8ln_status_string(int status) {

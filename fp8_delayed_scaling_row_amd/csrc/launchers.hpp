@@ -9,6 +9,10 @@
 
 namespace fp8ln {
 
+// Records `message` as the calling thread's last error (fp8ln_last_error) and
+// returns `status` (api.cpp).
+int report_error(int status, const char* message);
+
 // FP8 encodings (same values as fp8ln_fp8_dtype).
 enum Fp8Kind : int { kE4M3 = 0, kE5M2 = 1 };
 

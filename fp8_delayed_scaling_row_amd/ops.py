@@ -27,7 +27,7 @@ __all__ = [
     "linear_fwd", "linear_bwd", "gemm_bf16", "gemm_gelu_bf16", "transpose_bf16",
     "ln_linear_fwd_bf16", "ln_linear_bwd_bf16", "ln_mlp_fwd_bf16", "ln_mlp_bwd_bf16",
     "gemm_dgelu_bf16",
-    "ln_linear_fwd", "ln_linear_bwd", "ln_mlp_fwd", "ln_mlp_bwd", "fwd_fp8", "bwd_fp8",
+    "ln_linear_fwd", "ln_linear_bwd", "ln_linear_bwd_noalloc", "ln_mlp_fwd", "ln_mlp_bwd", "fwd_fp8", "bwd_fp8",
 ]
 
 
@@ -526,6 +526,23 @@ def ln_linear_bwd(recipe: Recipe, dy, x, gamma, ctx: LinearCtx, fwd: Meta, bwd: 
                                     _ptr(gamma), C.byref(c), C.byref(mf), C.byref(mb), _ptr(dx),
                                     _ptr(dgamma), _ptr(dbeta), _ptr(dweight), _ptr(dbias),
                                     _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def ln_linear_bwd_noalloc(recipe: Recipe, dy, x, gamma, ctx: LinearCtx, fwd: Meta, bwd: Meta,
+                          dx, dgamma, dbeta, dweight, dbias=None, stream=None) -> None:
+    """ln_linear_bwd with its workspace in the library's own device array (no
+    allocation by the library or by this binding)."""
+    M, N = dy.shape
+    K = x.shape[1]
+    _need(dy, torch.bfloat16, (M, N), "dy")
+    _need(dx, torch.bfloat16, (M, K), "dx")
+    _need(dweight, torch.float32, (N, K), "dweight")
+    _opt(dbias, torch.float32, (N,), "dbias")
+    r, mf, mb, c = recipe.as_c(), fwd.as_c(), bwd.as_c(), ctx.as_c()
+    check(lib().fp8ln_ln_linear_bwd_noalloc(C.byref(r), M, K, N, DTYPE_BF16, _ptr(dy), _ptr(x),
+                                            _ptr(gamma), C.byref(c), C.byref(mf), C.byref(mb),
+                                            _ptr(dx), _ptr(dgamma), _ptr(dbeta), _ptr(dweight),
+                                            _ptr(dbias), _stream(stream)))
 
 
 def ln_mlp_fwd(recipe: Recipe, x, gamma, beta, w1, b1, w2, b2, out, fwd: Meta, ctx: MlpCtx,

@@ -19,8 +19,9 @@
  * Conventions shared by every entry point
  *  - Every pointer argument is a device pointer unless stated otherwise, and the
  *    caller owns every buffer: inputs, outputs, saved context, FP8 state and
- *    workspace.  The library allocates no device memory and keeps no pointer
- *    after a call returns.  Buffers must stay alive until the stream reaches the
+ *    workspace.  The library allocates no device memory (its one fixed device
+ *    array, that of fp8ln_ln_linear_bwd_noalloc, comes with the loaded code) and
+ *    keeps no pointer after a call returns.  Buffers must stay alive until the stream reaches the
  *    call's kernels.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream) and runs
  *    asynchronously.  No call synchronises the host or copies data to the host:
@@ -468,6 +469,24 @@ int fp8ln_ln_linear_bwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_f
                         const fp8ln_meta* fwd, const fp8ln_meta* bwd, void* dx,
                         float* dgamma, float* dbeta, float* dweight, float* dbias,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): fp8ln_ln_linear_bwd
+ * without the workspace argument.  The same kernels run with their workspace in
+ * a 32 MiB (33554432-byte) device array that the library holds on each GPU it
+ * runs on until the process ends; it calls no allocator.  Sizes whose workspace
+ * (fp8ln_workspace_size(FP8LN_OP_LN_LINEAR_BWD, tokens, in, out)) exceeds 32 MiB
+ * return FP8LN_ERR_UNSUPPORTED before anything is enqueued (2048 tokens at
+ * 768 -> 2304 need about 19 MB).  All calls on one GPU share its array: calls
+ * that overlap on a GPU (other streams, other threads) race and must be
+ * ordered by the caller.  Arguments, outputs and errors are otherwise those of
+ * fp8ln_ln_linear_bwd. */
+int fp8ln_ln_linear_bwd_noalloc(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_features,
+                                int64_t out_features, int32_t params_dtype, const void* dy,
+                                const void* x, const void* gamma, const fp8ln_linear_ctx* ctx,
+                                const fp8ln_meta* fwd, const fp8ln_meta* bwd, void* dx,
+                                float* dgamma, float* dbeta, float* dweight, float* dbias,
+                                void* stream);
 
 /* ---- LayerNormMLP ([T] setup listing: te.LayerNormMLP(H, 4*H); [G] "The
  *      building blocks") ------------------------------------------------------ */
