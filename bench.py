@@ -58,6 +58,10 @@ def parse():
                    help="counter run: N headline launches plus 3 plain 1 GiB copies")
     p.add_argument("--profile-gemm", type=int, nargs=4, metavar=("M", "N", "K", "REPS"),
                    help="counter run: REPS launches of one E4M3 GEMM (fp32 output)")
+    p.add_argument("--profile-kernel", nargs=2, metavar=("KIND", "REPS"),
+                   help="counter run: REPS launches of one kernel of the 16384-token "
+                        "scale-up layer: fc1, fc2_dgrad, fc2_fwd, wgrad, ln_bwd, cast_dy, "
+                        "cast_w (plus 3 plain 1 GiB copies for the HBM calibration)")
     p.add_argument("--bf16", action="store_true",
                    help="with --profile-gemm: the bf16 GEMM instead of the FP8 one")
     p.add_argument("--oracle-workloads", action="store_true",
@@ -161,6 +165,29 @@ def bench_ln_cast(torch, ops, inputs, steps, warmup):
 
 
 COPY_BYTES = 1 << 30     # each calibration copy reads and writes this many bytes
+PROBE_ELEMS = 1 << 29    # stream probe: 1 GiB of bf16 read, 512 MiB of bytes written
+
+
+def stream_probe_gbs(torch, ops, reps=10):
+    """GB/s of the library's streaming probe (fp8ln_stream_probe): the LayerNorm +
+    cast step's traffic, 2 B read and 1 B written per element with non-temporal
+    accesses and no arithmetic, over 1.5 GiB per launch (past the 256 MB
+    last-level cache), HIP events on the launch stream."""
+    x = torch.empty(PROBE_ELEMS, dtype=torch.bfloat16, device="cuda").fill_(1.5)
+    out = torch.empty(PROBE_ELEMS, dtype=torch.uint8, device="cuda")
+    ops.stream_probe(x, out)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        ops.stream_probe(x, out)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    del x, out
+    torch.cuda.empty_cache()
+    return 3 * PROBE_ELEMS / (ms * 1e-3) / 1e9
 
 
 def copy_ceiling_gbs(torch, reps=10):
@@ -209,6 +236,66 @@ def profile_ln(torch, ops, inputs, n):
         torch.neg(src, out=dst)
     torch.cuda.synchronize()
     print(json.dumps(dict(profile_ln=n, copies=3, copy_bytes=COPY_BYTES)), flush=True)
+
+
+def profile_kernel(torch, ops, inputs, kind, reps):
+    """Launches for a rocprofv3 run on one kernel of the scale-up layer (16384
+    tokens, 2048 -> 8192 -> 2048, HYBRID): the GEMMs with their step's epilogues
+    and operand formats, the LayerNorm backward and the casts; then three
+    elementwise copies of a 1 GiB bf16 tensor (FETCH_SIZE / WRITE_SIZE
+    calibration)."""
+    M, H, F = 16384, 2048, 8192
+    E4, E5 = ops.E4M3, ops.E5M2
+    one = torch.ones(1, device="cuda")
+    amax = torch.zeros(1, device="cuda")
+    u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device="cuda")
+    bf = lambda *s: torch.empty(s, dtype=torch.bfloat16, device="cuda")
+    wl = "profile"
+    if kind == "fc1":
+        a, b, q, qt, h = _codes(torch, M, H), _codes(torch, F, H), u8(M, F), u8(F, M), bf(M, F)
+        fn = lambda: ops.gemm_gelu_fp8(a, E4, b, E4, one, one, E4, one, amax.data_ptr(), q, qt, h)
+    elif kind == "fc2_dgrad":
+        a, b, q, qt = _codes(torch, M, H), _codes(torch, F, H), u8(M, F), u8(F, M)
+        h = (torch.randn((M, F), device="cuda") * 2).to(torch.bfloat16)
+        db = torch.empty(F, device="cuda")
+        ws = torch.empty(ops.workspace_size(ops.OP_GEMM_DGELU_FP8, M, F), dtype=torch.uint8,
+                         device="cuda")
+        fn = lambda: ops.gemm_dgelu_fp8(a, E5, b, E4, one, one, h, E5, one, amax.data_ptr(), q,
+                                        qt, db, workspace=ws)
+    elif kind == "fc2_fwd":
+        a, b, o = _codes(torch, M, F), _codes(torch, H, F), bf(M, H)
+        fn = lambda: ops.gemm(a, E4, b, E4, one, one, o)
+    elif kind == "wgrad":
+        a, b = _codes(torch, F, M), _codes(torch, H, M)
+        o = torch.empty((F, H), device="cuda")
+        fn = lambda: ops.gemm(a, E5, b, E4, one, one, o)
+    elif kind == "ln_bwd":
+        x = inputs.normal_bf16((M, H), inputs.seed_for(wl, "x"), device="cuda")
+        g, _ = inputs.layernorm_params(H, wl, device="cuda")
+        dln = torch.randn((M, H), device="cuda") * 1e-3
+        mean = x.float().mean(dim=1)
+        rstd = torch.rsqrt(x.float().var(dim=1, unbiased=False) + 1e-5)
+        dx, dg, db = bf(M, H), torch.empty(H, device="cuda"), torch.empty(H, device="cuda")
+        fn = lambda: ops.layernorm_bwd(dln, x, mean, rstd, g, dx, dg, db)
+    elif kind == "cast_dy":
+        dy = inputs.normal_bf16((M, H), inputs.seed_for(wl, "dy"), std=1e-3, device="cuda")
+        q, qt, cs = u8(M, H), u8(H, M), torch.empty(H, device="cuda")
+        fn = lambda: ops.cast_amax(dy, E5, one, amax.data_ptr(), q, qt, cs)
+    elif kind == "cast_w":
+        w = inputs.linear_weight(F, H, wl, "w1", device="cuda")
+        q, qt = u8(F, H), u8(H, F)
+        fn = lambda: ops.cast_amax(w, E4, one, amax.data_ptr(), q, qt)
+    else:
+        raise SystemExit(f"unknown kernel kind {kind!r}")
+    for _ in range(reps):
+        fn()
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps(dict(profile_kernel=kind, reps=reps, copies=3, copy_bytes=COPY_BYTES)),
+          flush=True)
 
 
 def _read_counter_csv(path, counter):
@@ -287,6 +374,72 @@ def gemm_kernel_ms(torch, ops, M, N, K, out_dtype, reps=20, bf16=False):
                 ops.gemm(a, ops.E4M3, b, ops.E4M3, one, one, out)
 
     return _graph_ms(torch, launches, 1, 3) / reps
+
+
+def _codes(torch, *shape):
+    """Random finite FP8 codes of both signs (0x77 keeps E4M3 and E5M2 finite)."""
+    c = torch.randint(0, 0x77, shape, dtype=torch.uint8, device="cuda")
+    return c | (torch.randint(0, 2, shape, dtype=torch.uint8, device="cuda") << 7)
+
+
+def mlp_gemm_kinds(torch, ops, M, H, F, backward, bwd_fp8=None, reps=10):
+    """Each GEMM of one LayerNormMLP layer step launched alone through the C-ABI
+    entry point that runs the same kernel (tile, epilogue, operand formats) as
+    the module step: average ms per launch over `reps` graph-replayed launches,
+    TFLOP/s and fraction of the FP8 peak."""
+    E4 = ops.E4M3
+    bf = ops.E5M2 if bwd_fp8 is None else bwd_fp8
+    one = torch.ones(1, device="cuda")
+    amax = torch.zeros(1, device="cuda")
+    u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device="cuda")
+    out = []
+
+    def run(name, m, n, k, make):
+        fn = make()
+        ms = _graph_ms(torch, lambda _: [fn() for _ in range(reps)], 1, 3) / reps
+        tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
+        out.append(dict(kind=name, mnk=[m, n, k], kernel_ms=round(ms, 5),
+                        achieved=round(tf, 1), frac=round(tf / FP8_PEAK_TFLOPS, 4)))
+        torch.cuda.empty_cache()
+
+    def fc1():
+        a, b, q, qt = _codes(torch, M, H), _codes(torch, F, H), u8(M, F), u8(F, M)
+        h = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
+        return lambda: ops.gemm_gelu_fp8(a, E4, b, E4, one, one, E4, one, amax.data_ptr(), q,
+                                         q_out_t=qt if backward else None,
+                                         h_out=h if backward else None)
+
+    def fc2():
+        a, b = _codes(torch, M, F), _codes(torch, H, F)
+        o = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+        return lambda: ops.gemm(a, E4, b, E4, one, one, o)
+
+    run("fc1 fwd: GELU epilogue" + (", bf16 h, FP8 codes + transpose" if backward else
+                                     ", FP8 codes"), M, F, H, fc1)
+    run("fc2 fwd: bf16 out", M, H, F, fc2)
+    if backward:
+        def dgrad2():
+            a, b = _codes(torch, M, H), _codes(torch, F, H)
+            h = (torch.randn((M, F), device="cuda") * 2).to(torch.bfloat16)
+            q, qt = u8(M, F), u8(F, M)
+            db = torch.empty(F, device="cuda")
+            ws = torch.empty(ops.workspace_size(ops.OP_GEMM_DGELU_FP8, M, F), dtype=torch.uint8,
+                             device="cuda")
+            return lambda: ops.gemm_dgelu_fp8(a, bf, b, E4, one, one, h, bf, one,
+                                              amax.data_ptr(), q, qt, db, workspace=ws)
+
+        def fp32(m, n, k):
+            def make():
+                a, b = _codes(torch, m, k), _codes(torch, n, k)
+                o = torch.empty((m, n), device="cuda")
+                return lambda: ops.gemm(a, bf, b, E4, one, one, o)
+            return make
+
+        run("fc2 dgrad: GELU' + dH FP8 cast, transpose, dbias partials", M, F, H, dgrad2)
+        run("fc2 wgrad: fp32 out", H, F, M, fp32(H, F, M))
+        run("fc1 dgrad: fp32 out", M, H, F, fp32(M, H, F))
+        run("fc1 wgrad: fp32 out", F, H, M, fp32(F, H, M))
+    return out
 
 
 def _graph_ms(torch, step, unroll, replays):
@@ -392,7 +545,7 @@ def bench_mlp_fwd(torch, ops, inputs, steps, warmup, M=2048, H=768, F=3072, reus
 
     t = _time_steps(torch, step, steps, warmup, unroll=4)
     flops = 2 * 2.0 * M * H * F
-    return dict(t, flops=flops, gemm=(M, F, H, torch.bfloat16))
+    return dict(t, flops=flops, gemm=(M, F, H, torch.bfloat16), kinds=(M, H, F, False))
 
 
 def bench_linear_fwd_bf16(torch, ops, inputs, steps, warmup, M=256, K=768, N=2304):
@@ -493,7 +646,8 @@ def bench_mlp_stack(torch, ops, inputs, steps, warmup, fmt, M=16384, H=2048, F=8
 
     t = _time_steps(torch, step, steps, warmup, unroll=1)
     flops = layers * 6 * 2.0 * M * H * F
-    return dict(t, flops=flops, gemm=(M, F, H, torch.float32))
+    bwd = ops.E4M3 if fmt == ops.FORMAT_E4M3 else ops.E5M2
+    return dict(t, flops=flops, gemm=(M, F, H, torch.float32), kinds=(M, H, F, True, bwd))
 
 
 def bench_mlp_stack_bf16(torch, ops, inputs, steps, warmup, M=16384, H=2048, F=8192, layers=12):
@@ -557,45 +711,66 @@ def _time_steps(torch, step, steps, warmup, unroll=4):
 
 # ---- CPU baseline ----------------------------------------------------------------
 
-def cpu_baseline(inputs, budget_s=12.0):
-    """The oracle's LayerNorm + cast + amax on sampled 2048-row blocks of the
-    headline workload, repeated until budget_s of CPU time has passed."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(inputs, budget_s=12.0, single_s=4.0):
+    """The C++ oracle's LayerNorm + cast + amax (float64, OpenMP over rows, -O2)
+    on a sampled 8192-row block of the headline workload, repeated until
+    budget_s has passed, on all the threads OpenMP is given; then the same on
+    one thread for single_s."""
     import numpy as np
-    import oracle
+    import oracle.cxx as X
     from fp8_delayed_scaling_row_amd.inputs import spiky_normal_bf16, seed_for
-    rows, hidden = 2048, 2048
+    rows, hidden = 8192, 2048
     x = spiky_normal_bf16((rows, hidden), seed_for("cpu-baseline", "x"), drift=2.0)
     g, b = inputs.layernorm_params(hidden, "cpu-baseline")
     bits = lambda t: t.view(__import__("torch").int16).numpy().view(np.uint16)
     xb, gb, bb = bits(x), bits(g), bits(b)
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.ln_cast_amax(xb, gb, bb, float(np.float32(1e-5)), np.float32(7.0), oracle.E4M3)
-        n += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
-    byts = n * (rows * hidden * 3 + rows * 8)
-    return dict(value=byts / dt / 1e9, unit="GB/s", cores=1, kind="oracle",
-                sample=f"{n} x LayerNorm+cast+amax of a 2048 x 2048 bf16 block "
-                       f"({dt:.1f} s, numpy float64, single thread)")
+    eps = float(np.float32(1e-5))
+    byts = rows * hidden * 3 + rows * 8
+
+    def run(budget):
+        n = 0
+        t0 = time.perf_counter()
+        while True:
+            X.ln_cast_amax(xb, gb, bb, eps, np.float32(7.0), "e4m3")
+            n += 1
+            if time.perf_counter() - t0 >= budget:
+                break
+        dt = time.perf_counter() - t0
+        return n, dt, n * byts / dt / 1e9
+
+    threads = X.threads()
+    n, dt, gbs = run(budget_s)
+    X.set_threads(1)
+    n1, dt1, gbs1 = run(single_s)
+    X.set_threads(threads)
+    return dict(value=round(gbs, 4), unit="GB/s", cores=threads, kind="oracle",
+                cpu=_cpu_model(), nproc=os.cpu_count(), one_thread_gbs=round(gbs1, 4),
+                sample=f"{n} x LayerNorm+cast+amax of an 8192 x 2048 bf16 block of the headline "
+                       f"workload ({dt:.1f} s, C++ oracle, float64, OpenMP on {threads} "
+                       f"threads; one thread: {n1} blocks in {dt1:.1f} s)")
 
 
 def oracle_workloads(inputs, log):
-    """The oracle (numpy float64; its GEMMs are float64 BLAS products) timed on one
-    step of each GEMM-bound workload's shapes on this host: LayerNormLinear forward
-    at 8 x 32 tokens, its backward at 2048 tokens, LayerNormMLP forward at 2048
-    tokens, and one layer (forward + backward) of the 16384-token 2048/8192
-    scale-up, whose 12-layer step is that time x 12."""
+    """The C++ oracle (float64, exact integer-accumulated GEMMs, OpenMP over rows)
+    timed on one step of each GEMM-bound workload's shapes on this host:
+    LayerNormLinear forward at 8 x 32 tokens, its backward at 2048 tokens,
+    LayerNormMLP forward at 2048 tokens, and one layer (forward + backward) of the
+    16384-token 2048/8192 scale-up, whose 12-layer step is that time x 12."""
     import numpy as np
     import torch
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max((d.get("num_threads", 1) for d in threadpool_info()), default=1)
-    except Exception:   # noqa: BLE001 - the count is informational
-        blas_threads = None
+    import oracle.cxx as X
     bits = lambda t: t.view(torch.int16).numpy().view(np.uint16)
     orc = oracle.Recipe(format=oracle.FORMAT_HYBRID, amax_history_len=16)
 
@@ -623,37 +798,37 @@ def oracle_workloads(inputs, log):
     # LayerNormLinear fwd, 256 tokens, 768 -> 2304
     x, g, b, w, dy = linear_parts(256, 768, 2304, "oracle/ln_linear_fwd")
     mf = oracle.linear_fwd_meta(orc)
-    dt, _ = timed(lambda: oracle.ln_linear_fwd(orc, mf, x, g, b, w))
+    dt, _ = timed(lambda: X.ln_linear_fwd(orc, mf, x, g, b, w))
     out.append(dict(workload="ln_linear_fwd", oracle_ms=dt * 1e3, flops=2.0 * 256 * 2304 * 768))
     # LayerNormLinear bwd, 2048 tokens
     x, g, b, w, dy = linear_parts(2048, 768, 2304, "oracle/ln_linear_bwd")
     mf, mb = oracle.linear_fwd_meta(orc), oracle.linear_bwd_meta(orc)
-    _, (o, ctx) = timed(lambda: oracle.ln_linear_fwd(orc, mf, x, g, b, w))
-    dt, _ = timed(lambda: oracle.ln_linear_bwd(orc, mf, mb, dy, ctx, x, g))
+    _, (o, ctx) = timed(lambda: X.ln_linear_fwd(orc, mf, x, g, b, w))
+    dt, _ = timed(lambda: X.ln_linear_bwd(orc, mf, mb, dy, ctx, x, g))
     out.append(dict(workload="ln_linear_bwd", oracle_ms=dt * 1e3,
                     flops=2 * 2.0 * 2048 * 2304 * 768))
     # LayerNormMLP fwd, 2048 tokens, 768 -> 3072 -> 768
     orc4 = oracle.Recipe(format=oracle.FORMAT_E4M3, amax_history_len=16)
     x, g, b, w1, w2, dy = mlp_parts(2048, 768, 3072, "oracle/ln_mlp_fwd")
     mf = oracle.mlp_fwd_meta(orc4)
-    dt, _ = timed(lambda: oracle.ln_mlp_fwd(orc4, mf, x, g, b, w1, None, w2, None))
+    dt, _ = timed(lambda: X.ln_mlp_fwd(orc4, mf, x, g, b, w1, None, w2, None))
     out.append(dict(workload="ln_mlp_fwd", oracle_ms=dt * 1e3, flops=2 * 2.0 * 2048 * 3072 * 768))
     # one layer of the scale-up, forward + backward
     log("oracle: one 16384 x 2048 x 8192 layer ...")
     orc_h = oracle.Recipe(format=oracle.FORMAT_HYBRID, amax_history_len=1024)
     x, g, b, w1, w2, dy = mlp_parts(16384, 2048, 8192, "oracle/ln_mlp_x12")
     mf, mb = oracle.mlp_fwd_meta(orc_h), oracle.mlp_bwd_meta(orc_h)
-    dtf, (o, ctx) = timed(lambda: oracle.ln_mlp_fwd(orc_h, mf, x, g, b, w1, None, w2, None))
+    dtf, (o, ctx) = timed(lambda: X.ln_mlp_fwd(orc_h, mf, x, g, b, w1, None, w2, None))
     log(f"oracle: layer forward {dtf:.1f} s; backward ...")
-    dtb, _ = timed(lambda: oracle.ln_mlp_bwd(orc_h, mf, mb, dy, ctx, x, g))
+    dtb, _ = timed(lambda: X.ln_mlp_bwd(orc_h, mf, mb, dy, ctx, x, g))
     log(f"oracle: layer backward {dtb:.1f} s")
     out.append(dict(workload="ln_mlp_x12_hybrid", oracle_ms_one_layer=(dtf + dtb) * 1e3,
                     oracle_ms=(dtf + dtb) * 12e3, extrapolated_from="one layer x 12",
                     flops=12 * 6 * 2.0 * 16384 * 8192 * 2048))
     for r in out:
         r["oracle_tflops"] = r["flops"] / (r["oracle_ms"] * 1e-3) / 1e12
-    return dict(kind="oracle", blas_threads=blas_threads, cores=os.cpu_count(),
-                workloads=out)
+    return dict(kind="oracle", implementation="C++ (oracle/cpp), OpenMP", threads=X.threads(),
+                cpu=_cpu_model(), nproc=os.cpu_count(), workloads=out)
 
 
 def main():
@@ -683,6 +858,9 @@ def main():
     if args.profile_ln:
         profile_ln(torch, ops, inputs, args.profile_ln)
         return
+    if args.profile_kernel:
+        profile_kernel(torch, ops, inputs, args.profile_kernel[0], int(args.profile_kernel[1]))
+        return
     if args.profile_gemm:
         M, N, K, reps = args.profile_gemm
         ms = gemm_kernel_ms(torch, ops, M, N, K, torch.float32, reps=reps, bf16=args.bf16)
@@ -697,6 +875,7 @@ def main():
         head = bench_ln_cast(torch, ops, inputs, args.steps, args.warmup)
         torch.cuda.empty_cache()
         head["copy_gbs"] = copy_ceiling_gbs(torch)
+        head["probe_gbs"] = stream_probe_gbs(torch, ops)
     if not args.quick:
         runs = [
             ("ln_linear_fwd", "LayerNormLinear fwd 8x32 tokens, 768->2304, HYBRID, history 16",
@@ -733,20 +912,30 @@ def main():
             r = fn()
             M, N, K, odt = r["gemm"]
             bf16 = r.get("bf16", False)
-            gk_ms = gemm_kernel_ms(torch, ops, M, N, K, odt, bf16=bf16)
-            gflops = 2.0 * M * N * K
             tflops = r["flops"] / (r["ms"] * 1e-3) / 1e12
             peak = BF16_PEAK_TFLOPS if bf16 else FP8_PEAK_TFLOPS
             w = dict(
                 workload=name, description=desc, precision="bf16" if bf16 else "fp8",
                 ms_per_step=round(r["ms"], 5), eager_ms_per_step=round(r["eager_ms"], 5),
                 value=round(tflops, 2), unit="TFLOP/s",
-                frac_of_peak=round(tflops / peak, 4),
-                roofline=dict(bound="mfma", kernel=f"{'bf16' if bf16 else 'fp8'} gemm {M}x{N}x{K}",
-                              achieved=round(gflops / (gk_ms * 1e-3) / 1e12, 2),
-                              peak=peak, unit="TFLOP/s",
-                              frac=round(gflops / (gk_ms * 1e-3) / 1e12 / peak, 4),
-                              kernel_ms=round(gk_ms, 5)))
+                frac_of_peak=round(tflops / peak, 4))
+            if r.get("kinds"):
+                # the step's own GEMM kernels, each timed alone; the roofline
+                # names the one furthest below the peak
+                kinds = mlp_gemm_kinds(torch, ops, *r["kinds"])
+                worst = min(kinds, key=lambda k: k["frac"])
+                w["gemm_kinds"] = kinds
+                w["roofline"] = dict(bound="mfma", kernel=worst["kind"],
+                                     achieved=worst["achieved"], peak=peak, unit="TFLOP/s",
+                                     frac=worst["frac"], kernel_ms=worst["kernel_ms"])
+            else:
+                gk_ms = gemm_kernel_ms(torch, ops, M, N, K, odt, bf16=bf16)
+                gflops = 2.0 * M * N * K
+                w["roofline"] = dict(
+                    bound="mfma", kernel=f"{'bf16' if bf16 else 'fp8'} gemm {M}x{N}x{K}",
+                    achieved=round(gflops / (gk_ms * 1e-3) / 1e12, 2), peak=peak,
+                    unit="TFLOP/s", frac=round(gflops / (gk_ms * 1e-3) / 1e12 / peak, 4),
+                    kernel_ms=round(gk_ms, 5))
             twin = name.replace("_bf16", "")
             twin = "ln_mlp_x12_hybrid" if twin == "ln_mlp_x12" else twin
             fp8_twin = [x for x in workloads if x["workload"] == twin]
@@ -773,9 +962,24 @@ def main():
                                   frac=round(kgbs / HBM_PEAK_GBS, 4), traffic=traffic,
                                   kernel_ms=round(head["kernel_ms"], 5),
                                   bytes_per_launch=head["bytes"],
-                                  copy_ceiling=round(head["copy_gbs"], 1),
-                                  frac_of_copy_ceiling=round(kgbs / head["copy_gbs"], 4)))
+                                  copy_ceiling=round(head["probe_gbs"], 1),
+                                  copy_ceiling_kernel="fp8ln_stream_probe (2 B read + 1 B "
+                                                      "written per element, non-temporal)",
+                                  frac_of_copy_ceiling=round(kgbs / head["probe_gbs"], 4),
+                                  torch_copy_gbs=round(head["copy_gbs"], 1)))
     line["workloads"] = workloads
+    parts = {}
+    lf = [x for x in workloads if x["workload"] == "ln_linear_fwd"]
+    if lf:
+        parts.update(ln_linear_fwd_tflops=lf[0]["value"],
+                     ln_linear_fwd_frac_of_fp8_peak=lf[0]["frac_of_peak"],
+                     ln_linear_fwd_config="8x32 tokens, 768->2304, HYBRID, history 16")
+    if head:
+        parts.update(ln_cast_amax_gbs=line["value"],
+                     ln_cast_amax_frac_of_hbm=round(line["value"] / HBM_PEAK_GBS, 4),
+                     ln_cast_amax_kernel_frac_of_hbm=line["roofline"]["frac"])
+    if parts:
+        line["metric_parts"] = parts
     if not args.no_cpu_baseline and head:
         log("cpu baseline (oracle) ...")
         line["cpu_baseline"] = cpu_baseline(inputs)

@@ -85,6 +85,7 @@ SIGNATURES = {
                                      _P, _P, _P]),
     "fp8ln_cast_amax": (C.c_int, [_I64, _I64, _I32, _P, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "fp8ln_encode_range": (C.c_int, [C.c_uint32, _I64, _I32, _P, _P]),
+    "fp8ln_stream_probe": (C.c_int, [_I64, _P, _P, _P]),
     "fp8ln_gemm": (C.c_int, [_I64, _I64, _I64, _P, _I32, _P, _I32, _P, _P, _P, _I32, _P, _P]),
     "fp8ln_gemm_gelu_fp8": (C.c_int, [_I64, _I64, _I64, _P, _I32, _P, _I32, _P, _P, _P, _P, _P,
                                       _P, _I32, _P, _P, _I32, _P]),

@@ -493,6 +493,17 @@ int fp8ln_encode_range(uint32_t start, int64_t count, int32_t fp8_dtype, uint8_t
     return FP8LN_OK;
 }
 
+int fp8ln_stream_probe(int64_t n, const void* in, uint8_t* out, void* stream) {
+    REQUIRE(n >= 0 && n % 8 == 0, "n %lld must be a non-negative multiple of 8", (long long)n);
+    if (n > 0) {
+        REQUIRE_PTR(in); REQUIRE_PTR(out); REQUIRE_ALIGNED(in); REQUIRE_ALIGNED(out);
+    }
+    int s = check_current_device();
+    if (s) return s;
+    FP8LN_TRY(launch_stream_probe(n, in, out, as_stream(stream)), "stream probe launch");
+    return FP8LN_OK;
+}
+
 int fp8ln_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* A, int32_t a_dtype,
                const uint8_t* B, int32_t b_dtype, const float* sinv_a, const float* sinv_b,
                const void* bias, int32_t out_dtype, void* out, void* stream) {

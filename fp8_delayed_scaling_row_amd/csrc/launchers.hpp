@@ -78,6 +78,10 @@ size_t transpose_b16_workspace(int64_t rows, int64_t cols);
 hipError_t launch_transpose_b16(int64_t rows, int64_t cols, const void* in, void* out,
                                 float* colsum, void* workspace, hipStream_t stream);
 
+// stream.hip: out[i] = high byte of the 16-bit in[i] for n elements (n % 8 == 0),
+// non-temporal; the LayerNorm + cast step's traffic without its arithmetic.
+hipError_t launch_stream_probe(int64_t n, const void* in, uint8_t* out, hipStream_t stream);
+
 // gemm.hip
 enum GemmEpilogue : int {
     kEpiBf16Bias = 0,   // out bf16 = acc * alpha + bias

@@ -22,7 +22,7 @@ __all__ = [
     "FORMAT_E5M2", "GELU_TANH", "GELU_ERF", "E4M3", "E5M2", "META_FORWARD", "META_BACKWARD", "OP_CAST_AMAX",
     "OP_LAYERNORM_BWD", "OP_LN_LINEAR_BWD", "OP_LN_MLP_BWD", "OP_GEMM_DGELU_FP8", "OP_LINEAR_BWD",
     "check_support", "workspace_size", "meta_init",
-    "scaling_update", "ln_cast_amax", "cast_amax", "encode_range", "gemm", "gemm_gelu_fp8",
+    "scaling_update", "ln_cast_amax", "cast_amax", "encode_range", "stream_probe", "gemm", "gemm_gelu_fp8",
     "gemm_dgelu", "gemm_dgelu_fp8", "layernorm_bwd", "layernorm_fwd", "layernorm_bwd_bf16",
     "linear_fwd", "linear_bwd", "gemm_bf16", "gemm_gelu_bf16", "transpose_bf16",
     "ln_linear_fwd_bf16", "ln_linear_bwd_bf16", "ln_mlp_fwd_bf16", "ln_mlp_bwd_bf16",
@@ -109,6 +109,20 @@ class Meta:
     def amax_ptr(self, slot: int) -> int:
         """Address of history row 0 for `slot` (where the step records its amax)."""
         return self.history.data_ptr() + 4 * slot
+
+    def state_dict(self) -> dict:
+        """Host copy of the state (the per-tensor scale, its inverse and the amax
+        history, as fp8_meta keeps them), for a checkpoint."""
+        return dict(amax_history=self.history.cpu().clone(), scale=self.scale.cpu().clone(),
+                    scale_inv=self.scale_inv.cpu().clone())
+
+    def load_state_dict(self, d: dict) -> None:
+        """Restore a state_dict() (same history length and slot count)."""
+        if tuple(d["amax_history"].shape) != tuple(self.history.shape):
+            raise ValueError("history shape differs from this state block's")
+        self.history.copy_(d["amax_history"])
+        self.scale.copy_(d["scale"])
+        self.scale_inv.copy_(d["scale_inv"])
 
 
 class LinearCtx:
@@ -232,6 +246,13 @@ def cast_amax(x, fp8_dtype: int, scale, amax_ptr: int, out, out_t=None, colsum=N
                                 _ptr(ws), nbytes, _stream(stream)))
 
 
+def stream_probe(x, out, stream=None) -> None:
+    """out[i] = high byte of bf16 x[i] (the LayerNorm + cast step's traffic)."""
+    if x.dtype != torch.bfloat16 or out.dtype != torch.uint8 or out.numel() != x.numel():
+        raise ValueError("x must be bf16 and out uint8 with as many elements")
+    check(lib().fp8ln_stream_probe(x.numel(), _ptr(x), _ptr(out), _stream(stream)))
+
+
 def encode_range(start: int, count: int, fp8_dtype: int, out, stream=None) -> None:
     if out.dtype != torch.uint8 or out.numel() < count:
         raise ValueError("out must be a uint8 tensor with at least count elements")
@@ -288,7 +309,7 @@ def gemm_dgelu(a, a_dtype: int, b, b_dtype: int, sinv_a, sinv_b, h, out,
 
 def gemm_dgelu_fp8(a, a_dtype: int, b, b_dtype: int, sinv_a, sinv_b, h, q_dtype: int, q_scale,
                    q_amax_ptr: int, q_out, q_out_t=None, dbias=None, activation: int = GELU_TANH,
-                   stream=None):
+                   stream=None, workspace=None):
     """d = a.b^T * sinv_a * sinv_b * gelu'(h) (fp32, not stored); q_out = encode(d *
     q_scale), q_out_t its transpose, amax of d at q_amax_ptr, dbias = column sums of d."""
     M, K = a.shape
@@ -300,7 +321,10 @@ def gemm_dgelu_fp8(a, a_dtype: int, b, b_dtype: int, sinv_a, sinv_b, h, q_dtype:
     _opt(q_out_t, torch.uint8, (N, M), "q_out_t")
     _opt(dbias, torch.float32, (N,), "dbias")
     nbytes = workspace_size(OP_GEMM_DGELU_FP8, M, N) if dbias is not None else 0
-    ws = _workspace(nbytes, a.device) if dbias is not None else None
+    ws = None
+    if dbias is not None:
+        ws = workspace if workspace is not None else _workspace(nbytes, a.device)
+        nbytes = ws.numel()
     check(lib().fp8ln_gemm_dgelu_fp8(M, N, K, _ptr(a), a_dtype, _ptr(b), b_dtype, _ptr(sinv_a),
                                      _ptr(sinv_b), _ptr(h), q_dtype, _ptr(q_scale),
                                      C.c_void_p(q_amax_ptr), _ptr(q_out), _ptr(q_out_t),

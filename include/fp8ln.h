@@ -247,6 +247,13 @@ int fp8ln_cast_amax(int64_t rows, int64_t cols, int32_t in_dtype, const void* in
 int fp8ln_encode_range(uint32_t start, int64_t count, int32_t fp8_dtype, uint8_t* out,
                        void* stream);
 
+/* Streaming-bandwidth probe (measurement): out[i] = the high byte of the 16-bit
+ * word in[i] for n elements, i.e. the memory traffic of fp8ln_ln_cast_amax (2
+ * bytes read and 1 written per element, non-temporal accesses) without its
+ * arithmetic; its rate on a device is the practical ceiling of that step there.
+ * n: multiple of 8; in (2n bytes) and out (n bytes) 16-byte aligned. */
+int fp8ln_stream_probe(int64_t n, const void* in, uint8_t* out, void* stream);
+
 /* ---- FP8 GEMM ([G] "Playing with lower-precision formats"; [T] intro, FP8
  *      tensor cores) ------------------------------------------------------- */
 

@@ -39,6 +39,33 @@ def oracle_runs(fmt: str):
 
 
 @pytest.mark.parametrize("fp8", [ops.E4M3, ops.E5M2], ids=["e4m3", "e5m2"])
+def test_encoder_equals_cxx_oracle_on_every_float32(fp8):
+    """Element by element over all 2^32 binary32 patterns against the C++
+    oracle's table-exact encoder (which is itself checked exhaustively against
+    the nearest-value definition on the CPU)."""
+    import oracle.cxx as X
+    fmt = FMT[fp8]
+    chunk = 1 << 28
+    out = torch.empty(chunk, dtype=torch.uint8, device="cuda")
+    ref = np.empty(chunk, dtype=np.uint8)
+    for base in range(0, 1 << 32, chunk):
+        ops.encode_range(base, chunk, fp8, out)
+        X.encode_f32_range(base, chunk, fmt, ref)
+        got = out.cpu().numpy()
+        if not np.array_equal(got, ref):
+            i = int(np.nonzero(got != ref)[0][0])
+            raise AssertionError(f"pattern {base + i:#x}: gpu {got[i]:#x} oracle {ref[i]:#x}")
+
+
+def test_stream_probe_picks_the_high_bytes():
+    x = inputs.normal_bf16(((1 << 20) + 8,), inputs.seed_for("probe", "x"), device="cuda")
+    out = torch.empty(x.numel(), dtype=torch.uint8, device="cuda")
+    ops.stream_probe(x, out)
+    want = (x.view(torch.int16).to(torch.int32) >> 8) & 0xFF
+    assert torch.equal(out.to(torch.int32), want)
+
+
+@pytest.mark.parametrize("fp8", [ops.E4M3, ops.E5M2], ids=["e4m3", "e5m2"])
 def test_encoder_matches_oracle_on_every_float32(fp8):
     fmt = FMT[fp8]
     runs = oracle_runs(fmt)

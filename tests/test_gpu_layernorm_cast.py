@@ -319,3 +319,49 @@ def test_layernorm_module_bwd_bf16_grad(rows, hidden):
     assert np.all(np.abs(gdx - odx).max(axis=1) <= 1e-2 * norms + 1e-30)   # bf16 output
     assert_vector_close(dgamma.cpu().numpy(), odg, 1e-5, "dgamma")
     assert_vector_close(dbeta.cpu().numpy(), odb, 1e-5, "dbeta")
+
+
+def test_ln_cast_amax_32_drifting_steps_history_1024():
+    """The LN + cast + amax workload over its 32 steps: 65536 x 2048 rows of
+    N(0,1) with 0.1 % of entries x100 and the input scale drifting 1 -> 4, E4M3,
+    history 1024.  Every step: the scale update's history, scale and scale_inv
+    bit-exact against the oracle's (fed the GPU's recorded amaxes, identical-input
+    mode), the step's LayerNorm-output amax within 1e-6 relative of the oracle's
+    over all rows (C++ oracle, float64), and the codes of sampled rows by the
+    LayerNorm code rule."""
+    import oracle.cxx as X
+    rows, hidden, steps = 65536, 2048, 32
+    recipe = ops.Recipe(format=ops.FORMAT_E4M3, amax_history_len=1024)
+    meta = ops.Meta(recipe, 1, ops.META_FORWARD)
+    om = oracle.Meta.fresh(1024, [oracle.E4M3])
+    wl = "ln_cast_amax_65536x2048"
+    g, b = inputs.layernorm_params(hidden, wl)
+    gd, bd = g.cuda(), b.cuda()
+    gb, bb = to_np_bits(g), to_np_bits(b)
+    eps = float(np.float32(1e-5))
+    out = torch.empty((rows, hidden), dtype=torch.uint8, device="cuda")
+    rng = np.random.default_rng(32)
+    for s in range(steps):
+        print(f"c1 step {s}", flush=True)
+        x = inputs.spiky_normal_bf16((rows, hidden), inputs.seed_for(wl, "x", s),
+                                     drift=inputs.drift_factor(s, steps), device="cuda")
+        ops.scaling_update(recipe, meta)
+        oracle.scaling_update(om)
+        torch.cuda.synchronize()
+        for name in ("history", "scale", "scale_inv"):
+            got = getattr(meta, name).cpu().numpy().reshape(-1).view(np.uint32)
+            want = getattr(om, name).reshape(-1).view(np.uint32)
+            assert np.array_equal(got, want), f"step {s}: {name} differs"
+        ops.ln_cast_amax(recipe, x, gd, bd, ops.E4M3, meta.scale[0:1], meta.amax_ptr(0), out)
+        torch.cuda.synchronize()
+        gpu_amax = np.float32(meta.history[0, 0].item())
+        xb = to_np_bits(x)
+        sc = np.float32(om.scale[0])
+        _, oamax, _, _ = X.ln_cast_amax(xb, gb, bb, eps, sc, oracle.E4M3, stats=False)
+        assert abs(float(gpu_amax) - float(oamax)) <= 1e-6 * float(oamax), (s, gpu_amax, oamax)
+        om.record_amax(0, gpu_amax)          # identical input for the next update
+        sample = rng.integers(0, rows, 48)
+        y, _, _, gx, beta = _oracle_ln(xb[sample], gb, bb, eps, sc, oracle.E4M3)
+        compare_codes(out[torch.from_numpy(sample).cuda()].cpu().numpy(), y * float(sc),
+                      oracle.E4M3, ln_window(gx, beta, float(sc), y * float(sc)))
+    assert np.float32(meta.scale[0].item()) != 1.0

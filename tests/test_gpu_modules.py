@@ -443,6 +443,35 @@ def _oracle_meta(gpu: ops.Meta, fmt, n):
                        gpu.scale_inv.cpu().numpy().copy(), [fmt] * n)
 
 
+def _sampled_weight_grads(orc, om_f, om_b, x_bits, dy_bits, g_bits, b_bits, w1_bits, w2_bits, fs):
+    """The oracle's token-reduced backward results of one LayerNormMLP layer
+    (no biases) over every token, at the fc1 output features fs: rows fs of dW1,
+    columns fs of dW2, db1[fs] and all of db2.  The oracle's own steps (LayerNorm
+    + cast, weight casts, FP8 GEMMs, GELU, gradient casts) run on the whole token
+    set; only the fc1 columns fs of each product are formed, which is all these
+    results depend on.  The state blocks are not modified."""
+    ffmt, bfmt = oracle.fwd_format(orc), oracle.bwd_format(orc)
+    gelu, gelu_grad = ((oracle.gelu_erf, oracle.gelu_erf_grad) if orc.activation == ops.GELU_ERF
+                       else (oracle.gelu_tanh, oracle.gelu_tanh_grad))
+    ln = oracle.ln_cast_amax(x_bits, g_bits, b_bits, orc.eps64, om_f.scale[0], ffmt)
+    w1_q, _ = oracle.cast_amax(oracle.bf16_to_f64(w1_bits), om_f.scale[1], ffmt)
+    w2_q, _ = oracle.cast_amax(oracle.bf16_to_f64(w2_bits), om_f.scale[3], ffmt)
+    h = oracle.fp8_gemm_tn(ln["q"], ffmt, w1_q[fs], ffmt, om_f.scale_inv[0], om_f.scale_inv[1])
+    g_q, _ = oracle.cast_amax(gelu(h), om_f.scale[2], ffmt)
+    dy = oracle.bf16_to_f64(dy_bits)
+    dy_q, _ = oracle.cast_amax(dy, om_b.scale[0], bfmt)
+    dg = oracle.fp8_gemm_tn(dy_q, bfmt, np.ascontiguousarray(w2_q.T[fs]), ffmt,
+                            om_b.scale_inv[0], om_f.scale_inv[3])
+    dh = dg * gelu_grad(oracle.bf16_to_f64(oracle.f64_to_bf16_bits(h)))
+    dh_q, _ = oracle.cast_amax(dh, om_b.scale[1], bfmt)
+    return dict(
+        dw1_rows=oracle.fp8_gemm_tn(dh_q.T, bfmt, ln["q"].T, ffmt, om_b.scale_inv[1],
+                                    om_f.scale_inv[0]),
+        dw2_cols=oracle.fp8_gemm_tn(dy_q.T, bfmt, g_q.T, ffmt, om_b.scale_inv[0],
+                                    om_f.scale_inv[2]),
+        db1=dh.sum(axis=0), db2=dy.sum(axis=0))
+
+
 @pytest.mark.parametrize("fmt", [ops.FORMAT_HYBRID, ops.FORMAT_E4M3])
 def test_ln_mlp_x12_chain_layers_0_5_11(fmt):
     """The 12-layer scale-up chain (16384 tokens, 2048 -> 8192 -> 2048, history
@@ -481,7 +510,8 @@ def test_ln_mlp_x12_chain_layers_0_5_11(fmt):
             g, b, w1, w2 = d["dev"]
             ops.scaling_update(recipe, d["mf"])
             if step == 1 and l in checks:
-                saved[l] = dict(x=to_np_bits(x[rows_t]), mf=_oracle_meta(d["mf"], ffmt, 4))
+                saved[l] = dict(x=to_np_bits(x[rows_t]), mf=_oracle_meta(d["mf"], ffmt, 4),
+                                x_full=to_np_bits(x))
             ops.ln_mlp_fwd(recipe, x, g, b, w1, None, w2, None, d["out"], d["mf"], d["ctx"])
             x = d["out"]
         grad = dy
@@ -492,6 +522,7 @@ def test_ln_mlp_x12_chain_layers_0_5_11(fmt):
             ops.scaling_update(recipe, d["mb"])
             if step == 1 and l in checks:
                 saved[l]["dy"] = to_np_bits(grad[rows_t])
+                saved[l]["dy_full"] = to_np_bits(grad)
                 saved[l]["mb"] = _oracle_meta(d["mb"], bfmt, 2)
             dx = dxs[i % 2]
             ops.ln_mlp_bwd(recipe, grad, xin, d["dev"][0], d["ctx"], d["mf"], d["mb"], dx,
@@ -528,6 +559,17 @@ def test_ln_mlp_x12_chain_layers_0_5_11(fmt):
             win = win + s2 * 1.13 * float(alpha) * (d_ln @ w1abs.T)
         stats = compare_codes(ctx.g_q[rows_t].cpu().numpy(), octx["g"] * s2, ffmt, win)
         assert_gemm_close(sv["dx"], og["dx"], alarm=5e-2, what=f"{tag} dx")
+        # the token-reduced results over all 16384 tokens, at sampled fc1 features
+        fs = np.unique(np.concatenate([[0, F - 1], np.random.default_rng(l).integers(0, F, 6)]))
+        ref = _sampled_weight_grads(orc, sv["mf"], sv["mb"], sv["x_full"], sv["dy_full"],
+                                    gbits, bbits, w1bits, w2bits, fs)
+        gdw1, gdb1, gdw2, gdb2 = (t.cpu().numpy() for t in
+                                  (d["grads"][2], d["grads"][3], d["grads"][4], d["grads"][5]))
+        assert_gemm_close(gdw1[fs], ref["dw1_rows"], alarm=5e-2, what=f"{tag} dW1 rows")
+        assert_gemm_close(gdw2[:, fs].T, ref["dw2_cols"].T, alarm=5e-2,
+                          what=f"{tag} dW2 columns")
+        assert_vector_close(gdb1[fs], ref["db1"], 1e-3, f"{tag} db1")
+        assert_vector_close(gdb2, ref["db2"], 1e-5, f"{tag} db2")
         print(f"{fmt} {tag}: g codes {stats}")
 
 
@@ -618,3 +660,67 @@ def test_ln_mlp_fwd_front_equals_standalone_entry_points(M, H, F):
     assert torch.equal(ctx.w2_q, w2_q) and torch.equal(ctx.w2_qt, w2_qt)
     for s in (0, 1, 3):
         assert ma.history[0, s].view(torch.int32).item() == mb.history[0, s].view(torch.int32).item()
+
+
+# ---- the pages' workloads over their full step counts ---------------------------
+
+def test_ln_mlp_fwd_2048_tokens_16_steps():
+    """LayerNormMLP 768 -> 3072 -> 768 on 8 x 256 tokens, E4M3 on both GEMM inputs
+    with separate histories of length 16, over 16 steps (the history fills), each
+    step against the oracle's own chain."""
+    run_mlp(ops.Recipe(format=ops.FORMAT_E4M3, amax_history_len=16), 2048, 768, 3072, 16,
+            "c2-16", backward=False)
+
+
+# ---- checkpoint and resume of the FP8 state ---------------------------------------
+
+def _mlp_run(recipe, M, H, F, steps, first, state, wl):
+    """Steps first .. steps-1 of a LayerNormMLP training loop starting from
+    `state` (state_dicts of both metas, or None for fresh ones); returns the
+    outputs of every step and the final state."""
+    g, b = inputs.layernorm_params(H, wl, device="cuda")
+    w1 = inputs.linear_weight(F, H, wl, "w1", device="cuda")
+    w2 = inputs.linear_weight(H, F, wl, "w2", device="cuda")
+    mf, mb = ops.mlp_metas(recipe)
+    if state is not None:
+        mf.load_state_dict(state[0])
+        mb.load_state_dict(state[1])
+    ctx = ops.MlpCtx(M, H, F)
+    results = []
+    for step in range(first, steps):
+        x = inputs.normal_bf16((M, H), inputs.seed_for(wl, "x", step), device="cuda")
+        dy = inputs.normal_bf16((M, H), inputs.seed_for(wl, "dy", step), std=1e-3, device="cuda")
+        out = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+        dx = torch.empty_like(out)
+        grads = [torch.empty(H, device="cuda"), torch.empty(H, device="cuda"),
+                 torch.empty((F, H), device="cuda"), torch.empty(F, device="cuda"),
+                 torch.empty((H, F), device="cuda"), torch.empty(H, device="cuda")]
+        ops.scaling_update(recipe, mf)
+        ops.ln_mlp_fwd(recipe, x, g, b, w1, None, w2, None, out, mf, ctx)
+        ops.scaling_update(recipe, mb)
+        ops.ln_mlp_bwd(recipe, dy, x, g, ctx, mf, mb, dx, *grads)
+        results.append([out, dx, ctx.g_q.clone(), mf.history.clone(), mb.history.clone(),
+                        mf.scale.clone(), mb.scale.clone()] + grads)
+    torch.cuda.synchronize()
+    return results, (mf.state_dict(), mb.state_dict())
+
+
+@pytest.mark.parametrize("fmt", [ops.FORMAT_HYBRID, ops.FORMAT_E4M3])
+def test_resume_from_a_checkpoint_is_bit_identical(fmt):
+    """The FP8 state (scale, scale_inv, amax history per module and direction,
+    as the tutorial's fp8_meta holds it) is everything a step carries over:
+    restoring a snapshot taken after step k into fresh state blocks and running
+    steps k+1 .. n gives, bit for bit, what the uninterrupted run gave."""
+    recipe = ops.Recipe(format=fmt, amax_history_len=4)
+    M, H, F, n, k = 512, 768, 3072, 7, 3
+    wl = f"resume/{fmt}"
+    full, _ = _mlp_run(recipe, M, H, F, n, 0, None, wl)
+    _, snap = _mlp_run(recipe, M, H, F, k, 0, None, wl)
+    resumed, _ = _mlp_run(recipe, M, H, F, n, k, snap, wl)
+    assert len(resumed) == n - k
+    for step, (a, b) in enumerate(zip(full[k:], resumed)):
+        for i, (ta, tb) in enumerate(zip(a, b)):
+            assert torch.equal(ta.view(torch.uint8), tb.view(torch.uint8)), \
+                f"step {k + step}: result {i} differs after resume"
+    # the history really carried information: the resumed scales are not fresh ones
+    assert not torch.equal(resumed[0][5], torch.ones_like(resumed[0][5]))
