@@ -106,16 +106,15 @@ __device__ __forceinline__ uint32_t encode4(float v0, float v1, float v2, float 
 __device__ __forceinline__ float mul_round_odd(float v, float s) {
     const float p = v * s;
     const float e = fmaf(v, s, -p);            // exact remainder of the product
-    uint32_t b = __float_as_uint(p);
-    // only a finite non-zero product is adjusted: an infinite product (an
-    // infinite v, or an overflow) has a NaN or infinite remainder and must stay
-    // infinite, so that the encoder saturates it
-    const bool fix = (e != 0.0f) && ((b & 1u) == 0u) && (p != 0.0f) &&
-                     ((b & 0x7f800000u) != 0x7f800000u);
-    // same sign: the exact magnitude is larger -> step the bits up, else down
-    const uint32_t step = ((__float_as_uint(e) ^ b) & 0x80000000u) ? 0xffffffffu : 1u;
-    b += fix ? step : 0u;
-    return __uint_as_float(b);
+    const uint32_t b = __float_as_uint(p);
+    // Inexact (a non-zero finite remainder; an infinite product has a NaN or
+    // infinite remainder and stays infinite, so that the encoder saturates it):
+    // the product truncated toward zero is p itself when the remainder has p's
+    // sign and one step below p in magnitude otherwise, and forcing its last bit
+    // to 1 gives the round-to-odd result.
+    const uint32_t down = (uint32_t)((int32_t)(__float_as_uint(e) ^ b) >> 31);   // 0 or -1
+    const bool inexact = __builtin_amdgcn_classf(e, 0x198);   // +-normal, +-subnormal
+    return __uint_as_float(inexact ? ((b + down) | 1u) : b);
 }
 
 // Replace the code of every NaN among v[0..3] by 0x7F.

@@ -141,37 +141,72 @@ __device__ __forceinline__ T lds_ld(const lds8* a) {
     return *reinterpret_cast<const __attribute__((address_space(3))) T*>(a);
 }
 
-// Rows of RB bytes staged in a ring of LDS stages of STAGE bytes each: row r
-// lives in stage r / RPS, and its 16-byte chunk c at chunk position c ^ (r & SWM).
-template <int RB, int STAGE>
+// Smallest power of two P such that a stage of STAGE bytes holds a multiple of 32
+// rows of LB / P bytes.
+constexpr int staging_parts(int LB, int STAGE) {
+    int p = 1;
+    while ((STAGE / (LB / p)) % 32 != 0) p *= 2;
+    return p;
+}
+
+// A tile of ROWS rows of LB bytes staged in a ring of LDS stages of STAGE bytes.
+// Each row is cut into P parts of RB = LB / P bytes, P chosen so that a stage holds
+// RPS part rows with RPS a multiple of 32: the 32 rows that the lanes of a wave
+// touch at once (rows 32 k .. 32 k + 31 of one part) then always share a stage,
+// and the stage is picked from wave-uniform values, by scalar instructions, with
+// no per-lane select.  Part row s = part * ROWS + r lives in stage s / RPS, and
+// its 16-byte chunk c at chunk position c ^ (s & SWM).
+template <int LB, int ROWS, int STAGE>
 struct Staging {
+    static constexpr int P = staging_parts(LB, STAGE);
+    static constexpr int RB = LB / P;
     static constexpr int NC = RB / 16;
     static constexpr int RPS = STAGE / RB;
     static constexpr int SWM = (NC < 32 ? NC : 32) - 1;
-    static_assert(RB % 16 == 0 && RPS >= 1, "staging geometry");
+    static constexpr int UNITS = ROWS * P * NC;   // 16-byte chunks of the tile
+    static_assert(RB % 16 == 0 && RPS % 32 == 0 && ROWS % 32 == 0, "staging geometry");
 
+    // Start of part row part * ROWS + r_u, for a wave-uniform part and a
+    // wave-uniform multiple of 32 r_u (a scalar value, computed once per block of
+    // 32 rows and kept).
     template <class Ring>
-    __device__ __forceinline__ static lds8* at(Ring ring, int r, int c16) {
-        return ring(r / RPS) + (r % RPS) * RB + ((c16 ^ (r & SWM)) << 4);
+    __device__ __forceinline__ static lds8* row(Ring ring, int part, int r_u) {
+        const int s_u = part * ROWS + r_u;
+        return ring(s_u / RPS) + (s_u % RPS) * RB;
     }
-    // Copies ROWS staged rows to dst, whose rows are ld bytes
-    // apart, as 16-byte chunks; rows at or past rows_valid and chunks at or past
-    // bytes_valid are skipped.  Each wave writes whole rows, with non-temporal
-    // stores (the output is not read again by this kernel).
-    template <int ROWS, int NT, class Ring>
+    // Chunk c (of the part) of row r_l in [0, 32) below a row() start.
+    __device__ __forceinline__ static lds8* in_row(lds8* base, int r_l, int c) {
+        return base + r_l * RB + ((c ^ (r_l & SWM)) << 4);
+    }
+    // LDS address of chunk position u (positions in stage order)
+    template <class Ring>
+    __device__ __forceinline__ static lds8* pos(Ring ring, int u) {
+        return ring(u / (RPS * NC)) + (u % (RPS * NC)) * 16;
+    }
+    // tile row and byte column of the chunk that chunk position u holds
+    __device__ __forceinline__ static void source(int u, int& row, int& byte) {
+        const int s = u / NC, c = u % NC;
+        row = s % ROWS;
+        byte = (s / ROWS) * RB + ((c ^ (s & SWM)) << 4);
+    }
+    // Copies the staged tile to dst, whose rows are ld bytes apart, as 16-byte
+    // chunks; rows at or past rows_valid and bytes at or past bytes_valid are
+    // skipped.  Each wave writes whole part rows, with non-temporal stores (the
+    // output is not read again by this kernel).
+    template <int NT, class Ring>
     __device__ __forceinline__ static void copy_out(Ring ring, int t, uint8_t* dst, int64_t ld,
                                                     int64_t rows_valid, int64_t bytes_valid) {
-        constexpr int TOTAL = ROWS * NC;
         constexpr int PER_STAGE = RPS * NC / NT;   // loop iterations per stage
-        static_assert(TOTAL % NT == 0 && (RPS * NC) % NT == 0, "copy split");
+        static_assert(UNITS % NT == 0 && (RPS * NC) % NT == 0, "copy split");
 #pragma unroll
-        for (int it = 0; it < TOTAL / NT; ++it) {
+        for (int it = 0; it < UNITS / NT; ++it) {
             const int u = it * NT + t;
-            const int r = u / NC, c = u % NC;
-            const u32x4 w = lds_ld<u32x4>(ring(it / PER_STAGE) + (r % RPS) * RB +
-                                          ((c ^ (r & SWM)) << 4));
-            if (r < rows_valid && c * 16 < bytes_valid)
-                __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(dst + r * ld + c * 16));
+            const int s = u / NC, c = u % NC;
+            const int r = s % ROWS, col = (s / ROWS) * RB + c * 16;
+            const u32x4 w = lds_ld<u32x4>(ring(it / PER_STAGE) + (s % RPS) * RB +
+                                          ((c ^ (s & SWM)) << 4));
+            if (r < rows_valid && col < bytes_valid)
+                __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(dst + r * ld + col));
         }
     }
 };
@@ -427,28 +462,37 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int vb) {
     const float alpha = FA == kOpBf16 ? 1.0f : (*p.sinv_a) * (*p.sinv_b);   // bf16: no scales
     const int row_w = wm * WM + fr;      // tile row of this lane's i = 0 values
     const int col_w = wn * WN + 4 * fh;  // tile column of this lane's j = q = 0 values
+    // tile rows and columns inside the product (32-bit bounds tests below)
+    const int rows_in = (int)min<int64_t>(BM, M - m0);
+    const int cols_in = (int)min<int64_t>(BN, N - n0);
 
     if constexpr (EPI == kEpiDGeluFp8) {
         // Bring the tile of h into the ring in the bf16 staging layout (direct
         // loads, rows past M read as zero), then scale by gelu'(h) in place.
-        using G = Staging<BN * 2, STAGE>;
-        constexpr int IPW = BM * G::NC / 64 / NW;    // 64-chunk loads per wave
+        using G = Staging<BN * 2, BM, STAGE>;
+        static_assert(BM * G::P <= NS * G::RPS && G::UNITS % (64 * NW) == 0, "h staging");
+        constexpr int IPW = G::UNITS / 64 / NW;    // 64-chunk loads per wave
         const int64_t rows_h = min<int64_t>(BM, M - m0);
         const __amdgpu_buffer_rsrc_t rsrc_h = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(p.h_in + m0 * N), (short)0, (int)(rows_h * N * 2), kBufferWord3);
 #pragma unroll
         for (int jj = 0; jj < IPW; ++jj) {
             const int u0 = (wave * IPW + jj) * 64;
-            const int u = u0 + lane;
-            const int lr = u / G::NC;
-            const int c16 = (u % G::NC) ^ (lr & G::SWM);
-            const uint32_t voff = (uint32_t)(lr * N * 2 + n0 * 2 + c16 * 16);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rsrc_h, (lds_ptr)(ring(u0 / (G::RPS * G::NC)) + (u0 % (G::RPS * G::NC)) * 16), 16,
-                voff, 0, 0, 0);
+            int lr, byte;
+            G::source(u0 + lane, lr, byte);
+            const uint32_t voff = (uint32_t)(lr * N * 2 + n0 * 2 + byte);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_h, (lds_ptr)G::pos(ring, u0), 16, voff,
+                                                     0, 0, 0);
         }
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __syncthreads();
+        // staged row starts of the wave's 32 x 32 blocks, once per block
+        lds8* hrow[TM][TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                hrow[i][j] = G::row(ring, (wn * WN + 32 * j) / 8 / G::NC, wm * WM + 32 * i);
         auto scale_by_dgelu = [&](auto erf) __attribute__((always_inline)) {
             constexpr bool ERF = decltype(erf)::value;
 #pragma unroll
@@ -459,8 +503,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int vb) {
                     for (int q = 0; q < 4; ++q) {
                         const int lr = row_w + 32 * i;
                         const int lc = col_w + 32 * j + 8 * q;
-                        const u32x2 hw = lds_ld<u32x2>(G::at(ring, lr, lc / 8) + 8 * fh);
-                        const bool ok = m0 + lr < M && n0 + lc < N;
+                        const u32x2 hw = lds_ld<u32x2>(
+                            G::in_row(hrow[i][j], fr, (wn * WN + 32 * j + 8 * q) / 8 % G::NC) +
+                            8 * fh);
+                        const bool ok = lr < rows_in && lc < cols_in;
                         const float hv[4] = {bf16_lo(hw.x), bf16_hi(hw.x), bf16_lo(hw.y),
                                              bf16_hi(hw.y)};
 #pragma unroll
@@ -483,18 +529,18 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int vb) {
         for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int64_t gn = n0 + col_w + 32 * j + 8 * q;
+                const int cn = col_w + 32 * j + 8 * q;
                 float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
                 if constexpr (EPI == kEpiBf16Bias || EPI == kEpiGeluFp8 || EPI == kEpiGeluBf16) {
-                    if (p.bias && gn < N) {
-                        const uint2 bw = *reinterpret_cast<const uint2*>(p.bias + gn);
+                    if (p.bias && cn < cols_in) {
+                        const uint2 bw = *reinterpret_cast<const uint2*>(p.bias + n0 + cn);
                         bv[0] = bf16_lo(bw.x); bv[1] = bf16_hi(bw.x);
                         bv[2] = bf16_lo(bw.y); bv[3] = bf16_hi(bw.y);
                     }
                 }
 #pragma unroll
                 for (int i = 0; i < TM; ++i) {
-                    const bool ok = m0 + row_w + 32 * i < M && gn < N;
+                    const bool ok = row_w + 32 * i < rows_in && cn < cols_in;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const float x = acc[j][i][4 * q + e];
@@ -533,28 +579,37 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int vb) {
 
     if constexpr (EPI == kEpiF32 || EPI == kEpiDGeluF32) {
         // fp32 rows; a 256 x 256 tile goes out in two passes of 128 rows
-        using G = Staging<BN * 4, STAGE>;
-        constexpr int PASSES = (BM * BN * 4 + NS * STAGE - 1) / (NS * STAGE);
+        constexpr int P4 = staging_parts(BN * 4, STAGE);
+        constexpr int CAP = NS * (STAGE / (BN * 4 / P4)) / P4;   // tile rows one pass holds
+        constexpr int PASSES = (BM + CAP - 1) / CAP;
         constexpr int RPP = BM / PASSES;
-        static_assert(RPP % WM == 0 && RPP <= NS * G::RPS, "f32 staging");
+        using G = Staging<BN * 4, RPP, STAGE>;
+        static_assert(RPP * PASSES == BM && RPP % WM == 0 && RPP * G::P <= NS * G::RPS,
+                      "f32 staging");
 #pragma unroll
         for (int ps = 0; ps < PASSES; ++ps) {
             if (wm * WM >= ps * RPP && wm * WM < (ps + 1) * RPP) {
+                lds8* frow[TM][TN];
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        frow[i][j] = G::row(ring, (wn * WN + 32 * j) / 4 / G::NC,
+                                            wm * WM + 32 * i - ps * RPP);
 #pragma unroll
                 for (int i = 0; i < TM; ++i)
 #pragma unroll
                     for (int j = 0; j < TN; ++j)
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
-                            const int lr = row_w + 32 * i - ps * RPP;
-                            const int lc = col_w + 32 * j + 8 * q;
-                            lds_st(G::at(ring, lr, lc / 4),
+                            lds_st(G::in_row(frow[i][j], fr,
+                                             (wn * WN + 32 * j + 8 * q) / 4 % G::NC + fh),
                                    f32x4{acc[j][i][4 * q], acc[j][i][4 * q + 1],
                                          acc[j][i][4 * q + 2], acc[j][i][4 * q + 3]});
                         }
             }
             __syncthreads();
-            G::template copy_out<RPP, NT>(ring, t, (uint8_t*)p.out + ((m0 + ps * RPP) * N + n0) * 4,
+            G::template copy_out<NT>(ring, t, (uint8_t*)p.out + ((m0 + ps * RPP) * N + n0) * 4,
                                          N * 4, M - m0 - ps * RPP, (N - n0) * 4);
             __syncthreads();
         }
@@ -562,22 +617,27 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int vb) {
 
     // bf16 rows of the tile through the ring
     auto bf16_out = [&](uint16_t* dst) {
-        using G = Staging<BN * 2, STAGE>;
-        static_assert(BM <= NS * G::RPS, "bf16 staging");
+        using G = Staging<BN * 2, BM, STAGE>;
+        static_assert(BM * G::P <= NS * G::RPS, "bf16 staging");
+        lds8* brow[TM][TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                brow[i][j] = G::row(ring, (wn * WN + 32 * j) / 8 / G::NC, wm * WM + 32 * i);
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int j = 0; j < TN; ++j)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int lr = row_w + 32 * i;
-                    const int lc = col_w + 32 * j + 8 * q;
-                    lds_st(G::at(ring, lr, lc / 8) + 8 * fh,
+                    lds_st(G::in_row(brow[i][j], fr, (wn * WN + 32 * j + 8 * q) / 8 % G::NC) +
+                               8 * fh,
                            u32x2{pack_bf16x2(acc[j][i][4 * q], acc[j][i][4 * q + 1]),
                                  pack_bf16x2(acc[j][i][4 * q + 2], acc[j][i][4 * q + 3])});
                 }
         __syncthreads();
-        G::template copy_out<BM, NT>(ring, t, (uint8_t*)(dst + m0 * N + n0), N * 2, M - m0,
+        G::template copy_out<NT>(ring, t, (uint8_t*)(dst + m0 * N + n0), N * 2, M - m0,
                                     (N - n0) * 2);
         __syncthreads();
     };
@@ -612,9 +672,19 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int vb) {
         // transposed one (rows = output columns).  For the transposed copy the
         // four lanes of a quad swap bytes so that each holds one column of four
         // consecutive rows, written as one word.
-        using Q = Staging<BN, STAGE>;
-        using QT = Staging<BM, STAGE>;
-        static_assert(BM <= NS * Q::RPS && BN <= NS * QT::RPS, "code staging");
+        using Q = Staging<BN, BM, STAGE>;
+        using QT = Staging<BM, BN, STAGE>;
+        static_assert(BM * Q::P <= NS * Q::RPS && BN * QT::P <= NS * QT::RPS, "code staging");
+        static_assert(QT::P == 1, "transposed code rows are never cut");
+        lds8* qrow[TM][TN];
+        lds8* qtrow[TN];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                qrow[i][j] = Q::row(ring, (wn * WN + 32 * j) / 16 / Q::NC, wm * WM + 32 * i);
+            qtrow[j] = QT::row(ring, 0, wn * WN + 32 * j);
+        }
         const float qs = *p.q_scale;
         uint32_t amax_bits = 0;
         uint32_t codes[TM][TN][4];
@@ -645,14 +715,16 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int vb) {
                     if (__builtin_expect(cm > kInfBits, 0)) code = patch_nan4(code, gs);
                     if constexpr (EPI == kEpiGeluFp8) {
                         // rows and columns outside the product carry gelu(0) = 0
-                        if (!(m0 + lr < M && n0 + lc < N)) cm = 0;
+                        if (!(lr < rows_in && lc < cols_in)) cm = 0;
                     }
                     amax_bits = amax_bits > cm ? amax_bits : cm;
                     codes[i][j][q] = code;
-                    lds_st(Q::at(ring, lr, lc / 16) + 4 * ((lc / 4) % 4), code);
+                    lds_st(Q::in_row(qrow[i][j], fr, (wn * WN + 32 * j + 8 * q) / 16 % Q::NC) +
+                               4 * ((lc / 4) % 4),
+                           code);
                 }
         __syncthreads();
-        Q::template copy_out<BM, NT>(ring, t, p.q_out + m0 * N + n0, N, M - m0, N - n0);
+        Q::template copy_out<NT>(ring, t, p.q_out + m0 * N + n0, N, M - m0, N - n0);
         if (p.q_out_t) {
             __syncthreads();
             const bool odd = fr & 1, hi2 = fr & 2;
@@ -671,12 +743,14 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int vb) {
                             (int)c2, kDppQuadSwap1, 0xF, 0xF, false);
                         const uint32_t ct = odd ? __builtin_amdgcn_perm(o1, c2, 0x03070105u)
                                                 : __builtin_amdgcn_perm(o1, c2, 0x06020400u);
-                        const int tn = col_w + 32 * j + 8 * q + (fr & 3);  // staged row = column
                         const int tm = (row_w + 32 * i) & ~3;              // first of four rows
-                        lds_st(QT::at(ring, tn, tm / 16) + 4 * ((tm / 4) % 4), ct);
+                        lds_st(QT::in_row(qtrow[j], 8 * q + 4 * fh + (fr & 3),
+                                          (wm * WM + 32 * i) / 16 + (fr >> 4)) +
+                                   4 * ((tm / 4) % 4),
+                               ct);
                     }
             __syncthreads();
-            QT::template copy_out<BN, NT>(ring, t, p.q_out_t + n0 * M + m0, M, N - n0, M - m0);
+            QT::template copy_out<NT>(ring, t, p.q_out_t + n0 * M + m0, M, N - n0, M - m0);
         }
         if constexpr (EPI == kEpiDGeluFp8) {
             if (p.col_partial) {
