@@ -192,21 +192,30 @@ struct Staging {
     // Copies the staged tile to dst, whose rows are ld bytes apart, as 16-byte
     // chunks; rows at or past rows_valid and bytes at or past bytes_valid are
     // skipped.  Each wave writes whole part rows, with non-temporal stores (the
-    // output is not read again by this kernel).
-    template <int NT, class Ring>
+    // output is not read again by this kernel).  Thread t always takes chunk
+    // t % NC of part row t / NC of each group of NT / NC part rows, so its global
+    // address is one per-thread base plus a uniform offset per iteration.
+    template <int NT, bool CHECK, class Ring>
     __device__ __forceinline__ static void copy_out(Ring ring, int t, uint8_t* dst, int64_t ld,
                                                     int64_t rows_valid, int64_t bytes_valid) {
         constexpr int PER_STAGE = RPS * NC / NT;   // loop iterations per stage
+        constexpr int RPI = NT / NC;               // part rows per iteration
         static_assert(UNITS % NT == 0 && (RPS * NC) % NT == 0, "copy split");
+        static_assert(NT % NC == 0 && ROWS % RPI == 0 && RPS % RPI == 0, "copy rows");
+        const int r_t = t / NC, c = t % NC;
+        const int rv = (int)(rows_valid < ROWS ? rows_valid : ROWS) - r_t;
+        const int bv = (int)(bytes_valid < LB ? bytes_valid : LB) - c * 16;
+        uint8_t* base = dst + r_t * ld + c * 16;
 #pragma unroll
         for (int it = 0; it < UNITS / NT; ++it) {
-            const int u = it * NT + t;
-            const int s = u / NC, c = u % NC;
-            const int r = s % ROWS, col = (s / ROWS) * RB + c * 16;
-            const u32x4 w = lds_ld<u32x4>(ring(it / PER_STAGE) + (s % RPS) * RB +
+            const int s_u = it * RPI;                      // first part row of the iteration
+            const int r_u = s_u % ROWS, part = s_u / ROWS;
+            const int s = s_u + r_t;
+            const u32x4 w = lds_ld<u32x4>(ring(it / PER_STAGE) + (s_u % RPS + r_t) * RB +
                                           ((c ^ (s & SWM)) << 4));
-            if (r < rows_valid && col < bytes_valid)
-                __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(dst + r * ld + col));
+            if (!CHECK || (r_u < rv && part * RB < bv))
+                __builtin_nontemporal_store(
+                    w, reinterpret_cast<u32x4*>(base + r_u * ld + part * RB));
         }
     }
 };
@@ -236,10 +245,13 @@ __device__ __forceinline__ void butterfly_sum(float* v, int fr) {
     butterfly_step<NV / 16, 1>(v, fr);
 }
 
-// EPIX = epilogue + 16 ACT: ACT 1 and 2 fix the GELU form at compile time (tanh,
-// erf) for the GELU / GELU' epilogues whose loops would otherwise be compiled
-// once per form behind a runtime branch, which makes the register allocator
-// spill the accumulators; ACT 0 reads the form from the parameters.
+// EPIX = epilogue + 16 ACT + 64 FULL: ACT 1 and 2 fix the GELU form at compile
+// time (tanh, erf) for the GELU / GELU' epilogues whose loops would otherwise be
+// compiled once per form behind a runtime branch, which makes the register
+// allocator spill the accumulators; ACT 0 reads the form from the parameters.
+// FULL 1: no tile crosses the product's edge (the epilogue drops its bounds
+// tests; one copy of the epilogue per kernel, as two copies behind a branch
+// spill).
 // vb: the tile's block index (the kernel's own, or its index inside one problem
 // of a grouped launch).  GROUP only tags the grouped kernel's instantiation (the
 // same specialization called from two kernels does not resolve in hipcc's host
@@ -248,7 +260,8 @@ template <int BM, int BN, int WGM, int WGN, int NS, int FA, int FB, int EPIX, in
           bool GROUP = false>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, int vb) {
     constexpr int EPI = EPIX % 16;
-    constexpr int ACT = EPIX / 16;
+    constexpr int ACT = EPIX / 16 % 4;
+    constexpr bool FULLX = EPIX >= 64;
     static_assert(NS == 3 || NS == 4, "three or four pipeline stages");
     constexpr int NW = WGM * WGN;              // waves per workgroup
     constexpr int WM = BM / WGM, WN = BN / WGN;  // wave sub-tile
@@ -465,36 +478,247 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int vb) {
     // tile rows and columns inside the product (32-bit bounds tests below)
     const int rows_in = (int)min<int64_t>(BM, M - m0);
     const int cols_in = (int)min<int64_t>(BN, N - n0);
+    // FULLX: every tile lies wholly inside the product (M and N are multiples of
+    // the tile, checked by the launcher), so the epilogue has no bounds tests.
+    __shared__ float colp[EPI == kEpiDGeluFp8 ? WGM : 1][EPI == kEpiDGeluFp8 ? BN : 1];
+    __shared__ uint32_t red[NW];
+    auto epilogue = [&](auto full_tile) __attribute__((always_inline)) {
+        constexpr bool FULL = decltype(full_tile)::value;
+        auto in_rows = [&](int r) { return FULL || r < rows_in; };
+        auto in_cols = [&](int c) { return FULL || c < cols_in; };
 
-    if constexpr (EPI == kEpiDGeluFp8) {
-        // Bring the tile of h into the ring in the bf16 staging layout (direct
-        // loads, rows past M read as zero), then scale by gelu'(h) in place.
-        using G = Staging<BN * 2, BM, STAGE>;
-        static_assert(BM * G::P <= NS * G::RPS && G::UNITS % (64 * NW) == 0, "h staging");
-        constexpr int IPW = G::UNITS / 64 / NW;    // 64-chunk loads per wave
-        const int64_t rows_h = min<int64_t>(BM, M - m0);
-        const __amdgpu_buffer_rsrc_t rsrc_h = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(p.h_in + m0 * N), (short)0, (int)(rows_h * N * 2), kBufferWord3);
+        if constexpr (EPI == kEpiDGeluFp8) {
+            // Bring the tile of h into the ring in the bf16 staging layout (direct
+            // loads, rows past M read as zero), then scale by gelu'(h) in place.
+            using G = Staging<BN * 2, BM, STAGE>;
+            static_assert(BM * G::P <= NS * G::RPS && G::UNITS % (64 * NW) == 0, "h staging");
+            constexpr int IPW = G::UNITS / 64 / NW;    // 64-chunk loads per wave
+            const int64_t rows_h = min<int64_t>(BM, M - m0);
+            const __amdgpu_buffer_rsrc_t rsrc_h = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(p.h_in + m0 * N), (short)0, (int)(rows_h * N * 2), kBufferWord3);
 #pragma unroll
-        for (int jj = 0; jj < IPW; ++jj) {
-            const int u0 = (wave * IPW + jj) * 64;
-            int lr, byte;
-            G::source(u0 + lane, lr, byte);
-            const uint32_t voff = (uint32_t)(lr * N * 2 + n0 * 2 + byte);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_h, (lds_ptr)G::pos(ring, u0), 16, voff,
-                                                     0, 0, 0);
-        }
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        __syncthreads();
-        // staged row starts of the wave's 32 x 32 blocks, once per block
-        lds8* hrow[TM][TN];
+            for (int jj = 0; jj < IPW; ++jj) {
+                const int u0 = (wave * IPW + jj) * 64;
+                int lr, byte;
+                G::source(u0 + lane, lr, byte);
+                const uint32_t voff = (uint32_t)(lr * N * 2 + n0 * 2 + byte);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_h, (lds_ptr)G::pos(ring, u0), 16, voff,
+                                                         0, 0, 0);
+            }
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            __syncthreads();
+            // staged row starts of the wave's 32 x 32 blocks, once per block
+            lds8* hrow[TM][TN];
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    hrow[i][j] = G::row(ring, (wn * WN + 32 * j) / 8 / G::NC, wm * WM + 32 * i);
+            auto scale_by_dgelu = [&](auto erf) __attribute__((always_inline)) {
+                constexpr bool ERF = decltype(erf)::value;
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j) {
+                        // one 32 x 32 block at a time: without bounds branches the
+                        // scheduler would otherwise load every h value up front and
+                        // spill
+                        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int lr = row_w + 32 * i;
+                            const int lc = col_w + 32 * j + 8 * q;
+                            const u32x2 hw = lds_ld<u32x2>(
+                                G::in_row(hrow[i][j], fr, (wn * WN + 32 * j + 8 * q) / 8 % G::NC) +
+                                8 * fh);
+                            const bool ok = in_rows(lr) && in_cols(lc);
+                            const float hv[4] = {bf16_lo(hw.x), bf16_hi(hw.x), bf16_lo(hw.y),
+                                                 bf16_hi(hw.y)};
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const float gp = act_grad_f<ERF>(hv[e]);
+                                float v = ok ? acc[j][i][4 * q + e] * alpha * gp : 0.0f;
+                                // the product is formed here: the compiler would
+                                // otherwise sink it to its uses past the barrier and
+                                // keep (spill) both factors
+                                asm volatile("" : "+v"(v));
+                                acc[j][i][4 * q + e] = v;
+                            }
+                        }
+                    }
+            };
+            if constexpr (ACT != 0) {
+                scale_by_dgelu(std::integral_constant<bool, ACT == 2>{});
+            } else {
+                if (p.gelu_erf) scale_by_dgelu(std::true_type{});
+                else scale_by_dgelu(std::false_type{});
+            }
+            __syncthreads();   // h is consumed: the ring takes the codes next
+        } else {
+            // alpha (and the bias) in place; values outside the product become 0
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-                hrow[i][j] = G::row(ring, (wn * WN + 32 * j) / 8 / G::NC, wm * WM + 32 * i);
-        auto scale_by_dgelu = [&](auto erf) __attribute__((always_inline)) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int cn = col_w + 32 * j + 8 * q;
+                    float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                    if constexpr (EPI == kEpiBf16Bias || EPI == kEpiGeluFp8 || EPI == kEpiGeluBf16) {
+                        if (p.bias && in_cols(cn)) {
+                            const uint2 bw = *reinterpret_cast<const uint2*>(p.bias + n0 + cn);
+                            bv[0] = bf16_lo(bw.x); bv[1] = bf16_hi(bw.x);
+                            bv[2] = bf16_lo(bw.y); bv[3] = bf16_hi(bw.y);
+                        }
+                    }
+#pragma unroll
+                    for (int i = 0; i < TM; ++i) {
+                        const bool ok = in_rows(row_w + 32 * i) && in_cols(cn);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float x = acc[j][i][4 * q + e];
+                            if constexpr (EPI == kEpiBf16Bias || EPI == kEpiGeluFp8 ||
+                                          EPI == kEpiGeluBf16)
+                                acc[j][i][4 * q + e] = ok ? fmaf(x, alpha, bv[e]) : 0.0f;
+                            else
+                                acc[j][i][4 * q + e] = ok ? x * alpha : 0.0f;
+                        }
+                    }
+                }
+        }
+
+        if constexpr (EPI == kEpiDGeluF32 || EPI == kEpiDGeluBf16) {
+            // gelu'(h) from global memory, one 8-byte read per four values (here the
+            // per-value choice of the form measured faster than two loop copies)
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int64_t gm = m0 + row_w + 32 * i;
+                        const int64_t gn = n0 + col_w + 32 * j + 8 * q;
+                        if (in_rows(row_w + 32 * i) && in_cols(col_w + 32 * j + 8 * q)) {
+                            const uint2 hw = *reinterpret_cast<const uint2*>(p.h_in + gm * N + gn);
+                            const float hv[4] = {bf16_lo(hw.x), bf16_hi(hw.x), bf16_lo(hw.y),
+                                                 bf16_hi(hw.y)};
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                acc[j][i][4 * q + e] *= p.gelu_erf ? gelu_erf_grad_f(hv[e])
+                                                                   : gelu_grad_f(hv[e]);
+                        }
+                    }
+        }
+
+        if constexpr (EPI == kEpiF32 || EPI == kEpiDGeluF32) {
+            // fp32 rows; a 256 x 256 tile goes out in two passes of 128 rows
+            constexpr int P4 = staging_parts(BN * 4, STAGE);
+            constexpr int CAP = NS * (STAGE / (BN * 4 / P4)) / P4;   // tile rows one pass holds
+            constexpr int PASSES = (BM + CAP - 1) / CAP;
+            constexpr int RPP = BM / PASSES;
+            using G = Staging<BN * 4, RPP, STAGE>;
+            static_assert(RPP * PASSES == BM && RPP % WM == 0 && RPP * G::P <= NS * G::RPS,
+                          "f32 staging");
+#pragma unroll
+            for (int ps = 0; ps < PASSES; ++ps) {
+                if (wm * WM >= ps * RPP && wm * WM < (ps + 1) * RPP) {
+                    lds8* frow[TM][TN];
+#pragma unroll
+                    for (int i = 0; i < TM; ++i)
+#pragma unroll
+                        for (int j = 0; j < TN; ++j)
+                            frow[i][j] = G::row(ring, (wn * WN + 32 * j) / 4 / G::NC,
+                                                wm * WM + 32 * i - ps * RPP);
+#pragma unroll
+                    for (int i = 0; i < TM; ++i)
+#pragma unroll
+                        for (int j = 0; j < TN; ++j)
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                lds_st(G::in_row(frow[i][j], fr,
+                                                 (wn * WN + 32 * j + 8 * q) / 4 % G::NC + fh),
+                                       f32x4{acc[j][i][4 * q], acc[j][i][4 * q + 1],
+                                             acc[j][i][4 * q + 2], acc[j][i][4 * q + 3]});
+                            }
+                }
+                __syncthreads();
+                G::template copy_out<NT, !FULL>(ring, t, (uint8_t*)p.out + ((m0 + ps * RPP) * N + n0) * 4,
+                                             N * 4, M - m0 - ps * RPP, (N - n0) * 4);
+                __syncthreads();
+            }
+        }
+
+        // bf16 rows of the tile through the ring
+        auto bf16_out = [&](uint16_t* dst) {
+            using G = Staging<BN * 2, BM, STAGE>;
+            static_assert(BM * G::P <= NS * G::RPS, "bf16 staging");
+            lds8* brow[TM][TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    brow[i][j] = G::row(ring, (wn * WN + 32 * j) / 8 / G::NC, wm * WM + 32 * i);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        lds_st(G::in_row(brow[i][j], fr, (wn * WN + 32 * j + 8 * q) / 8 % G::NC) +
+                                   8 * fh,
+                               u32x2{pack_bf16x2(acc[j][i][4 * q], acc[j][i][4 * q + 1]),
+                                     pack_bf16x2(acc[j][i][4 * q + 2], acc[j][i][4 * q + 3])});
+                    }
+            __syncthreads();
+            G::template copy_out<NT, !FULL>(ring, t, (uint8_t*)(dst + m0 * N + n0), N * 2, M - m0,
+                                        (N - n0) * 2);
+            __syncthreads();
+        };
+        if constexpr (EPI == kEpiBf16Bias || EPI == kEpiGeluFp8 || EPI == kEpiGeluBf16) {
+            uint16_t* hdst = EPI == kEpiBf16Bias ? (uint16_t*)p.out : p.h_out;
+            if (hdst) bf16_out(hdst);
+        }
+        if constexpr (EPI == kEpiDGeluBf16) bf16_out((uint16_t*)p.out);
+        // gelu in place on every accumulator (values outside the product are 0, and
+        // gelu(0) = 0)
+        auto apply_gelu = [&](auto erf) __attribute__((always_inline)) {
             constexpr bool ERF = decltype(erf)::value;
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[j][i][r] = act_f<ERF>(acc[j][i][r]);
+        };
+        if constexpr (EPI == kEpiGeluBf16 || EPI == kEpiGeluFp8) {
+            if constexpr (ACT != 0) {
+                apply_gelu(std::integral_constant<bool, ACT == 2>{});
+            } else {
+                if (p.gelu_erf) apply_gelu(std::true_type{});
+                else apply_gelu(std::false_type{});
+            }
+        }
+        if constexpr (EPI == kEpiGeluBf16) bf16_out((uint16_t*)p.out);
+
+        if constexpr (EPI == kEpiGeluFp8 || EPI == kEpiDGeluFp8) {
+            // FP8 codes: first the row-major tile goes through the ring, then the
+            // transposed one (rows = output columns).  For the transposed copy the
+            // four lanes of a quad swap bytes so that each holds one column of four
+            // consecutive rows, written as one word.
+            using Q = Staging<BN, BM, STAGE>;
+            using QT = Staging<BM, BN, STAGE>;
+            static_assert(BM * Q::P <= NS * Q::RPS && BN * QT::P <= NS * QT::RPS, "code staging");
+            static_assert(QT::P == 1, "transposed code rows are never cut");
+            lds8* qrow[TM][TN];
+            lds8* qtrow[TN];
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+                    qrow[i][j] = Q::row(ring, (wn * WN + 32 * j) / 16 / Q::NC, wm * WM + 32 * i);
+                qtrow[j] = QT::row(ring, 0, wn * WN + 32 * j);
+            }
+            const float qs = *p.q_scale;
+            uint32_t amax_bits = 0;
+            uint32_t codes[TM][TN][4];
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -503,290 +727,97 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int vb) {
                     for (int q = 0; q < 4; ++q) {
                         const int lr = row_w + 32 * i;
                         const int lc = col_w + 32 * j + 8 * q;
-                        const u32x2 hw = lds_ld<u32x2>(
-                            G::in_row(hrow[i][j], fr, (wn * WN + 32 * j + 8 * q) / 8 % G::NC) +
-                            8 * fh);
-                        const bool ok = lr < rows_in && lc < cols_in;
-                        const float hv[4] = {bf16_lo(hw.x), bf16_hi(hw.x), bf16_lo(hw.y),
-                                             bf16_hi(hw.y)};
+                        float gs[4];
+                        uint32_t cm = 0;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            const float gp = act_grad_f<ERF>(hv[e]);
-                            acc[j][i][4 * q + e] = ok ? acc[j][i][4 * q + e] * alpha * gp : 0.0f;
+                            float g;
+                            if constexpr (EPI == kEpiGeluFp8) {
+                                g = acc[j][i][4 * q + e];   // gelu(h), applied above
+                                gs[e] = g * qs;
+                            } else {
+                                g = acc[j][i][4 * q + e];
+                                gs[e] = mul_round_odd(g, qs);
+                            }
+                            const uint32_t ab = abs_bits(g);
+                            cm = cm > ab ? cm : ab;
                         }
+                        uint32_t code = encode4<QF>(gs[0], gs[1], gs[2], gs[3]);
+                        if (__builtin_expect(cm > kInfBits, 0)) code = patch_nan4(code, gs);
+                        if constexpr (EPI == kEpiGeluFp8) {
+                            // rows and columns outside the product carry gelu(0) = 0
+                            if (!(in_rows(lr) && in_cols(lc))) cm = 0;
+                        }
+                        amax_bits = amax_bits > cm ? amax_bits : cm;
+                        codes[i][j][q] = code;
+                        lds_st(Q::in_row(qrow[i][j], fr, (wn * WN + 32 * j + 8 * q) / 16 % Q::NC) +
+                                   4 * ((lc / 4) % 4),
+                               code);
                     }
-        };
-        if constexpr (ACT != 0) {
-            scale_by_dgelu(std::integral_constant<bool, ACT == 2>{});
-        } else {
-            if (p.gelu_erf) scale_by_dgelu(std::true_type{});
-            else scale_by_dgelu(std::false_type{});
-        }
-        __syncthreads();   // h is consumed: the ring takes the codes next
-    } else {
-        // alpha (and the bias) in place; values outside the product become 0
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int cn = col_w + 32 * j + 8 * q;
-                float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-                if constexpr (EPI == kEpiBf16Bias || EPI == kEpiGeluFp8 || EPI == kEpiGeluBf16) {
-                    if (p.bias && cn < cols_in) {
-                        const uint2 bw = *reinterpret_cast<const uint2*>(p.bias + n0 + cn);
-                        bv[0] = bf16_lo(bw.x); bv[1] = bf16_hi(bw.x);
-                        bv[2] = bf16_lo(bw.y); bv[3] = bf16_hi(bw.y);
-                    }
-                }
-#pragma unroll
-                for (int i = 0; i < TM; ++i) {
-                    const bool ok = row_w + 32 * i < rows_in && cn < cols_in;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float x = acc[j][i][4 * q + e];
-                        if constexpr (EPI == kEpiBf16Bias || EPI == kEpiGeluFp8 ||
-                                      EPI == kEpiGeluBf16)
-                            acc[j][i][4 * q + e] = ok ? fmaf(x, alpha, bv[e]) : 0.0f;
-                        else
-                            acc[j][i][4 * q + e] = ok ? x * alpha : 0.0f;
-                    }
-                }
-            }
-    }
-
-    if constexpr (EPI == kEpiDGeluF32 || EPI == kEpiDGeluBf16) {
-        // gelu'(h) from global memory, one 8-byte read per four values (here the
-        // per-value choice of the form measured faster than two loop copies)
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int64_t gm = m0 + row_w + 32 * i;
-                    const int64_t gn = n0 + col_w + 32 * j + 8 * q;
-                    if (gm < M && gn < N) {
-                        const uint2 hw = *reinterpret_cast<const uint2*>(p.h_in + gm * N + gn);
-                        const float hv[4] = {bf16_lo(hw.x), bf16_hi(hw.x), bf16_lo(hw.y),
-                                             bf16_hi(hw.y)};
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            acc[j][i][4 * q + e] *= p.gelu_erf ? gelu_erf_grad_f(hv[e])
-                                                               : gelu_grad_f(hv[e]);
-                    }
-                }
-    }
-
-    if constexpr (EPI == kEpiF32 || EPI == kEpiDGeluF32) {
-        // fp32 rows; a 256 x 256 tile goes out in two passes of 128 rows
-        constexpr int P4 = staging_parts(BN * 4, STAGE);
-        constexpr int CAP = NS * (STAGE / (BN * 4 / P4)) / P4;   // tile rows one pass holds
-        constexpr int PASSES = (BM + CAP - 1) / CAP;
-        constexpr int RPP = BM / PASSES;
-        using G = Staging<BN * 4, RPP, STAGE>;
-        static_assert(RPP * PASSES == BM && RPP % WM == 0 && RPP * G::P <= NS * G::RPS,
-                      "f32 staging");
-#pragma unroll
-        for (int ps = 0; ps < PASSES; ++ps) {
-            if (wm * WM >= ps * RPP && wm * WM < (ps + 1) * RPP) {
-                lds8* frow[TM][TN];
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-#pragma unroll
-                    for (int j = 0; j < TN; ++j)
-                        frow[i][j] = G::row(ring, (wn * WN + 32 * j) / 4 / G::NC,
-                                            wm * WM + 32 * i - ps * RPP);
+            __syncthreads();
+            Q::template copy_out<NT, !FULL>(ring, t, p.q_out + m0 * N + n0, N, M - m0, N - n0);
+            if (p.q_out_t) {
+                __syncthreads();
+                const bool odd = fr & 1, hi2 = fr & 2;
 #pragma unroll
                 for (int i = 0; i < TM; ++i)
 #pragma unroll
                     for (int j = 0; j < TN; ++j)
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
-                            lds_st(G::in_row(frow[i][j], fr,
-                                             (wn * WN + 32 * j + 8 * q) / 4 % G::NC + fh),
-                                   f32x4{acc[j][i][4 * q], acc[j][i][4 * q + 1],
-                                         acc[j][i][4 * q + 2], acc[j][i][4 * q + 3]});
+                            const uint32_t code = codes[i][j][q];
+                            const uint32_t o2 = (uint32_t)__builtin_amdgcn_mov_dpp(
+                                (int)code, kDppQuadSwap2, 0xF, 0xF, false);
+                            const uint32_t c2 = hi2 ? __builtin_amdgcn_perm(o2, code, 0x03020706u)
+                                                    : __builtin_amdgcn_perm(o2, code, 0x05040100u);
+                            const uint32_t o1 = (uint32_t)__builtin_amdgcn_mov_dpp(
+                                (int)c2, kDppQuadSwap1, 0xF, 0xF, false);
+                            const uint32_t ct = odd ? __builtin_amdgcn_perm(o1, c2, 0x03070105u)
+                                                    : __builtin_amdgcn_perm(o1, c2, 0x06020400u);
+                            const int tm = (row_w + 32 * i) & ~3;              // first of four rows
+                            lds_st(QT::in_row(qtrow[j], 8 * q + 4 * fh + (fr & 3),
+                                              (wm * WM + 32 * i) / 16 + (fr >> 4)) +
+                                       4 * ((tm / 4) % 4),
+                                   ct);
                         }
+                __syncthreads();
+                QT::template copy_out<NT, !FULL>(ring, t, p.q_out_t + n0 * M + m0, M, N - n0, M - m0);
             }
-            __syncthreads();
-            G::template copy_out<NT>(ring, t, (uint8_t*)p.out + ((m0 + ps * RPP) * N + n0) * 4,
-                                         N * 4, M - m0 - ps * RPP, (N - n0) * 4);
-            __syncthreads();
-        }
-    }
-
-    // bf16 rows of the tile through the ring
-    auto bf16_out = [&](uint16_t* dst) {
-        using G = Staging<BN * 2, BM, STAGE>;
-        static_assert(BM * G::P <= NS * G::RPS, "bf16 staging");
-        lds8* brow[TM][TN];
+            if constexpr (EPI == kEpiDGeluFp8) {
+                if (p.col_partial) {
+                    // column sums of the tile in a fixed order: over i in a lane, a
+                    // butterfly over the 32 lanes of equal lane / 32, then over wm
+                    constexpr int NV = 16 * TN;   // columns per lane
+                    float v[NV];
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+                    for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
-                brow[i][j] = G::row(ring, (wn * WN + 32 * j) / 8 / G::NC, wm * WM + 32 * i);
+                        for (int r = 0; r < 16; ++r) {
+                            float a = 0.0f;
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    lds_st(G::in_row(brow[i][j], fr, (wn * WN + 32 * j + 8 * q) / 8 % G::NC) +
-                               8 * fh,
-                           u32x2{pack_bf16x2(acc[j][i][4 * q], acc[j][i][4 * q + 1]),
-                                 pack_bf16x2(acc[j][i][4 * q + 2], acc[j][i][4 * q + 3])});
-                }
-        __syncthreads();
-        G::template copy_out<NT>(ring, t, (uint8_t*)(dst + m0 * N + n0), N * 2, M - m0,
-                                    (N - n0) * 2);
-        __syncthreads();
-    };
-    if constexpr (EPI == kEpiBf16Bias || EPI == kEpiGeluFp8 || EPI == kEpiGeluBf16) {
-        uint16_t* hdst = EPI == kEpiBf16Bias ? (uint16_t*)p.out : p.h_out;
-        if (hdst) bf16_out(hdst);
-    }
-    if constexpr (EPI == kEpiDGeluBf16) bf16_out((uint16_t*)p.out);
-    // gelu in place on every accumulator (values outside the product are 0, and
-    // gelu(0) = 0)
-    auto apply_gelu = [&](auto erf) __attribute__((always_inline)) {
-        constexpr bool ERF = decltype(erf)::value;
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[j][i][r] = act_f<ERF>(acc[j][i][r]);
-    };
-    if constexpr (EPI == kEpiGeluBf16 || EPI == kEpiGeluFp8) {
-        if constexpr (ACT != 0) {
-            apply_gelu(std::integral_constant<bool, ACT == 2>{});
-        } else {
-            if (p.gelu_erf) apply_gelu(std::true_type{});
-            else apply_gelu(std::false_type{});
-        }
-    }
-    if constexpr (EPI == kEpiGeluBf16) bf16_out((uint16_t*)p.out);
-
-    if constexpr (EPI == kEpiGeluFp8 || EPI == kEpiDGeluFp8) {
-        // FP8 codes: first the row-major tile goes through the ring, then the
-        // transposed one (rows = output columns).  For the transposed copy the
-        // four lanes of a quad swap bytes so that each holds one column of four
-        // consecutive rows, written as one word.
-        using Q = Staging<BN, BM, STAGE>;
-        using QT = Staging<BM, BN, STAGE>;
-        static_assert(BM * Q::P <= NS * Q::RPS && BN * QT::P <= NS * QT::RPS, "code staging");
-        static_assert(QT::P == 1, "transposed code rows are never cut");
-        lds8* qrow[TM][TN];
-        lds8* qtrow[TN];
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-                qrow[i][j] = Q::row(ring, (wn * WN + 32 * j) / 16 / Q::NC, wm * WM + 32 * i);
-            qtrow[j] = QT::row(ring, 0, wn * WN + 32 * j);
-        }
-        const float qs = *p.q_scale;
-        uint32_t amax_bits = 0;
-        uint32_t codes[TM][TN][4];
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int lr = row_w + 32 * i;
-                    const int lc = col_w + 32 * j + 8 * q;
-                    float gs[4];
-                    uint32_t cm = 0;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        float g;
-                        if constexpr (EPI == kEpiGeluFp8) {
-                            g = acc[j][i][4 * q + e];   // gelu(h), applied above
-                            gs[e] = g * qs;
-                        } else {
-                            g = acc[j][i][4 * q + e];
-                            gs[e] = mul_round_odd(g, qs);
+                            for (int i = 0; i < TM; ++i) a += acc[j][i][r];
+                            v[16 * j + r] = a;
                         }
-                        const uint32_t ab = abs_bits(g);
-                        cm = cm > ab ? cm : ab;
+                    butterfly_sum<NV>(v, fr);
+#pragma unroll
+                    for (int k = 0; k < NV / 32; ++k) {
+                        const int c = fr * (NV / 32) + k;   // = 16 j + 4 q + e
+                        const int j = c / 16, q = (c / 4) % 4, e = c % 4;
+                        colp[wm][col_w + 32 * j + 8 * q + e] = v[k];
                     }
-                    uint32_t code = encode4<QF>(gs[0], gs[1], gs[2], gs[3]);
-                    if (__builtin_expect(cm > kInfBits, 0)) code = patch_nan4(code, gs);
-                    if constexpr (EPI == kEpiGeluFp8) {
-                        // rows and columns outside the product carry gelu(0) = 0
-                        if (!(lr < rows_in && lc < cols_in)) cm = 0;
-                    }
-                    amax_bits = amax_bits > cm ? amax_bits : cm;
-                    codes[i][j][q] = code;
-                    lds_st(Q::in_row(qrow[i][j], fr, (wn * WN + 32 * j + 8 * q) / 16 % Q::NC) +
-                               4 * ((lc / 4) % 4),
-                           code);
-                }
-        __syncthreads();
-        Q::template copy_out<NT>(ring, t, p.q_out + m0 * N + n0, N, M - m0, N - n0);
-        if (p.q_out_t) {
-            __syncthreads();
-            const bool odd = fr & 1, hi2 = fr & 2;
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const uint32_t code = codes[i][j][q];
-                        const uint32_t o2 = (uint32_t)__builtin_amdgcn_mov_dpp(
-                            (int)code, kDppQuadSwap2, 0xF, 0xF, false);
-                        const uint32_t c2 = hi2 ? __builtin_amdgcn_perm(o2, code, 0x03020706u)
-                                                : __builtin_amdgcn_perm(o2, code, 0x05040100u);
-                        const uint32_t o1 = (uint32_t)__builtin_amdgcn_mov_dpp(
-                            (int)c2, kDppQuadSwap1, 0xF, 0xF, false);
-                        const uint32_t ct = odd ? __builtin_amdgcn_perm(o1, c2, 0x03070105u)
-                                                : __builtin_amdgcn_perm(o1, c2, 0x06020400u);
-                        const int tm = (row_w + 32 * i) & ~3;              // first of four rows
-                        lds_st(QT::in_row(qtrow[j], 8 * q + 4 * fh + (fr & 3),
-                                          (wm * WM + 32 * i) / 16 + (fr >> 4)) +
-                                   4 * ((tm / 4) % 4),
-                               ct);
-                    }
-            __syncthreads();
-            QT::template copy_out<NT>(ring, t, p.q_out_t + n0 * M + m0, M, N - n0, M - m0);
-        }
-        if constexpr (EPI == kEpiDGeluFp8) {
-            if (p.col_partial) {
-                // column sums of the tile in a fixed order: over i in a lane, a
-                // butterfly over the 32 lanes of equal lane / 32, then over wm
-                constexpr int NV = 16 * TN;   // columns per lane
-                float v[NV];
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
+                    __syncthreads();
+                    if (t < BN && in_cols(t)) {
                         float a = 0.0f;
 #pragma unroll
-                        for (int i = 0; i < TM; ++i) a += acc[j][i][r];
-                        v[16 * j + r] = a;
+                        for (int w = 0; w < WGM; ++w) a += colp[w][t];
+                        p.col_partial[(int64_t)tile_m * N + n0 + t] = a;
                     }
-                butterfly_sum<NV>(v, fr);
-                __shared__ float colp[WGM][BN];
-#pragma unroll
-                for (int k = 0; k < NV / 32; ++k) {
-                    const int c = fr * (NV / 32) + k;   // = 16 j + 4 q + e
-                    const int j = c / 16, q = (c / 4) % 4, e = c % 4;
-                    colp[wm][col_w + 32 * j + 8 * q + e] = v[k];
-                }
-                __syncthreads();
-                if (t < BN && n0 + t < N) {
-                    float a = 0.0f;
-#pragma unroll
-                    for (int w = 0; w < WGM; ++w) a += colp[w][t];
-                    p.col_partial[(int64_t)tile_m * N + n0 + t] = a;
                 }
             }
+            block_amax_atomic<false>(amax_bits, p.q_amax, red);
         }
-        __shared__ uint32_t red[NW];
-        block_amax_atomic<false>(amax_bits, p.q_amax, red);
-    }
+    };
+    epilogue(std::integral_constant<bool, FULLX>{});
 }
 
 // 256 x 256 tiles, eight waves of 64 x 128 (two waves per SIMD), one workgroup
@@ -883,6 +914,16 @@ hipError_t launch_typed(const GemmParams& p, hipStream_t stream) {
                                stream, p);
             break;
         case kTile128x256:
+            // the FP8-output epilogues (the longest) without bounds tests where
+            // every tile is whole
+            if constexpr (EPI % 16 == kEpiGeluFp8 || EPI % 16 == kEpiDGeluFp8) {
+                if (p.M % 128 == 0 && p.N % 256 == 0) {
+                    hipLaunchKernelGGL((gemm_kernel_128x256<FA, FB, EPI + 64, QF>),
+                                       dim3((unsigned)(p.M / 128 * (p.N / 256))), dim3(256), 0,
+                                       stream, p);
+                    break;
+                }
+            }
             hipLaunchKernelGGL((gemm_kernel_128x256<FA, FB, EPI, QF>),
                                dim3((unsigned)(cdiv(p.M, 128) * cdiv(p.N, 256))), dim3(256), 0,
                                stream, p);
