@@ -31,6 +31,8 @@ GELU_ERF = 1
 META_FORWARD = 0
 META_BACKWARD = 1
 
+STEP_WS_BYTES = 64   # FP8LN_STEP_WS_BYTES
+
 OP_CAST_AMAX = 0
 OP_LAYERNORM_BWD = 1
 OP_LN_LINEAR_BWD = 2
@@ -114,6 +116,8 @@ SIGNATURES = {
                                    _MP, _MP, _P, _P, _P, _P, _SZ, _P]),
     "fp8ln_ln_linear_fwd": (C.c_int, [_RP, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _MP,
                                       C.POINTER(LinearCtxStruct), _P]),
+    "fp8ln_ln_linear_fwd_step": (C.c_int, [_RP, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P,
+                                           _MP, C.POINTER(LinearCtxStruct), _P, _P]),
     "fp8ln_ln_linear_bwd": (C.c_int, [_RP, _I64, _I64, _I64, _I32, _P, _P, _P,
                                       C.POINTER(LinearCtxStruct), _MP, _MP, _P, _P, _P, _P, _P,
                                       _P, _SZ, _P]),

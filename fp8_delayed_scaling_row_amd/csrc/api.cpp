@@ -1118,11 +1118,13 @@ int fp8ln_linear_bwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_feat
     return FP8LN_OK;
 }
 
-int fp8ln_ln_linear_fwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_features,
-                        int64_t out_features, int32_t params_dtype, const void* x,
-                        const void* gamma, const void* beta, const void* weight,
-                        const void* bias, void* out, const fp8ln_meta* fwd,
-                        const fp8ln_linear_ctx* ctx, void* stream) {
+// LayerNormLinear forward; with step_ws, the step-start scaling update of the
+// forward state comes first (folded into the prologue launch when it runs).
+static int ln_linear_fwd_impl(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_features,
+                              int64_t out_features, int32_t params_dtype, const void* x,
+                              const void* gamma, const void* beta, const void* weight,
+                              const void* bias, void* out, const fp8ln_meta* fwd,
+                              const fp8ln_linear_ctx* ctx, void* step_ws, void* stream) {
     int s = check_recipe(recipe);
     if (s) return s;
     const int64_t M = tokens, K = in_features, N = out_features;
@@ -1137,7 +1139,7 @@ int fp8ln_ln_linear_fwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_f
                     (long long)N);
     if ((s = check_meta(fwd, 2, FP8LN_META_FORWARD, "forward"))) return s;
     REQUIRE_PTR(ctx);
-    REQUIRE(ctx->ln_q && ctx->w_q, "ctx.ln_q and ctx.w_q are required");
+    REQUIRE((M == 0 || ctx->ln_q) && ctx->w_q, "ctx.ln_q and ctx.w_q are required");
     if (ctx->ln_qt && M % 16 != 0)
         return fail(FP8LN_ERR_UNSUPPORTED, "ctx.ln_qt needs tokens %% 16 == 0");
     REQUIRE(!ctx->reuse_weight_codes || ctx->w_scale_inv,
@@ -1155,6 +1157,7 @@ int fp8ln_ln_linear_fwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_f
     }
     if (ctx->ln_qt) CHECK(check_transpose_rows(M, "ln_linear_fwd"));
     CHECK(check_gemm_size(M, N, K, 1, false, "ln_linear_fwd"));
+    if (step_ws) REQUIRE_ALIGNED(step_ws);
     if ((s = check_current_device())) return s;
     hipStream_t st = as_stream(stream);
     const int f = meta_fp8(recipe, FP8LN_META_FORWARD);
@@ -1162,15 +1165,23 @@ int fp8ln_ln_linear_fwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_f
     // FP8 weight storage: reuse the codes (and their scale_inv) of an earlier
     // forward of this ctx, or cast now and record the scale_inv that goes with them
     const float* w_sinv = ctx->w_scale_inv ? ctx->w_scale_inv : fwd->scale_inv + 1;
+    FusedUpdate upd{hist, fwd->scale, fwd->scale_inv, recipe->amax_history_len, fwd->n_slots,
+                    recipe->margin, fp8_max_of(f), (uint32_t*)step_ws, 0, {1, 0}};
     bool fused = false;   // LayerNorm rows and weight cast in one launch (small shapes)
-    if (M > 0 && !ctx->reuse_weight_codes) {
+    if (M > 0) {
         const CastJob wj{weight, N, K, fwd->scale + 1, hist + 1, ctx->w_q, ctx->w_qt,
                          fwd->scale_inv + 1, ctx->w_scale_inv};
         FP8LN_TRY(launch_fwd_prologue(M, (int)K, x, gamma, beta, recipe->ln_eps, f,
                                       fwd->scale + 0, hist + 0, ctx->ln_q, ctx->mean, ctx->rstd,
-                                      &wj, 1, &fused, st),
+                                      &wj, ctx->reuse_weight_codes ? 0 : 1, &fused, st,
+                                      step_ws ? &upd : nullptr),
                   "forward prologue launch");
     }
+    if (step_ws && !fused)   // the update as its own launch, before anything reads a scale
+        FP8LN_TRY(launch_scaling_update(hist, fwd->scale, fwd->scale_inv,
+                                        recipe->amax_history_len, fwd->n_slots, recipe->margin,
+                                        fp8_max_of(f), st),
+                  "scaling_update launch");
     if (M > 0) {
         if (!fused)
             FP8LN_TRY(launch_ln_cast_amax(M, (int)K, x, gamma, beta, recipe->ln_eps, f,
@@ -1188,8 +1199,33 @@ int fp8ln_ln_linear_fwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_f
                                kEpiBf16Bias);
     p.bias = (const uint16_t*)bias;
     p.out = out;
+    if (step_ws && fused) {   // the folded update's roll, by the GEMM's first workgroup
+        p.roll_hist = hist;
+        p.roll_ws = (uint32_t*)step_ws;
+        p.roll_len = recipe->amax_history_len;
+        p.roll_slots = fwd->n_slots;
+    }
     FP8LN_TRY(launch_gemm(p, st), "gemm launch");
     return FP8LN_OK;
+}
+
+int fp8ln_ln_linear_fwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_features,
+                        int64_t out_features, int32_t params_dtype, const void* x,
+                        const void* gamma, const void* beta, const void* weight,
+                        const void* bias, void* out, const fp8ln_meta* fwd,
+                        const fp8ln_linear_ctx* ctx, void* stream) {
+    return ln_linear_fwd_impl(recipe, tokens, in_features, out_features, params_dtype, x, gamma,
+                              beta, weight, bias, out, fwd, ctx, nullptr, stream);
+}
+
+int fp8ln_ln_linear_fwd_step(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_features,
+                             int64_t out_features, int32_t params_dtype, const void* x,
+                             const void* gamma, const void* beta, const void* weight,
+                             const void* bias, void* out, const fp8ln_meta* fwd,
+                             const fp8ln_linear_ctx* ctx, void* step_ws, void* stream) {
+    REQUIRE_PTR(step_ws);
+    return ln_linear_fwd_impl(recipe, tokens, in_features, out_features, params_dtype, x, gamma,
+                              beta, weight, bias, out, fwd, ctx, step_ws, stream);
 }
 
 int fp8ln_ln_linear_bwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_features,

@@ -35,15 +35,16 @@ constexpr int kCPitch = kCT + 4;    // byte pitch of the cast kernel's transpose
 // per-tile latency of tensors with few tiles (a weight of a few MB leaves most
 // CUs idle, and each tile's arithmetic is then on the critical path).
 // Workgroup `vblock` of `vgrid` (the kernel's own grid, or a share of a larger
-// launch that also runs other jobs).
-template <bool IN_F32, int FMT, int NT>
+// launch that also runs other jobs).  `pre` runs once the first tile is in
+// flight and before *scale_ptr and *copy_src are read (all threads call it).
+// CHECK: as block_amax_atomic's.
+template <bool IN_F32, int FMT, int NT, bool CHECK = true, class Pre = NoPre>
 __device__ __forceinline__ void cast_tiles(
-    const void* __restrict__ in, int64_t rows, int64_t cols, const float* __restrict__ scale_ptr,
+    const void* __restrict__ in, int64_t rows, int64_t cols, const float* scale_ptr,
     float* __restrict__ amax_ptr, uint8_t* __restrict__ out, uint8_t* __restrict__ out_t,
-    float* __restrict__ partial, const float* __restrict__ copy_src, float* __restrict__ copy_dst,
-    int vblock, int vgrid) {
+    float* __restrict__ partial, const float* copy_src, float* __restrict__ copy_dst,
+    int vblock, int vgrid, Pre pre = {}) {
     __shared__ uint32_t tq[kCT * kCPitch / 4];
-    if (copy_dst && vblock == 0 && threadIdx.x == 0) *copy_dst = *copy_src;
     constexpr int BANDS = 512 / NT;     // 128-row tile = BANDS bands of NT / 4 rows
     constexpr int RPT = 4 * BANDS;      // rows per thread
     __shared__ float psum[NT / 16][kCT];
@@ -53,7 +54,6 @@ __device__ __forceinline__ void cast_tiles(
     const int p = t / 16;
     const int tiles_x = (int)((cols + kCT - 1) / kCT);
     const int tiles = tiles_x * (int)((rows + kCT - 1) / kCT);
-    const float s = *scale_ptr;
 
     typedef typename std::conditional<IN_F32, float4, uint4>::type Raw;
     constexpr int RPR = IN_F32 ? 2 : 1;   // 16-byte loads per row segment of 8 values
@@ -84,6 +84,9 @@ __device__ __forceinline__ void cast_tiles(
 
     uint32_t cm = 0;
     load_tile(vblock);
+    pre();
+    const float s = *scale_ptr;
+    if (copy_dst && vblock == 0 && threadIdx.x == 0) *copy_dst = *copy_src;
     for (int tile = vblock; tile < tiles; tile += vgrid) {
         const int64_t r0 = (int64_t)(tile / tiles_x) * kCT;
         const int64_t c0 = (int64_t)(tile % tiles_x) * kCT + 8 * j;
@@ -174,7 +177,7 @@ __device__ __forceinline__ void cast_tiles(
         }
         __syncthreads();   // tq and psum are rewritten by the next tile
     }
-    block_amax_atomic(cm, amax_ptr, red);
+    block_amax_atomic<CHECK>(cm, amax_ptr, red);
 }
 
 }  // namespace fp8ln

@@ -117,6 +117,21 @@ __device__ __forceinline__ float mul_round_odd(float v, float s) {
     return __uint_as_float(inexact ? ((b + down) | 1u) : b);
 }
 
+// The delayed scale from a history window: fp8_max / max / 2^margin as one
+// binary32 division and an exact power-of-two step; the old scale stays when the
+// window holds a NaN, its max is zero or not finite, or the result is not a
+// finite positive number.
+__device__ __forceinline__ float delayed_scale(float window_max, bool any_nan, float old_scale,
+                                               float fp8_max, int margin) {
+    float sc = old_scale;
+    if (!any_nan && window_max > 0.0f && window_max <= 3.402823466e38f) {
+        float ns = fp8_max / window_max;   // IEEE binary32 division
+        ns = ldexpf(ns, -margin);          // exact unless the result is subnormal
+        if (ns > 0.0f && ns <= 3.402823466e38f) sc = ns;
+    }
+    return sc;
+}
+
 // Replace the code of every NaN among v[0..3] by 0x7F.
 __device__ __forceinline__ uint32_t patch_nan4(uint32_t codes, const float* v) {
 #pragma unroll
@@ -129,6 +144,11 @@ __device__ __forceinline__ uint32_t patch_nan4(uint32_t codes, const float* v) {
 __device__ __forceinline__ uint32_t abs_bits(float x) { return __float_as_uint(x) & 0x7fffffffu; }
 
 constexpr uint32_t kInfBits = 0x7f800000u;
+
+// A body's hook that does nothing (see ln_cast_amax_rows, cast_tiles).
+struct NoPre {
+    __device__ void operator()() const {}
+};
 
 // ---- reductions ----------------------------------------------------------------
 
@@ -159,6 +179,18 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
     v += dpp_f32<kDppRowMirror>(v);
     v += __shfl_xor(v, 16, kWave);
     v += __shfl_xor(v, 32, kWave);
+    return v;
+}
+
+// Wave-wide max with fmaxf semantics (a NaN operand is dropped): DPP steps
+// inside each 16-lane row, then two shuffles across rows.
+__device__ __forceinline__ float wave_max_f32(float v) {
+    v = fmaxf(v, dpp_f32<kDppQuadSwap1>(v));
+    v = fmaxf(v, dpp_f32<kDppQuadSwap2>(v));
+    v = fmaxf(v, dpp_f32<kDppRowHalfMirror>(v));
+    v = fmaxf(v, dpp_f32<kDppRowMirror>(v));
+    v = fmaxf(v, __shfl_xor(v, 16, kWave));
+    v = fmaxf(v, __shfl_xor(v, 32, kWave));
     return v;
 }
 

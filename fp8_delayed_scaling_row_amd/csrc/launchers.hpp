@@ -50,11 +50,29 @@ struct CastJob {
     const float* copy_src;
     float* copy_dst;
 };
+// The step-start scaling update folded into the prologue (upd non-null): every
+// workgroup forms its own slot's scale from the history window (the update's
+// arithmetic), records its amax into ws instead of the history, and the last
+// workgroup to finish rolls the history with row 0 = the recorded amaxes (0 for
+// slots this launch does not cast) and writes every slot's scale and scale_inv.
+// ws: kStepWsWords words, zero on entry, zero again when the launch ends.
+constexpr int kStepWsWords = 16;
+constexpr int kMaxMetaSlots = 8;
+struct FusedUpdate {
+    float* hist;        // [len][n_slots]
+    float* scale;       // [n_slots]
+    float* scale_inv;   // [n_slots]
+    int len, n_slots, margin;
+    float fp8_max;
+    uint32_t* ws;       // [0, n_slots): amax bits per slot, [kStepWsWords - 1]: counter
+    int ln_slot;
+    int cast_slot[kMaxPrologueCasts];
+};
 hipError_t launch_fwd_prologue(int64_t rows, int hidden, const void* x, const void* gamma,
                                const void* beta, float eps, int fp8, const float* scale,
                                float* amax, uint8_t* out, float* mean, float* rstd,
                                const CastJob* casts, int n_casts, bool* launched,
-                               hipStream_t stream);
+                               hipStream_t stream, const FusedUpdate* upd = nullptr);
 
 // cast.hip
 size_t cast_workspace(int64_t rows, int64_t cols);
@@ -120,6 +138,13 @@ struct GemmParams {
     float* col_partial;     // kEpiDGeluFp8: [ceil(M / tile rows)][N] column sums, or null
     int gelu_erf;           // GELU epilogues: 0 = tanh form, 1 = erf form
     int epilogue;
+    // The step's history roll when the scaling update was folded into the
+    // forward (see FusedUpdate): workgroup 0 moves every row of roll_hist
+    // [roll_len][roll_slots] down by one, sets row 0 to the amax bits recorded in
+    // roll_ws and clears them.  Null roll_hist: no roll.
+    float* roll_hist;
+    uint32_t* roll_ws;
+    int roll_len, roll_slots;
 };
 
 // Rows of the col_partial array launch_gemm writes for an M-row product (its

@@ -35,13 +35,16 @@ namespace fp8ln {
 // CPL * 512, so every lane owns CPL whole chunks and no lane needs masking.
 // FMT kLnOutBf16 is the plain LayerNorm: y rounded to bf16, no scale, no amax.
 // NTHR threads per workgroup; workgroup `vblock` of `vgrid` (the kernel's own
-// grid, or a share of a larger launch that also runs other jobs).
-template <int CPL, int FMT, bool FULL, int NTHR>
+// grid, or a share of a larger launch that also runs other jobs).  `pre` runs
+// once the first row is in flight and before *scale_ptr is read (a launch that
+// forms the scale itself does so there, its loads overlapping the row's); all
+// threads call it.  CHECK: as block_amax_atomic's.
+template <int CPL, int FMT, bool FULL, int NTHR, bool CHECK = true, class Pre = NoPre>
 __device__ __forceinline__ void ln_cast_amax_rows(
     const uint4* __restrict__ x, const uint4* __restrict__ gamma, const uint4* __restrict__ beta,
-    int64_t rows, int hidden, float eps, const float* __restrict__ scale_ptr,
+    int64_t rows, int hidden, float eps, const float* scale_ptr,
     float* __restrict__ amax_ptr, void* __restrict__ out, float* __restrict__ mean_out,
-    float* __restrict__ rstd_out, int vblock, int vgrid) {
+    float* __restrict__ rstd_out, int vblock, int vgrid, Pre pre = {}) {
     constexpr int kWavesPerBlock = NTHR / kWave;
     __shared__ float4 gb[2][CPL * kWave][2];   // gamma, beta widened to fp32, 8 per chunk
     __shared__ uint32_t red[kWavesPerBlock];
@@ -50,7 +53,6 @@ __device__ __forceinline__ void ln_cast_amax_rows(
     const int nchunk = FULL ? CPL * kWave : hidden / 8;
     const float inv_h = 1.0f / (float)hidden;
     constexpr bool kBf16 = FMT == kLnOutBf16;
-    const float s = kBf16 ? 1.0f : *scale_ptr;
 
     const int64_t stride = (int64_t)vgrid * kWavesPerBlock;
     int64_t row = (int64_t)vblock * kWavesPerBlock + wave;
@@ -79,6 +81,8 @@ __device__ __forceinline__ void ln_cast_amax_rows(
         gb[1][c][1] = make_float4(b[4], b[5], b[6], b[7]);
     }
     __syncthreads();
+    pre();
+    const float s = kBf16 ? 1.0f : *scale_ptr;
 
     uint32_t amax_bits = 0;
     for (; row < rows; row += stride) {
@@ -160,7 +164,7 @@ __device__ __forceinline__ void ln_cast_amax_rows(
             if (rstd_out) rstd_out[row] = rs;
         }
     }
-    if constexpr (!kBf16) block_amax_atomic(amax_bits, amax_ptr, red);
+    if constexpr (!kBf16) block_amax_atomic<CHECK>(amax_bits, amax_ptr, red);
 }
 
 

@@ -35,26 +35,97 @@ struct ProloguePack {
     int n_casts;
     int cast_blocks[kMaxPrologueCasts];
     CastJob cast[kMaxPrologueCasts];
+    int fused;          // the scaling update is folded in (upd below)
+    FusedUpdate upd;
 };
+
+// The update's scales of every slot from the history window (fmaxf max, a NaN
+// flagged apart), as fp8ln's scaling update forms them: sh[2 q] = scale of slot
+// q, sh[2 q + 1] = 1 / scale.  Thread t reads entries t, t + 512, ... of the
+// flattened [len][n_slots] history; n_slots divides 512, so all of a thread's
+// entries belong to slot t % n_slots, and lanes of one slot meet in a butterfly
+// over the lane bits at and above n_slots.  Workgroup 0 also writes the scales
+// into the state block: every workgroup computes the same values, and a
+// workgroup that reads a slot's old scale after the write gets the same result
+// (the old scale enters only where it is kept), so the write needs no ordering.
+__device__ __forceinline__ void window_scales(const FusedUpdate& u, float* sh) {
+    __shared__ float wmax[kThreads / kWave][kMaxMetaSlots];
+    __shared__ int wnan[kThreads / kWave][kMaxMetaSlots];
+    const int n = u.n_slots, total = u.len * n;
+    float m = 0.0f;
+    int nan = 0;
+    for (int j = threadIdx.x; j < total; j += kThreads) {
+        const float v = u.hist[j];
+        m = fmaxf(m, v);
+        nan |= v != v;
+    }
+    for (int off = n; off < kWave; off <<= 1) {   // n is a power of two
+        m = fmaxf(m, __shfl_xor(m, off, kWave));
+        nan |= __shfl_xor(nan, off, kWave);
+    }
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    if (lane < n) {
+        wmax[wave][lane] = m;
+        wnan[wave][lane] = nan;
+    }
+    __syncthreads();
+    if (threadIdx.x < n) {
+        const int q = threadIdx.x;
+        float a = 0.0f;
+        int any = 0;
+        for (int w = 0; w < kThreads / kWave; ++w) {
+            a = fmaxf(a, wmax[w][q]);
+            any |= wnan[w][q];
+        }
+        const float sc = delayed_scale(a, any != 0, u.scale[q], u.fp8_max, u.margin);
+        sh[2 * q] = sc;
+        sh[2 * q + 1] = 1.0f / sc;
+        if (blockIdx.x == 0) {
+            u.scale[q] = sc;
+            u.scale_inv[q] = 1.0f / sc;
+        }
+    }
+    __syncthreads();
+}
 
 // Workgroups [0, ln_blocks) normalise rows; the following cast_blocks[0]
 // workgroups cast the first weight, then the second.
-template <int CPL, int FMT, bool FULL>
+template <int CPL, int FMT, bool FULL, bool FUSED>
 __global__ __launch_bounds__(kThreads) void fwd_prologue_kernel(ProloguePack p) {
+    // fused update: every slot's scale and 1 / scale, formed while the first
+    // rows are in flight (the amaxes go to ws; the forward's last GEMM rolls
+    // the history)
+    __shared__ float sh[2 * kMaxMetaSlots];
+    auto pre = [&]() { window_scales(p.upd, sh); };
     int b = blockIdx.x;
     if (b < p.ln_blocks) {
-        ln_cast_amax_rows<CPL, FMT, FULL, kThreads>(p.x, p.gamma, p.beta, p.rows, p.hidden, p.eps,
-                                                    p.scale, p.amax, p.out, p.mean, p.rstd, b,
-                                                    p.ln_blocks);
+        if constexpr (FUSED) {
+            const int q = p.upd.ln_slot;
+            ln_cast_amax_rows<CPL, FMT, FULL, kThreads, false>(
+                p.x, p.gamma, p.beta, p.rows, p.hidden, p.eps, sh + 2 * q,
+                reinterpret_cast<float*>(p.upd.ws + q), p.out, p.mean, p.rstd, b, p.ln_blocks,
+                pre);
+        } else {
+            ln_cast_amax_rows<CPL, FMT, FULL, kThreads>(p.x, p.gamma, p.beta, p.rows, p.hidden,
+                                                        p.eps, p.scale, p.amax, p.out, p.mean,
+                                                        p.rstd, b, p.ln_blocks);
+        }
         return;
     }
     b -= p.ln_blocks;
     for (int j = 0; j < kMaxPrologueCasts; ++j) {   // block-uniform choice of the job
         if (j < p.n_casts && b < p.cast_blocks[j]) {
             const CastJob& c = p.cast[j];
-            cast_tiles<false, FMT, kThreads>(c.in, c.rows, c.cols, c.scale, c.amax, c.out,
-                                             c.out_t, nullptr, c.copy_src, c.copy_dst, b,
-                                             p.cast_blocks[j]);
+            if constexpr (FUSED) {
+                const int q = p.upd.cast_slot[j];
+                cast_tiles<false, FMT, kThreads, false>(
+                    c.in, c.rows, c.cols, sh + 2 * q, reinterpret_cast<float*>(p.upd.ws + q),
+                    c.out, c.out_t, nullptr, sh + 2 * q + 1, c.copy_dst, b, p.cast_blocks[j], pre);
+            } else {
+                cast_tiles<false, FMT, kThreads>(c.in, c.rows, c.cols, c.scale, c.amax, c.out,
+                                                 c.out_t, nullptr, c.copy_src, c.copy_dst, b,
+                                                 p.cast_blocks[j]);
+            }
             return;
         }
         b -= p.cast_blocks[j];
@@ -75,29 +146,37 @@ hipError_t capacity(Kernel k, int& cache) {
     return hipSuccess;
 }
 
-template <int CPL, int FMT, bool FULL>
+template <int CPL, int FMT, bool FULL, bool FUSED>
 hipError_t launch_typed(ProloguePack& p, bool* launched, hipStream_t stream) {
     static int cap = 0;
-    hipError_t e = capacity(fwd_prologue_kernel<CPL, FMT, FULL>, cap);
+    hipError_t e = capacity(fwd_prologue_kernel<CPL, FMT, FULL, FUSED>, cap);
     if (e != hipSuccess) return e;
     int64_t total = p.ln_blocks;
     for (int j = 0; j < p.n_casts; ++j) total += p.cast_blocks[j];
     // only when every workgroup is resident at once: the jobs then overlap fully
     if (total > cap) return hipSuccess;
-    hipLaunchKernelGGL((fwd_prologue_kernel<CPL, FMT, FULL>), dim3((unsigned)total),
+    hipLaunchKernelGGL((fwd_prologue_kernel<CPL, FMT, FULL, FUSED>), dim3((unsigned)total),
                        dim3(kThreads), 0, stream, p);
     *launched = true;
     return hipGetLastError();
 }
 
-template <int CPL>
+template <int CPL, bool FUSED>
 hipError_t launch_cpl(ProloguePack& p, int fp8, bool* launched, hipStream_t stream) {
     const bool full = p.hidden == CPL * kWave * 8;
     if (fp8 == kE4M3)
-        return full ? launch_typed<CPL, kE4M3, true>(p, launched, stream)
-                    : launch_typed<CPL, kE4M3, false>(p, launched, stream);
-    return full ? launch_typed<CPL, kE5M2, true>(p, launched, stream)
-                : launch_typed<CPL, kE5M2, false>(p, launched, stream);
+        return full ? launch_typed<CPL, kE4M3, true, FUSED>(p, launched, stream)
+                    : launch_typed<CPL, kE4M3, false, FUSED>(p, launched, stream);
+    return full ? launch_typed<CPL, kE5M2, true, FUSED>(p, launched, stream)
+                : launch_typed<CPL, kE5M2, false, FUSED>(p, launched, stream);
+}
+
+template <bool FUSED>
+hipError_t launch_fused(ProloguePack& p, int fp8, bool* launched, hipStream_t stream) {
+    const int chunks = p.hidden / 8;
+    if (chunks <= 64) return launch_cpl<1, FUSED>(p, fp8, launched, stream);
+    if (chunks <= 128) return launch_cpl<2, FUSED>(p, fp8, launched, stream);
+    return launch_cpl<4, FUSED>(p, fp8, launched, stream);
 }
 
 }  // namespace
@@ -106,7 +185,7 @@ hipError_t launch_fwd_prologue(int64_t rows, int hidden, const void* x, const vo
                                const void* beta, float eps, int fp8, const float* scale,
                                float* amax, uint8_t* out, float* mean, float* rstd,
                                const CastJob* casts, int n_casts, bool* launched,
-                               hipStream_t stream) {
+                               hipStream_t stream, const FusedUpdate* upd) {
     *launched = false;
     if (rows <= 0 || hidden > 2048 || n_casts < 0 || n_casts > kMaxPrologueCasts)
         return hipSuccess;
@@ -124,15 +203,20 @@ hipError_t launch_fwd_prologue(int64_t rows, int hidden, const void* x, const vo
     p.rstd = rstd;
     p.ln_blocks = (int)((rows + kThreads / kWave - 1) / (kThreads / kWave));
     p.n_casts = n_casts;
+    if (upd) {
+        const int n = upd->n_slots;
+        if (upd->len < 1 || upd->len > 1024 || n < 1 || n > kMaxMetaSlots || (n & (n - 1)))
+            return hipSuccess;
+        p.fused = 1;
+        p.upd = *upd;
+    }
     for (int j = 0; j < n_casts; ++j) {
         if (casts[j].rows <= 0 || casts[j].cols <= 0) return hipSuccess;
         p.cast[j] = casts[j];
         p.cast_blocks[j] = (int)(((casts[j].rows + kCT - 1) / kCT) * ((casts[j].cols + kCT - 1) / kCT));
     }
-    const int chunks = hidden / 8;
-    if (chunks <= 64) return launch_cpl<1>(p, fp8, launched, stream);
-    if (chunks <= 128) return launch_cpl<2>(p, fp8, launched, stream);
-    return launch_cpl<4>(p, fp8, launched, stream);
+    return p.fused ? launch_fused<true>(p, fp8, launched, stream)
+                   : launch_fused<false>(p, fp8, launched, stream);
 }
 
 }  // namespace fp8ln

@@ -34,18 +34,6 @@ __global__ __launch_bounds__(kThreads) void meta_init_kernel(float* hist, float*
     }
 }
 
-// Wave-wide max with fmaxf semantics (a NaN operand is dropped): DPP steps
-// inside each 16-lane row, then two shuffles across rows.
-__device__ __forceinline__ float wave_max_f32(float v) {
-    v = fmaxf(v, dpp_f32<kDppQuadSwap1>(v));
-    v = fmaxf(v, dpp_f32<kDppQuadSwap2>(v));
-    v = fmaxf(v, dpp_f32<kDppRowHalfMirror>(v));
-    v = fmaxf(v, dpp_f32<kDppRowMirror>(v));
-    v = fmaxf(v, __shfl_xor(v, 16, kWave));
-    v = fmaxf(v, __shfl_xor(v, 32, kWave));
-    return v;
-}
-
 // One workgroup updates every slot of one state block in a single pass over the
 // history: every thread loads its share once into registers, the per-slot max
 // comes from those registers, and the shifted rows are written back from them.
@@ -116,12 +104,7 @@ __global__ __launch_bounds__(kThreads) void scaling_update_kernel(float* hist, f
             a = fmaxf(a, red_max[w][tid]);
             any_nan |= red_nan[w][tid];
         }
-        float sc = scale[tid];
-        if (!any_nan && a > 0.0f && a <= 3.402823466e38f) {
-            float ns = fp8_max / a;          // IEEE binary32 division
-            ns = ldexpf(ns, -margin);        // exact unless the result is subnormal
-            if (ns > 0.0f && ns <= 3.402823466e38f) sc = ns;
-        }
+        const float sc = delayed_scale(a, any_nan != 0, scale[tid], fp8_max, margin);
         scale[tid] = sc;
         scale_inv[tid] = 1.0f / sc;
     }

@@ -520,6 +520,29 @@ def linear_bwd(recipe: Recipe, dy, ctx: LinearCtx, fwd: Meta, bwd: Meta, dx, dwe
                                  _ptr(workspace), workspace.numel(), _stream(stream)))
 
 
+def step_workspace(device="cuda"):
+    """A zeroed step workspace for ln_linear_fwd_step / ln_mlp_fwd_step (every call
+    leaves it zero again; one per stream of steps)."""
+    return torch.zeros(_abi.STEP_WS_BYTES // 4, dtype=torch.int32, device=device)
+
+
+def ln_linear_fwd_step(recipe: Recipe, x, gamma, beta, weight, bias, out, fwd: Meta,
+                       ctx: LinearCtx, step_ws, stream=None) -> None:
+    """scaling_update(recipe, fwd) then ln_linear_fwd(...), the update folded into
+    the forward's first launch where the shape allows."""
+    M, K = x.shape
+    N = weight.shape[0]
+    _need(x, torch.bfloat16, (M, K), "x")
+    _need(weight, torch.bfloat16, (N, K), "weight")
+    _opt(bias, torch.bfloat16, (N,), "bias")
+    _need(out, torch.bfloat16, (M, N), "out")
+    _need(step_ws, torch.int32, (_abi.STEP_WS_BYTES // 4,), "step_ws")
+    r, m, c = recipe.as_c(), fwd.as_c(), ctx.as_c()
+    check(lib().fp8ln_ln_linear_fwd_step(C.byref(r), M, K, N, DTYPE_BF16, _ptr(x), _ptr(gamma),
+                                         _ptr(beta), _ptr(weight), _ptr(bias), _ptr(out),
+                                         C.byref(m), C.byref(c), _ptr(step_ws), _stream(stream)))
+
+
 def ln_linear_fwd(recipe: Recipe, x, gamma, beta, weight, bias, out, fwd: Meta, ctx: LinearCtx,
                   stream=None) -> None:
     M, K = x.shape

@@ -461,6 +461,30 @@ int fp8ln_ln_linear_fwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_f
                         const void* bias, void* out, const fp8ln_meta* fwd,
                         const fp8ln_linear_ctx* ctx, void* stream);
 
+/* Bytes of the step workspace of fp8ln_ln_linear_fwd_step / fp8ln_ln_mlp_fwd_step. */
+#define FP8LN_STEP_WS_BYTES 64
+
+/* One forward step of LayerNormLinear: fp8ln_scaling_update(recipe, fwd) followed
+ * by fp8ln_ln_linear_fwd with the same arguments, with identical results (history,
+ * scale, scale_inv, ctx contents and out, bit for bit).  The delayed recipe knows
+ * the step's scales before it sees the step's data ("Turbo-charging your
+ * transformer training", "Playing with lower-precision formats"; tutorial
+ * "Accelerating Transformer Training with NVIDIA Transformer Engine ...", FP8
+ * recipe setup: amax history, max reduction), so the update needs no launch of
+ * its own: where the forward's first launch (LayerNorm rows and weight cast side
+ * by side) serves the shape, each of its workgroups forms its scale from the
+ * history window itself and the last one to finish rolls the history (the
+ * pages' "fused" operations: fewer launches, "Turbo-charging ...", "What does
+ * 'fused' really mean?").  Otherwise the update runs as its own launch first.
+ * step_ws: device buffer of FP8LN_STEP_WS_BYTES, 16-byte aligned, all zero
+ * before the first call; every call leaves it zero.  Calls that share a step_ws
+ * or a state block must not overlap (the same stream orders them). */
+int fp8ln_ln_linear_fwd_step(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_features,
+                             int64_t out_features, int32_t params_dtype, const void* x,
+                             const void* gamma, const void* beta, const void* weight,
+                             const void* bias, void* out, const fp8ln_meta* fwd,
+                             const fp8ln_linear_ctx* ctx, void* step_ws, void* stream);
+
 /* Backward of fp8ln_ln_linear_fwd for the output gradient dy bf16
  * [tokens][out_features]:
  *   dy_q = encode(dy * bwd.scale[0]) in the backward format, amax -> bwd history

@@ -121,6 +121,19 @@ def test_unsupported_shapes_and_dtypes_are_rejected(lib):
     assert b"aligned" in lib.fp8ln_last_error()
 
 
+def test_forward_step_checks_its_workspace(lib):
+    r = _recipe()
+    p = C.c_void_p(256)
+    mf = _abi.MetaStruct(256, 256, 256, 2, _abi.META_FORWARD)
+    ctx = _abi.LinearCtxStruct(256, 256, 256, 256, 256, 256)
+    args = (C.byref(r), 32, 768, 2304, _abi.DTYPE_BF16, p, p, p, p, None, p, C.byref(mf),
+            C.byref(ctx))
+    s = lib.fp8ln_ln_linear_fwd_step(*args, None, None)
+    assert s == _abi.FP8LN_ERR_INVALID_ARG and b"step_ws" in lib.fp8ln_last_error()
+    s = lib.fp8ln_ln_linear_fwd_step(*args, C.c_void_p(260), None)
+    assert s == _abi.FP8LN_ERR_INVALID_ARG and b"aligned" in lib.fp8ln_last_error()
+
+
 def test_check_support_reports_a_reason_without_a_gpu(lib):
     buf = C.create_string_buffer(128)
     ok = lib.fp8ln_check_support(0, buf, len(buf))

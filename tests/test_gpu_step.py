@@ -1,0 +1,110 @@
+"""The forward step with the scaling update folded in, against the two calls it
+stands for (fp8ln_scaling_update, then the forward): the same history, scales,
+codes, statistics and outputs, bit for bit, step after step, eagerly and from a
+replayed HIP graph.  The two-call path is itself checked against the oracle by
+the module tests, so this identity carries that parity over."""
+import pytest
+import torch
+
+from fp8_delayed_scaling_row_amd import inputs, ops
+
+pytestmark = pytest.mark.gpu
+
+
+def _linear_state(M, K, N, recipe, training):
+    mf, _ = ops.linear_metas(recipe)
+    return dict(mf=mf, ctx=ops.LinearCtx(M, K, N, training=training),
+                out=torch.empty((M, N), dtype=torch.bfloat16, device="cuda"))
+
+
+def _linear_snapshot(st):
+    c = st["ctx"]
+    snap = dict(out=st["out"].clone(), hist=st["mf"].history.clone(),
+                scale=st["mf"].scale.clone(), scale_inv=st["mf"].scale_inv.clone(),
+                ln_q=c.ln_q.clone(), w_q=c.w_q.clone(), mean=c.mean.clone(),
+                rstd=c.rstd.clone(), w_scale_inv=c.w_scale_inv.clone())
+    if c.ln_qt is not None:
+        snap.update(ln_qt=c.ln_qt.clone(), w_qt=c.w_qt.clone())
+    return snap
+
+
+def _same(a, b, what):
+    for k in a:
+        x, y = a[k], b[k]
+        if x.dtype == torch.float32:
+            x, y = x.view(torch.int32), y.view(torch.int32)   # bit patterns (NaN too)
+        elif x.dtype == torch.bfloat16:
+            x, y = x.view(torch.int16), y.view(torch.int16)
+        assert torch.equal(x, y), f"{what}: {k} differs"
+
+
+def _x(M, K, wl, s, poison):
+    x = inputs.normal_bf16((M, K), inputs.seed_for(wl, "x", s), device="cuda")
+    if poison and M > 3:
+        x[1, 5] = float("nan")     # a NaN row amax enters the history
+        x[3, 0] = float("inf")
+    return x * (1.0 + 0.5 * s)
+
+
+# (tokens, in, out, format, history length, margin, FP8 weight storage, training)
+CASES = [
+    (256, 768, 2304, ops.FORMAT_HYBRID, 16, 0, False, False),   # the pages' QKV layer
+    (256, 768, 2304, ops.FORMAT_HYBRID, 16, 0, True, False),    # FP8 weight storage
+    (130, 272, 144, ops.FORMAT_E4M3, 1024, 1, False, False),    # ragged, long window
+    (64, 2048, 512, ops.FORMAT_E5M2, 16, 0, False, True),       # widest rows, transposes
+    (8192, 2048, 2048, ops.FORMAT_HYBRID, 16, 0, False, False), # update as its own launch
+    (0, 64, 32, ops.FORMAT_HYBRID, 16, 0, False, False),        # no tokens: the update only
+]
+
+
+@pytest.mark.parametrize("M,K,N,fmt,L,margin,reuse,training", CASES)
+def test_ln_linear_fwd_step_equals_update_then_forward(M, K, N, fmt, L, margin, reuse, training):
+    recipe = ops.Recipe(format=fmt, amax_history_len=L, margin=margin)
+    wl = f"step-{M}x{K}x{N}"
+    g, b = inputs.layernorm_params(K, wl, device="cuda")
+    w = inputs.linear_weight(N, K, wl, "w", device="cuda")
+    bias = (torch.randn(N, device="cuda") * 0.1).to(torch.bfloat16)
+    two, one = _linear_state(M, K, N, recipe, training), _linear_state(M, K, N, recipe, training)
+    ws = ops.step_workspace()
+    for s in range(6):
+        x = _x(M, K, wl, s, poison=(s == 2 and M == 256 and not reuse))
+        if reuse and s == 1:
+            two["ctx"].reuse_weight_codes = one["ctx"].reuse_weight_codes = True
+        ops.scaling_update(recipe, two["mf"])
+        ops.ln_linear_fwd(recipe, x, g, b, w, bias, two["out"], two["mf"], two["ctx"])
+        ops.ln_linear_fwd_step(recipe, x, g, b, w, bias, one["out"], one["mf"], one["ctx"], ws)
+        torch.cuda.synchronize()
+        _same(_linear_snapshot(two), _linear_snapshot(one), f"step {s}")
+        assert int(ws.abs().sum().item()) == 0, f"step {s}: workspace not cleared"
+
+
+def test_ln_linear_fwd_step_graph_replays_match_eager():
+    M, K, N = 256, 768, 2304
+    recipe = ops.Recipe(format=ops.FORMAT_HYBRID, amax_history_len=16)
+    wl = "step-graph"
+    g, b = inputs.layernorm_params(K, wl, device="cuda")
+    w = inputs.linear_weight(N, K, wl, "w", device="cuda")
+    bias = (torch.randn(N, device="cuda") * 0.1).to(torch.bfloat16)
+    xs = [_x(M, K, wl, s, poison=False) for s in range(5)]
+    eager, graphed = _linear_state(M, K, N, recipe, False), _linear_state(M, K, N, recipe, False)
+    ws = ops.step_workspace()
+    x_in = torch.empty_like(xs[0])
+    ops.scaling_update(recipe, eager["mf"])
+    ops.ln_linear_fwd(recipe, xs[0], g, b, w, bias, eager["out"], eager["mf"], eager["ctx"])
+    ops.ln_linear_fwd_step(recipe, xs[0], g, b, w, bias, graphed["out"], graphed["mf"],
+                           graphed["ctx"], ws)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ops.ln_linear_fwd_step(recipe, x_in, g, b, w, bias, graphed["out"], graphed["mf"],
+                               graphed["ctx"], ws)
+    for s in range(1, 5):
+        ops.scaling_update(recipe, eager["mf"])
+        ops.ln_linear_fwd(recipe, xs[s], g, b, w, bias, eager["out"], eager["mf"], eager["ctx"])
+        torch.cuda.synchronize()
+        x_in.copy_(xs[s])
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        _same(_linear_snapshot(eager), _linear_snapshot(graphed), f"replay {s}")
+        assert int(ws.abs().sum().item()) == 0
