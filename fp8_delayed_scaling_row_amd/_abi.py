@@ -126,6 +126,8 @@ SIGNATURES = {
                                               _P, _P, _P]),
     "fp8ln_ln_mlp_fwd": (C.c_int, [_RP, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _P,
                                    _MP, C.POINTER(MlpCtxStruct), _P]),
+    "fp8ln_ln_mlp_fwd_step": (C.c_int, [_RP, _I64, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P,
+                                        _P, _MP, C.POINTER(MlpCtxStruct), _P, _P]),
     "fp8ln_ln_mlp_bwd": (C.c_int, [_RP, _I64, _I64, _I64, _I32, _P, _P, _P,
                                    C.POINTER(MlpCtxStruct), _MP, _MP, _P, _P, _P, _P, _P, _P, _P,
                                    _P, _SZ, _P]),

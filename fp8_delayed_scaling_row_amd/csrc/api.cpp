@@ -1291,10 +1291,13 @@ int fp8ln_ln_linear_bwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_f
     return FP8LN_OK;
 }
 
-int fp8ln_ln_mlp_fwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t hidden, int64_t ffn,
-                     int32_t params_dtype, const void* x, const void* gamma, const void* beta,
-                     const void* w1, const void* b1, const void* w2, const void* b2, void* out,
-                     const fp8ln_meta* fwd, const fp8ln_mlp_ctx* ctx, void* stream) {
+// LayerNormMLP forward; with step_ws, the step-start scaling update of the
+// forward state comes first (folded in when the prologue launch serves the shape).
+static int ln_mlp_fwd_impl(const fp8ln_recipe* recipe, int64_t tokens, int64_t hidden,
+                           int64_t ffn, int32_t params_dtype, const void* x, const void* gamma,
+                           const void* beta, const void* w1, const void* b1, const void* w2,
+                           const void* b2, void* out, const fp8ln_meta* fwd,
+                           const fp8ln_mlp_ctx* ctx, void* step_ws, void* stream) {
     int s = check_recipe(recipe);
     if (s) return s;
     const int64_t M = tokens, H = hidden, F = ffn;
@@ -1309,7 +1312,7 @@ int fp8ln_ln_mlp_fwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t hidden,
                     (long long)F);
     if ((s = check_meta(fwd, 4, FP8LN_META_FORWARD, "forward"))) return s;
     REQUIRE_PTR(ctx);
-    REQUIRE(ctx->ln_q && ctx->w1_q && ctx->w2_q && ctx->g_q,
+    REQUIRE((M == 0 || (ctx->ln_q && ctx->g_q)) && ctx->w1_q && ctx->w2_q,
             "ctx.ln_q, w1_q, w2_q and g_q are required");
     if ((ctx->ln_qt || ctx->g_qt) && M % 16 != 0)
         return fail(FP8LN_ERR_UNSUPPORTED, "transposed activations need tokens %% 16 == 0");
@@ -1336,6 +1339,7 @@ int fp8ln_ln_mlp_fwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t hidden,
     if (ctx->ln_qt) CHECK(check_transpose_rows(M, "ln_mlp_fwd"));
     CHECK(check_gemm_size(M, F, H, 1, false, "ln_mlp_fwd fc1"));
     CHECK(check_gemm_size(M, H, F, 1, false, "ln_mlp_fwd fc2"));
+    if (step_ws) REQUIRE_ALIGNED(step_ws);
     if ((s = check_current_device())) return s;
     hipStream_t st = as_stream(stream);
     const int f = meta_fp8(recipe, FP8LN_META_FORWARD);
@@ -1345,8 +1349,10 @@ int fp8ln_ln_mlp_fwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t hidden,
     float* wsi = ctx->w_scale_inv;
     const float* w1_sinv = wsi ? wsi + 0 : fwd->scale_inv + 1;
     const float* w2_sinv = wsi ? wsi + 1 : fwd->scale_inv + 3;
+    FusedUpdate upd{hist, fwd->scale, fwd->scale_inv, recipe->amax_history_len, fwd->n_slots,
+                    recipe->margin, fp8_max_of(f), (uint32_t*)step_ws, 0, {1, 3}};
     bool fused = false;   // LayerNorm rows and both weight casts in one launch (small shapes)
-    if (M > 0 && !ctx->reuse_weight_codes) {
+    if (M > 0) {
         const CastJob wj[2] = {
             {w1, F, H, fwd->scale + 1, hist + 1, ctx->w1_q, ctx->w1_qt, fwd->scale_inv + 1,
              wsi ? wsi + 0 : nullptr},
@@ -1354,9 +1360,18 @@ int fp8ln_ln_mlp_fwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t hidden,
              wsi ? wsi + 1 : nullptr}};
         FP8LN_TRY(launch_fwd_prologue(M, (int)H, x, gamma, beta, recipe->ln_eps, f,
                                       fwd->scale + 0, hist + 0, ctx->ln_q, ctx->mean, ctx->rstd,
-                                      wj, 2, &fused, st),
+                                      wj, ctx->reuse_weight_codes ? 0 : 2, &fused, st,
+                                      step_ws ? &upd : nullptr),
                   "forward prologue launch");
     }
+    if (step_ws && !fused)   // the update as its own launch, before anything reads a scale
+        FP8LN_TRY(launch_scaling_update(hist, fwd->scale, fwd->scale_inv,
+                                        recipe->amax_history_len, fwd->n_slots, recipe->margin,
+                                        fp8_max_of(f), st),
+                  "scaling_update launch");
+    // folded update: the GELU output's amax joins the others in step_ws, and the
+    // fc2 GEMM's first workgroup rolls the history
+    const bool roll = step_ws && fused;
     if (M > 0) {
         if (!fused)
             FP8LN_TRY(launch_ln_cast_amax(M, (int)H, x, gamma, beta, recipe->ln_eps, f,
@@ -1382,7 +1397,7 @@ int fp8ln_ln_mlp_fwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t hidden,
     p1.q_out = ctx->g_q;
     p1.q_out_t = ctx->g_qt;
     p1.q_scale = fwd->scale + 2;
-    p1.q_amax = hist + 2;
+    p1.q_amax = roll ? (float*)((uint32_t*)step_ws + 2) : hist + 2;
     p1.q_fp8 = f;
     p1.gelu_erf = recipe->activation == FP8LN_GELU_ERF;
     FP8LN_TRY(launch_gemm(p1, st), "fc1 launch");
@@ -1390,8 +1405,32 @@ int fp8ln_ln_mlp_fwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t hidden,
                                 kEpiBf16Bias);
     p2.bias = (const uint16_t*)b2;
     p2.out = out;
+    if (roll) {
+        p2.roll_hist = hist;
+        p2.roll_ws = (uint32_t*)step_ws;
+        p2.roll_len = recipe->amax_history_len;
+        p2.roll_slots = fwd->n_slots;
+    }
     FP8LN_TRY(launch_gemm(p2, st), "fc2 launch");
     return FP8LN_OK;
+}
+
+int fp8ln_ln_mlp_fwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t hidden, int64_t ffn,
+                     int32_t params_dtype, const void* x, const void* gamma, const void* beta,
+                     const void* w1, const void* b1, const void* w2, const void* b2, void* out,
+                     const fp8ln_meta* fwd, const fp8ln_mlp_ctx* ctx, void* stream) {
+    return ln_mlp_fwd_impl(recipe, tokens, hidden, ffn, params_dtype, x, gamma, beta, w1, b1, w2,
+                           b2, out, fwd, ctx, nullptr, stream);
+}
+
+int fp8ln_ln_mlp_fwd_step(const fp8ln_recipe* recipe, int64_t tokens, int64_t hidden,
+                          int64_t ffn, int32_t params_dtype, const void* x, const void* gamma,
+                          const void* beta, const void* w1, const void* b1, const void* w2,
+                          const void* b2, void* out, const fp8ln_meta* fwd,
+                          const fp8ln_mlp_ctx* ctx, void* step_ws, void* stream) {
+    REQUIRE_PTR(step_ws);
+    return ln_mlp_fwd_impl(recipe, tokens, hidden, ffn, params_dtype, x, gamma, beta, w1, b1, w2,
+                           b2, out, fwd, ctx, step_ws, stream);
 }
 
 int fp8ln_ln_mlp_bwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t hidden, int64_t ffn,

@@ -608,6 +608,26 @@ def ln_mlp_fwd(recipe: Recipe, x, gamma, beta, w1, b1, w2, b2, out, fwd: Meta, c
                                  C.byref(m), C.byref(c), _stream(stream)))
 
 
+def ln_mlp_fwd_step(recipe: Recipe, x, gamma, beta, w1, b1, w2, b2, out, fwd: Meta,
+                    ctx: MlpCtx, step_ws, stream=None) -> None:
+    """scaling_update(recipe, fwd) then ln_mlp_fwd(...), the update folded into the
+    forward's launches where the shape allows."""
+    M, H = x.shape
+    F = w1.shape[0]
+    _need(x, torch.bfloat16, (M, H), "x")
+    _need(w1, torch.bfloat16, (F, H), "w1")
+    _need(w2, torch.bfloat16, (H, F), "w2")
+    _opt(b1, torch.bfloat16, (F,), "b1")
+    _opt(b2, torch.bfloat16, (H,), "b2")
+    _need(out, torch.bfloat16, (M, H), "out")
+    _need(step_ws, torch.int32, (_abi.STEP_WS_BYTES // 4,), "step_ws")
+    r, m, c = recipe.as_c(), fwd.as_c(), ctx.as_c()
+    check(lib().fp8ln_ln_mlp_fwd_step(C.byref(r), M, H, F, DTYPE_BF16, _ptr(x), _ptr(gamma),
+                                      _ptr(beta), _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2),
+                                      _ptr(out), C.byref(m), C.byref(c), _ptr(step_ws),
+                                      _stream(stream)))
+
+
 def ln_mlp_bwd(recipe: Recipe, dy, x, gamma, ctx: MlpCtx, fwd: Meta, bwd: Meta, dx, dgamma,
                dbeta, dw1, db1, dw2, db2, workspace=None, stream=None) -> None:
     M, H = dy.shape

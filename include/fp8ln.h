@@ -538,6 +538,17 @@ int fp8ln_ln_mlp_fwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t hidden,
                      const void* b2, void* out, const fp8ln_meta* fwd,
                      const fp8ln_mlp_ctx* ctx, void* stream);
 
+/* One forward step of LayerNormMLP: fp8ln_scaling_update(recipe, fwd) followed by
+ * fp8ln_ln_mlp_fwd with the same arguments, with identical results, the update
+ * folded into the forward's launches as in fp8ln_ln_linear_fwd_step (the GELU
+ * output's amax is recorded with the others and the fc2 GEMM rolls the history).
+ * step_ws as for fp8ln_ln_linear_fwd_step. */
+int fp8ln_ln_mlp_fwd_step(const fp8ln_recipe* recipe, int64_t tokens, int64_t hidden,
+                          int64_t ffn, int32_t params_dtype, const void* x, const void* gamma,
+                          const void* beta, const void* w1, const void* b1, const void* w2,
+                          const void* b2, void* out, const fp8ln_meta* fwd,
+                          const fp8ln_mlp_ctx* ctx, void* step_ws, void* stream);
+
 /* Backward of fp8ln_ln_mlp_fwd for dy bf16 [tokens][hidden]:
  *   dy_q = encode(dy * bwd.scale[0]); db2 = column sums of dy
  *   dH = (dy_q . w2_q) * bwd.scale_inv[0] * fwd.scale_inv[3] * gelu'(h)

@@ -108,3 +108,54 @@ def test_ln_linear_fwd_step_graph_replays_match_eager():
         torch.cuda.synchronize()
         _same(_linear_snapshot(eager), _linear_snapshot(graphed), f"replay {s}")
         assert int(ws.abs().sum().item()) == 0
+
+
+def _mlp_state(M, H, F, recipe, training):
+    mf, _ = ops.mlp_metas(recipe)
+    return dict(mf=mf, ctx=ops.MlpCtx(M, H, F, training=training),
+                out=torch.empty((M, H), dtype=torch.bfloat16, device="cuda"))
+
+
+def _mlp_snapshot(st):
+    c = st["ctx"]
+    snap = dict(out=st["out"].clone(), hist=st["mf"].history.clone(),
+                scale=st["mf"].scale.clone(), scale_inv=st["mf"].scale_inv.clone(),
+                ln_q=c.ln_q.clone(), w1_q=c.w1_q.clone(), w2_q=c.w2_q.clone(), g_q=c.g_q.clone(),
+                mean=c.mean.clone(), rstd=c.rstd.clone(), w_scale_inv=c.w_scale_inv.clone())
+    for k in ("ln_qt", "w1_qt", "w2_qt", "g_qt", "h"):
+        if getattr(c, k) is not None:
+            snap[k] = getattr(c, k).clone()
+    return snap
+
+
+# (tokens, hidden, ffn, format, history length, activation, FP8 weight storage, training)
+MLP_CASES = [
+    (2048, 768, 3072, ops.FORMAT_E4M3, 16, ops.GELU_TANH, False, False),   # the pages' MLP
+    (2048, 768, 3072, ops.FORMAT_E4M3, 16, ops.GELU_TANH, True, False),    # FP8 weights
+    (144, 256, 400, ops.FORMAT_HYBRID, 1024, ops.GELU_ERF, False, True),   # ragged, long window
+    (16384, 2048, 8192, ops.FORMAT_HYBRID, 16, ops.GELU_TANH, False, False),  # update apart
+]
+
+
+@pytest.mark.parametrize("M,H,F,fmt,L,act,reuse,training", MLP_CASES)
+def test_ln_mlp_fwd_step_equals_update_then_forward(M, H, F, fmt, L, act, reuse, training):
+    recipe = ops.Recipe(format=fmt, amax_history_len=L, activation=act)
+    wl = f"mlp-step-{M}x{H}x{F}"
+    g, b = inputs.layernorm_params(H, wl, device="cuda")
+    w1 = inputs.linear_weight(F, H, wl, "w1", device="cuda")
+    w2 = inputs.linear_weight(H, F, wl, "w2", device="cuda")
+    b1 = (torch.randn(F, device="cuda") * 0.1).to(torch.bfloat16)
+    b2 = (torch.randn(H, device="cuda") * 0.1).to(torch.bfloat16)
+    two, one = _mlp_state(M, H, F, recipe, training), _mlp_state(M, H, F, recipe, training)
+    ws = ops.step_workspace()
+    for s in range(4 if M > 4096 else 6):
+        x = _x(M, H, wl, s, poison=(s == 2 and M == 2048 and not reuse))
+        if reuse and s == 1:
+            two["ctx"].reuse_weight_codes = one["ctx"].reuse_weight_codes = True
+        ops.scaling_update(recipe, two["mf"])
+        ops.ln_mlp_fwd(recipe, x, g, b, w1, b1, w2, b2, two["out"], two["mf"], two["ctx"])
+        ops.ln_mlp_fwd_step(recipe, x, g, b, w1, b1, w2, b2, one["out"], one["mf"], one["ctx"],
+                            ws)
+        torch.cuda.synchronize()
+        _same(_mlp_snapshot(two), _mlp_snapshot(one), f"step {s}")
+        assert int(ws.abs().sum().item()) == 0, f"step {s}: workspace not cleared"
