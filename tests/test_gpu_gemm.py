@@ -48,6 +48,30 @@ def test_small_integer_gemm_is_bit_exact(fa, fb, M, N, K):
     np.testing.assert_array_equal(out.cpu().numpy(), av @ bv.T)
 
 
+# Small products on 64 x 64 tiles: the whole-K tile (K <= 1024 bytes, at most one
+# tile per CU; 1 and 16 steps) and the four-stage ring for long K (49 steps = 12
+# rounds and one step over, 33 = eight rounds and one over, 23 = five rounds and
+# three over).
+@pytest.mark.parametrize("fa,fb", PAIRS, ids=["e4m3xe4m3", "e5m2xe4m3", "e4m3xe5m2", "e5m2xe5m2"])
+@pytest.mark.parametrize("M,N,K", [(64, 64, 64), (200, 144, 1024), (1024, 512, 3136),
+                                   (130, 208, 2112), (70, 64, 1472)])
+def test_small_tile_variants_are_bit_exact(fa, fb, M, N, K):
+    """|a|, |b| <= 8 and K <= 3136: every partial sum is an integer below 2^24."""
+    a, av = int_codes((M, K), fa, M * 5 + K)
+    b, bv = int_codes((N, K), fb, N * 11 + K)
+    out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    ops.gemm(dev(a), fa, dev(b), fb, _scalar(1.0), _scalar(1.0), out)
+    bias_bits = oracle.f64_to_bf16_bits(np.random.default_rng(N).integers(-64, 65, N) / 64.0)
+    bias = torch.from_numpy(bias_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    ob = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ops.gemm(dev(a), fa, dev(b), fb, _scalar(0.5), _scalar(0.25), ob, bias)
+    torch.cuda.synchronize()
+    exact = av @ bv.T
+    np.testing.assert_array_equal(out.cpu().numpy(), exact)
+    ref = oracle.f64_to_bf16_bits(exact * 0.125 + oracle.bf16_to_f64(bias_bits)[None, :])
+    np.testing.assert_array_equal(ob.view(torch.int16).cpu().numpy().view(np.uint16), ref)
+
+
 def test_layout_pins_permutation_and_single_entries():
     M, N, K = 64, 128, 256
     rng = np.random.default_rng(0)
