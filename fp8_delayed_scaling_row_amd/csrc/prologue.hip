@@ -101,7 +101,7 @@ __global__ __launch_bounds__(kThreads) void fwd_prologue_kernel(ProloguePack p) 
     if (b < p.ln_blocks) {
         if constexpr (FUSED) {
             const int q = p.upd.ln_slot;
-            ln_cast_amax_rows<CPL, FMT, FULL, kThreads, false>(
+            ln_cast_amax_rows<CPL, FMT, FULL, kThreads, true>(
                 p.x, p.gamma, p.beta, p.rows, p.hidden, p.eps, sh + 2 * q,
                 reinterpret_cast<float*>(p.upd.ws + q), p.out, p.mean, p.rstd, b, p.ln_blocks,
                 pre);
@@ -118,7 +118,7 @@ __global__ __launch_bounds__(kThreads) void fwd_prologue_kernel(ProloguePack p) 
             const CastJob& c = p.cast[j];
             if constexpr (FUSED) {
                 const int q = p.upd.cast_slot[j];
-                cast_tiles<false, FMT, kThreads, false>(
+                cast_tiles<false, FMT, kThreads, true>(
                     c.in, c.rows, c.cols, sh + 2 * q, reinterpret_cast<float*>(p.upd.ws + q),
                     c.out, c.out_t, nullptr, sh + 2 * q + 1, c.copy_dst, b, p.cast_blocks[j], pre);
             } else {
