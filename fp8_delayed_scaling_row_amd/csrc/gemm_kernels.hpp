@@ -164,9 +164,6 @@ __device__ __forceinline__ void roll_history(float* hist, uint32_t* ws, int len,
     }
 }
 
-// Stages of the whole-K tile (K up to 16 x 64 bytes held in LDS at once).
-constexpr int kWholeKStages = 16;
-
 // Smallest power of two P such that a stage of STAGE bytes holds a multiple of 32
 // rows of LB / P bytes.
 constexpr int staging_parts(int LB, int STAGE) {
@@ -288,8 +285,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int vb) {
     constexpr int EPI = EPIX % 16;
     constexpr int ACT = EPIX / 16 % 4;
     constexpr bool FULLX = EPIX >= 64;
-    static_assert(NS == 3 || NS == 4 || NS == 0, "three or four pipeline stages, or whole K");
-    constexpr int NSE = NS == 0 ? 4 : NS;        // ring stages the epilogue stages through
+    static_assert(NS == 3 || NS == 4, "three or four pipeline stages");
     constexpr int NW = WGM * WGN;              // waves per workgroup
     constexpr int WM = BM / WGM, WN = BN / WGN;  // wave sub-tile
     constexpr int TM = WM / 32, TN = WN / 32;  // 32 x 32 MFMA tiles per wave
@@ -299,12 +295,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int vb) {
     constexpr int B_DMA = B_BYTES / 1024 / NW;
     constexpr int P = A_DMA + B_DMA;           // vector-memory ops per wave and stage
     // one LDS array per pipeline stage, so the compiler tracks each stage's loads
-    // (whole K, NS = 0: one array of kWholeKStages stages, all loaded at once)
-    __shared__ __attribute__((aligned(16))) uint8_t st0[NS == 0 ? 16 : STAGE];
-    __shared__ __attribute__((aligned(16))) uint8_t st1[NS == 0 ? 16 : STAGE];
-    __shared__ __attribute__((aligned(16))) uint8_t st2[NS == 0 ? 16 : STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t st2[STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t st3[NS == 4 ? STAGE : 16];
-    __shared__ __attribute__((aligned(16))) uint8_t stk[NS == 0 ? kWholeKStages * STAGE : 16];
 
     const int t = threadIdx.x;
     if constexpr (!GROUP) {
@@ -454,7 +448,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int vb) {
         // MFMAs (and lifts MFMAs of the previous step past the barrier), which
         // costs a step of latency cover.
         __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(NS >= 2 ? (NS - 2) * P : 0));
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * P));
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         issue(refill, (int64_t)(kt + NS - 1) * BKS);
         __builtin_amdgcn_sched_barrier(0);
@@ -466,22 +460,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int vb) {
     // and no step multiplies one).
     const int nk = (int)((K + BKS - 1) / BKS);
     int kt = 0;
-    if constexpr (NS == 0) {
-        issue(stk, 0);
-        if (nk > 1) issue(stk + STAGE, BKS);
-    } else {
-        issue(st0, 0);
-        issue(st1, BKS);
-    }
-    if constexpr (NS == 0) {
-        // every stage in flight at once: one memory latency for the whole K
-        // (small problems, where a ring's per-step waits add up to most of the
-        // time), then the MFMAs back to back
-        for (int k = 2; k < nk; ++k) issue(stk + k * STAGE, (int64_t)k * BKS);
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        __syncthreads();
-        for (int k = 0; k < nk; ++k) compute(stk + k * STAGE);
-    } else if constexpr (NS == 4) {
+    issue(st0, 0);
+    issue(st1, BKS);
+    if constexpr (NS == 4) {
         issue(st2, 2 * BKS);
         for (; kt + 4 <= nk; kt += 4) {
             step(st0, st3, kt);
@@ -515,7 +496,6 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int vb) {
     // so the 32 rows a wave writes at once fall on different banks.
     constexpr int NT = 64 * NW;
     auto ring = [&](int sidx) -> lds8* {
-        if constexpr (NS == 0) return (lds8*)(stk + sidx * STAGE);
         return sidx == 0 ? (lds8*)st0 : sidx == 1 ? (lds8*)st1 : sidx == 2 ? (lds8*)st2 : (lds8*)st3;
     };
     const float alpha = FA == kOpBf16 ? 1.0f : (*p.sinv_a) * (*p.sinv_b);   // bf16: no scales
@@ -537,7 +517,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int vb) {
             // Bring the tile of h into the ring in the bf16 staging layout (direct
             // loads, rows past M read as zero), then scale by gelu'(h) in place.
             using G = Staging<BN * 2, BM, STAGE>;
-            static_assert(BM * G::P <= NSE * G::RPS && G::UNITS % (64 * NW) == 0, "h staging");
+            static_assert(BM * G::P <= NS * G::RPS && G::UNITS % (64 * NW) == 0, "h staging");
             constexpr int IPW = G::UNITS / 64 / NW;    // 64-chunk loads per wave
             const int64_t rows_h = min<int64_t>(BM, M - m0);
             const __amdgpu_buffer_rsrc_t rsrc_h = __builtin_amdgcn_make_buffer_rsrc(
@@ -657,11 +637,11 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int vb) {
         if constexpr (EPI == kEpiF32 || EPI == kEpiDGeluF32) {
             // fp32 rows; a 256 x 256 tile goes out in two passes of 128 rows
             constexpr int P4 = staging_parts(BN * 4, STAGE);
-            constexpr int CAP = NSE * (STAGE / (BN * 4 / P4)) / P4;   // tile rows one pass holds
+            constexpr int CAP = NS * (STAGE / (BN * 4 / P4)) / P4;   // tile rows one pass holds
             constexpr int PASSES = (BM + CAP - 1) / CAP;
             constexpr int RPP = BM / PASSES;
             using G = Staging<BN * 4, RPP, STAGE>;
-            static_assert(RPP * PASSES == BM && RPP % WM == 0 && RPP * G::P <= NSE * G::RPS,
+            static_assert(RPP * PASSES == BM && RPP % WM == 0 && RPP * G::P <= NS * G::RPS,
                           "f32 staging");
 #pragma unroll
             for (int ps = 0; ps < PASSES; ++ps) {
@@ -695,7 +675,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int vb) {
         // bf16 rows of the tile through the ring
         auto bf16_out = [&](uint16_t* dst) {
             using G = Staging<BN * 2, BM, STAGE>;
-            static_assert(BM * G::P <= NSE * G::RPS, "bf16 staging");
+            static_assert(BM * G::P <= NS * G::RPS, "bf16 staging");
             lds8* brow[TM][TN];
 #pragma unroll
             for (int i = 0; i < TM; ++i)
@@ -751,7 +731,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int vb) {
             // consecutive rows, written as one word.
             using Q = Staging<BN, BM, STAGE>;
             using QT = Staging<BM, BN, STAGE>;
-            static_assert(BM * Q::P <= NSE * Q::RPS && BN * QT::P <= NSE * QT::RPS, "code staging");
+            static_assert(BM * Q::P <= NS * Q::RPS && BN * QT::P <= NS * QT::RPS, "code staging");
             static_assert(QT::P == 1, "transposed code rows are never cut");
             lds8* qrow[TM][TN];
             lds8* qtrow[TN];
@@ -897,15 +877,6 @@ void gemm_kernel_64(GemmParams p) {
     gemm_tile<64, 64, 2, 2, 4, FA, FB, EPI, QF>(p, blockIdx.x);
 }
 
-// 64 x 64 tiles with the whole K (at most kWholeKStages steps) loaded in one go,
-// one workgroup per CU (128 KB of LDS): for products with at most one tile per
-// CU, whose time a ring's per-step load waits would otherwise set.
-template <int FA, int FB, int EPI, int QF>
-__global__ __attribute__((amdgpu_waves_per_eu(1, 1))) __launch_bounds__(256)
-void gemm_kernel_64_wk(GemmParams p) {
-    gemm_tile<64, 64, 2, 2, 0, FA, FB, EPI, QF>(p, blockIdx.x);
-}
-
 // Up to kMaxGemmGroup independent small fp32-output products in one launch:
 // blocks [start[k], start[k + 1]) are the tiles of product k, each computed
 // exactly as the kernel of that tile shape computes it alone.  Small problems leave
@@ -985,12 +956,6 @@ hipError_t launch_typed(const GemmParams& p, hipStream_t stream) {
             break;
         case kTile64:
             if constexpr (EPI % 16 != kEpiDGeluFp8) {
-                if (cdiv(p.K, 64) <= kWholeKStages && cdiv(p.M, 64) * cdiv(p.N, 64) <= 256) {
-                    hipLaunchKernelGGL((gemm_kernel_64_wk<FA, FB, EPI, QF>),
-                                       dim3((unsigned)(cdiv(p.M, 64) * cdiv(p.N, 64))), dim3(256),
-                                       0, stream, p);
-                    break;
-                }
                 hipLaunchKernelGGL((gemm_kernel_64<FA, FB, EPI, QF>),
                                    dim3((unsigned)(cdiv(p.M, 64) * cdiv(p.N, 64))), dim3(256), 0,
                                    stream, p);

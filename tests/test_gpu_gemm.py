@@ -48,10 +48,8 @@ def test_small_integer_gemm_is_bit_exact(fa, fb, M, N, K):
     np.testing.assert_array_equal(out.cpu().numpy(), av @ bv.T)
 
 
-# Small products on 64 x 64 tiles: the whole-K tile (K <= 1024 bytes, at most one
-# tile per CU; 1 and 16 steps) and the four-stage ring for long K (49 steps = 12
-# rounds and one step over, 33 = eight rounds and one over, 23 = five rounds and
-# three over).
+# Small products on 64 x 64 tiles with 1, 16, 49, 33 and 23 steps of K (whole
+# rounds of the four-stage ring with 0, 1 and 3 steps over).
 @pytest.mark.parametrize("fa,fb", PAIRS, ids=["e4m3xe4m3", "e5m2xe4m3", "e4m3xe5m2", "e5m2xe5m2"])
 @pytest.mark.parametrize("M,N,K", [(64, 64, 64), (200, 144, 1024), (1024, 512, 3136),
                                    (130, 208, 2112), (70, 64, 1472)])
