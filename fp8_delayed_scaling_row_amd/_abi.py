@@ -83,6 +83,7 @@ SIGNATURES = {
     "fp8ln_workspace_size": (_SZ, [_I32, _I64, _I64, _I64]),
     "fp8ln_meta_init": (C.c_int, [_RP, _MP, _P]),
     "fp8ln_scaling_update": (C.c_int, [_RP, _MP, _P]),
+    "fp8ln_scaling_update_batch": (C.c_int, [_RP, C.POINTER(MetaStruct), _I32, _P]),
     "fp8ln_ln_cast_amax": (C.c_int, [_RP, _I64, _I64, _I32, _P, _P, _P, _I32, _P, _P, _P, _P,
                                      _P, _P, _P]),
     "fp8ln_cast_amax": (C.c_int, [_I64, _I64, _I32, _P, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),

@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/fp8ln.h"
@@ -415,6 +416,31 @@ int fp8ln_scaling_update(const fp8ln_recipe* recipe, const fp8ln_meta* meta, voi
                                     recipe->amax_history_len, meta->n_slots, recipe->margin, fmax,
                                     as_stream(stream)),
               "scaling_update launch");
+    return FP8LN_OK;
+}
+
+int fp8ln_scaling_update_batch(const fp8ln_recipe* recipe, const fp8ln_meta* metas, int32_t n,
+                               void* stream) {
+    int s = check_recipe(recipe);
+    if (s) return s;
+    REQUIRE(n >= 0, "n < 0");
+    if (n > 0) REQUIRE_PTR(metas);
+    for (int32_t i = 0; i < n; ++i)
+        if ((s = check_meta(metas + i, 1, -1, "state"))) return s;
+    if ((s = check_current_device())) return s;
+    hipStream_t st = as_stream(stream);
+    UpdateBatch b;   // kernel arguments are copied at launch
+    for (int32_t base = 0; base < n; base += kMaxUpdateBatch) {
+        const int cnt = n - base < kMaxUpdateBatch ? (int)(n - base) : kMaxUpdateBatch;
+        b.len = recipe->amax_history_len;
+        b.margin = recipe->margin;
+        for (int k = 0; k < cnt; ++k) {
+            const fp8ln_meta& m = metas[base + k];
+            b.job[k] = UpdateJob{m.amax_history, m.scale, m.scale_inv, m.n_slots,
+                                 fp8_max_of(meta_fp8(recipe, m.kind))};
+        }
+        FP8LN_TRY(launch_scaling_update_batch(b, cnt, st), "scaling_update_batch launch");
+    }
     return FP8LN_OK;
 }
 

@@ -19,6 +19,20 @@ enum Fp8Kind : int { kE4M3 = 0, kE5M2 = 1 };
 // scaling.hip
 hipError_t launch_meta_init(float* hist, float* scale, float* scale_inv, int len, int n_slots,
                             hipStream_t stream);
+// Up to kMaxUpdateBatch state blocks updated in one launch (same recipe).
+constexpr int kMaxUpdateBatch = 64;
+struct UpdateJob {
+    float* hist;
+    float* scale;
+    float* scale_inv;
+    int n_slots;
+    float fp8_max;
+};
+struct UpdateBatch {
+    UpdateJob job[kMaxUpdateBatch];
+    int len, margin;
+};
+hipError_t launch_scaling_update_batch(const UpdateBatch& b, int n, hipStream_t stream);
 hipError_t launch_scaling_update(float* hist, float* scale, float* scale_inv, int len,
                                  int n_slots, int margin, float fp8_max, hipStream_t stream);
 

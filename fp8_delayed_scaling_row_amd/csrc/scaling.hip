@@ -40,10 +40,9 @@ __global__ __launch_bounds__(kThreads) void meta_init_kernel(float* hist, float*
 // Element j = tid + 256 t of the flattened [len][n_slots] history belongs to
 // slot j % n_slots; when n_slots divides 256 (1, 2, 4, 8 slots) that slot is the
 // same for all of a thread's elements and one running max suffices.
-__global__ __launch_bounds__(kThreads) void scaling_update_kernel(float* hist, float* scale,
-                                                                 float* scale_inv, int len,
-                                                                 int n_slots, int margin,
-                                                                 float fp8_max) {
+__device__ __forceinline__ void scaling_update_block(float* hist, float* scale, float* scale_inv,
+                                                     int len, int n_slots, int margin,
+                                                     float fp8_max) {
     __shared__ float red_max[kThreads / kWave][kMaxSlots];
     __shared__ int red_nan[kThreads / kWave][kMaxSlots];
     const int tid = threadIdx.x;
@@ -119,7 +118,28 @@ __global__ __launch_bounds__(kThreads) void scaling_update_kernel(float* hist, f
     if (tid < n_slots) hist[tid] = 0.0f;
 }
 
+__global__ __launch_bounds__(kThreads) void scaling_update_kernel(float* hist, float* scale,
+                                                                 float* scale_inv, int len,
+                                                                 int n_slots, int margin,
+                                                                 float fp8_max) {
+    scaling_update_block(hist, scale, scale_inv, len, n_slots, margin, fp8_max);
+}
+
+// Many state blocks in one launch, one workgroup each (the same work as one
+// scaling_update_kernel per block).
+__global__ __launch_bounds__(kThreads) void scaling_update_batch_kernel(UpdateBatch b) {
+    const UpdateJob& j = b.job[blockIdx.x];
+    scaling_update_block(j.hist, j.scale, j.scale_inv, b.len, j.n_slots, b.margin, j.fp8_max);
+}
+
 }  // namespace
+
+hipError_t launch_scaling_update_batch(const UpdateBatch& b, int n, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    if (n > kMaxUpdateBatch) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(scaling_update_batch_kernel, dim3(n), dim3(kThreads), 0, stream, b);
+    return hipGetLastError();
+}
 
 hipError_t launch_meta_init(float* hist, float* scale, float* scale_inv, int len, int n_slots,
                             hipStream_t stream) {

@@ -205,6 +205,13 @@ def scaling_update(recipe: Recipe, meta: Meta, stream=None) -> None:
     check(lib().fp8ln_scaling_update(C.byref(r), C.byref(m), _stream(stream)))
 
 
+def scaling_update_batch(recipe: Recipe, metas, stream=None) -> None:
+    """scaling_update of every state block in metas, in one launch per 64."""
+    arr = (_abi.MetaStruct * len(metas))(*[m.as_c() for m in metas])
+    check(lib().fp8ln_scaling_update_batch(C.byref(recipe.as_c()), arr, len(metas),
+                                           _stream(stream)))
+
+
 # ---- kernels ------------------------------------------------------------------
 
 def ln_cast_amax(recipe: Recipe, x, gamma, beta, fp8_dtype: int, scale, amax_ptr: int, out,

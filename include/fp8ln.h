@@ -212,6 +212,14 @@ int fp8ln_meta_init(const fp8ln_recipe* recipe, const fp8ln_meta* meta, void* st
  * amaxes into row 0.  fp8_max is 448 for E4M3 slots and 57344 for E5M2 slots. */
 int fp8ln_scaling_update(const fp8ln_recipe* recipe, const fp8ln_meta* meta, void* stream);
 
+/* fp8ln_scaling_update for n state blocks of one recipe (a host array of n
+ * fp8ln_meta; each block keeps its own kind and slot count), with the same
+ * results, in one launch per 64 blocks: a model updates every module's forward
+ * and backward state at the start of its step (the recipe's update touches only
+ * a block's own history, so its order among the blocks does not matter). */
+int fp8ln_scaling_update_batch(const fp8ln_recipe* recipe, const fp8ln_meta* metas, int32_t n,
+                               void* stream);
+
 /* ---- fused LayerNorm + FP8 cast + amax ([T] setup listing, LayerNormLinear;
  *      [G] "The building blocks") ------------------------------------------ */
 

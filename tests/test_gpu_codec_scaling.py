@@ -148,3 +148,39 @@ def test_scaling_update_bit_exact(L, n, kind, fmt, margin):
             new[0] = np.float32(3e-39)      # scale overflows: kept
         m.history[0].copy_(torch.from_numpy(new))
         om.history[0] = new
+
+
+@pytest.mark.parametrize("fmt,L,margin", [(ops.FORMAT_HYBRID, 1024, 0), (ops.FORMAT_E4M3, 16, 1)])
+def test_scaling_update_batch_equals_one_by_one(fmt, L, margin):
+    """70 state blocks of mixed kinds and slot counts (two launches of the batch)
+    updated together and one at a time: identical histories, scales and scale_inv
+    over four steps, with zero columns, inf, NaN and subnormal amaxes in them."""
+    r = ops.Recipe(format=fmt, amax_history_len=L, margin=margin)
+    shapes = [(1 + k % 4, k % 2) for k in range(70)]    # (slots, kind)
+    one = [ops.Meta(r, n, kind) for n, kind in shapes]
+    many = [ops.Meta(r, n, kind) for n, kind in shapes]
+    rng = np.random.default_rng(L + margin)
+    for k, ((n, _), a, b) in enumerate(zip(shapes, one, many)):
+        hist = inputs.random_history(L, n, inputs.seed_for("batch", f"{k}")).numpy()
+        if k % 5 == 0:
+            hist[:, 0] = 0.0
+        if k % 7 == 1:
+            hist[L // 2, n - 1] = np.inf
+        if k % 11 == 2:
+            hist[L - 1, 0] = np.nan
+        if k % 13 == 3:
+            hist[0, n - 1] = 1e-40
+        a.history.copy_(torch.from_numpy(hist))
+        b.history.copy_(torch.from_numpy(hist))
+    for step in range(4):
+        for m in one:
+            ops.scaling_update(r, m)
+        ops.scaling_update_batch(r, many)
+        torch.cuda.synchronize()
+        for k, (a, b) in enumerate(zip(one, many)):
+            for x, y in ((a.history, b.history), (a.scale, b.scale), (a.scale_inv, b.scale_inv)):
+                assert torch.equal(x.view(torch.int32), y.view(torch.int32)), f"step {step} block {k}"
+        for (n, _), a, b in zip(shapes, one, many):
+            new = torch.from_numpy(np.exp2(rng.uniform(-12, 12, size=n)).astype(np.float32))
+            a.history[0].copy_(new)
+            b.history[0].copy_(new)
