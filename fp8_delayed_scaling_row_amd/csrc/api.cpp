@@ -458,7 +458,7 @@ int fp8ln_ln_cast_amax(const fp8ln_recipe* recipe, int64_t rows, int64_t hidden,
         return fail(FP8LN_ERR_UNSUPPORTED, "hidden %lld must be a multiple of 8 in 8..8192",
                     (long long)hidden);
     if (out_t && (rows % 16 != 0 || hidden % 16 != 0))
-        return fail(FP8LN_ERR_UNSUPPORTED, "a transposed output needs rows and hidden % 16 == 0");
+        return fail(FP8LN_ERR_UNSUPPORTED, "a transposed output needs rows and hidden %% 16 == 0");
     REQUIRE_PTR(gamma); REQUIRE_PTR(beta); REQUIRE_PTR(scale); REQUIRE_PTR(amax);
     REQUIRE_ALIGNED(gamma); REQUIRE_ALIGNED(beta);
     if (rows > 0) {

@@ -38,6 +38,7 @@
 
 #include "device_common.hpp"
 #include "launchers.hpp"
+#include "step_update.hpp"
 
 namespace fp8ln {
 
@@ -139,29 +140,6 @@ __device__ __forceinline__ void lds_st(lds8* a, T v) {
 template <class T>
 __device__ __forceinline__ T lds_ld(const lds8* a) {
     return *reinterpret_cast<const __attribute__((address_space(3))) T*>(a);
-}
-
-// The history roll of a folded scaling update (GemmParams::roll_*), by one
-// workgroup: every value is read into registers before any is written.
-__device__ __forceinline__ void roll_history(float* hist, uint32_t* ws, int len, int n) {
-    constexpr int kPer = 32;   // len * n <= 1024 * 8 values over at least 256 threads
-    const int t = threadIdx.x, nt = blockDim.x, moved = (len - 1) * n;
-    float keep[kPer];
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-        const int j = t + k * nt;
-        keep[k] = j < moved ? hist[j] : 0.0f;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-        const int j = t + k * nt;
-        if (j < moved) hist[j + n] = keep[k];
-    }
-    if (t < n) {
-        hist[t] = __uint_as_float(ws[t]);
-        ws[t] = 0u;
-    }
 }
 
 // Smallest power of two P such that a stage of STAGE bytes holds a multiple of 32

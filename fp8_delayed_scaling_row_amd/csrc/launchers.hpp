@@ -66,10 +66,11 @@ struct CastJob {
 };
 // The step-start scaling update folded into the prologue (upd non-null): every
 // workgroup forms its own slot's scale from the history window (the update's
-// arithmetic), records its amax into ws instead of the history, and the last
-// workgroup to finish rolls the history with row 0 = the recorded amaxes (0 for
-// slots this launch does not cast) and writes every slot's scale and scale_inv.
-// ws: kStepWsWords words, zero on entry, zero again when the launch ends.
+// arithmetic) and records its amax into ws instead of the history; workgroup 0
+// writes every slot's scale and scale_inv, and the first workgroup of the
+// forward's last GEMM rolls the history with row 0 = the recorded amaxes (0 for
+// slots the step does not cast) and clears ws.
+// ws: kStepWsWords words, zero on entry, zero again when the step ends.
 constexpr int kStepWsWords = 16;
 constexpr int kMaxMetaSlots = 8;
 struct FusedUpdate {
@@ -78,7 +79,7 @@ struct FusedUpdate {
     float* scale_inv;   // [n_slots]
     int len, n_slots, margin;
     float fp8_max;
-    uint32_t* ws;       // [0, n_slots): amax bits per slot, [kStepWsWords - 1]: counter
+    uint32_t* ws;       // [0, n_slots): amax bits per slot
     int ln_slot;
     int cast_slot[kMaxPrologueCasts];
 };

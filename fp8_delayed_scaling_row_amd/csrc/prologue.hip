@@ -12,6 +12,7 @@
 #include "device_common.hpp"
 #include "launchers.hpp"
 #include "ln_fwd_body.hpp"
+#include "step_update.hpp"
 
 namespace fp8ln {
 
@@ -39,55 +40,6 @@ struct ProloguePack {
     FusedUpdate upd;
 };
 
-// The update's scales of every slot from the history window (fmaxf max, a NaN
-// flagged apart), as fp8ln's scaling update forms them: sh[2 q] = scale of slot
-// q, sh[2 q + 1] = 1 / scale.  Thread t reads entries t, t + 512, ... of the
-// flattened [len][n_slots] history; n_slots divides 512, so all of a thread's
-// entries belong to slot t % n_slots, and lanes of one slot meet in a butterfly
-// over the lane bits at and above n_slots.  Workgroup 0 also writes the scales
-// into the state block: every workgroup computes the same values, and a
-// workgroup that reads a slot's old scale after the write gets the same result
-// (the old scale enters only where it is kept), so the write needs no ordering.
-__device__ __forceinline__ void window_scales(const FusedUpdate& u, float* sh) {
-    __shared__ float wmax[kThreads / kWave][kMaxMetaSlots];
-    __shared__ int wnan[kThreads / kWave][kMaxMetaSlots];
-    const int n = u.n_slots, total = u.len * n;
-    float m = 0.0f;
-    int nan = 0;
-    for (int j = threadIdx.x; j < total; j += kThreads) {
-        const float v = u.hist[j];
-        m = fmaxf(m, v);
-        nan |= v != v;
-    }
-    for (int off = n; off < kWave; off <<= 1) {   // n is a power of two
-        m = fmaxf(m, __shfl_xor(m, off, kWave));
-        nan |= __shfl_xor(nan, off, kWave);
-    }
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    if (lane < n) {
-        wmax[wave][lane] = m;
-        wnan[wave][lane] = nan;
-    }
-    __syncthreads();
-    if (threadIdx.x < n) {
-        const int q = threadIdx.x;
-        float a = 0.0f;
-        int any = 0;
-        for (int w = 0; w < kThreads / kWave; ++w) {
-            a = fmaxf(a, wmax[w][q]);
-            any |= wnan[w][q];
-        }
-        const float sc = delayed_scale(a, any != 0, u.scale[q], u.fp8_max, u.margin);
-        sh[2 * q] = sc;
-        sh[2 * q + 1] = 1.0f / sc;
-        if (blockIdx.x == 0) {
-            u.scale[q] = sc;
-            u.scale_inv[q] = 1.0f / sc;
-        }
-    }
-    __syncthreads();
-}
-
 // Workgroups [0, ln_blocks) normalise rows; the following cast_blocks[0]
 // workgroups cast the first weight, then the second.
 template <int CPL, int FMT, bool FULL, bool FUSED>
@@ -96,7 +48,7 @@ __global__ __launch_bounds__(kThreads) void fwd_prologue_kernel(ProloguePack p) 
     // rows are in flight (the amaxes go to ws; the forward's last GEMM rolls
     // the history)
     __shared__ float sh[2 * kMaxMetaSlots];
-    auto pre = [&]() { window_scales(p.upd, sh); };
+    auto pre = [&]() { window_scales<kThreads>(p.upd, sh); };
     int b = blockIdx.x;
     if (b < p.ln_blocks) {
         if constexpr (FUSED) {
