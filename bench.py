@@ -514,11 +514,12 @@ def bench_linear_bwd(torch, ops, inputs, steps, warmup, M=2048, K=768, N=2304):
     ws = torch.empty(ops.workspace_size(ops.OP_LN_LINEAR_BWD, M, K, N), dtype=torch.uint8, device="cuda")
     ops.scaling_update(recipe, mf)
     ops.ln_linear_fwd(recipe, x, g, b, w, None, out, mf, ctx)
+    step_ws = ops.step_workspace()
 
     def step(s):
-        ops.scaling_update(recipe, mb)
-        ops.ln_linear_bwd(recipe, dys[s % 4], x, g, ctx, mf, mb, dx, dgamma, dbeta, dw, dbias,
-                          workspace=ws)
+        # the backward state's scaling update folded into the gradient cast
+        ops.ln_linear_bwd_step(recipe, dys[s % 4], x, g, ctx, mf, mb, dx, dgamma, dbeta, dw,
+                               step_ws, dbias, workspace=ws)
 
     t = _time_steps(torch, step, steps, warmup, unroll=4)
     flops = 2 * 2.0 * M * N * K

@@ -122,6 +122,9 @@ SIGNATURES = {
     "fp8ln_ln_linear_bwd": (C.c_int, [_RP, _I64, _I64, _I64, _I32, _P, _P, _P,
                                       C.POINTER(LinearCtxStruct), _MP, _MP, _P, _P, _P, _P, _P,
                                       _P, _SZ, _P]),
+    "fp8ln_ln_linear_bwd_step": (C.c_int, [_RP, _I64, _I64, _I64, _I32, _P, _P, _P,
+                                           C.POINTER(LinearCtxStruct), _MP, _MP, _P, _P, _P, _P,
+                                           _P, _P, _SZ, _P, _P]),
     "fp8ln_ln_linear_bwd_noalloc": (C.c_int, [_RP, _I64, _I64, _I64, _I32, _P, _P, _P,
                                               C.POINTER(LinearCtxStruct), _MP, _MP, _P, _P, _P,
                                               _P, _P, _P]),
@@ -132,6 +135,9 @@ SIGNATURES = {
     "fp8ln_ln_mlp_bwd": (C.c_int, [_RP, _I64, _I64, _I64, _I32, _P, _P, _P,
                                    C.POINTER(MlpCtxStruct), _MP, _MP, _P, _P, _P, _P, _P, _P, _P,
                                    _P, _SZ, _P]),
+    "fp8ln_ln_mlp_bwd_step": (C.c_int, [_RP, _I64, _I64, _I64, _I32, _P, _P, _P,
+                                        C.POINTER(MlpCtxStruct), _MP, _MP, _P, _P, _P, _P, _P,
+                                        _P, _P, _P, _SZ, _P, _P]),
 }
 
 _lib = None

@@ -1254,12 +1254,35 @@ int fp8ln_ln_linear_fwd_step(const fp8ln_recipe* recipe, int64_t tokens, int64_t
                               beta, weight, bias, out, fwd, ctx, step_ws, stream);
 }
 
-int fp8ln_ln_linear_bwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_features,
-                        int64_t out_features, int32_t params_dtype, const void* dy,
-                        const void* x, const void* gamma, const fp8ln_linear_ctx* ctx,
-                        const fp8ln_meta* fwd, const fp8ln_meta* bwd, void* dx,
-                        float* dgamma, float* dbeta, float* dweight, float* dbias,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The step-start scaling update of a backward state block folded into the
+// gradient cast, or nothing to fold (nullopt-like: ok false).
+struct BwdFold {
+    bool ok;
+    FusedUpdate upd;
+};
+
+BwdFold bwd_fold(const fp8ln_recipe* recipe, const fp8ln_meta* bwd, int bf, void* step_ws,
+                 int64_t M) {
+    BwdFold f{false, FusedUpdate{bwd->amax_history, bwd->scale, bwd->scale_inv,
+                                 recipe->amax_history_len, bwd->n_slots, recipe->margin,
+                                 fp8_max_of(bf), (uint32_t*)step_ws, 0, {0, 0}}};
+    const int n = bwd->n_slots;
+    f.ok = step_ws && M > 0 && (n & (n - 1)) == 0;
+    return f;
+}
+
+// LayerNormLinear backward; with step_ws, the step-start scaling update of the
+// backward state comes first (folded into the gradient cast where it can be).
+int ln_linear_bwd_impl(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_features,
+                       int64_t out_features, int32_t params_dtype, const void* dy,
+                       const void* x, const void* gamma, const fp8ln_linear_ctx* ctx,
+                       const fp8ln_meta* fwd, const fp8ln_meta* bwd, void* dx, float* dgamma,
+                       float* dbeta, float* dweight, float* dbias, void* workspace,
+                       size_t workspace_bytes, void* step_ws, void* stream) {
     int s = check_recipe(recipe);
     if (s) return s;
     const int64_t M = tokens, K = in_features, N = out_features;
@@ -1290,15 +1313,28 @@ int fp8ln_ln_linear_bwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_f
     REQUIRE_ALIGNED(workspace);
     CHECK(check_gemm_size(M, K, N, 1, false, "ln_linear_bwd dgrad"));
     CHECK(check_gemm_size(N, K, M, 1, false, "ln_linear_bwd wgrad"));
+    if (step_ws) REQUIRE_ALIGNED(step_ws);
     if ((s = check_current_device())) return s;
     hipStream_t st = as_stream(stream);
     const LinearWs w = linear_ws(workspace, M, K, N);
     const int ff = meta_fp8(recipe, FP8LN_META_FORWARD);
     const int bf = meta_fp8(recipe, FP8LN_META_BACKWARD);
+    SumBatch sums;   // dbias, dgamma / dbeta: one launch at the end
+    const BwdFold fold = bwd_fold(recipe, bwd, bf, step_ws, M);
 
-    FP8LN_TRY(launch_cast_amax(M, N, false, dy, bf, bwd->scale + 0, bwd->amax_history + 0, w.dy_q,
-                               w.dy_qt, dbias, w.cast_ws, st),
-              "grad cast launch");
+    if (step_ws && !fold.ok)
+        FP8LN_TRY(launch_scaling_update(bwd->amax_history, bwd->scale, bwd->scale_inv,
+                                        recipe->amax_history_len, bwd->n_slots, recipe->margin,
+                                        fp8_max_of(bf), st),
+                  "scaling_update launch");
+    if (fold.ok)
+        FP8LN_TRY(launch_cast_amax_step(M, N, dy, bf, fold.upd, w.dy_q, w.dy_qt, dbias, w.cast_ws,
+                                        &sums, st),
+                  "grad cast launch");
+    else
+        FP8LN_TRY(launch_cast_amax(M, N, false, dy, bf, bwd->scale + 0, bwd->amax_history + 0,
+                                   w.dy_q, w.dy_qt, dbias, w.cast_ws, st, nullptr, nullptr, &sums),
+                  "grad cast launch");
     // dgrad: dLN[M][K] = dy_q[M][N] . (w_qt[K][N])^T
     GemmParams dg = gemm_params(M, K, N, w.dy_q, bf, ctx->w_qt, ff, bwd->scale_inv + 0,
                                 ctx->w_scale_inv ? ctx->w_scale_inv : fwd->scale_inv + 1,
@@ -1312,9 +1348,44 @@ int fp8ln_ln_linear_bwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_f
     const GemmParams grads[2] = {dg, wg};
     FP8LN_TRY(launch_gemm_group(grads, 2, st), "dgrad / wgrad launch");
     FP8LN_TRY(launch_ln_bwd(M, (int)K, w.dln, false, x, ctx->mean, ctx->rstd, gamma, dx, dgamma, dbeta,
-                            w.ln_ws, st),
+                            w.ln_ws, st, &sums),
               "layernorm_bwd launch");
+    if (fold.ok) {   // the folded update's roll, once the cast's window reads are done
+        sums.roll_hist = bwd->amax_history;
+        sums.roll_ws = (uint32_t*)step_ws;
+        sums.roll_len = recipe->amax_history_len;
+        sums.roll_slots = bwd->n_slots;
+    }
+    FP8LN_TRY(launch_sum_batch(sums, st), "column sums launch");
     return FP8LN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8ln_ln_linear_bwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_features,
+                        int64_t out_features, int32_t params_dtype, const void* dy,
+                        const void* x, const void* gamma, const fp8ln_linear_ctx* ctx,
+                        const fp8ln_meta* fwd, const fp8ln_meta* bwd, void* dx,
+                        float* dgamma, float* dbeta, float* dweight, float* dbias,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    return ln_linear_bwd_impl(recipe, tokens, in_features, out_features, params_dtype, dy, x,
+                              gamma, ctx, fwd, bwd, dx, dgamma, dbeta, dweight, dbias, workspace,
+                              workspace_bytes, nullptr, stream);
+}
+
+int fp8ln_ln_linear_bwd_step(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_features,
+                             int64_t out_features, int32_t params_dtype, const void* dy,
+                             const void* x, const void* gamma, const fp8ln_linear_ctx* ctx,
+                             const fp8ln_meta* fwd, const fp8ln_meta* bwd, void* dx,
+                             float* dgamma, float* dbeta, float* dweight, float* dbias,
+                             void* workspace, size_t workspace_bytes, void* step_ws,
+                             void* stream) {
+    REQUIRE_PTR(step_ws);
+    return ln_linear_bwd_impl(recipe, tokens, in_features, out_features, params_dtype, dy, x,
+                              gamma, ctx, fwd, bwd, dx, dgamma, dbeta, dweight, dbias, workspace,
+                              workspace_bytes, step_ws, stream);
 }
 
 // LayerNormMLP forward; with step_ws, the step-start scaling update of the
@@ -1459,11 +1530,19 @@ int fp8ln_ln_mlp_fwd_step(const fp8ln_recipe* recipe, int64_t tokens, int64_t hi
                            b2, out, fwd, ctx, step_ws, stream);
 }
 
-int fp8ln_ln_mlp_bwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t hidden, int64_t ffn,
-                     int32_t params_dtype, const void* dy, const void* x, const void* gamma,
-                     const fp8ln_mlp_ctx* ctx, const fp8ln_meta* fwd, const fp8ln_meta* bwd,
-                     void* dx, float* dgamma, float* dbeta, float* dw1, float* db1, float* dw2,
-                     float* db2, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// LayerNormMLP backward; with step_ws, the step-start scaling update of the
+// backward state comes first (folded into the gradient cast where it can be; the
+// fc1 gradient's amax is then recorded with the cast's).
+int ln_mlp_bwd_impl(const fp8ln_recipe* recipe, int64_t tokens, int64_t hidden, int64_t ffn,
+                    int32_t params_dtype, const void* dy, const void* x, const void* gamma,
+                    const fp8ln_mlp_ctx* ctx, const fp8ln_meta* fwd, const fp8ln_meta* bwd,
+                    void* dx, float* dgamma, float* dbeta, float* dw1, float* db1, float* dw2,
+                    float* db2, void* workspace, size_t workspace_bytes, void* step_ws,
+                    void* stream) {
     int s = check_recipe(recipe);
     if (s) return s;
     const int64_t M = tokens, H = hidden, F = ffn;
@@ -1498,15 +1577,28 @@ int fp8ln_ln_mlp_bwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t hidden,
     CHECK(check_gemm_size(M, F, H, 1, true, "ln_mlp_bwd fc2 dgrad"));
     CHECK(check_gemm_size(H, F, M, 1, false, "ln_mlp_bwd wgrad"));
     CHECK(check_gemm_size(M, H, F, 1, false, "ln_mlp_bwd fc1 dgrad"));
+    if (step_ws) REQUIRE_ALIGNED(step_ws);
     if ((s = check_current_device())) return s;
     hipStream_t st = as_stream(stream);
     const MlpWs w = mlp_ws(workspace, M, H, F);
     const int ff = meta_fp8(recipe, FP8LN_META_FORWARD);
     const int bf = meta_fp8(recipe, FP8LN_META_BACKWARD);
+    SumBatch sums;   // db2, db1, dgamma / dbeta: one launch at the end
+    const BwdFold fold = bwd_fold(recipe, bwd, bf, step_ws, M);
 
-    FP8LN_TRY(launch_cast_amax(M, H, false, dy, bf, bwd->scale + 0, bwd->amax_history + 0, w.dy_q,
-                               w.dy_qt, db2, w.cast_ws, st),
-              "fc2 grad cast launch");
+    if (step_ws && !fold.ok)
+        FP8LN_TRY(launch_scaling_update(bwd->amax_history, bwd->scale, bwd->scale_inv,
+                                        recipe->amax_history_len, bwd->n_slots, recipe->margin,
+                                        fp8_max_of(bf), st),
+                  "scaling_update launch");
+    if (fold.ok)
+        FP8LN_TRY(launch_cast_amax_step(M, H, dy, bf, fold.upd, w.dy_q, w.dy_qt, db2, w.cast_ws,
+                                        &sums, st),
+                  "fc2 grad cast launch");
+    else
+        FP8LN_TRY(launch_cast_amax(M, H, false, dy, bf, bwd->scale + 0, bwd->amax_history + 0,
+                                   w.dy_q, w.dy_qt, db2, w.cast_ws, st, nullptr, nullptr, &sums),
+                  "fc2 grad cast launch");
     // fc2 dgrad with the GELU derivative and the fc1 gradient cast fused:
     // dH[M][F] = dy_q[M][H] . (w2_qt[F][H])^T * gelu'(h) -> dh_q, dh_qt, amax, db1
     GemmParams dg2 = gemm_params(M, F, H, w.dy_q, bf, ctx->w2_qt, ff, bwd->scale_inv + 0,
@@ -1516,15 +1608,15 @@ int fp8ln_ln_mlp_bwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t hidden,
     dg2.q_out = w.dh_q;
     dg2.q_out_t = w.dh_qt;
     dg2.q_scale = bwd->scale + 1;
-    dg2.q_amax = bwd->amax_history + 1;
+    // folded update: the history is rolled after the last kernel, so the amax goes
+    // to the step workspace as the cast's does
+    dg2.q_amax = fold.ok ? (float*)((uint32_t*)step_ws + 1) : bwd->amax_history + 1;
     dg2.q_fp8 = bf;
     dg2.col_partial = db1 ? w.dh_part : nullptr;
     dg2.gelu_erf = recipe->activation == FP8LN_GELU_ERF;
     FP8LN_TRY(launch_gemm(dg2, st), "fc2 dgrad launch");
-    if (db1)
-        FP8LN_TRY(launch_sum_partials(w.dh_part, M > 0 ? gemm_partial_rows(M, F, H) : 0, F, db1,
-                                      nullptr, F, st),
-                  "db1 launch");
+    if (db1 && !sums.add(w.dh_part, M > 0 ? gemm_partial_rows(M, F, H) : 0, F, db1, nullptr, F))
+        return fail(FP8LN_ERR_INVALID_ARG, "internal: column sum batch full");
     // fc2 wgrad: dW2[H][F] = dy_qt[H][M] . (g_qt[F][M])^T
     GemmParams wg2 = gemm_params(H, F, M, w.dy_qt, bf, ctx->g_qt, ff, bwd->scale_inv + 0,
                                  fwd->scale_inv + 2, kEpiF32);
@@ -1542,9 +1634,42 @@ int fp8ln_ln_mlp_bwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t hidden,
     const GemmParams grads[3] = {wg2, dg1, wg1};
     FP8LN_TRY(launch_gemm_group(grads, 3, st), "fc2 wgrad / fc1 dgrad / fc1 wgrad launch");
     FP8LN_TRY(launch_ln_bwd(M, (int)H, w.dln, false, x, ctx->mean, ctx->rstd, gamma, dx, dgamma, dbeta,
-                            w.ln_ws, st),
+                            w.ln_ws, st, &sums),
               "layernorm_bwd launch");
+    if (fold.ok) {   // the folded update's roll, once the cast's window reads are done
+        sums.roll_hist = bwd->amax_history;
+        sums.roll_ws = (uint32_t*)step_ws;
+        sums.roll_len = recipe->amax_history_len;
+        sums.roll_slots = bwd->n_slots;
+    }
+    FP8LN_TRY(launch_sum_batch(sums, st), "column sums launch");
     return FP8LN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8ln_ln_mlp_bwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t hidden, int64_t ffn,
+                     int32_t params_dtype, const void* dy, const void* x, const void* gamma,
+                     const fp8ln_mlp_ctx* ctx, const fp8ln_meta* fwd, const fp8ln_meta* bwd,
+                     void* dx, float* dgamma, float* dbeta, float* dw1, float* db1, float* dw2,
+                     float* db2, void* workspace, size_t workspace_bytes, void* stream) {
+    return ln_mlp_bwd_impl(recipe, tokens, hidden, ffn, params_dtype, dy, x, gamma, ctx, fwd, bwd,
+                           dx, dgamma, dbeta, dw1, db1, dw2, db2, workspace, workspace_bytes,
+                           nullptr, stream);
+}
+
+int fp8ln_ln_mlp_bwd_step(const fp8ln_recipe* recipe, int64_t tokens, int64_t hidden,
+                          int64_t ffn, int32_t params_dtype, const void* dy, const void* x,
+                          const void* gamma, const fp8ln_mlp_ctx* ctx, const fp8ln_meta* fwd,
+                          const fp8ln_meta* bwd, void* dx, float* dgamma, float* dbeta,
+                          float* dw1, float* db1, float* dw2, float* db2, void* workspace,
+                          size_t workspace_bytes, void* step_ws, void* stream) {
+    REQUIRE_PTR(step_ws);
+    return ln_mlp_bwd_impl(recipe, tokens, hidden, ffn, params_dtype, dy, x, gamma, ctx, fwd, bwd,
+                           dx, dgamma, dbeta, dw1, db1, dw2, db2, workspace, workspace_bytes,
+                           step_ws, stream);
 }
 
 }  // extern "C"

@@ -14,6 +14,7 @@
 #include "cast_body.hpp"
 #include "device_common.hpp"
 #include "launchers.hpp"
+#include "step_update.hpp"
 
 namespace fp8ln {
 
@@ -30,6 +31,22 @@ __global__ __launch_bounds__(NT) void cast_tile_kernel(
     float* __restrict__ partial, const float* __restrict__ copy_src, float* __restrict__ copy_dst) {
     cast_tiles<IN_F32, FMT, NT>(in, rows, cols, scale_ptr, amax_ptr, out, out_t, partial, copy_src,
                                 copy_dst, blockIdx.x, gridDim.x);
+}
+
+// The cast with the step's scaling update folded in (bf16 input): every
+// workgroup forms the scales from the history window while its first tile is in
+// flight, casts with slot u.cast_slot[0]'s and records its amax into u.ws; the
+// history is rolled by a later launch of the step.
+template <int FMT, int NT>
+__global__ __launch_bounds__(NT) void cast_tile_step_kernel(
+    const void* __restrict__ in, int64_t rows, int64_t cols, FusedUpdate u,
+    uint8_t* __restrict__ out, uint8_t* __restrict__ out_t, float* __restrict__ partial) {
+    __shared__ float sh[2 * kMaxMetaSlots];
+    const int q = u.cast_slot[0];
+    cast_tiles<false, FMT, NT, true>(in, rows, cols, sh + 2 * q,
+                                     reinterpret_cast<float*>(u.ws + q), out, out_t, partial,
+                                     nullptr, nullptr, blockIdx.x, gridDim.x,
+                                     [&]() { window_scales<NT>(u, sh); });
 }
 
 // in [rows][cols] -> out [cols][rows], 64 x 64 byte tiles (cols % 16 == 0,
@@ -162,6 +179,29 @@ hipError_t launch_cast_typed(int64_t rows, int64_t cols, const void* in, const f
     return hipGetLastError();
 }
 
+template <int FMT>
+hipError_t launch_cast_step_typed(int64_t rows, int64_t cols, const void* in,
+                                  const FusedUpdate& u, uint8_t* out, uint8_t* out_t,
+                                  float* partial, hipStream_t stream) {
+    static int resident = 0, resident_wide = 0;
+    int cus = 0;
+    hipError_t e = resident_blocks(cast_tile_step_kernel<FMT, 256>, 256, resident, &cus);
+    if (e != hipSuccess) return e;
+    e = resident_blocks(cast_tile_step_kernel<FMT, 512>, 512, resident_wide);
+    if (e != hipSuccess) return e;
+    const int64_t tiles = ((cols + kCT - 1) / kCT) * ((rows + kCT - 1) / kCT);
+    if (tiles <= 2 * (int64_t)cus) {   // as launch_cast_typed
+        const unsigned blocks = (unsigned)(tiles < resident_wide ? tiles : resident_wide);
+        hipLaunchKernelGGL((cast_tile_step_kernel<FMT, 512>), dim3(blocks), dim3(512), 0, stream,
+                           in, rows, cols, u, out, out_t, partial);
+    } else {
+        const unsigned blocks = (unsigned)(tiles < resident ? tiles : resident);
+        hipLaunchKernelGGL((cast_tile_step_kernel<FMT, 256>), dim3(blocks), dim3(256), 0, stream,
+                           in, rows, cols, u, out, out_t, partial);
+    }
+    return hipGetLastError();
+}
+
 template <bool IN_F32>
 hipError_t launch_cast_fmt(int64_t rows, int64_t cols, const void* in, int fp8,
                            const float* scale, float* amax, uint8_t* out, uint8_t* out_t,
@@ -180,10 +220,22 @@ size_t cast_workspace(int64_t rows, int64_t cols) {
     return (size_t)((rows + kCT - 1) / kCT) * (size_t)cols * sizeof(float);
 }
 
+namespace {
+
+// The second stage of the column sums: added to `sums` when given, else launched.
+hipError_t cast_colsums(const float* partial, int64_t rows, int64_t cols, float* colsum,
+                        SumBatch* sums, hipStream_t stream) {
+    const int64_t nrows = (rows + kCT - 1) / kCT;
+    if (sums && sums->add(partial, nrows, cols, colsum, nullptr, cols)) return hipSuccess;
+    return launch_sum_partials(partial, nrows, cols, colsum, nullptr, cols, stream);
+}
+
+}  // namespace
+
 hipError_t launch_cast_amax(int64_t rows, int64_t cols, bool in_f32, const void* in, int fp8,
                             const float* scale, float* amax, uint8_t* out, uint8_t* out_t,
                             float* colsum, void* workspace, hipStream_t stream,
-                            const float* copy_src, float* copy_dst) {
+                            const float* copy_src, float* copy_dst, SumBatch* sums) {
     if (cols == 0) return hipSuccess;
     float* partial = colsum ? (float*)workspace : nullptr;
     if (rows > 0) {
@@ -194,8 +246,23 @@ hipError_t launch_cast_amax(int64_t rows, int64_t cols, bool in_f32, const void*
         if (e != hipSuccess) return e;
     }
     if (!colsum) return hipSuccess;
-    return launch_sum_partials(partial, (rows + kCT - 1) / kCT, cols, colsum, nullptr, cols,
-                               stream);
+    return cast_colsums(partial, rows, cols, colsum, sums, stream);
+}
+
+hipError_t launch_cast_amax_step(int64_t rows, int64_t cols, const void* in, int fp8,
+                                 const FusedUpdate& u, uint8_t* out, uint8_t* out_t,
+                                 float* colsum, void* workspace, SumBatch* sums,
+                                 hipStream_t stream) {
+    const int n = u.n_slots, q = u.cast_slot[0];
+    if (rows <= 0 || cols <= 0 || u.len < 1 || u.len > 1024 || n < 1 || n > kMaxMetaSlots ||
+        (n & (n - 1)) || q < 0 || q >= n)
+        return hipErrorInvalidValue;
+    float* partial = colsum ? (float*)workspace : nullptr;
+    hipError_t e = fp8 == kE4M3
+        ? launch_cast_step_typed<kE4M3>(rows, cols, in, u, out, out_t, partial, stream)
+        : launch_cast_step_typed<kE5M2>(rows, cols, in, u, out, out_t, partial, stream);
+    if (e != hipSuccess || !colsum) return e;
+    return cast_colsums(partial, rows, cols, colsum, sums, stream);
 }
 
 hipError_t launch_transpose_u8(int64_t rows, int64_t cols, const uint8_t* in, uint8_t* out,

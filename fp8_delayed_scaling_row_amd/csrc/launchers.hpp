@@ -44,9 +44,11 @@ hipError_t launch_ln_cast_amax(int64_t rows, int hidden, const void* x, const vo
                                float* amax, void* out, float* mean, float* rstd,
                                hipStream_t stream);
 size_t ln_bwd_workspace(int64_t rows, int hidden);
+struct SumBatch;
 hipError_t launch_ln_bwd(int64_t rows, int hidden, const void* dy, bool dy_bf16, const void* x,
                          const float* mean, const float* rstd, const void* gamma, void* dx,
-                         float* dgamma, float* dbeta, void* workspace, hipStream_t stream);
+                         float* dgamma, float* dbeta, void* workspace, hipStream_t stream,
+                         SumBatch* sums = nullptr);
 
 // prologue.hip: the LayerNorm + cast + amax of the rows and up to two weight
 // casts (bf16 [rows][cols] -> codes, optional transposed copy, amax, scale_inv
@@ -93,14 +95,46 @@ hipError_t launch_fwd_prologue(int64_t rows, int hidden, const void* x, const vo
 size_t cast_workspace(int64_t rows, int64_t cols);
 // copy_src / copy_dst: when given, *copy_dst = *copy_src is done by the cast
 // kernel (the scale_inv that goes with the codes it writes).
+// sums: when given, the column sums are added to it instead of launched.
 hipError_t launch_cast_amax(int64_t rows, int64_t cols, bool in_f32, const void* in, int fp8,
                             const float* scale, float* amax, uint8_t* out, uint8_t* out_t,
                             float* colsum, void* workspace, hipStream_t stream,
-                            const float* copy_src = nullptr, float* copy_dst = nullptr);
+                            const float* copy_src = nullptr, float* copy_dst = nullptr,
+                            SumBatch* sums = nullptr);
+// The same cast of bf16 [rows][cols] (rows > 0) with the step's scaling update
+// folded in: every workgroup forms the scales from the history window (the cast
+// uses slot u.cast_slot[0]'s) and records the amax into u.ws; workgroup 0 writes
+// every slot's scale and scale_inv; a later launch rolls the history.
+hipError_t launch_cast_amax_step(int64_t rows, int64_t cols, const void* in, int fp8,
+                                 const FusedUpdate& u, uint8_t* out, uint8_t* out_t,
+                                 float* colsum, void* workspace, SumBatch* sums,
+                                 hipStream_t stream);
 // out[j] = sum over r < nrows of partial[r][j] in a fixed order; columns j < split
 // go to out0[j], the others to out1[j - split].
+struct SumJob {
+    const float* partial;
+    int64_t nrows, width;
+    float* out0;
+    float* out1;
+    int64_t split;
+};
 hipError_t launch_sum_partials(const float* partial, int64_t nrows, int64_t width, float* out0,
                                float* out1, int64_t split, hipStream_t stream);
+// Column sums gathered from several kernels (launchers given a SumBatch add their
+// job instead of launching it) and run as one launch, each with the order of its
+// own launch; roll_hist (optional): the folded scaling update's history roll
+// (roll_history), done by the launch's first workgroup.
+constexpr int kMaxSumJobs = 4;
+struct SumBatch {
+    SumJob job[kMaxSumJobs];
+    int n = 0;
+    float* roll_hist = nullptr;
+    uint32_t* roll_ws = nullptr;
+    int roll_len = 0, roll_slots = 0;
+    bool add(const float* partial, int64_t nrows, int64_t width, float* out0, float* out1,
+             int64_t split);   // false when full
+};
+hipError_t launch_sum_batch(const SumBatch& b, hipStream_t stream);
 hipError_t launch_transpose_u8(int64_t rows, int64_t cols, const uint8_t* in, uint8_t* out,
                                hipStream_t stream);
 hipError_t launch_encode_range(uint32_t start, int64_t count, int fp8, uint8_t* out,

@@ -138,7 +138,7 @@ template <int CPL>
 hipError_t launch_ln_bwd_cpl(int64_t rows, int hidden, const void* dy, bool dy_bf16,
                              const void* x, const float* mean, const float* rstd,
                              const void* gamma, void* dx, float* dgamma, float* dbeta,
-                             void* workspace, hipStream_t stream) {
+                             void* workspace, hipStream_t stream, SumBatch* sums) {
     const int blocks = ln_bwd_blocks(rows);
     const size_t smem = (size_t)2 * hidden * sizeof(float);
     float* partial = (float*)workspace;
@@ -152,6 +152,8 @@ hipError_t launch_ln_bwd_cpl(int64_t rows, int hidden, const void* dy, bool dy_b
                            (uint4*)dx, partial, rows, hidden);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (sums && sums->add(partial, blocks, 2 * (int64_t)hidden, dgamma, dbeta, hidden))
+        return hipSuccess;
     return launch_sum_partials(partial, blocks, 2 * (int64_t)hidden, dgamma, dbeta, hidden,
                                stream);
 }
@@ -164,19 +166,20 @@ size_t ln_bwd_workspace(int64_t rows, int hidden) {
 
 hipError_t launch_ln_bwd(int64_t rows, int hidden, const void* dy, bool dy_bf16, const void* x,
                          const float* mean, const float* rstd, const void* gamma, void* dx,
-                         float* dgamma, float* dbeta, void* workspace, hipStream_t stream) {
+                         float* dgamma, float* dbeta, void* workspace, hipStream_t stream,
+                         SumBatch* sums) {
     const int chunks = hidden / 8;
     if (chunks <= 64)
         return launch_ln_bwd_cpl<1>(rows, hidden, dy, dy_bf16, x, mean, rstd, gamma, dx, dgamma, dbeta,
-                                    workspace, stream);
+                                    workspace, stream, sums);
     if (chunks <= 128)
         return launch_ln_bwd_cpl<2>(rows, hidden, dy, dy_bf16, x, mean, rstd, gamma, dx, dgamma, dbeta,
-                                    workspace, stream);
+                                    workspace, stream, sums);
     if (chunks <= 256)
         return launch_ln_bwd_cpl<4>(rows, hidden, dy, dy_bf16, x, mean, rstd, gamma, dx, dgamma, dbeta,
-                                    workspace, stream);
+                                    workspace, stream, sums);
     return launch_ln_bwd_cpl<8>(rows, hidden, dy, dy_bf16, x, mean, rstd, gamma, dx, dgamma, dbeta,
-                                workspace, stream);
+                                workspace, stream, sums);
 }
 
 }  // namespace fp8ln

@@ -528,8 +528,8 @@ def linear_bwd(recipe: Recipe, dy, ctx: LinearCtx, fwd: Meta, bwd: Meta, dx, dwe
 
 
 def step_workspace(device="cuda"):
-    """A zeroed step workspace for ln_linear_fwd_step / ln_mlp_fwd_step (every call
-    leaves it zero again; one per stream of steps)."""
+    """A zeroed step workspace for the *_step calls (every call leaves it zero
+    again; one per stream of steps)."""
     return torch.zeros(_abi.STEP_WS_BYTES // 4, dtype=torch.int32, device=device)
 
 
@@ -580,6 +580,29 @@ def ln_linear_bwd(recipe: Recipe, dy, x, gamma, ctx: LinearCtx, fwd: Meta, bwd: 
                                     _ptr(gamma), C.byref(c), C.byref(mf), C.byref(mb), _ptr(dx),
                                     _ptr(dgamma), _ptr(dbeta), _ptr(dweight), _ptr(dbias),
                                     _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def ln_linear_bwd_step(recipe: Recipe, dy, x, gamma, ctx: LinearCtx, fwd: Meta, bwd: Meta, dx,
+                       dgamma, dbeta, dweight, step_ws, dbias=None, workspace=None,
+                       stream=None) -> None:
+    """scaling_update(recipe, bwd) then ln_linear_bwd(...), the update folded into
+    the gradient cast where it can be."""
+    M, N = dy.shape
+    K = x.shape[1]
+    _need(dy, torch.bfloat16, (M, N), "dy")
+    _need(dx, torch.bfloat16, (M, K), "dx")
+    _need(dweight, torch.float32, (N, K), "dweight")
+    _opt(dbias, torch.float32, (N,), "dbias")
+    _need(step_ws, torch.int32, (_abi.STEP_WS_BYTES // 4,), "step_ws")
+    nbytes = workspace_size(_abi.OP_LN_LINEAR_BWD, M, K, N)
+    if workspace is None:
+        workspace = _workspace(nbytes, dy.device)
+    r, mf, mb, c = recipe.as_c(), fwd.as_c(), bwd.as_c(), ctx.as_c()
+    check(lib().fp8ln_ln_linear_bwd_step(C.byref(r), M, K, N, DTYPE_BF16, _ptr(dy), _ptr(x),
+                                         _ptr(gamma), C.byref(c), C.byref(mf), C.byref(mb),
+                                         _ptr(dx), _ptr(dgamma), _ptr(dbeta), _ptr(dweight),
+                                         _ptr(dbias), _ptr(workspace), workspace.numel(),
+                                         _ptr(step_ws), _stream(stream)))
 
 
 def ln_linear_bwd_noalloc(recipe: Recipe, dy, x, gamma, ctx: LinearCtx, fwd: Meta, bwd: Meta,
@@ -653,6 +676,30 @@ def ln_mlp_bwd(recipe: Recipe, dy, x, gamma, ctx: MlpCtx, fwd: Meta, bwd: Meta, 
                                  C.byref(c), C.byref(mf), C.byref(mb), _ptr(dx), _ptr(dgamma),
                                  _ptr(dbeta), _ptr(dw1), _ptr(db1), _ptr(dw2), _ptr(db2),
                                  _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def ln_mlp_bwd_step(recipe: Recipe, dy, x, gamma, ctx: MlpCtx, fwd: Meta, bwd: Meta, dx, dgamma,
+                    dbeta, dw1, db1, dw2, db2, step_ws, workspace=None, stream=None) -> None:
+    """scaling_update(recipe, bwd) then ln_mlp_bwd(...), the update folded into the
+    gradient cast where it can be."""
+    M, H = dy.shape
+    F = ctx.w1_q.shape[0]
+    _need(dy, torch.bfloat16, (M, H), "dy")
+    _need(dx, torch.bfloat16, (M, H), "dx")
+    _need(dw1, torch.float32, (F, H), "dw1")
+    _need(dw2, torch.float32, (H, F), "dw2")
+    _opt(db1, torch.float32, (F,), "db1")
+    _opt(db2, torch.float32, (H,), "db2")
+    _need(step_ws, torch.int32, (_abi.STEP_WS_BYTES // 4,), "step_ws")
+    nbytes = workspace_size(_abi.OP_LN_MLP_BWD, M, H, F)
+    if workspace is None:
+        workspace = _workspace(nbytes, dy.device)
+    r, mf, mb, c = recipe.as_c(), fwd.as_c(), bwd.as_c(), ctx.as_c()
+    check(lib().fp8ln_ln_mlp_bwd_step(C.byref(r), M, H, F, DTYPE_BF16, _ptr(dy), _ptr(x),
+                                      _ptr(gamma), C.byref(c), C.byref(mf), C.byref(mb), _ptr(dx),
+                                      _ptr(dgamma), _ptr(dbeta), _ptr(dw1), _ptr(db1), _ptr(dw2),
+                                      _ptr(db2), _ptr(workspace), workspace.numel(),
+                                      _ptr(step_ws), _stream(stream)))
 
 
 def linear_metas(recipe: Recipe, device="cuda"):

@@ -469,7 +469,7 @@ int fp8ln_ln_linear_fwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_f
                         const void* bias, void* out, const fp8ln_meta* fwd,
                         const fp8ln_linear_ctx* ctx, void* stream);
 
-/* Bytes of the step workspace of fp8ln_ln_linear_fwd_step / fp8ln_ln_mlp_fwd_step. */
+/* Bytes of the step workspace of the *_step entry points. */
 #define FP8LN_STEP_WS_BYTES 64
 
 /* One forward step of LayerNormLinear: fp8ln_scaling_update(recipe, fwd) followed
@@ -481,9 +481,9 @@ int fp8ln_ln_linear_fwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_f
  * recipe setup: amax history, max reduction), so the update needs no launch of
  * its own: where the forward's first launch (LayerNorm rows and weight cast side
  * by side) serves the shape, each of its workgroups forms its scale from the
- * history window itself and the last one to finish rolls the history (the
- * pages' "fused" operations: fewer launches, "Turbo-charging ...", "What does
- * 'fused' really mean?").  Otherwise the update runs as its own launch first.
+ * history window itself and the GEMM's first workgroup then rolls the history
+ * (the pages' "fused" operations: fewer launches, "Turbo-charging ...", "What
+ * does 'fused' really mean?").  Otherwise the update runs as its own launch first.
  * step_ws: device buffer of FP8LN_STEP_WS_BYTES, 16-byte aligned, all zero
  * before the first call; every call leaves it zero.  Calls that share a step_ws
  * or a state block must not overlap (the same stream orders them). */
@@ -508,6 +508,26 @@ int fp8ln_ln_linear_bwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_f
                         const fp8ln_meta* fwd, const fp8ln_meta* bwd, void* dx,
                         float* dgamma, float* dbeta, float* dweight, float* dbias,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* One backward step of LayerNormLinear: fp8ln_scaling_update(recipe, bwd)
+ * followed by fp8ln_ln_linear_bwd with the same arguments, with identical results
+ * (backward history, scale, scale_inv and every output, bit for bit).  As in the
+ * forward step, the delayed recipe knows the step's gradient scale from earlier
+ * steps' amaxes alone, so the update rides in the gradient cast: each of its
+ * workgroups forms the scales from the history window, records the amax in
+ * step_ws, and the backward's last launch (its column sums) rolls the history
+ * ("Turbo-charging your transformer training", "What does 'fused' really
+ * mean?": fewer launches).  With no tokens, or when bwd->n_slots is not 1, 2, 4
+ * or 8, the update runs as its own launch first.  step_ws as for
+ * fp8ln_ln_linear_fwd_step (a step's forward and backward may share one, in
+ * stream order). */
+int fp8ln_ln_linear_bwd_step(const fp8ln_recipe* recipe, int64_t tokens, int64_t in_features,
+                             int64_t out_features, int32_t params_dtype, const void* dy,
+                             const void* x, const void* gamma, const fp8ln_linear_ctx* ctx,
+                             const fp8ln_meta* fwd, const fp8ln_meta* bwd, void* dx,
+                             float* dgamma, float* dbeta, float* dweight, float* dbias,
+                             void* workspace, size_t workspace_bytes, void* step_ws,
+                             void* stream);
 
 /* For callers that cannot allocate device memory (code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc): fp8ln_ln_linear_bwd
@@ -575,6 +595,18 @@ int fp8ln_ln_mlp_bwd(const fp8ln_recipe* recipe, int64_t tokens, int64_t hidden,
                      const fp8ln_meta* bwd, void* dx, float* dgamma, float* dbeta,
                      float* dw1, float* db1, float* dw2, float* db2, void* workspace,
                      size_t workspace_bytes, void* stream);
+
+/* One backward step of LayerNormMLP: fp8ln_scaling_update(recipe, bwd) followed
+ * by fp8ln_ln_mlp_bwd with the same arguments, with identical results, the
+ * update folded in as in fp8ln_ln_linear_bwd_step (the fc1 gradient's amax,
+ * from the fc2 dgrad's fused cast, is recorded in step_ws with the output
+ * gradient's).  step_ws as for fp8ln_ln_linear_fwd_step. */
+int fp8ln_ln_mlp_bwd_step(const fp8ln_recipe* recipe, int64_t tokens, int64_t hidden,
+                          int64_t ffn, int32_t params_dtype, const void* dy, const void* x,
+                          const void* gamma, const fp8ln_mlp_ctx* ctx, const fp8ln_meta* fwd,
+                          const fp8ln_meta* bwd, void* dx, float* dgamma, float* dbeta,
+                          float* dw1, float* db1, float* dw2, float* db2, void* workspace,
+                          size_t workspace_bytes, void* step_ws, void* stream);
 
 #ifdef __cplusplus
 }

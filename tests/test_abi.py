@@ -134,6 +134,23 @@ def test_forward_step_checks_its_workspace(lib):
     assert s == _abi.FP8LN_ERR_INVALID_ARG and b"aligned" in lib.fp8ln_last_error()
 
 
+def test_backward_steps_check_their_workspace(lib):
+    r = _recipe()
+    p = C.c_void_p(256)
+    mf = _abi.MetaStruct(256, 256, 256, 4, _abi.META_FORWARD)
+    mb = _abi.MetaStruct(256, 256, 256, 2, _abi.META_BACKWARD)
+    lctx = _abi.LinearCtxStruct(256, 256, 256, 256, 256, 256)
+    s = lib.fp8ln_ln_linear_bwd_step(C.byref(r), 32, 768, 2304, _abi.DTYPE_BF16, p, p, p,
+                                     C.byref(lctx), C.byref(mf), C.byref(mb), p, p, p, p, None,
+                                     p, 1 << 30, None, None)
+    assert s == _abi.FP8LN_ERR_INVALID_ARG and b"step_ws" in lib.fp8ln_last_error()
+    mctx = _abi.MlpCtxStruct(*([256] * len(_abi.MlpCtxStruct._fields_)))
+    s = lib.fp8ln_ln_mlp_bwd_step(C.byref(r), 32, 768, 3072, _abi.DTYPE_BF16, p, p, p,
+                                  C.byref(mctx), C.byref(mf), C.byref(mb), p, p, p, p, None, p,
+                                  None, p, 1 << 30, None, None)
+    assert s == _abi.FP8LN_ERR_INVALID_ARG and b"step_ws" in lib.fp8ln_last_error()
+
+
 def test_check_support_reports_a_reason_without_a_gpu(lib):
     buf = C.create_string_buffer(128)
     ok = lib.fp8ln_check_support(0, buf, len(buf))
