@@ -21,8 +21,7 @@ namespace fp8ln {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTile = 64;           // rows and columns of one transposition tile
-constexpr int kTPad = kTile + 16;   // byte pitch of the transposition tile
+constexpr int kTile = 64;           // rows and columns of one bf16 transposition tile
 
 template <bool IN_F32, int FMT, int NT>
 __global__ __launch_bounds__(NT) void cast_tile_kernel(
@@ -49,28 +48,85 @@ __global__ __launch_bounds__(NT) void cast_tile_step_kernel(
                                      [&]() { window_scales<NT>(u, sh); });
 }
 
-// in [rows][cols] -> out [cols][rows], 64 x 64 byte tiles (cols % 16 == 0,
-// rows % 16 == 0).
+// in [rows][cols] -> out [cols][rows] (rows % 16 == 0, cols % 16 == 0), over
+// kTR x kTC byte tiles on a resident grid, the next tile's loads in flight while
+// the current one is transposed; reads are kTC-byte row segments and writes
+// kTR-byte row segments of the output.  Thread t owns the 4 x 4 byte blocks at
+// columns 4 (t % (kTC / 4)) .. +3 and rows 4 (t / (kTC / 4)) + kRP p .. +3 of a
+// tile: it loads one word of each of those rows (kTC / 4 lanes read kTC
+// contiguous bytes of a row), transposes each block in registers with byte
+// selects and writes one word per column (four rows) into LDS; then each thread
+// reads 16-byte pieces of output rows (columns of the tile) and stores them.
+constexpr int kTR = 128;                    // tile rows (bytes of an output row segment)
+constexpr int kTC = 128;                    // tile columns (bytes of an input row segment)
+constexpr int kTB = kTC / 4;                // threads across a tile row
+constexpr int kRP = 4 * (256 / kTB);        // rows covered by one pass of the workgroup
+constexpr int kTPass = kTR / kRP;           // passes per tile
+constexpr int kTW = kTR / 4 + 1;            // words per LDS row of the transposed tile
+constexpr int kTChunks = kTC * (kTR / 16) / 256;   // 16-byte output pieces per thread
+
+__device__ __forceinline__ void transpose4x4_u8(const uint32_t w[4], uint32_t col[4]) {
+    // perm(hi, lo, s): byte i of the result is byte s_i of {hi:lo} (lo = bytes 0-3)
+    const uint32_t t01l = __builtin_amdgcn_perm(w[1], w[0], 0x05010400u);
+    const uint32_t t01h = __builtin_amdgcn_perm(w[1], w[0], 0x07030602u);
+    const uint32_t t23l = __builtin_amdgcn_perm(w[3], w[2], 0x05010400u);
+    const uint32_t t23h = __builtin_amdgcn_perm(w[3], w[2], 0x07030602u);
+    col[0] = __builtin_amdgcn_perm(t23l, t01l, 0x05040100u);
+    col[1] = __builtin_amdgcn_perm(t23l, t01l, 0x07060302u);
+    col[2] = __builtin_amdgcn_perm(t23h, t01h, 0x05040100u);
+    col[3] = __builtin_amdgcn_perm(t23h, t01h, 0x07060302u);
+}
+
 __global__ __launch_bounds__(kThreads) void transpose_u8_kernel(const uint8_t* __restrict__ in,
                                                                 int64_t rows, int64_t cols,
                                                                 uint8_t* __restrict__ out) {
-    __shared__ uint8_t tile[kTile][kTPad];
+    static_assert(kThreads == 256, "thread layout");
+    __shared__ uint32_t tw[kTC][kTW];
     const int t = threadIdx.x;
-    const int lr = t / 4;
-    const int lc = (t % 4) * 16;
-    const int64_t r = (int64_t)blockIdx.y * kTile + lr;
-    const int64_t c0 = (int64_t)blockIdx.x * kTile + lc;
-    uint4 w = make_uint4(0, 0, 0, 0);
-    if (r < rows && c0 < cols) w = load_nt(reinterpret_cast<const uint4*>(in + r * cols + c0));
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    const int a = t / kTB, b = t % kTB;
+    const int64_t tiles_x = (cols + kTC - 1) / kTC;
+    const int64_t tiles = tiles_x * ((rows + kTR - 1) / kTR);
+    uint32_t w[kTPass][4];
+    auto load = [&](int64_t tile) {
+        const int64_t r0 = (tile / tiles_x) * kTR + 4 * a;
+        const int64_t c = (tile % tiles_x) * kTC + 4 * b;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) tile[lc + i][lr] = (uint8_t)(ws[i / 4] >> (8 * (i % 4)));
-    __syncthreads();
-    const int64_t oc = (int64_t)blockIdx.x * kTile + lr;
-    const int64_t orow0 = (int64_t)blockIdx.y * kTile + lc;
-    if (oc < cols && orow0 < rows)
-        store_nt(reinterpret_cast<uint4*>(out + oc * rows + orow0),
-                 *reinterpret_cast<const uint4*>(&tile[lr][lc]));
+        for (int p = 0; p < kTPass; ++p) {
+            const int64_t r = r0 + kRP * p;
+            const bool ok = tile < tiles && r < rows && c < cols;   // 4-row, 4-column groups are whole
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                w[p][k] = ok ? __builtin_nontemporal_load(
+                                   reinterpret_cast<const uint32_t*>(in + (r + k) * cols + c))
+                             : 0u;
+        }
+    };
+    load(blockIdx.x);
+    for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+        uint32_t col[kTPass][4];
+#pragma unroll
+        for (int p = 0; p < kTPass; ++p) transpose4x4_u8(w[p], col[p]);
+        load(tile + gridDim.x);   // in flight while this tile goes through LDS
+#pragma unroll
+        for (int p = 0; p < kTPass; ++p)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) tw[4 * b + k][kRP / 4 * p + a] = col[p][k];
+        __syncthreads();
+        const int64_t c0 = (tile % tiles_x) * kTC, r0 = (tile / tiles_x) * kTR;
+#pragma unroll
+        for (int q = 0; q < kTChunks; ++q) {
+            const int u = t + q * kThreads;      // piece u: column u / (kTR / 16), rows 16 (u % ..)
+            const int oc = u / (kTR / 16), om = u % (kTR / 16);
+            uint4 v;
+            v.x = tw[oc][4 * om];
+            v.y = tw[oc][4 * om + 1];
+            v.z = tw[oc][4 * om + 2];
+            v.w = tw[oc][4 * om + 3];
+            const int64_t gc = c0 + oc, gr = r0 + 16 * om;
+            if (gc < cols && gr < rows) store_nt(reinterpret_cast<uint4*>(out + gc * rows + gr), v);
+        }
+        __syncthreads();   // the tile's LDS is free for the next
+    }
 }
 
 // in [rows][cols] -> out [cols][rows] for 16-bit elements (bf16), 64 x 64 tiles
@@ -268,9 +324,13 @@ hipError_t launch_cast_amax_step(int64_t rows, int64_t cols, const void* in, int
 hipError_t launch_transpose_u8(int64_t rows, int64_t cols, const uint8_t* in, uint8_t* out,
                                hipStream_t stream) {
     if (rows == 0 || cols == 0) return hipSuccess;
-    if ((rows + kTile - 1) / kTile > 65535) return hipErrorInvalidValue;   // grid y limit
-    const dim3 grid((unsigned)((cols + kTile - 1) / kTile), (unsigned)((rows + kTile - 1) / kTile));
-    hipLaunchKernelGGL(transpose_u8_kernel, grid, dim3(kThreads), 0, stream, in, rows, cols, out);
+    static int resident = 0;
+    hipError_t e = resident_blocks(transpose_u8_kernel, kThreads, resident);
+    if (e != hipSuccess) return e;
+    const int64_t tiles = ((cols + kTC - 1) / kTC) * ((rows + kTR - 1) / kTR);
+    const unsigned blocks = (unsigned)(tiles < resident ? tiles : resident);
+    hipLaunchKernelGGL(transpose_u8_kernel, dim3(blocks), dim3(kThreads), 0, stream, in, rows,
+                       cols, out);
     return hipGetLastError();
 }
 
