@@ -35,6 +35,7 @@ def _oracle_ln(x_bits, g_bits, b_bits, eps, scale, fmt):
     (48, 1024, ops.E5M2, True, 5000.0),
     (64, 8192, ops.E4M3, False, 60.0),
     (16, 4096, ops.E4M3, True, 1.0),
+    (272, 208, ops.E5M2, True, 300.0),   # transposed tiles cut on both edges
     (0, 768, ops.E4M3, False, 1.0),
 ])
 def test_ln_cast_amax_matches_oracle(rows, hidden, fp8, with_t, scale):
