@@ -48,11 +48,12 @@ def test_small_integer_gemm_is_bit_exact(fa, fb, M, N, K):
     np.testing.assert_array_equal(out.cpu().numpy(), av @ bv.T)
 
 
-# Small products on 64 x 64 tiles with 1, 16, 49, 33 and 23 steps of K (whole
-# rounds of the four-stage ring with 0, 1 and 3 steps over).
+# Small products on 64 x 64 tiles with 1, 16, 49, 33, 23 and 17 steps of K
+# (whole rounds of the four-stage ring with 0, 1 and 3 steps over), the last cut
+# on every edge (M % 64, N % 64 and K % 64 all 16).
 @pytest.mark.parametrize("fa,fb", PAIRS, ids=["e4m3xe4m3", "e5m2xe4m3", "e4m3xe5m2", "e5m2xe5m2"])
 @pytest.mark.parametrize("M,N,K", [(64, 64, 64), (200, 144, 1024), (1024, 512, 3136),
-                                   (130, 208, 2112), (70, 64, 1472)])
+                                   (130, 208, 2112), (70, 64, 1472), (2000, 784, 1040)])
 def test_small_tile_variants_are_bit_exact(fa, fb, M, N, K):
     """|a|, |b| <= 8 and K <= 3136: every partial sum is an integer below 2^24."""
     a, av = int_codes((M, K), fa, M * 5 + K)
