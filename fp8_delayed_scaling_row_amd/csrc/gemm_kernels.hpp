@@ -13,13 +13,15 @@
 // wgrad products are all of this form once the cast kernels have written the
 // transposed operand copies.
 //
-// Tiling (gfx950): every wave owns a 64 x 128 sub-tile (64 x 64 for the smallest
-// tile) built from V_MFMA_F32_32X32X64_F8F6F4 results accumulated in fp32
-// registers, two waves per SIMD.  Three workgroup shapes: 256 x 256 over eight
-// waves (one workgroup per CU, least LDS and L2 traffic per MFMA, for long K);
-// 128 x 256 over four waves with a three-stage ring, two workgroups per CU so
-// that one's epilogue overlaps the other's main loop (K up to 2048); and 128 x
-// 128 over four waves for problems too small to fill the CUs otherwise.  The
+// Tiling (gfx950): every wave owns a sub-tile of V_MFMA_F32_32X32X64_F8F6F4
+// results accumulated in fp32 registers (64 x 128 in the large tiles), two or
+// more waves per SIMD.  Four workgroup shapes: 256 x 256 over eight waves (one
+// workgroup per CU, least LDS and L2 traffic per MFMA, for long K); 128 x 256
+// over four waves with a three-stage ring, two workgroups per CU so that one's
+// epilogue overlaps the other's main loop (K up to 2048); 128 x 128 over four
+// waves of 64 x 64 and 64 x 64 over four waves of 32 x 32 for problems too
+// small to fill the CUs otherwise; independent small products can share one
+// grouped launch.  The
 // operand formats (E4M3 / E5M2) are chosen per operand by the instruction's
 // cbsz / blgp fields.  K advances 64 bytes per stage through an LDS ring filled
 // by direct-to-LDS buffer loads issued NS - 1 stages ahead, so memory latency

@@ -135,6 +135,7 @@ struct SumBatch {
              int64_t split);   // false when full
 };
 hipError_t launch_sum_batch(const SumBatch& b, hipStream_t stream);
+// in [rows][cols] -> out [cols][rows] bytes (rows, cols % 16 == 0).
 hipError_t launch_transpose_u8(int64_t rows, int64_t cols, const uint8_t* in, uint8_t* out,
                                hipStream_t stream);
 hipError_t launch_encode_range(uint32_t start, int64_t count, int fp8, uint8_t* out,
