@@ -30,8 +30,9 @@ Readings (the pages name the modules and the recipe, not their internals):
   wgrad with the forward's
   FP8 input codes; bias gradients are column sums of the unquantised
   gradient; dx, dgamma, dbeta come from the LayerNorm backward.  Results are
-  float64 here; the HIP path returns dx in bf16 and the rest in fp32 ("converts
-  gradients back to BF16 or FP32 for the optimizer").
+  float64 here; the HIP path returns dx in bf16 and the rest in fp32, the two
+  precisions in which the pages have gradients leave FP8 ("Turbo-charging your
+  transformer training", "Playing with lower-precision formats: BF16 vs FP8").
 """
 from __future__ import annotations
 
