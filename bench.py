@@ -18,11 +18,12 @@ speedup over them, the comparison the pages make.
 Step times are replays of consecutive steps captured once in a HIP graph (the
 same kernels on the same buffers, without host launch gaps); the host-launched
 step time is reported beside them as eager_ms_per_step.  The roofline's kernel
-duration comes from HIP events around eager launches of that kernel.
+duration comes from HIP events around graph-replayed back-to-back launches of that
+kernel (an event pair around each host-launched kernel is reported beside it).
 
 Every input is synthetic and generated on the device before timing.  The CPU
-baseline runs the oracle (numpy, float64) on a bounded sample of the headline
-workload on this host.
+baseline runs the C++ oracle (float64, OpenMP on the host's cores) on a bounded
+sample of the headline workload on this host.
 """
 from __future__ import annotations
 

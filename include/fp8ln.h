@@ -53,7 +53,7 @@ extern "C" {
 typedef enum {
     FP8LN_OK = 0,
     FP8LN_ERR_INVALID_ARG = -1,   /* null pointer, bad size, bad enum value   */
-    FP8LN_ERR_UNSUPPORTED = -2,   /* valid request this build does not serve */
+    FP8LN_ERR_UNSUPPORTED = -2,   /* valid request the library does not serve */
     FP8LN_ERR_HIP = -3            /* a HIP runtime call or launch failed      */
 } fp8ln_status;
 
