@@ -232,3 +232,42 @@ def test_largest_contraction_passes_the_size_check(lib):
     p = C.c_void_p(256)
     lib.fp8ln_gemm(16, 16, OK_K, p, 0, p, 0, p, p, None, _abi.DTYPE_F32, p, None)
     assert b"contraction" not in lib.fp8ln_last_error()
+
+
+C_CALLER = r"""
+#include <stdio.h>
+#include "fp8ln.h"
+int main(void) {
+    char reason[128];
+    const int ok = fp8ln_check_support(0, reason, sizeof reason);
+    fp8ln_recipe r = {0};
+    r.amax_history_len = 0;   /* outside 1..1024: refused before any device call */
+    const int s = fp8ln_scaling_update(&r, NULL, NULL);
+    printf("%s|%s|%d\n", fp8ln_status_string(FP8LN_OK), fp8ln_status_string(s), ok == 0 || ok == 1);
+    return s == FP8LN_ERR_INVALID_ARG ? 0 : 1;
+}
+"""
+
+
+def test_header_serves_a_c99_caller(tmp_path):
+    """The boundary is plain C: a C99 program (pedantic, warnings as errors)
+    includes the header, links the library and calls it (argument checks and
+    status strings need no GPU)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    if not os.path.exists(_abi.LIB_PATH):
+        pytest.fail(f"{_abi.LIB_PATH} is not built")
+    src = tmp_path / "caller.c"
+    src.write_text(C_CALLER)
+    exe = tmp_path / "caller"
+    libdir = os.path.dirname(_abi.LIB_PATH)
+    subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                    f"-I{os.path.dirname(HEADER)}", str(src), "-o", str(exe), f"-L{libdir}",
+                    "-lfp8ln", f"-Wl,-rpath,{libdir}"], check=True, capture_output=True,
+                   text=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert r.stdout.strip() == "ok|invalid argument|1", r.stdout
