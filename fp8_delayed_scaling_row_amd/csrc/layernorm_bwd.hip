@@ -50,28 +50,44 @@ __global__ __launch_bounds__(kThreads) void ln_bwd_kernel(
 
     for (int64_t row = (int64_t)blockIdx.x * kWavesPerBlock + wave; row < rows;
          row += (int64_t)gridDim.x * kWavesPerBlock) {
+        // Every load of the row goes out before any is used: chunks past the row
+        // read the row's last chunk (the index is clamped, so there is no branch
+        // around the loads) and are masked below.  With a branch per chunk the
+        // compiler waits for each chunk's loads before issuing the next chunk's,
+        // and a row costs one memory round trip per chunk.
         const float mu = mean[row];
         const float rs = rstd[row];
+        uint4 xr[CPL], dr[DY_BF16 ? CPL : 2 * CPL];
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = lane + i * kWave;
+            const int64_t cc = row * nchunk + (c < nchunk ? c : nchunk - 1);
+            xr[i] = load_nt(x + cc);
+            if constexpr (DY_BF16) {
+                dr[i] = load_nt((const uint4*)dy_raw + cc);
+            } else {
+                dr[2 * i] = load_nt((const uint4*)dy_raw + 2 * cc);
+                dr[2 * i + 1] = load_nt((const uint4*)dy_raw + 2 * cc + 1);
+            }
+        }
         float xh[CPL * 8], d[CPL * 8];
         float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
-            const int c = lane + i * kWave;
-            if (c < nchunk) {
-                unpack_bf16x8(load_nt(x + row * nchunk + c), xh + 8 * i);
-                if constexpr (DY_BF16) {
-                    unpack_bf16x8(load_nt((const uint4*)dy_raw + row * nchunk + c), d + 8 * i);
-                } else {
-                    const float4* dy = (const float4*)dy_raw;
-                    const float4 a = load_nt(dy + (row * nchunk + c) * 2);
-                    const float4 b2 = load_nt(dy + (row * nchunk + c) * 2 + 1);
-                    d[8 * i + 0] = a.x; d[8 * i + 1] = a.y; d[8 * i + 2] = a.z;
-                    d[8 * i + 3] = a.w; d[8 * i + 4] = b2.x; d[8 * i + 5] = b2.y;
-                    d[8 * i + 6] = b2.z; d[8 * i + 7] = b2.w;
-                }
+            const bool valid = lane + i * kWave < nchunk;
+            unpack_bf16x8(xr[i], xh + 8 * i);
+            if constexpr (DY_BF16) {
+                unpack_bf16x8(dr[i], d + 8 * i);
             } else {
+                const uint4 a = dr[2 * i], b2 = dr[2 * i + 1];
+                const uint32_t w[8] = {a.x, a.y, a.z, a.w, b2.x, b2.y, b2.z, b2.w};
 #pragma unroll
-                for (int k = 0; k < 8; ++k) { xh[8 * i + k] = mu; d[8 * i + k] = 0.0f; }
+                for (int k = 0; k < 8; ++k) d[8 * i + k] = __uint_as_float(w[k]);
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {   // chunks past the row: xhat 0, no gradient
+                xh[8 * i + k] = valid ? xh[8 * i + k] : mu;
+                d[8 * i + k] = valid ? d[8 * i + k] : 0.0f;
             }
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
