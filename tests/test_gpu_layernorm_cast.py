@@ -214,8 +214,11 @@ def test_cast_amax_infinities_nan_and_overflow(fp8, in_f32, with_nan):
     assert np.isnan(a) if with_nan else a == np.inf
 
 
+# hidden 1544 and 3080: the last chunk of a lane is past the row for all lanes but
+# one (four chunks per lane) or for most (eight per lane), so the masking of the
+# chunks past the row is exercised at every per-lane chunk count
 @pytest.mark.parametrize("rows,hidden", [(1, 8), (37, 768), (2048, 768), (513, 2048),
-                                         (64, 4096), (0, 256)])
+                                         (64, 4096), (0, 256), (130, 1544), (70, 3080)])
 def test_layernorm_bwd_matches_oracle(rows, hidden):
     wl = f"lnb/{rows}x{hidden}"
     x = inputs.normal_bf16((rows, hidden), inputs.seed_for(wl, "x"))
@@ -280,8 +283,11 @@ def test_layernorm_module_fwd_matches_oracle(rows, hidden):
     print(f"layernorm {rows}x{hidden}: {stats}")
 
 
+# hidden 1544 and 3080: the last chunk of a lane is past the row for all lanes but
+# one (four chunks per lane) or for most (eight per lane), so the masking of the
+# chunks past the row is exercised at every per-lane chunk count
 @pytest.mark.parametrize("rows,hidden", [(1, 8), (37, 768), (2048, 768), (513, 2048),
-                                         (64, 4096), (0, 256)])
+                                         (64, 4096), (0, 256), (130, 1544), (70, 3080)])
 def test_layernorm_module_bwd_bf16_grad(rows, hidden):
     """The plain LayerNorm backward with a bf16 incoming gradient against the
     oracle's float64 backward; and on the same values it equals the fp32-gradient
