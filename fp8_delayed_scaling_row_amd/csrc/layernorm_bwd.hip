@@ -29,7 +29,8 @@ __global__ __launch_bounds__(kThreads) void ln_bwd_kernel(
     const void* __restrict__ dy_raw, const uint4* __restrict__ x, const float* __restrict__ mean,
     const float* __restrict__ rstd, const uint4* __restrict__ gamma, uint4* __restrict__ dx,
     float* __restrict__ partial, int64_t rows, int hidden) {
-    extern __shared__ float sm[];   // [2][hidden]: dgamma, dbeta of the block
+    extern __shared__ float4 sm_raw[];   // [2][hidden] floats: dgamma, dbeta of the block
+    float* sm = reinterpret_cast<float*>(sm_raw);
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int nchunk = hidden / 8;
@@ -121,7 +122,11 @@ __global__ __launch_bounds__(kThreads) void ln_bwd_kernel(
             }
         }
     }
-    // combine the block's waves in a fixed order (wave 0 first)
+    // combine the block's waves in a fixed order (wave 0 first), 16 bytes at a
+    // time: a lane's eight columns are 32 contiguous bytes of LDS, and 4-byte
+    // accesses at that lane stride would meet in a few banks
+    float4* sg = reinterpret_cast<float4*>(sm);
+    float4* sd = reinterpret_cast<float4*>(sm + hidden);
     for (int w = 0; w < kWavesPerBlock; ++w) {
         if (wave == w) {
 #pragma unroll
@@ -129,17 +134,26 @@ __global__ __launch_bounds__(kThreads) void ln_bwd_kernel(
                 const int c = lane + i * kWave;
                 if (c < nchunk) {
 #pragma unroll
-                    for (int k = 0; k < 8; ++k) {
-                        float* pg = sm + c * 8 + k;
-                        float* pd = sm + hidden + c * 8 + k;
-                        *pg = w == 0 ? dg[8 * i + k] : *pg + dg[8 * i + k];
-                        *pd = w == 0 ? db[8 * i + k] : *pd + db[8 * i + k];
+                    for (int h = 0; h < 2; ++h) {
+                        const float* a = dg + 8 * i + 4 * h;
+                        const float* b = db + 8 * i + 4 * h;
+                        float4 ga = make_float4(a[0], a[1], a[2], a[3]);
+                        float4 da = make_float4(b[0], b[1], b[2], b[3]);
+                        if (w != 0) {
+                            const float4 go = sg[2 * c + h], dold = sd[2 * c + h];
+                            ga = make_float4(go.x + ga.x, go.y + ga.y, go.z + ga.z, go.w + ga.w);
+                            da = make_float4(dold.x + da.x, dold.y + da.y, dold.z + da.z,
+                                             dold.w + da.w);
+                        }
+                        sg[2 * c + h] = ga;
+                        sd[2 * c + h] = da;
                     }
                 }
             }
         }
         __syncthreads();
     }
+    // 4-byte stores: the workspace carries no alignment promise
     float* pb = partial + (int64_t)blockIdx.x * 2 * hidden;
     for (int j = threadIdx.x; j < 2 * hidden; j += kThreads) pb[j] = sm[j];
 }
