@@ -369,100 +369,199 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, int vb) {
         return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                    (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     };
-    auto compute = [&](const uint8_t* stage) {
-        const uint8_t* sa = stage;
-        const uint8_t* sb = stage + A_BYTES;
-        v8i af[TM];
-#pragma unroll
-        for (int i = 0; i < TM; ++i) af[i] = frag(sa, wm * WM + 32 * i + fr);
-        if constexpr (FA == kOpBf16) {
-            // bf16: a stage holds 32 elements of K per row, two 32x32x16 MFMAs.
-            // Each lane splits its 32-byte fragment into halves h = 0, 1; MFMA h
-            // sums over the elements of half h of every lane.  A and B split
-            // alike, so every k meets its partner exactly once.
-            static_assert(FB == kOpBf16, "bf16 takes bf16");
-            v8i bfr[TN];
-#pragma unroll
-            for (int j = 0; j < TN; ++j) bfr[j] = frag(sb, wn * WN + 32 * j + fr);
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
+    // The 256 x 256 tile reads each stage's fragments one step early (its waves
+    // have registers for a second fragment set); the other tiles read them at the
+    // start of the step that uses them.
+    constexpr bool kEarlyFrags = BM == 256 && BN == 256;
+    if constexpr (kEarlyFrags) {
+        // One stage's operand fragments: TM of A, TN of B.
+        struct Frags {
+            v8i a[TM];
+            v8i b[TN];
+        };
+        auto read_frags = [&](const uint8_t* stage, Frags& f) {
+    #pragma unroll
+            for (int i = 0; i < TM; ++i) f.a[i] = frag(stage, wm * WM + 32 * i + fr);
+    #pragma unroll
+            for (int j = 0; j < TN; ++j) f.b[j] = frag(stage + A_BYTES, wn * WN + 32 * j + fr);
+        };
+        auto mfmas = [&](const Frags& f) {
+            if constexpr (FA == kOpBf16) {
+                // bf16: a stage holds 32 elements of K per row, two 32x32x16 MFMAs.
+                // Each lane splits its 32-byte fragment into halves h = 0, 1; MFMA h
+                // sums over the elements of half h of every lane.  A and B split
+                // alike, so every k meets its partner exactly once.
+                static_assert(FB == kOpBf16, "bf16 takes bf16");
+    #pragma unroll
+                for (int h = 0; h < 2; ++h)
+    #pragma unroll
+                    for (int j = 0; j < TN; ++j)
+    #pragma unroll
+                        for (int i = 0; i < TM; ++i) {
+                            const v8i& bv = f.b[j];
+                            const v8i& av = f.a[i];
+                            const v4i b4 = h ? v4i{bv[4], bv[5], bv[6], bv[7]}
+                                             : v4i{bv[0], bv[1], bv[2], bv[3]};
+                            const v4i a4 = h ? v4i{av[4], av[5], av[6], av[7]}
+                                             : v4i{av[0], av[1], av[2], av[3]};
+                            acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                __builtin_bit_cast(v8bf, b4), __builtin_bit_cast(v8bf, a4),
+                                acc[j][i], 0, 0, 0);
+                        }
+            } else {
+                // D[n][m] = sum_k B[n][k] A[m][k]: the B rows are the MFMA's first operand
+    #pragma unroll
                 for (int j = 0; j < TN; ++j)
-#pragma unroll
-                    for (int i = 0; i < TM; ++i) {
-                        const v8i& bv = bfr[j];
-                        const v8i& av = af[i];
-                        const v4i b4 = h ? v4i{bv[4], bv[5], bv[6], bv[7]}
-                                         : v4i{bv[0], bv[1], bv[2], bv[3]};
-                        const v4i a4 = h ? v4i{av[4], av[5], av[6], av[7]}
-                                         : v4i{av[0], av[1], av[2], av[3]};
-                        acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            __builtin_bit_cast(v8bf, b4), __builtin_bit_cast(v8bf, a4),
-                            acc[j][i], 0, 0, 0);
-                    }
-            return;
-        }
-        // D[n][m] = sum_k B[n][k] A[m][k]: the B rows are the MFMA's first operand
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const v8i bf = frag(sb, wn * WN + 32 * j + fr);
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-                acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    bf, af[i], acc[j][i], FB, FA, 0, 0, 0, 0);
-        }
-    };
-    // Stage kt lives in st[kt % NS]; loads run NS - 1 stages ahead.  Before
-    // reading stage kt a wave waits for its own loads of that stage (the NS - 2
-    // later stages may stay in flight), then the barrier makes every wave's loads
-    // visible and frees the stage read in the previous step, which is refilled
-    // right away.  The barrier is a bare s_barrier: __syncthreads() adds a
-    // workgroup fence, which waits for every outstanding load, the prefetched
-    // stages included.  The barrier also waits for the wave's own LDS reads, so
-    // no wave refills a stage another wave is still reading.  Every step looks
-    // the same: the look-ahead stages past the end of K are filled with zeros
-    // (all chunks out of range), so the wait count is a constant.
-    auto step = [&](uint8_t* cur, uint8_t* refill, int kt) {
-        // Scheduling fences keep the wait, the barrier and the refill at the top
-        // of the step: left to itself the scheduler sinks the refill below the
-        // MFMAs (and lifts MFMAs of the previous step past the barrier), which
-        // costs a step of latency cover.
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * P));
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        issue(refill, (int64_t)(kt + NS - 1) * BKS);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(cur);
-    };
+    #pragma unroll
+                    for (int i = 0; i < TM; ++i)
+                        acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            f.b[j], f.a[i], acc[j][i], FB, FA, 0, 0, 0, 0);
+            }
+        };
+        // Stage kt lives in st[kt % NS] and its fragments are read into registers one
+        // step early: step kt multiplies the fragments of stage kt (read during step
+        // kt - 1) while it reads those of stage kt + 1, so the MFMAs never wait on LDS
+        // at the start of a step.  Before reading stage kt + 1 a wave waits for its
+        // own loads of that stage (the NS - 2 later stages may stay in flight); the
+        // barrier then makes every wave's loads visible and shows that every wave has
+        // its stage-kt fragments in registers, so st[kt % NS] is refilled right away,
+        // with stage kt + NS.  The barrier is a bare s_barrier: __syncthreads() adds a
+        // workgroup fence, which waits for every outstanding load, the prefetched
+        // stages included.  Every step looks the same: the look-ahead stages past the
+        // end of K are filled with zeros (all chunks out of range), so the wait count
+        // is a constant.  Two fragment sets alternate, so the step sequence is
+        // unrolled by 2 NS and the stage buffers and fragment sets are fixed per step.
+        uint8_t* const ring_st[4] = {st0, st1, st2, st3};
+        Frags fa, fb;
+        auto step = [&](int i, int kt) {   // i: position in the unrolled sequence
+            Frags& use = (i & 1) ? fb : fa;
+            Frags& load = (i & 1) ? fa : fb;
+            // Scheduling fences keep the wait, the barrier and the refill at the top
+            // of the step: left to itself the scheduler sinks the refill below the
+            // MFMAs (and lifts MFMAs of the previous step past the barrier), which
+            // costs a step of latency cover.
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * P));
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            issue(ring_st[i % NS], (int64_t)(kt + NS) * BKS);
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(ring_st[(i + 1) % NS], load);
+            mfmas(use);
+        };
 
-    // Whole rounds of NS steps, then the last nk % NS steps one by one (the same
-    // step code, so the waits stay constant; only stages past K are zero-filled,
-    // and no step multiplies one).
-    const int nk = (int)((K + BKS - 1) / BKS);
-    int kt = 0;
-    issue(st0, 0);
-    issue(st1, BKS);
-    if constexpr (NS == 4) {
+        const int nk = (int)((K + BKS - 1) / BKS);
+        issue(st0, 0);
+        issue(st1, BKS);
         issue(st2, 2 * BKS);
-        for (; kt + 4 <= nk; kt += 4) {
-            step(st0, st3, kt);
-            step(st1, st0, kt + 1);
-            step(st2, st1, kt + 2);
-            step(st3, st2, kt + 3);
+        if constexpr (NS == 4) issue(st3, 3 * BKS);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 1) * P));
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        read_frags(st0, fa);
+        int kt = 0;
+        for (; kt + 2 * NS <= nk; kt += 2 * NS) {
+    #pragma unroll
+            for (int i = 0; i < 2 * NS; ++i) step(i, kt + i);
         }
-        if (kt < nk) step(st0, st3, kt);
-        if (kt + 1 < nk) step(st1, st0, kt + 1);
-        if (kt + 2 < nk) step(st2, st1, kt + 2);
+    #pragma unroll
+        for (int i = 0; i < 2 * NS - 1; ++i)
+            if (kt + i < nk) step(i, kt + i);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // the zero-filled look-ahead stages
     } else {
-        for (; kt + 3 <= nk; kt += 3) {
-            step(st0, st2, kt);
-            step(st1, st0, kt + 1);
-            step(st2, st1, kt + 2);
+        auto compute = [&](const uint8_t* stage) {
+            const uint8_t* sa = stage;
+            const uint8_t* sb = stage + A_BYTES;
+            v8i af[TM];
+    #pragma unroll
+            for (int i = 0; i < TM; ++i) af[i] = frag(sa, wm * WM + 32 * i + fr);
+            if constexpr (FA == kOpBf16) {
+                // bf16: a stage holds 32 elements of K per row, two 32x32x16 MFMAs.
+                // Each lane splits its 32-byte fragment into halves h = 0, 1; MFMA h
+                // sums over the elements of half h of every lane.  A and B split
+                // alike, so every k meets its partner exactly once.
+                static_assert(FB == kOpBf16, "bf16 takes bf16");
+                v8i bfr[TN];
+    #pragma unroll
+                for (int j = 0; j < TN; ++j) bfr[j] = frag(sb, wn * WN + 32 * j + fr);
+    #pragma unroll
+                for (int h = 0; h < 2; ++h)
+    #pragma unroll
+                    for (int j = 0; j < TN; ++j)
+    #pragma unroll
+                        for (int i = 0; i < TM; ++i) {
+                            const v8i& bv = bfr[j];
+                            const v8i& av = af[i];
+                            const v4i b4 = h ? v4i{bv[4], bv[5], bv[6], bv[7]}
+                                             : v4i{bv[0], bv[1], bv[2], bv[3]};
+                            const v4i a4 = h ? v4i{av[4], av[5], av[6], av[7]}
+                                             : v4i{av[0], av[1], av[2], av[3]};
+                            acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                __builtin_bit_cast(v8bf, b4), __builtin_bit_cast(v8bf, a4),
+                                acc[j][i], 0, 0, 0);
+                        }
+                return;
+            }
+            // D[n][m] = sum_k B[n][k] A[m][k]: the B rows are the MFMA's first operand
+    #pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const v8i bf = frag(sb, wn * WN + 32 * j + fr);
+    #pragma unroll
+                for (int i = 0; i < TM; ++i)
+                    acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        bf, af[i], acc[j][i], FB, FA, 0, 0, 0, 0);
+            }
+        };
+        // Stage kt lives in st[kt % NS]; loads run NS - 1 stages ahead.  Before
+        // reading stage kt a wave waits for its own loads of that stage (the NS - 2
+        // later stages may stay in flight), then the barrier makes every wave's loads
+        // visible and frees the stage read in the previous step, which is refilled
+        // right away.  The barrier is a bare s_barrier: __syncthreads() adds a
+        // workgroup fence, which waits for every outstanding load, the prefetched
+        // stages included.  The barrier also waits for the wave's own LDS reads, so
+        // no wave refills a stage another wave is still reading.  Every step looks
+        // the same: the look-ahead stages past the end of K are filled with zeros
+        // (all chunks out of range), so the wait count is a constant.
+        auto step = [&](uint8_t* cur, uint8_t* refill, int kt) {
+            // Scheduling fences keep the wait, the barrier and the refill at the top
+            // of the step: left to itself the scheduler sinks the refill below the
+            // MFMAs (and lifts MFMAs of the previous step past the barrier), which
+            // costs a step of latency cover.
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * P));
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            issue(refill, (int64_t)(kt + NS - 1) * BKS);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(cur);
+        };
+
+        // Whole rounds of NS steps, then the last nk % NS steps one by one (the same
+        // step code, so the waits stay constant; only stages past K are zero-filled,
+        // and no step multiplies one).
+        const int nk = (int)((K + BKS - 1) / BKS);
+        int kt = 0;
+        issue(st0, 0);
+        issue(st1, BKS);
+        if constexpr (NS == 4) {
+            issue(st2, 2 * BKS);
+            for (; kt + 4 <= nk; kt += 4) {
+                step(st0, st3, kt);
+                step(st1, st0, kt + 1);
+                step(st2, st1, kt + 2);
+                step(st3, st2, kt + 3);
+            }
+            if (kt < nk) step(st0, st3, kt);
+            if (kt + 1 < nk) step(st1, st0, kt + 1);
+            if (kt + 2 < nk) step(st2, st1, kt + 2);
+        } else {
+            for (; kt + 3 <= nk; kt += 3) {
+                step(st0, st2, kt);
+                step(st1, st0, kt + 1);
+                step(st2, st1, kt + 2);
+            }
+            if (kt < nk) step(st0, st2, kt);
+            if (kt + 1 < nk) step(st1, st0, kt + 1);
         }
-        if (kt < nk) step(st0, st2, kt);
-        if (kt + 1 < nk) step(st1, st0, kt + 1);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // the zero-filled look-ahead stages
     }
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // the zero-filled look-ahead stages
     __syncthreads();                            // the ring is free for the epilogue
 
     // ---- epilogue ----------------------------------------------------------------
