@@ -26,14 +26,15 @@ def int_bf16(shape, seed, lim=4):
     return oracle.f64_to_bf16_bits(vals), vals
 
 
-# (M, N, K): 64 x 64 tiles, 128 x 128, 128 x 256, and 256 x 256 (K > 1024)
+# (M, N, K): 64 x 64 tiles, 128 x 128, 128 x 256, and 256 x 256 (K > 1024; its steps
+# of 32 elements run in rounds of eight, here with 1, 4 and 7 steps over)
 SHAPES = [(1, 16, 16), (130, 144, 272), (257, 400, 64), (1024, 1024, 512), (2048, 1024, 128),
-          (4096, 4096, 256), (4096, 4096, 1040)]
+          (4096, 4096, 256), (4096, 4096, 1040), (4096, 4096, 1152), (4096, 4096, 1248)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
 def test_bf16_gemm_is_bit_exact_on_small_integers(M, N, K):
-    """|a|, |b| <= 4 and K <= 1040: every partial sum is an integer below 2^24, so
+    """|a|, |b| <= 4 and K <= 1248: every partial sum is an integer below 2^24, so
     fp32 accumulation in any order is exact."""
     a, av = int_bf16((M, K), M + 3 * K)
     b, bv = int_bf16((N, K), N + 5 * K)

@@ -246,14 +246,17 @@ def test_gelu_gemm_random_within_tolerance(M, N, K):
 
 # 128 x 256 tiles (K <= 2048; the second is ragged in M and N), then 256 x 256
 # tiles (K > 2048)
-# K steps of 64 bytes left after whole rounds of the ring: 256 x 256 tiles (four
-# stages) with 2, 1 and 3 steps over, 128 x 256 tiles (three stages) with 1 and 2
+# K steps of 64 bytes left after whole unrolled rounds: the 256 x 256 tile runs
+# its steps in rounds of eight (four ring stages, two fragment sets), here with 2,
+# 1 and 3 steps over; 128 x 256 tiles (three stages) with 1 and 2
 BIG = [(4096, 4096, 64), (4000, 4112, 48), (2048, 8192, 2176), (2048, 8192, 2112),
        (2048, 8192, 2240), (4096, 4096, 320)]
+# the 256 x 256 tile with 4, 6 and 7 steps over its rounds of eight
+BIG_TAILS = [(2048, 8192, 2304), (2048, 8192, 2432), (2048, 8192, 2496)]
 
 
 @pytest.mark.parametrize("fa,fb", PAIRS, ids=["e4m3xe4m3", "e5m2xe4m3", "e4m3xe5m2", "e5m2xe5m2"])
-@pytest.mark.parametrize("M,N,K", BIG)
+@pytest.mark.parametrize("M,N,K", BIG + BIG_TAILS)
 def test_small_integer_gemm_large_tiles_is_bit_exact(fa, fb, M, N, K):
     """Exact integer products through the 256 x 256 kernel: fp32 output bit for
     bit, and bf16 output (with a bias on a 1/64 grid) equal to the round-to-
